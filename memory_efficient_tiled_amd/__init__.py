@@ -1,0 +1,11 @@
+"""MI355X-native memory-efficient (tiled, online-softmax) attention forward.
+
+The compute path is the HIP library ``libattn.so`` (built from ``csrc/``);
+this package only marshals arguments to its C entry points.
+"""
+from .binding import (attn_fwd, attn_fwd_check, attn_fwd_num_splits,
+                      attn_fwd_workspace_bytes, lib_path, load_library,
+                      AttnError)
+
+__all__ = ["attn_fwd", "attn_fwd_check", "attn_fwd_num_splits",
+           "attn_fwd_workspace_bytes", "lib_path", "load_library", "AttnError"]

@@ -1,0 +1,161 @@
+"""ctypes binding to libattn.so -- argument marshalling only.
+
+Every step of the attention forward runs in the HIP library; this module
+checks tensor metadata, allocates the outputs with torch (device memory is
+torch's), passes raw device pointers and torch's current HIP stream, and turns
+non-zero return codes into exceptions.  There is no fallback: if the library
+is missing or fails, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn.so"
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+
+ATTN_OK = 0
+ATTN_EINVAL = -1
+ATTN_EUNSUPPORTED = -2
+ATTN_ENOMEM = -3
+ATTN_EHIP = -4
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"attn error {code}: {msg}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+_INT = ctypes.c_int
+_VP = ctypes.c_void_p
+_FP = ctypes.POINTER(ctypes.c_float)
+
+
+def load_library():
+    """Load libattn.so (built in-tree next to this file); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    shape_args = [_INT] * 6                    # B, Hq, Hkv, Nq, Nkv, D
+    lib.attn_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [ctypes.c_float, _INT, _INT, _VP]
+    lib.attn_fwd.restype = _INT
+    lib.attn_fwd_split.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [ctypes.c_float, _INT, _INT, _INT, _VP]
+    lib.attn_fwd_split.restype = _INT
+    lib.attn_fwd_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [ctypes.c_float, _INT, _INT]
+    lib.attn_fwd_check.restype = _INT
+    lib.attn_fwd_num_splits.argtypes = shape_args + [_INT, _INT, _INT]
+    lib.attn_fwd_num_splits.restype = _INT
+    lib.attn_fwd_workspace_bytes.argtypes = [_INT, _INT, _INT, _INT, _INT, _INT]
+    lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_strerror.argtypes = [_INT]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = _INT
+    _lib = lib
+    return lib
+
+
+def _raise(code: int):
+    lib = load_library()
+    msg = lib.attn_strerror(code).decode()
+    if code == ATTN_EHIP:
+        msg += f" (hipError {lib.attn_last_hip_error()})"
+    raise AttnError(code, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def attn_fwd_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Hq, Hkv, Nq, Nkv,
+                   D, scale, causal, dtype_code) -> int:
+    """Host-only argument validation (no HIP call); returns the error code."""
+    return load_library().attn_fwd_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr,
+                                         B, Hq, Hkv, Nq, Nkv, D, scale,
+                                         int(causal), dtype_code)
+
+
+def attn_fwd_num_splits(B, Hq, Hkv, Nq, Nkv, D, causal, dtype_code,
+                        num_cus=256) -> int:
+    """The split-KV count the library picks for this shape (host-only)."""
+    return load_library().attn_fwd_num_splits(B, Hq, Hkv, Nq, Nkv, D,
+                                              int(causal), dtype_code, num_cus)
+
+
+def attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, num_splits) -> int:
+    return load_library().attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, num_splits)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
+             out=None, lse=None, return_lse: bool = True, num_splits: int = 0):
+    """O = softmax(scale * Q K^T [causal top-left mask]) V on the GPU.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; contiguous, same dtype
+    (float16 or bfloat16), on one HIP device.  Returns (out, lse) with out
+    like q and lse float32 [B, Hq, Nq] (natural log), or just out when
+    ``return_lse`` is False.  ``num_splits`` = 0 lets the library choose the
+    split-KV count; a positive value forces it.  Runs on torch's current
+    stream; no host synchronisation.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, D]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)}")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    lse_ptr = lse.data_ptr() if (return_lse and lse is not None) else None
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
+                                float(scale), int(bool(causal)), dt,
+                                int(num_splits), stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return (out, lse) if return_lse else out

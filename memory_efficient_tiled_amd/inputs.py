@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module is shared by the oracle's tests, the GPU parity tests and the
+bench.  It holds none of the attention arithmetic: it draws Gaussian tensors
+from a seeded PCG64 stream, rounds them to the 16-bit input type and describes
+the workload shapes.  Both sides of every parity check read the same arrays.
+
+Workload shapes follow the pages:
+  * the isolated attention sweep (B=1, H=16, D=64, fp16) of the English
+    noflash-attention post at ai-navigate-news.com, section "It's actually
+    faster too!" (its benchmark table);
+  * the GQA decoder shape behind the Qwen 2.5 0.5B table of the same post,
+    section "Where it landed" (14 query heads over 2 KV heads, D=64);
+  * the 17K- and 75K-token video sequences of the same post, section
+    "The problem" (24 heads: the score-matrix sizes quoted there are
+    24 x N^2 x 4 bytes).
+The pages publish no tensors, so every input is synthetic.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    D: int
+    dtype: str
+    causal: bool
+    k_offset_std: float | None = None   # per-channel offset added to K
+    sampled_rows: int | None = None      # oracle rows per head at full size
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic flops: 4*B*Hq*Nq*Nkv*D, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.Nq * self.Nkv * self.D
+        return f / 2.0 if self.causal else f
+
+    def describe(self) -> str:
+        return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} Nq={self.Nq} "
+                f"Nkv={self.Nkv} D={self.D} {self.dtype} "
+                f"{'causal' if self.causal else 'non-causal'}")
+
+
+def _w(**kw) -> Workload:
+    return Workload(**kw)
+
+
+WORKLOADS: dict[str, Workload] = {}
+WORKLOADS["tiny-256"] = _w(name="tiny-256", B=1, Hq=16, Hkv=16, Nq=256, Nkv=256,
+                           D=64, dtype=F16, causal=False,
+                           note="tiny non-causal MHA")
+for _n in (1024, 2048, 4096, 8192, 16384):
+    WORKLOADS[f"sweep-{_n}"] = _w(name=f"sweep-{_n}", B=1, Hq=16, Hkv=16, Nq=_n,
+                                  Nkv=_n, D=64, dtype=F16, causal=False,
+                                  note="isolated MHA sweep")
+for _n in (4096, 8192, 16384):
+    WORKLOADS[f"gqa-causal-{_n}"] = _w(name=f"gqa-causal-{_n}", B=1, Hq=14, Hkv=2,
+                                       Nq=_n, Nkv=_n, D=64, dtype=F16, causal=True,
+                                       note="causal GQA decoder prefill")
+WORKLOADS["dit-17160"] = _w(name="dit-17160", B=1, Hq=24, Hkv=24, Nq=17160,
+                            Nkv=17160, D=128, dtype=BF16, causal=False,
+                            k_offset_std=0.5,
+                            note="video-DiT self-attention, K per-channel offset")
+WORKLOADS["dit-75600"] = _w(name="dit-75600", B=1, Hq=24, Hkv=24, Nq=75600,
+                            Nkv=75600, D=128, dtype=BF16, causal=False,
+                            sampled_rows=256,
+                            note="long video-DiT self-attention")
+
+HEADLINE = "dit-17160"
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); raw bits.
+
+    Inputs here are finite Gaussian draws, so no NaN handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> the 16-bit storage array (float16, or uint16 bf16 bits)."""
+    if dtype == F16:
+        return x.astype(np.float16)
+    if dtype == BF16:
+        return f32_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+@dataclasses.dataclass
+class Inputs:
+    q: np.ndarray          # [B, Hq, Nq, D]   float16 or uint16 (bf16 bits)
+    k: np.ndarray          # [B, Hkv, Nkv, D]
+    v: np.ndarray          # [B, Hkv, Nkv, D]
+    dtype: str
+    seed: int
+    k_offset: np.ndarray | None = None   # float32 [D], already folded into k
+    rows: np.ndarray | None = None       # int64 [Hq, R] sampled query rows
+
+
+def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
+                dtype: str, seed: int = 0, k_offset_std: float | None = None,
+                sampled_rows: int | None = None) -> Inputs:
+    """Draw q, k, v iid N(0,1) (float32), in that order, from PCG64(seed).
+
+    With ``k_offset_std`` a per-channel offset c = std*z, z ~ N(0,1) of shape
+    [D], is drawn next and added to every key row in float32 before rounding.
+    With ``sampled_rows`` = R, each query head then draws R-2 distinct interior
+    rows (rows 0 and Nq-1 are always included), sorted.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, Hq, Nq, D), dtype=np.float32)
+    qs = to_storage(q, dtype)
+    del q
+    k = rng.standard_normal((B, Hkv, Nkv, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Nkv, D), dtype=np.float32)
+    off = None
+    if k_offset_std is not None:
+        off = (np.float32(k_offset_std)
+               * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
+        k += off
+    ks = to_storage(k, dtype)
+    del k
+    vs = to_storage(v, dtype)
+    del v
+    rows = None
+    if sampled_rows is not None:
+        rows = sample_rows(rng, Hq, Nq, sampled_rows)
+    return Inputs(q=qs, k=ks, v=vs, dtype=dtype, seed=seed, k_offset=off,
+                  rows=rows)
+
+
+def sample_rows(rng: np.random.Generator, Hq: int, Nq: int, R: int) -> np.ndarray:
+    """Per head: rows 0 and Nq-1 plus R-2 distinct interior rows, sorted."""
+    if Nq <= R:
+        return np.tile(np.arange(Nq, dtype=np.int64), (Hq, 1))
+    out = np.empty((Hq, R), dtype=np.int64)
+    for h in range(Hq):
+        mid = rng.choice(Nq - 2, R - 2, replace=False) + 1
+        out[h] = np.sort(np.concatenate([[0, Nq - 1], mid]))
+    return out
+
+
+def make_workload_inputs(w: Workload, seed: int = 0,
+                         sampled_rows: int | None = None) -> Inputs:
+    R = sampled_rows if sampled_rows is not None else w.sampled_rows
+    return make_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, seed=seed,
+                       k_offset_std=w.k_offset_std, sampled_rows=R)

@@ -1,0 +1,9 @@
+"""CPU oracle (float64) for the attention forward -- test infrastructure only.
+
+Only tests, the smoke check and the bench's CPU-baseline leg may use it.
+"""
+from .softmax_attention import (attention, attention_from_storage,
+                        decode, decode_bf16, decode_f16, scale_value)
+
+__all__ = ["attention", "attention_from_storage",
+           "decode", "decode_bf16", "decode_f16", "scale_value"]

@@ -1,0 +1,137 @@
+"""CPU oracle for scaled-dot-product attention forward (float64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the bench's CPU
+baseline leg use it.  It shares no code with the HIP library.
+
+What it computes
+----------------
+The English noflash-attention post (ai-navigate-news.com, section "The DIY
+approach") describes its tiled attention as the same mathematics as full
+attention: a query chunk's scores against all keys, a softmax over each row,
+and a product with V, with the rows of all chunks put together.  Tiling over
+keys with a running max and running sum (the post's "online softmax" tier in
+the same section) changes the evaluation order only.  The result of the
+method is therefore exactly softmax attention, and this oracle is that
+definition written out, one query row at a time, in float64:
+
+    s_ij   = scale * <q_i, k_j>                      for j in J_i
+    lse_i  = ln sum_{j in J_i} exp(s_ij)             (natural log)
+    o_i    = sum_{j in J_i} exp(s_ij - lse_i) * v_j
+
+evaluated with the row maximum subtracted before exponentiating (the
+max-subtraction also appears in the chunked snippet of the ai-manual.ru
+article, section 3 "Self-written memory-efficient attention").
+
+Readings where the pages are silent (listed again in the design notes):
+  * J_i = all keys, or with ``causal`` the keys j <= i (top-left alignment,
+    as PyTorch's scaled_dot_product_attention applies is_causal);
+  * query head hq reads KV head hq // (Hq // Hkv): the post's "flattened GQA"
+    groups consecutive query heads on one KV head (section "The DIY
+    approach");
+  * scale defaults to 1/sqrt(D) (the ai-manual.ru snippet divides by
+    sqrt(dim)); it is used as the float32 value the GPU receives;
+  * no epsilon in the denominator (the ai-manual.ru snippet adds 1e-8; after
+    max subtraction the row sum is >= 1, so it is left out) and no flush-to-
+    zero threshold (the post's fp16 workaround): the oracle is exact.
+
+Rows are processed in groups of query rows purely to bound memory; the
+arithmetic of each row is untouched by the grouping.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Decoding the 16-bit inputs exactly into float64.
+# ---------------------------------------------------------------------------
+
+
+def decode_f16(a: np.ndarray) -> np.ndarray:
+    """IEEE binary16 values -> float64 (exact)."""
+    return np.asarray(a, dtype=np.float16).astype(np.float64)
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64 (exact).
+
+    A bfloat16 is the upper half of an IEEE binary32, so the bits shifted
+    left by 16 are the binary32 encoding of the same value.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return decode_f16(a)
+    if dtype == "bf16":
+        return decode_bf16(a)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def scale_value(scale: float | None, D: int) -> float:
+    """The softmax scale as the float32 the kernel is given, in float64."""
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    return float(np.float32(s))
+
+
+# ---------------------------------------------------------------------------
+# The definition.
+# ---------------------------------------------------------------------------
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+              causal: bool, rows: np.ndarray | None = None,
+              row_group: int = 256) -> tuple[np.ndarray, np.ndarray]:
+    """Exact softmax attention in float64.
+
+    q: [B, Hq, Nq, D], k and v: [B, Hkv, Nkv, D], all float64.
+    rows: None (all Nq rows) or int array [Hq, R] or [R] of query rows.
+    Returns (o [B, Hq, R, D], lse [B, Hq, R]) in float64, natural log.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nkv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k and v")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if rows is None:
+        rows_h = np.tile(np.arange(Nq, dtype=np.int64), (Hq, 1))
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        rows_h = np.tile(rows, (Hq, 1)) if rows.ndim == 1 else rows
+    R = rows_h.shape[1]
+    o = np.empty((B, Hq, R, D), dtype=np.float64)
+    lse = np.empty((B, Hq, R), dtype=np.float64)
+    key_idx = np.arange(Nkv, dtype=np.int64)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G                      # consecutive query heads share a KV head
+            kk = k[b, hk]
+            vv = v[b, hk]
+            for r0 in range(0, R, row_group):
+                ri = rows_h[hq, r0:r0 + row_group]
+                s = scale * (q[b, hq, ri] @ kk.T)            # [r, Nkv]
+                if causal:
+                    s = np.where(key_idx[None, :] <= ri[:, None], s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                denom = e.sum(axis=1, keepdims=True)
+                o[b, hq, r0:r0 + len(ri)] = (e @ vv) / denom
+                lse[b, hq, r0:r0 + len(ri)] = (m + np.log(denom))[:, 0]
+    return o, lse
+
+
+def attention_from_storage(q, k, v, dtype: str, scale: float | None,
+                           causal: bool, rows=None):
+    """Decode 16-bit storage arrays, then evaluate :func:`attention`."""
+    D = q.shape[-1]
+    return attention(decode(q, dtype), decode(k, dtype), decode(v, dtype),
+                     scale_value(scale, D), causal, rows=rows)

@@ -1,0 +1,327 @@
+"""Pins for the CPU oracle: facts fixed by mathematics, not by the oracle.
+
+Every pin takes an ``attn(q, k, v, scale, causal, rows=None) -> (o, lse)``
+callable (float64 arrays, q [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D]) and raises
+AssertionError when the callable disagrees.  ``test_oracle.py`` runs them on
+the oracle; its mutation test runs them on copies of the oracle with a
+planted mistake and requires each mistake to be caught.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from decimal import Decimal, localcontext
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+TOL = 1e-12
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max rel err {err:.3e} > {tol:.1e}"
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _dyadic(rng, shape, denom=8, lim=16):
+    """Small random multiples of 1/denom: exact in binary floating point."""
+    return rng.integers(-lim, lim + 1, size=shape).astype(np.float64) / denom
+
+
+# ---------------------------------------------------------------------------
+# 1. High-precision brute force (exact rational scores, 40-digit exp/log).
+# ---------------------------------------------------------------------------
+
+def _bruteforce(q, k, v, scale, causal):
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, Nq, D))
+    lse = np.zeros((B, Hq, Nq))
+    sc = Fraction(scale)
+    with localcontext() as ctx:
+        ctx.prec = 40
+        for b in range(B):
+            for h in range(Hq):
+                kh = h // G
+                for i in range(Nq):
+                    keys = [j for j in range(Nkv) if (not causal) or j <= i]
+                    ex = []
+                    for j in keys:
+                        s = sc * sum(Fraction(float(q[b, h, i, d])) *
+                                     Fraction(float(k[b, kh, j, d])) for d in range(D))
+                        ex.append((Decimal(s.numerator) / Decimal(s.denominator)).exp())
+                    total = sum(ex, Decimal(0))
+                    lse[b, h, i] = float(total.ln())
+                    for d in range(D):
+                        acc = sum((e * Decimal(float(v[b, kh, j, d]))
+                                   for e, j in zip(ex, keys)), Decimal(0))
+                        o[b, h, i, d] = float(acc / total)
+    return o, lse
+
+
+def pin_bruteforce(attn):
+    cases = [
+        # B, Hq, Hkv, Nq, Nkv, D, causal, scale
+        (1, 1, 1, 1, 1, 1, False, 0.5),
+        (1, 2, 1, 5, 6, 3, False, 0.7),
+        (1, 2, 1, 5, 6, 3, True, 0.7),
+        (2, 3, 3, 4, 4, 2, True, 1.25),
+        (1, 4, 2, 7, 3, 2, True, 0.375),
+        (1, 2, 2, 3, 8, 4, False, 2.0),
+    ]
+    rng = _rng(11)
+    for B, Hq, Hkv, Nq, Nkv, D, causal, scale in cases:
+        q = _dyadic(rng, (B, Hq, Nq, D))
+        k = _dyadic(rng, (B, Hkv, Nkv, D))
+        v = _dyadic(rng, (B, Hkv, Nkv, D))
+        o_ref, l_ref = _bruteforce(q, k, v, scale, causal)
+        o, l = attn(q, k, v, scale, causal)
+        _close(o, o_ref, what=f"bruteforce o {B,Hq,Hkv,Nq,Nkv,D,causal}")
+        _close(l, l_ref, what=f"bruteforce lse {B,Hq,Hkv,Nq,Nkv,D,causal}")
+
+
+# ---------------------------------------------------------------------------
+# 2. An independent library implementation (PyTorch's CPU SDPA, float64).
+# ---------------------------------------------------------------------------
+
+def pin_torch_sdpa(attn):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(12)
+    cases = [
+        (1, 4, 4, 33, 33, 16, False),
+        (2, 6, 2, 40, 40, 8, True),
+        (1, 7, 1, 17, 29, 8, True),     # Nq < Nkv, top-left causal
+        (1, 4, 2, 29, 17, 8, True),     # Nq > Nkv
+        (1, 2, 1, 9, 70, 32, False),
+    ]
+    for B, Hq, Hkv, Nq, Nkv, D, causal in cases:
+        q = rng.standard_normal((B, Hq, Nq, D))
+        k = rng.standard_normal((B, Hkv, Nkv, D))
+        v = rng.standard_normal((B, Hkv, Nkv, D))
+        scale = 1.0 / math.sqrt(D)
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            is_causal=causal, scale=scale, enable_gqa=(Hq != Hkv)).numpy()
+        o, _ = attn(q, k, v, scale, causal)
+        _close(o, ref, tol=1e-11, what=f"torch sdpa {B,Hq,Hkv,Nq,Nkv,D,causal}")
+
+
+# ---------------------------------------------------------------------------
+# 3. Hand-derived worked examples (tests/golden).
+# ---------------------------------------------------------------------------
+
+def _eval_expr(expr):
+    return float(eval(expr, {"__builtins__": {}},
+                      {"e": math.e, "log": math.log, "exp": math.exp}))
+
+
+def pin_golden(attn):
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    for case in data["cases"]:
+        q = np.array(case["q"], dtype=np.float64)[None, None]
+        k = np.array(case["k"], dtype=np.float64)[None, None]
+        v = np.array(case["v"], dtype=np.float64)[None, None]
+        o, lse = attn(q, k, v, case["scale"], case["causal"])
+        eo = np.array([[_eval_expr(x) for x in row] for row in case["expected_o"]])
+        el = np.array([_eval_expr(x) for x in case["expected_lse"]])
+        _close(o[0, 0], eo, what=f"golden {case['name']} o")
+        _close(lse[0, 0], el, what=f"golden {case['name']} lse")
+
+
+# ---------------------------------------------------------------------------
+# 4. Closed forms and special cases.
+# ---------------------------------------------------------------------------
+
+def pin_q_zero(attn):
+    """Q = 0: every allowed key has the same score, so o is the mean of the
+    allowed V rows and lse = ln(number of allowed keys)."""
+    rng = _rng(13)
+    for causal in (False, True):
+        B, Hq, Hkv, Nq, Nkv, D = 1, 4, 2, 12, 10, 8
+        q = np.zeros((B, Hq, Nq, D))
+        k = rng.standard_normal((B, Hkv, Nkv, D))
+        v = rng.standard_normal((B, Hkv, Nkv, D))
+        o, lse = attn(q, k, v, 0.3, causal)
+        for h in range(Hq):
+            kh = h // (Hq // Hkv)
+            for i in range(Nq):
+                n = min(i + 1, Nkv) if causal else Nkv
+                _close(o[0, h, i], v[0, kh, :n].mean(axis=0), what="q=0 o")
+                _close(lse[0, h, i], math.log(n), what="q=0 lse")
+
+
+def pin_v_const(attn):
+    rng = _rng(14)
+    for causal in (False, True):
+        B, Hq, Hkv, Nq, Nkv, D = 2, 3, 1, 9, 9, 5
+        q = rng.standard_normal((B, Hq, Nq, D)) * 3
+        k = rng.standard_normal((B, Hkv, Nkv, D)) * 3
+        c = rng.standard_normal(D)
+        v = np.broadcast_to(c, (B, Hkv, Nkv, D)).copy()
+        o, _ = attn(q, k, v, 0.5, causal)
+        _close(o, np.broadcast_to(c, o.shape), what="v const")
+
+
+def pin_causal_row0(attn):
+    """Causal row 0 sees key 0 only: o_0 = v_0, lse_0 = scale*q_0.k_0."""
+    rng = _rng(15)
+    B, Hq, Hkv, N, D = 2, 4, 2, 6, 4
+    q = rng.standard_normal((B, Hq, N, D))
+    k = rng.standard_normal((B, Hkv, N, D))
+    v = rng.standard_normal((B, Hkv, N, D))
+    o, lse = attn(q, k, v, 0.9, True)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // 2
+            _close(o[b, h, 0], v[b, kh, 0], what="causal row 0 o")
+            _close(lse[b, h, 0], 0.9 * float(q[b, h, 0] @ k[b, kh, 0]),
+                   what="causal row 0 lse")
+
+
+def pin_single_key(attn):
+    rng = _rng(16)
+    q = rng.standard_normal((1, 2, 5, 3))
+    k = rng.standard_normal((1, 2, 1, 3))
+    v = rng.standard_normal((1, 2, 1, 3))
+    o, lse = attn(q, k, v, 0.8, False)
+    for h in range(2):
+        _close(o[0, h], np.broadcast_to(v[0, h, 0], (5, 3)), what="Nkv=1 o")
+        _close(lse[0, h], 0.8 * (q[0, h] @ k[0, h, 0]), what="Nkv=1 lse")
+
+
+def pin_dominant_key(attn):
+    """q_i = k_j* = a*u with a large: softmax mass concentrates on j*."""
+    rng = _rng(17)
+    Nkv, D = 16, 8
+    k = rng.standard_normal((1, 1, Nkv, D)) * 0.1
+    v = rng.standard_normal((1, 1, Nkv, D))
+    u = np.zeros(D)
+    u[3] = 1.0
+    js = 5
+    k[0, 0, js] = 12.0 * u
+    q = (12.0 * u)[None, None, None, :]
+    o, lse = attn(q, k, v, 1.0, False)
+    # every other score is at most 12*max|k_j[3]| < 12*0.5, so the gap is > 70
+    _close(o[0, 0, 0], v[0, 0, js], tol=1e-20 + 1e-12, what="dominant key o")
+    _close(lse[0, 0, 0], 144.0, what="dominant key lse")
+
+
+# ---------------------------------------------------------------------------
+# 5. Invariants.
+# ---------------------------------------------------------------------------
+
+def pin_key_shift(attn):
+    """K_j += c for every j shifts each score of row i by scale*q_i.c:
+    o unchanged, lse_i += scale*q_i.c."""
+    rng = _rng(18)
+    for causal in (False, True):
+        q = rng.standard_normal((1, 2, 7, 6))
+        k = rng.standard_normal((1, 2, 9, 6))
+        v = rng.standard_normal((1, 2, 9, 6))
+        c = rng.standard_normal(6)
+        o1, l1 = attn(q, k, v, 0.4, causal)
+        o2, l2 = attn(q, k + c, v, 0.4, causal)
+        _close(o2, o1, tol=1e-11, what="key shift o")
+        _close(l2, l1 + 0.4 * (q @ c), tol=1e-11, what="key shift lse")
+
+
+def pin_kv_permutation(attn):
+    rng = _rng(19)
+    q = rng.standard_normal((1, 2, 5, 4))
+    k = rng.standard_normal((1, 1, 11, 4))
+    v = rng.standard_normal((1, 1, 11, 4))
+    p = rng.permutation(11)
+    o1, l1 = attn(q, k, v, 0.6, False)
+    o2, l2 = attn(q, k[:, :, p], v[:, :, p], 0.6, False)
+    _close(o2, o1, tol=1e-11, what="kv permutation o")
+    _close(l2, l1, tol=1e-11, what="kv permutation lse")
+
+
+def pin_query_permutation(attn):
+    rng = _rng(20)
+    q = rng.standard_normal((1, 3, 8, 4))
+    k = rng.standard_normal((1, 3, 6, 4))
+    v = rng.standard_normal((1, 3, 6, 4))
+    p = rng.permutation(8)
+    o1, l1 = attn(q, k, v, 0.6, False)
+    o2, l2 = attn(q[:, :, p], k, v, 0.6, False)
+    _close(o2, o1[:, :, p], what="query permutation o")
+    _close(l2, l1[:, :, p], what="query permutation lse")
+
+
+def pin_gqa_repeat(attn):
+    """GQA equals MHA with each KV head repeated for its G query heads."""
+    rng = _rng(21)
+    for causal in (False, True):
+        B, Hq, Hkv, N, D = 2, 6, 2, 7, 4
+        q = rng.standard_normal((B, Hq, N, D))
+        k = rng.standard_normal((B, Hkv, N, D))
+        v = rng.standard_normal((B, Hkv, N, D))
+        G = Hq // Hkv
+        o1, l1 = attn(q, k, v, 0.5, causal)
+        o2, l2 = attn(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.5, causal)
+        _close(o1, o2, what="gqa o")
+        _close(l1, l2, what="gqa lse")
+
+
+def pin_linear_in_v(attn):
+    rng = _rng(22)
+    q = rng.standard_normal((1, 2, 6, 4))
+    k = rng.standard_normal((1, 2, 6, 4))
+    v1 = rng.standard_normal((1, 2, 6, 4))
+    v2 = rng.standard_normal((1, 2, 6, 4))
+    for causal in (False, True):
+        oa, _ = attn(q, k, v1, 0.7, causal)
+        ob, _ = attn(q, k, v2, 0.7, causal)
+        oc, _ = attn(q, k, 2.0 * v1 - 3.0 * v2, 0.7, causal)
+        _close(oc, 2.0 * oa - 3.0 * ob, tol=1e-11, what="linearity in v")
+
+
+def pin_convex_hull(attn):
+    rng = _rng(23)
+    q = rng.standard_normal((1, 2, 9, 4)) * 2
+    k = rng.standard_normal((1, 2, 9, 4)) * 2
+    v = rng.standard_normal((1, 2, 9, 4))
+    for causal in (False, True):
+        o, _ = attn(q, k, v, 1.0, causal)
+        for h in range(2):
+            for i in range(9):
+                n = i + 1 if causal else 9
+                lo = v[0, h, :n].min(axis=0) - 1e-12
+                hi = v[0, h, :n].max(axis=0) + 1e-12
+                assert np.all(o[0, h, i] >= lo) and np.all(o[0, h, i] <= hi), \
+                    "convex hull violated"
+
+
+def pin_rows_subset(attn):
+    """Selecting query rows returns exactly those rows of the full result."""
+    rng = _rng(24)
+    for causal in (False, True):
+        q = rng.standard_normal((1, 2, 20, 4))
+        k = rng.standard_normal((1, 1, 20, 4))
+        v = rng.standard_normal((1, 1, 20, 4))
+        rows = np.array([[0, 3, 19], [1, 7, 12]])
+        of, lf = attn(q, k, v, 0.5, causal)
+        os_, ls = attn(q, k, v, 0.5, causal, rows=rows)
+        for h in range(2):
+            _close(os_[0, h], of[0, h, rows[h]], what="rows subset o")
+            _close(ls[0, h], lf[0, h, rows[h]], what="rows subset lse")
+
+
+ALL_PINS = [pin_bruteforce, pin_torch_sdpa, pin_golden, pin_q_zero, pin_v_const,
+            pin_causal_row0, pin_single_key, pin_dominant_key, pin_key_shift,
+            pin_kv_permutation, pin_query_permutation, pin_gqa_repeat,
+            pin_linear_in_v, pin_convex_hull, pin_rows_subset]

@@ -1,0 +1,134 @@
+"""CPU tests: the oracle against its pins, plus the input generator.
+
+The pins (tests/oracle_pins.py) come from exact arithmetic, closed forms,
+invariants and an independent library implementation -- never from the
+oracle itself.  The mutation test plants plausible mistakes in copies of
+the oracle (on the CPU) and requires every one to be caught by some pin.
+"""
+import inspect
+import math
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.softmax_attention as oracle_mod
+from memory_efficient_tiled_amd import inputs
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle.attention)
+
+
+# (description, original text, replacement) -- each a mistake a reader might make
+MUTANTS = [
+    ("dropped scale", "s = scale * (q[b, hq, ri] @ kk.T)", "s = (q[b, hq, ri] @ kk.T)"),
+    ("wrong exponent sign", "e = np.exp(s - m)", "e = np.exp(m - s)"),
+    ("gqa modulo mapping", "hk = hq // G", "hk = hq % Hkv"),
+    ("k and v swapped", "kk = k[b, hk]\n            vv = v[b, hk]",
+     "kk = v[b, hk]\n            vv = k[b, hk]"),
+    ("causal strict (off by one)", "key_idx[None, :] <= ri[:, None]",
+     "key_idx[None, :] < ri[:, None]"),
+    ("causal one key too many", "key_idx[None, :] <= ri[:, None]",
+     "key_idx[None, :] <= ri[:, None] + 1"),
+    ("causal uses position in group", "key_idx[None, :] <= ri[:, None]",
+     "key_idx[None, :] <= np.arange(len(ri))[:, None]"),
+    ("lse in base 2", "(m + np.log(denom))", "(m + np.log2(denom))"),
+    ("lse drops the max", "(m + np.log(denom))", "(0 * m + np.log(denom))"),
+    ("missing normalisation", "(e @ vv) / denom", "(e @ vv)"),
+    ("keys read in reverse", "q[b, hq, ri] @ kk.T", "q[b, hq, ri] @ kk[::-1].T"),
+]
+
+
+def _mutant(original, replacement):
+    src = inspect.getsource(oracle_mod)
+    assert original in src, f"mutation anchor not found: {original!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(original, replacement), "<oracle mutant>", "exec"),
+         mod.__dict__)
+    return mod.attention
+
+
+@pytest.mark.parametrize("name,original,replacement", MUTANTS,
+                         ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, original, replacement):
+    attn = _mutant(original, replacement)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(attn)
+        except Exception:   # AssertionError, or a crash on NaN/shape errors
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake: {name}"
+
+
+def test_decode_bf16_known_patterns():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x7F80, 0x0001,
+                     0x7F7F], dtype=np.uint16)
+    want = [1.0, -1.0, 3.140625, 0.0, -0.0, math.inf, 2.0 ** -133,
+            (2 - 2 ** -7) * 2.0 ** 127]
+    got = oracle.decode_bf16(bits)
+    assert list(got) == want
+
+
+def test_decode_f16_known_patterns():
+    a = np.array([0x3C00, 0xC000, 0x0001, 0x7BFF], dtype=np.uint16).view(np.float16)
+    assert list(oracle.decode_f16(a)) == [1.0, -2.0, 2.0 ** -24, 65504.0]
+
+
+def test_scale_value_is_float32():
+    assert oracle.scale_value(None, 64) == 0.125
+    assert oracle.scale_value(None, 128) == float(np.float32(1 / math.sqrt(128)))
+    assert oracle.scale_value(None, 128) != 1 / math.sqrt(128)
+
+
+def test_generator_bf16_rounding_matches_torch():
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = rng.standard_normal(100_000, dtype=np.float32)
+    # exact ties: low 16 bits equal to 0x8000, both parities of bit 16
+    ties = (rng.integers(0x3F00, 0x4100, 1000).astype(np.uint32) << 16) | 0x8000
+    x = np.concatenate([x, ties.view(np.float32), -ties.view(np.float32)])
+    ours = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_generator_is_seeded_and_ordered():
+    a = inputs.make_inputs(1, 2, 1, 5, 6, 8, "f16", seed=3)
+    b = inputs.make_inputs(1, 2, 1, 5, 6, 8, "f16", seed=3)
+    c = inputs.make_inputs(1, 2, 1, 5, 6, 8, "f16", seed=4)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.v, b.v)
+    assert not np.array_equal(a.q, c.q)
+    rng = np.random.Generator(np.random.PCG64(3))
+    q = rng.standard_normal((1, 2, 5, 8), dtype=np.float32)
+    assert np.array_equal(a.q, q.astype(np.float16))
+    assert a.q.shape == (1, 2, 5, 8) and a.k.shape == (1, 1, 6, 8)
+
+
+def test_generator_key_offset_and_rows():
+    w = inputs.make_inputs(1, 3, 3, 50, 50, 8, "bf16", seed=1, k_offset_std=0.5,
+                           sampled_rows=10)
+    assert w.k_offset.shape == (8,) and w.k.dtype == np.uint16
+    assert w.rows.shape == (3, 10)
+    for r in w.rows:
+        assert r[0] == 0 and r[-1] == 49 and len(set(r.tolist())) == 10
+    # the offset is constant over keys: the mean key moves by about the offset
+    kmean = oracle.decode_bf16(w.k).mean(axis=(0, 1, 2))
+    assert np.allclose(kmean, w.k_offset, atol=0.5)
+
+
+def test_workload_table():
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    assert (w.B, w.Hq, w.Hkv, w.Nq, w.D, w.dtype, w.causal) == \
+        (1, 24, 24, 17160, 128, "bf16", False)
+    assert w.flops == 4.0 * 24 * 17160 ** 2 * 128
+    assert inputs.WORKLOADS["gqa-causal-4096"].flops == 2.0 * 14 * 4096 ** 2 * 64
+    # the score matrix the tiled method avoids: 24 heads x N^2 x 4 bytes is
+    # the 26 GB quoted for 17K tokens and >500 GB for 75K tokens
+    assert abs(24 * 17160 ** 2 * 4 / 2 ** 30 - 26.3) < 0.1
+    assert 24 * 75600 ** 2 * 4 > 500e9
