@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Attention-forward throughput on one MI355X.
+
+One step = one attention forward (every kernel of the path) over the
+workload's synthetic inputs, already resident in HBM.  Prints one JSON line:
+TFLOP/s (4*B*Hq*Nq*Nkv*D, halved when causal), the fraction of the dense
+bf16/fp16 MFMA peak, a parity check of sampled rows against the CPU oracle,
+and that oracle's own throughput on the same rows (a reported baseline).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+SOURCE = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc", "attn_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    with open(SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"attn_fwd_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    t = re.search(r"hbm bytes per launch:\s*`?([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != source_hash():
+        return None
+    return float(t.group(1))
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0, help="0 = library choice")
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="query rows per head for the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this attention forward runs on one GPU; --gpus "
+              f"{args.gpus} is not supported (sharding over heads is described "
+              "in the design notes, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from memory_efficient_tiled_amd import attn_fwd, attn_fwd_num_splits, inputs
+    from memory_efficient_tiled_amd.binding import ATTN_BF16, ATTN_F16
+
+    name = args.workload or inputs.HEADLINE
+    w = inputs.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    progress(f"workload {name}: {w.describe()}; generating inputs")
+    want_cpu = not args.no_cpu_baseline
+    x = inputs.make_workload_inputs(w, seed=args.seed,
+                                    sampled_rows=args.cpu_rows if want_cpu else None)
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if w.dtype == "bf16"
+                             else np.ascontiguousarray(a))
+        t = t.to(dev)
+        return t.view(torch.bfloat16) if w.dtype == "bf16" else t
+
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    dcode = ATTN_BF16 if w.dtype == "bf16" else ATTN_F16
+    splits = args.splits or attn_fwd_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                                                w.causal, dcode)
+    progress(f"inputs on {torch.cuda.get_device_name(dev)}; split-KV count {splits}; "
+             f"warmup {args.warmup}")
+
+    def step():
+        attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse,
+                 num_splits=args.splits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    progress(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[w.dtype]
+    progress(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); "
+             f"wall {wall:.3f} s")
+
+    traffic = measured_traffic(name)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                "traffic": traffic}
+
+    result = {
+        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak "
+                  "(B=1,H=24,D=128,N=17K)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "pct_of_mfma_peak": round(100 * tflops / peak, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{name}: {w.note}, {w.describe()}",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv,
+                   "D": w.D, "causal": w.causal, "scale": w.scale, "seed": args.seed,
+                   "k_offset_std": w.k_offset_std, "split_kv": splits,
+                   "kernel_source": source_hash()},
+        "roofline": roofline,
+    }
+
+    if want_cpu:
+        import oracle
+        from tests.parity import gather_rows
+        progress(f"oracle on {x.rows.shape[1]} rows x {w.Hq} heads")
+        o_gpu = out.float().cpu().numpy().astype(np.float64)
+        l_gpu = lse.cpu().numpy().astype(np.float64)
+        sc = oracle.scale_value(w.scale, w.D)
+        G = w.Hq // w.Hkv
+        c0 = time.perf_counter()
+        o_ref = np.empty((w.B, w.Hq, x.rows.shape[1], w.D))
+        l_ref = np.empty((w.B, w.Hq, x.rows.shape[1]))
+        for b in range(w.B):
+            for hk in range(w.Hkv):
+                kh = oracle.decode(x.k[b:b + 1, hk:hk + 1], w.dtype)
+                vh = oracle.decode(x.v[b:b + 1, hk:hk + 1], w.dtype)
+                for g in range(G):
+                    h = hk * G + g
+                    qh = oracle.decode(x.q[b:b + 1, h:h + 1], w.dtype)
+                    oh, lh = oracle.attention(qh, kh, vh, sc, w.causal, rows=x.rows[h])
+                    o_ref[b, h], l_ref[b, h] = oh[0, 0], lh[0, 0]
+        cpu_s = time.perf_counter() - c0
+        rows = x.rows
+        if w.causal:
+            sample_flops = float(sum(4.0 * w.D * np.minimum(r + 1, w.Nkv).sum()
+                                     for r in rows)) * w.B
+        else:
+            sample_flops = 4.0 * w.D * w.Nkv * rows.size * w.B
+        o_s, l_s = gather_rows(o_gpu, rows), gather_rows(l_gpu, rows)
+        err = np.abs(o_s - o_ref)
+        result["parity"] = {"rows_per_head": int(rows.shape[1]),
+                            "max_abs_err": float(err.max()),
+                            "mean_abs_err": float(err.mean()),
+                            "lse_max_abs_err": float(np.abs(l_s - l_ref).max()),
+                            "pass": bool(err.max() <= 4e-3 and err.mean() <= 5e-4 and
+                                         np.abs(l_s - l_ref).max() <= 1e-3)}
+        result["cpu_baseline"] = {
+            "value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{rows.shape[1]} query rows per head x {w.Hq} heads of {name} "
+                      f"({sample_flops / 1e9:.1f} GFLOP algorithmic, {cpu_s:.1f} s, "
+                      f"float64 numpy, {cpu_model()})"}
+        progress(f"oracle {cpu_s:.1f} s; parity {result['parity']}")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,125 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) memory-efficient attention forward.
+ *
+ * The operation is the one the English noflash-attention post
+ * (ai-navigate-news.com, section "The DIY approach") tiles over query chunks
+ * and, in its online-softmax tier, over key tiles with a running max and
+ * running sum: exact softmax attention,
+ *
+ *     O[b,h,i,:] = sum_{j in J_i} softmax_j(scale * <Q[b,h,i,:], K[b,g(h),j,:]>) V[b,g(h),j,:]
+ *     LSE[b,h,i] = ln sum_{j in J_i} exp(scale * <Q[b,h,i,:], K[b,g(h),j,:]>)
+ *
+ * without ever forming the Nq x Nkv score matrix.  g(h) = h / (Hq / Hkv): the
+ * post's flattened GQA groups consecutive query heads on one KV head.  J_i is
+ * every key, or with `causal` the keys j <= i (top-left alignment, the
+ * semantics of PyTorch's scaled_dot_product_attention is_causal, which is the
+ * API the post patches; section "Other areas where this could be useful").
+ *
+ * Layout (all tensors): contiguous [batch, heads, seq_len, head_dim], the
+ * head dimension fastest -- the layout the ai-manual.ru article's chunked
+ * snippet unpacks (section 3).  Q is [B,Hq,Nq,D], K and V are [B,Hkv,Nkv,D],
+ * `out` is [B,Hq,Nq,D] in the input dtype, `lse` is float32 [B,Hq,Nq].
+ * Inputs are fp16 or bf16; all arithmetic accumulates in fp32.
+ *
+ * Pointers are device pointers on the current HIP device unless stated.
+ * The caller owns every buffer; the library keeps no pointer after return.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream): results are valid when the stream has reached the call.
+ *
+ * Errors: every entry point returns ATTN_OK (0) or a negative code.  Argument
+ * errors are detected on the host before any HIP call.  There is no fallback
+ * path: on error nothing has been launched (ATTN_EINVAL, ATTN_EUNSUPPORTED,
+ * ATTN_ENOMEM) or a launch failed (ATTN_EHIP; attn_last_hip_error() gives the
+ * hipError_t).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,       /* bad argument (shape, pointer, alignment, dtype, scale) */
+  ATTN_EUNSUPPORTED = -2, /* the current device is not gfx950 */
+  ATTN_ENOMEM = -3,       /* split-KV workspace could not be allocated */
+  ATTN_EHIP = -4          /* a HIP call or kernel launch failed */
+};
+
+/*
+ * attn_fwd -- O and LSE of exact softmax attention (definition above).
+ *
+ * q, k, v : device pointers, fp16/bf16 per `dtype`, 16-byte aligned.
+ * out     : device pointer, [B,Hq,Nq,D], same dtype; must not overlap q/k/v.
+ * lse     : device pointer to float32 [B,Hq,Nq] (natural log), or NULL to
+ *           skip writing it.
+ * B, Hq, Hkv, Nq, Nkv : > 0, Hq a multiple of Hkv.
+ * D       : 64 or 128.
+ * scale   : finite softmax scale (PyTorch's default is 1/sqrt(D); the
+ *           ai-manual.ru snippet divides scores by sqrt(dim)).
+ * causal  : 0 = every key, 1 = keys j <= i (top-left).
+ * dtype   : ATTN_F16 or ATTN_BF16.
+ * stream  : hipStream_t to launch on.
+ *
+ * Short query ranges over long key ranges are split over key ranges
+ * (split-KV); the partial results are merged by their log-sum-exp.  The
+ * split path takes a workspace of attn_fwd_workspace_bytes() bytes with
+ * hipMallocAsync/hipFreeAsync on `stream`; with one split nothing is
+ * allocated.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+             float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_fwd_split -- attn_fwd with the split-KV count chosen by the caller.
+ * num_splits = 0 picks it as attn_fwd does; a positive value is clamped to
+ * the number of key tiles.  Every split count computes the same function;
+ * results differ only by fp32 rounding order.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* out,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                   float scale, int causal, int dtype, int num_splits,
+                   void* stream);
+
+/*
+ * attn_fwd_check -- the argument validation of attn_fwd, host only: makes no
+ * HIP call and dereferences no pointer.  Returns ATTN_OK or ATTN_EINVAL.
+ */
+int attn_fwd_check(const void* q, const void* k, const void* v, const void* out,
+                   const float* lse, int B, int Hq, int Hkv, int Nq, int Nkv,
+                   int D, float scale, int causal, int dtype);
+
+/*
+ * attn_fwd_num_splits -- host only: the split-KV count attn_fwd would use
+ * for this shape on a device with `num_cus` compute units (256 on MI355X).
+ * Returns >= 1, or ATTN_EINVAL for invalid shapes.
+ */
+int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                        int causal, int dtype, int num_cus);
+
+/*
+ * attn_fwd_workspace_bytes -- host only: device bytes the split path
+ * allocates for `num_splits` splits (0 when num_splits <= 1): fp32 partial
+ * outputs [num_splits,B,Hq,Nq,D] and partial LSE [num_splits,B,Hq,Nq].
+ */
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
+                                int num_splits);
+
+/* attn_strerror -- static description of a return code (never NULL). */
+const char* attn_strerror(int code);
+
+/* attn_last_hip_error -- the hipError_t behind the calling thread's last
+ * ATTN_EHIP / ATTN_ENOMEM / ATTN_EUNSUPPORTED, 0 if none. */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,125 @@
+"""Shared helpers for the GPU parity tests: upload, run, oracle, compare.
+
+Inputs come from the seeded generator; expected values come from the CPU
+oracle only.  The GPU result is read back as its exact 16-bit values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+
+import oracle
+from memory_efficient_tiled_amd import attn_fwd, inputs
+
+# Tolerances for the named workloads, on outputs and on the log-sum-exp.
+MAX_ERR = 4e-3
+MEAN_ERR = 5e-4
+LSE_ERR = 1e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(a: np.ndarray, dtype: str, device):
+    import torch
+    if dtype == inputs.F16:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device) \
+        .view(torch.bfloat16)
+
+
+def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of the output type at |x|: the error that
+    rounding the exact result to the output type alone can cause."""
+    mant = 10 if dtype == inputs.F16 else 7
+    ax = np.maximum(np.abs(x), 2.0 ** -14)
+    return 0.5 * 2.0 ** (np.floor(np.log2(ax)) - mant)
+
+
+@dataclasses.dataclass
+class Result:
+    max_err: float
+    mean_err: float
+    lse_err: float
+    n: int
+
+
+def oracle_rows(x: inputs.Inputs, scale, causal, rows=None):
+    """Oracle output for all rows, or for rows [Hq, R], one head at a time."""
+    B, Hq, Nq, D = x.q.shape
+    Hkv = x.k.shape[1]
+    G = Hq // Hkv
+    R = Nq if rows is None else rows.shape[1]
+    o = np.empty((B, Hq, R, D))
+    lse = np.empty((B, Hq, R))
+    sc = oracle.scale_value(scale, D)
+    for b in range(B):
+        for hk in range(Hkv):
+            kh = oracle.decode(x.k[b:b + 1, hk:hk + 1], x.dtype)
+            vh = oracle.decode(x.v[b:b + 1, hk:hk + 1], x.dtype)
+            for g in range(G):
+                h = hk * G + g
+                qh = oracle.decode(x.q[b:b + 1, h:h + 1], x.dtype)
+                r = None if rows is None else rows[h]
+                oh, lh = oracle.attention(qh, kh, vh, sc, causal, rows=r)
+                o[b, h] = oh[0, 0]
+                lse[b, h] = lh[0, 0]
+    return o, lse
+
+
+def run_gpu(x: inputs.Inputs, scale, causal, device, num_splits=0,
+            return_lse=True):
+    import torch
+    q = to_device(x.q, x.dtype, device)
+    k = to_device(x.k, x.dtype, device)
+    v = to_device(x.v, x.dtype, device)
+    res = attn_fwd(q, k, v, causal=causal, scale=scale, num_splits=num_splits,
+                   return_lse=return_lse)
+    torch.cuda.synchronize(device)
+    if return_lse:
+        out, lse = res
+        return out.float().cpu().numpy().astype(np.float64), \
+            lse.cpu().numpy().astype(np.float64)
+    return res.float().cpu().numpy().astype(np.float64), None
+
+
+def compare(o_gpu, l_gpu, o_ref, l_ref, dtype, rounding_allowance=False,
+            max_err=MAX_ERR, mean_err=MEAN_ERR, lse_err=LSE_ERR, what=""):
+    """Element-wise comparison against the oracle.
+
+    With ``rounding_allowance`` the bounds also admit half an ulp of the
+    output type at |ref| (used for edge shapes with few keys, where |o| is
+    of order 1 and the output rounding alone can reach 2^-9).
+    """
+    assert o_gpu.shape == o_ref.shape, (o_gpu.shape, o_ref.shape)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite outputs"
+    err = np.abs(o_gpu - o_ref)
+    bound = np.full_like(err, max_err)
+    mbound = mean_err
+    if rounding_allowance:
+        hu = half_ulp(o_ref, dtype)
+        bound = bound + hu
+        mbound = mean_err + float(hu.mean())
+    r = Result(float(err.max()), float(err.mean()), 0.0, err.size)
+    if l_gpu is not None:
+        assert np.all(np.isfinite(l_gpu)), f"{what}: non-finite lse"
+        r.lse_err = float(np.abs(l_gpu - l_ref).max())
+    log(f"  {what}: max|err| {r.max_err:.3e} mean|err| {r.mean_err:.3e} "
+        f"lse {r.lse_err:.3e} over {r.n} values")
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), \
+        f"{what}: max err {r.max_err:.3e} at {worst} exceeds bound"
+    assert r.mean_err <= mbound, f"{what}: mean err {r.mean_err:.3e} > {mbound:.3e}"
+    assert r.lse_err <= lse_err, f"{what}: lse err {r.lse_err:.3e} > {lse_err}"
+    return r
+
+
+def gather_rows(a, rows):
+    """a [B, Hq, Nq, ...] -> [B, Hq, R, ...] at per-head rows [Hq, R]."""
+    B, Hq = a.shape[:2]
+    return np.stack([np.stack([a[b, h, rows[h]] for h in range(Hq)])
+                     for b in range(B)])

@@ -1,0 +1,129 @@
+"""CPU tests of the C ABI: exports, host-side validation, split heuristic.
+
+No test here launches GPU work: only entry points that return before any
+HIP call (validation failures, host-only queries) are called.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_efficient_tiled_amd as mta
+from memory_efficient_tiled_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, EINVAL = binding.ATTN_OK, binding.ATTN_EINVAL
+F16, BF16 = binding.ATTN_F16, binding.ATTN_BF16
+
+# Fake, aligned, non-overlapping addresses: validation never dereferences.
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+GOOD = dict(B=1, Hq=4, Hkv=2, Nq=100, Nkv=300, D=128, scale=0.088, causal=0,
+            dtype=BF16)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(attn_\w+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mta.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "attn_fwd" in names and len(names) >= 7
+    so = ctypes.CDLL(mta.lib_path())
+    for n in names:
+        assert hasattr(so, n), f"{n} declared in attn.h but not exported"
+
+
+def check(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    ptrs = dict(q=Q, k=K, v=V, out=O, lse=L)
+    for p in ("q", "k", "v", "out", "lse"):
+        if p in kw:
+            ptrs[p] = kw[p]
+    return binding.attn_fwd_check(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["out"],
+                                  ptrs["lse"], a["B"], a["Hq"], a["Hkv"],
+                                  a["Nq"], a["Nkv"], a["D"], a["scale"],
+                                  a["causal"], a["dtype"])
+
+
+def test_valid_arguments_pass():
+    assert check() == OK
+    assert check(D=64, dtype=F16, causal=1) == OK
+    assert check(lse=None) == OK          # LSE output is optional
+    assert check(scale=-0.5) == OK        # any finite scale
+    assert check(scale=0.0) == OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=0), dict(Hq=0), dict(Hkv=0), dict(Nq=0), dict(Nkv=-5),
+    dict(Hq=6, Hkv=4),                     # Hq not a multiple of Hkv
+    dict(D=96), dict(D=256), dict(dtype=2), dict(causal=2),
+    dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(q=None), dict(k=None), dict(v=None), dict(out=None),
+    dict(q=Q + 8), dict(out=O + 2), dict(lse=L + 2),       # misaligned
+    dict(out=Q), dict(out=K + 64), dict(lse=O + 16),       # aliasing
+    dict(B=70000, Hq=70000, Hkv=70000),                    # row count overflow
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_invalid_arguments_rejected(kw):
+    assert check(**kw) == EINVAL
+
+
+def test_attn_fwd_rejects_before_any_hip_call(lib):
+    # null pointers are caught by validation; no device is touched
+    rc = lib.attn_fwd(None, None, None, None, None, 1, 1, 1, 8, 8, 64,
+                      0.125, 0, F16, None)
+    assert rc == EINVAL
+    rc = lib.attn_fwd_split(Q, K, V, O, L, 1, 1, 1, 8, 8, 64, 0.125, 0, F16,
+                            -1, None)
+    assert rc == EINVAL
+
+
+def test_split_heuristic():
+    # the headline video shape fills the chip without splitting
+    assert binding.attn_fwd_num_splits(1, 24, 24, 17160, 17160, 128, 0, BF16) == 1
+    assert binding.attn_fwd_num_splits(1, 24, 24, 75600, 75600, 128, 0, BF16) == 1
+    # one query row over a long key range: split over keys
+    s = binding.attn_fwd_num_splits(1, 16, 16, 1, 65536, 128, 0, BF16)
+    assert 2 <= s <= 64
+    # short key ranges never split
+    assert binding.attn_fwd_num_splits(1, 1, 1, 1, 64, 64, 0, F16) == 1
+    assert binding.attn_fwd_num_splits(0, 1, 1, 1, 64, 64, 0, F16) == EINVAL
+
+
+def test_workspace_bytes():
+    assert binding.attn_fwd_workspace_bytes(1, 16, 1, 65536, 128, 1) == 0
+    assert binding.attn_fwd_workspace_bytes(2, 16, 10, 65536, 128, 4) == \
+        4 * 2 * 16 * 10 * (128 + 1) * 4
+
+
+def test_strerror(lib):
+    for code in (OK, EINVAL, binding.ATTN_EUNSUPPORTED, binding.ATTN_ENOMEM,
+                 binding.ATTN_EHIP, 12345):
+        assert lib.attn_strerror(code)
+
+
+def test_python_wrapper_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="HIP device"):
+        mta.attn_fwd(x, x, x)
+
+
+def test_oracle_not_on_product_path():
+    """The package never imports the oracle."""
+    pkg = os.path.join(ROOT, "memory_efficient_tiled_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f

@@ -1,0 +1,181 @@
+"""GPU parity: the HIP attention forward against the CPU oracle.
+
+Every case draws seeded inputs, runs the library through its C ABI on the
+GPU and compares with the float64 oracle element by element.  The named
+workloads use the fixed tolerances (max |err| <= 4e-3, mean |err| <= 5e-4,
+|lse err| <= 1e-3); at full size the oracle evaluates sampled query rows.
+"""
+import numpy as np
+import pytest
+
+from memory_efficient_tiled_amd import inputs
+from tests.parity import (compare, gather_rows, log, oracle_rows, run_gpu,
+                          to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed=0, scale=None,
+          rows=None, num_splits=0, allowance=True, k_offset_std=None):
+    log(f"case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} "
+        f"causal={causal} seed={seed} splits={num_splits} scale={scale}")
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed,
+                           k_offset_std=k_offset_std, sampled_rows=rows)
+    o, l = run_gpu(x, scale, causal, device, num_splits=num_splits)
+    r = None if rows is None else x.rows
+    o_ref, l_ref = oracle_rows(x, scale, causal, rows=r)
+    if r is not None:
+        o, l = gather_rows(o, r), gather_rows(l, r)
+    return compare(o, l, o_ref, l_ref, dtype, rounding_allowance=allowance,
+                   what=f"N={Nq}x{Nkv} D={D} {dtype} causal={causal}")
+
+
+# -- the named workloads -----------------------------------------------------
+
+def _workload(device, name, rows=None):
+    w = inputs.WORKLOADS[name]
+    return _case(device, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, w.causal,
+                 rows=rows, allowance=False, k_offset_std=w.k_offset_std)
+
+
+def test_tiny_256(gpu_device):
+    _workload(gpu_device, "tiny-256")
+
+
+@pytest.mark.parametrize("n", [1024, 2048])
+def test_sweep_full(gpu_device, n):
+    _workload(gpu_device, f"sweep-{n}")
+
+
+@pytest.mark.parametrize("n", [4096, 8192, 16384])
+def test_sweep_sampled(gpu_device, n):
+    _workload(gpu_device, f"sweep-{n}", rows=64)
+
+
+@pytest.mark.parametrize("n", [4096, 8192, 16384])
+def test_gqa_causal(gpu_device, n):
+    _workload(gpu_device, f"gqa-causal-{n}", rows=96)
+
+
+def test_dit_17160(gpu_device):
+    _workload(gpu_device, "dit-17160", rows=96)
+
+
+def test_dit_75600(gpu_device):
+    # 256 sampled query rows per head, including rows 0 and Nq-1 (in the
+    # ragged last query tile)
+    _workload(gpu_device, "dit-75600", rows=256)
+
+
+# -- edge shapes -------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 7, 63, 65, 129, 1000])
+def test_ragged_lengths(gpu_device, n, causal, D, dtype):
+    _case(gpu_device, 2, 4, 2, n, n, D, dtype, causal, seed=n)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nkv", [(100, 300), (300, 100), (1, 777), (513, 64)])
+def test_nq_ne_nkv(gpu_device, nq, nkv, causal):
+    _case(gpu_device, 1, 4, 1, nq, nkv, 128, inputs.BF16, causal, seed=nq + nkv)
+
+
+@pytest.mark.parametrize("G", [1, 2, 7, 8])
+def test_gqa_groups(gpu_device, G):
+    _case(gpu_device, 1, 2 * G, 2, 300, 300, 64, inputs.F16, True, seed=G)
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_decode_long_keys(gpu_device, G):
+    # one query row over 64K keys: the split-KV path
+    _case(gpu_device, 1, 2 * G, 2, 1, 65536, 128, inputs.BF16, False, seed=40 + G)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forced_splits(gpu_device, splits, causal):
+    _case(gpu_device, 1, 3, 1, 200, 1500, 64, inputs.F16, causal, seed=7,
+          num_splits=splits)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.5])
+def test_scale_values(gpu_device, scale):
+    _case(gpu_device, 1, 2, 2, 130, 190, 64, inputs.F16, True, seed=9,
+          scale=scale)
+
+
+# -- exact properties --------------------------------------------------------
+
+def _dev(x, dtype, device):
+    return to_device(x, dtype, device)
+
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+def test_causal_row0_is_v0_exactly(gpu_device, dtype):
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd
+    x = inputs.make_inputs(1, 4, 2, 300, 300, 128, dtype, seed=3)
+    out, lse = attn_fwd(_dev(x.q, dtype, gpu_device), _dev(x.k, dtype, gpu_device),
+                        _dev(x.v, dtype, gpu_device), causal=True)
+    torch.cuda.synchronize()
+    v = _dev(x.v, dtype, gpu_device)
+    for h in range(4):
+        assert torch.equal(out[0, h, 0], v[0, h // 2, 0]), f"head {h}"
+
+
+def test_constant_v(gpu_device):
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd
+    x = inputs.make_inputs(1, 2, 2, 200, 500, 64, inputs.F16, seed=4)
+    c = np.linspace(-2, 2, 64).astype(np.float16)
+    vc = np.broadcast_to(c, x.v.shape).copy()
+    out, _ = attn_fwd(_dev(x.q, inputs.F16, gpu_device), _dev(x.k, inputs.F16, gpu_device),
+                      _dev(vc, inputs.F16, gpu_device))
+    torch.cuda.synchronize()
+    err = np.abs(out.float().cpu().numpy() - c.astype(np.float32)).max()
+    log(f"  constant V: max|err| {err:.3e}")
+    assert err <= 4e-3
+
+
+def test_deterministic(gpu_device):
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd
+    x = inputs.make_inputs(1, 4, 4, 1000, 3000, 128, inputs.BF16, seed=5)
+    args = [_dev(a, inputs.BF16, gpu_device) for a in (x.q, x.k, x.v)]
+    for splits in (1, 4):
+        o1, l1 = attn_fwd(*args, num_splits=splits)
+        o2, l2 = attn_fwd(*args, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_without_lse(gpu_device):
+    x = inputs.make_inputs(1, 2, 2, 100, 100, 64, inputs.F16, seed=6)
+    o, _ = run_gpu(x, None, False, gpu_device, return_lse=False)
+    o_ref, _ = oracle_rows(x, None, False)
+    compare(o, None, o_ref, None, inputs.F16, rounding_allowance=True,
+            what="no lse")
+
+
+def test_no_device_allocation_without_split(gpu_device):
+    """The non-split path allocates nothing: torch's allocator sees only the
+    outputs, and the library's own workspace query is zero."""
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd, attn_fwd_num_splits
+    w = inputs.WORKLOADS["dit-17160"]
+    assert attn_fwd_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, False, 1) == 1
+    x = inputs.make_inputs(1, 2, 2, 4096, 4096, 128, inputs.BF16, seed=8)
+    args = [_dev(a, inputs.BF16, gpu_device) for a in (x.q, x.k, x.v)]
+    out = torch.empty_like(args[0])
+    lse = torch.empty(1, 2, 4096, dtype=torch.float32, device=gpu_device)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.max_memory_allocated()
+    attn_fwd(*args, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == before
+    free0, _ = torch.cuda.mem_get_info()
+    assert free0 > 0
