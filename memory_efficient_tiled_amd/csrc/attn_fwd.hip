@@ -19,9 +19,9 @@
 //    row are in lane lane^32.  Row max and row sum are therefore in-lane plus
 //    one exchange between the two wave halves.
 //  * The probabilities are already laid out as the B operand of
-//    O^T = V^T P^T, so P never leaves registers.  V^T is the A operand: V is
-//    written to LDS transposed ([d][key]) so each lane reads its operand with
-//    two 8-byte loads.
+//    O^T = V^T P^T, so P never leaves registers.  V^T is the A operand: V stays
+//    row-major in LDS and each lane gathers its 8 keys of one column with two
+//    transposing 8-byte LDS reads (ds_read_b64_tr_b16).
 //  * The output accumulator O^T also has one query row per lane, so the
 //    per-row rescale by alpha = 2^(m_old - m_new) is a plain multiply.
 //
@@ -115,30 +115,66 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// Copy one 16-byte chunk per lane from global memory straight into LDS: lane
+// i of the wave writes lds_base + 16*i (lds_base must be wave-uniform).
+__device__ __forceinline__ void g2lds16(const uint16_t* g, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
 
-template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * QB * 32;
-  constexpr int KRS = D + 8;       // K tile row stride in LDS (elements): +16 B breaks bank aliasing
-  constexpr int VRS = BN + 4;      // V^T tile row stride in LDS (elements)
-  constexpr int KTILE = BN * KRS;
-  constexpr int VTILE = D * VRS;
-  constexpr int DC = D / 16;       // 16-wide reduction chunks of Q K^T
-  constexpr int NKB = BN / 32;     // 32-key blocks per tile
-  constexpr int NDB = D / 32;      // 32-wide output column blocks
-  constexpr int NKC = BN / 16;     // 16-key reduction chunks of P V
-  constexpr int KCH = BN * D / 8;  // 16-byte chunks per K (or V) tile
-  static_assert(KCH % NT == 0, "tile must split evenly over threads");
-  constexpr int KLD = KCH / NT;
-  constexpr int KG = KLD >= 4 ? 4 : KLD;  // keys packed per transposed V store
-  constexpr int VPAIRS = KLD / KG;
-  static_assert(VPAIRS * KG == KLD, "V staging must cover the tile");
-  static_assert(KG == 4 || KG == 2, "unsupported V staging width");
+// Transposing LDS read: in each 16-lane group, lane i receives element i%4 of
+// the 4-element (8-byte) words addressed by lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Both halves of the wave exchange a value; the max (sum) of the two results
+// is the max (sum) over lanes l and l^32, identical in both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The running max is only raised when a row's new maximum exceeds it by more
+// than kLazyRescale (base-2 units).  Until then probabilities are computed
+// against the stale max and may reach 2^kLazyRescale; the final O / l and
+// lse = m + log2(l) are the same function of the scores whichever reference
+// max was used, so the result is unchanged up to rounding while the O
+// rescale is skipped on almost every tile.
+constexpr float kLazyRescale = 8.0f;
+
+// One workgroup: NW waves x 32 query rows, all on KV head hq / G, looping
+// over BN-key tiles of its key range.  K and V tiles go from HBM straight
+// into LDS (double-buffered) in a swizzled row-major layout:
+//   K: 16-byte chunk c of key row r is stored at chunk c ^ (r & 7)
+//      (conflict-free 16-byte row reads for the K operand);
+//   V: chunk c of row r is stored at chunk c ^ (2 * (r & 3))
+//      (conflict-free transposing 8-byte reads for the V^T operand).
+template <int D, class Tag, bool CAUSAL, int NW, int BN, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
+  constexpr int BM = NW * 32;
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int TILE = BN * D;        // elements of one K (or V) tile
+  constexpr int INSTR = BN * CPR / 64;  // 1 KB wave copies per tile
+  static_assert(INSTR % NW == 0, "tile copies must split evenly over waves");
+  constexpr int IPW = INSTR / NW;
+  constexpr int DC = D / 16;          // reduction chunks of Q K^T
+  constexpr int NKB = BN / 32;        // 32-key blocks per tile
+  constexpr int NDB = D / 32;         // 32-wide output column blocks
+  constexpr int NKC = BN / 16;        // reduction chunks of P V
   using N = Num<Tag>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KTILE + VTILE)];
+  __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf1[TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -159,6 +195,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
   const int hk = hq / p.G;
   const int q0 = qt * BM;
+  const int wq0 = q0 + wave * 32;       // first query row of this wave
 
   const int kbeg = sp * p.split_len;
   int kend = min(p.Nkv, kbeg + p.split_len);
@@ -170,122 +207,59 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
   const uint16_t* __restrict__ Kg = p.k + krow0 * D;
   const uint16_t* __restrict__ Vg = p.v + krow0 * D;
 
-  // Q^T operands for the whole key loop.
-  u32x4 qf[QB][DC];
+  // Issue this wave's share of the copies of the tile starting at key k0.
+  // Rows past the last key re-read the last key: they are masked to -inf in
+  // the scores, so their (finite) V values are multiplied by exactly 0.
+  auto issue = [&](int k0, uint16_t* ks, uint16_t* vs) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = q0 + (wave * QB + qb) * 32 + l32;
+    for (int j = 0; j < IPW; ++j) {
+      const int ins = wave * IPW + j;
+      const int slot = ins * 64 + lane;
+      const int row = slot / CPR, pc = slot % CPR;
+      const int key = min(k0 + row, p.Nkv - 1);
+      const uint16_t* kr = Kg + (size_t)key * D;
+      const uint16_t* vr = Vg + (size_t)key * D;
+      g2lds16(kr + ((pc ^ (row & 7)) << 3), ks + ins * 512);
+      g2lds16(vr + ((pc ^ ((row & 3) << 1)) << 3), vs + ins * 512);
+    }
+  };
+
+  // Q^T operands for the whole key loop.
+  u32x4 qf[DC];
+  {
+    const int row = wq0 + l32;
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < p.Nq)
-        x = *(const u32x4*)(p.q + (qrow0 + row) * D + kc * 16 + hl * 8);
-      qf[qb][kc] = x ^ p.qsign;
+      if (row < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + row) * D + kc * 16 + hl * 8);
+      qf[kc] = x ^ p.qsign;
     }
   }
 
-  f32x16 oacc[QB][NDB];
-  float m[QB], l[QB];
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const int qrow = wq0 + l32;
 
-  u32x4 kst[KLD];
-  u32x4 vst[VPAIRS][KG];
+  // Lane-invariant parts of the operand addresses.
+  const int v_g = lane >> 4, v_r = lane & 15;
+  const int v_key = 4 * hl + (v_r >> 2);          // key within a 16-key chunk (first half)
+  const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);  // column within a 32-wide block
+  const int v_sw = (v_key & 3) << 1;
 
-  auto gload = [&](int k0) {
+  auto compute = [&](int k0, const uint16_t* ks, const uint16_t* vs) {
+    // S^T = K Q^T.
+    f32x16 s[NKB];
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = i * NT + tid;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const int key = k0 + row;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < p.Nkv) x = *(const u32x4*)(Kg + (size_t)key * D + col * 8);
-      kst[i] = x;
-    }
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int pr = 0; pr < VPAIRS; ++pr) {
-      const int pi = pr * NT + tid;
-      const int g = pi % (BN / KG), dc = pi / (BN / KG);
+    for (int kc = 0; kc < DC; ++kc) {
 #pragma unroll
-      for (int r = 0; r < KG; ++r) {
-        const int key = k0 + g * KG + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < p.Nkv) x = *(const u32x4*)(Vg + (size_t)key * D + dc * 8);
-        vst[pr][r] = x;
-      }
-    }
-  };
-
-  auto lstore = [&](int buf) {
-    uint16_t* Ks = smem + buf * (KTILE + VTILE);
-    uint16_t* Vs = Ks + KTILE;
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = i * NT + tid;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *(u32x4*)(Ks + row * KRS + col * 8) = kst[i];
-    }
-#pragma unroll
-    for (int pr = 0; pr < VPAIRS; ++pr) {
-      const int pi = pr * NT + tid;
-      const int g = pi % (BN / KG), dc = pi / (BN / KG);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint16_t* dst = Vs + (dc * 8 + e) * VRS + g * KG;
-        if (KG == 4) {
-          uint32_t a0 = vst[pr][0][w], a1 = vst[pr][1][w], a2 = vst[pr][2][w], a3 = vst[pr][3][w];
-          u32x2 y;
-          if (e & 1) {
-            y[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-            y[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-          } else {
-            y[0] = (a0 & 0xffffu) | (a1 << 16);
-            y[1] = (a2 & 0xffffu) | (a3 << 16);
-          }
-          *(u32x2*)dst = y;
-        } else {
-          uint32_t a0 = vst[pr][0][w], a1 = vst[pr][1][w];
-          *(uint32_t*)dst = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        }
-      }
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(kbeg);
-    lstore(0);
-    __syncthreads();
-  }
-
-  const int wq0 = q0 + wave * QB * 32;  // first query row of this wave
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = kbeg + t * BN;
-    const bool more = t + 1 < ntiles;
-    if (more) gload(k0 + BN);
-
-    const uint16_t* Ks = smem + (t & 1) * (KTILE + VTILE);
-    const uint16_t* Vs = Ks + KTILE;
-
-    // S^T = K Q^T for this tile.
-    f32x16 s[QB][NKB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int kc = 0; kc < DC; ++kc) {
-        const u32x4 a = *(const u32x4*)(Ks + (kb * 32 + l32) * KRS + kc * 16 + hl * 8);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = N::mfma(a, qf[qb][kc], s[qb][kb]);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = kb * 32 + l32;
+        const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ (row & 7)) << 3));
+        s[kb] = N::mfma(a, qf[kc], s[kb]);
       }
     }
 
@@ -293,110 +267,116 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const bool need_mask = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0);
     if (need_mask) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int row = wq0 + qb * 32 + l32;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-            const bool ok = key < kend && (!CAUSAL || key <= row);
-            if (!ok) s[qb][kb][e] = -INFINITY;
-          }
-      }
-    }
-
-    // Online softmax (base 2), then P in the input type as the B operand.
-    u32x4 pf[QB][NKC];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][kb][e]);
-      mx = fmaxf(mx, xor32(mx));
-      const float mc = (mx == -INFINITY) ? -INFINITY : mx * p.c;
-      const float mnew = fmaxf(m[qb], mc);
-      const float mb = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(m[qb] - mb);
-      m[qb] = mnew;
-      float rs = 0.f;
-#pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float sv = s[qb][kb][e];
-          float x = fast_exp2(fmaf(sv, p.c, -mb));
-          if (need_mask && sv == -INFINITY) x = 0.f;
-          s[qb][kb][e] = x;
-          rs += x;
-        }
-      l[qb] = l[qb] * alpha + rs;  // lane-partial: the partner lane holds the other keys
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          u32x4 y;
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            y[w] = N::pack2(s[qb][kb][8 * hf + 2 * w], s[qb][kb][8 * hf + 2 * w + 1]);
-          pf[qb][kb * 2 + hf] = y;
+          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+          const bool ok = key < kend && (!CAUSAL || key <= qrow);
+          if (!ok) s[kb][e] = -INFINITY;
         }
     }
 
-    // O^T += V^T P^T.
+    // Online softmax in base 2 with a lazily raised running max.
+    float mx = -INFINITY;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const uint16_t* src = Vs + (db * 32 + l32) * VRS + kc * 16 + 4 * hl;
-        const u32x2 lo = *(const u32x2*)src;
-        const u32x2 hi = *(const u32x2*)(src + 8);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    mx = pair_max(mx);
+    const float mc = (mx == -INFINITY) ? -INFINITY : mx * p.c;
+    if (__builtin_amdgcn_ballot_w64(mc > m + kLazyRescale)) {
+      const float mnew = fmaxf(m, mc);
+      const float alpha = fast_exp2(m - ((mnew == -INFINITY) ? 0.f : mnew));
+      m = mnew;
+      l *= alpha;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = N::mfma(a, pf[qb][kc], oacc[qb][db]);
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    const float mb = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+    u32x4 pf[NKC];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float sv = s[kb][e];
+        float x = fast_exp2(fmaf(sv, p.c, -mb));
+        if (need_mask && sv == -INFINITY) x = 0.f;
+        s[kb][e] = x;
+        rs += x;
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 y;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          y[w] = N::pack2(s[kb][8 * hf + 2 * w], s[kb][8 * hf + 2 * w + 1]);
+        pf[kb * 2 + hf] = y;
       }
     }
+    l += rs;  // lane-partial: lane l^32 holds the row's other keys
 
-    if (more) lstore((t + 1) & 1);
+    // O^T += V^T P^T; V^T operands come from transposing reads of V.
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int key = kc * 16 + v_key;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = db * 32 + v_d;
+        const u32x2 lo = lds_read_tr16(vs + key * D + ((((d >> 3) ^ v_sw)) << 3) + (d & 7));
+        const u32x2 hi = lds_read_tr16(vs + (key + 8) * D + ((((d >> 3) ^ v_sw)) << 3) + (d & 7));
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = N::mfma(a, pf[kc], oacc[db]);
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    issue(kbeg, kbuf0, vbuf0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < ntiles; t += 2) {
+    const int k0 = kbeg + t * BN;
+    if (t + 1 < ntiles) issue(k0 + BN, kbuf1, vbuf1);
+    compute(k0, kbuf0, vbuf0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) issue(k0 + 2 * BN, kbuf0, vbuf0);
+    compute(k0 + BN, kbuf1, vbuf1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // Epilogue: combine the two lane halves' row sums, normalise, store.
+  const float lt = pair_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  if (qrow < p.Nq) {
+    if (SPLIT) {
+      const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
+      float* dst = p.opart + prow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wq0 + qb * 32 + l32;
-    const float lt = l[qb] + xor32(l[qb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_v = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
-    if (row < p.Nq) {
-      if (SPLIT) {
-        const size_t prow = (size_t)sp * p.rows + qrow0 + row;
-        float* dst = p.opart + prow * D;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int i = 0; i < 4; ++i) {
+          f32x4 y = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                     oacc[db][4 * i + 3] * inv};
+          *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+        }
+      if (hl == 0) p.lsepart[prow] = lse_v;
+    } else {
+      uint16_t* dst = p.o + (qrow0 + qrow) * D;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f32x4 y = {oacc[qb][db][4 * i] * inv, oacc[qb][db][4 * i + 1] * inv,
-                       oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv};
-            *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-          }
-        if (hl == 0) p.lsepart[prow] = lse_v;
-      } else {
-        uint16_t* dst = p.o + (qrow0 + row) * D;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            u32x2 y = {N::pack2(oacc[qb][db][4 * i] * inv, oacc[qb][db][4 * i + 1] * inv),
-                       N::pack2(oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv)};
-            *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-          }
-        if (hl == 0 && p.lse) p.lse[qrow0 + row] = lse_v;
-      }
+        for (int i = 0; i < 4; ++i) {
+          u32x2 y = {N::pack2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv),
+                     N::pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv)};
+          *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+        }
+      if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
     }
   }
 }
@@ -439,11 +419,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 
 // Tile table per head dimension.
 struct TileCfg {
-  int NW, QB, BN;
-  int BM() const { return NW * QB * 32; }
+  int NW, BN;
+  constexpr int BM() const { return NW * 32; }
 };
-constexpr TileCfg kCfgD64 = {4, 1, 64};
-constexpr TileCfg kCfgD128 = {4, 1, 64};
+constexpr TileCfg kCfgD64 = {4, 64};
+constexpr TileCfg kCfgD128 = {4, 64};
 constexpr int kResidentWgPerCu = 2;
 
 inline TileCfg cfg_for(int D) { return D == 64 ? kCfgD64 : kCfgD128; }
@@ -535,7 +515,7 @@ int choose_splits(int B, int Hq, int Nq, int Nkv, int D, int num_cus) {
 template <int D, class Tag, bool CAUSAL, bool SPLIT>
 hipError_t launch_main(const Params& p, hipStream_t stream) {
   constexpr TileCfg c = (D == 64) ? kCfgD64 : kCfgD128;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, SPLIT>), dim3(p.total),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.BN, SPLIT>), dim3(p.total),
                      dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
