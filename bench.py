@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows per head for the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this size "
+                         "(scales the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -94,6 +97,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "launches": max(1, args.steps)}), flush=True)
+        return
 
     from memory_efficient_tiled_amd import attn_fwd, attn_fwd_num_splits, inputs
     from memory_efficient_tiled_amd.binding import ATTN_BF16, ATTN_F16

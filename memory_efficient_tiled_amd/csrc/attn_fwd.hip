@@ -150,25 +150,28 @@ __device__ __forceinline__ float pair_sum(float x) {
 // rescale is skipped on almost every tile.
 constexpr float kLazyRescale = 8.0f;
 
-// One workgroup: NW waves x 32 query rows, all on KV head hq / G, looping
-// over BN-key tiles of its key range.  K and V tiles go from HBM straight
-// into LDS (double-buffered) in a swizzled row-major layout:
+// One workgroup: NW waves x QB x 32 query rows, all on KV head hq / G,
+// looping over BN-key tiles of its key range.  Each K or V operand read from
+// LDS feeds QB MFMAs (one per 32-row query block of the wave), so LDS read
+// traffic per flop falls as 1/QB.  K and V tiles go from HBM straight into
+// LDS (double-buffered) in a swizzled row-major layout:
 //   K: 16-byte chunk c of key row r is stored at chunk c ^ (r & 7)
 //      (conflict-free 16-byte row reads for the K operand);
 //   V: chunk c of row r is stored at chunk c ^ (2 * (r & 3))
 //      (conflict-free transposing 8-byte reads for the V^T operand).
-template <int D, class Tag, bool CAUSAL, int NW, int BN, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
-  constexpr int BM = NW * 32;
-  constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int TILE = BN * D;        // elements of one K (or V) tile
+template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, QB == 1 ? 2 : 1) void attn_fwd_kernel(Params p) {
+  constexpr int BM = NW * QB * 32;
+  constexpr int WR = QB * 32;           // query rows per wave
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int TILE = BN * D;          // elements of one K (or V) tile
   constexpr int INSTR = BN * CPR / 64;  // 1 KB wave copies per tile
   static_assert(INSTR % NW == 0, "tile copies must split evenly over waves");
   constexpr int IPW = INSTR / NW;
-  constexpr int DC = D / 16;          // reduction chunks of Q K^T
-  constexpr int NKB = BN / 32;        // 32-key blocks per tile
-  constexpr int NDB = D / 32;         // 32-wide output column blocks
-  constexpr int NKC = BN / 16;        // reduction chunks of P V
+  constexpr int DC = D / 16;            // reduction chunks of Q K^T
+  constexpr int NKB = BN / 32;          // 32-key blocks per tile
+  constexpr int NDB = D / 32;           // 32-wide output column blocks
+  constexpr int NKC = BN / 16;          // reduction chunks of P V
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[TILE];
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
   const int hk = hq / p.G;
   const int q0 = qt * BM;
-  const int wq0 = q0 + wave * 32;       // first query row of this wave
+  const int wq0 = q0 + wave * WR;       // first query row of this wave
 
   const int kbeg = sp * p.split_len;
   int kend = min(p.Nkv, kbeg + p.split_len);
@@ -225,22 +228,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   };
 
   // Q^T operands for the whole key loop.
-  u32x4 qf[DC];
-  {
-    const int row = wq0 + l32;
+  u32x4 qf[QB][DC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wq0 + qb * 32 + l32;
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (row < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + row) * D + kc * 16 + hl * 8);
-      qf[kc] = x ^ p.qsign;
+      qf[qb][kc] = x ^ p.qsign;
     }
   }
 
-  f32x16 oacc[NDB];
+  f32x16 oacc[QB][NDB];
+  float m[QB], l[QB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
-  const int qrow = wq0 + l32;
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
+  }
 
   // Lane-invariant parts of the operand addresses.
   const int v_g = lane >> 4, v_r = lane & 15;
@@ -250,16 +258,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
 
   auto compute = [&](int k0, const uint16_t* ks, const uint16_t* vs) {
     // S^T = K Q^T.
-    f32x16 s[NKB];
+    f32x16 s[QB][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int row = kb * 32 + l32;
         const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ (row & 7)) << 3));
-        s[kb] = N::mfma(a, qf[kc], s[kb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = N::mfma(a, qf[qb][kc], s[qb][kb]);
       }
     }
 
@@ -267,54 +278,70 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     const bool need_mask = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = wq0 + qb * 32 + l32;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-          const bool ok = key < kend && (!CAUSAL || key <= qrow);
-          if (!ok) s[kb][e] = -INFINITY;
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+            const bool ok = key < kend && (!CAUSAL || key <= qrow);
+            if (!ok) s[qb][kb][e] = -INFINITY;
+          }
+      }
     }
 
     // Online softmax in base 2 with a lazily raised running max.
-    float mx = -INFINITY;
+    float mc[QB];
+    bool grow = false;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = pair_max(mx);
-    const float mc = (mx == -INFINITY) ? -INFINITY : mx * p.c;
-    if (__builtin_amdgcn_ballot_w64(mc > m + kLazyRescale)) {
-      const float mnew = fmaxf(m, mc);
-      const float alpha = fast_exp2(m - ((mnew == -INFINITY) ? 0.f : mnew));
-      m = mnew;
-      l *= alpha;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][kb][e]);
+      mx = pair_max(mx);
+      mc[qb] = (mx == -INFINITY) ? -INFINITY : mx * p.c;
+      grow = grow || (mc[qb] > m[qb] + kLazyRescale);
     }
-    const float mb = (m == -INFINITY) ? 0.f : m;
-    float rs = 0.f;
-    u32x4 pf[NKC];
+    if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mnew = fmaxf(m[qb], mc[qb]);
+        const float alpha = fast_exp2(m[qb] - ((mnew == -INFINITY) ? 0.f : mnew));
+        m[qb] = mnew;
+        l[qb] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float sv = s[kb][e];
-        float x = fast_exp2(fmaf(sv, p.c, -mb));
-        if (need_mask && sv == -INFINITY) x = 0.f;
-        s[kb][e] = x;
-        rs += x;
-      }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 y;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          y[w] = N::pack2(s[kb][8 * hf + 2 * w], s[kb][8 * hf + 2 * w + 1]);
-        pf[kb * 2 + hf] = y;
+        for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
       }
     }
-    l += rs;  // lane-partial: lane l^32 holds the row's other keys
+    u32x4 pf[QB][NKC];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mb = (m[qb] == -INFINITY) ? 0.f : m[qb];
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float sv = s[qb][kb][e];
+          float x = fast_exp2(fmaf(sv, p.c, -mb));
+          if (need_mask && sv == -INFINITY) x = 0.f;
+          s[qb][kb][e] = x;
+          rs += x;
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          u32x4 y;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            y[w] = N::pack2(s[qb][kb][8 * hf + 2 * w], s[qb][kb][8 * hf + 2 * w + 1]);
+          pf[qb][kb * 2 + hf] = y;
+        }
+      }
+      l[qb] += rs;  // lane-partial: lane l^32 holds the row's other keys
+    }
 
     // O^T += V^T P^T; V^T operands come from transposing reads of V.
 #pragma unroll
@@ -323,10 +350,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = db * 32 + v_d;
-        const u32x2 lo = lds_read_tr16(vs + key * D + ((((d >> 3) ^ v_sw)) << 3) + (d & 7));
-        const u32x2 hi = lds_read_tr16(vs + (key + 8) * D + ((((d >> 3) ^ v_sw)) << 3) + (d & 7));
+        const int off = (((d >> 3) ^ v_sw) << 3) + (d & 7);
+        const u32x2 lo = lds_read_tr16(vs + key * D + off);
+        const u32x2 hi = lds_read_tr16(vs + (key + 8) * D + off);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = N::mfma(a, pf[kc], oacc[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = N::mfma(a, pf[qb][kc], oacc[qb][db]);
       }
     }
   };
@@ -350,33 +379,37 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   }
 
   // Epilogue: combine the two lane halves' row sums, normalise, store.
-  const float lt = pair_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse_v = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
-  if (qrow < p.Nq) {
-    if (SPLIT) {
-      const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
-      float* dst = p.opart + prow * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = wq0 + qb * 32 + l32;
+    const float lt = pair_sum(l[qb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_v = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+    if (qrow < p.Nq) {
+      if (SPLIT) {
+        const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
+        float* dst = p.opart + prow * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 y = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
-                     oacc[db][4 * i + 3] * inv};
-          *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-        }
-      if (hl == 0) p.lsepart[prow] = lse_v;
-    } else {
-      uint16_t* dst = p.o + (qrow0 + qrow) * D;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+          for (int i = 0; i < 4; ++i) {
+            f32x4 y = {oacc[qb][db][4 * i] * inv, oacc[qb][db][4 * i + 1] * inv,
+                       oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv};
+            *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+          }
+        if (hl == 0) p.lsepart[prow] = lse_v;
+      } else {
+        uint16_t* dst = p.o + (qrow0 + qrow) * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x2 y = {N::pack2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv),
-                     N::pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv)};
-          *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-        }
-      if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u32x2 y = {N::pack2(oacc[qb][db][4 * i] * inv, oacc[qb][db][4 * i + 1] * inv),
+                       N::pack2(oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv)};
+            *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+          }
+        if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
+      }
     }
   }
 }
@@ -419,11 +452,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 
 // Tile table per head dimension.
 struct TileCfg {
-  int NW, BN;
-  constexpr int BM() const { return NW * 32; }
+  int NW, QB, BN;
+  constexpr int BM() const { return NW * QB * 32; }
 };
-constexpr TileCfg kCfgD64 = {4, 64};
-constexpr TileCfg kCfgD128 = {4, 64};
+#ifndef ATTN_D128_CFG
+#define ATTN_D128_CFG {4, 1, 64}
+#endif
+#ifndef ATTN_D64_CFG
+#define ATTN_D64_CFG {4, 1, 64}
+#endif
+constexpr TileCfg kCfgD64 = ATTN_D64_CFG;
+constexpr TileCfg kCfgD128 = ATTN_D128_CFG;
 constexpr int kResidentWgPerCu = 2;
 
 inline TileCfg cfg_for(int D) { return D == 64 ? kCfgD64 : kCfgD128; }
@@ -515,7 +554,7 @@ int choose_splits(int B, int Hq, int Nq, int Nkv, int D, int num_cus) {
 template <int D, class Tag, bool CAUSAL, bool SPLIT>
 hipError_t launch_main(const Params& p, hipStream_t stream) {
   constexpr TileCfg c = (D == 64) ? kCfgD64 : kCfgD128;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.BN, SPLIT>), dim3(p.total),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, SPLIT>), dim3(p.total),
                      dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
