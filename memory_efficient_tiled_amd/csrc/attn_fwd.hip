@@ -35,11 +35,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -142,27 +144,64 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The running max is only raised when a row's new maximum exceeds it by more
-// than kLazyRescale (base-2 units).  Until then probabilities are computed
-// against the stale max and may reach 2^kLazyRescale; the final O / l and
-// lse = m + log2(l) are the same function of the scores whichever reference
-// max was used, so the result is unchanged up to rounding while the O
-// rescale is skipped on almost every tile.
-constexpr float kLazyRescale = 8.0f;
+// LDS swizzles.  gfx950 serves a 16-byte LDS read 16 lanes (256 bytes, all
+// 64 banks) at a time and an 8-byte read 32 lanes at a time, so a pattern is
+// conflict-free when those lanes cover 16 distinct 16-byte bank groups.
+//  * K operand reads: the 16 lanes of a group read the same chunk of 16
+//    consecutive key rows.  With 256-byte rows (D = 128) the chunk is XORed
+//    with r & 15; with 128-byte rows (D = 64) two rows share the 64 banks and
+//    the chunk is XORed with (r >> 1) & 7.
+//  * V^T operand reads (transposing, 8 bytes per lane): 32 lanes read 4 keys
+//    x 64 contiguous bytes.  With 256-byte rows the 4 keys go to 4 disjoint
+//    64-byte quarters (XOR 4 * (r & 3)); with 128-byte rows keys r and r + 2
+//    share banks and are separated by XOR 4 * ((r >> 1) & 1).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
-// One workgroup: NW waves x QB x 32 query rows, all on KV head hq / G,
-// looping over BN-key tiles of its key range.  Each K or V operand read from
-// LDS feeds QB MFMAs (one per 32-row query block of the wave), so LDS read
-// traffic per flop falls as 1/QB.  K and V tiles go from HBM straight into
-// LDS (double-buffered) in a swizzled row-major layout:
-//   K: 16-byte chunk c of key row r is stored at chunk c ^ (r & 7)
-//      (conflict-free 16-byte row reads for the K operand);
-//   V: chunk c of row r is stored at chunk c ^ (2 * (r & 3))
-//      (conflict-free transposing 8-byte reads for the V^T operand).
-template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, QB == 1 ? 2 : 1) void attn_fwd_kernel(Params p) {
-  constexpr int BM = NW * QB * 32;
-  constexpr int WR = QB * 32;           // query rows per wave
+// Probabilities are formed against a running reference max m that is only
+// raised when a tile would otherwise produce a probability above 2^8: the
+// final O / l and lse = m + log2(l) are the same function of the scores for
+// any reference, so the result is unchanged up to rounding.  The check is
+// done on the in-lane partial row sum (each term is at most the sum), which
+// the softmax needs anyway, so no per-tile row max is computed unless a tile
+// fails it (and on the first tile, where m is still -inf).
+constexpr float kMaxPartialSum = 256.0f;
+
+// Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9.
+constexpr int kRawBufferFlags = 0x00020000;
+
+// Copy 16 bytes per lane from a buffer into LDS: lane i writes lds + 16 i
+// (lds wave-uniform).  Offsets at or beyond the buffer's size read zero.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+// One workgroup: NW waves x 32 query rows, all on KV head hq / G, looping
+// over BN-key tiles of its key range.  K and V tiles go from HBM (mostly L2)
+// straight into LDS, two buffers each, in a swizzled row-major layout:
+// 16-byte chunk c of key row r is stored at chunk c ^ k_swz(r) (K) or
+// c ^ v_swz(r) (V).
+//
+// Software pipeline, one barrier per key tile t (scores S_t already in
+// registers when the step starts):
+//   wait for this wave's copies of K_{t+1}, V_t; barrier
+//   start copies of K_{t+2} (into the buffer K_t used) and V_{t+1}
+//   S_{t+1} = K_{t+1} Q^T on the matrix cores, interleaved with the softmax
+//   of S_t on the vector ALUs (the two are independent)
+//   O += P_t V_t
+// The barrier also certifies that every wave has finished reading the
+// buffers the new copies overwrite (K_t in the previous step's product,
+// V_{t-1} in the previous step's P V).
+template <int D, class Tag, bool CAUSAL, int NW, int BN, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
+  constexpr int BM = NW * 32;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // elements of one K (or V) tile
   constexpr int INSTR = BN * CPR / 64;  // 1 KB wave copies per tile
@@ -172,6 +211,7 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? 2 : 1) void attn_fwd_kernel(Para
   constexpr int NKB = BN / 32;          // 32-key blocks per tile
   constexpr int NDB = D / 32;           // 32-wide output column blocks
   constexpr int NKC = BN / 16;          // reduction chunks of P V
+  constexpr int ROWB = D * 2;           // bytes per K/V row
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[TILE];
@@ -198,7 +238,8 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? 2 : 1) void attn_fwd_kernel(Para
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
   const int hk = hq / p.G;
   const int q0 = qt * BM;
-  const int wq0 = q0 + wave * WR;       // first query row of this wave
+  const int wq0 = q0 + wave * 32;       // first query row of this wave
+  const int qrow = wq0 + l32;           // this lane's query row
 
   const int kbeg = sp * p.split_len;
   int kend = min(p.Nkv, kbeg + p.split_len);
@@ -207,143 +248,133 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? 2 : 1) void attn_fwd_kernel(Para
 
   const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
   const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
-  const uint16_t* __restrict__ Kg = p.k + krow0 * D;
-  const uint16_t* __restrict__ Vg = p.v + krow0 * D;
+  const uint16_t* Kg = p.k + krow0 * D;
+  const uint16_t* Vg = p.v + krow0 * D;
 
-  // Issue this wave's share of the copies of the tile starting at key k0.
-  // Rows past the last key re-read the last key: they are masked to -inf in
-  // the scores, so their (finite) V values are multiplied by exactly 0.
-  auto issue = [&](int k0, uint16_t* ks, uint16_t* vs) {
+  // Per-lane byte offsets of this wave's copy slots within a tile (the same
+  // for every tile) and the LDS slot each copy fills.
+  uint32_t koff[IPW], voff[IPW];
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int ins = wave * IPW + j;
-      const int slot = ins * 64 + lane;
-      const int row = slot / CPR, pc = slot % CPR;
-      const int key = min(k0 + row, p.Nkv - 1);
-      const uint16_t* kr = Kg + (size_t)key * D;
-      const uint16_t* vr = Vg + (size_t)key * D;
-      g2lds16(kr + ((pc ^ (row & 7)) << 3), ks + ins * 512);
-      g2lds16(vr + ((pc ^ ((row & 3) << 1)) << 3), vs + ins * 512);
-    }
+  for (int j = 0; j < IPW; ++j) {
+    const int slot = (wave * IPW + j) * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    koff[j] = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
+    voff[j] = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
+  }
+  // Copy tile `t` of K (or V) into LDS.  The buffer ends at the last key, so
+  // rows past it read as zero: their scores are masked to -inf and their V
+  // rows are multiplied by exactly 0.
+  auto issue = [&](const uint16_t* base, int t, uint16_t* dst, const uint32_t* off) {
+    const int k0 = kbeg + t * BN;
+    const int nrows = min(BN, p.Nkv - k0);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * D), 0, nrows * ROWB,
+                                          kRawBufferFlags);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) buf2lds16(r, dst + (wave * IPW + j) * 512, off[j]);
   };
 
   // Q^T operands for the whole key loop.
-  u32x4 qf[QB][DC];
+  u32x4 qf[DC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wq0 + qb * 32 + l32;
-#pragma unroll
-    for (int kc = 0; kc < DC; ++kc) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + row) * D + kc * 16 + hl * 8);
-      qf[qb][kc] = x ^ p.qsign;
-    }
+  for (int kc = 0; kc < DC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qrow < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + qrow) * D + kc * 16 + hl * 8);
+    qf[kc] = x ^ p.qsign;
   }
 
-  f32x16 oacc[QB][NDB];
-  float m[QB], l[QB];
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
 
-  // Lane-invariant parts of the operand addresses.
+  // Lane-invariant parts of the V^T operand addresses.
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);          // key within a 16-key chunk (first half)
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);  // column within a 32-wide block
-  const int v_sw = (v_key & 3) << 1;
+  const int v_sw = v_swz<D>(v_key);               // same for key v_key + 16 kc (+ 8)
 
-  auto compute = [&](int k0, const uint16_t* ks, const uint16_t* vs) {
-    // S^T = K Q^T.
-    f32x16 s[QB][NKB];
+  // S^T = K Q^T for one tile, accumulated into s (zeroed here).
+  auto qk = [&](const uint16_t* ks, f32x16* s) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int row = kb * 32 + l32;
-        const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ (row & 7)) << 3));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = N::mfma(a, qf[qb][kc], s[qb][kb]);
+        const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ k_swz<D>(row)) << 3));
+        s[kb] = N::mfma(a, qf[kc], s[kb]);
       }
     }
+  };
 
-    // Keys past the valid range, and (causal) keys after the row, get -inf.
-    const bool need_mask = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0);
-    if (need_mask) {
+  // Keys past the valid range, and (causal) keys after the row, get -inf.
+  // Only tiles that straddle the end of the key range or the diagonal.
+  auto mask = [&](int t, f32x16* s) {
+    const int k0 = kbeg + t * BN;
+    const bool need = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0);
+    if (need) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wq0 + qb * 32 + l32;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+          const bool ok = key < kend && (!CAUSAL || key <= qrow);
+          if (!ok) s[kb][e] = -INFINITY;
+        }
+    }
+  };
+
+  // Probabilities of one tile against reference max mb, packed as the P^T
+  // operands; returns the lane-partial row sum.
+  auto probs = [&](const f32x16* s, float mb, u32x4* pf) {
+    float rs = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-            const bool ok = key < kend && (!CAUSAL || key <= qrow);
-            if (!ok) s[qb][kb][e] = -INFINITY;
-          }
+    for (int kb = 0; kb < NKB; ++kb) {
+      float x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = fast_exp2(fmaf(s[kb][e], p.c, -mb));
+        rs += x[e];
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 y;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) y[w] = N::pack2(x[8 * hf + 2 * w], x[8 * hf + 2 * w + 1]);
+        pf[kb * 2 + hf] = y;
       }
     }
+    return rs;
+  };
 
-    // Online softmax in base 2 with a lazily raised running max.
-    float mc[QB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+  // Softmax of one tile: fast path against the current reference; if any
+  // row's reference is still -inf or a partial sum exceeds the bound, raise
+  // the reference to the true running max, rescale O and l, and redo.
+  auto softmax = [&](const f32x16* s, u32x4* pf) {
+    float rs = probs(s, m, pf);
+    if (__builtin_amdgcn_ballot_w64(!(m > -INFINITY) || !(rs <= kMaxPartialSum))) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][kb][e]);
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
       mx = pair_max(mx);
-      mc[qb] = (mx == -INFINITY) ? -INFINITY : mx * p.c;
-      grow = grow || (mc[qb] > m[qb] + kLazyRescale);
+      const float mc = (mx == -INFINITY) ? -INFINITY : mx * p.c;
+      const float mnew = fmaxf(m, mc);
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      rs = probs(s, (m == -INFINITY) ? 0.f : m, pf);
     }
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mnew = fmaxf(m[qb], mc[qb]);
-        const float alpha = fast_exp2(m[qb] - ((mnew == -INFINITY) ? 0.f : mnew));
-        m[qb] = mnew;
-        l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
-      }
-    }
-    u32x4 pf[QB][NKC];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mb = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float sv = s[qb][kb][e];
-          float x = fast_exp2(fmaf(sv, p.c, -mb));
-          if (need_mask && sv == -INFINITY) x = 0.f;
-          s[qb][kb][e] = x;
-          rs += x;
-        }
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          u32x4 y;
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            y[w] = N::pack2(s[qb][kb][8 * hf + 2 * w], s[qb][kb][8 * hf + 2 * w + 1]);
-          pf[qb][kb * 2 + hf] = y;
-        }
-      }
-      l[qb] += rs;  // lane-partial: lane l^32 holds the row's other keys
-    }
+    l += rs;  // lane-partial: lane l^32 holds the row's other keys
+  };
 
-    // O^T += V^T P^T; V^T operands come from transposing reads of V.
+  // O^T += V^T P^T; V^T operands come from transposing reads of V.
+  auto pv = [&](const uint16_t* vs, const u32x4* pf) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int key = kc * 16 + v_key;
@@ -354,62 +385,80 @@ __global__ __launch_bounds__(NW * 64, QB == 1 ? 2 : 1) void attn_fwd_kernel(Para
         const u32x2 lo = lds_read_tr16(vs + key * D + off);
         const u32x2 hi = lds_read_tr16(vs + (key + 8) * D + off);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = N::mfma(a, pf[qb][kc], oacc[qb][db]);
+        oacc[db] = N::mfma(a, pf[kc], oacc[db]);
       }
     }
   };
 
+  // One pipeline step for tile t whose scores are in `s`; K_t and V_t sit in
+  // (kc, vc), tile t + 1 goes to (kn, vn).  LAST: no tile t + 1.
+  auto step = [&](auto last, int t, f32x16* s, f32x16* sn, uint16_t* kc, uint16_t* vc,
+                  uint16_t* kn, uint16_t* vn) {
+    constexpr bool LAST = decltype(last)::value;
+    mask(t, s);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!LAST) {
+      if (t + 2 < ntiles) issue(Kg, t + 2, kc, koff);
+      issue(Vg, t + 1, vn, voff);
+      qk(kn, sn);
+    }
+    u32x4 pf[NKC];
+    softmax(s, pf);
+    pv(vc, pf);
+  };
+  using Last = std::integral_constant<bool, true>;
+  using More = std::integral_constant<bool, false>;
+
+  f32x16 sa[NKB], sb[NKB];
   if (ntiles > 0) {
-    issue(kbeg, kbuf0, vbuf0);
+    issue(Kg, 0, kbuf0, koff);
+    issue(Vg, 0, vbuf0, voff);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
-  for (int t = 0; t < ntiles; t += 2) {
-    const int k0 = kbeg + t * BN;
-    if (t + 1 < ntiles) issue(k0 + BN, kbuf1, vbuf1);
-    compute(k0, kbuf0, vbuf0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) issue(k0 + 2 * BN, kbuf0, vbuf0);
-    compute(k0 + BN, kbuf1, vbuf1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (ntiles > 1) issue(Kg, 1, kbuf1, koff);
+    qk(kbuf0, sa);
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      step(More{}, t, sa, sb, kbuf0, vbuf0, kbuf1, vbuf1);
+      step(More{}, t + 1, sb, sa, kbuf1, vbuf1, kbuf0, vbuf0);
+    }
+    if (t + 1 < ntiles) {
+      step(More{}, t, sa, sb, kbuf0, vbuf0, kbuf1, vbuf1);
+      step(Last{}, t + 1, sb, sa, kbuf1, vbuf1, kbuf0, vbuf0);
+    } else {
+      step(Last{}, t, sa, sb, kbuf0, vbuf0, kbuf1, vbuf1);
+    }
   }
 
   // Epilogue: combine the two lane halves' row sums, normalise, store.
+  const float lt = pair_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  if (qrow < p.Nq) {
+    if (SPLIT) {
+      const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
+      float* dst = p.opart + prow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wq0 + qb * 32 + l32;
-    const float lt = pair_sum(l[qb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_v = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
-    if (qrow < p.Nq) {
-      if (SPLIT) {
-        const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
-        float* dst = p.opart + prow * D;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int i = 0; i < 4; ++i) {
+          f32x4 y = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
+                     oacc[db][4 * i + 3] * inv};
+          *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+        }
+      if (hl == 0) p.lsepart[prow] = lse_v;
+    } else {
+      uint16_t* dst = p.o + (qrow0 + qrow) * D;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f32x4 y = {oacc[qb][db][4 * i] * inv, oacc[qb][db][4 * i + 1] * inv,
-                       oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv};
-            *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-          }
-        if (hl == 0) p.lsepart[prow] = lse_v;
-      } else {
-        uint16_t* dst = p.o + (qrow0 + qrow) * D;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            u32x2 y = {N::pack2(oacc[qb][db][4 * i] * inv, oacc[qb][db][4 * i + 1] * inv),
-                       N::pack2(oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv)};
-            *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-          }
-        if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
-      }
+        for (int i = 0; i < 4; ++i) {
+          u32x2 y = {N::pack2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv),
+                     N::pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv)};
+          *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+        }
+      if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
     }
   }
 }
@@ -452,17 +501,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 
 // Tile table per head dimension.
 struct TileCfg {
-  int NW, QB, BN;
-  constexpr int BM() const { return NW * QB * 32; }
+  int NW, BN;
+  constexpr int BM() const { return NW * 32; }
 };
-#ifndef ATTN_D128_CFG
-#define ATTN_D128_CFG {4, 1, 64}
-#endif
-#ifndef ATTN_D64_CFG
-#define ATTN_D64_CFG {4, 1, 64}
-#endif
-constexpr TileCfg kCfgD64 = ATTN_D64_CFG;
-constexpr TileCfg kCfgD128 = ATTN_D128_CFG;
+constexpr TileCfg kCfgD64 = {4, 64};
+constexpr TileCfg kCfgD128 = {4, 64};
 constexpr int kResidentWgPerCu = 2;
 
 inline TileCfg cfg_for(int D) { return D == 64 ? kCfgD64 : kCfgD128; }
@@ -554,7 +597,7 @@ int choose_splits(int B, int Hq, int Nq, int Nkv, int D, int num_cus) {
 template <int D, class Tag, bool CAUSAL, bool SPLIT>
 hipError_t launch_main(const Params& p, hipStream_t stream) {
   constexpr TileCfg c = (D == 64) ? kCfgD64 : kCfgD128;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, SPLIT>), dim3(p.total),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.BN, SPLIT>), dim3(p.total),
                      dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -609,7 +652,10 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   p.n_splits = S;
   p.split_len = tiles_per_split * c.BN;
   p.rows = B * Hq * Nq;
-  p.c = fabsf(scale) * kLog2e;
+  // A masked score is -inf and must give a probability of exactly 0, so the
+  // factor applied to scores stays positive: for scale 0 every finite score
+  // times FLT_MIN rounds to a base-2 exponent of 0, as it should.
+  p.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
   const long long total = (long long)B * Hq * p.n_qtiles * S;
   if (total > INT32_MAX) return ATTN_EINVAL;
