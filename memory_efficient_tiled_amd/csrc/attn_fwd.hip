@@ -183,8 +183,10 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
                                            voff, 0, 0, 0);
 }
 
-// One workgroup: NW waves x 32 query rows, all on KV head hq / G, looping
-// over BN-key tiles of its key range.  K and V tiles go from HBM (mostly L2)
+// One workgroup: NW waves x QB x 32 query rows, all on KV head hq / G,
+// looping over BN-key tiles of its key range.  Each K or V operand read from
+// LDS feeds QB MFMAs (one per 32-row query block of the wave), so LDS read
+// traffic per flop falls as 1 / QB.  K and V tiles go from HBM (mostly L2)
 // straight into LDS, two buffers each, in a swizzled row-major layout:
 // 16-byte chunk c of key row r is stored at chunk c ^ k_swz(r) (K) or
 // c ^ v_swz(r) (V).
@@ -199,9 +201,10 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
 // The barrier also certifies that every wave has finished reading the
 // buffers the new copies overwrite (K_t in the previous step's product,
 // V_{t-1} in the previous step's P V).
-template <int D, class Tag, bool CAUSAL, int NW, int BN, bool SPLIT>
+template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
-  constexpr int BM = NW * 32;
+  constexpr int WR = QB * 32;           // query rows per wave
+  constexpr int BM = NW * WR;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // elements of one K (or V) tile
   constexpr int INSTR = BN * CPR / 64;  // 1 KB wave copies per tile
@@ -238,8 +241,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest causal rows first
   const int hk = hq / p.G;
   const int q0 = qt * BM;
-  const int wq0 = q0 + wave * 32;       // first query row of this wave
-  const int qrow = wq0 + l32;           // this lane's query row
+  const int wq0 = q0 + wave * WR;       // first query row of this wave
 
   const int kbeg = sp * p.split_len;
   int kend = min(p.Nkv, kbeg + p.split_len);
@@ -275,18 +277,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   };
 
   // Q^T operands for the whole key loop.
-  u32x4 qf[DC];
+  u32x4 qf[QB][DC];
 #pragma unroll
-  for (int kc = 0; kc < DC; ++kc) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qrow < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + qrow) * D + kc * 16 + hl * 8);
-    qf[kc] = x ^ p.qsign;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wq0 + qb * 32 + l32;
+#pragma unroll
+    for (int kc = 0; kc < DC; ++kc) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (row < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + row) * D + kc * 16 + hl * 8);
+      qf[qb][kc] = x ^ p.qsign;
+    }
   }
 
-  f32x16 oacc[NDB];
+  // O^T accumulators: block (qb, db) at oacc[qb * NDB + db].
+  f32x16 oacc[QB * NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  for (int i = 0; i < QB * NDB; ++i) oacc[i] = f32x16{};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
 
   // Lane-invariant parts of the V^T operand addresses.
   const int v_g = lane >> 4, v_r = lane & 15;
@@ -294,17 +306,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);  // column within a 32-wide block
   const int v_sw = v_swz<D>(v_key);               // same for key v_key + 16 kc (+ 8)
 
+  // Scores of a tile: s[qb * NKB + kb] (32 keys x 32 rows); probabilities
+  // pf[qb * NKC + kc] (16 keys x 32 rows, the P^T operands).
+
   // S^T = K Q^T for one tile, accumulated into s (zeroed here).
   auto qk = [&](const uint16_t* ks, f32x16* s) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int i = 0; i < QB * NKB; ++i) s[i] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int row = kb * 32 + l32;
         const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ k_swz<D>(row)) << 3));
-        s[kb] = N::mfma(a, qf[kc], s[kb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, qf[qb][kc], s[qb * NKB + kb]);
       }
     }
   };
@@ -316,26 +332,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     const bool need = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0);
     if (need) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = wq0 + qb * 32 + l32;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-          const bool ok = key < kend && (!CAUSAL || key <= qrow);
-          if (!ok) s[kb][e] = -INFINITY;
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+            const bool ok = key < kend && (!CAUSAL || key <= qrow);
+            if (!ok) s[qb * NKB + kb][e] = -INFINITY;
+          }
+      }
     }
   };
 
-  // Probabilities of one tile against reference max mb, packed as the P^T
-  // operands; returns the lane-partial row sum.
-  auto probs = [&](const f32x16* s, float mb, u32x4* pf) {
+  // Probabilities of query block qb of one tile against reference max mb,
+  // packed as its P^T operands; returns the lane-partial row sum.
+  auto probs = [&](const f32x16* s, int qb, float mb, u32x4* pf) {
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float x[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        x[e] = fast_exp2(fmaf(s[kb][e], p.c, -mb));
+        x[e] = fast_exp2(fmaf(s[qb * NKB + kb][e], p.c, -mb));
         rs += x[e];
       }
 #pragma unroll
@@ -343,34 +363,44 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         u32x4 y;
 #pragma unroll
         for (int w = 0; w < 4; ++w) y[w] = N::pack2(x[8 * hf + 2 * w], x[8 * hf + 2 * w + 1]);
-        pf[kb * 2 + hf] = y;
+        pf[qb * NKC + kb * 2 + hf] = y;
       }
     }
     return rs;
   };
 
-  // Softmax of one tile: fast path against the current reference; if any
+  // Softmax of one tile: fast path against the current references; if any
   // row's reference is still -inf or a partial sum exceeds the bound, raise
-  // the reference to the true running max, rescale O and l, and redo.
+  // the references to the true running max, rescale O and l, and redo.
   auto softmax = [&](const f32x16* s, u32x4* pf) {
-    float rs = probs(s, m, pf);
-    if (__builtin_amdgcn_ballot_w64(!(m > -INFINITY) || !(rs <= kMaxPartialSum))) {
-      float mx = -INFINITY;
+    float rs[QB];
+    bool bad = false;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-      mx = pair_max(mx);
-      const float mc = (mx == -INFINITY) ? -INFINITY : mx * p.c;
-      const float mnew = fmaxf(m, mc);
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      rs = probs(s, (m == -INFINITY) ? 0.f : m, pf);
+    for (int qb = 0; qb < QB; ++qb) {
+      rs[qb] = probs(s, qb, m[qb], pf);
+      bad = bad || !(m[qb] > -INFINITY) || !(rs[qb] <= kMaxPartialSum);
     }
-    l += rs;  // lane-partial: lane l^32 holds the row's other keys
+    if (__builtin_amdgcn_ballot_w64(bad)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb * NKB + kb][e]);
+        mx = pair_max(mx);
+        const float mc = (mx == -INFINITY) ? -INFINITY : mx * p.c;
+        const float mnew = fmaxf(m[qb], mc);
+        const float alpha = (m[qb] == -INFINITY) ? 0.f : fast_exp2(m[qb] - mnew);
+        m[qb] = mnew;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[qb * NDB + db] *= alpha;
+        rs[qb] = probs(s, qb, (mnew == -INFINITY) ? 0.f : mnew, pf);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] += rs[qb];  // lane-partial: lane l^32 holds the rest
   };
 
   // O^T += V^T P^T; V^T operands come from transposing reads of V.
@@ -385,7 +415,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
         const u32x2 lo = lds_read_tr16(vs + key * D + off);
         const u32x2 hi = lds_read_tr16(vs + (key + 8) * D + off);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = N::mfma(a, pf[kc], oacc[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb * NDB + db] = N::mfma(a, pf[qb * NKC + kc], oacc[qb * NDB + db]);
       }
     }
   };
@@ -403,14 +435,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
       issue(Vg, t + 1, vn, voff);
       qk(kn, sn);
     }
-    u32x4 pf[NKC];
+    u32x4 pf[QB * NKC];
     softmax(s, pf);
     pv(vc, pf);
   };
   using Last = std::integral_constant<bool, true>;
   using More = std::integral_constant<bool, false>;
 
-  f32x16 sa[NKB], sb[NKB];
+  f32x16 sa[QB * NKB], sb[QB * NKB];
   if (ntiles > 0) {
     issue(Kg, 0, kbuf0, koff);
     issue(Vg, 0, vbuf0, voff);
@@ -432,33 +464,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   }
 
   // Epilogue: combine the two lane halves' row sums, normalise, store.
-  const float lt = pair_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse_v = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
-  if (qrow < p.Nq) {
-    if (SPLIT) {
-      const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
-      float* dst = p.opart + prow * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = wq0 + qb * 32 + l32;
+    const float lt = pair_sum(l[qb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_v = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+    if (qrow < p.Nq) {
+      if (SPLIT) {
+        const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
+        float* dst = p.opart + prow * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 y = {oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
-                     oacc[db][4 * i + 3] * inv};
-          *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-        }
-      if (hl == 0) p.lsepart[prow] = lse_v;
-    } else {
-      uint16_t* dst = p.o + (qrow0 + qrow) * D;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+          for (int i = 0; i < 4; ++i) {
+            const f32x16& o = oacc[qb * NDB + db];
+            f32x4 y = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv, o[4 * i + 3] * inv};
+            *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+          }
+        if (hl == 0) p.lsepart[prow] = lse_v;
+      } else {
+        uint16_t* dst = p.o + (qrow0 + qrow) * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x2 y = {N::pack2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv),
-                     N::pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv)};
-          *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
-        }
-      if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x16& o = oacc[qb * NDB + db];
+            u32x2 y = {N::pack2(o[4 * i] * inv, o[4 * i + 1] * inv),
+                       N::pack2(o[4 * i + 2] * inv, o[4 * i + 3] * inv)};
+            *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+          }
+        if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
+      }
     }
   }
 }
@@ -499,16 +536,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // Host side.
 // ---------------------------------------------------------------------------
 
-// Tile table per head dimension.
+// Tile table: waves per workgroup, 32-row query blocks per wave, keys per
+// tile.  At D = 128 a wave holds 32 rows (the register file allows no
+// more at two waves per SIMD).  At D = 64 it can hold 64, which halves the
+// LDS and L2 traffic per flop; that pays when the 256-row workgroups still
+// give every CU two of them and no causal diagonal is wasted, otherwise the
+// 32-row tiles are faster.
 struct TileCfg {
-  int NW, BN;
-  constexpr int BM() const { return NW * 32; }
+  int NW, QB, BN;
+  constexpr int BM() const { return NW * QB * 32; }
 };
-constexpr TileCfg kCfgD64 = {4, 64};
-constexpr TileCfg kCfgD128 = {4, 64};
+enum { kCfgD64Narrow = 0, kCfgD64Wide = 1, kCfgD128 = 2 };
+constexpr TileCfg kCfgs[3] = {{4, 1, 64}, {4, 2, 32}, {4, 1, 64}};
 constexpr int kResidentWgPerCu = 2;
 
-inline TileCfg cfg_for(int D) { return D == 64 ? kCfgD64 : kCfgD128; }
+int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
+  if (D == 128) return kCfgD128;
+  const long long wide_wgs = (long long)B * Hq * ((Nq + kCfgs[kCfgD64Wide].BM() - 1) /
+                                                  kCfgs[kCfgD64Wide].BM());
+  const long long slots = (long long)kResidentWgPerCu * (num_cus > 0 ? num_cus : 256);
+  return (!causal && wide_wgs >= slots) ? kCfgD64Wide : kCfgD64Narrow;
+}
 
 thread_local int g_last_hip_error = 0;
 
@@ -581,8 +629,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
 
 // Split-KV count: enough workgroups for every CU to hold kResidentWgPerCu of
 // them, with each split keeping at least 8 key tiles.
-int choose_splits(int B, int Hq, int Nq, int Nkv, int D, int num_cus) {
-  const TileCfg c = cfg_for(D);
+int choose_splits(const TileCfg& c, int B, int Hq, int Nq, int Nkv, int num_cus) {
   const long long wgs = (long long)B * Hq * ((Nq + c.BM() - 1) / c.BM());
   const long long target = (long long)kResidentWgPerCu * (num_cus > 0 ? num_cus : 256);
   if (wgs >= target) return 1;
@@ -594,19 +641,30 @@ int choose_splits(int B, int Hq, int Nq, int Nkv, int D, int num_cus) {
   return s < 1 ? 1 : (int)s;
 }
 
-template <int D, class Tag, bool CAUSAL, bool SPLIT>
+template <int D, int CFG, class Tag, bool CAUSAL, bool SPLIT>
 hipError_t launch_main(const Params& p, hipStream_t stream) {
-  constexpr TileCfg c = (D == 64) ? kCfgD64 : kCfgD128;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.BN, SPLIT>), dim3(p.total),
+  constexpr TileCfg c = kCfgs[CFG];
+  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, SPLIT>), dim3(p.total),
                      dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, class Tag>
+template <int D, int CFG, class Tag>
 hipError_t dispatch(const Params& p, bool causal, bool split, hipStream_t st) {
   if (causal)
-    return split ? launch_main<D, Tag, true, true>(p, st) : launch_main<D, Tag, true, false>(p, st);
-  return split ? launch_main<D, Tag, false, true>(p, st) : launch_main<D, Tag, false, false>(p, st);
+    return split ? launch_main<D, CFG, Tag, true, true>(p, st)
+                 : launch_main<D, CFG, Tag, true, false>(p, st);
+  return split ? launch_main<D, CFG, Tag, false, true>(p, st)
+               : launch_main<D, CFG, Tag, false, false>(p, st);
+}
+
+// The wide D = 64 tiles are only selected without a causal mask.
+template <class Tag>
+hipError_t dispatch64(const Params& p, int cfg, bool causal, bool split, hipStream_t st) {
+  if (cfg == kCfgD64Wide && !causal)
+    return split ? launch_main<64, kCfgD64Wide, Tag, false, true>(p, st)
+                 : launch_main<64, kCfgD64Wide, Tag, false, false>(p, st);
+  return dispatch<64, kCfgD64Narrow, Tag>(p, causal, split, st);
 }
 
 template <int D, class Tag>
@@ -628,9 +686,10 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   rc = device_info(&di);
   if (rc != ATTN_OK) return rc;
 
-  const TileCfg c = cfg_for(D);
+  const int cfg = select_cfg(B, Hq, Nq, D, causal, di.cus);
+  const TileCfg c = kCfgs[cfg];
   const int ktiles = (Nkv + c.BN - 1) / c.BN;
-  int S = num_splits > 0 ? num_splits : choose_splits(B, Hq, Nq, Nkv, D, di.cus);
+  int S = num_splits > 0 ? num_splits : choose_splits(c, B, Hq, Nq, Nkv, di.cus);
   if (S > ktiles) S = ktiles;
   const int tiles_per_split = (ktiles + S - 1) / S;
   S = (ktiles + tiles_per_split - 1) / tiles_per_split;  // drop empty trailing splits
@@ -678,11 +737,11 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   hipError_t e;
   const bool cz = causal != 0;
   if (D == 64)
-    e = dtype == ATTN_BF16 ? dispatch<64, TagBF16>(p, cz, split, stream)
-                           : dispatch<64, TagF16>(p, cz, split, stream);
+    e = dtype == ATTN_BF16 ? dispatch64<TagBF16>(p, cfg, cz, split, stream)
+                           : dispatch64<TagF16>(p, cfg, cz, split, stream);
   else
-    e = dtype == ATTN_BF16 ? dispatch<128, TagBF16>(p, cz, split, stream)
-                           : dispatch<128, TagF16>(p, cz, split, stream);
+    e = dtype == ATTN_BF16 ? dispatch<128, kCfgD128, TagBF16>(p, cz, split, stream)
+                           : dispatch<128, kCfgD128, TagF16>(p, cz, split, stream);
   if (e == hipSuccess && split) {
     if (D == 64)
       e = dtype == ATTN_BF16 ? launch_combine<64, TagBF16>(p, stream)
@@ -730,9 +789,9 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int caus
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
   if ((D != 64 && D != 128) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
   if (causal != 0 && causal != 1) return ATTN_EINVAL;
-  const TileCfg c = cfg_for(D);
+  const TileCfg c = kCfgs[select_cfg(B, Hq, Nq, D, causal, num_cus)];
   const int ktiles = (Nkv + c.BN - 1) / c.BN;
-  int S = choose_splits(B, Hq, Nq, Nkv, D, num_cus);
+  int S = choose_splits(c, B, Hq, Nq, Nkv, num_cus);
   if (S > ktiles) S = ktiles;
   const int tps = (ktiles + S - 1) / S;
   return (ktiles + tps - 1) / tps;

@@ -107,6 +107,23 @@ def test_scale_values(gpu_device, scale):
           scale=scale)
 
 
+# -- the 64-row tiles of D = 64 --------------------------------------------
+# Chosen for non-causal D = 64 grids of at least two 256-row workgroups per
+# CU (here 2 x 32 heads x 9 query tiles = 576 on 256 CUs): ragged query and
+# key tails, GQA, Nq != Nkv, both dtypes, forced splits.
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+@pytest.mark.parametrize("nkv", [33, 700, 2100])
+def test_wide_d64_tiles(gpu_device, nkv, dtype):
+    _case(gpu_device, 2, 32, 8, 2100, nkv, 64, dtype, False, seed=nkv, rows=24)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_wide_d64_tiles_split(gpu_device, splits):
+    _case(gpu_device, 2, 32, 8, 2100, 2000, 64, inputs.F16, False, seed=11,
+          rows=24, num_splits=splits)
+
+
 # -- exact properties --------------------------------------------------------
 
 def _dev(x, dtype, device):
