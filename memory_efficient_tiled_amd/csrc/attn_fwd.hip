@@ -144,17 +144,25 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS layouts of the K and V tiles (16-byte units, CPR = D / 8 per row).
-// gfx950 serves a 16-byte LDS read 16 lanes (256 bytes, all 64 banks) at a
-// time and an 8-byte read 32 lanes at a time, so a read is conflict-free
-// when those lanes cover 256 contiguous bytes.
-//   K: unit (key / 16, chunk, key % 16).  A K operand read (16 lanes: 16
-//      consecutive keys, one chunk) is 256 contiguous bytes.
-//   V: unit (chunk / 4, key, chunk % 4): 32-column blocks of 64-byte rows.
-//      A transposing V^T operand read (32 lanes: 4 consecutive keys x 64
-//      bytes) is 256 contiguous bytes.
-// Every operand of a tile is one per-lane base address plus an immediate,
-// and each 1 KB copy instruction reads 64 contiguous bytes from 16 rows.
+// LDS swizzles.  gfx950 serves a 16-byte LDS read 16 lanes (256 bytes, all
+// 64 banks) at a time and an 8-byte read 32 lanes at a time, so a pattern is
+// conflict-free when those lanes cover 16 distinct 16-byte bank groups.
+//  * K operand reads: the 16 lanes of a group read the same chunk of 16
+//    consecutive key rows.  With 256-byte rows (D = 128) the chunk is XORed
+//    with r & 15; with 128-byte rows (D = 64) two rows share the 64 banks and
+//    the chunk is XORed with (r >> 1) & 7.
+//  * V^T operand reads (transposing, 8 bytes per lane): 32 lanes read 4 keys
+//    x 64 contiguous bytes.  With 256-byte rows the 4 keys go to 4 disjoint
+//    64-byte quarters (XOR 4 * (r & 3)); with 128-byte rows keys r and r + 2
+//    share banks and are separated by XOR 4 * ((r >> 1) & 1).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 // Probabilities are formed against a running reference max m that is only
 // raised when a tile would otherwise produce a probability above 2^8: the
@@ -179,7 +187,9 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
 // looping over BN-key tiles of its key range.  Each K or V operand read from
 // LDS feeds QB MFMAs (one per 32-row query block of the wave), so LDS read
 // traffic per flop falls as 1 / QB.  K and V tiles go from HBM (mostly L2)
-// straight into LDS, two buffers each, in the layouts above.
+// straight into LDS, two buffers each, in a swizzled row-major layout:
+// 16-byte chunk c of key row r is stored at chunk c ^ k_swz(r) (K) or
+// c ^ v_swz(r) (V).
 //
 // Software pipeline, one barrier per key tile t (scores S_t already in
 // registers when the step starts):
@@ -243,16 +253,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   const uint16_t* Kg = p.k + krow0 * D;
   const uint16_t* Vg = p.v + krow0 * D;
 
-  // Global byte offsets (within a tile, the same for every tile) of the
-  // 16-byte units this lane copies: LDS unit u of this wave's copies.
+  // Per-lane byte offsets of this wave's copy slots within a tile (the same
+  // for every tile) and the LDS slot each copy fills.
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int u = (wave * IPW + j) * 64 + lane;
-    const int kr = (u / (CPR * 16)) * 16 + (u & 15), kch = (u / 16) % CPR;
-    const int vr = (u % (BN * 4)) / 4, vch = (u / (BN * 4)) * 4 + (u & 3);
-    koff[j] = kr * ROWB + kch * 16;
-    voff[j] = vr * ROWB + vch * 16;
+    const int slot = (wave * IPW + j) * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    koff[j] = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
+    voff[j] = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
   }
   // Copy tile `t` of K (or V) into LDS.  The buffer ends at the last key, so
   // rows past it read as zero: their scores are masked to -inf and their V
@@ -291,14 +300,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     l[qb] = 0.f;
   }
 
-  // Per-lane element offsets of the K operand (chunk 2 kc + hl of key
-  // 32 kb + l32) and of the V^T operand (key 16 kc + v_key (+ 8), column
-  // 32 db + v_d .. + 3); the rest of each address is an immediate.
+  // Lane-invariant parts of the V^T operand addresses.
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);          // key within a 16-key chunk (first half)
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);  // column within a 32-wide block
-  const int k_lane = ((l32 >> 4) * CPR * 16 + hl * 16 + (l32 & 15)) * 8;
-  const int v_lane = v_key * 32 + v_d;
+  const int v_sw = v_swz<D>(v_key);               // same for key v_key + 16 kc (+ 8)
 
   // Scores of a tile: s[qb * NKB + kb] (32 keys x 32 rows); probabilities
   // pf[qb * NKC + kc] (16 keys x 32 rows, the P^T operands).
@@ -311,7 +317,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
     for (int kc = 0; kc < DC; ++kc) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 a = *(const u32x4*)(ks + k_lane + kb * 2 * CPR * 128 + kc * 256);
+        const int row = kb * 32 + l32;
+        const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ k_swz<D>(row)) << 3));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, qf[qb][kc], s[qb * NKB + kb]);
       }
@@ -400,11 +407,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
   auto pv = [&](const uint16_t* vs, const u32x4* pf) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
+      const int key = kc * 16 + v_key;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* va = vs + v_lane + db * BN * 32 + kc * 512;
-        const u32x2 lo = lds_read_tr16(va);
-        const u32x2 hi = lds_read_tr16(va + 256);
+        const int d = db * 32 + v_d;
+        const int off = (((d >> 3) ^ v_sw) << 3) + (d & 7);
+        const u32x2 lo = lds_read_tr16(vs + key * D + off);
+        const u32x2 hi = lds_read_tr16(vs + (key + 8) * D + off);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
