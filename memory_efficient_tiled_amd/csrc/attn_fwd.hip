@@ -176,6 +176,10 @@ constexpr float kMaxPartialSum = 256.0f;
 // Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9.
 constexpr int kRawBufferFlags = 0x00020000;
 
+// Waves per SIMD that every kernel is compiled for: each wave may use up to
+// 256 of the SIMD's 512 vector registers (arch + accumulation).
+constexpr int kWavesPerSimd = 2;
+
 // Copy 16 bytes per lane from a buffer into LDS: lane i writes lds + 16 i
 // (lds wave-uniform).  Offsets at or beyond the buffer's size read zero.
 __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
@@ -202,7 +206,7 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
 // buffers the new copies overwrite (K_t in the previous step's product,
 // V_{t-1} in the previous step's P V).
 template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
   constexpr int WR = QB * 32;           // query rows per wave
   constexpr int BM = NW * WR;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
@@ -537,24 +541,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 
 // Tile table: waves per workgroup, 32-row query blocks per wave, keys per
-// tile.  At D = 128 a wave holds 32 rows (the register file allows no
-// more at two waves per SIMD).  At D = 64 it can hold 64, which halves the
-// LDS and L2 traffic per flop; that pays when the 256-row workgroups still
-// give every CU two of them and no causal diagonal is wasted, otherwise the
-// 32-row tiles are faster.
+// tile.  Every kernel runs two waves per SIMD (8 per CU), so a CU holds
+// 8 / NW workgroups.  At D = 128 a wave holds 32 rows (the register file
+// allows no more at two waves per SIMD) and the workgroup has 8 waves: each
+// K/V tile copied into LDS then serves 256 query rows, which halves the
+// L2 -> LDS traffic of a 4-wave workgroup.  At D = 64 a wave can hold 64
+// rows, which halves the LDS and L2 traffic per flop; that pays when the
+// 256-row workgroups still give every CU two of them and no causal diagonal
+// is wasted, otherwise the 32-row tiles are faster.
 struct TileCfg {
   int NW, QB, BN;
   constexpr int BM() const { return NW * QB * 32; }
+  constexpr int resident_per_cu() const { return 4 * kWavesPerSimd / NW; }
 };
 enum { kCfgD64Narrow = 0, kCfgD64Wide = 1, kCfgD128 = 2 };
-constexpr TileCfg kCfgs[3] = {{4, 1, 64}, {4, 2, 32}, {4, 1, 64}};
-constexpr int kResidentWgPerCu = 2;
+constexpr TileCfg kCfgs[3] = {{4, 1, 64}, {4, 2, 32}, {8, 1, 64}};
 
 int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
   if (D == 128) return kCfgD128;
-  const long long wide_wgs = (long long)B * Hq * ((Nq + kCfgs[kCfgD64Wide].BM() - 1) /
-                                                  kCfgs[kCfgD64Wide].BM());
-  const long long slots = (long long)kResidentWgPerCu * (num_cus > 0 ? num_cus : 256);
+  const TileCfg& w = kCfgs[kCfgD64Wide];
+  const long long wide_wgs = (long long)B * Hq * ((Nq + w.BM() - 1) / w.BM());
+  const long long slots = (long long)w.resident_per_cu() * (num_cus > 0 ? num_cus : 256);
   return (!causal && wide_wgs >= slots) ? kCfgD64Wide : kCfgD64Narrow;
 }
 
@@ -627,11 +634,11 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
   return ATTN_OK;
 }
 
-// Split-KV count: enough workgroups for every CU to hold kResidentWgPerCu of
-// them, with each split keeping at least 8 key tiles.
+// Split-KV count: enough workgroups for every CU to hold as many as are
+// resident at once, with each split keeping at least 8 key tiles.
 int choose_splits(const TileCfg& c, int B, int Hq, int Nq, int Nkv, int num_cus) {
   const long long wgs = (long long)B * Hq * ((Nq + c.BM() - 1) / c.BM());
-  const long long target = (long long)kResidentWgPerCu * (num_cus > 0 ? num_cus : 256);
+  const long long target = (long long)c.resident_per_cu() * (num_cus > 0 ? num_cus : 256);
   if (wgs >= target) return 1;
   const int ktiles = (Nkv + c.BN - 1) / c.BN;
   long long s = (target + wgs - 1) / wgs;
