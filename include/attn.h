@@ -66,11 +66,13 @@ enum {
  * dtype   : ATTN_F16 or ATTN_BF16.
  * stream  : hipStream_t to launch on.
  *
- * Short query ranges over long key ranges are split over key ranges
- * (split-KV); the partial results are merged by their log-sum-exp.  The
- * split path takes a workspace of attn_fwd_workspace_bytes() bytes with
- * hipMallocAsync/hipFreeAsync on `stream`; with one split nothing is
- * allocated.
+ * Query rows are processed in tiles of attn_plan.tile_rows rows.  Where
+ * the tiles cannot keep every compute unit busy -- a grid smaller than the
+ * device, or, without a mask, the last partial round of a grid that fills it
+ * -- those tiles are split over key ranges (split-KV) and the pieces merged
+ * by their log-sum-exp.  Pieces take a workspace of
+ * attn_plan.workspace_bytes bytes from hipMallocAsync/hipFreeAsync on
+ * `stream`; when nothing is split nothing is allocated.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nkv, int D,
@@ -78,9 +80,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 
 /*
  * attn_fwd_split -- attn_fwd with the split-KV count chosen by the caller.
- * num_splits = 0 picks it as attn_fwd does; a positive value is clamped to
- * the number of key tiles.  Every split count computes the same function;
- * results differ only by fp32 rounding order.
+ * num_splits = 0 plans as attn_fwd does; a positive value splits every
+ * query tile into that many key ranges (clamped to the number of key
+ * tiles).  Every split count computes the same function; results differ
+ * only by fp32 rounding order.
  */
 int attn_fwd_split(const void* q, const void* k, const void* v, void* out,
                    float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
@@ -96,17 +99,41 @@ int attn_fwd_check(const void* q, const void* k, const void* v, const void* out,
                    int D, float scale, int causal, int dtype);
 
 /*
- * attn_fwd_num_splits -- host only: the split-KV count attn_fwd would use
- * for this shape on a device with `num_cus` compute units (256 on MI355X).
+ * attn_plan -- how attn_fwd_split covers a shape (see attn_fwd_plan).
+ * Output rows are numbered (b * Hq + h) * Nq + i, 0 <= r < B*Hq*Nq.
+ */
+typedef struct attn_plan {
+  int tile_rows;          /* query rows per workgroup tile */
+  int num_splits;         /* key-range pieces per split tile; 1 = no split */
+  long long split_rows;   /* rows [B*Hq*Nq - split_rows, B*Hq*Nq) are merged
+                             from pieces (0 when num_splits == 1) */
+  size_t workspace_bytes; /* device bytes allocated per call: fp32 partial
+                             outputs [num_splits, split_rows, D] and LSE
+                             [num_splits, split_rows] */
+} attn_plan;
+
+/*
+ * attn_fwd_plan -- host only: fills *plan with what attn_fwd_split (same
+ * num_splits; 0 = as attn_fwd) does for this shape on a device with
+ * `num_cus` compute units (256 on MI355X; <= 0 means 256).  Returns ATTN_OK,
+ * or ATTN_EINVAL for invalid shapes, a negative num_splits or a NULL plan.
+ */
+int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal,
+                  int dtype, int num_splits, int num_cus, attn_plan* plan);
+
+/*
+ * attn_fwd_num_splits -- host only: attn_fwd_plan(..., 0, num_cus)'s
+ * num_splits, the split-KV count attn_fwd uses for the tiles it splits.
  * Returns >= 1, or ATTN_EINVAL for invalid shapes.
  */
 int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                         int causal, int dtype, int num_cus);
 
 /*
- * attn_fwd_workspace_bytes -- host only: device bytes the split path
- * allocates for `num_splits` splits (0 when num_splits <= 1): fp32 partial
- * outputs [num_splits,B,Hq,Nq,D] and partial LSE [num_splits,B,Hq,Nq].
+ * attn_fwd_workspace_bytes -- host only: device bytes for splitting every
+ * row into `num_splits` pieces (0 when num_splits <= 1): fp32 partial
+ * outputs [num_splits,B,Hq,Nq,D] and partial LSE [num_splits,B,Hq,Nq].  An
+ * upper bound of attn_plan.workspace_bytes for the same num_splits.
  */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
                                 int num_splits);

@@ -4,8 +4,9 @@ The compute path is the HIP library ``libattn.so`` (built from ``csrc/``);
 this package only marshals arguments to its C entry points.
 """
 from .binding import (attn_fwd, attn_fwd_check, attn_fwd_num_splits,
-                      attn_fwd_workspace_bytes, lib_path, load_library,
-                      AttnError)
+                      attn_fwd_plan, attn_fwd_workspace_bytes, lib_path,
+                      load_library, AttnError, AttnPlan)
 
 __all__ = ["attn_fwd", "attn_fwd_check", "attn_fwd_num_splits",
-           "attn_fwd_workspace_bytes", "lib_path", "load_library", "AttnError"]
+           "attn_fwd_plan", "attn_fwd_workspace_bytes", "lib_path",
+           "load_library", "AttnError", "AttnPlan"]

@@ -27,6 +27,14 @@ ATTN_EHIP = -4
 _lib = None
 
 
+class AttnPlan(ctypes.Structure):
+    """struct attn_plan: how the library covers a shape (see attn_fwd_plan)."""
+    _fields_ = [("tile_rows", ctypes.c_int),
+                ("num_splits", ctypes.c_int),
+                ("split_rows", ctypes.c_longlong),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 class AttnError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"attn error {code}: {msg}")
@@ -63,6 +71,9 @@ def load_library():
     lib.attn_fwd_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
         [ctypes.c_float, _INT, _INT]
     lib.attn_fwd_check.restype = _INT
+    lib.attn_fwd_plan.argtypes = shape_args + [_INT, _INT, _INT, _INT,
+                                               ctypes.POINTER(AttnPlan)]
+    lib.attn_fwd_plan.restype = _INT
     lib.attn_fwd_num_splits.argtypes = shape_args + [_INT, _INT, _INT]
     lib.attn_fwd_num_splits.restype = _INT
     lib.attn_fwd_workspace_bytes.argtypes = [_INT, _INT, _INT, _INT, _INT, _INT]
@@ -105,6 +116,19 @@ def attn_fwd_num_splits(B, Hq, Hkv, Nq, Nkv, D, causal, dtype_code,
     """The split-KV count the library picks for this shape (host-only)."""
     return load_library().attn_fwd_num_splits(B, Hq, Hkv, Nq, Nkv, D,
                                               int(causal), dtype_code, num_cus)
+
+
+def attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype_code, num_splits=0,
+                  num_cus=256) -> AttnPlan:
+    """How the library covers this shape: rows per tile, split count, the
+    rows merged from split pieces and the workspace bytes (host-only)."""
+    plan = AttnPlan()
+    rc = load_library().attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, int(causal),
+                                      dtype_code, num_splits, num_cus,
+                                      ctypes.byref(plan))
+    if rc != ATTN_OK:
+        _raise(rc)
+    return plan
 
 
 def attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, num_splits) -> int:

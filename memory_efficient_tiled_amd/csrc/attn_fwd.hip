@@ -97,11 +97,13 @@ struct Params {
   const uint16_t* v;
   uint16_t* o;        // final output (non-split) or unused
   float* lse;         // final LSE (non-split), may be null
-  float* opart;       // split: [S][B*Hq*Nq][D] fp32
-  float* lsepart;     // split: [S][B*Hq*Nq]
+  float* opart;       // split: [S][prows][D] fp32, rows from row0 on
+  float* lsepart;     // split: [S][prows]
   int Hq, Nq, Nkv, G, Hkv;
-  int n_qtiles, n_splits, split_len, total;
-  int rows;           // B*Hq*Nq
+  int n_qtiles, n_splits, split_len;
+  int total;          // workgroups of this launch
+  int tile0;          // first query tile of this launch
+  int row0, prows;    // split: output rows [row0, row0 + prows) have partials
   float c;            // |scale| * log2(e)
   uint32_t qsign;     // 0x80008000 flips the sign of Q (negative scale)
 };
@@ -238,6 +240,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     sp = bid % p.n_splits;
     bid /= p.n_splits;
   }
+  bid += p.tile0;
   int qt = bid % p.n_qtiles;
   bid /= p.n_qtiles;
   const int hq = bid % p.Hq;
@@ -247,8 +250,9 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const int q0 = qt * BM;
   const int wq0 = q0 + wave * WR;       // first query row of this wave
 
-  const int kbeg = sp * p.split_len;
-  int kend = min(p.Nkv, kbeg + p.split_len);
+  // A split launch covers one key range per piece; otherwise every key.
+  const int kbeg = SPLIT ? sp * p.split_len : 0;
+  int kend = SPLIT ? min(p.Nkv, kbeg + p.split_len) : p.Nkv;
   if (CAUSAL) kend = min(kend, q0 + BM);  // keys past the tile's last row are all masked
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     const float lse_v = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
     if (qrow < p.Nq) {
       if (SPLIT) {
-        const size_t prow = (size_t)sp * p.rows + qrow0 + qrow;
+        const size_t prow = (size_t)sp * p.prows + (qrow0 + qrow - p.row0);
         float* dst = p.opart + prow * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -505,12 +509,13 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 }
 
 // Merge split-KV partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
+// Partial row r belongs to output row row0 + r.
 template <int D, class Tag>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
                                                            const float* __restrict__ lsepart,
                                                            uint16_t* __restrict__ o,
                                                            float* __restrict__ lse, int rows,
-                                                           int n_splits) {
+                                                           int row0, int n_splits) {
   using N = Num<Tag>;
   constexpr int C4 = D / 4;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -532,8 +537,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   u32x2 y = {N::pack2(acc[0] * inv, acc[1] * inv), N::pack2(acc[2] * inv, acc[3] * inv)};
-  *(u32x2*)(o + row * D + c4 * 4) = y;
-  if (c4 == 0 && lse) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  *(u32x2*)(o + (row0 + row) * D + c4 * 4) = y;
+  if (c4 == 0 && lse) lse[row0 + row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -634,18 +639,98 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
   return ATTN_OK;
 }
 
-// Split-KV count: enough workgroups for every CU to hold as many as are
-// resident at once, with each split keeping at least 8 key tiles.
-int choose_splits(const TileCfg& c, int B, int Hq, int Nq, int Nkv, int num_cus) {
-  const long long wgs = (long long)B * Hq * ((Nq + c.BM() - 1) / c.BM());
-  const long long target = (long long)c.resident_per_cu() * (num_cus > 0 ? num_cus : 256);
-  if (wgs >= target) return 1;
-  const int ktiles = (Nkv + c.BN - 1) / c.BN;
-  long long s = (target + wgs - 1) / wgs;
-  const long long by_keys = ktiles / 8;
-  if (s > by_keys) s = by_keys;
-  if (s > 64) s = 64;
+// How one call covers its query tiles (tile index (b * Hq + h) * n_qtiles +
+// qt): tiles [0, first_split) run whole in a launch that writes the output
+// directly; the key range of each tile in [first_split, tiles) is cut into
+// `splits` pieces of `split_len` keys, computed by a second launch into fp32
+// partials and merged by their log-sum-exp.  Those tiles are the last ones,
+// so their rows are one contiguous range [row0, rows).
+struct Plan {
+  int cfg;
+  int D;
+  int n_qtiles;
+  int splits;
+  int split_len;
+  long long tiles;
+  long long first_split;
+  long long row0, rows;
+  size_t workspace_bytes() const {
+    return splits > 1 ? (size_t)splits * (size_t)(rows - row0) * (D + 1) * sizeof(float) : 0;
+  }
+};
+
+// Cost model for cutting `rem` equal tiles of `ktiles` key steps into s
+// pieces on `slots` workgroup slots, in key steps of one workgroup: the
+// pieces run in ceil(s * rem / slots) rounds, each piece spends about
+// kPieceFillSteps steps filling its pipeline and writing fp32 partials, and
+// the merge streams ~8 (D + 1) bytes per row and piece through HBM, about
+// kMergeStepsPerPiece steps of the whole chip per tile and piece (a 64-key
+// step of a 256-row tile is ~8 MFLOP, ~2 us on one CU).
+constexpr double kPieceFillSteps = 2.0;
+constexpr double kMergeStepsPerPiece = 0.03;
+constexpr int kMaxSplits = 64;
+constexpr int kMinStepsPerPiece = 8;
+
+int balanced_splits(long long rem, long long slots, int ktiles) {
+  int best = 1;
+  double best_cost = (double)((rem + slots - 1) / slots) * ktiles;
+  const int smax = std::min(kMaxSplits, ktiles / kMinStepsPerPiece);
+  for (int s = 2; s <= smax; ++s) {
+    const int steps = (ktiles + s - 1) / s;
+    const double rounds = (double)((s * rem + slots - 1) / slots);
+    const double cost = rounds * (steps + kPieceFillSteps) + kMergeStepsPerPiece * s * rem;
+    if (cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+// Causal tiles differ in length and are launched longest first, so the
+// hardware's dynamic dispatch balances them; only a grid smaller than the
+// chip is split, into enough pieces to fill every slot.
+int causal_splits(long long tiles, long long slots, int ktiles) {
+  if (tiles >= slots) return 1;
+  long long s = (slots + tiles - 1) / tiles;
+  s = std::min<long long>(s, std::min(kMaxSplits, ktiles / kMinStepsPerPiece));
   return s < 1 ? 1 : (int)s;
+}
+
+// num_splits > 0 cuts every tile into that many pieces (at most one per key
+// tile).  Otherwise, without a mask, the grid runs in rounds of `slots`
+// equal workgroups and only the tiles of the last, partial round are cut,
+// so that they finish in a fraction of a round.
+Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int num_cus) {
+  Plan pl;
+  pl.cfg = select_cfg(B, Hq, Nq, D, causal, num_cus);
+  pl.D = D;
+  const TileCfg c = kCfgs[pl.cfg];
+  pl.n_qtiles = (Nq + c.BM() - 1) / c.BM();
+  pl.tiles = (long long)B * Hq * pl.n_qtiles;
+  pl.rows = (long long)B * Hq * Nq;
+  const long long slots = (long long)c.resident_per_cu() * (num_cus > 0 ? num_cus : 256);
+  const int ktiles = (Nkv + c.BN - 1) / c.BN;
+  long long first = 0;
+  int S;
+  if (num_splits > 0) {
+    S = num_splits;
+  } else if (causal) {
+    S = causal_splits(pl.tiles, slots, ktiles);
+  } else {
+    const long long rem = pl.tiles % slots;
+    first = pl.tiles - rem;
+    S = rem ? balanced_splits(rem, slots, ktiles) : 1;
+  }
+  if (S > ktiles) S = ktiles;
+  const int tps = (ktiles + S - 1) / S;
+  S = (ktiles + tps - 1) / tps;  // drop empty trailing pieces
+  pl.splits = S;
+  pl.split_len = tps * c.BN;
+  pl.first_split = S > 1 ? first : pl.tiles;
+  const long long bh = pl.first_split / pl.n_qtiles, qt = pl.first_split % pl.n_qtiles;
+  pl.row0 = S > 1 ? bh * Nq + qt * c.BM() : pl.rows;
+  return pl;
 }
 
 template <int D, int CFG, class Tag, bool CAUSAL, bool SPLIT>
@@ -676,10 +761,10 @@ hipError_t dispatch64(const Params& p, int cfg, bool causal, bool split, hipStre
 
 template <int D, class Tag>
 hipError_t launch_combine(const Params& p, hipStream_t st) {
-  const size_t threads = (size_t)p.rows * (D / 4);
+  const size_t threads = (size_t)p.prows * (D / 4);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL((attn_combine_kernel<D, Tag>), dim3(blocks), dim3(256), 0, st, p.opart,
-                     p.lsepart, p.o, p.lse, p.rows, p.n_splits);
+                     p.lsepart, p.o, p.lse, p.prows, p.row0, p.n_splits);
   return hipGetLastError();
 }
 
@@ -693,13 +778,9 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   rc = device_info(&di);
   if (rc != ATTN_OK) return rc;
 
-  const int cfg = select_cfg(B, Hq, Nq, D, causal, di.cus);
-  const TileCfg c = kCfgs[cfg];
-  const int ktiles = (Nkv + c.BN - 1) / c.BN;
-  int S = num_splits > 0 ? num_splits : choose_splits(c, B, Hq, Nq, Nkv, di.cus);
-  if (S > ktiles) S = ktiles;
-  const int tiles_per_split = (ktiles + S - 1) / S;
-  S = (ktiles + tiles_per_split - 1) / tiles_per_split;  // drop empty trailing splits
+  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, causal, num_splits, di.cus);
+  const long long split_wgs = (pl.tiles - pl.first_split) * pl.splits;
+  if (pl.first_split > INT32_MAX || split_wgs > INT32_MAX) return ATTN_EINVAL;
 
   Params p;
   p.q = (const uint16_t*)q;
@@ -714,48 +795,55 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   p.Nkv = Nkv;
   p.G = Hq / Hkv;
   p.Hkv = Hkv;
-  p.n_qtiles = (Nq + c.BM() - 1) / c.BM();
-  p.n_splits = S;
-  p.split_len = tiles_per_split * c.BN;
-  p.rows = B * Hq * Nq;
+  p.n_qtiles = pl.n_qtiles;
+  p.n_splits = pl.splits;
+  p.split_len = pl.split_len;
+  p.row0 = (int)pl.row0;
+  p.prows = (int)(pl.rows - pl.row0);
   // A masked score is -inf and must give a probability of exactly 0, so the
   // factor applied to scores stays positive: for scale 0 every finite score
   // times FLT_MIN rounds to a base-2 exponent of 0, as it should.
   p.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
-  const long long total = (long long)B * Hq * p.n_qtiles * S;
-  if (total > INT32_MAX) return ATTN_EINVAL;
-  p.total = (int)total;
 
-  const bool split = S > 1;
   void* ws = nullptr;
-  if (split) {
-    const size_t bytes = attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, S);
-    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  if (split_wgs > 0) {
+    hipError_t e = hipMallocAsync(&ws, pl.workspace_bytes(), stream);
     if (e != hipSuccess || !ws) {
       g_last_hip_error = (int)e;
       (void)hipGetLastError();
       return ATTN_ENOMEM;
     }
     p.opart = (float*)ws;
-    p.lsepart = p.opart + (size_t)S * p.rows * D;
+    p.lsepart = p.opart + (size_t)pl.splits * p.prows * D;
   }
 
-  hipError_t e;
   const bool cz = causal != 0;
-  if (D == 64)
-    e = dtype == ATTN_BF16 ? dispatch64<TagBF16>(p, cfg, cz, split, stream)
-                           : dispatch64<TagF16>(p, cfg, cz, split, stream);
-  else
-    e = dtype == ATTN_BF16 ? dispatch<128, kCfgD128, TagBF16>(p, cz, split, stream)
-                           : dispatch<128, kCfgD128, TagF16>(p, cz, split, stream);
-  if (e == hipSuccess && split) {
+  auto launch = [&](bool split) {
     if (D == 64)
-      e = dtype == ATTN_BF16 ? launch_combine<64, TagBF16>(p, stream)
-                             : launch_combine<64, TagF16>(p, stream);
-    else
-      e = dtype == ATTN_BF16 ? launch_combine<128, TagBF16>(p, stream)
-                             : launch_combine<128, TagF16>(p, stream);
+      return dtype == ATTN_BF16 ? dispatch64<TagBF16>(p, pl.cfg, cz, split, stream)
+                                : dispatch64<TagF16>(p, pl.cfg, cz, split, stream);
+    return dtype == ATTN_BF16 ? dispatch<128, kCfgD128, TagBF16>(p, cz, split, stream)
+                              : dispatch<128, kCfgD128, TagF16>(p, cz, split, stream);
+  };
+  hipError_t e = hipSuccess;
+  if (pl.first_split > 0) {  // whole tiles
+    p.total = (int)pl.first_split;
+    p.tile0 = 0;
+    e = launch(false);
+  }
+  if (e == hipSuccess && split_wgs > 0) {  // pieces of the remaining tiles, then the merge
+    p.total = (int)split_wgs;
+    p.tile0 = (int)pl.first_split;
+    e = launch(true);
+    if (e == hipSuccess) {
+      if (D == 64)
+        e = dtype == ATTN_BF16 ? launch_combine<64, TagBF16>(p, stream)
+                               : launch_combine<64, TagF16>(p, stream);
+      else
+        e = dtype == ATTN_BF16 ? launch_combine<128, TagBF16>(p, stream)
+                               : launch_combine<128, TagF16>(p, stream);
+    }
   }
   if (ws) {
     hipError_t ef = hipFreeAsync(ws, stream);
@@ -796,12 +884,22 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int caus
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
   if ((D != 64 && D != 128) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
   if (causal != 0 && causal != 1) return ATTN_EINVAL;
-  const TileCfg c = kCfgs[select_cfg(B, Hq, Nq, D, causal, num_cus)];
-  const int ktiles = (Nkv + c.BN - 1) / c.BN;
-  int S = choose_splits(c, B, Hq, Nq, Nkv, num_cus);
-  if (S > ktiles) S = ktiles;
-  const int tps = (ktiles + S - 1) / S;
-  return (ktiles + tps - 1) / tps;
+  return make_plan(B, Hq, Nq, Nkv, D, causal, 0, num_cus).splits;
+}
+
+int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,
+                  int num_splits, int num_cus, attn_plan* plan) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
+  if ((D != 64 && D != 128) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
+  if ((causal != 0 && causal != 1) || num_splits < 0 || !plan) return ATTN_EINVAL;
+  if ((long long)B * Hq * Nq > INT32_MAX || (long long)B * Hkv * Nkv > INT32_MAX)
+    return ATTN_EINVAL;
+  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, causal, num_splits, num_cus);
+  plan->tile_rows = kCfgs[pl.cfg].BM();
+  plan->num_splits = pl.splits;
+  plan->split_rows = pl.rows - pl.row0;
+  plan->workspace_bytes = pl.workspace_bytes();
+  return ATTN_OK;
 }
 
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D, int num_splits) {

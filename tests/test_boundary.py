@@ -88,16 +88,53 @@ def test_attn_fwd_rejects_before_any_hip_call(lib):
     assert rc == EINVAL
 
 
+def plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype=BF16, num_splits=0):
+    return binding.attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype,
+                                 num_splits, 256)
+
+
 def test_split_heuristic():
-    # the headline video shape fills the chip without splitting
-    assert binding.attn_fwd_num_splits(1, 24, 24, 17160, 17160, 128, 0, BF16) == 1
-    assert binding.attn_fwd_num_splits(1, 24, 24, 75600, 75600, 128, 0, BF16) == 1
-    # one query row over a long key range: split over keys
-    s = binding.attn_fwd_num_splits(1, 16, 16, 1, 65536, 128, 0, BF16)
-    assert 2 <= s <= 64
+    # the 17160-token video shape: 24 heads x 68 tiles of 256 rows = 6 full
+    # rounds on 256 CUs + 96 tiles; only those 96 tiles (the last 28 of head
+    # 22 and all 68 of head 23) are cut over their key range
+    p = plan(1, 24, 24, 17160, 17160, 128, 0)
+    assert p.tile_rows == 256 and p.num_splits >= 2
+    assert p.split_rows == 27 * 256 + 8 + 17160
+    assert p.workspace_bytes == p.num_splits * p.split_rows * 129 * 4
+    assert binding.attn_fwd_num_splits(1, 24, 24, 17160, 17160, 128, 0, BF16) \
+        == p.num_splits
+    # 75600 tokens: 24 x 296 tiles = 27 rounds + 192 tiles, the last 192
+    p = plan(1, 24, 24, 75600, 75600, 128, 0)
+    assert p.num_splits >= 2 and p.split_rows == 191 * 256 + 80
+    # a grid of whole rounds is never split
+    p = plan(1, 32, 32, 2048, 2048, 128, 0)
+    assert p.num_splits == 1 and p.split_rows == 0 and p.workspace_bytes == 0
+    # causal grids that fill the device are balanced by launch order instead
+    assert plan(1, 32, 8, 16384, 16384, 128, 1).num_splits == 1
+    # one query row over a long key range: every row split over keys
+    p = plan(1, 16, 16, 1, 65536, 128, 0)
+    assert 2 <= p.num_splits <= 64 and p.split_rows == 16
     # short key ranges never split
-    assert binding.attn_fwd_num_splits(1, 1, 1, 1, 64, 64, 0, F16) == 1
+    assert plan(1, 1, 1, 1, 64, 64, 0, F16).num_splits == 1
     assert binding.attn_fwd_num_splits(0, 1, 1, 1, 64, 64, 0, F16) == EINVAL
+    # a forced count splits every row
+    p = plan(1, 24, 24, 17160, 17160, 128, 0, num_splits=3)
+    assert p.num_splits == 3 and p.split_rows == 24 * 17160
+    with pytest.raises(binding.AttnError):
+        plan(1, 3, 2, 10, 10, 64, 0)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 26, 26, 2600, 2000, 128), (1, 26, 13, 2600, 2000, 128),
+    (1, 40, 8, 1700, 1000, 64), (2, 32, 8, 2100, 2000, 64)])
+def test_tail_split_shapes(shape):
+    """The shapes the GPU tests use for the last-round split: some, not all,
+    rows are split, starting inside a head."""
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    p = plan(B, Hq, Hkv, Nq, Nkv, D, 0, F16)
+    assert p.num_splits >= 2
+    assert 0 < p.split_rows < B * Hq * Nq
+    assert p.split_rows % Nq != 0
 
 
 def test_workspace_bytes():

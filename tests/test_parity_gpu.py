@@ -124,6 +124,27 @@ def test_wide_d64_tiles_split(gpu_device, splits):
           rows=24, num_splits=splits)
 
 
+# -- split of the last partial round ---------------------------------------
+# Grids that fill the device but end in a partial round of workgroups cut
+# only that round's tiles over their key range (first split tile inside a
+# head, ragged last query tile, GQA), for both tile widths.
+
+@pytest.mark.parametrize("shape,dtype", [
+    ((1, 26, 26, 2600, 2000, 128), inputs.BF16),
+    ((1, 26, 13, 2600, 2000, 128), inputs.F16),
+    ((1, 40, 8, 1700, 1000, 64), inputs.BF16),
+])
+def test_last_round_split(gpu_device, shape, dtype):
+    from memory_efficient_tiled_amd import attn_fwd_plan
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    p = attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, False, 0)
+    assert p.num_splits >= 2 and 0 < p.split_rows < B * Hq * Nq
+    # 64 sampled rows per head (rows 0 and Nq-1 included) land on both sides
+    # of the first split row
+    _case(gpu_device, B, Hq, Hkv, Nq, Nkv, D, dtype, False, seed=Hq + D,
+          rows=64)
+
+
 # -- exact properties --------------------------------------------------------
 
 def _dev(x, dtype, device):
@@ -178,12 +199,11 @@ def test_without_lse(gpu_device):
 
 
 def test_no_device_allocation_without_split(gpu_device):
-    """The non-split path allocates nothing: torch's allocator sees only the
-    outputs, and the library's own workspace query is zero."""
+    """A call that splits nothing allocates nothing: the library's plan has
+    no workspace, and torch's allocator sees only the outputs."""
     import torch
-    from memory_efficient_tiled_amd import attn_fwd, attn_fwd_num_splits
-    w = inputs.WORKLOADS["dit-17160"]
-    assert attn_fwd_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, False, 1) == 1
+    from memory_efficient_tiled_amd import attn_fwd, attn_fwd_plan
+    assert attn_fwd_plan(1, 2, 2, 4096, 4096, 128, False, 1).workspace_bytes > 0
     x = inputs.make_inputs(1, 2, 2, 4096, 4096, 128, inputs.BF16, seed=8)
     args = [_dev(a, inputs.BF16, gpu_device) for a in (x.q, x.k, x.v)]
     out = torch.empty_like(args[0])
@@ -191,7 +211,7 @@ def test_no_device_allocation_without_split(gpu_device):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     before = torch.cuda.max_memory_allocated()
-    attn_fwd(*args, out=out, lse=lse)
+    attn_fwd(*args, out=out, lse=lse, num_splits=1)
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() == before
     free0, _ = torch.cuda.mem_get_info()
