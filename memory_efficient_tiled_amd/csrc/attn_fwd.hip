@@ -207,7 +207,14 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
 // The barrier also certifies that every wave has finished reading the
 // buffers the new copies overwrite (K_t in the previous step's product,
 // V_{t-1} in the previous step's P V).
-template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, bool SPLIT>
+//
+// With SB (single-buffered scores) a step is instead: barrier; start copies of
+// K_{t+1}, V_{t+1}; S_t = K_t Q^T; softmax of S_t; O += P_t V_t.  The scores
+// then need one register tile, not two, and the overlap of matrix and vector
+// work comes from the other wave on the SIMD.  QL > 0 keeps the last QL of
+// the DC reduction chunks of Q^T in LDS (each wave its own rows, read back in
+// operand order) instead of registers.
+template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
   constexpr int WR = QB * 32;           // query rows per wave
   constexpr int BM = NW * WR;
@@ -221,15 +228,19 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   constexpr int NDB = D / 32;           // 32-wide output column blocks
   constexpr int NKC = BN / 16;          // reduction chunks of P V
   constexpr int ROWB = D * 2;           // bytes per K/V row
+  constexpr int DCR = DC - QL;          // Q^T chunks held in registers
+  static_assert(QL >= 0 && QL < DC, "at least one Q^T chunk stays in registers");
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf2[SB ? TILE : 8];
+  __shared__ __attribute__((aligned(1024))) u32x4 qlds[QL > 0 ? NW * QB * QL * 64 : 1];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
@@ -284,8 +295,10 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     for (int j = 0; j < IPW; ++j) buf2lds16(r, dst + (wave * IPW + j) * 512, off[j]);
   };
 
-  // Q^T operands for the whole key loop.
-  u32x4 qf[QB][DC];
+  // Q^T operands for the whole key loop: chunks below DCR in registers, the
+  // rest in this wave's LDS slots (written and read by this wave only).
+  u32x4 qf[QB][DCR];
+  const int qmine = wave * QB * QL * 64 + lane;  // this lane's slot in qlds
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wq0 + qb * 32 + l32;
@@ -293,9 +306,25 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     for (int kc = 0; kc < DC; ++kc) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (row < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + row) * D + kc * 16 + hl * 8);
-      qf[qb][kc] = x ^ p.qsign;
+      if (kc < DCR)
+        qf[qb][kc < DCR ? kc : 0] = x ^ p.qsign;
+      else
+        qlds[qmine + (qb * QL + (kc - DCR)) * 64] = x ^ p.qsign;
     }
   }
+  // The LDS chunks are re-read at every use, from index qi: the caller
+  // passes it through an empty asm once per tile, which hides it from the
+  // compiler, so the (loop-invariant) reads are not hoisted out of the key
+  // loop into registers.
+  auto qop = [&](int qb, int kc, int qi) -> u32x4 {
+    if (kc < DCR) return qf[qb][kc < DCR ? kc : 0];
+    return qlds[qi + (qb * QL + (kc - DCR)) * 64];
+  };
+  auto qindex = [&]() {
+    int qi = qmine;
+    if constexpr (QL > 0) asm volatile("" : "+v"(qi));
+    return qi;
+  };
 
   // O^T accumulators: block (qb, db) at oacc[qb * NDB + db].
   f32x16 oacc[QB * NDB];
@@ -319,16 +348,20 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 
   // S^T = K Q^T for one tile, accumulated into s (zeroed here).
   auto qk = [&](const uint16_t* ks, f32x16* s) {
+    const int qi = qindex();
 #pragma unroll
     for (int i = 0; i < QB * NKB; ++i) s[i] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
+      u32x4 bq[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) bq[qb] = qop(qb, kc, qi);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int row = kb * 32 + l32;
         const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ k_swz<D>(row)) << 3));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, qf[qb][kc], s[qb * NKB + kb]);
+        for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, bq[qb], s[qb * NKB + kb]);
       }
     }
   };
@@ -354,41 +387,65 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     }
   };
 
-  // Probabilities of query block qb of one tile against reference max mb,
-  // packed as its P^T operands; returns the lane-partial row sum.
-  auto probs = [&](const f32x16* s, int qb, float mb, u32x4* pf) {
-    float rs = 0.f;
+  // Scores of query block qb of one tile -> probabilities against reference
+  // max mb, in place; returns the lane-partial row sum.
+  auto probs = [&](f32x16* s, int qb, float mb) {
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float x[16];
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        x[e] = fast_exp2(fmaf(s[qb * NKB + kb][e], p.c, -mb));
-        rs += x[e];
+        s[qb * NKB + kb][e] = fast_exp2(fmaf(s[qb * NKB + kb][e], p.c, -mb));
+        rs[e & 3] += s[qb * NKB + kb][e];
       }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 y;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) y[w] = N::pack2(x[8 * hf + 2 * w], x[8 * hf + 2 * w + 1]);
-        pf[qb * NKC + kb * 2 + hf] = y;
-      }
-    }
-    return rs;
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
 
-  // Softmax of one tile: fast path against the current references; if any
-  // row's reference is still -inf or a partial sum exceeds the bound, raise
-  // the references to the true running max, rescale O and l, and redo.
-  auto softmax = [&](const f32x16* s, u32x4* pf) {
-    float rs[QB];
+  // Raw scores of tile t again, masked: the slow path of the softmax needs
+  // them after the fast path has overwritten them.  With SB, K_t is still in
+  // LDS (ks); otherwise its buffer is being refilled and K comes from global
+  // memory (rows past the key range read as zero).
+  auto rescore = [&](int t, f32x16* s, const uint16_t* ks) {
+    if constexpr (SB) {
+      qk(ks, s);
+      mask(t, s);
+      return;
+    }
+    const int k0 = kbeg + t * BN;
+#pragma unroll
+    for (int i = 0; i < QB * NKB; ++i) s[i] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < DC; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int key = k0 + kb * 32 + l32;
+        u32x4 a = {0u, 0u, 0u, 0u};
+        if (key < p.Nkv) a = *(const u32x4*)(Kg + (size_t)key * D + kc * 16 + hl * 8);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, qop(qb, kc, qmine), s[qb * NKB + kb]);
+      }
+    }
+    mask(t, s);
+  };
+
+  // Softmax of tile t, in two parts.  softmax_fast: probabilities against
+  // the current references, in place; true if some row's reference is still
+  // -inf or a partial sum exceeds the bound.  softmax_finish: in that case
+  // recompute the scores, raise the references to the true running max,
+  // rescale O and l, and redo; then accumulate l and pack the P^T operands.
+  auto softmax_fast = [&](f32x16* s, float* rs) {
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      rs[qb] = probs(s, qb, m[qb], pf);
+      rs[qb] = probs(s, qb, m[qb]);
       bad = bad || !(m[qb] > -INFINITY) || !(rs[qb] <= kMaxPartialSum);
     }
+    return bad;
+  };
+  auto softmax_finish = [&](int t, f32x16* s, float* rs, bool bad, u32x4* pf,
+                            const uint16_t* ks) {
     if (__builtin_amdgcn_ballot_w64(bad)) {
+      rescore(t, s, ks);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float mx = -INFINITY;
@@ -404,11 +461,23 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
         l[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[qb * NDB + db] *= alpha;
-        rs[qb] = probs(s, qb, (mnew == -INFINITY) ? 0.f : mnew, pf);
+        rs[qb] = probs(s, qb, (mnew == -INFINITY) ? 0.f : mnew);
       }
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l[qb] += rs[qb];  // lane-partial: lane l^32 holds the rest
+    for (int qb = 0; qb < QB; ++qb) {
+      l[qb] += rs[qb];  // lane-partial: lane l^32 holds the rest
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          u32x4 y;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            y[w] = N::pack2(s[qb * NKB + kb][8 * hf + 2 * w], s[qb * NKB + kb][8 * hf + 2 * w + 1]);
+          pf[qb * NKC + kb * 2 + hf] = y;
+        }
+    }
   };
 
   // O^T += V^T P^T; V^T operands come from transposing reads of V.
@@ -443,15 +512,66 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
       issue(Vg, t + 1, vn, voff);
       qk(kn, sn);
     }
+    float rs[QB];
+    const bool bad = softmax_fast(s, rs);
     u32x4 pf[QB * NKC];
-    softmax(s, pf);
+    softmax_finish(t, s, rs, bad, pf, nullptr);
     pv(vc, pf);
   };
   using Last = std::integral_constant<bool, true>;
   using More = std::integral_constant<bool, false>;
 
-  f32x16 sa[QB * NKB], sb[QB * NKB];
-  if (ntiles > 0) {
+  // Single-buffered steps.  Waves w and w + NW/2 share a SIMD; the second
+  // group runs half a step late: after the barrier of step t it first forms
+  // O += P_{t-1} V_{t-1}, then S_t and its softmax, so each wave's vector
+  // work overlaps the other's matrix work.  K_t sits in kbuf[t % 2] and V_t
+  // in vbuf[t % 3]: the copies of step t (K_{t+1}, V_{t+1}) overwrite K_{t-1}
+  // and V_{t-2}, which every wave has finished with once past the barrier.
+  f32x16 sa[QB * NKB], sb[SB ? 1 : QB * NKB];
+  if constexpr (SB) {
+    const bool late = NW >= 2 && wave >= NW / 2;
+    u32x4 pf[QB * NKC];
+    // One step: K_t in kc, V_t in vc, V_{t-1} in vp; K_{t+1}, V_{t+1} go to
+    // kn, vn.  Whole loop iterations pass the buffers as distinct LDS arrays,
+    // so the compiler sees that the reads do not touch what the copies fill.
+    auto sb_step = [&](int t, uint16_t* kc, uint16_t* vc, uint16_t* vp, uint16_t* kn,
+                       uint16_t* vn) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        issue(Kg, t + 1, kn, koff);
+        issue(Vg, t + 1, vn, voff);
+      }
+      if (late && t > 0) pv(vp, pf);
+      qk(kc, sa);
+      mask(t, sa);
+      float rs[QB];
+      const bool bad = softmax_fast(sa, rs);
+      softmax_finish(t, sa, rs, bad, pf, kc);
+      if (!late) pv(vc, pf);
+    };
+    auto kbufs = [&](int i) { return i ? kbuf1 : kbuf0; };
+    auto vbufs = [&](int i) { return i == 0 ? vbuf0 : i == 1 ? vbuf1 : vbuf2; };
+    if (ntiles > 0) {
+      issue(Kg, 0, kbuf0, koff);
+      issue(Vg, 0, vbuf0, voff);
+    }
+    int t = 0;
+    for (; t + 6 <= ntiles; t += 6) {  // K_t in kbuf[t % 2], V_t in vbuf[t % 3]
+      sb_step(t, kbuf0, vbuf0, vbuf2, kbuf1, vbuf1);
+      sb_step(t + 1, kbuf1, vbuf1, vbuf0, kbuf0, vbuf2);
+      sb_step(t + 2, kbuf0, vbuf2, vbuf1, kbuf1, vbuf0);
+      sb_step(t + 3, kbuf1, vbuf0, vbuf2, kbuf0, vbuf1);
+      sb_step(t + 4, kbuf0, vbuf1, vbuf0, kbuf1, vbuf2);
+      sb_step(t + 5, kbuf1, vbuf2, vbuf1, kbuf0, vbuf0);
+    }
+    for (; t < ntiles; ++t) {
+      const int v3 = t % 3;
+      sb_step(t, kbufs(t & 1), vbufs(v3), vbufs(v3 == 0 ? 2 : v3 - 1), kbufs((t + 1) & 1),
+              vbufs(v3 == 2 ? 0 : v3 + 1));
+    }
+    if (late && ntiles > 0) pv(vbufs((ntiles - 1) % 3), pf);
+  } else if (ntiles > 0) {
     issue(Kg, 0, kbuf0, koff);
     issue(Vg, 0, vbuf0, voff);
     __builtin_amdgcn_s_waitcnt(0);
@@ -555,19 +675,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // 256-row workgroups still give every CU two of them and no causal diagonal
 // is wasted, otherwise the 32-row tiles are faster.
 struct TileCfg {
-  int NW, QB, BN;
+  int NW, QB, BN, QL;
+  bool SB;
   constexpr int BM() const { return NW * QB * 32; }
   constexpr int resident_per_cu() const { return 4 * kWavesPerSimd / NW; }
 };
-enum { kCfgD64Narrow = 0, kCfgD64Wide = 1, kCfgD128 = 2 };
-constexpr TileCfg kCfgs[3] = {{4, 1, 64}, {4, 2, 32}, {8, 1, 64}};
+enum { kCfgD64Narrow = 0, kCfgD64Wide = 1, kCfgD128Narrow = 2, kCfgD128Wide = 3 };
+constexpr TileCfg kCfgs[4] = {{4, 1, 64, 0, false},
+                              {4, 2, 32, 0, false},
+                              {8, 1, 64, 0, false},
+                              {8, 2, 32, 3, true}};
 
+// The wide tiles of each head dimension are used without a causal mask when
+// they still fill every slot of the device at least once.
 int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
-  if (D == 128) return kCfgD128;
-  const TileCfg& w = kCfgs[kCfgD64Wide];
+  const int narrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
+  const int wide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
+  const TileCfg& w = kCfgs[wide];
   const long long wide_wgs = (long long)B * Hq * ((Nq + w.BM() - 1) / w.BM());
   const long long slots = (long long)w.resident_per_cu() * (num_cus > 0 ? num_cus : 256);
-  return (!causal && wide_wgs >= slots) ? kCfgD64Wide : kCfgD64Narrow;
+  return (!causal && wide_wgs >= slots) ? wide : narrow;
 }
 
 thread_local int g_last_hip_error = 0;
@@ -736,7 +863,8 @@ Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits
 template <int D, int CFG, class Tag, bool CAUSAL, bool SPLIT>
 hipError_t launch_main(const Params& p, hipStream_t stream) {
   constexpr TileCfg c = kCfgs[CFG];
-  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, SPLIT>), dim3(p.total),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT>),
+                     dim3(p.total),
                      dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -750,13 +878,15 @@ hipError_t dispatch(const Params& p, bool causal, bool split, hipStream_t st) {
                : launch_main<D, CFG, Tag, false, false>(p, st);
 }
 
-// The wide D = 64 tiles are only selected without a causal mask.
-template <class Tag>
-hipError_t dispatch64(const Params& p, int cfg, bool causal, bool split, hipStream_t st) {
-  if (cfg == kCfgD64Wide && !causal)
-    return split ? launch_main<64, kCfgD64Wide, Tag, false, true>(p, st)
-                 : launch_main<64, kCfgD64Wide, Tag, false, false>(p, st);
-  return dispatch<64, kCfgD64Narrow, Tag>(p, causal, split, st);
+// The wide tiles are only selected without a causal mask.
+template <int D, class Tag>
+hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, hipStream_t st) {
+  constexpr int kNarrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
+  constexpr int kWide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
+  if (cfg == kWide && !causal)
+    return split ? launch_main<D, kWide, Tag, false, true>(p, st)
+                 : launch_main<D, kWide, Tag, false, false>(p, st);
+  return dispatch<D, kNarrow, Tag>(p, causal, split, st);
 }
 
 template <int D, class Tag>
@@ -821,10 +951,10 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   const bool cz = causal != 0;
   auto launch = [&](bool split) {
     if (D == 64)
-      return dtype == ATTN_BF16 ? dispatch64<TagBF16>(p, pl.cfg, cz, split, stream)
-                                : dispatch64<TagF16>(p, pl.cfg, cz, split, stream);
-    return dtype == ATTN_BF16 ? dispatch<128, kCfgD128, TagBF16>(p, cz, split, stream)
-                              : dispatch<128, kCfgD128, TagF16>(p, cz, split, stream);
+      return dtype == ATTN_BF16 ? dispatch_d<64, TagBF16>(p, pl.cfg, cz, split, stream)
+                                : dispatch_d<64, TagF16>(p, pl.cfg, cz, split, stream);
+    return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, stream)
+                              : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, stream);
   };
   hipError_t e = hipSuccess;
   if (pl.first_split > 0) {  // whole tiles

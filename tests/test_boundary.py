@@ -94,18 +94,21 @@ def plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype=BF16, num_splits=0):
 
 
 def test_split_heuristic():
-    # the 17160-token video shape: 24 heads x 68 tiles of 256 rows = 6 full
-    # rounds on 256 CUs + 96 tiles; only those 96 tiles (the last 28 of head
-    # 22 and all 68 of head 23) are cut over their key range
+    # the 17160-token video shape: 24 heads x 34 tiles of 512 rows (one per
+    # CU) = 3 full rounds on 256 CUs + 48 tiles; only those 48 tiles (the
+    # last 14 of head 22 and all 34 of head 23) are cut over their key range
     p = plan(1, 24, 24, 17160, 17160, 128, 0)
-    assert p.tile_rows == 256 and p.num_splits >= 2
-    assert p.split_rows == 27 * 256 + 8 + 17160
+    assert p.tile_rows == 512 and p.num_splits >= 2
+    assert p.split_rows == 13 * 512 + 264 + 17160
     assert p.workspace_bytes == p.num_splits * p.split_rows * 129 * 4
     assert binding.attn_fwd_num_splits(1, 24, 24, 17160, 17160, 128, 0, BF16) \
         == p.num_splits
-    # 75600 tokens: 24 x 296 tiles = 27 rounds + 192 tiles, the last 192
+    # 75600 tokens: 24 x 148 tiles = 13 rounds + 224 tiles, the last 224
     p = plan(1, 24, 24, 75600, 75600, 128, 0)
-    assert p.num_splits >= 2 and p.split_rows == 191 * 256 + 80
+    assert p.num_splits >= 2 and p.split_rows == 75 * 512 + 336 + 75600
+    # grids below one round of 512-row tiles use 256-row tiles
+    assert plan(1, 26, 26, 2600, 2000, 128, 0).tile_rows == 256
+    assert plan(1, 24, 24, 17160, 17160, 128, 1).tile_rows == 256
     # a grid of whole rounds is never split
     p = plan(1, 32, 32, 2048, 2048, 128, 0)
     assert p.num_splits == 1 and p.split_rows == 0 and p.workspace_bytes == 0
@@ -126,7 +129,8 @@ def test_split_heuristic():
 
 @pytest.mark.parametrize("shape", [
     (1, 26, 26, 2600, 2000, 128), (1, 26, 13, 2600, 2000, 128),
-    (1, 40, 8, 1700, 1000, 64), (2, 32, 8, 2100, 2000, 64)])
+    (1, 40, 8, 1700, 1000, 64), (2, 32, 8, 2100, 2000, 64),
+    (1, 64, 8, 2100, 1000, 128)])
 def test_tail_split_shapes(shape):
     """The shapes the GPU tests use for the last-round split: some, not all,
     rows are split, starting inside a head."""

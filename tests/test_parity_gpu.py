@@ -124,6 +124,42 @@ def test_wide_d64_tiles_split(gpu_device, splits):
           rows=24, num_splits=splits)
 
 
+# -- the 512-row tiles of D = 128 -------------------------------------------
+# Chosen for non-causal D = 128 grids of at least one 512-row workgroup per
+# CU (here 64 heads x 5 query tiles = 320 on 256 CUs, so the last 64 tiles
+# are also split over keys): ragged query and key tails, GQA, both dtypes,
+# forced splits, and keys that grow along the sequence so that the scores
+# keep raising the running reference (the softmax's slow path).
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+@pytest.mark.parametrize("nkv", [33, 1000, 2047])
+def test_wide_d128_tiles(gpu_device, nkv, dtype):
+    from memory_efficient_tiled_amd import attn_fwd_plan
+    assert attn_fwd_plan(1, 64, 8, 2100, nkv, 128, False, 0).tile_rows == 512
+    _case(gpu_device, 1, 64, 8, 2100, nkv, 128, dtype, False, seed=nkv + 1,
+          rows=24)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_wide_d128_tiles_split(gpu_device, splits):
+    _case(gpu_device, 1, 64, 64, 2100, 1500, 128, inputs.BF16, False, seed=12,
+          rows=24, num_splits=splits)
+
+
+def test_wide_d128_rising_scores(gpu_device):
+    """Keys scaled up 8x along the sequence: the row maxima keep rising, so
+    the running reference is raised (the softmax's slow path) on many key
+    tiles, not only the first."""
+    x = inputs.make_inputs(1, 64, 8, 2100, 2047, 128, inputs.F16, seed=13,
+                           sampled_rows=24)
+    ramp = np.linspace(1.0, 8.0, 2047, dtype=np.float32)[None, None, :, None]
+    x.k = (x.k.astype(np.float32) * ramp).astype(np.float16)
+    o, l = run_gpu(x, None, False, gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, False, rows=x.rows)
+    compare(gather_rows(o, x.rows), gather_rows(l, x.rows), o_ref, l_ref,
+            inputs.F16, rounding_allowance=True, what="rising scores")
+
+
 # -- split of the last partial round ---------------------------------------
 # Grids that fill the device but end in a partial round of workgroups cut
 # only that round's tiles over their key range (first split tile inside a
