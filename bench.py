@@ -46,7 +46,7 @@ def measured_traffic(workload: str):
         return None
     text = open(path).read()
     h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
-    t = re.search(r"hbm bytes per launch:\s*`?([0-9.eE+]+)", text)
+    t = re.search(r"hbm bytes per step:\s*`?([0-9.eE+]+)", text)
     if not h or not t or h.group(1) != source_hash():
         return None
     return float(t.group(1))

@@ -28,10 +28,11 @@
 // Softmax runs in base 2: scores are scaled by scale*log2(e) and exponentiated
 // with v_exp_f32; the log-sum-exp is converted back to natural log.
 //
-// Split-KV: when query tiles alone cannot fill the 256 compute units, the key
-// range is divided into splits; each writes an fp32 partial output normalised
-// by its own row sum, plus its partial log-sum-exp, and a second kernel merges
-// them with weights exp(lse_s - lse).
+// Split-KV: query tiles that cannot keep the 256 compute units busy (all of
+// a small grid, or the last partial round of a large one) are divided into
+// key ranges; each piece writes an fp32 partial output normalised by its own
+// row sum, plus its partial log-sum-exp, and a second kernel merges them with
+// weights exp(lse_s - lse).
 
 #include <hip/hip_runtime.h>
 
@@ -193,9 +194,9 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
 // looping over BN-key tiles of its key range.  Each K or V operand read from
 // LDS feeds QB MFMAs (one per 32-row query block of the wave), so LDS read
 // traffic per flop falls as 1 / QB.  K and V tiles go from HBM (mostly L2)
-// straight into LDS, two buffers each, in a swizzled row-major layout:
-// 16-byte chunk c of key row r is stored at chunk c ^ k_swz(r) (K) or
-// c ^ v_swz(r) (V).
+// straight into LDS (two buffers each; three for V with SB), in a swizzled
+// row-major layout: 16-byte chunk c of key row r is stored at chunk
+// c ^ k_swz(r) (K) or c ^ v_swz(r) (V).
 //
 // Software pipeline, one barrier per key tile t (scores S_t already in
 // registers when the step starts):
@@ -211,9 +212,10 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
 // With SB (single-buffered scores) a step is instead: barrier; start copies of
 // K_{t+1}, V_{t+1}; S_t = K_t Q^T; softmax of S_t; O += P_t V_t.  The scores
 // then need one register tile, not two, and the overlap of matrix and vector
-// work comes from the other wave on the SIMD.  QL > 0 keeps the last QL of
-// the DC reduction chunks of Q^T in LDS (each wave its own rows, read back in
-// operand order) instead of registers.
+// work comes from the other wave on the SIMD, which runs half a step late
+// (see the loop).  QL > 0 keeps the last QL of the DC reduction chunks of
+// Q^T in LDS (each wave its own rows, read back in operand order) instead of
+// registers.
 template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
   constexpr int WR = QB * 32;           // query rows per wave
