@@ -143,18 +143,20 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the whole region gives the mean,
+    # the gaps give per-step median and minimum
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     progress(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    t1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.dtype]
     progress(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); "
@@ -173,6 +175,8 @@ def main():
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "step_ms": {"mean": round(ms, 5), "median": round(per_step[len(per_step) // 2], 5),
+                    "min": round(per_step[0], 5), "max": round(per_step[-1], 5)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{name}: {w.note}, {w.describe()}",

@@ -99,6 +99,43 @@ int attn_fwd_check(const void* q, const void* k, const void* v, const void* out,
                    int D, float scale, int causal, int dtype);
 
 /*
+ * attn_fwd_strided -- attn_fwd_split on strided tensors, so that a
+ * scaled-dot-product-attention front end (the English noflash-attention
+ * post, section "From gfx906 to a broader release": the op is routed in
+ * under PyTorch's SDPA call) can pass views such as [B,N,H,D] storage
+ * transposed to [B,H,N,D] without copying.
+ *
+ * q_stride, k_stride, v_stride, o_stride: host arrays of 3 element strides
+ * for the batch, head and sequence dimensions of Q, K, V and out (logical
+ * shapes as in attn_fwd); the head dimension D is contiguous.  NULL means
+ * the contiguous layout.  Each stride must be a non-negative multiple of 8;
+ * sequence strides must lie in [D, 2^24]; no two elements of `out` may share
+ * an address; `out` must not overlap q, k or v, nor `lse` any tensor
+ * (ATTN_EINVAL otherwise).  `lse` stays contiguous [B,Hq,Nq].  Everything
+ * else (num_splits, workspace, errors) is as for attn_fwd_split.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* out,
+                     float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     const long long* q_stride, const long long* k_stride,
+                     const long long* v_stride, const long long* o_stride,
+                     float scale, int causal, int dtype, int num_splits,
+                     void* stream);
+
+/*
+ * attn_fwd_strided_check -- the argument validation of attn_fwd_strided,
+ * host only (no HIP call, no pointer dereferenced except the stride
+ * arrays).  Returns ATTN_OK or ATTN_EINVAL.
+ */
+int attn_fwd_strided_check(const void* q, const void* k, const void* v,
+                           const void* out, const float* lse, int B, int Hq,
+                           int Hkv, int Nq, int Nkv, int D,
+                           const long long* q_stride,
+                           const long long* k_stride,
+                           const long long* v_stride,
+                           const long long* o_stride, float scale,
+                           int causal, int dtype);
+
+/*
  * attn_plan -- how attn_fwd_split covers a shape (see attn_fwd_plan).
  * Output rows are numbered (b * Hq + h) * Nq + i, 0 <= r < B*Hq*Nq.
  */

@@ -71,6 +71,13 @@ def load_library():
     lib.attn_fwd_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
         [ctypes.c_float, _INT, _INT]
     lib.attn_fwd_check.restype = _INT
+    _LLP = ctypes.POINTER(ctypes.c_longlong)
+    lib.attn_fwd_strided.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [_LLP] * 4 + [ctypes.c_float, _INT, _INT, _INT, _VP]
+    lib.attn_fwd_strided.restype = _INT
+    lib.attn_fwd_strided_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [_LLP] * 4 + [ctypes.c_float, _INT, _INT]
+    lib.attn_fwd_strided_check.restype = _INT
     lib.attn_fwd_plan.argtypes = shape_args + [_INT, _INT, _INT, _INT,
                                                ctypes.POINTER(AttnPlan)]
     lib.attn_fwd_plan.restype = _INT
@@ -135,16 +142,26 @@ def attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, num_splits) -> int:
     return load_library().attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, num_splits)
 
 
+def strides3(t):
+    """ctypes array of the (batch, head, sequence) element strides of a 4-D
+    tensor whose last dimension is contiguous."""
+    if t.stride(3) != 1:
+        raise ValueError("the head dimension (last) must be contiguous")
+    return (ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
              out=None, lse=None, return_lse: bool = True, num_splits: int = 0):
     """O = softmax(scale * Q K^T [causal top-left mask]) V on the GPU.
 
-    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; contiguous, same dtype
-    (float16 or bfloat16), on one HIP device.  Returns (out, lse) with out
-    like q and lse float32 [B, Hq, Nq] (natural log), or just out when
-    ``return_lse`` is False.  ``num_splits`` = 0 lets the library choose the
-    split-KV count; a positive value forces it.  Runs on torch's current
-    stream; no host synchronisation.
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; same dtype (float16 or
+    bfloat16), on one HIP device, any strides with the last dimension
+    contiguous (e.g. [B, N, H, D] storage viewed as [B, H, N, D]).  Returns
+    (out, lse) with out [B, Hq, Nq, D] (new tensors are contiguous; a given
+    ``out`` may be strided) and lse float32 [B, Hq, Nq] (natural log), or
+    just out when ``return_lse`` is False.  ``num_splits`` = 0 lets the
+    library choose the split-KV count; a positive value forces it.  Runs on
+    torch's current stream; no host synchronisation.
     """
     import torch
     lib = load_library()
@@ -155,8 +172,6 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
             raise ValueError(f"{name} must be on a HIP device, got {t.device}")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D [B, H, N, D]")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     if not (q.device == k.device == v.device):
@@ -170,16 +185,23 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    lse_ptr = lse.data_ptr() if (return_lse and lse is not None) else None
+        out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, Hq, Nq, D) or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must be [B, Hq, Nq, D] with the dtype and device of q")
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        elif (tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32
+              or not lse.is_contiguous() or lse.device != q.device):
+            raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor on q's device")
+    lse_ptr = lse.data_ptr() if return_lse else None
+    qs, ks, vs, os_ = strides3(q), strides3(k), strides3(v), strides3(out)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
-                                float(scale), int(bool(causal)), dt,
-                                int(num_splits), stream)
+        rc = lib.attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
+                                  qs, ks, vs, os_, float(scale), int(bool(causal)), dt,
+                                  int(num_splits), stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (out, lse) if return_lse else out

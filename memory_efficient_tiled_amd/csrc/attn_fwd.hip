@@ -42,6 +42,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <utility>
 #include <type_traits>
 
 #include "attn.h"
@@ -107,6 +108,10 @@ struct Params {
   int row0, prows;    // split: output rows [row0, row0 + prows) have partials
   float c;            // |scale| * log2(e)
   uint32_t qsign;     // 0x80008000 flips the sign of Q (negative scale)
+  // Element strides of the batch, head and sequence dimensions (the head
+  // dimension is contiguous); row strides fit in 32 bits.
+  int64_t qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
+  int qsn, ksn, vsn, osn;
 };
 
 // Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
@@ -216,7 +221,11 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* ld
 // (see the loop).  QL > 0 keeps the last QL of the DC reduction chunks of
 // Q^T in LDS (each wave its own rows, read back in operand order) instead of
 // registers.
-template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB, bool SPLIT>
+//
+// STRIDED takes the tensors' batch, head and sequence strides from Params;
+// otherwise the layouts are contiguous and the strides compile-time values.
+template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB, bool SPLIT,
+          bool STRIDED>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
   constexpr int WR = QB * 32;           // query rows per wave
   constexpr int BM = NW * WR;
@@ -269,10 +278,13 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   if (CAUSAL) kend = min(kend, q0 + BM);  // keys past the tile's last row are all masked
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
-  const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
-  const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
-  const uint16_t* Kg = p.k + krow0 * D;
-  const uint16_t* Vg = p.v + krow0 * D;
+  const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;  // LSE / partial row of query 0
+  const int64_t kvh = (int64_t)p.Nkv * D, qh = (int64_t)p.Nq * D;
+  const int qsn = STRIDED ? p.qsn : D, ksn = STRIDED ? p.ksn : D;
+  const int vsn = STRIDED ? p.vsn : D, osn = STRIDED ? p.osn : D;
+  const uint16_t* Qg = p.q + (STRIDED ? b * p.qsb + hq * p.qsh : ((int64_t)b * p.Hq + hq) * qh);
+  const uint16_t* Kg = p.k + (STRIDED ? b * p.ksb + hk * p.ksh : ((int64_t)b * p.Hkv + hk) * kvh);
+  const uint16_t* Vg = p.v + (STRIDED ? b * p.vsb + hk * p.vsh : ((int64_t)b * p.Hkv + hk) * kvh);
 
   // Per-lane byte offsets of this wave's copy slots within a tile (the same
   // for every tile) and the LDS slot each copy fills.
@@ -281,18 +293,18 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   for (int j = 0; j < IPW; ++j) {
     const int slot = (wave * IPW + j) * 64 + lane;
     const int row = slot / CPR, pc = slot % CPR;
-    koff[j] = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
-    voff[j] = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
+    koff[j] = row * ksn * 2 + ((pc ^ k_swz<D>(row)) << 4);
+    voff[j] = row * vsn * 2 + ((pc ^ v_swz<D>(row)) << 4);
   }
-  // Copy tile `t` of K (or V) into LDS.  The buffer ends at the last key, so
-  // rows past it read as zero: their scores are masked to -inf and their V
-  // rows are multiplied by exactly 0.
-  auto issue = [&](const uint16_t* base, int t, uint16_t* dst, const uint32_t* off) {
+  // Copy tile `t` of K (or V, rows `sn` elements apart) into LDS.  The
+  // buffer ends with the last key's row, so rows past it (which start at or
+  // beyond that end, as sn >= D) read as zero: their scores are masked to
+  // -inf and their V rows are multiplied by exactly 0.
+  auto issue = [&](const uint16_t* base, int sn, int t, uint16_t* dst, const uint32_t* off) {
     const int k0 = kbeg + t * BN;
     const int nrows = min(BN, p.Nkv - k0);
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * D), 0, nrows * ROWB,
-                                          kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (size_t)k0 * sn), 0, (nrows - 1) * sn * 2 + ROWB, kRawBufferFlags);
 #pragma unroll
     for (int j = 0; j < IPW; ++j) buf2lds16(r, dst + (wave * IPW + j) * 512, off[j]);
   };
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < p.Nq) x = *(const u32x4*)(p.q + (qrow0 + row) * D + kc * 16 + hl * 8);
+      if (row < p.Nq) x = *(const u32x4*)(Qg + (size_t)row * qsn + kc * 16 + hl * 8);
       if (kc < DCR)
         qf[qb][kc < DCR ? kc : 0] = x ^ p.qsign;
       else
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
       for (int kb = 0; kb < NKB; ++kb) {
         const int key = k0 + kb * 32 + l32;
         u32x4 a = {0u, 0u, 0u, 0u};
-        if (key < p.Nkv) a = *(const u32x4*)(Kg + (size_t)key * D + kc * 16 + hl * 8);
+        if (key < p.Nkv) a = *(const u32x4*)(Kg + (size_t)key * ksn + kc * 16 + hl * 8);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, qop(qb, kc, qmine), s[qb * NKB + kb]);
       }
@@ -510,8 +522,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (!LAST) {
-      if (t + 2 < ntiles) issue(Kg, t + 2, kc, koff);
-      issue(Vg, t + 1, vn, voff);
+      if (t + 2 < ntiles) issue(Kg, ksn, t + 2, kc, koff);
+      issue(Vg, vsn, t + 1, vn, voff);
       qk(kn, sn);
     }
     float rs[QB];
@@ -541,8 +553,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (t + 1 < ntiles) {
-        issue(Kg, t + 1, kn, koff);
-        issue(Vg, t + 1, vn, voff);
+        issue(Kg, ksn, t + 1, kn, koff);
+        issue(Vg, vsn, t + 1, vn, voff);
       }
       if (late && t > 0) pv(vp, pf);
       qk(kc, sa);
@@ -555,8 +567,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     auto kbufs = [&](int i) { return i ? kbuf1 : kbuf0; };
     auto vbufs = [&](int i) { return i == 0 ? vbuf0 : i == 1 ? vbuf1 : vbuf2; };
     if (ntiles > 0) {
-      issue(Kg, 0, kbuf0, koff);
-      issue(Vg, 0, vbuf0, voff);
+      issue(Kg, ksn, 0, kbuf0, koff);
+      issue(Vg, vsn, 0, vbuf0, voff);
     }
     int t = 0;
     for (; t + 6 <= ntiles; t += 6) {  // K_t in kbuf[t % 2], V_t in vbuf[t % 3]
@@ -574,11 +586,11 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     }
     if (late && ntiles > 0) pv(vbufs((ntiles - 1) % 3), pf);
   } else if (ntiles > 0) {
-    issue(Kg, 0, kbuf0, koff);
-    issue(Vg, 0, vbuf0, voff);
+    issue(Kg, ksn, 0, kbuf0, koff);
+    issue(Vg, vsn, 0, vbuf0, voff);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (ntiles > 1) issue(Kg, 1, kbuf1, koff);
+    if (ntiles > 1) issue(Kg, ksn, 1, kbuf1, koff);
     qk(kbuf0, sa);
     int t = 0;
     for (; t + 2 < ntiles; t += 2) {
@@ -614,7 +626,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
           }
         if (hl == 0) p.lsepart[prow] = lse_v;
       } else {
-        uint16_t* dst = p.o + (qrow0 + qrow) * D;
+        uint16_t* dst = p.o + (STRIDED ? b * p.osb + hq * p.osh : ((int64_t)b * p.Hq + hq) * qh) +
+                        (size_t)qrow * osn;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -632,12 +645,13 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 
 // Merge split-KV partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
 // Partial row r belongs to output row row0 + r.
-template <int D, class Tag>
+template <int D, class Tag, bool STRIDED>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
                                                            const float* __restrict__ lsepart,
                                                            uint16_t* __restrict__ o,
                                                            float* __restrict__ lse, int rows,
-                                                           int row0, int n_splits) {
+                                                           int row0, int n_splits, int Hq, int Nq,
+                                                           int64_t osb, int64_t osh, int osn) {
   using N = Num<Tag>;
   constexpr int C4 = D / 4;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -659,7 +673,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   u32x2 y = {N::pack2(acc[0] * inv, acc[1] * inv), N::pack2(acc[2] * inv, acc[3] * inv)};
-  *(u32x2*)(o + (row0 + row) * D + c4 * 4) = y;
+  const int r = row0 + (int)row;
+  size_t at = (size_t)r * D;  // contiguous: output row r
+  if (STRIDED) {
+    const int i = r % Nq, bh = r / Nq;
+    at = (bh / Hq) * osb + (bh % Hq) * osh + (size_t)i * osn;
+  }
+  *(u32x2*)(o + at + c4 * 4) = y;
   if (c4 == 0 && lse) lse[row0 + row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
@@ -668,14 +688,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 
 // Tile table: waves per workgroup, 32-row query blocks per wave, keys per
-// tile.  Every kernel runs two waves per SIMD (8 per CU), so a CU holds
-// 8 / NW workgroups.  At D = 128 a wave holds 32 rows (the register file
-// allows no more at two waves per SIMD) and the workgroup has 8 waves: each
-// K/V tile copied into LDS then serves 256 query rows, which halves the
-// L2 -> LDS traffic of a 4-wave workgroup.  At D = 64 a wave can hold 64
-// rows, which halves the LDS and L2 traffic per flop; that pays when the
-// 256-row workgroups still give every CU two of them and no causal diagonal
-// is wasted, otherwise the 32-row tiles are faster.
+// tile, Q^T chunks kept in LDS, pipeline.  Every kernel runs two waves per
+// SIMD (8 per CU), so a CU holds 8 / NW workgroups.  At D = 128 the
+// workgroup has 8 waves, so each K/V tile copied into LDS serves 256 or 512
+// query rows.  64 rows per wave halve the LDS and L2 traffic per flop; at
+// D = 128 that needs the single-buffered pipeline and part of Q^T in LDS to
+// fit the registers.  The wide tiles pay when they still give every slot of
+// the device a workgroup and no causal diagonal is wasted; otherwise the
+// 32-row waves are faster.
 struct TileCfg {
   int NW, QB, BN, QL;
   bool SB;
@@ -734,14 +754,63 @@ int device_info(DeviceInfo* out) {
   return d.gfx950 ? ATTN_OK : ATTN_EUNSUPPORTED;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+// Element strides of one tensor's batch, head and sequence dimensions; the
+// head dimension (D) is contiguous.
+struct Strides {
+  int64_t b, h, n;
+};
+struct Layout {
+  Strides q, k, v, o;
+};
+
+Layout contiguous_layout(int Hq, int Hkv, int Nq, int Nkv, int D) {
+  const Strides qs{(int64_t)Hq * Nq * D, (int64_t)Nq * D, D};
+  const Strides ks{(int64_t)Hkv * Nkv * D, (int64_t)Nkv * D, D};
+  return Layout{qs, ks, ks, qs};
+}
+
+// Bytes from a tensor's base to the end of its last element.
+__int128 extent_bytes(const Strides& s, int B, int H, int N, int D) {
+  return 2 * ((__int128)(B - 1) * s.b + (__int128)(H - 1) * s.h + (__int128)(N - 1) * s.n + D);
+}
+
+bool overlaps128(const void* a, __int128 na, const void* b, __int128 nb) {
+  const __int128 x = (__int128)(uintptr_t)a, y = (__int128)(uintptr_t)b;
   return x < y + nb && y < x + na;
+}
+
+// Strides the kernels can take: non-negative multiples of 8 elements (so
+// every row starts 16-byte aligned), row strides of at least one row (the
+// K/V copies rely on rows past the last key starting beyond its end) and at
+// most 2^24 elements (per-lane copy offsets are 32-bit).
+bool strides_ok(const Strides& s, int D) {
+  if (s.b < 0 || s.h < 0 || s.n < D || s.n > (1 << 24)) return false;
+  return ((s.b | s.h | s.n) & 7) == 0;
+}
+
+// No two elements of the output share an address: ordered by stride, each
+// dimension of extent > 1 must step over everything the smaller ones span.
+bool dense_enough(const Strides& s, int B, int H, int N, int D) {
+  int64_t st[3] = {s.b, s.h, s.n};
+  int64_t sz[3] = {B, H, N};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i]) {
+        std::swap(st[i], st[j]);
+        std::swap(sz[i], sz[j]);
+      }
+  __int128 span = D;  // the contiguous head dimension
+  for (int i = 0; i < 3; ++i) {
+    if (sz[i] == 1) continue;
+    if ((__int128)st[i] < span) return false;
+    span = (__int128)st[i] * sz[i];
+  }
+  return true;
 }
 
 int validate(const void* q, const void* k, const void* v, const void* out, const float* lse,
              int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
-             int dtype) {
+             int dtype, const Layout& L) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
   if (D != 64 && D != 128) return ATTN_EINVAL;
@@ -755,14 +824,17 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
   const size_t rows = (size_t)B * Hq * Nq;
   const size_t krows = (size_t)B * Hkv * Nkv;
   if (rows > (size_t)INT32_MAX || krows > (size_t)INT32_MAX) return ATTN_EINVAL;
-  const size_t qbytes = rows * D * 2, kbytes = krows * D * 2;
-  if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kbytes) ||
-      overlaps(out, qbytes, v, kbytes))
+  if (!strides_ok(L.q, D) || !strides_ok(L.k, D) || !strides_ok(L.v, D) || !strides_ok(L.o, D))
+    return ATTN_EINVAL;
+  if (!dense_enough(L.o, B, Hq, Nq, D)) return ATTN_EINVAL;
+  const __int128 qb = extent_bytes(L.q, B, Hq, Nq, D), ob = extent_bytes(L.o, B, Hq, Nq, D);
+  const __int128 kb = extent_bytes(L.k, B, Hkv, Nkv, D), vb = extent_bytes(L.v, B, Hkv, Nkv, D);
+  if (overlaps128(out, ob, q, qb) || overlaps128(out, ob, k, kb) || overlaps128(out, ob, v, vb))
     return ATTN_EINVAL;
   if (lse) {
-    const size_t lbytes = rows * 4;
-    if (overlaps(lse, lbytes, q, qbytes) || overlaps(lse, lbytes, k, kbytes) ||
-        overlaps(lse, lbytes, v, kbytes) || overlaps(lse, lbytes, out, qbytes))
+    const __int128 lb = (__int128)rows * 4;
+    if (overlaps128(lse, lb, q, qb) || overlaps128(lse, lb, k, kb) ||
+        overlaps128(lse, lb, v, vb) || overlaps128(lse, lb, out, ob))
       return ATTN_EINVAL;
   }
   return ATTN_OK;
@@ -863,47 +935,59 @@ Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits
 }
 
 template <int D, int CFG, class Tag, bool CAUSAL, bool SPLIT>
-hipError_t launch_main(const Params& p, hipStream_t stream) {
+hipError_t launch_main(const Params& p, bool strided, hipStream_t stream) {
   constexpr TileCfg c = kCfgs[CFG];
-  hipLaunchKernelGGL((attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT>),
-                     dim3(p.total),
-                     dim3(c.NW * 64), 0, stream, p);
+  if (strided)
+    hipLaunchKernelGGL(
+        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true>),
+        dim3(p.total), dim3(c.NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(
+        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, false>),
+        dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, int CFG, class Tag>
-hipError_t dispatch(const Params& p, bool causal, bool split, hipStream_t st) {
+hipError_t dispatch(const Params& p, bool causal, bool split, bool strided, hipStream_t st) {
   if (causal)
-    return split ? launch_main<D, CFG, Tag, true, true>(p, st)
-                 : launch_main<D, CFG, Tag, true, false>(p, st);
-  return split ? launch_main<D, CFG, Tag, false, true>(p, st)
-               : launch_main<D, CFG, Tag, false, false>(p, st);
+    return split ? launch_main<D, CFG, Tag, true, true>(p, strided, st)
+                 : launch_main<D, CFG, Tag, true, false>(p, strided, st);
+  return split ? launch_main<D, CFG, Tag, false, true>(p, strided, st)
+               : launch_main<D, CFG, Tag, false, false>(p, strided, st);
 }
 
 // The wide tiles are only selected without a causal mask.
 template <int D, class Tag>
-hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, hipStream_t st) {
+hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool strided,
+                      hipStream_t st) {
   constexpr int kNarrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
   constexpr int kWide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
   if (cfg == kWide && !causal)
-    return split ? launch_main<D, kWide, Tag, false, true>(p, st)
-                 : launch_main<D, kWide, Tag, false, false>(p, st);
-  return dispatch<D, kNarrow, Tag>(p, causal, split, st);
+    return split ? launch_main<D, kWide, Tag, false, true>(p, strided, st)
+                 : launch_main<D, kWide, Tag, false, false>(p, strided, st);
+  return dispatch<D, kNarrow, Tag>(p, causal, split, strided, st);
 }
 
 template <int D, class Tag>
-hipError_t launch_combine(const Params& p, hipStream_t st) {
+hipError_t launch_combine(const Params& p, bool strided, hipStream_t st) {
   const size_t threads = (size_t)p.prows * (D / 4);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((attn_combine_kernel<D, Tag>), dim3(blocks), dim3(256), 0, st, p.opart,
-                     p.lsepart, p.o, p.lse, p.prows, p.row0, p.n_splits);
+  if (strided)
+    hipLaunchKernelGGL((attn_combine_kernel<D, Tag, true>), dim3(blocks), dim3(256), 0, st,
+                       p.opart, p.lsepart, p.o, p.lse, p.prows, p.row0, p.n_splits, p.Hq, p.Nq,
+                       p.osb, p.osh, p.osn);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<D, Tag, false>), dim3(blocks), dim3(256), 0, st,
+                       p.opart, p.lsepart, p.o, p.lse, p.prows, p.row0, p.n_splits, p.Hq, p.Nq,
+                       p.osb, p.osh, p.osn);
   return hipGetLastError();
 }
 
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
-        int Nq, int Nkv, int D, float scale, int causal, int dtype, int num_splits,
-        hipStream_t stream) {
-  int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype);
+        int Nq, int Nkv, int D, const Layout& L, float scale, int causal, int dtype,
+        int num_splits, hipStream_t stream) {
+  int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype, L);
   if (rc != ATTN_OK) return rc;
   if (num_splits < 0) return ATTN_EINVAL;
   DeviceInfo di;
@@ -919,6 +1003,10 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
   p.o = (uint16_t*)out;
+  p.qsb = L.q.b, p.qsh = L.q.h, p.qsn = (int)L.q.n;
+  p.ksb = L.k.b, p.ksh = L.k.h, p.ksn = (int)L.k.n;
+  p.vsb = L.v.b, p.vsh = L.v.h, p.vsn = (int)L.v.n;
+  p.osb = L.o.b, p.osh = L.o.h, p.osn = (int)L.o.n;
   p.lse = lse;
   p.opart = nullptr;
   p.lsepart = nullptr;
@@ -951,12 +1039,15 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   }
 
   const bool cz = causal != 0;
+  const Layout C = contiguous_layout(Hq, Hkv, Nq, Nkv, D);
+  auto same = [](const Strides& a, const Strides& b) { return a.b == b.b && a.h == b.h && a.n == b.n; };
+  const bool strided = !(same(L.q, C.q) && same(L.k, C.k) && same(L.v, C.v) && same(L.o, C.o));
   auto launch = [&](bool split) {
     if (D == 64)
-      return dtype == ATTN_BF16 ? dispatch_d<64, TagBF16>(p, pl.cfg, cz, split, stream)
-                                : dispatch_d<64, TagF16>(p, pl.cfg, cz, split, stream);
-    return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, stream)
-                              : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, stream);
+      return dtype == ATTN_BF16 ? dispatch_d<64, TagBF16>(p, pl.cfg, cz, split, strided, stream)
+                                : dispatch_d<64, TagF16>(p, pl.cfg, cz, split, strided, stream);
+    return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, strided, stream)
+                              : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, strided, stream);
   };
   hipError_t e = hipSuccess;
   if (pl.first_split > 0) {  // whole tiles
@@ -970,11 +1061,11 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     e = launch(true);
     if (e == hipSuccess) {
       if (D == 64)
-        e = dtype == ATTN_BF16 ? launch_combine<64, TagBF16>(p, stream)
-                               : launch_combine<64, TagF16>(p, stream);
+        e = dtype == ATTN_BF16 ? launch_combine<64, TagBF16>(p, strided, stream)
+                               : launch_combine<64, TagF16>(p, strided, stream);
       else
-        e = dtype == ATTN_BF16 ? launch_combine<128, TagBF16>(p, stream)
-                               : launch_combine<128, TagF16>(p, stream);
+        e = dtype == ATTN_BF16 ? launch_combine<128, TagBF16>(p, strided, stream)
+                               : launch_combine<128, TagF16>(p, strided, stream);
     }
   }
   if (ws) {
@@ -994,21 +1085,61 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
              int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype, void* stream) {
-  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype, 0,
-             (hipStream_t)stream);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, contiguous_layout(Hq, Hkv, Nq, Nkv, D),
+             scale, causal, dtype, 0, (hipStream_t)stream);
 }
 
 int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype,
                    int num_splits, void* stream) {
-  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype, num_splits,
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, contiguous_layout(Hq, Hkv, Nq, Nkv, D),
+             scale, causal, dtype, num_splits, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+// Strides from the C arrays (batch, head, sequence); NULL = contiguous.
+Layout strided_layout(int Hq, int Hkv, int Nq, int Nkv, int D, const long long* qs,
+                      const long long* ks, const long long* vs, const long long* os) {
+  Layout L = contiguous_layout(Hq, Hkv, Nq, Nkv, D);
+  auto take = [](Strides& s, const long long* a) {
+    if (a) s = Strides{a[0], a[1], a[2]};
+  };
+  take(L.q, qs);
+  take(L.k, ks);
+  take(L.v, vs);
+  take(L.o, os);
+  return L;
+}
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                     int Hq, int Hkv, int Nq, int Nkv, int D, const long long* q_stride,
+                     const long long* k_stride, const long long* v_stride,
+                     const long long* o_stride, float scale, int causal, int dtype,
+                     int num_splits, void* stream) {
+  const Layout L = strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, L, scale, causal, dtype, num_splits,
              (hipStream_t)stream);
 }
 
 int attn_fwd_check(const void* q, const void* k, const void* v, const void* out, const float* lse,
                    int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
                    int dtype) {
-  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype);
+  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
+                  contiguous_layout(Hq, Hkv, Nq, Nkv, D));
+}
+
+int attn_fwd_strided_check(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                           const long long* q_stride, const long long* k_stride,
+                           const long long* v_stride, const long long* o_stride, float scale,
+                           int causal, int dtype) {
+  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
+                  strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride));
 }
 
 int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,

@@ -1,0 +1,122 @@
+"""CPU tests of the SDPA front end and the strided C ABI validation.
+
+No GPU work: the front end's argument screening runs on CPU tensors (every
+check before the device check), patch() is exercised with CPU calls that it
+hands to PyTorch, and the strided validation entry point makes no HIP call.
+"""
+import ctypes
+
+import pytest
+import torch
+import torch.nn.functional as F
+
+import memory_efficient_tiled_amd as mta
+from memory_efficient_tiled_amd import binding, frontend
+
+OK, EINVAL = binding.ATTN_OK, binding.ATTN_EINVAL
+BF16 = binding.ATTN_BF16
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def t(*shape, dtype=torch.float16, **kw):
+    return torch.zeros(*shape, dtype=dtype, **kw)
+
+
+def reason(q, k, v, **kw):
+    return frontend.unsupported_reason(q, k, v, **kw)
+
+
+def test_cpu_tensors_only_fail_the_device_check():
+    q = t(2, 4, 100, 64)
+    assert reason(q, q, q) == "inputs must be on one HIP device"
+    # [B, N, H, E] storage viewed as [B, H, N, E]: accepted layout
+    s = t(2, 100, 4, 128).transpose(1, 2)
+    assert reason(s, s, s) == "inputs must be on one HIP device"
+
+
+@pytest.mark.parametrize("kw,frag", [
+    ({"attn_mask": t(100, 100)}, "attn_mask"),
+    ({"dropout_p": 0.1}, "dropout"),
+])
+def test_unsupported_arguments(kw, frag):
+    q = t(1, 2, 100, 64)
+    assert frag in reason(q, q, q, **kw)
+
+
+def test_unsupported_inputs():
+    q = t(1, 2, 100, 64)
+    assert "dtype" in reason(q.float(), q.float(), q.float())
+    assert "head dimension" in reason(t(1, 2, 10, 80), t(1, 2, 10, 80), t(1, 2, 10, 80))
+    assert "3-D" in reason(t(2, 100, 64)[0], t(2, 100, 64)[0], t(2, 100, 64)[0])
+    k = t(1, 1, 100, 64)
+    assert "enable_gqa" in reason(q, k, k)
+    assert reason(q, k, k, enable_gqa=True) == "inputs must be on one HIP device"
+    assert "multiple" in reason(t(1, 3, 10, 64), t(1, 2, 10, 64), t(1, 2, 10, 64),
+                                enable_gqa=True)
+    assert "last dimension" in reason(t(1, 2, 64, 100).transpose(2, 3), q, q)
+    padded = t(1, 2, 100, 68)[..., :64]          # row stride 68: not a multiple of 8
+    assert "multiples of 8" in reason(padded, padded, padded)
+    g = t(1, 2, 10, 64).requires_grad_()
+    assert "backward" in reason(g, g, g)
+    assert "scale" in reason(q, q, q, scale=float("inf"))
+
+
+def test_sdpa_raises_for_unsupported_calls():
+    q = t(1, 2, 10, 64)
+    with pytest.raises(NotImplementedError):
+        mta.sdpa(q, q, q, attn_mask=t(10, 10))
+
+
+def test_patch_routes_and_restores():
+    orig = F.scaled_dot_product_attention
+    q = torch.randn(1, 2, 10, 64)
+    ref = orig(q, q, q)
+    try:
+        mta.patch(fallback=False)
+        assert F.scaled_dot_product_attention is not orig
+        with pytest.raises(NotImplementedError):
+            F.scaled_dot_product_attention(q, q, q)     # CPU: not served, no fallback
+        mta.patch(fallback=True)
+        before = mta.sdpa_stats()["fallback"]
+        out = F.scaled_dot_product_attention(q, q, q)
+        assert torch.equal(out, ref)
+        assert mta.sdpa_stats()["fallback"] == before + 1
+    finally:
+        mta.unpatch()
+    assert F.scaled_dot_product_attention is orig
+
+
+def strides(*s):
+    return (ctypes.c_longlong * 3)(*s)
+
+
+def check(qs=None, ks=None, vs=None, os_=None, B=2, Hq=4, Hkv=2, Nq=100, Nkv=300,
+          D=128, out=O):
+    lib = mta.load_library()
+    return lib.attn_fwd_strided_check(Q, K, V, out, L, B, Hq, Hkv, Nq, Nkv, D,
+                                      qs, ks, vs, os_, 0.088, 0, BF16)
+
+
+def test_strided_check_accepts_common_layouts():
+    assert check() == OK                                           # NULL: contiguous
+    # [B, N, H, D] storage of every tensor
+    assert check(strides(100 * 4 * 128, 128, 4 * 128), strides(300 * 2 * 128, 128, 2 * 128),
+                 strides(300 * 2 * 128, 128, 2 * 128), strides(100 * 4 * 128, 128, 4 * 128)) == OK
+    # padded rows, broadcast batch stride of K/V (B > 1, stride 0 for reads only)
+    assert check(qs=strides(4 * 100 * 136, 100 * 136, 136), ks=strides(0, 300 * 128, 128)) == OK
+    # contiguous layout spelled out equals NULL
+    lib = mta.load_library()
+    assert lib.attn_fwd_check(Q, K, V, O, L, 2, 4, 2, 100, 300, 128, 0.088, 0, BF16) == OK
+
+
+@pytest.mark.parametrize("kw", [
+    {"qs": strides(4 * 100 * 128, 100 * 128, 64)},         # row stride < D
+    {"ks": strides(0, 300 * 128, 132)},                     # not a multiple of 8
+    {"vs": strides(-8, 300 * 128, 128)},                     # negative
+    {"ks": strides(0, 0, 1 << 25)},                          # row stride > 2^24
+    {"os_": strides(4 * 100 * 128, 0, 128)},                 # output heads overlap
+    {"os_": strides(4 * 100 * 128, 128, 128)},               # output rows overlap heads
+    {"os_": strides(4 * 100 * 128, 100 * 128, 128), "out": Q + 256},  # out overlaps q
+])
+def test_strided_check_rejects(kw):
+    assert check(**kw) == EINVAL

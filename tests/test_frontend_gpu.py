@@ -1,0 +1,138 @@
+"""GPU parity of strided layouts and of the SDPA front end against the oracle.
+
+Inputs are the seeded generator's [B, H, N, D] arrays; on the device they
+are stored in another layout and handed over as views, so the kernels read
+them through strides.  Expected values come from the CPU oracle on the
+logical arrays.
+"""
+import numpy as np
+import pytest
+
+from memory_efficient_tiled_amd import binding, inputs
+from tests.parity import compare, gather_rows, log, oracle_rows, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _view(a, dtype, device, layout):
+    """Device view of logical [B, H, N, D] array `a` stored as `layout`."""
+    if layout == "bhnd":
+        return to_device(a, dtype, device)
+    if layout == "bnhd":       # sequence-major storage, heads interleaved
+        return to_device(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), dtype,
+                         device).transpose(1, 2)
+    if layout == "padded":     # rows of D + 8 elements
+        pad = np.zeros(a.shape[:3] + (8,), dtype=a.dtype)
+        return to_device(np.concatenate([a, pad], axis=3), dtype, device)[..., :a.shape[3]]
+    raise ValueError(layout)
+
+
+def _empty_out(B, H, N, D, like, layout):
+    import torch
+    if layout == "bnhd":
+        return torch.empty(B, N, H, D, dtype=like.dtype, device=like.device).transpose(1, 2)
+    return torch.empty(B, H, N, D, dtype=like.dtype, device=like.device)
+
+
+def _case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, layout, out_layout,
+          seed, rows=None, num_splits=0):
+    import torch
+    log(f"strided case {layout}->{out_layout} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} "
+        f"Nkv={Nkv} D={D} {dtype} causal={causal} splits={num_splits}")
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed, sampled_rows=rows)
+    q, k, v = (_view(a, dtype, device, layout) for a in (x.q, x.k, x.v))
+    assert layout == "bhnd" or not q.is_contiguous()
+    out = _empty_out(B, Hq, Nq, D, q, out_layout)
+    o, l = binding.attn_fwd(q, k, v, causal=causal, out=out, num_splits=num_splits)
+    torch.cuda.synchronize(device)
+    o = o.float().cpu().numpy().astype(np.float64)
+    l = l.cpu().numpy().astype(np.float64)
+    r = None if rows is None else x.rows
+    o_ref, l_ref = oracle_rows(x, None, causal, rows=r)
+    if r is not None:
+        o, l = gather_rows(o, r), gather_rows(l, r)
+    compare(o, l, o_ref, l_ref, dtype, rounding_allowance=True,
+            what=f"{layout} N={Nq}x{Nkv} D={D} {dtype} causal={causal}")
+
+
+def test_strided_wide_d128_with_last_round_split(gpu_device):
+    # 512-row tiles, 64 x 5 = 320 tiles: the last 64 are split and merged,
+    # the merge writing through the output's strides
+    _case(gpu_device, 1, 64, 8, 2100, 1000, 128, inputs.BF16, False, "bnhd", "bnhd",
+          seed=21, rows=24)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_strided_narrow_d128(gpu_device, causal):
+    _case(gpu_device, 2, 4, 2, 300, 300, 128, inputs.BF16, causal, "bnhd", "bhnd", seed=22)
+
+
+def test_padded_rows_gqa_causal_d64(gpu_device):
+    _case(gpu_device, 1, 14, 2, 1000, 1000, 64, inputs.F16, True, "padded", "padded",
+          seed=23, rows=64)
+
+
+def test_strided_wide_d64(gpu_device):
+    _case(gpu_device, 2, 32, 8, 2100, 2000, 64, inputs.F16, False, "bnhd", "bnhd",
+          seed=24, rows=24)
+
+
+@pytest.mark.parametrize("splits", [3, 8])
+def test_strided_forced_splits(gpu_device, splits):
+    _case(gpu_device, 1, 3, 1, 200, 1500, 64, inputs.F16, True, "bnhd", "bnhd",
+          seed=25, num_splits=splits)
+
+
+# -- the SDPA front end --------------------------------------------------------
+
+def _oracle_out(x, causal):
+    o_ref, _ = oracle_rows(x, None, causal)
+    return o_ref
+
+
+def test_sdpa_matches_oracle(gpu_device):
+    import torch
+    import memory_efficient_tiled_amd as mta
+    x = inputs.make_inputs(2, 8, 2, 333, 333, 128, inputs.BF16, seed=26)
+    q, k, v = (_view(a, inputs.BF16, gpu_device, "bnhd") for a in (x.q, x.k, x.v))
+    o = mta.sdpa(q, k, v, is_causal=True, enable_gqa=True)
+    torch.cuda.synchronize(gpu_device)
+    assert o.shape == q.shape and o.is_contiguous()
+    compare(o.float().cpu().numpy().astype(np.float64), None, _oracle_out(x, True), None,
+            inputs.BF16, rounding_allowance=True, what="sdpa 4-D")
+
+
+def test_sdpa_three_dimensional(gpu_device):
+    import torch
+    import memory_efficient_tiled_amd as mta
+    x = inputs.make_inputs(1, 4, 4, 100, 260, 64, inputs.F16, seed=27)
+    q, k, v = (to_device(a, inputs.F16, gpu_device)[0] for a in (x.q, x.k, x.v))
+    o = mta.sdpa(q, k, v)
+    torch.cuda.synchronize(gpu_device)
+    assert o.shape == q.shape
+    compare(o.float().cpu().numpy().astype(np.float64)[None], None, _oracle_out(x, False),
+            None, inputs.F16, rounding_allowance=True, what="sdpa 3-D")
+
+
+def test_patched_torch_sdpa(gpu_device):
+    import torch
+    import torch.nn.functional as F
+    import memory_efficient_tiled_amd as mta
+    x = inputs.make_inputs(1, 4, 4, 150, 150, 64, inputs.F16, seed=28)
+    q, k, v = (to_device(a, inputs.F16, gpu_device) for a in (x.q, x.k, x.v))
+    try:
+        mta.patch(fallback=True)
+        s0 = mta.sdpa_stats()
+        o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+        torch.cuda.synchronize(gpu_device)
+        s1 = mta.sdpa_stats()
+        assert s1["native"] == s0["native"] + 1
+        compare(o.float().cpu().numpy().astype(np.float64), None, _oracle_out(x, True),
+                None, inputs.F16, rounding_allowance=True, what="patched sdpa")
+        # float32 is not served: handed to PyTorch's own (float32) attention
+        qf, kf, vf = q.float(), k.float(), v.float()
+        F.scaled_dot_product_attention(qf, kf, vf)
+        torch.cuda.synchronize(gpu_device)
+        assert mta.sdpa_stats()["fallback"] == s1["fallback"] + 1
+    finally:
+        mta.unpatch()
