@@ -1,9 +1,10 @@
-"""CPU oracle (float64) for the attention forward -- test infrastructure only.
+"""CPU oracle (float64) for attention forward and gradients -- test infrastructure only.
 
 Only tests, the smoke check and the bench's CPU-baseline leg may use it.
 """
-from .softmax_attention import (attention, attention_from_storage,
-                        decode, decode_bf16, decode_f16, scale_value)
+from .softmax_attention import (attention, attention_backward,
+                                attention_from_storage, decode, decode_bf16,
+                                decode_f16, scale_value)
 
-__all__ = ["attention", "attention_from_storage",
+__all__ = ["attention", "attention_backward", "attention_from_storage",
            "decode", "decode_bf16", "decode_f16", "scale_value"]

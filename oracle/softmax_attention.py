@@ -135,3 +135,65 @@ def attention_from_storage(q, k, v, dtype: str, scale: float | None,
     D = q.shape[-1]
     return attention(decode(q, dtype), decode(k, dtype), decode(v, dtype),
                      scale_value(scale, D), causal, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# The gradients.
+# ---------------------------------------------------------------------------
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                       do: np.ndarray, scale: float, causal: bool,
+                       row_group: int = 256):
+    """Gradients of softmax attention in float64: (dq, dk, dv).
+
+    For a loss whose gradient with respect to the output is ``do``
+    ([B, Hq, Nq, D]), the chain rule through the definition above, row by
+    row: with P_ij = exp(s_ij - lse_i) over the allowed keys,
+
+        dv_j  += sum_i P_ij do_i                  (dO flows through the sum)
+        dP_ij  = <do_i, v_j>
+        dS_ij  = P_ij (dP_ij - sum_l P_il dP_il)  (the softmax Jacobian)
+        dq_i   = scale * sum_j dS_ij k_j
+        dk_j  += scale * sum_i dS_ij q_i
+
+    K/V gradients of a KV head sum over the query heads that read it (the
+    GQA grouping of the forward).  Masked keys have P = 0 and get nothing
+    from that row.  The post's first tier keeps autograd through its tiled
+    forward (section "The DIY approach"); these are the gradients it yields.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nkv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or do.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v and do")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    key_idx = np.arange(Nkv, dtype=np.int64)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            kk = k[b, hk]
+            vv = v[b, hk]
+            for r0 in range(0, Nq, row_group):
+                ri = np.arange(r0, min(Nq, r0 + row_group), dtype=np.int64)
+                s = scale * (q[b, hq, ri] @ kk.T)
+                if causal:
+                    s = np.where(key_idx[None, :] <= ri[:, None], s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                p = e / e.sum(axis=1, keepdims=True)              # softmax rows
+                g = do[b, hq, ri]                                  # dL/dO rows
+                dv[b, hk] += p.T @ g
+                dp = g @ vv.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, hq, ri] = scale * (ds @ kk)
+                dk[b, hk] += scale * (ds.T @ q[b, hq, ri])
+    return dq, dk, dv

@@ -1,0 +1,99 @@
+"""Pins for the oracle's attention gradients: facts fixed by mathematics.
+
+Every pin takes ``bwd(q, k, v, do, scale, causal) -> (dq, dk, dv)`` (float64
+arrays, q/do [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D]) and raises AssertionError when
+it disagrees.  The strongest is the derivative itself: central finite
+differences of the (separately pinned) forward oracle along random
+directions.  ``test_oracle.py`` runs them on the oracle and on copies of it
+with planted mistakes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _inputs(seed, B=1, Hq=2, Hkv=1, Nq=6, Nkv=7, D=4):
+    r = _rng(seed)
+    return (r.standard_normal((B, Hq, Nq, D)), r.standard_normal((B, Hkv, Nkv, D)),
+            r.standard_normal((B, Hkv, Nkv, D)), r.standard_normal((B, Hq, Nq, D)))
+
+
+def _close(a, b, tol, what):
+    err = float(np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))))
+    assert err <= tol, f"{what}: rel err {err:.3e} > {tol:.1e}"
+
+
+def pin_finite_differences(bwd):
+    """<grad, direction> equals the central difference of L = sum(O * dO)."""
+    for seed, causal, Nq, Nkv in ((1, False, 6, 7), (2, True, 7, 7), (3, True, 5, 9)):
+        q, k, v, do = _inputs(seed, Nq=Nq, Nkv=Nkv)
+        scale = 0.7
+        dq, dk, dv = bwd(q, k, v, do, scale, causal)
+        r = _rng(100 + seed)
+        h = 1e-5
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            d = r.standard_normal(x.shape)
+            def loss(xx):
+                args = {"q": q, "k": k, "v": v}
+                args[name] = xx
+                o, _ = oracle.attention(args["q"], args["k"], args["v"], scale, causal)
+                return float(np.sum(o * do))
+            fd = (loss(x + h * d) - loss(x - h * d)) / (2 * h)
+            an = float(np.sum(g * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), \
+                f"d{name} (causal={causal}): finite difference {fd:.10f} vs {an:.10f}"
+
+
+def pin_causal_row0_dq(bwd):
+    """Causal row 0 sees only key 0 (P = 1), so its dS row is exactly 0."""
+    q, k, v, do = _inputs(4, Nq=6, Nkv=6)
+    dq, _, _ = bwd(q, k, v, do, 0.5, True)
+    assert np.all(dq[:, :, 0] == 0.0), "dq of causal row 0 must vanish"
+
+
+def pin_zero_do(bwd):
+    q, k, v, do = _inputs(5)
+    for g in bwd(q, k, v, np.zeros_like(do), 0.5, False):
+        assert np.all(g == 0.0), "zero output gradient must give zero gradients"
+
+
+def pin_column_sums(bwd):
+    """Rows of P sum to 1 and rows of dS to 0, so summed over keys
+    dv = sum of do over the query rows of the group, and dk sums to 0."""
+    for causal in (False, True):
+        q, k, v, do = _inputs(6, Hq=4, Hkv=2, Nq=8, Nkv=8)
+        _, dk, dv = bwd(q, k, v, do, 0.8, causal)
+        G = 2
+        for hk in range(2):
+            want = do[0, hk * G:(hk + 1) * G].sum(axis=(0, 1))
+            _close(dv[0, hk].sum(axis=0), want, 1e-12, f"sum of dv (causal={causal})")
+            _close(dk[0, hk].sum(axis=0), np.zeros(4), 1e-12, f"sum of dk (causal={causal})")
+
+
+def pin_linear_in_do(bwd):
+    q, k, v, d1 = _inputs(7)
+    d2 = _inputs(8)[3]
+    g1, g2, g12 = (bwd(q, k, v, d, 0.5, True) for d in (d1, d2, 2.0 * d1 - 3.0 * d2))
+    for a, b, c in zip(g1, g2, g12):
+        _close(c, 2.0 * a - 3.0 * b, 1e-12, "linearity in do")
+
+
+def pin_gqa_repeat(bwd):
+    """GQA equals MHA on repeated K/V with the K/V gradients summed back."""
+    q, k, v, do = _inputs(9, Hq=6, Hkv=2, Nq=5, Nkv=6)
+    dq, dk, dv = bwd(q, k, v, do, 0.6, False)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    dq2, dkr, dvr = bwd(q, kr, vr, do, 0.6, False)
+    _close(dq, dq2, 1e-12, "gqa dq")
+    _close(dk, dkr.reshape(1, 2, 3, 6, 4).sum(axis=2), 1e-12, "gqa dk")
+    _close(dv, dvr.reshape(1, 2, 3, 6, 4).sum(axis=2), 1e-12, "gqa dv")
+
+
+ALL_PINS = [pin_finite_differences, pin_causal_row0_dq, pin_zero_do, pin_column_sums,
+            pin_linear_in_do, pin_gqa_repeat]

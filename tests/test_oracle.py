@@ -67,6 +67,52 @@ def test_pins_catch_planted_mistake(name, original, replacement):
     assert caught, f"no pin catches the planted mistake: {name}"
 
 
+from tests import oracle_bwd_pins
+
+
+@pytest.mark.parametrize("pin", oracle_bwd_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_backward_pin(pin):
+    pin(oracle.attention_backward)
+
+
+BWD_MUTANTS = [
+    ("dq without scale", "dq[b, hq, ri] = scale * (ds @ kk)", "dq[b, hq, ri] = (ds @ kk)"),
+    ("jacobian without the row term", "ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))",
+     "ds = p * dp"),
+    ("dv uses unnormalised weights", "dv[b, hk] += p.T @ g", "dv[b, hk] += e.T @ g"),
+    ("dk from k instead of q", "dk[b, hk] += scale * (ds.T @ q[b, hq, ri])",
+     "dk[b, hk] += scale * (ds.T @ kk[ri % kk.shape[0]])"),
+    ("dp against k", "dp = g @ vv.T", "dp = g @ kk.T"),
+    ("dk overwritten, not summed over the group", "dk[b, hk] += scale", "dk[b, hk] = scale"),
+    ("causal off by one", "key_idx[None, :] <= ri[:, None], s, -np.inf)\n                m = s.max(axis=1, keepdims=True)\n                e = np.exp(s - m)\n                p = e",
+     "key_idx[None, :] < ri[:, None] + 2, s, -np.inf)\n                m = s.max(axis=1, keepdims=True)\n                e = np.exp(s - m)\n                p = e"),
+]
+
+
+def _bwd_mutant(original, replacement):
+    src = inspect.getsource(oracle_mod)
+    assert src.count(original) >= 1, f"mutation anchor not found: {original!r}"
+    start = src.index("def attention_backward(")
+    src = src[:start] + src[start:].replace(original, replacement, 1)
+    mod = types.ModuleType("oracle_bwd_mutant")
+    exec(compile(src, "<oracle backward mutant>", "exec"), mod.__dict__)
+    return mod.attention_backward
+
+
+@pytest.mark.parametrize("name,original,replacement", BWD_MUTANTS,
+                         ids=[m[0] for m in BWD_MUTANTS])
+def test_backward_pins_catch_planted_mistake(name, original, replacement):
+    bwd = _bwd_mutant(original, replacement)
+    caught = []
+    for pin in oracle_bwd_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(bwd)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake: {name}"
+
+
 def test_decode_bf16_known_patterns():
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x7F80, 0x0001,
                      0x7F7F], dtype=np.uint16)
