@@ -34,64 +34,22 @@
 // row sum, plus its partial log-sum-exp, and a second kernel merges them with
 // weights exp(lse_s - lse).
 
-#include <hip/hip_runtime.h>
-
-#include <float.h>
-#include <math.h>
-#include <stdint.h>
-#include <string.h>
+#include "attn_common.h"
 
 #include <mutex>
-#include <utility>
 #include <type_traits>
-
-#include "attn.h"
+#include <utility>
 
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-
-struct TagF16 {};
-struct TagBF16 {};
-
-template <class Tag>
-struct Num;
-
-template <>
-struct Num<TagBF16> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  // Two fp32 -> two bf16 (round to nearest even) in one 32-bit word.
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    f32x2 x = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-  }
-};
-
-template <>
-struct Num<TagF16> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    f32x2 x = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
-  }
-};
+// Probabilities are formed against a running reference max m that is only
+// raised when a tile would otherwise produce a probability above 2^8: the
+// final O / l and lse = m + log2(l) are the same function of the scores for
+// any reference, so the result is unchanged up to rounding.  The check is
+// done on the in-lane partial row sum (each term is at most the sum), which
+// the softmax needs anyway, so no per-tile row max is computed unless a tile
+// fails it (and on the first tile, where m is still -inf).
+constexpr float kMaxPartialSum = 256.0f;
 
 struct Params {
   const uint16_t* q;
@@ -113,87 +71,6 @@ struct Params {
   int64_t qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
   int qsn, ksn, vsn, osn;
 };
-
-// Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
-// so that each XCD receives a contiguous range of logical tiles: the query
-// tiles of one head then share that XCD's L2 for their K/V stream.
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int q = total >> 3, r = total & 7;
-  const int x = bid & 7, s = bid >> 3;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Copy one 16-byte chunk per lane from global memory straight into LDS: lane
-// i of the wave writes lds_base + 16*i (lds_base must be wave-uniform).
-__device__ __forceinline__ void g2lds16(const uint16_t* g, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
-// Transposing LDS read: in each 16-lane group, lane i receives element i%4 of
-// the 4-element (8-byte) words addressed by lanes 4e + i/4, e = 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  typedef short i16x4 __attribute__((ext_vector_type(4)));
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// Both halves of the wave exchange a value; the max (sum) of the two results
-// is the max (sum) over lanes l and l^32, identical in both lanes.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// LDS swizzles.  gfx950 serves a 16-byte LDS read 16 lanes (256 bytes, all
-// 64 banks) at a time and an 8-byte read 32 lanes at a time, so a pattern is
-// conflict-free when those lanes cover 16 distinct 16-byte bank groups.
-//  * K operand reads: the 16 lanes of a group read the same chunk of 16
-//    consecutive key rows.  With 256-byte rows (D = 128) the chunk is XORed
-//    with r & 15; with 128-byte rows (D = 64) two rows share the 64 banks and
-//    the chunk is XORed with (r >> 1) & 7.
-//  * V^T operand reads (transposing, 8 bytes per lane): 32 lanes read 4 keys
-//    x 64 contiguous bytes.  With 256-byte rows the 4 keys go to 4 disjoint
-//    64-byte quarters (XOR 4 * (r & 3)); with 128-byte rows keys r and r + 2
-//    share banks and are separated by XOR 4 * ((r >> 1) & 1).
-template <int D>
-__device__ __forceinline__ int k_swz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
-
-// Probabilities are formed against a running reference max m that is only
-// raised when a tile would otherwise produce a probability above 2^8: the
-// final O / l and lse = m + log2(l) are the same function of the scores for
-// any reference, so the result is unchanged up to rounding.  The check is
-// done on the in-lane partial row sum (each term is at most the sum), which
-// the softmax needs anyway, so no per-tile row max is computed unless a tile
-// fails it (and on the first tile, where m is still -inf).
-constexpr float kMaxPartialSum = 256.0f;
-
-// Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9.
-constexpr int kRawBufferFlags = 0x00020000;
-
-// Waves per SIMD that every kernel is compiled for: each wave may use up to
-// 256 of the SIMD's 512 vector registers (arch + accumulation).
-constexpr int kWavesPerSimd = 2;
-
-// Copy 16 bytes per lane from a buffer into LDS: lane i writes lds + 16 i
-// (lds wave-uniform).  Offsets at or beyond the buffer's size read zero.
-__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
-}
 
 // One workgroup: NW waves x QB x 32 query rows, all on KV head hq / G,
 // looping over BN-key tiles of its key range.  Each K or V operand read from
@@ -1081,6 +958,16 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
 
 }  // namespace
 
+namespace attn_host {
+int check_device(int* cus) {
+  DeviceInfo di;
+  const int rc = device_info(&di);
+  if (cus) *cus = di.cus;
+  return rc;
+}
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace attn_host
+
 extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
@@ -1177,7 +1064,7 @@ const char* attn_strerror(int code) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument";
     case ATTN_EUNSUPPORTED: return "unsupported device (gfx950 required)";
-    case ATTN_ENOMEM: return "split-KV workspace allocation failed";
+    case ATTN_ENOMEM: return "device workspace allocation failed";
     case ATTN_EHIP: return "HIP launch or runtime error";
     default: return "unknown error code";
   }
