@@ -1,5 +1,6 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) memory-efficient attention forward.
+ * attn.h -- C ABI of the MI355X (gfx950) memory-efficient attention forward
+ * and its gradients.
  *
  * The operation is the one the English noflash-attention post
  * (ai-navigate-news.com, section "The DIY approach") tiles over query chunks
@@ -47,7 +48,7 @@ enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,       /* bad argument (shape, pointer, alignment, dtype, scale) */
   ATTN_EUNSUPPORTED = -2, /* the current device is not gfx950 */
-  ATTN_ENOMEM = -3,       /* split-KV workspace could not be allocated */
+  ATTN_ENOMEM = -3,       /* a device workspace could not be allocated */
   ATTN_EHIP = -4          /* a HIP call or kernel launch failed */
 };
 
@@ -174,6 +175,49 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D,
  */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
                                 int num_splits);
+
+/*
+ * attn_bwd -- gradients of attn_fwd's O with respect to Q, K and V.
+ *
+ * The post keeps training possible through its tiled forward (first tier,
+ * section "The DIY approach": the chunked attention stays differentiable).
+ * With P[i,j] = exp(scale <Q_i, K_j> - LSE_i) over J_i (0 elsewhere) and dO
+ * the gradient arriving at O:
+ *
+ *     dV_j = sum_i P[i,j] dO_i,        dP[i,j] = <dO_i, V_j>,
+ *     Delta_i = <dO_i, O_i>,           dS[i,j] = P[i,j] (dP[i,j] - Delta_i),
+ *     dQ_i = scale sum_j dS[i,j] K_j,  dK_j = scale sum_i dS[i,j] Q_i,
+ *
+ * where the sums for dK and dV of a KV head run over every query head of its
+ * group.  The probabilities are recomputed tile by tile from `lse`; nothing
+ * of size Nq x Nkv is stored.
+ *
+ * q, k, v  : the forward's inputs (contiguous [B,H,N,D], fp16/bf16).
+ * out, lse : the forward's outputs for these inputs (attn_fwd with the same
+ *            scale and causal flag; `lse` must not be NULL).
+ * dout     : [B,Hq,Nq,D], same dtype: the gradient at `out`.
+ * dq       : [B,Hq,Nq,D]; dk, dv: [B,Hkv,Nkv,D]; same dtype, written
+ *            completely (no accumulation into their previous contents);
+ *            must not overlap each other or any input.
+ * All pointers 16-byte aligned; D in {64, 128}; Hq a multiple of Hkv.
+ * Allocates a float32 [B,Hq,Nq] workspace (Delta) on `stream` with
+ * hipMallocAsync and frees it there.  Returns ATTN_OK, ATTN_EINVAL,
+ * ATTN_EUNSUPPORTED, ATTN_ENOMEM or ATTN_EHIP.  Results are deterministic
+ * (no atomics).
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out,
+             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale,
+             int causal, int dtype, void* stream);
+
+/*
+ * attn_bwd_check -- host only: attn_bwd's argument validation; makes no HIP
+ * call and dereferences no pointer.  Returns ATTN_OK or ATTN_EINVAL.
+ */
+int attn_bwd_check(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, const void* dq,
+                   const void* dk, const void* dv, int B, int Hq, int Hkv,
+                   int Nq, int Nkv, int D, float scale, int causal, int dtype);
 
 /* attn_strerror -- static description of a return code (never NULL). */
 const char* attn_strerror(int code);

@@ -1,14 +1,15 @@
-"""MI355X-native memory-efficient (tiled, online-softmax) attention forward.
+"""MI355X-native memory-efficient (tiled, online-softmax) attention: forward
+and gradients.
 
 The compute path is the HIP library ``libattn.so`` (built from ``csrc/``);
 this package only marshals arguments to its C entry points.
 """
-from .binding import (attn_fwd, attn_fwd_check, attn_fwd_num_splits,
+from .binding import (attn_bwd, attn_bwd_check, attn_fwd, attn_fwd_check, attn_fwd_num_splits,
                       attn_fwd_plan, attn_fwd_workspace_bytes, lib_path,
                       load_library, AttnError, AttnPlan)
 from .frontend import patch, sdpa, stats as sdpa_stats, unpatch, unsupported_reason
 
-__all__ = ["attn_fwd", "attn_fwd_check", "attn_fwd_num_splits",
+__all__ = ["attn_bwd", "attn_bwd_check", "attn_fwd", "attn_fwd_check", "attn_fwd_num_splits",
            "attn_fwd_plan", "attn_fwd_workspace_bytes", "lib_path",
            "load_library", "AttnError", "AttnPlan", "sdpa", "patch", "unpatch",
            "sdpa_stats", "unsupported_reason"]

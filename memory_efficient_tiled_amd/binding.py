@@ -1,6 +1,7 @@
 """ctypes binding to libattn.so -- argument marshalling only.
 
-Every step of the attention forward runs in the HIP library; this module
+Every step of the attention forward and of its gradients runs in the HIP
+library; this module
 checks tensor metadata, allocates the outputs with torch (device memory is
 torch's), passes raw device pointers and torch's current HIP stream, and turns
 non-zero return codes into exceptions.  There is no fallback: if the library
@@ -85,6 +86,10 @@ def load_library():
     lib.attn_fwd_num_splits.restype = _INT
     lib.attn_fwd_workspace_bytes.argtypes = [_INT, _INT, _INT, _INT, _INT, _INT]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [_VP] * 9 + shape_args + [ctypes.c_float, _INT, _INT, _VP]
+    lib.attn_bwd.restype = _INT
+    lib.attn_bwd_check.argtypes = [_VP] * 9 + shape_args + [ctypes.c_float, _INT, _INT]
+    lib.attn_bwd_check.restype = _INT
     lib.attn_strerror.argtypes = [_INT]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -205,3 +210,68 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
     if rc != ATTN_OK:
         _raise(rc)
     return (out, lse) if return_lse else out
+
+
+def attn_bwd_check(q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr, dk_ptr,
+                   dv_ptr, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype_code) -> int:
+    """Host-only validation of attn_bwd's arguments; returns the error code."""
+    return load_library().attn_bwd_check(q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr,
+                                         dq_ptr, dk_ptr, dv_ptr, B, Hq, Hkv, Nq, Nkv, D,
+                                         scale, int(causal), dtype_code)
+
+
+def attn_bwd(q, k, v, out, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None):
+    """(dq, dk, dv): gradients of attn_fwd's output with respect to q, k, v.
+
+    q, k, v, out, lse are the forward's inputs and outputs (same scale and
+    causal flag), dout the gradient at out.  Every tensor must be contiguous
+    ([B, H, N, D], lse float32 [B, Hq, Nq]) and on one HIP device; dq, dk, dv
+    are allocated unless given.  Runs on torch's current stream.
+    """
+    import torch
+    lib = load_library()
+    named = (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse))
+    for name, t in named:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError(f"{name} must be on q's HIP device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4:
+        raise ValueError("q must be 4-D [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nkv, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)}")
+    for name, t in (("out", out), ("dout", dout)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q's shape and dtype")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Nq]")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    grads = []
+    for name, g, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if g is None:
+            g = torch.empty_like(like, memory_format=torch.contiguous_format)
+        elif (tuple(g.shape) != tuple(like.shape) or g.dtype != like.dtype
+              or g.device != like.device or not g.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous with the shape and dtype of "
+                             f"its input")
+        grads.append(g)
+    dq, dk, dv = grads
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, float(scale),
+                          int(bool(causal)), dt, stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return dq, dk, dv

@@ -10,7 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "attn_fwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip")]
 OUT = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -19,7 +19,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep the compiler from emitting packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-I", os.path.join(ROOT, "include"),
+    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
 ]
 
 

@@ -1,0 +1,550 @@
+// attn_bwd.hip -- gradients of the attention forward (dQ, dK, dV) for gfx950.
+//
+// The English noflash-attention post keeps autograd through its tiled
+// forward (first tier, section "The DIY approach").  With the forward's row
+// log-sum-exp saved, the probabilities are recomputed tile by tile and the
+// gradients never need the Nq x Nkv matrices either:
+//
+//   P_ij  = exp(s_ij - lse_i),  s_ij = scale <q_i, k_j>   (0 where masked)
+//   dV_j  = sum_i P_ij dO_i            dP_ij = <dO_i, V_j>
+//   Delta_i = sum_d dO_id O_id  (= sum_j P_ij dP_ij)
+//   dS_ij = P_ij (dP_ij - Delta_i)
+//   dQ_i  = scale sum_j dS_ij K_j      dK_j = scale sum_i dS_ij Q_i
+//
+// K/V gradients of a KV head sum over the Hq / Hkv query heads that read it.
+// Three kernels, no atomics (results are bitwise reproducible):
+//  * attn_delta_kernel: Delta, one fp32 per query row;
+//  * attn_dkdv_kernel: one workgroup per block of 128 keys of one KV head,
+//    looping over every query tile of every query head of the group, with
+//    dK and dV accumulated in registers;
+//  * attn_dq_kernel: one workgroup per 128 query rows, looping over key tiles
+//    like the forward, with dQ accumulated in registers.
+// The matrix products use the forward's operand layouts (see attn_fwd.hip):
+// a 32x32 accumulator tile is packed in place as the B operand of the next
+// product, and the other operand is read from LDS either row-wise (16-byte
+// reads, k_swz layout) or transposed (ds_read_b64_tr_b16, v_swz layout).
+
+#include "attn_common.h"
+
+namespace {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;     // natural log, [B, Hq, Nq]
+  float* delta;         // [B, Hq, Nq]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, Hq, Hkv, Nq, Nkv, G;
+  int n_tiles;          // per head: query tiles (dQ) or key blocks (dK/dV)
+  int total;            // workgroups of the launch
+  float cs;             // scale * log2(e) (signed)
+  float scale;
+};
+
+template <class Tag>
+__device__ __forceinline__ float lo_f32(uint32_t w);
+template <class Tag>
+__device__ __forceinline__ float hi_f32(uint32_t w);
+template <>
+__device__ __forceinline__ float lo_f32<TagBF16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <>
+__device__ __forceinline__ float hi_f32<TagBF16>(uint32_t w) {
+  return __uint_as_float(w & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ float lo_f32<TagF16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+template <>
+__device__ __forceinline__ float hi_f32<TagF16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+
+// Delta_r = sum_d dO[r, d] O[r, d] in fp32: D / 8 lanes per row, one 16-byte
+// load of each tensor per lane, a butterfly over the row's lanes.
+template <int D, class Tag>
+__global__ __launch_bounds__(256) void attn_delta_kernel(BwdParams p, int rows) {
+  constexpr int L = D / 8;  // lanes per row
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row = gid / L, part = gid % L;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)(p.o + (size_t)row * D + part * 8);
+    const u32x4 g = *(const u32x4*)(p.dout + (size_t)row * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc += lo_f32<Tag>(a[i]) * lo_f32<Tag>(g[i]) + hi_f32<Tag>(a[i]) * hi_f32<Tag>(g[i]);
+  }
+#pragma unroll
+  for (int w = 1; w < L; w <<= 1) acc += __shfl_xor(acc, w, L);
+  if (row < rows && part == 0) p.delta[row] = acc;
+}
+
+// Per-lane byte offsets for copying a [rows x D] tile into LDS with either
+// swizzle, IPW wave copies of 1 KB per wave.
+template <int D, int IPW, bool ROWREAD>
+__device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t* off) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int slot = (wave * IPW + j) * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    off[j] = row * D * 2 + ((pc ^ (ROWREAD ? k_swz<D>(row) : v_swz<D>(row))) << 4);
+  }
+}
+
+// Copies the ROWS-row tile starting at row r0 of a [rows_total x D] matrix
+// at `base` into LDS (rows past rows_total read as zero; r0 < rows_total).
+template <int D, int IPW, int ROWS>
+__device__ __forceinline__ void copy_tile(const uint16_t* base, int r0, int rows_total,
+                                          uint16_t* dst, int wave, const uint32_t* off) {
+  const int n = min(ROWS, rows_total - r0);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + (size_t)r0 * D), 0, (uint32_t)(n * D * 2), kRawBufferFlags);
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) buf2lds16(r, dst + (wave * IPW + j) * 512, off[j]);
+}
+
+// A operand read along rows (16 bytes: chunk 2 kc + hl of row `row`).
+template <int D>
+__device__ __forceinline__ u32x4 read_rows(const uint16_t* t, int row, int kc, int hl) {
+  return *(const u32x4*)(t + row * D + (((2 * kc + hl) ^ k_swz<D>(row)) << 3));
+}
+
+// A operand read transposed: 8 consecutive rows (in the accumulator's
+// interleaving) of columns db*32 + v_d .. + 3, rows from `row` and row + 8.
+template <int D>
+__device__ __forceinline__ u32x4 read_cols(const uint16_t* t, int row, int db, int v_d,
+                                           int v_sw) {
+  const int d = db * 32 + v_d;
+  const int off = (((d >> 3) ^ v_sw) << 3) + (d & 7);
+  const u32x2 lo = lds_read_tr16(t + row * D + off);
+  const u32x2 hi = lds_read_tr16(t + (row + 8) * D + off);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Pack accumulator tile `s` (16 values per lane) as two B operands of
+// 16 reduction rows each.
+template <class Tag>
+__device__ __forceinline__ void pack_tile(const f32x16& s, u32x4* out) {
+  using N = Num<Tag>;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    u32x4 y;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) y[w] = N::pack2(s[8 * hf + 2 * w], s[8 * hf + 2 * w + 1]);
+    out[hf] = y;
+  }
+}
+
+// Store accumulator tiles acc[db] (rows = d, column = this lane's row r) as
+// row r of a 16-bit [*, D] matrix, times `mul`.
+template <int D, class Tag>
+__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16* acc, float mul, int hl) {
+  using N = Num<Tag>;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16& o = acc[db];
+      u32x2 y = {N::pack2(o[4 * i] * mul, o[4 * i + 1] * mul),
+                 N::pack2(o[4 * i + 2] * mul, o[4 * i + 3] * mul)};
+      *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+    }
+}
+
+// dK, dV for 128 keys (4 waves x 32) of KV head hk: loop over the query
+// tiles (64 rows) of the G query heads on that head.  Per tile and wave:
+//   S = Q K^T, dP = dO V^T          (rows: 64 queries, columns: 32 keys)
+//   P = exp2(cs S - lse log2 e) (0 where masked), dS = P (dP - Delta)
+//   dV^T += dO^T P, dK^T += Q^T dS  (rows: D, columns: 32 keys)
+// K and V of the wave's keys stay in registers (B operands); Q and dO tiles
+// are copied into LDS twice each (row-read and transposed layouts) with
+// their lse and Delta, two buffers deep.  One wave per SIMD: the
+// accumulators need more than 256 registers.
+template <int D, class Tag, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
+  constexpr int NW = 4, BK = NW * 32, BQ = 64;
+  constexpr int DC = D / 16, NDB = D / 32, NKC = BQ / 16, CPR = D / 8;
+  constexpr int TILE = BQ * D;
+  constexpr int IPW = BQ * CPR / 64 / NW;
+  using N = Num<Tag>;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t qr[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t qt[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t gr[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t gt[2][TILE];
+  __shared__ __attribute__((aligned(256))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(256))) float del_s[2][BQ];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+
+  int bid = xcd_remap(blockIdx.x, p.total);
+  const int kt = bid % p.n_tiles;
+  bid /= p.n_tiles;
+  const int hk = bid % p.Hkv;
+  const int b = bid / p.Hkv;
+  const int k0 = kt * BK;
+  const int key = k0 + wave * 32 + l32;     // this lane's key (accumulator column)
+
+  const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  u32x4 kf[DC], vf[DC];
+#pragma unroll
+  for (int kc = 0; kc < DC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key < p.Nkv) {
+      x = *(const u32x4*)(p.k + (krow0 + key) * D + kc * 16 + hl * 8);
+      y = *(const u32x4*)(p.v + (krow0 + key) * D + kc * 16 + hl * 8);
+    }
+    kf[kc] = x;
+    vf[kc] = y;
+  }
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dk[i] = dv[i] = f32x16{};
+
+  uint32_t roff[IPW], toff[IPW];
+  copy_offsets<D, IPW, true>(wave, lane, roff);
+  copy_offsets<D, IPW, false>(wave, lane, toff);
+
+  // Query tiles: for every head of the group, from the first tile that can
+  // see a key of this block (causal) to the last.
+  const int nqt = (p.Nq + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? min(nqt, k0 / BQ) : 0;
+  const int per_head = nqt - qt0;
+  const int steps = p.G * per_head;
+
+  auto head_tile = [&](int u, int* hq, int* q0) {
+    *hq = hk * p.G + u / per_head;
+    *q0 = (qt0 + u % per_head) * BQ;
+  };
+  auto issue = [&](int u, int buf) {
+    int hq, q0;
+    head_tile(u, &hq, &q0);
+    const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+    const uint16_t* qb = p.q + qrow0 * D;
+    const uint16_t* gb = p.dout + qrow0 * D;
+    copy_tile<D, IPW, BQ>(qb, q0, p.Nq, qr[buf], wave, roff);
+    copy_tile<D, IPW, BQ>(qb, q0, p.Nq, qt[buf], wave, toff);
+    copy_tile<D, IPW, BQ>(gb, q0, p.Nq, gr[buf], wave, roff);
+    copy_tile<D, IPW, BQ>(gb, q0, p.Nq, gt[buf], wave, toff);
+    if (wave < 2) {  // lse (wave 0) and Delta (wave 1): one dword per lane
+      const float* src = (wave == 0 ? p.lse : p.delta) + qrow0 + q0;
+      const int n = min(BQ, p.Nq - q0);
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 4, kRawBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(wave == 0 ? lse_s[buf] : del_s[buf]), 4,
+          lane * 4, 0, 0, 0);
+    }
+  };
+
+  const int v_g = lane >> 4, v_r = lane & 15;
+  const int v_key = 4 * hl + (v_r >> 2);
+  const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
+  const int v_sw = v_swz<D>(v_key);
+
+  if (steps > 0) issue(0, 0);
+  for (int u = 0; u < steps; ++u) {
+    const int buf = u & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (u + 1 < steps) issue(u + 1, buf ^ 1);
+    int hq, q0;
+    head_tile(u, &hq, &q0);
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < DC; ++kc) {
+        s[qb] = N::mfma(read_rows<D>(qr[buf], qb * 32 + l32, kc, hl), kf[kc], s[qb]);
+        dp[qb] = N::mfma(read_rows<D>(gr[buf], qb * 32 + l32, kc, hl), vf[kc], dp[qb]);
+      }
+    }
+    // P and dS; accumulator register e of block qb is query row
+    // q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4 and key `key`.
+    u32x4 pp[NKC], ps[NKC];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = qb * 32 + 8 * j + 4 * hl;
+        const f32x4 ls = *(const f32x4*)(&lse_s[buf][r]);
+        const f32x4 dl = *(const f32x4*)(&del_s[buf][r]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qrow = q0 + r + e;
+          const bool ok = qrow < p.Nq && key < p.Nkv && (!CAUSAL || key <= qrow);
+          const float pv = ok ? fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e] * kLog2e)) : 0.f;
+          s[qb][4 * j + e] = pv;
+          dp[qb][4 * j + e] = pv * (dp[qb][4 * j + e] - dl[e]);
+        }
+      }
+      pack_tile<Tag>(s[qb], &pp[qb * 2]);
+      pack_tile<Tag>(dp[qb], &ps[qb * 2]);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (reduction over the tile's 64 queries).
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int row = kc * 16 + v_key;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = N::mfma(read_cols<D>(gt[buf], row, db, v_d, v_sw), pp[kc], dv[db]);
+        dk[db] = N::mfma(read_cols<D>(qt[buf], row, db, v_d, v_sw), ps[kc], dk[db]);
+      }
+    }
+  }
+
+  if (key < p.Nkv) {
+    store_row<D, Tag>(p.dk + (krow0 + key) * D, dk, p.scale, hl);
+    store_row<D, Tag>(p.dv + (krow0 + key) * D, dv, 1.f, hl);
+  }
+}
+
+// dQ for 128 query rows (4 waves x 32) of query head hq: loop over key
+// tiles (32 keys) like the forward.  Per tile and wave:
+//   S^T = K Q^T, dP^T = V dO^T      (rows: 32 keys, columns: 32 queries)
+//   P, dS as above (lse and Delta: one value per lane)
+//   dQ^T += K^T dS^T                (rows: D, columns: 32 queries)
+// Q and dO stay in registers; K is copied into LDS twice (row-read and
+// transposed layouts) and V once, two buffers deep.
+template <int D, class Tag, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
+  constexpr int NW = 4, BM = NW * 32, BN = 32;
+  constexpr int DC = D / 16, NDB = D / 32, CPR = D / 8;
+  constexpr int TILE = BN * D;
+  constexpr int IPW = BN * CPR / 64 / NW;
+  using N = Num<Tag>;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t kr[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kt[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vr[2][TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+
+  int bid = xcd_remap(blockIdx.x, p.total);
+  int qt = bid % p.n_tiles;
+  bid /= p.n_tiles;
+  const int hq = bid % p.Hq;
+  const int b = bid / p.Hq;
+  if (CAUSAL) qt = p.n_tiles - 1 - qt;  // longest first
+  const int hk = hq / p.G;
+  const int q0 = qt * BM;
+  const int qrow = q0 + wave * 32 + l32;  // this lane's query (accumulator column)
+  const int kend = CAUSAL ? min(p.Nkv, q0 + BM) : p.Nkv;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+  const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  u32x4 qf[DC], gf[DC];
+#pragma unroll
+  for (int kc = 0; kc < DC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (qrow < p.Nq) {
+      x = *(const u32x4*)(p.q + (qrow0 + qrow) * D + kc * 16 + hl * 8);
+      y = *(const u32x4*)(p.dout + (qrow0 + qrow) * D + kc * 16 + hl * 8);
+    }
+    qf[kc] = x;
+    gf[kc] = y;
+  }
+  const float nl2 = qrow < p.Nq ? -p.lse[qrow0 + qrow] * kLog2e : 0.f;
+  const float dl = qrow < p.Nq ? p.delta[qrow0 + qrow] : 0.f;
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
+
+  uint32_t roff[IPW], toff[IPW];
+  copy_offsets<D, IPW, true>(wave, lane, roff);
+  copy_offsets<D, IPW, false>(wave, lane, toff);
+  const uint16_t* Kg = p.k + krow0 * D;
+  const uint16_t* Vg = p.v + krow0 * D;
+  auto issue = [&](int t, int buf) {
+    copy_tile<D, IPW, BN>(Kg, t * BN, p.Nkv, kr[buf], wave, roff);
+    copy_tile<D, IPW, BN>(Kg, t * BN, p.Nkv, kt[buf], wave, toff);
+    copy_tile<D, IPW, BN>(Vg, t * BN, p.Nkv, vr[buf], wave, roff);
+  };
+
+  const int v_g = lane >> 4, v_r = lane & 15;
+  const int v_key = 4 * hl + (v_r >> 2);
+  const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
+  const int v_sw = v_swz<D>(v_key);
+
+  if (ntiles > 0) issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < DC; ++kc) {
+      s = N::mfma(read_rows<D>(kr[buf], l32, kc, hl), qf[kc], s);
+      dp = N::mfma(read_rows<D>(vr[buf], l32, kc, hl), gf[kc], dp);
+    }
+    // register e is key t*BN + 8 (e / 4) + 4 hl + e % 4 of query qrow
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kk = t * BN + 8 * (e >> 2) + 4 * hl + (e & 3);
+      const bool ok = qrow < p.Nq && kk < p.Nkv && (!CAUSAL || kk <= qrow);
+      const float pv = ok ? fast_exp2(fmaf(p.cs, s[e], nl2)) : 0.f;
+      dp[e] = pv * (dp[e] - dl);
+    }
+    u32x4 ps[2];
+    pack_tile<Tag>(dp, ps);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int row = kc * 16 + v_key;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dq[db] = N::mfma(read_cols<D>(kt[buf], row, db, v_d, v_sw), ps[kc], dq[db]);
+    }
+  }
+  if (qrow < p.Nq) store_row<D, Tag>(p.dq + (qrow0 + qrow) * D, dq, p.scale, hl);
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+
+bool overlaps_bytes(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, const void* dq, const void* dk, const void* dv, int B, int Hq,
+                 int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
+  if (Hq % Hkv != 0) return ATTN_EINVAL;
+  if (D != 64 && D != 128) return ATTN_EINVAL;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (!isfinite(scale)) return ATTN_EINVAL;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const void* outs[3] = {dq, dk, dv};
+  for (const void* x : ins)
+    if (!x || ((uintptr_t)x & 15)) return ATTN_EINVAL;
+  for (const void* x : outs)
+    if (!x || ((uintptr_t)x & 15)) return ATTN_EINVAL;
+  const size_t rows = (size_t)B * Hq * Nq, krows = (size_t)B * Hkv * Nkv;
+  if (rows > (size_t)INT32_MAX || krows > (size_t)INT32_MAX) return ATTN_EINVAL;
+  const size_t qb = rows * D * 2, kb = krows * D * 2;
+  const size_t in_bytes[6] = {qb, kb, kb, qb, qb, rows * 4};
+  const size_t out_bytes[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps_bytes(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (overlaps_bytes(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ATTN_EINVAL;
+  }
+  return ATTN_OK;
+}
+
+template <int D, class Tag>
+hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
+  const int rows = p.B * p.Hq * p.Nq;
+  const size_t threads = (size_t)rows * (D / 8);
+  hipLaunchKernelGGL((attn_delta_kernel<D, Tag>), dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, st, p, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdParams pk = p;
+  pk.n_tiles = (p.Nkv + 127) / 128;
+  pk.total = p.B * p.Hkv * pk.n_tiles;
+  if (causal)
+    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, true>), dim3(pk.total), dim3(256), 0, st, pk);
+  else
+    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, false>), dim3(pk.total), dim3(256), 0, st, pk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdParams pq = p;
+  pq.n_tiles = (p.Nq + 127) / 128;
+  pq.total = p.B * p.Hq * pq.n_tiles;
+  if (causal)
+    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, true>), dim3(pq.total), dim3(256), 0, st, pq);
+  else
+    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, false>), dim3(pq.total), dim3(256), 0, st, pq);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_check(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, const void* dq, const void* dk,
+                   const void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale,
+                   int causal, int dtype) {
+  return validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                      dtype);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+             int Nkv, int D, float scale, int causal, int dtype, void* stream) {
+  int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
+                        causal, dtype);
+  if (rc != ATTN_OK) return rc;
+  rc = attn_host::check_device(nullptr);
+  if (rc != ATTN_OK) return rc;
+  const long long kgrid = (long long)B * Hkv * ((Nkv + 127) / 128);
+  const long long qgrid = (long long)B * Hq * ((Nq + 127) / 128);
+  if (kgrid > INT32_MAX || qgrid > INT32_MAX) return ATTN_EINVAL;
+
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  const size_t rows = (size_t)B * Hq * Nq;
+  hipError_t e = hipMallocAsync(&ws, rows * sizeof(float), st);
+  if (e != hipSuccess || !ws) {
+    attn_host::set_last_hip_error((int)e);
+    (void)hipGetLastError();
+    return ATTN_ENOMEM;
+  }
+  BwdParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)out;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.delta = (float*)ws;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nkv = Nkv;
+  p.G = Hq / Hkv;
+  p.n_tiles = 0;
+  p.total = 0;
+  p.cs = scale * kLog2e;
+  p.scale = scale;
+  const bool cz = causal != 0;
+  if (D == 64)
+    e = dtype == ATTN_BF16 ? launch_bwd<64, TagBF16>(p, cz, st) : launch_bwd<64, TagF16>(p, cz, st);
+  else
+    e = dtype == ATTN_BF16 ? launch_bwd<128, TagBF16>(p, cz, st)
+                           : launch_bwd<128, TagF16>(p, cz, st);
+  const hipError_t ef = hipFreeAsync(ws, st);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) {
+    attn_host::set_last_hip_error((int)e);
+    return ATTN_EHIP;
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -13,9 +13,14 @@ it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
   Calls it cannot serve are handed to the original PyTorch function only
   with ``fallback=True`` (the default raises); ``unpatch()`` restores the
   original; ``stats()`` counts the calls each way.
+* With autograd on and an input that requires grad, ``sdpa`` keeps the
+  forward's log-sum-exp and its backward is the library's gradient kernels
+  (``binding.attn_bwd``), which need contiguous tensors: strided inputs are
+  copied once, in the backward only.
 
 Only argument checks and marshalling happen here; the computation is the
-HIP library's (``binding.attn_fwd``), which raises if it is not built.
+HIP library's (``binding.attn_fwd`` / ``binding.attn_bwd``), which raises if
+it is not built.
 """
 from __future__ import annotations
 
@@ -39,8 +44,6 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
         return "attn_mask is not supported"
     if dropout_p != 0.0:
         return "dropout is not supported"
-    if any(t.requires_grad for t in ts) and torch.is_grad_enabled():
-        return "no backward pass (inputs require grad)"
     if not (query.dim() == key.dim() == value.dim()) or query.dim() not in (3, 4):
         return "inputs must all be 3-D [H, N, E] or 4-D [B, H, N, E]"
     if not (query.dtype == key.dtype == value.dtype) or query.dtype not in (
@@ -86,12 +89,47 @@ def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,
                                 is_causal, scale, enable_gqa)
     if reason is not None:
         raise NotImplementedError(f"memory_efficient_tiled_amd.sdpa: {reason}")
+    import torch
     squeeze = query.dim() == 3
     q, k, v = ((t.unsqueeze(0) for t in (query, key, value)) if squeeze
                else (query, key, value))
-    out = binding.attn_fwd(q, k, v, causal=bool(is_causal), scale=scale,
-                           return_lse=False)
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
+        out = _attention_fn().apply(q, k, v, bool(is_causal), scale)
+    else:
+        out = binding.attn_fwd(q, k, v, causal=bool(is_causal), scale=scale,
+                               return_lse=False)
     return out.squeeze(0) if squeeze else out
+
+
+_fn = None
+
+
+def _attention_fn():
+    """torch.autograd.Function over the library's forward and gradients
+    (defined on first use so that importing this module needs no torch)."""
+    global _fn
+    if _fn is not None:
+        return _fn
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            out, lse = binding.attn_fwd(q, k, v, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.causal, ctx.scale = causal, scale
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse = ctx.saved_tensors
+            q, k, v, dout = (t.contiguous() for t in (q, k, v, dout))
+            dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, dout, causal=ctx.causal,
+                                          scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    _fn = _Attention
+    return _fn
 
 
 def _patched(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,

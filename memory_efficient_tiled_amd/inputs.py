@@ -148,6 +148,15 @@ def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
                   rows=rows)
 
 
+def make_dout(x: Inputs, seed: int | None = None) -> np.ndarray:
+    """The gradient arriving at the output for backward tests: iid N(0,1) of
+    q's shape, rounded to the input type, from its own PCG64 stream (keyed on
+    [seed, 1], so q, k and v are unaffected)."""
+    s = x.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64([s, 1]))
+    return to_storage(rng.standard_normal(x.q.shape, dtype=np.float32), x.dtype)
+
+
 def sample_rows(rng: np.random.Generator, Hq: int, Nq: int, R: int) -> np.ndarray:
     """Per head: rows 0 and Nq-1 plus R-2 distinct interior rows, sorted."""
     if Nq <= R:

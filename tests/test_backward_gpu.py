@@ -1,0 +1,189 @@
+"""GPU parity of the attention gradients (dQ, dK, dV) against the oracle.
+
+The forward runs on the GPU (its output and log-sum-exp feed the gradient
+kernels, as in training); the oracle computes the exact float64 gradients
+from the same 16-bit inputs and the same seeded output gradient.
+
+Tolerance.  Each gradient row (the D values of one query row of dQ, or of
+one key row of dK, dV) is a sum over keys (dQ) or queries (dK, dV) of terms
+x_t in which one 16-bit operand was rounded from fp32 by the kernel (P or
+dS, relative error <= u = 2^-8 for bf16, 2^-11 for fp16), the other an exact
+input, accumulated in fp32.  The rounding errors are independent from term
+to term, so an element's error has a standard deviation of about
+u / sqrt(3) * sqrt(sum_t x_t^2).  The other factor of every term (dO, Q or
+K) is an input of zero mean, so sqrt(sum_t x_t^2) is also about the
+root-mean-square of that gradient row, rms_row(ref).  Delta = <dO, O> is
+read from the 16-bit output, whose elements are off by about u |O|: Delta_i
+is off by about u b_i, b_i = sqrt(sum_d (dO_id O_id)^2), and every dS_ij of
+row i by P_ij u b_i.  In dQ_i that adds scale u b_i |sum_j P_ij K_j| (the
+oracle's attention output with K in place of V); in dK_j it adds terms of
+random sign whose root sum of squares is at most
+scale u max_i(b_i) max|Q| sqrt(sum_i P_ij^2) (causal: the max over the rows
+i >= j that see key j), and sqrt(sum_i P_ij^2) is rms_row(dV_j) (dO has unit
+variance).  This term dominates in short causal
+rows, where dS nearly cancels.  The bounds are max|err| <= 12 u rms_row(ref)
++ 2 u rms(ref) + the Delta term (x12 for dQ, x6 for dK, whose estimate
+already takes maxima) + half an ulp of the output type (beyond 6 standard
+deviations), and mean|err| <= 1.5 u rms(ref) (the mean of |N(0, s)| is
+0.8 s).  Keys that no query may see
+(causal, key index >= Nq) must get exactly zero gradients.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from memory_efficient_tiled_amd import binding, inputs
+from tests.parity import half_ulp, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+U = {inputs.BF16: 2.0 ** -8, inputs.F16: 2.0 ** -11}
+
+
+def _decode(a, dtype):
+    return oracle.decode(a, dtype)
+
+
+def _host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_grad(name, got, ref, dtype, what, zero_from=None, extra=0.0):
+    """Compare one gradient; keys zero_from.. along axis 2 must be exactly 0;
+    `extra` (per row or element) is the bound's Delta term."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what} {name}: non-finite values"
+    err = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    rms_row = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+    u = U[dtype]
+    bound = 12.0 * u * rms_row + 2.0 * u * rms + extra + half_ulp(ref, dtype)
+    mbound = 1.5 * u * rms
+    ratio = float(np.max(err / (u * rms_row + u * rms + 1e-300)))
+    log(f"  {what} {name}: max|err| {err.max():.3e} mean|err| {err.mean():.3e} "
+        f"rms(ref) {rms:.3e} (max err/(u (rms_row + rms)) {ratio:.2f}, "
+        f"mean/(u rms) {err.mean() / (u * rms + 1e-300):.2f})")
+    if zero_from is not None:
+        assert np.all(ref[:, :, zero_from:] == 0.0)
+        assert np.all(got[:, :, zero_from:] == 0.0), \
+            f"{what} {name}: non-zero gradient for keys no query sees"
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), f"{what} {name}: err {err[worst]:.3e} at {worst} > bound"
+    assert err.mean() <= mbound, f"{what} {name}: mean err {err.mean():.3e} > {mbound:.3e}"
+
+
+def delta_terms(x, do, ref, causal):
+    """Per-row Delta terms of the bound for (dq, dk, dv) (see the header)."""
+    dtype = x.dtype
+    q, k, v, g = (_decode(a, dtype) for a in (x.q, x.k, x.v, do))
+    B, Hq, Nq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = oracle.scale_value(None, D)
+    u = U[dtype]
+    o, _ = oracle.attention(q, k, v, sc, causal)
+    pk, _ = oracle.attention(q, k, k, sc, causal)                      # sum_j P_ij K_j
+    b = np.sqrt(np.sum((g * o) ** 2, axis=-1, keepdims=True))        # [B,Hq,Nq,1]
+    t_dq = 12.0 * sc * u * b * np.abs(pk)
+    bg = b[..., 0].reshape(B, Hkv, G, Nq).max(axis=2)                 # [B,Hkv,Nq]
+    Nkv = k.shape[2]
+    if causal:   # rows i >= j see key j
+        suffix = np.maximum.accumulate(bg[:, :, ::-1], axis=-1)[:, :, ::-1]
+        bmax = np.zeros((B, Hkv, Nkv))
+        n = min(Nq, Nkv)
+        bmax[:, :, :n] = suffix[:, :, :n]
+        bmax = bmax[..., None]
+    else:
+        bmax = bg.max(axis=-1)[:, :, None, None]
+    qmax = np.abs(q).reshape(B, Hkv, -1).max(axis=-1)[:, :, None, None]
+    rms_dv = np.sqrt(np.mean(ref[2] ** 2, axis=-1, keepdims=True))
+    t_dk = 6.0 * sc * u * bmax * qmax * rms_dv
+    return t_dq, t_dk, 0.0
+
+
+def run_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed):
+    import torch
+    what = (f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} "
+            f"causal={causal} seed={seed}")
+    log(what)
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed)
+    do = inputs.make_dout(x)
+    q, k, v, g = (to_device(a, dtype, device) for a in (x.q, x.k, x.v, do))
+    out, lse = binding.attn_fwd(q, k, v, causal=causal)
+    dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, g, causal=causal)
+    torch.cuda.synchronize(device)
+    sc = oracle.scale_value(None, D)
+    ref = oracle.attention_backward(_decode(x.q, dtype), _decode(x.k, dtype),
+                                    _decode(x.v, dtype), _decode(do, dtype), sc, causal)
+    unseen = Nq if causal and Nkv > Nq else None
+    terms = delta_terms(x, do, ref, causal)
+    for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, terms):
+        check_grad(name, _host(got), r, dtype, what, None if name == "dq" else unseen, t)
+
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mha_d64_ragged(gpu_device, dtype, causal):
+    # neither length a multiple of the 64-query, 128-key or 128-row tiles
+    run_case(gpu_device, 1, 3, 3, 333, 270, 64, dtype, causal, seed=41)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_d128(gpu_device, causal):
+    run_case(gpu_device, 2, 6, 2, 300, 300, 128, inputs.BF16, causal, seed=42)
+
+
+def test_more_keys_than_queries_causal(gpu_device):
+    # keys past the last query row receive exactly zero gradient
+    run_case(gpu_device, 1, 2, 1, 130, 600, 64, inputs.F16, True, seed=43)
+
+
+def test_more_queries_than_keys(gpu_device):
+    run_case(gpu_device, 1, 4, 4, 700, 90, 128, inputs.F16, True, seed=44)
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, 129])
+def test_short_sequences(gpu_device, n):
+    run_case(gpu_device, 1, 2, 2, n, n, 64, inputs.BF16, False, seed=45 + n)
+
+
+def test_long_d128_several_tiles(gpu_device):
+    run_case(gpu_device, 1, 4, 4, 1500, 1500, 128, inputs.BF16, False, seed=46)
+
+
+def test_deterministic(gpu_device):
+    import torch
+    x = inputs.make_inputs(1, 4, 2, 500, 500, 128, inputs.BF16, seed=47)
+    q, k, v, g = (to_device(a, inputs.BF16, gpu_device)
+                  for a in (x.q, x.k, x.v, inputs.make_dout(x)))
+    out, lse = binding.attn_fwd(q, k, v)
+    a = binding.attn_bwd(q, k, v, out, lse, g)
+    b = binding.attn_bwd(q, k, v, out, lse, g)
+    torch.cuda.synchronize(gpu_device)
+    for x1, x2 in zip(a, b):
+        assert torch.equal(x1, x2)
+
+
+def test_sdpa_autograd(gpu_device):
+    """sdpa() under autograd: strided (bnhd) inputs, GQA, causal."""
+    import torch
+    import memory_efficient_tiled_amd as mta
+    dtype = inputs.BF16
+    x = inputs.make_inputs(1, 4, 2, 200, 200, 64, dtype, seed=48)
+    do = inputs.make_dout(x)
+    leaves = []
+    for a in (x.q, x.k, x.v):
+        t = to_device(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), dtype, gpu_device)
+        t.requires_grad_(True)
+        leaves.append(t)
+    q, k, v = (t.transpose(1, 2) for t in leaves)
+    o = mta.sdpa(q, k, v, is_causal=True, enable_gqa=True)
+    o.backward(to_device(do, dtype, gpu_device))
+    torch.cuda.synchronize(gpu_device)
+    sc = oracle.scale_value(None, 64)
+    ref = oracle.attention_backward(_decode(x.q, dtype), _decode(x.k, dtype),
+                                    _decode(x.v, dtype), _decode(do, dtype), sc, True)
+    terms = delta_terms(x, do, ref, True)
+    for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
+        got = _host(leaf.grad.transpose(1, 2))
+        check_grad(name, got, r, dtype, "sdpa autograd", None, t)
