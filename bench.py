@@ -7,7 +7,13 @@ TFLOP/s (4*B*Hq*Nq*Nkv*D, halved when causal), the fraction of the dense
 bf16/fp16 MFMA peak, a parity check of sampled rows against the CPU oracle,
 and that oracle's own throughput on the same rows (a reported baseline).
 
+With ``--pass bwd`` a step is one gradient computation (attn_bwd: dQ, dK, dV
+from the forward's output and log-sum-exp, computed once before timing) and
+the algorithmic flops are 2.5 times the forward's (five products of the
+forward's size: S again, dP, dV, dK, dQ); parity covers dQ of sampled rows.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+                    [--pass fwd|bwd]
 """
 from __future__ import annotations
 
@@ -25,29 +31,36 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
-SOURCE = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc")
+# the kernel sources each pass runs (a measurement taken on other sources is stale)
+SOURCES = {"fwd": ("attn_common.h", "attn_fwd.hip"),
+           "bwd": ("attn_common.h", "attn_bwd.hip")}
 PROFILES = os.path.join(ROOT, "profiles")
+BWD_FLOP_FACTOR = 2.5
 
 
 def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    with open(SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(pass_: str = "fwd") -> str:
+    h = hashlib.sha256()
+    for name in SOURCES[pass_]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"attn_fwd_{workload}_hbm_counters.md")
+def measured_traffic(workload: str, pass_: str = "fwd"):
+    """HBM bytes per step from a committed counter summary, if it was taken
+    on the current kernel sources; otherwise None."""
+    path = os.path.join(PROFILES, f"attn_{pass_}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
     t = re.search(r"hbm bytes per step:\s*`?([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != source_hash():
+    if not h or not t or h.group(1) != source_hash(pass_):
         return None
     return float(t.group(1))
 
@@ -84,6 +97,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows per head for the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the gradients")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this size "
                          "(scales the HBM byte counters)")
@@ -109,13 +124,14 @@ def main():
                           "launches": max(1, args.steps)}), flush=True)
         return
 
-    from memory_efficient_tiled_amd import attn_fwd, attn_fwd_num_splits, inputs
+    from memory_efficient_tiled_amd import attn_bwd, attn_fwd, attn_fwd_num_splits, inputs
     from memory_efficient_tiled_amd.binding import ATTN_BF16, ATTN_F16
 
+    bwd = args.pass_ == "bwd"
     name = args.workload or inputs.HEADLINE
     w = inputs.WORKLOADS[name]
     dev = torch.device("cuda:0")
-    progress(f"workload {name}: {w.describe()}; generating inputs")
+    progress(f"workload {name}: {w.describe()}; pass {args.pass_}; generating inputs")
     want_cpu = not args.no_cpu_baseline
     x = inputs.make_workload_inputs(w, seed=args.seed,
                                     sampled_rows=args.cpu_rows if want_cpu else None)
@@ -135,9 +151,21 @@ def main():
     progress(f"inputs on {torch.cuda.get_device_name(dev)}; split-KV count {splits}; "
              f"warmup {args.warmup}")
 
-    def step():
+    def fwd_step():
         attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse,
                  num_splits=args.splits)
+
+    if bwd:
+        dout = inputs.make_dout(x, seed=args.seed)
+        g = up(dout)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        fwd_step()
+
+        def step():
+            attn_bwd(q, k, v, out, lse, g, causal=w.causal, scale=w.scale,
+                     dq=dq, dk=dk, dv=dv)
+    else:
+        step = fwd_step
 
     for _ in range(args.warmup):
         step()
@@ -157,19 +185,25 @@ def main():
     wall = time.perf_counter() - wall0
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    tflops = w.flops / (ms * 1e-3) / 1e12
+    flops = w.flops * (BWD_FLOP_FACTOR if bwd else 1.0)
+    tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.dtype]
     progress(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); "
              f"wall {wall:.3f} s")
 
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name, args.pass_)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                 "traffic": traffic}
 
+    if bwd:
+        metric = ("attention bwd (dQ, dK, dV) TFLOP/s and % of MI355X bf16 MFMA peak "
+                  "(2.5x forward flops)")
+    else:
+        metric = ("attention fwd TFLOP/s and % of MI355X bf16 MFMA peak "
+                  "(B=1,H=24,D=128,N=17K)")
     result = {
-        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak "
-                  "(B=1,H=24,D=128,N=17K)",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
@@ -180,57 +214,114 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{name}: {w.note}, {w.describe()}",
+                   "pass": args.pass_,
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv,
                    "D": w.D, "causal": w.causal, "scale": w.scale, "seed": args.seed,
-                   "k_offset_std": w.k_offset_std, "split_kv": splits,
-                   "kernel_source": source_hash()},
+                   "k_offset_std": w.k_offset_std,
+                   "split_kv": None if bwd else splits,
+                   "kernel_source": source_hash(args.pass_)},
         "roofline": roofline,
     }
 
     if want_cpu:
         import oracle
-        from tests.parity import gather_rows
-        progress(f"oracle on {x.rows.shape[1]} rows x {w.Hq} heads")
-        o_gpu = out.float().cpu().numpy().astype(np.float64)
-        l_gpu = lse.cpu().numpy().astype(np.float64)
-        sc = oracle.scale_value(w.scale, w.D)
-        G = w.Hq // w.Hkv
-        c0 = time.perf_counter()
-        o_ref = np.empty((w.B, w.Hq, x.rows.shape[1], w.D))
-        l_ref = np.empty((w.B, w.Hq, x.rows.shape[1]))
-        for b in range(w.B):
-            for hk in range(w.Hkv):
-                kh = oracle.decode(x.k[b:b + 1, hk:hk + 1], w.dtype)
-                vh = oracle.decode(x.v[b:b + 1, hk:hk + 1], w.dtype)
-                for g in range(G):
-                    h = hk * G + g
-                    qh = oracle.decode(x.q[b:b + 1, h:h + 1], w.dtype)
-                    oh, lh = oracle.attention(qh, kh, vh, sc, w.causal, rows=x.rows[h])
-                    o_ref[b, h], l_ref[b, h] = oh[0, 0], lh[0, 0]
-        cpu_s = time.perf_counter() - c0
-        rows = x.rows
-        if w.causal:
-            sample_flops = float(sum(4.0 * w.D * np.minimum(r + 1, w.Nkv).sum()
-                                     for r in rows)) * w.B
+        if bwd:
+            cpu_leg_bwd(result, x, w, name, dout, dq, np, oracle)
         else:
-            sample_flops = 4.0 * w.D * w.Nkv * rows.size * w.B
-        o_s, l_s = gather_rows(o_gpu, rows), gather_rows(l_gpu, rows)
-        err = np.abs(o_s - o_ref)
-        result["parity"] = {"rows_per_head": int(rows.shape[1]),
-                            "max_abs_err": float(err.max()),
-                            "mean_abs_err": float(err.mean()),
-                            "lse_max_abs_err": float(np.abs(l_s - l_ref).max()),
-                            "pass": bool(err.max() <= 4e-3 and err.mean() <= 5e-4 and
-                                         np.abs(l_s - l_ref).max() <= 1e-3)}
-        result["cpu_baseline"] = {
-            "value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
-            "cores": blas_threads(), "kind": "oracle",
-            "sample": f"{rows.shape[1]} query rows per head x {w.Hq} heads of {name} "
-                      f"({sample_flops / 1e9:.1f} GFLOP algorithmic, {cpu_s:.1f} s, "
-                      f"float64 numpy, {cpu_model()})"}
-        progress(f"oracle {cpu_s:.1f} s; parity {result['parity']}")
+            cpu_leg_fwd(result, x, w, name, out, lse, np, oracle)
 
     print(json.dumps(result), flush=True)
+
+
+def cpu_leg_fwd(result, x, w, name, out, lse, np, oracle):
+    """Parity of sampled output rows and the oracle's throughput on them."""
+    from tests.parity import gather_rows
+    progress(f"oracle on {x.rows.shape[1]} rows x {w.Hq} heads")
+    o_gpu = out.float().cpu().numpy().astype(np.float64)
+    l_gpu = lse.cpu().numpy().astype(np.float64)
+    sc = oracle.scale_value(w.scale, w.D)
+    G = w.Hq // w.Hkv
+    c0 = time.perf_counter()
+    o_ref = np.empty((w.B, w.Hq, x.rows.shape[1], w.D))
+    l_ref = np.empty((w.B, w.Hq, x.rows.shape[1]))
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            kh = oracle.decode(x.k[b:b + 1, hk:hk + 1], w.dtype)
+            vh = oracle.decode(x.v[b:b + 1, hk:hk + 1], w.dtype)
+            for g in range(G):
+                h = hk * G + g
+                qh = oracle.decode(x.q[b:b + 1, h:h + 1], w.dtype)
+                oh, lh = oracle.attention(qh, kh, vh, sc, w.causal, rows=x.rows[h])
+                o_ref[b, h], l_ref[b, h] = oh[0, 0], lh[0, 0]
+    cpu_s = time.perf_counter() - c0
+    rows = x.rows
+    if w.causal:
+        sample_flops = float(sum(4.0 * w.D * np.minimum(r + 1, w.Nkv).sum()
+                                 for r in rows)) * w.B
+    else:
+        sample_flops = 4.0 * w.D * w.Nkv * rows.size * w.B
+    o_s, l_s = gather_rows(o_gpu, rows), gather_rows(l_gpu, rows)
+    err = np.abs(o_s - o_ref)
+    result["parity"] = {"rows_per_head": int(rows.shape[1]),
+                        "max_abs_err": float(err.max()),
+                        "mean_abs_err": float(err.mean()),
+                        "lse_max_abs_err": float(np.abs(l_s - l_ref).max()),
+                        "pass": bool(err.max() <= 4e-3 and err.mean() <= 5e-4 and
+                                     np.abs(l_s - l_ref).max() <= 1e-3)}
+    result["cpu_baseline"] = {
+        "value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+        "cores": blas_threads(), "kind": "oracle",
+        "sample": f"{rows.shape[1]} query rows per head x {w.Hq} heads of {name} "
+                  f"({sample_flops / 1e9:.1f} GFLOP algorithmic, {cpu_s:.1f} s, "
+                  f"float64 numpy, {cpu_model()})"}
+    progress(f"oracle {cpu_s:.1f} s; parity {result['parity']}")
+
+
+def cpu_leg_bwd(result, x, w, name, dout, dq, np, oracle):
+    """dQ of sampled query rows against the oracle, and the oracle's gradient
+    throughput on them.  dQ of row i depends on row i's inputs and every key
+    only, so the oracle runs on the sampled rows alone: every fourth row of
+    the forward's sample (causal: the first rows, which keep their
+    positions).  The sample's flops count the five products over those rows."""
+    from tests.parity import gather_rows
+    R = max(2, x.rows.shape[1] // 4)
+    rows = (np.tile(np.arange(min(R, w.Nq)), (w.Hq, 1)) if w.causal else x.rows[:, ::4])
+    progress(f"oracle gradients on {rows.shape[1]} rows x {w.Hq} heads")
+    dq_gpu = gather_rows(dq.float().cpu().numpy().astype(np.float64), rows)
+    sc = oracle.scale_value(w.scale, w.D)
+    G = w.Hq // w.Hkv
+    c0 = time.perf_counter()
+    dq_ref = np.empty_like(dq_gpu)
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            kh = oracle.decode(x.k[b:b + 1, hk:hk + 1], w.dtype)
+            vh = oracle.decode(x.v[b:b + 1, hk:hk + 1], w.dtype)
+            for gi in range(G):
+                h = hk * G + gi
+                qh = oracle.decode(x.q[b:b + 1, h:h + 1, rows[h]], w.dtype)
+                gh = oracle.decode(dout[b:b + 1, h:h + 1, rows[h]], w.dtype)
+                dqh, _, _ = oracle.attention_backward(qh, kh, vh, gh, sc, w.causal)
+                dq_ref[b, h] = dqh[0, 0]
+    cpu_s = time.perf_counter() - c0
+    if w.causal:
+        sample_flops = float(sum(10.0 * w.D * np.minimum(r + 1, w.Nkv).sum()
+                                 for r in rows)) * w.B
+    else:
+        sample_flops = 10.0 * w.D * w.Nkv * rows.size * w.B
+    err = np.abs(dq_gpu - dq_ref)
+    rms = float(np.sqrt(np.mean(dq_ref ** 2)))
+    u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11
+    result["parity"] = {"rows_per_head": int(rows.shape[1]), "tensor": "dq",
+                        "max_abs_err": float(err.max()),
+                        "mean_abs_err": float(err.mean()), "rms_ref": rms,
+                        "pass": bool(err.mean() <= 1.5 * u * rms)}
+    result["cpu_baseline"] = {
+        "value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+        "cores": blas_threads(), "kind": "oracle",
+        "sample": f"dQ of {rows.shape[1]} query rows per head x {w.Hq} heads of {name} "
+                  f"({sample_flops / 1e9:.1f} GFLOP algorithmic, {cpu_s:.1f} s, "
+                  f"float64 numpy, {cpu_model()})"}
+    progress(f"oracle {cpu_s:.1f} s; parity {result['parity']}")
 
 
 if __name__ == "__main__":
