@@ -12,19 +12,29 @@
 //   dQ_i  = scale sum_j dS_ij K_j      dK_j = scale sum_i dS_ij Q_i
 //
 // K/V gradients of a KV head sum over the Hq / Hkv query heads that read it.
-// Three kernels, no atomics (results are bitwise reproducible):
-//  * attn_delta_kernel: Delta, one fp32 per query row;
+// Kernels, no atomics (results are bitwise reproducible):
+//  * attn_delta_kernel: Delta and lse log2(e), one fp32 each per query row;
 //  * attn_dkdv_kernel: one workgroup per block of 128 keys of one KV head,
-//    looping over every query tile of every query head of the group, with
-//    dK and dV accumulated in registers;
+//    looping over every query tile of the query heads it covers, with dK and
+//    dV accumulated in registers.  When the KV heads alone give too few
+//    workgroups, the query heads of a group are split over several
+//    workgroups that write fp32 partial sums, and attn_dkdv_reduce adds them;
 //  * attn_dq_kernel: one workgroup per 128 query rows, looping over key tiles
 //    like the forward, with dQ accumulated in registers.
 // The matrix products use the forward's operand layouts (see attn_fwd.hip):
 // a 32x32 accumulator tile is packed in place as the B operand of the next
 // product, and the other operand is read from LDS either row-wise (16-byte
 // reads, k_swz layout) or transposed (ds_read_b64_tr_b16, v_swz layout).
+//
+// Padding rows need no masks: rows past Nq (queries) or Nkv (keys) are read
+// as zeros, so a padded query row has dO = 0 and Delta = 0 and adds nothing
+// to dK and dV, and a padded key has K = V = 0 and adds nothing to dQ; the
+// gradients of padded rows themselves are never stored.  Only the causal
+// mask is applied, and only on the tiles that straddle the diagonal.
 
 #include "attn_common.h"
+
+#include <type_traits>
 
 namespace {
 
@@ -36,10 +46,14 @@ struct BwdParams {
   const uint16_t* dout;
   const float* lse;     // natural log, [B, Hq, Nq]
   float* delta;         // [B, Hq, Nq]
+  float* lse2;          // lse * log2(e), [B, Hq, Nq]
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  float* dkp;           // fp32 partial dK / dV, [hsplit, B, Hkv, Nkv, D], when hsplit > 1
+  float* dvp;
   int B, Hq, Hkv, Nq, Nkv, G;
+  int hsplit;           // workgroups sharing the query heads of one KV head
   int n_tiles;          // per head: query tiles (dQ) or key blocks (dK/dV)
   int total;            // workgroups of the launch
   float cs;             // scale * log2(e) (signed)
@@ -82,7 +96,10 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(BwdParams p, int rows) 
   }
 #pragma unroll
   for (int w = 1; w < L; w <<= 1) acc += __shfl_xor(acc, w, L);
-  if (row < rows && part == 0) p.delta[row] = acc;
+  if (row < rows && part == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
 }
 
 // Per-lane byte offsets for copying a [rows x D] tile into LDS with either
@@ -159,28 +176,31 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const f32x16* acc, floa
 }
 
 // dK, dV for 128 keys (4 waves x 32) of KV head hk: loop over the query
-// tiles (64 rows) of the G query heads on that head.  Per tile and wave:
-//   S = Q K^T, dP = dO V^T          (rows: 64 queries, columns: 32 keys)
-//   P = exp2(cs S - lse log2 e) (0 where masked), dS = P (dP - Delta)
+// tiles (BQ = 32 NQB rows) of the query heads this workgroup covers.  Per
+// tile and wave:
+//   S = Q K^T, dP = dO V^T          (rows: BQ queries, columns: 32 keys)
+//   P = exp2(cs S - lse2) (0 above the causal diagonal), dS = P (dP - Delta)
 //   dV^T += dO^T P, dK^T += Q^T dS  (rows: D, columns: 32 keys)
 // K and V of the wave's keys stay in registers (B operands); Q and dO tiles
 // are copied into LDS twice each (row-read and transposed layouts) with
-// their lse and Delta, two buffers deep.  One wave per SIMD: the
-// accumulators need more than 256 registers.
-template <int D, class Tag, bool CAUSAL>
+// their lse2 and Delta, two buffers deep.  The loop is unrolled by two so
+// that each buffer's LDS addresses are compile-time offsets.  One wave per
+// SIMD: the accumulators and operands need more than 256 registers.
+template <int D, class Tag, bool CAUSAL, int NQB>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
-  constexpr int NW = 4, BK = NW * 32, BQ = 64;
+  constexpr int NW = 4, BK = NW * 32, BQ = NQB * 32;
   constexpr int DC = D / 16, NDB = D / 32, NKC = BQ / 16, CPR = D / 8;
   constexpr int TILE = BQ * D;
   constexpr int IPW = BQ * CPR / 64 / NW;
+  static_assert(IPW >= 1 && IPW * 64 * NW == BQ * CPR, "tile copy shape");
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t qr[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t qt[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gr[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gt[2][TILE];
-  __shared__ __attribute__((aligned(256))) float lse_s[2][BQ];
-  __shared__ __attribute__((aligned(256))) float del_s[2][BQ];
+  __shared__ __attribute__((aligned(256))) float lse_s[2][64];
+  __shared__ __attribute__((aligned(256))) float del_s[2][64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -189,10 +209,15 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
   int bid = xcd_remap(blockIdx.x, p.total);
   const int kt = bid % p.n_tiles;
   bid /= p.n_tiles;
+  const int hs = bid % p.hsplit;
+  bid /= p.hsplit;
   const int hk = bid % p.Hkv;
   const int b = bid / p.Hkv;
   const int k0 = kt * BK;
-  const int key = k0 + wave * 32 + l32;     // this lane's key (accumulator column)
+  const int kw0 = k0 + wave * 32;           // the wave's first key
+  const int key = kw0 + l32;                // this lane's key (accumulator column)
+  const int hpw = p.G / p.hsplit;           // query heads per workgroup
+  const int h0 = hk * p.G + hs * hpw;
 
   const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
   u32x4 kf[DC], vf[DC];
@@ -214,20 +239,21 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
   copy_offsets<D, IPW, true>(wave, lane, roff);
   copy_offsets<D, IPW, false>(wave, lane, toff);
 
-  // Query tiles: for every head of the group, from the first tile that can
-  // see a key of this block (causal) to the last.
+  // Query tiles: for every covered head, from the first tile that can see a
+  // key of this block (causal) to the last.
   const int nqt = (p.Nq + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? min(nqt, k0 / BQ) : 0;
   const int per_head = nqt - qt0;
-  const int steps = p.G * per_head;
+  const int steps = hpw * per_head;
 
-  auto head_tile = [&](int u, int* hq, int* q0) {
-    *hq = hk * p.G + u / per_head;
+  auto tile_start = [&](int u, int* hq, int* q0) {
+    *hq = h0 + u / per_head;
     *q0 = (qt0 + u % per_head) * BQ;
   };
-  auto issue = [&](int u, int buf) {
+  auto issue = [&](int u, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     int hq, q0;
-    head_tile(u, &hq, &q0);
+    tile_start(u, &hq, &q0);
     const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
     const uint16_t* qb = p.q + qrow0 * D;
     const uint16_t* gb = p.dout + qrow0 * D;
@@ -235,8 +261,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
     copy_tile<D, IPW, BQ>(qb, q0, p.Nq, qt[buf], wave, toff);
     copy_tile<D, IPW, BQ>(gb, q0, p.Nq, gr[buf], wave, roff);
     copy_tile<D, IPW, BQ>(gb, q0, p.Nq, gt[buf], wave, toff);
-    if (wave < 2) {  // lse (wave 0) and Delta (wave 1): one dword per lane
-      const float* src = (wave == 0 ? p.lse : p.delta) + qrow0 + q0;
+    if (wave < 2) {  // lse2 (wave 0) and Delta (wave 1): one dword per lane
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + qrow0 + q0;
       const int n = min(BQ, p.Nq - q0);
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 4, kRawBufferFlags);
@@ -251,30 +277,13 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
   const int v_sw = v_swz<D>(v_key);
 
-  if (steps > 0) issue(0, 0);
-  for (int u = 0; u < steps; ++u) {
-    const int buf = u & 1;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (u + 1 < steps) issue(u + 1, buf ^ 1);
-    int hq, q0;
-    head_tile(u, &hq, &q0);
-
-    f32x16 s[2], dp[2];
+  // P and dS of one tile in place of S and dP; accumulator register e of
+  // block qb is query row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.
+  auto probs = [&](auto mskc, auto bufc, f32x16* s, f32x16* dp, int q0) {
+    constexpr bool MSK = decltype(mskc)::value;
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = dp[qb] = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < DC; ++kc) {
-        s[qb] = N::mfma(read_rows<D>(qr[buf], qb * 32 + l32, kc, hl), kf[kc], s[qb]);
-        dp[qb] = N::mfma(read_rows<D>(gr[buf], qb * 32 + l32, kc, hl), vf[kc], dp[qb]);
-      }
-    }
-    // P and dS; accumulator register e of block qb is query row
-    // q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4 and key `key`.
-    u32x4 pp[NKC], ps[NKC];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = qb * 32 + 8 * j + 4 * hl;
@@ -282,17 +291,43 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
         const f32x4 dl = *(const f32x4*)(&del_s[buf][r]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int qrow = q0 + r + e;
-          const bool ok = qrow < p.Nq && key < p.Nkv && (!CAUSAL || key <= qrow);
-          const float pv = ok ? fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e] * kLog2e)) : 0.f;
+          float pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
+          if (MSK && key > q0 + r + e) pv = 0.f;
           s[qb][4 * j + e] = pv;
           dp[qb][4 * j + e] = pv * (dp[qb][4 * j + e] - dl[e]);
         }
       }
+  };
+
+  auto tile = [&](int u, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (u + 1 < steps) issue(u + 1, std::integral_constant<int, buf ^ 1>{});
+    int hq, q0;
+    tile_start(u, &hq, &q0);
+
+    f32x16 s[NQB], dp[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < DC; ++kc) {
+        s[qb] = N::mfma(read_rows<D>(qr[buf], qb * 32 + l32, kc, hl), kf[kc], s[qb]);
+        dp[qb] = N::mfma(read_rows<D>(gr[buf], qb * 32 + l32, kc, hl), vf[kc], dp[qb]);
+      }
+    }
+    if (CAUSAL && kw0 + 31 > q0)
+      probs(std::true_type{}, bufc, s, dp, q0);
+    else
+      probs(std::false_type{}, bufc, s, dp, q0);
+    u32x4 pp[NKC], ps[NKC];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
       pack_tile<Tag>(s[qb], &pp[qb * 2]);
       pack_tile<Tag>(dp[qb], &ps[qb * 2]);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (reduction over the tile's 64 queries).
+    // dV^T += dO^T P, dK^T += Q^T dS (reduction over the tile's queries).
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int row = kc * 16 + v_key;
@@ -302,31 +337,72 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
         dk[db] = N::mfma(read_cols<D>(qt[buf], row, db, v_d, v_sw), ps[kc], dk[db]);
       }
     }
+  };
+
+  if (steps > 0) issue(0, std::integral_constant<int, 0>{});
+  for (int u = 0; u < steps; u += 2) {
+    tile(u, std::integral_constant<int, 0>{});
+    if (u + 1 < steps) tile(u + 1, std::integral_constant<int, 1>{});
   }
 
   if (key < p.Nkv) {
-    store_row<D, Tag>(p.dk + (krow0 + key) * D, dk, p.scale, hl);
-    store_row<D, Tag>(p.dv + (krow0 + key) * D, dv, 1.f, hl);
+    if (p.hsplit == 1) {
+      store_row<D, Tag>(p.dk + (krow0 + key) * D, dk, p.scale, hl);
+      store_row<D, Tag>(p.dv + (krow0 + key) * D, dv, 1.f, hl);
+    } else {
+      const size_t part = (size_t)hs * p.B * p.Hkv * p.Nkv;
+      float* dkr = p.dkp + (part + krow0 + key) * D;
+      float* dvr = p.dvp + (part + krow0 + key) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = db * 32 + 8 * i + 4 * hl;
+          *(f32x4*)(dkr + d) = f32x4{dk[db][4 * i], dk[db][4 * i + 1], dk[db][4 * i + 2],
+                                     dk[db][4 * i + 3]};
+          *(f32x4*)(dvr + d) = f32x4{dv[db][4 * i], dv[db][4 * i + 1], dv[db][4 * i + 2],
+                                     dv[db][4 * i + 3]};
+        }
+    }
   }
+}
+
+// dK, dV = sums of the hsplit partials (dK times scale), rounded to 16 bits;
+// four elements per thread.
+template <class Tag>
+__global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4) {
+  using N = Num<Tag>;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const size_t stride = n4;  // float4s per partial
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < p.hsplit; ++h) {
+    a += ((const f32x4*)p.dkp)[h * stride + i];
+    c += ((const f32x4*)p.dvp)[h * stride + i];
+  }
+  a *= p.scale;
+  ((u32x2*)p.dk)[i] = u32x2{N::pack2(a[0], a[1]), N::pack2(a[2], a[3])};
+  ((u32x2*)p.dv)[i] = u32x2{N::pack2(c[0], c[1]), N::pack2(c[2], c[3])};
 }
 
 // dQ for 128 query rows (4 waves x 32) of query head hq: loop over key
 // tiles (32 keys) like the forward.  Per tile and wave:
 //   S^T = K Q^T, dP^T = V dO^T      (rows: 32 keys, columns: 32 queries)
-//   P, dS as above (lse and Delta: one value per lane)
+//   P, dS as above (lse2 and Delta: one value per lane)
 //   dQ^T += K^T dS^T                (rows: D, columns: 32 queries)
 // Q and dO stay in registers; K is copied into LDS twice (row-read and
-// transposed layouts) and V once, two buffers deep.
+// transposed layouts) and V once, two buffers deep, the loop unrolled by two.
 template <int D, class Tag, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   constexpr int NW = 4, BM = NW * 32, BN = 32;
   constexpr int DC = D / 16, NDB = D / 32, CPR = D / 8;
   constexpr int TILE = BN * D;
   constexpr int IPW = BN * CPR / 64 / NW;
+  static_assert(IPW >= 1 && IPW * 64 * NW == BN * CPR, "tile copy shape");
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kr[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t kt[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ktr[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vr[2][TILE];
 
   const int tid = threadIdx.x;
@@ -341,7 +417,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   if (CAUSAL) qt = p.n_tiles - 1 - qt;  // longest first
   const int hk = hq / p.G;
   const int q0 = qt * BM;
-  const int qrow = q0 + wave * 32 + l32;  // this lane's query (accumulator column)
+  const int qw0 = q0 + wave * 32;         // the wave's first query row
+  const int qrow = qw0 + l32;             // this lane's query (accumulator column)
   const int kend = CAUSAL ? min(p.Nkv, q0 + BM) : p.Nkv;
   const int ntiles = (kend + BN - 1) / BN;
 
@@ -358,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
     qf[kc] = x;
     gf[kc] = y;
   }
-  const float nl2 = qrow < p.Nq ? -p.lse[qrow0 + qrow] * kLog2e : 0.f;
+  const float nl2 = qrow < p.Nq ? -p.lse2[qrow0 + qrow] : 0.f;
   const float dl = qrow < p.Nq ? p.delta[qrow0 + qrow] : 0.f;
   f32x16 dq[NDB];
 #pragma unroll
@@ -369,9 +446,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   copy_offsets<D, IPW, false>(wave, lane, toff);
   const uint16_t* Kg = p.k + krow0 * D;
   const uint16_t* Vg = p.v + krow0 * D;
-  auto issue = [&](int t, int buf) {
+  auto issue = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     copy_tile<D, IPW, BN>(Kg, t * BN, p.Nkv, kr[buf], wave, roff);
-    copy_tile<D, IPW, BN>(Kg, t * BN, p.Nkv, kt[buf], wave, toff);
+    copy_tile<D, IPW, BN>(Kg, t * BN, p.Nkv, ktr[buf], wave, toff);
     copy_tile<D, IPW, BN>(Vg, t * BN, p.Nkv, vr[buf], wave, roff);
   };
 
@@ -380,26 +458,32 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
   const int v_sw = v_swz<D>(v_key);
 
-  if (ntiles > 0) issue(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // register e of the score tile is key t*BN + 8 (e / 4) + 4 hl + e % 4
+  auto probs = [&](auto mskc, f32x16& s, f32x16& dp, int t) {
+    constexpr bool MSK = decltype(mskc)::value;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float pv = fast_exp2(fmaf(p.cs, s[e], nl2));
+      if (MSK && t * BN + 8 * (e >> 2) + 4 * hl + (e & 3) > qrow) pv = 0.f;
+      dp[e] = pv * (dp[e] - dl);
+    }
+  };
+
+  auto tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+    if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, buf ^ 1>{});
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
       s = N::mfma(read_rows<D>(kr[buf], l32, kc, hl), qf[kc], s);
       dp = N::mfma(read_rows<D>(vr[buf], l32, kc, hl), gf[kc], dp);
     }
-    // register e is key t*BN + 8 (e / 4) + 4 hl + e % 4 of query qrow
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kk = t * BN + 8 * (e >> 2) + 4 * hl + (e & 3);
-      const bool ok = qrow < p.Nq && kk < p.Nkv && (!CAUSAL || kk <= qrow);
-      const float pv = ok ? fast_exp2(fmaf(p.cs, s[e], nl2)) : 0.f;
-      dp[e] = pv * (dp[e] - dl);
-    }
+    if (CAUSAL && t * BN + 31 > qw0)
+      probs(std::true_type{}, s, dp, t);
+    else
+      probs(std::false_type{}, s, dp, t);
     u32x4 ps[2];
     pack_tile<Tag>(dp, ps);
 #pragma unroll
@@ -407,8 +491,14 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
       const int row = kc * 16 + v_key;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dq[db] = N::mfma(read_cols<D>(kt[buf], row, db, v_d, v_sw), ps[kc], dq[db]);
+        dq[db] = N::mfma(read_cols<D>(ktr[buf], row, db, v_d, v_sw), ps[kc], dq[db]);
     }
+  };
+
+  if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
   if (qrow < p.Nq) store_row<D, Tag>(p.dq + (qrow0 + qrow) * D, dq, p.scale, hl);
 }
@@ -451,6 +541,21 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   return ATTN_OK;
 }
 
+#ifndef ATTN_BWD_NQB
+#define ATTN_BWD_NQB 2
+#endif
+constexpr int kDkdvQueryBlocks = ATTN_BWD_NQB;  // 32-row query blocks per dK/dV tile
+
+// Workgroups over which the query heads of one KV head are split for dK/dV:
+// the smallest divisor of G that gives at least two workgroups per compute
+// unit (G when none does).
+int bwd_head_split(int B, int Hkv, int Nkv, int G, int cus) {
+  const long long base = (long long)B * Hkv * ((Nkv + 127) / 128);
+  for (int d = 1; d < G; ++d)
+    if (G % d == 0 && base * d >= 2LL * cus) return d;
+  return G;
+}
+
 template <int D, class Tag>
 hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   const int rows = p.B * p.Hq * p.Nq;
@@ -461,13 +566,23 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   if (e != hipSuccess) return e;
   BwdParams pk = p;
   pk.n_tiles = (p.Nkv + 127) / 128;
-  pk.total = p.B * p.Hkv * pk.n_tiles;
+  pk.total = p.B * p.Hkv * p.hsplit * pk.n_tiles;
+  constexpr int NQB = kDkdvQueryBlocks;
   if (causal)
-    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, true>), dim3(pk.total), dim3(256), 0, st, pk);
+    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, true, NQB>), dim3(pk.total), dim3(256), 0, st,
+                       pk);
   else
-    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, false>), dim3(pk.total), dim3(256), 0, st, pk);
+    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, false, NQB>), dim3(pk.total), dim3(256), 0, st,
+                       pk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.hsplit > 1) {
+    const size_t n4 = (size_t)p.B * p.Hkv * p.Nkv * D / 4;
+    hipLaunchKernelGGL((attn_dkdv_reduce<Tag>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                       st, p, n4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   BwdParams pq = p;
   pq.n_tiles = (p.Nq + 127) / 128;
   pq.total = p.B * p.Hq * pq.n_tiles;
@@ -496,16 +611,22 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
                         causal, dtype);
   if (rc != ATTN_OK) return rc;
-  rc = attn_host::check_device(nullptr);
+  int cus = 0;
+  rc = attn_host::check_device(&cus);
   if (rc != ATTN_OK) return rc;
-  const long long kgrid = (long long)B * Hkv * ((Nkv + 127) / 128);
+  const int G = Hq / Hkv;
+  const int hsplit = bwd_head_split(B, Hkv, Nkv, G, cus);
+  const long long kgrid = (long long)B * Hkv * hsplit * ((Nkv + 127) / 128);
   const long long qgrid = (long long)B * Hq * ((Nq + 127) / 128);
   if (kgrid > INT32_MAX || qgrid > INT32_MAX) return ATTN_EINVAL;
 
+  // workspace: Delta and lse2 per query row, then (split) the fp32 partials
   hipStream_t st = (hipStream_t)stream;
   void* ws = nullptr;
   const size_t rows = (size_t)B * Hq * Nq;
-  hipError_t e = hipMallocAsync(&ws, rows * sizeof(float), st);
+  const size_t rows_bytes = (rows * sizeof(float) + 255) / 256 * 256;
+  const size_t part = hsplit > 1 ? (size_t)hsplit * B * Hkv * Nkv * D * sizeof(float) : 0;
+  hipError_t e = hipMallocAsync(&ws, 2 * rows_bytes + 2 * part, st);
   if (e != hipSuccess || !ws) {
     attn_host::set_last_hip_error((int)e);
     (void)hipGetLastError();
@@ -519,6 +640,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   p.dout = (const uint16_t*)dout;
   p.lse = lse;
   p.delta = (float*)ws;
+  p.lse2 = (float*)((char*)ws + rows_bytes);
+  p.dkp = hsplit > 1 ? (float*)((char*)ws + 2 * rows_bytes) : nullptr;
+  p.dvp = hsplit > 1 ? (float*)((char*)ws + 2 * rows_bytes + part) : nullptr;
+  p.hsplit = hsplit;
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
@@ -527,7 +652,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   p.Hkv = Hkv;
   p.Nq = Nq;
   p.Nkv = Nkv;
-  p.G = Hq / Hkv;
+  p.G = G;
   p.n_tiles = 0;
   p.total = 0;
   p.cs = scale * kLog2e;
