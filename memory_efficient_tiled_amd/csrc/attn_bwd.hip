@@ -14,9 +14,10 @@
 // K/V gradients of a KV head sum over the Hq / Hkv query heads that read it.
 // Kernels, no atomics (results are bitwise reproducible):
 //  * attn_delta_kernel: Delta and lse log2(e), one fp32 each per query row;
-//  * attn_dkdv_kernel: one workgroup per block of 128 keys of one KV head,
-//    looping over every query tile of the query heads it covers, with dK and
-//    dV accumulated in registers.  When the KV heads alone give too few
+//  * attn_dkdv_pair_kernel: one workgroup per block of 128 keys of one KV
+//    head, looping over every query tile of the query heads it covers, with
+//    dK and dV accumulated in registers (dV in one wave of a pair, dK in the
+//    other).  When the KV heads alone give too few
 //    workgroups, the query heads of a group are split over several
 //    workgroups that write fp32 partial sums, and attn_dkdv_reduce adds them;
 //  * attn_dq_kernel: one workgroup per 128 query rows, looping over key tiles
@@ -175,20 +176,41 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const f32x16* acc, floa
     }
 }
 
-// dK, dV for 128 keys (4 waves x 32) of KV head hk: loop over the query
-// tiles (BQ = 32 NQB rows) of the query heads this workgroup covers.  Per
-// tile and wave:
-//   S = Q K^T, dP = dO V^T          (rows: BQ queries, columns: 32 keys)
-//   P = exp2(cs S - lse2) (0 above the causal diagonal), dS = P (dP - Delta)
-//   dV^T += dO^T P, dK^T += Q^T dS  (rows: D, columns: 32 keys)
-// K and V of the wave's keys stay in registers (B operands); Q and dO tiles
-// are copied into LDS twice each (row-read and transposed layouts) with
-// their lse2 and Delta, two buffers deep.  The loop is unrolled by two so
-// that each buffer's LDS addresses are compile-time offsets.  One wave per
-// SIMD: the accumulators and operands need more than 256 registers.
-template <int D, class Tag, bool CAUSAL, int NQB>
-__global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
-  constexpr int NW = 4, BK = NW * 32, BQ = NQB * 32;
+// Stores a wave's dK^T or dV^T accumulators (column = this lane's key):
+// 16-bit rows times `mul`, or the fp32 partial of head split `hs`.
+template <int D, class Tag>
+__device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst, float* part,
+                                              const f32x16* acc, float mul, size_t krow, int hs,
+                                              int hl) {
+  constexpr int NDB = D / 32;
+  if (p.hsplit == 1) {
+    store_row<D, Tag>(dst + krow * D, acc, mul, hl);
+    return;
+  }
+  float* r = part + ((size_t)hs * p.B * p.Hkv * p.Nkv + krow) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(f32x4*)(r + db * 32 + 8 * i + 4 * hl) =
+          f32x4{acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]};
+}
+
+// dK, dV with paired waves: 8 waves over 128 keys; waves w and w + 4 (which
+// share a SIMD) own keys k0 + 32 (w % 4).  K and V of those keys stay in
+// registers, K in wave w, V in wave w + 4.  Per query tile of 64 rows:
+//   1. wave w:     S = Q K^T, P = exp2(cs S - lse2) (0 above the causal
+//                  diagonal), written to LDS packed as a B operand;
+//      wave w + 4: dP = dO V^T.
+//   2. wave w:     dV^T += dO^T P;
+//      wave w + 4: reads P, dS = P (dP - Delta), dK^T += Q^T dS.
+// Each wave needs half the registers of one that does all four products,
+// so two waves fit on a SIMD and one wave's softmax work overlaps the
+// other's matrix products.  Q and dO tiles are in LDS twice each, two
+// buffers deep, with lse2 and Delta.
+template <int D, class Tag, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
+  constexpr int NW = 8, BK = 128, BQ = 64, NQB = 2;
   constexpr int DC = D / 16, NDB = D / 32, NKC = BQ / 16, CPR = D / 8;
   constexpr int TILE = BQ * D;
   constexpr int IPW = BQ * CPR / 64 / NW;
@@ -199,12 +221,15 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t qt[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gr[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gt[2][TILE];
-  __shared__ __attribute__((aligned(256))) float lse_s[2][64];
-  __shared__ __attribute__((aligned(256))) float del_s[2][64];
+  __shared__ __attribute__((aligned(1024))) u32x4 xp[4][NKC][64];
+  __shared__ __attribute__((aligned(256))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(256))) float del_s[2][BQ];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int kw = wave & 3;
+  const bool pw = wave < 4;  // computes P (else dS)
 
   int bid = xcd_remap(blockIdx.x, p.total);
   const int kt = bid % p.n_tiles;
@@ -214,33 +239,28 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
   const int hk = bid % p.Hkv;
   const int b = bid / p.Hkv;
   const int k0 = kt * BK;
-  const int kw0 = k0 + wave * 32;           // the wave's first key
-  const int key = kw0 + l32;                // this lane's key (accumulator column)
-  const int hpw = p.G / p.hsplit;           // query heads per workgroup
+  const int kw0 = k0 + kw * 32;
+  const int key = kw0 + l32;
+  const int hpw = p.G / p.hsplit;
   const int h0 = hk * p.G + hs * hpw;
 
   const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
-  u32x4 kf[DC], vf[DC];
+  const uint16_t* kv = pw ? p.k : p.v;
+  u32x4 bf[DC];
 #pragma unroll
   for (int kc = 0; kc < DC; ++kc) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key < p.Nkv) {
-      x = *(const u32x4*)(p.k + (krow0 + key) * D + kc * 16 + hl * 8);
-      y = *(const u32x4*)(p.v + (krow0 + key) * D + kc * 16 + hl * 8);
-    }
-    kf[kc] = x;
-    vf[kc] = y;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key < p.Nkv) x = *(const u32x4*)(kv + (krow0 + key) * D + kc * 16 + hl * 8);
+    bf[kc] = x;
   }
-  f32x16 dk[NDB], dv[NDB];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) dk[i] = dv[i] = f32x16{};
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
   uint32_t roff[IPW], toff[IPW];
   copy_offsets<D, IPW, true>(wave, lane, roff);
   copy_offsets<D, IPW, false>(wave, lane, toff);
 
-  // Query tiles: for every covered head, from the first tile that can see a
-  // key of this block (causal) to the last.
   const int nqt = (p.Nq + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? min(nqt, k0 / BQ) : 0;
   const int per_head = nqt - qt0;
@@ -277,9 +297,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
   const int v_sw = v_swz<D>(v_key);
 
-  // P and dS of one tile in place of S and dP; accumulator register e of
-  // block qb is query row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.
-  auto probs = [&](auto mskc, auto bufc, f32x16* s, f32x16* dp, int q0) {
+  // P in place of S (P waves); accumulator register e of block qb is query
+  // row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.
+  auto probs = [&](auto mskc, auto bufc, f32x16* s, int q0) {
     constexpr bool MSK = decltype(mskc)::value;
     constexpr int buf = decltype(bufc)::value;
 #pragma unroll
@@ -288,13 +308,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
       for (int j = 0; j < 4; ++j) {
         const int r = qb * 32 + 8 * j + 4 * hl;
         const f32x4 ls = *(const f32x4*)(&lse_s[buf][r]);
-        const f32x4 dl = *(const f32x4*)(&del_s[buf][r]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
           if (MSK && key > q0 + r + e) pv = 0.f;
           s[qb][4 * j + e] = pv;
-          dp[qb][4 * j + e] = pv * (dp[qb][4 * j + e] - dl[e]);
         }
       }
   };
@@ -307,35 +325,57 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
     int hq, q0;
     tile_start(u, &hq, &q0);
 
-    f32x16 s[NQB], dp[NQB];
+    // 1. S (P waves) or dP (dS waves)
+    const uint16_t* ra = pw ? qr[buf] : gr[buf];
+    f32x16 s[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      s[qb] = dp[qb] = f32x16{};
+      s[qb] = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < DC; ++kc) {
-        s[qb] = N::mfma(read_rows<D>(qr[buf], qb * 32 + l32, kc, hl), kf[kc], s[qb]);
-        dp[qb] = N::mfma(read_rows<D>(gr[buf], qb * 32 + l32, kc, hl), vf[kc], dp[qb]);
+      for (int kc = 0; kc < DC; ++kc)
+        s[qb] = N::mfma(read_rows<D>(ra, qb * 32 + l32, kc, hl), bf[kc], s[qb]);
+    }
+    u32x4 bop[NKC];
+    if (pw) {
+      if (CAUSAL && kw0 + 31 > q0)
+        probs(std::true_type{}, bufc, s, q0);
+      else
+        probs(std::false_type{}, bufc, s, q0);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) pack_tile<Tag>(s[qb], &bop[qb * 2]);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) xp[kw][kc][lane] = bop[kc];
+    }
+    __syncthreads();
+    if (!pw) {
+      // dS = P (dP - Delta) from the partner's P
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x4 w = xp[kw][qb * 2 + hf][lane];
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * hf + jj;
+            const f32x4 dl = *(const f32x4*)(&del_s[buf][qb * 32 + 8 * j + 4 * hl]);
+            const float pv[4] = {lo_f32<Tag>(w[2 * jj]), hi_f32<Tag>(w[2 * jj]),
+                                 lo_f32<Tag>(w[2 * jj + 1]), hi_f32<Tag>(w[2 * jj + 1])};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              s[qb][4 * j + e] = pv[e] * (s[qb][4 * j + e] - dl[e]);
+          }
+        }
+        pack_tile<Tag>(s[qb], &bop[qb * 2]);
       }
     }
-    if (CAUSAL && kw0 + 31 > q0)
-      probs(std::true_type{}, bufc, s, dp, q0);
-    else
-      probs(std::false_type{}, bufc, s, dp, q0);
-    u32x4 pp[NKC], ps[NKC];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      pack_tile<Tag>(s[qb], &pp[qb * 2]);
-      pack_tile<Tag>(dp[qb], &ps[qb * 2]);
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS (reduction over the tile's queries).
+    // 2. dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves)
+    const uint16_t* rb = pw ? gt[buf] : qt[buf];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int row = kc * 16 + v_key;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv[db] = N::mfma(read_cols<D>(gt[buf], row, db, v_d, v_sw), pp[kc], dv[db]);
-        dk[db] = N::mfma(read_cols<D>(qt[buf], row, db, v_d, v_sw), ps[kc], dk[db]);
-      }
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = N::mfma(read_cols<D>(rb, row, db, v_d, v_sw), bop[kc], acc[db]);
     }
   };
 
@@ -346,24 +386,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(BwdParams p) {
   }
 
   if (key < p.Nkv) {
-    if (p.hsplit == 1) {
-      store_row<D, Tag>(p.dk + (krow0 + key) * D, dk, p.scale, hl);
-      store_row<D, Tag>(p.dv + (krow0 + key) * D, dv, 1.f, hl);
-    } else {
-      const size_t part = (size_t)hs * p.B * p.Hkv * p.Nkv;
-      float* dkr = p.dkp + (part + krow0 + key) * D;
-      float* dvr = p.dvp + (part + krow0 + key) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = db * 32 + 8 * i + 4 * hl;
-          *(f32x4*)(dkr + d) = f32x4{dk[db][4 * i], dk[db][4 * i + 1], dk[db][4 * i + 2],
-                                     dk[db][4 * i + 3]};
-          *(f32x4*)(dvr + d) = f32x4{dv[db][4 * i], dv[db][4 * i + 1], dv[db][4 * i + 2],
-                                     dv[db][4 * i + 3]};
-        }
-    }
+    if (pw)
+      store_kv_grad<D, Tag>(p, p.dv, p.dvp, acc, 1.f, krow0 + key, hs, hl);
+    else
+      store_kv_grad<D, Tag>(p, p.dk, p.dkp, acc, p.scale, krow0 + key, hs, hl);
   }
 }
 
@@ -541,11 +567,6 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   return ATTN_OK;
 }
 
-#ifndef ATTN_BWD_NQB
-#define ATTN_BWD_NQB 2
-#endif
-constexpr int kDkdvQueryBlocks = ATTN_BWD_NQB;  // 32-row query blocks per dK/dV tile
-
 // Workgroups over which the query heads of one KV head are split for dK/dV:
 // the smallest divisor of G that gives at least two workgroups per compute
 // unit (G when none does).
@@ -567,12 +588,11 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   BwdParams pk = p;
   pk.n_tiles = (p.Nkv + 127) / 128;
   pk.total = p.B * p.Hkv * p.hsplit * pk.n_tiles;
-  constexpr int NQB = kDkdvQueryBlocks;
   if (causal)
-    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, true, NQB>), dim3(pk.total), dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, true>), dim3(pk.total), dim3(512), 0, st,
                        pk);
   else
-    hipLaunchKernelGGL((attn_dkdv_kernel<D, Tag, false, NQB>), dim3(pk.total), dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, false>), dim3(pk.total), dim3(512), 0, st,
                        pk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
