@@ -100,13 +100,16 @@ __device__ __forceinline__ float pair_sum(float x) {
 //    x 64 contiguous bytes.  With 256-byte rows the 4 keys go to 4 disjoint
 //    64-byte quarters (XOR 4 * (r & 3)); with 128-byte rows keys r and r + 2
 //    share banks and are separated by XOR 4 * ((r >> 1) & 1).
+//  Rows of 512 bytes (D = 256) start on bank 0 like 256-byte rows and use
+//  the same two swizzles.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  static_assert(D == 64 || D == 128 || D == 256, "swizzles cover D = 64, 128, 256");
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
 // Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9.

@@ -572,22 +572,32 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // D = 128 that needs the single-buffered pipeline and part of Q^T in LDS to
 // fit the registers.  The wide tiles pay when they still give every slot of
 // the device a workgroup and no causal diagonal is wasted; otherwise the
-// 32-row waves are faster.
+// 32-row waves are faster.  At D = 256 a wave's 32 rows of O take 128
+// registers, so there is one tile: 32-row waves, 32-key tiles, the
+// single-buffered pipeline and half of Q^T (8 of 16 chunks) in LDS.
 struct TileCfg {
   int NW, QB, BN, QL;
   bool SB;
   constexpr int BM() const { return NW * QB * 32; }
   constexpr int resident_per_cu() const { return 4 * kWavesPerSimd / NW; }
 };
-enum { kCfgD64Narrow = 0, kCfgD64Wide = 1, kCfgD128Narrow = 2, kCfgD128Wide = 3 };
-constexpr TileCfg kCfgs[4] = {{4, 1, 64, 0, false},
+enum {
+  kCfgD64Narrow = 0,
+  kCfgD64Wide = 1,
+  kCfgD128Narrow = 2,
+  kCfgD128Wide = 3,
+  kCfgD256 = 4
+};
+constexpr TileCfg kCfgs[5] = {{4, 1, 64, 0, false},
                               {4, 2, 32, 0, false},
                               {8, 1, 64, 0, false},
-                              {8, 2, 32, 3, true}};
+                              {8, 2, 32, 3, true},
+                              {8, 1, 32, 8, true}};
 
 // The wide tiles of each head dimension are used without a causal mask when
 // they still fill every slot of the device at least once.
 int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
+  if (D == 256) return kCfgD256;
   const int narrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
   const int wide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
   const TileCfg& w = kCfgs[wide];
@@ -597,6 +607,8 @@ int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
 }
 
 thread_local int g_last_hip_error = 0;
+
+bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256; }
 
 struct DeviceInfo {
   bool init = false;
@@ -690,7 +702,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
              int dtype, const Layout& L) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
-  if (D != 64 && D != 128) return ATTN_EINVAL;
+  if (!head_dim_ok(D)) return ATTN_EINVAL;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (causal != 0 && causal != 1) return ATTN_EINVAL;
   if (!isfinite(scale)) return ATTN_EINVAL;
@@ -838,8 +850,8 @@ hipError_t dispatch(const Params& p, bool causal, bool split, bool strided, hipS
 template <int D, class Tag>
 hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool strided,
                       hipStream_t st) {
-  constexpr int kNarrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
-  constexpr int kWide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
+  constexpr int kNarrow = D == 256 ? kCfgD256 : D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
+  constexpr int kWide = D == 256 ? kCfgD256 : D == 128 ? kCfgD128Wide : kCfgD64Wide;
   if (cfg == kWide && !causal)
     return split ? launch_main<D, kWide, Tag, false, true>(p, strided, st)
                  : launch_main<D, kWide, Tag, false, false>(p, strided, st);
@@ -923,6 +935,9 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     if (D == 64)
       return dtype == ATTN_BF16 ? dispatch_d<64, TagBF16>(p, pl.cfg, cz, split, strided, stream)
                                 : dispatch_d<64, TagF16>(p, pl.cfg, cz, split, strided, stream);
+    if (D == 256)
+      return dtype == ATTN_BF16 ? dispatch_d<256, TagBF16>(p, pl.cfg, cz, split, strided, stream)
+                                : dispatch_d<256, TagF16>(p, pl.cfg, cz, split, strided, stream);
     return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, strided, stream)
                               : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, strided, stream);
   };
@@ -940,6 +955,9 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
       if (D == 64)
         e = dtype == ATTN_BF16 ? launch_combine<64, TagBF16>(p, strided, stream)
                                : launch_combine<64, TagF16>(p, strided, stream);
+      else if (D == 256)
+        e = dtype == ATTN_BF16 ? launch_combine<256, TagBF16>(p, strided, stream)
+                               : launch_combine<256, TagF16>(p, strided, stream);
       else
         e = dtype == ATTN_BF16 ? launch_combine<128, TagBF16>(p, strided, stream)
                                : launch_combine<128, TagF16>(p, strided, stream);
@@ -1032,7 +1050,7 @@ int attn_fwd_strided_check(const void* q, const void* k, const void* v, const vo
 int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,
                         int num_cus) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
-  if ((D != 64 && D != 128) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
+  if (!head_dim_ok(D) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
   if (causal != 0 && causal != 1) return ATTN_EINVAL;
   return make_plan(B, Hq, Nq, Nkv, D, causal, 0, num_cus).splits;
 }
@@ -1040,7 +1058,7 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int caus
 int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,
                   int num_splits, int num_cus, attn_plan* plan) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
-  if ((D != 64 && D != 128) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
+  if (!head_dim_ok(D) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
   if ((causal != 0 && causal != 1) || num_splits < 0 || !plan) return ATTN_EINVAL;
   if ((long long)B * Hq * Nq > INT32_MAX || (long long)B * Hkv * Nkv > INT32_MAX)
     return ATTN_EINVAL;

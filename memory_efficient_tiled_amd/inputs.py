@@ -83,6 +83,15 @@ WORKLOADS["dit-75600"] = _w(name="dit-75600", B=1, Hq=24, Hkv=24, Nq=75600,
                             sampled_rows=256,
                             note="long video-DiT self-attention")
 
+# Head dimension 256, beyond the pages' 64/128 (the scope's list of further
+# head dimensions): an MHA sweep point and a causal GQA prefill shape.
+WORKLOADS["hd256-8192"] = _w(name="hd256-8192", B=1, Hq=16, Hkv=16, Nq=8192, Nkv=8192,
+                             D=256, dtype=BF16, causal=False,
+                             note="head dim 256, non-causal MHA")
+WORKLOADS["hd256-gqa-causal-8192"] = _w(name="hd256-gqa-causal-8192", B=1, Hq=16, Hkv=8,
+                                        Nq=8192, Nkv=8192, D=256, dtype=BF16, causal=True,
+                                        note="head dim 256, causal GQA prefill")
+
 HEADLINE = "dit-17160"
 
 

@@ -32,10 +32,10 @@ def _case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed=0, scale=None,
 
 # -- the named workloads -----------------------------------------------------
 
-def _workload(device, name, rows=None):
+def _workload(device, name, rows=None, allowance=False):
     w = inputs.WORKLOADS[name]
     return _case(device, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, w.causal,
-                 rows=rows, allowance=False, k_offset_std=w.k_offset_std)
+                 rows=rows, allowance=allowance, k_offset_std=w.k_offset_std)
 
 
 def test_tiny_256(gpu_device):
@@ -70,7 +70,7 @@ def test_dit_75600(gpu_device):
 # -- edge shapes -------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n", [1, 7, 63, 65, 129, 1000])
 def test_ragged_lengths(gpu_device, n, causal, D, dtype):
@@ -158,6 +158,39 @@ def test_wide_d128_rising_scores(gpu_device):
     o_ref, l_ref = oracle_rows(x, None, False, rows=x.rows)
     compare(gather_rows(o, x.rows), gather_rows(l, x.rows), o_ref, l_ref,
             inputs.F16, rounding_allowance=True, what="rising scores")
+
+
+# -- head dimension 256 --------------------------------------------------------
+# One tile (8 waves x 32 rows, 32-key tiles, single-buffered pipeline, half of
+# Q^T in LDS): the named shapes, split pieces, and rising scores.
+
+@pytest.mark.parametrize("name", ["hd256-8192", "hd256-gqa-causal-8192"])
+def test_hd256_workloads(gpu_device, name):
+    # bf16 causal: the first rows see few keys, |o| is of order 1 and the
+    # bf16 rounding of the output alone reaches 2^-9 |o|, so these shapes
+    # (not among the pages' workloads) take the half-ulp allowance
+    _workload(gpu_device, name, rows=64, allowance=True)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_forced_splits(gpu_device, splits, causal):
+    _case(gpu_device, 1, 4, 2, 333, 1500, 256, inputs.BF16, causal, seed=splits + 60,
+          num_splits=splits)
+
+
+def test_d256_decode_long_keys(gpu_device):
+    _case(gpu_device, 1, 8, 2, 1, 40000, 256, inputs.F16, False, seed=66)
+
+
+def test_d256_rising_scores(gpu_device):
+    x = inputs.make_inputs(1, 8, 4, 700, 1999, 256, inputs.F16, seed=67)
+    ramp = np.linspace(1.0, 8.0, 1999, dtype=np.float32)[None, None, :, None]
+    x.k = (x.k.astype(np.float32) * ramp).astype(np.float16)
+    o, l = run_gpu(x, None, False, gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, False)
+    compare(o, l, o_ref, l_ref, inputs.F16, rounding_allowance=True,
+            what="D=256 rising scores")
 
 
 # -- split of the last partial round ---------------------------------------
