@@ -101,15 +101,20 @@ __device__ __forceinline__ float pair_sum(float x) {
 //    64-byte quarters (XOR 4 * (r & 3)); with 128-byte rows keys r and r + 2
 //    share banks and are separated by XOR 4 * ((r >> 1) & 1).
 //  Rows of 512 bytes (D = 256) start on bank 0 like 256-byte rows and use
-//  the same two swizzles.
+//  the same two swizzles.  Rows of 192 bytes (D = 96, 12 chunks) start on
+//  bank groups 0, 12, 8, 4 for r % 4 = 0..3: XOR-ing the chunk with
+//  (r >> 2) & 3 (which keeps it below 12) spreads 16 consecutive rows over
+//  all 16 groups, and 4 consecutive keys already cover four disjoint
+//  quarters for the transposing reads.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
-  static_assert(D == 64 || D == 128 || D == 256, "swizzles cover D = 64, 128, 256");
-  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+  static_assert(D == 64 || D == 96 || D == 128 || D == 256,
+                "swizzles cover D = 64, 96, 128, 256");
+  return D >= 128 ? (r & 15) : D == 96 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
-  return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  return D >= 128 ? 4 * (r & 3) : D == 96 ? 0 : 4 * ((r >> 1) & 1);
 }
 
 // Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9.

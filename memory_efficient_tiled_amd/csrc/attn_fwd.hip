@@ -574,7 +574,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // the device a workgroup and no causal diagonal is wasted; otherwise the
 // 32-row waves are faster.  At D = 256 a wave's 32 rows of O take 128
 // registers, so there is one tile: 32-row waves, 32-key tiles, the
-// single-buffered pipeline and half of Q^T (8 of 16 chunks) in LDS.
+// single-buffered pipeline and half of Q^T (8 of 16 chunks) in LDS.  At
+// D = 96 (12 chunks per row) the copies split evenly over 4 waves with
+// 64-key tiles: the D = 64 narrow tile.
 struct TileCfg {
   int NW, QB, BN, QL;
   bool SB;
@@ -586,18 +588,21 @@ enum {
   kCfgD64Wide = 1,
   kCfgD128Narrow = 2,
   kCfgD128Wide = 3,
-  kCfgD256 = 4
+  kCfgD256 = 4,
+  kCfgD96 = 5
 };
-constexpr TileCfg kCfgs[5] = {{4, 1, 64, 0, false},
+constexpr TileCfg kCfgs[6] = {{4, 1, 64, 0, false},
                               {4, 2, 32, 0, false},
                               {8, 1, 64, 0, false},
                               {8, 2, 32, 3, true},
-                              {8, 1, 32, 8, true}};
+                              {8, 1, 32, 8, true},
+                              {4, 1, 64, 0, false}};
 
 // The wide tiles of each head dimension are used without a causal mask when
 // they still fill every slot of the device at least once.
 int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
   if (D == 256) return kCfgD256;
+  if (D == 96) return kCfgD96;
   const int narrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
   const int wide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
   const TileCfg& w = kCfgs[wide];
@@ -608,7 +613,7 @@ int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
 
 thread_local int g_last_hip_error = 0;
 
-bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256; }
+bool head_dim_ok(int D) { return D == 64 || D == 96 || D == 128 || D == 256; }
 
 struct DeviceInfo {
   bool init = false;
@@ -850,8 +855,14 @@ hipError_t dispatch(const Params& p, bool causal, bool split, bool strided, hipS
 template <int D, class Tag>
 hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool strided,
                       hipStream_t st) {
-  constexpr int kNarrow = D == 256 ? kCfgD256 : D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
-  constexpr int kWide = D == 256 ? kCfgD256 : D == 128 ? kCfgD128Wide : kCfgD64Wide;
+  constexpr int kNarrow = D == 256 ? kCfgD256
+                          : D == 96 ? kCfgD96
+                          : D == 128 ? kCfgD128Narrow
+                                     : kCfgD64Narrow;
+  constexpr int kWide = D == 256 ? kCfgD256
+                        : D == 96 ? kCfgD96
+                        : D == 128 ? kCfgD128Wide
+                                   : kCfgD64Wide;
   if (cfg == kWide && !causal)
     return split ? launch_main<D, kWide, Tag, false, true>(p, strided, st)
                  : launch_main<D, kWide, Tag, false, false>(p, strided, st);
@@ -938,6 +949,9 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     if (D == 256)
       return dtype == ATTN_BF16 ? dispatch_d<256, TagBF16>(p, pl.cfg, cz, split, strided, stream)
                                 : dispatch_d<256, TagF16>(p, pl.cfg, cz, split, strided, stream);
+    if (D == 96)
+      return dtype == ATTN_BF16 ? dispatch_d<96, TagBF16>(p, pl.cfg, cz, split, strided, stream)
+                                : dispatch_d<96, TagF16>(p, pl.cfg, cz, split, strided, stream);
     return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, strided, stream)
                               : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, strided, stream);
   };
@@ -958,6 +972,9 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
       else if (D == 256)
         e = dtype == ATTN_BF16 ? launch_combine<256, TagBF16>(p, strided, stream)
                                : launch_combine<256, TagF16>(p, strided, stream);
+      else if (D == 96)
+        e = dtype == ATTN_BF16 ? launch_combine<96, TagBF16>(p, strided, stream)
+                               : launch_combine<96, TagF16>(p, strided, stream);
       else
         e = dtype == ATTN_BF16 ? launch_combine<128, TagBF16>(p, strided, stream)
                                : launch_combine<128, TagF16>(p, strided, stream);

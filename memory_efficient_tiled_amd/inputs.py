@@ -92,6 +92,14 @@ WORKLOADS["hd256-gqa-causal-8192"] = _w(name="hd256-gqa-causal-8192", B=1, Hq=16
                                         Nq=8192, Nkv=8192, D=256, dtype=BF16, causal=True,
                                         note="head dim 256, causal GQA prefill")
 
+# Head dimension 96 (same list): MHA, non-causal and causal, 8192 tokens.
+WORKLOADS["hd96-8192"] = _w(name="hd96-8192", B=1, Hq=32, Hkv=32, Nq=8192, Nkv=8192,
+                            D=96, dtype=BF16, causal=False,
+                            note="head dim 96, non-causal MHA")
+WORKLOADS["hd96-causal-8192"] = _w(name="hd96-causal-8192", B=1, Hq=32, Hkv=32, Nq=8192,
+                                   Nkv=8192, D=96, dtype=BF16, causal=True,
+                                   note="head dim 96, causal MHA prefill")
+
 HEADLINE = "dit-17160"
 
 

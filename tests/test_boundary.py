@@ -62,13 +62,14 @@ def test_valid_arguments_pass():
     assert check(lse=None) == OK          # LSE output is optional
     assert check(scale=-0.5) == OK        # any finite scale
     assert check(scale=0.0) == OK
-    assert check(D=256) == OK             # head dims 64, 128 and 256
+    assert check(D=256) == OK             # head dims 64, 96, 128 and 256
+    assert check(D=96) == OK
 
 
 @pytest.mark.parametrize("kw", [
     dict(B=0), dict(Hq=0), dict(Hkv=0), dict(Nq=0), dict(Nkv=-5),
     dict(Hq=6, Hkv=4),                     # Hq not a multiple of Hkv
-    dict(D=96), dict(D=32), dict(D=512), dict(dtype=2), dict(causal=2),
+    dict(D=80), dict(D=32), dict(D=512), dict(dtype=2), dict(causal=2),
     dict(scale=float("inf")), dict(scale=float("nan")),
     dict(q=None), dict(k=None), dict(v=None), dict(out=None),
     dict(q=Q + 8), dict(out=O + 2), dict(lse=L + 2),       # misaligned
@@ -113,6 +114,7 @@ def test_split_heuristic():
     # D = 256 has one tile: 8 waves of 32 rows
     assert plan(1, 16, 16, 8192, 8192, 256, 0).tile_rows == 256
     assert plan(1, 16, 8, 8192, 8192, 256, 1).tile_rows == 256
+    assert plan(1, 32, 32, 8192, 8192, 96, 0).tile_rows == 128
     # a grid of whole rounds is never split
     p = plan(1, 32, 32, 2048, 2048, 128, 0)
     assert p.num_splits == 1 and p.split_rows == 0 and p.workspace_bytes == 0

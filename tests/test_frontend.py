@@ -47,8 +47,9 @@ def test_unsupported_inputs():
     q = t(1, 2, 100, 64)
     assert "dtype" in reason(q.float(), q.float(), q.float())
     assert "head dimension" in reason(t(1, 2, 10, 80), t(1, 2, 10, 80), t(1, 2, 10, 80))
-    w = t(1, 2, 10, 256)
-    assert reason(w, w, w) == "inputs must be on one HIP device"
+    for e in (96, 256):
+        w = t(1, 2, 10, e)
+        assert reason(w, w, w) == "inputs must be on one HIP device"
     wg = t(1, 2, 10, 256).requires_grad_()
     assert "gradients" in reason(wg, wg, wg)
     assert "3-D" in reason(t(2, 100, 64)[0], t(2, 100, 64)[0], t(2, 100, 64)[0])

@@ -70,7 +70,7 @@ def test_dit_75600(gpu_device):
 # -- edge shapes -------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n", [1, 7, 63, 65, 129, 1000])
 def test_ragged_lengths(gpu_device, n, causal, D, dtype):
@@ -191,6 +191,24 @@ def test_d256_rising_scores(gpu_device):
     o_ref, l_ref = oracle_rows(x, None, False)
     compare(o, l, o_ref, l_ref, inputs.F16, rounding_allowance=True,
             what="D=256 rising scores")
+
+
+# -- head dimension 96 ---------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["hd96-8192", "hd96-causal-8192"])
+def test_hd96_workloads(gpu_device, name):
+    _workload(gpu_device, name, rows=64, allowance=True)
+
+
+@pytest.mark.parametrize("splits", [3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d96_forced_splits_gqa(gpu_device, splits, causal):
+    _case(gpu_device, 1, 6, 2, 333, 1500, 96, inputs.F16, causal, seed=splits + 70,
+          num_splits=splits)
+
+
+def test_d96_decode_long_keys(gpu_device):
+    _case(gpu_device, 1, 8, 2, 1, 30000, 96, inputs.BF16, False, seed=73)
 
 
 # -- split of the last partial round ---------------------------------------
