@@ -60,9 +60,10 @@ enum {
  * lse     : device pointer to float32 [B,Hq,Nq] (natural log), or NULL to
  *           skip writing it.
  * B, Hq, Hkv, Nq, Nkv : > 0, Hq a multiple of Hkv.
- * D       : 64, 96, 128 or 256 (the tile table is per head dimension;
- *           the extension past the pages' 64/128 follows the scope's list
- *           of further head dimensions).
+ * D       : 64, 80, 96, 128 or 256 (the tile table is per head
+ *           dimension; the extension past the pages' 64/128 follows the
+ *           scope's list of further head dimensions; 80 is computed as 96
+ *           with zero padding inside the kernel).
  * scale   : finite softmax scale (PyTorch's default is 1/sqrt(D); the
  *           ai-manual.ru snippet divides scores by sqrt(dim)).
  * causal  : 0 = every key, 1 = keys j <= i (top-left).
@@ -201,8 +202,8 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
  * dq       : [B,Hq,Nq,D]; dk, dv: [B,Hkv,Nkv,D]; same dtype, written
  *            completely (no accumulation into their previous contents);
  *            must not overlap each other or any input.
- * All pointers 16-byte aligned; D in {64, 128} (the forward also takes 96
- * and 256; their gradients are not built); Hq a multiple of Hkv.
+ * All pointers 16-byte aligned; D in {64, 128} (the forward also takes 80,
+ * 96 and 256; their gradients are not built); Hq a multiple of Hkv.
  * Allocates a float32 [B,Hq,Nq] workspace (Delta) on `stream` with
  * hipMallocAsync and frees it there.  Returns ATTN_OK, ATTN_EINVAL,
  * ATTN_EUNSUPPORTED, ATTN_ENOMEM or ATTN_EHIP.  Results are deterministic

@@ -51,6 +51,12 @@ namespace {
 // fails it (and on the first tile, where m is still -inf).
 constexpr float kMaxPartialSum = 256.0f;
 
+// Columns the products run over for head dimension D (see attn_fwd_kernel).
+constexpr int compute_dim(int D) { return D == 80 ? 96 : D; }
+
+// A buffer offset past every tile's buffer size: such a copy reads zeros.
+constexpr uint32_t kPadOffset = 0x80000000u;
+
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
@@ -101,21 +107,28 @@ struct Params {
 //
 // STRIDED takes the tensors' batch, head and sequence strides from Params;
 // otherwise the layouts are contiguous and the strides compile-time values.
+//
+// The products run over DP = compute_dim(D) columns: D itself, except that
+// D = 80 (not a multiple of the 32-column output blocks) is computed as 96
+// with the last two 16-byte chunks of every Q, K and V row read as zeros and
+// the matching output columns not stored.
 template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB, bool SPLIT,
           bool STRIDED>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
+  constexpr int DP = compute_dim(D);    // columns of the products and LDS rows
   constexpr int WR = QB * 32;           // query rows per wave
   constexpr int BM = NW * WR;
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int TILE = BN * D;          // elements of one K (or V) tile
+  constexpr int CPR = DP / 8;           // 16-byte chunks per LDS row
+  constexpr int CPG = D / 8;            // 16-byte chunks per row in memory
+  constexpr int TILE = BN * DP;         // elements of one K (or V) tile
   constexpr int INSTR = BN * CPR / 64;  // 1 KB wave copies per tile
   static_assert(INSTR % NW == 0, "tile copies must split evenly over waves");
   constexpr int IPW = INSTR / NW;
-  constexpr int DC = D / 16;            // reduction chunks of Q K^T
+  constexpr int DC = DP / 16;           // reduction chunks of Q K^T
   constexpr int NKB = BN / 32;          // 32-key blocks per tile
-  constexpr int NDB = D / 32;           // 32-wide output column blocks
+  constexpr int NDB = DP / 32;          // 32-wide output column blocks
   constexpr int NKC = BN / 16;          // reduction chunks of P V
-  constexpr int ROWB = D * 2;           // bytes per K/V row
+  constexpr int ROWB = D * 2;           // bytes per K/V row in memory
   constexpr int DCR = DC - QL;          // Q^T chunks held in registers
   static_assert(QL >= 0 && QL < DC, "at least one Q^T chunk stays in registers");
   using N = Num<Tag>;
@@ -164,14 +177,16 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const uint16_t* Vg = p.v + (STRIDED ? b * p.vsb + hk * p.vsh : ((int64_t)b * p.Hkv + hk) * kvh);
 
   // Per-lane byte offsets of this wave's copy slots within a tile (the same
-  // for every tile) and the LDS slot each copy fills.
+  // for every tile) and the LDS slot each copy fills.  Padding chunks (past
+  // the row in memory) get an offset beyond any buffer, so they read zero.
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int slot = (wave * IPW + j) * 64 + lane;
     const int row = slot / CPR, pc = slot % CPR;
-    koff[j] = row * ksn * 2 + ((pc ^ k_swz<D>(row)) << 4);
-    voff[j] = row * vsn * 2 + ((pc ^ v_swz<D>(row)) << 4);
+    const int kch = pc ^ k_swz<DP>(row), vch = pc ^ v_swz<DP>(row);
+    koff[j] = kch < CPG ? row * ksn * 2 + (kch << 4) : kPadOffset;
+    voff[j] = vch < CPG ? row * vsn * 2 + (vch << 4) : kPadOffset;
   }
   // Copy tile `t` of K (or V, rows `sn` elements apart) into LDS.  The
   // buffer ends with the last key's row, so rows past it (which start at or
@@ -196,7 +211,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < p.Nq) x = *(const u32x4*)(Qg + (size_t)row * qsn + kc * 16 + hl * 8);
+      if (row < p.Nq && kc * 16 + hl * 8 < D)
+        x = *(const u32x4*)(Qg + (size_t)row * qsn + kc * 16 + hl * 8);
       if (kc < DCR)
         qf[qb][kc < DCR ? kc : 0] = x ^ p.qsign;
       else
@@ -232,7 +248,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);          // key within a 16-key chunk (first half)
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);  // column within a 32-wide block
-  const int v_sw = v_swz<D>(v_key);               // same for key v_key + 16 kc (+ 8)
+  const int v_sw = v_swz<DP>(v_key);              // same for key v_key + 16 kc (+ 8)
 
   // Scores of a tile: s[qb * NKB + kb] (32 keys x 32 rows); probabilities
   // pf[qb * NKC + kc] (16 keys x 32 rows, the P^T operands).
@@ -250,7 +266,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int row = kb * 32 + l32;
-        const u32x4 a = *(const u32x4*)(ks + row * D + (((2 * kc + hl) ^ k_swz<D>(row)) << 3));
+        const u32x4 a = *(const u32x4*)(ks + row * DP + (((2 * kc + hl) ^ k_swz<DP>(row)) << 3));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, bq[qb], s[qb * NKB + kb]);
       }
@@ -311,7 +327,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
       for (int kb = 0; kb < NKB; ++kb) {
         const int key = k0 + kb * 32 + l32;
         u32x4 a = {0u, 0u, 0u, 0u};
-        if (key < p.Nkv) a = *(const u32x4*)(Kg + (size_t)key * ksn + kc * 16 + hl * 8);
+        if (key < p.Nkv && kc * 16 + hl * 8 < D)
+          a = *(const u32x4*)(Kg + (size_t)key * ksn + kc * 16 + hl * 8);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb * NKB + kb] = N::mfma(a, qop(qb, kc, qmine), s[qb * NKB + kb]);
       }
@@ -380,8 +397,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
       for (int db = 0; db < NDB; ++db) {
         const int d = db * 32 + v_d;
         const int off = (((d >> 3) ^ v_sw) << 3) + (d & 7);
-        const u32x2 lo = lds_read_tr16(vs + key * D + off);
-        const u32x2 hi = lds_read_tr16(vs + (key + 8) * D + off);
+        const u32x2 lo = lds_read_tr16(vs + key * DP + off);
+        const u32x2 hi = lds_read_tr16(vs + (key + 8) * DP + off);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -497,9 +514,10 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            const int col = db * 32 + 8 * i + 4 * hl;
             const f32x16& o = oacc[qb * NDB + db];
             f32x4 y = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv, o[4 * i + 3] * inv};
-            *(f32x4*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+            if (DP == D || col < D) *(f32x4*)(dst + col) = y;
           }
         if (hl == 0) p.lsepart[prow] = lse_v;
       } else {
@@ -509,10 +527,11 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            const int col = db * 32 + 8 * i + 4 * hl;
             const f32x16& o = oacc[qb * NDB + db];
             u32x2 y = {N::pack2(o[4 * i] * inv, o[4 * i + 1] * inv),
                        N::pack2(o[4 * i + 2] * inv, o[4 * i + 3] * inv)};
-            *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+            if (DP == D || col < D) *(u32x2*)(dst + col) = y;
           }
         if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
       }
@@ -576,7 +595,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // registers, so there is one tile: 32-row waves, 32-key tiles, the
 // single-buffered pipeline and half of Q^T (8 of 16 chunks) in LDS.  At
 // D = 96 (12 chunks per row) the copies split evenly over 4 waves with
-// 64-key tiles: the D = 64 narrow tile.
+// 64-key tiles: the D = 64 narrow tile.  D = 80 runs the D = 96 tile with
+// two zero chunks per row.
 struct TileCfg {
   int NW, QB, BN, QL;
   bool SB;
@@ -602,7 +622,7 @@ constexpr TileCfg kCfgs[6] = {{4, 1, 64, 0, false},
 // they still fill every slot of the device at least once.
 int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
   if (D == 256) return kCfgD256;
-  if (D == 96) return kCfgD96;
+  if (D == 96 || D == 80) return kCfgD96;
   const int narrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
   const int wide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
   const TileCfg& w = kCfgs[wide];
@@ -613,7 +633,7 @@ int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
 
 thread_local int g_last_hip_error = 0;
 
-bool head_dim_ok(int D) { return D == 64 || D == 96 || D == 128 || D == 256; }
+bool head_dim_ok(int D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
 
 struct DeviceInfo {
   bool init = false;
@@ -856,13 +876,13 @@ template <int D, class Tag>
 hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool strided,
                       hipStream_t st) {
   constexpr int kNarrow = D == 256 ? kCfgD256
-                          : D == 96 ? kCfgD96
-                          : D == 128 ? kCfgD128Narrow
-                                     : kCfgD64Narrow;
+                          : D == 96 || D == 80 ? kCfgD96
+                          : D == 128           ? kCfgD128Narrow
+                                               : kCfgD64Narrow;
   constexpr int kWide = D == 256 ? kCfgD256
-                        : D == 96 ? kCfgD96
-                        : D == 128 ? kCfgD128Wide
-                                   : kCfgD64Wide;
+                        : D == 96 || D == 80 ? kCfgD96
+                        : D == 128           ? kCfgD128Wide
+                                             : kCfgD64Wide;
   if (cfg == kWide && !causal)
     return split ? launch_main<D, kWide, Tag, false, true>(p, strided, st)
                  : launch_main<D, kWide, Tag, false, false>(p, strided, st);
@@ -952,6 +972,9 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     if (D == 96)
       return dtype == ATTN_BF16 ? dispatch_d<96, TagBF16>(p, pl.cfg, cz, split, strided, stream)
                                 : dispatch_d<96, TagF16>(p, pl.cfg, cz, split, strided, stream);
+    if (D == 80)
+      return dtype == ATTN_BF16 ? dispatch_d<80, TagBF16>(p, pl.cfg, cz, split, strided, stream)
+                                : dispatch_d<80, TagF16>(p, pl.cfg, cz, split, strided, stream);
     return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, strided, stream)
                               : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, strided, stream);
   };
@@ -975,6 +998,9 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
       else if (D == 96)
         e = dtype == ATTN_BF16 ? launch_combine<96, TagBF16>(p, strided, stream)
                                : launch_combine<96, TagF16>(p, strided, stream);
+      else if (D == 80)
+        e = dtype == ATTN_BF16 ? launch_combine<80, TagBF16>(p, strided, stream)
+                               : launch_combine<80, TagF16>(p, strided, stream);
       else
         e = dtype == ATTN_BF16 ? launch_combine<128, TagBF16>(p, strided, stream)
                                : launch_combine<128, TagF16>(p, strided, stream);

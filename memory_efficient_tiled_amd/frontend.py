@@ -5,7 +5,7 @@ release") ships its method as a replacement for PyTorch's SDPA call: calls
 it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
 
 * ``sdpa(query, key, value, ...)`` has SDPA's signature and semantics for
-  what this library computes (head dim 64, 96, 128 or 256; no mask, no
+  what this library computes (head dim 64, 80, 96, 128 or 256; no mask, no
   dropout, top-left causal, GQA via ``enable_gqa``, default scale
   1/sqrt(E)) and raises ``NotImplementedError`` for anything else; inputs may be strided views such as [B, N, H, E]
   storage transposed to [B, H, N, E] (no copy is made).
@@ -50,8 +50,8 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
             torch.float16, torch.bfloat16):
         return "dtype must be float16 or bfloat16 for all inputs"
     E = query.shape[-1]
-    if E not in (64, 96, 128, 256) or key.shape[-1] != E or value.shape[-1] != E:
-        return "head dimension must be 64, 96, 128 or 256 for query, key and value"
+    if E not in (64, 80, 96, 128, 256) or key.shape[-1] != E or value.shape[-1] != E:
+        return "head dimension must be 64, 80, 96, 128 or 256 for query, key and value"
     if E not in (64, 128) and torch.is_grad_enabled() and any(t.requires_grad for t in ts):
         return "gradients are built for head dimensions 64 and 128 only"
     if key.shape != value.shape:

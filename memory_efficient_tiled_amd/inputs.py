@@ -100,6 +100,11 @@ WORKLOADS["hd96-causal-8192"] = _w(name="hd96-causal-8192", B=1, Hq=32, Hkv=32, 
                                    Nkv=8192, D=96, dtype=BF16, causal=True,
                                    note="head dim 96, causal MHA prefill")
 
+# Head dimension 80 (same list): MHA, non-causal, 8192 tokens, fp16.
+WORKLOADS["hd80-8192"] = _w(name="hd80-8192", B=1, Hq=32, Hkv=32, Nq=8192, Nkv=8192,
+                            D=80, dtype=F16, causal=False,
+                            note="head dim 80, non-causal MHA")
+
 HEADLINE = "dit-17160"
 
 

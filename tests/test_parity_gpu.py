@@ -70,7 +70,7 @@ def test_dit_75600(gpu_device):
 # -- edge shapes -------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
-@pytest.mark.parametrize("D", [64, 96, 128, 256])
+@pytest.mark.parametrize("D", [64, 80, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n", [1, 7, 63, 65, 129, 1000])
 def test_ragged_lengths(gpu_device, n, causal, D, dtype):
@@ -209,6 +209,33 @@ def test_d96_forced_splits_gqa(gpu_device, splits, causal):
 
 def test_d96_decode_long_keys(gpu_device):
     _case(gpu_device, 1, 8, 2, 1, 30000, 96, inputs.BF16, False, seed=73)
+
+
+# -- head dimension 80 (computed as 96 with two zero chunks per row) ---------
+
+def test_hd80_workload(gpu_device):
+    _workload(gpu_device, "hd80-8192", rows=64, allowance=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d80_forced_splits_gqa(gpu_device, causal):
+    _case(gpu_device, 1, 6, 3, 250, 1300, 80, inputs.BF16, causal, seed=80, num_splits=4)
+
+
+def test_d80_strided(gpu_device):
+    """[B, N, H, 80] storage: rows of the sequence are H * 80 elements apart,
+    so the zero chunks must not pick up the next head's values."""
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd
+    x = inputs.make_inputs(1, 4, 4, 300, 300, 80, inputs.F16, seed=81)
+    q, k, v = (to_device(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), inputs.F16,
+                         gpu_device).transpose(1, 2) for a in (x.q, x.k, x.v))
+    out, lse = attn_fwd(q, k, v)
+    torch.cuda.synchronize(gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, False)
+    compare(out.float().cpu().numpy().astype(np.float64),
+            lse.cpu().numpy().astype(np.float64), o_ref, l_ref, inputs.F16,
+            rounding_allowance=True, what="D=80 strided")
 
 
 # -- split of the last partial round ---------------------------------------
