@@ -25,7 +25,11 @@ article, section 3 "Self-written memory-efficient attention").
 
 Readings where the pages are silent (listed again in the design notes):
   * J_i = all keys, or with ``causal`` the keys j <= i (top-left alignment,
-    as PyTorch's scaled_dot_product_attention applies is_causal);
+    as PyTorch's scaled_dot_product_attention applies is_causal); with a
+    ``causal_offset`` c the keys j <= i + c (c = Nkv - Nq is the bottom-right
+    alignment of PyTorch's causal_lower_right bias, where the last query
+    row sees every key).  A row whose J_i is empty (bottom-right with
+    Nq > Nkv) has o_i = 0 and lse_i = -inf: the sum over an empty set;
   * query head hq reads KV head hq // (Hq // Hkv): the post's "flattened GQA"
     groups consecutive query heads on one KV head (section "The DIY
     approach");
@@ -85,11 +89,13 @@ def scale_value(scale: float | None, D: int) -> float:
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
               causal: bool, rows: np.ndarray | None = None,
-              row_group: int = 256) -> tuple[np.ndarray, np.ndarray]:
+              row_group: int = 256,
+              causal_offset: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """Exact softmax attention in float64.
 
     q: [B, Hq, Nq, D], k and v: [B, Hkv, Nkv, D], all float64.
     rows: None (all Nq rows) or int array [Hq, R] or [R] of query rows.
+    causal_offset: with ``causal``, row i sees keys j <= i + causal_offset.
     Returns (o [B, Hq, R, D], lse [B, Hq, R]) in float64, natural log.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -120,12 +126,14 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                 ri = rows_h[hq, r0:r0 + row_group]
                 s = scale * (q[b, hq, ri] @ kk.T)            # [r, Nkv]
                 if causal:
-                    s = np.where(key_idx[None, :] <= ri[:, None], s, -np.inf)
+                    s = np.where(key_idx[None, :] <= ri[:, None] + causal_offset, s, -np.inf)
                 m = s.max(axis=1, keepdims=True)
+                empty = ~np.isfinite(m)                        # rows with no allowed key
+                m = np.where(empty, 0.0, m)
                 e = np.exp(s - m)
-                denom = e.sum(axis=1, keepdims=True)
+                denom = np.where(empty, 1.0, e.sum(axis=1, keepdims=True))
                 o[b, hq, r0:r0 + len(ri)] = (e @ vv) / denom
-                lse[b, hq, r0:r0 + len(ri)] = (m + np.log(denom))[:, 0]
+                lse[b, hq, r0:r0 + len(ri)] = np.where(empty, -np.inf, (m + np.log(denom)))[:, 0]
     return o, lse
 
 
@@ -144,7 +152,7 @@ def attention_from_storage(q, k, v, dtype: str, scale: float | None,
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                        do: np.ndarray, scale: float, causal: bool,
-                       row_group: int = 256):
+                       row_group: int = 256, causal_offset: int = 0):
     """Gradients of softmax attention in float64: (dq, dk, dv).
 
     For a loss whose gradient with respect to the output is ``do``
@@ -159,7 +167,8 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
     K/V gradients of a KV head sum over the query heads that read it (the
     GQA grouping of the forward).  Masked keys have P = 0 and get nothing
-    from that row.  The post's first tier keeps autograd through its tiled
+    from that row; a row with no allowed key (see ``attention``) has o = 0
+    whatever the inputs, so all its gradients are 0.  The post's first tier keeps autograd through its tiled
     forward (section "The DIY approach"); these are the gradients it yields.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -186,10 +195,11 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 ri = np.arange(r0, min(Nq, r0 + row_group), dtype=np.int64)
                 s = scale * (q[b, hq, ri] @ kk.T)
                 if causal:
-                    s = np.where(key_idx[None, :] <= ri[:, None], s, -np.inf)
+                    s = np.where(key_idx[None, :] <= ri[:, None] + causal_offset, s, -np.inf)
                 m = s.max(axis=1, keepdims=True)
+                m = np.where(np.isfinite(m), m, 0.0)             # rows with no allowed key
                 e = np.exp(s - m)
-                p = e / e.sum(axis=1, keepdims=True)              # softmax rows
+                p = e / np.maximum(e.sum(axis=1, keepdims=True), 1e-300)   # softmax rows
                 g = do[b, hq, ri]                                  # dL/dO rows
                 dv[b, hk] += p.T @ g
                 dp = g @ vv.T

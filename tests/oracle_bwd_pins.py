@@ -1,6 +1,6 @@
 """Pins for the oracle's attention gradients: facts fixed by mathematics.
 
-Every pin takes ``bwd(q, k, v, do, scale, causal) -> (dq, dk, dv)`` (float64
+Every pin takes ``bwd(q, k, v, do, scale, causal, causal_offset=0) -> (dq, dk, dv)`` (float64
 arrays, q/do [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D]) and raises AssertionError when
 it disagrees.  The strongest is the derivative itself: central finite
 differences of the (separately pinned) forward oracle along random
@@ -95,5 +95,36 @@ def pin_gqa_repeat(bwd):
     _close(dv, dvr.reshape(1, 2, 3, 6, 4).sum(axis=2), 1e-12, "gqa dv")
 
 
+def pin_finite_differences_offset(bwd):
+    """The same derivative check with the causal diagonal moved by an offset:
+    bottom-right alignment (Nkv - Nq) with more keys than queries, and with
+    more queries than keys, where the first rows see no key at all (their
+    output is 0 whatever the inputs, so they contribute no gradient)."""
+    for seed, Nq, Nkv in ((11, 5, 9), (12, 9, 5)):
+        c = Nkv - Nq
+        q, k, v, do = _inputs(seed, Hq=2, Hkv=1, Nq=Nq, Nkv=Nkv)
+        scale = 0.6
+        dq, dk, dv = bwd(q, k, v, do, scale, True, causal_offset=c)
+        r = _rng(200 + seed)
+        h = 1e-5
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            d = r.standard_normal(x.shape)
+            def loss(xx):
+                args = {"q": q, "k": k, "v": v}
+                args[name] = xx
+                o, _ = oracle.attention(args["q"], args["k"], args["v"], scale, True,
+                                        causal_offset=c)
+                return float(np.sum(o * do))
+            fd = (loss(x + h * d) - loss(x - h * d)) / (2 * h)
+            an = float(np.sum(g * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), \
+                f"d{name} (offset {c}): finite difference {fd:.10f} vs {an:.10f}"
+        if c < 0:
+            assert np.all(dq[:, :, :-c] == 0.0), "rows without keys have no dq"
+        else:
+            # the last row sees every key; key c + i is the first that row i sees
+            assert np.all(np.isfinite(dk)) and np.any(dk[:, :, -1] != 0.0)
+
+
 ALL_PINS = [pin_finite_differences, pin_causal_row0_dq, pin_zero_do, pin_column_sums,
-            pin_linear_in_do, pin_gqa_repeat]
+            pin_linear_in_do, pin_gqa_repeat, pin_finite_differences_offset]

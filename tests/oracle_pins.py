@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import json
 import math
+import warnings
 import os
 from decimal import Decimal, localcontext
 from fractions import Fraction
@@ -321,7 +322,61 @@ def pin_rows_subset(attn):
             _close(ls[0, h], lf[0, h, rows[h]], what="rows subset lse")
 
 
+# ---------------------------------------------------------------------------
+# 6. Causal alignment with an offset (bottom-right: offset = Nkv - Nq).
+# ---------------------------------------------------------------------------
+
+def pin_causal_offset_torch(attn):
+    """PyTorch CPU SDPA in float64 with its lower-right causal bias (and an
+    explicit boolean tril mask for other offsets) on the rows that see a
+    key; rows that see none are o = 0, lse = -inf by definition."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention.bias import causal_lower_right
+    rng = _rng(30)
+    for B, Hq, Hkv, Nq, Nkv, D, off in [(1, 4, 2, 17, 29, 8, None), (2, 2, 1, 5, 40, 16, None),
+                                       (1, 3, 1, 29, 17, 8, None), (1, 2, 2, 12, 12, 8, 3),
+                                       (1, 2, 1, 20, 9, 8, -4)]:
+        c = Nkv - Nq if off is None else off
+        q = rng.standard_normal((B, Hq, Nq, D))
+        k = rng.standard_normal((B, Hkv, Nkv, D))
+        v = rng.standard_normal((B, Hkv, Nkv, D))
+        scale = 1.0 / math.sqrt(D)
+        if off is None:
+            mask = causal_lower_right(Nq, Nkv)   # NaN rows when Nq > Nkv: not compared
+        else:
+            mask = torch.ones(Nq, Nkv, dtype=torch.bool).tril(diagonal=off)
+        kt, vt = (torch.from_numpy(np.repeat(a, Hq // Hkv, axis=1)) for a in (k, v))
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore", UserWarning)
+            ref = F.scaled_dot_product_attention(torch.from_numpy(q), kt, vt, attn_mask=mask,
+                                                 scale=scale).numpy()
+        o, lse = attn(q, k, v, scale, True, causal_offset=c)
+        seen = np.arange(Nq) + c >= 0
+        _close(o[:, :, seen], ref[:, :, seen], tol=1e-11,
+               what=f"causal offset {c} vs torch {B,Hq,Hkv,Nq,Nkv,D}")
+        assert np.all(o[:, :, ~seen] == 0.0), "rows without keys must be 0"
+        assert np.all(np.isneginf(lse[:, :, ~seen])), "rows without keys: lse = -inf"
+        assert np.all(np.isfinite(lse[:, :, seen]))
+
+
+def pin_causal_offset_shift(attn):
+    """With Nq <= Nkv, bottom-right attention of Q equals the last Nq rows of
+    top-left attention of Q placed after Nkv - Nq other query rows."""
+    rng = _rng(31)
+    for G in (1, 3):
+        q = rng.standard_normal((1, 2 * G, 7, 8))
+        k = rng.standard_normal((1, 2, 19, 8))
+        v = rng.standard_normal((1, 2, 19, 8))
+        pad = np.concatenate([rng.standard_normal((1, 2 * G, 12, 8)), q], axis=2)
+        o1, l1 = attn(q, k, v, 0.4, True, causal_offset=12)
+        o2, l2 = attn(pad, k, v, 0.4, True)
+        _close(o1, o2[:, :, 12:], what="offset shift o")
+        _close(l1, l2[:, :, 12:], what="offset shift lse")
+
+
 ALL_PINS = [pin_bruteforce, pin_torch_sdpa, pin_golden, pin_q_zero, pin_v_const,
             pin_causal_row0, pin_single_key, pin_dominant_key, pin_key_shift,
             pin_kv_permutation, pin_query_permutation, pin_gqa_repeat,
-            pin_linear_in_v, pin_convex_hull, pin_rows_subset]
+            pin_linear_in_v, pin_convex_hull, pin_rows_subset,
+            pin_causal_offset_torch, pin_causal_offset_shift]

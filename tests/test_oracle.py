@@ -41,6 +41,12 @@ MUTANTS = [
     ("lse drops the max", "(m + np.log(denom))", "(0 * m + np.log(denom))"),
     ("missing normalisation", "(e @ vv) / denom", "(e @ vv)"),
     ("keys read in reverse", "q[b, hq, ri] @ kk.T", "q[b, hq, ri] @ kk[::-1].T"),
+    ("causal offset ignored", "key_idx[None, :] <= ri[:, None] + causal_offset",
+     "key_idx[None, :] <= ri[:, None]"),
+    ("causal offset with the wrong sign", "key_idx[None, :] <= ri[:, None] + causal_offset",
+     "key_idx[None, :] <= ri[:, None] - causal_offset"),
+    ("empty rows get lse 0", "np.where(empty, -np.inf, (m + np.log(denom)))",
+     "np.where(empty, 0.0, (m + np.log(denom)))"),
 ]
 
 
@@ -84,8 +90,10 @@ BWD_MUTANTS = [
      "dk[b, hk] += scale * (ds.T @ kk[ri % kk.shape[0]])"),
     ("dp against k", "dp = g @ vv.T", "dp = g @ kk.T"),
     ("dk overwritten, not summed over the group", "dk[b, hk] += scale", "dk[b, hk] = scale"),
-    ("causal off by one", "key_idx[None, :] <= ri[:, None], s, -np.inf)\n                m = s.max(axis=1, keepdims=True)\n                e = np.exp(s - m)\n                p = e",
-     "key_idx[None, :] < ri[:, None] + 2, s, -np.inf)\n                m = s.max(axis=1, keepdims=True)\n                e = np.exp(s - m)\n                p = e"),
+    ("causal off by one", "key_idx[None, :] <= ri[:, None] + causal_offset",
+     "key_idx[None, :] < ri[:, None] + 2 + causal_offset"),
+    ("causal offset ignored", "key_idx[None, :] <= ri[:, None] + causal_offset",
+     "key_idx[None, :] <= ri[:, None]"),
 ]
 
 
