@@ -14,7 +14,9 @@
  * post's flattened GQA groups consecutive query heads on one KV head.  J_i is
  * every key, or with `causal` the keys j <= i (top-left alignment, the
  * semantics of PyTorch's scaled_dot_product_attention is_causal, which is the
- * API the post patches; section "Other areas where this could be useful").
+ * API the post patches; section "Other areas where this could be useful"),
+ * or the keys j <= i + Nkv - Nq (bottom-right alignment, an option of the
+ * same API).  An empty J_i gives O = 0 and LSE = -inf.
  *
  * Layout (all tensors): contiguous [batch, heads, seq_len, head_dim], the
  * head dimension fastest -- the layout the ai-manual.ru article's chunked
@@ -44,6 +46,13 @@ extern "C" {
 
 typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
 
+/* Values of the `causal` argument. */
+enum {
+  ATTN_CAUSAL_NONE = 0,         /* every key */
+  ATTN_CAUSAL_TOP_LEFT = 1,     /* keys j <= i */
+  ATTN_CAUSAL_BOTTOM_RIGHT = 2  /* keys j <= i + Nkv - Nq */
+};
+
 enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,       /* bad argument (shape, pointer, alignment, dtype, scale) */
@@ -66,7 +75,13 @@ enum {
  *           with zero padding inside the kernel).
  * scale   : finite softmax scale (PyTorch's default is 1/sqrt(D); the
  *           ai-manual.ru snippet divides scores by sqrt(dim)).
- * causal  : 0 = every key, 1 = keys j <= i (top-left).
+ * causal  : ATTN_CAUSAL_NONE (0) = every key, ATTN_CAUSAL_TOP_LEFT (1) =
+ *           keys j <= i (PyTorch's is_causal), ATTN_CAUSAL_BOTTOM_RIGHT (2) =
+ *           keys j <= i + Nkv - Nq (PyTorch's causal_lower_right bias: the
+ *           last query row sees every key, as when new queries follow a
+ *           cache of earlier keys).  With Nq > Nkv the first Nq - Nkv rows
+ *           of a bottom-right call see no key: their output is 0 and their
+ *           LSE -inf.
  * dtype   : ATTN_F16 or ATTN_BF16.
  * stream  : hipStream_t to launch on.
  *

@@ -19,6 +19,10 @@ _LIB_NAME = "libattn.so"
 ATTN_F16 = 0
 ATTN_BF16 = 1
 
+ATTN_CAUSAL_NONE = 0
+ATTN_CAUSAL_TOP_LEFT = 1
+ATTN_CAUSAL_BOTTOM_RIGHT = 2
+
 ATTN_OK = 0
 ATTN_EINVAL = -1
 ATTN_EUNSUPPORTED = -2
@@ -106,6 +110,20 @@ def _raise(code: int):
     raise AttnError(code, msg)
 
 
+def causal_code(causal) -> int:
+    """The C ABI's causal mode: False/None -> none, True or "top_left" ->
+    keys j <= i, "bottom_right" -> keys j <= i + Nkv - Nq; ints pass through."""
+    if causal is None or causal is False:
+        return ATTN_CAUSAL_NONE
+    if causal is True or causal == "top_left":
+        return ATTN_CAUSAL_TOP_LEFT
+    if causal == "bottom_right":
+        return ATTN_CAUSAL_BOTTOM_RIGHT
+    if isinstance(causal, int):
+        return causal
+    raise ValueError(f"causal must be a bool, 'top_left' or 'bottom_right', got {causal!r}")
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.float16:
@@ -120,14 +138,14 @@ def attn_fwd_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, Hq, Hkv, Nq, Nkv,
     """Host-only argument validation (no HIP call); returns the error code."""
     return load_library().attn_fwd_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr,
                                          B, Hq, Hkv, Nq, Nkv, D, scale,
-                                         int(causal), dtype_code)
+                                         causal_code(causal), dtype_code)
 
 
 def attn_fwd_num_splits(B, Hq, Hkv, Nq, Nkv, D, causal, dtype_code,
                         num_cus=256) -> int:
     """The split-KV count the library picks for this shape (host-only)."""
     return load_library().attn_fwd_num_splits(B, Hq, Hkv, Nq, Nkv, D,
-                                              int(causal), dtype_code, num_cus)
+                                              causal_code(causal), dtype_code, num_cus)
 
 
 def attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype_code, num_splits=0,
@@ -135,7 +153,7 @@ def attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype_code, num_splits=0,
     """How the library covers this shape: rows per tile, split count, the
     rows merged from split pieces and the workspace bytes (host-only)."""
     plan = AttnPlan()
-    rc = load_library().attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, int(causal),
+    rc = load_library().attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, causal_code(causal),
                                       dtype_code, num_splits, num_cus,
                                       ctypes.byref(plan))
     if rc != ATTN_OK:
@@ -155,9 +173,12 @@ def strides3(t):
     return (ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2))
 
 
-def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
+def attn_fwd(q, k, v, causal=False, scale: float | None = None,
              out=None, lse=None, return_lse: bool = True, num_splits: int = 0):
-    """O = softmax(scale * Q K^T [causal top-left mask]) V on the GPU.
+    """O = softmax(scale * Q K^T [causal mask]) V on the GPU.
+
+    ``causal``: False, True (= "top_left", keys j <= i) or "bottom_right"
+    (keys j <= i + Nkv - Nq; rows that see no key give 0 and LSE -inf).
 
     q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; same dtype (float16 or
     bfloat16), on one HIP device, any strides with the last dimension
@@ -205,7 +226,7 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None,
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = lib.attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
-                                  qs, ks, vs, os_, float(scale), int(bool(causal)), dt,
+                                  qs, ks, vs, os_, float(scale), causal_code(causal), dt,
                                   int(num_splits), stream)
     if rc != ATTN_OK:
         _raise(rc)
@@ -217,10 +238,10 @@ def attn_bwd_check(q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr, dk_p
     """Host-only validation of attn_bwd's arguments; returns the error code."""
     return load_library().attn_bwd_check(q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr,
                                          dq_ptr, dk_ptr, dv_ptr, B, Hq, Hkv, Nq, Nkv, D,
-                                         scale, int(causal), dtype_code)
+                                         scale, causal_code(causal), dtype_code)
 
 
-def attn_bwd(q, k, v, out, lse, dout, causal: bool = False, scale: float | None = None,
+def attn_bwd(q, k, v, out, lse, dout, causal=False, scale: float | None = None,
              dq=None, dk=None, dv=None):
     """(dq, dk, dv): gradients of attn_fwd's output with respect to q, k, v.
 
@@ -271,7 +292,7 @@ def attn_bwd(q, k, v, out, lse, dout, causal: bool = False, scale: float | None 
         rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                           dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, float(scale),
-                          int(bool(causal)), dt, stream)
+                          causal_code(causal), dt, stream)
     if rc != ATTN_OK:
         _raise(rc)
     return dq, dk, dv

@@ -55,6 +55,7 @@ struct BwdParams {
   float* dvp;
   int B, Hq, Hkv, Nq, Nkv, G;
   int hsplit;           // workgroups sharing the query heads of one KV head
+  int coff;             // causal: row i sees keys j <= i + coff
   int n_tiles;          // per head: query tiles (dQ) or key blocks (dK/dV)
   int total;            // workgroups of the launch
   float cs;             // scale * log2(e) (signed)
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   copy_offsets<D, IPW, false>(wave, lane, toff);
 
   const int nqt = (p.Nq + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? min(nqt, k0 / BQ) : 0;
+  const int qt0 = CAUSAL ? min(nqt, max(0, k0 - p.coff) / BQ) : 0;
   const int per_head = nqt - qt0;
   const int steps = hpw * per_head;
 
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
-          if (MSK && key > q0 + r + e) pv = 0.f;
+          if (MSK && key > q0 + r + e + p.coff) pv = 0.f;
           s[qb][4 * j + e] = pv;
         }
       }
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     }
     u32x4 bop[NKC];
     if (pw) {
-      if (CAUSAL && kw0 + 31 > q0)
+      if (CAUSAL && kw0 + 31 > q0 + p.coff)
         probs(std::true_type{}, bufc, s, q0);
       else
         probs(std::false_type{}, bufc, s, q0);
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   const int q0 = qt * BM;
   const int qw0 = q0 + wave * 32;         // the wave's first query row
   const int qrow = qw0 + l32;             // this lane's query (accumulator column)
-  const int kend = CAUSAL ? min(p.Nkv, q0 + BM) : p.Nkv;
+  const int kend = CAUSAL ? max(0, min(p.Nkv, q0 + BM + p.coff)) : p.Nkv;
   const int ntiles = (kend + BN - 1) / BN;
 
   const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float pv = fast_exp2(fmaf(p.cs, s[e], nl2));
-      if (MSK && t * BN + 8 * (e >> 2) + 4 * hl + (e & 3) > qrow) pv = 0.f;
+      if (MSK && t * BN + 8 * (e >> 2) + 4 * hl + (e & 3) > qrow + p.coff) pv = 0.f;
       dp[e] = pv * (dp[e] - dl);
     }
   };
@@ -506,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
       s = N::mfma(read_rows<D>(kr[buf], l32, kc, hl), qf[kc], s);
       dp = N::mfma(read_rows<D>(vr[buf], l32, kc, hl), gf[kc], dp);
     }
-    if (CAUSAL && t * BN + 31 > qw0)
+    if (CAUSAL && t * BN + 31 > qw0 + p.coff)
       probs(std::true_type{}, s, dp, t);
     else
       probs(std::false_type{}, s, dp, t);
@@ -545,7 +546,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (Hq % Hkv != 0) return ATTN_EINVAL;
   if (D != 64 && D != 128) return ATTN_EINVAL;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
-  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
   if (!isfinite(scale)) return ATTN_EINVAL;
   const void* ins[6] = {q, k, v, o, dout, lse};
   const void* outs[3] = {dq, dk, dv};
@@ -675,6 +676,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   p.G = G;
   p.n_tiles = 0;
   p.total = 0;
+  p.coff = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0;
   p.cs = scale * kLog2e;
   p.scale = scale;
   const bool cz = causal != 0;

@@ -72,6 +72,7 @@ struct Params {
   int row0, prows;    // split: output rows [row0, row0 + prows) have partials
   float c;            // |scale| * log2(e)
   uint32_t qsign;     // 0x80008000 flips the sign of Q (negative scale)
+  int coff;           // causal: row i sees keys j <= i + coff (0 top-left, Nkv - Nq bottom-right)
   // Element strides of the batch, head and sequence dimensions (the head
   // dimension is contiguous); row strides fit in 32 bits.
   int64_t qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   // A split launch covers one key range per piece; otherwise every key.
   const int kbeg = SPLIT ? sp * p.split_len : 0;
   int kend = SPLIT ? min(p.Nkv, kbeg + p.split_len) : p.Nkv;
-  if (CAUSAL) kend = min(kend, q0 + BM);  // keys past the tile's last row are all masked
+  if (CAUSAL) kend = max(0, min(kend, q0 + BM + p.coff));  // keys past the last row's are masked
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
   const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;  // LSE / partial row of query 0
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   // Only tiles that straddle the end of the key range or the diagonal.
   auto mask = [&](int t, f32x16* s) {
     const int k0 = kbeg + t * BN;
-    const bool need = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0);
+    const bool need = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0 + p.coff);
     if (need) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-            const bool ok = key < kend && (!CAUSAL || key <= qrow);
+            const bool ok = key < kend && (!CAUSAL || key <= qrow + p.coff);
             if (!ok) s[qb * NKB + kb][e] = -INFINITY;
           }
       }
@@ -729,7 +730,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
   if (Hq % Hkv != 0) return ATTN_EINVAL;
   if (!head_dim_ok(D)) return ATTN_EINVAL;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
-  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
   if (!isfinite(scale)) return ATTN_EINVAL;
   if (!q || !k || !v || !out) return ATTN_EINVAL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return ATTN_EINVAL;
@@ -945,6 +946,7 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   // times FLT_MIN rounds to a base-2 exponent of 0, as it should.
   p.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  p.coff = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0;
 
   void* ws = nullptr;
   if (split_wgs > 0) {
@@ -1094,7 +1096,7 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int caus
                         int num_cus) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
   if (!head_dim_ok(D) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
-  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
   return make_plan(B, Hq, Nq, Nkv, D, causal, 0, num_cus).splits;
 }
 
@@ -1102,7 +1104,8 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, in
                   int num_splits, int num_cus, attn_plan* plan) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
   if (!head_dim_ok(D) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
-  if ((causal != 0 && causal != 1) || num_splits < 0 || !plan) return ATTN_EINVAL;
+  if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT || num_splits < 0 || !plan)
+    return ATTN_EINVAL;
   if ((long long)B * Hq * Nq > INT32_MAX || (long long)B * Hkv * Nkv > INT32_MAX)
     return ATTN_EINVAL;
   const Plan pl = make_plan(B, Hq, Nq, Nkv, D, causal, num_splits, num_cus);

@@ -5,9 +5,12 @@ release") ships its method as a replacement for PyTorch's SDPA call: calls
 it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
 
 * ``sdpa(query, key, value, ...)`` has SDPA's signature and semantics for
-  what this library computes (head dim 64, 80, 96, 128 or 256; no mask, no
-  dropout, top-left causal, GQA via ``enable_gqa``, default scale
-  1/sqrt(E)) and raises ``NotImplementedError`` for anything else; inputs may be strided views such as [B, N, H, E]
+  what this library computes (head dim 64, 80, 96, 128 or 256; no dropout;
+  top-left causal through ``is_causal``; PyTorch's causal biases
+  ``causal_upper_left`` / ``causal_lower_right`` as ``attn_mask`` (the
+  latter is bottom-right alignment, rows that see no key give 0); GQA via
+  ``enable_gqa``, default scale 1/sqrt(E)) and raises ``NotImplementedError``
+  for anything else (other masks included); inputs may be strided views such as [B, N, H, E]
   storage transposed to [B, H, N, E] (no copy is made).
 * ``patch()`` installs it as ``torch.nn.functional.scaled_dot_product_attention``.
   Calls it cannot serve are handed to the original PyTorch function only
@@ -33,6 +36,26 @@ _fallback = False
 _counts = {"native": 0, "fallback": 0}
 
 
+def _causal_bias_mode(attn_mask):
+    """"top_left" / "bottom_right" for PyTorch's causal bias objects, else None."""
+    try:
+        from torch.nn.attention.bias import CausalBias, CausalVariant
+    except ImportError:
+        return None
+    if not isinstance(attn_mask, CausalBias):
+        return None
+    return ("bottom_right" if attn_mask.variant == CausalVariant.LOWER_RIGHT
+            else "top_left")
+
+
+def causal_mode(attn_mask, is_causal):
+    """The library's causal mode for an SDPA call it serves."""
+    mode = _causal_bias_mode(attn_mask)
+    if mode is not None:
+        return mode
+    return "top_left" if is_causal else False
+
+
 def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
                        is_causal=False, scale=None, enable_gqa=False):
     """Why this library cannot serve an SDPA call, or None if it can."""
@@ -41,7 +64,12 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
     if not all(isinstance(t, torch.Tensor) for t in ts):
         return "query, key and value must be tensors"
     if attn_mask is not None:
-        return "attn_mask is not supported"
+        if _causal_bias_mode(attn_mask) is None:
+            return "attn_mask is not supported (only PyTorch's causal biases)"
+        if is_causal:
+            return "is_causal together with a causal bias"
+        if (attn_mask.seq_len_q, attn_mask.seq_len_kv) != (query.shape[-2], key.shape[-2]):
+            return "the causal bias's lengths differ from the inputs'"
     if dropout_p != 0.0:
         return "dropout is not supported"
     if not (query.dim() == key.dim() == value.dim()) or query.dim() not in (3, 4):
@@ -95,11 +123,11 @@ def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,
     squeeze = query.dim() == 3
     q, k, v = ((t.unsqueeze(0) for t in (query, key, value)) if squeeze
                else (query, key, value))
+    mode = causal_mode(attn_mask, is_causal)
     if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
-        out = _attention_fn().apply(q, k, v, bool(is_causal), scale)
+        out = _attention_fn().apply(q, k, v, mode, scale)
     else:
-        out = binding.attn_fwd(q, k, v, causal=bool(is_causal), scale=scale,
-                               return_lse=False)
+        out = binding.attn_fwd(q, k, v, causal=mode, scale=scale, return_lse=False)
     return out.squeeze(0) if squeeze else out
 
 
@@ -140,7 +168,7 @@ def _patched(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,
                                 is_causal, scale, enable_gqa)
     if reason is None:
         _counts["native"] += 1
-        return sdpa(query, key, value, None, 0.0, is_causal, scale, enable_gqa)
+        return sdpa(query, key, value, attn_mask, 0.0, is_causal, scale, enable_gqa)
     if not _fallback:
         raise NotImplementedError(f"memory_efficient_tiled_amd.sdpa: {reason}")
     _counts["fallback"] += 1

@@ -48,7 +48,7 @@ class Result:
     n: int
 
 
-def oracle_rows(x: inputs.Inputs, scale, causal, rows=None):
+def oracle_rows(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
     """Oracle output for all rows, or for rows [Hq, R], one head at a time."""
     B, Hq, Nq, D = x.q.shape
     Hkv = x.k.shape[1]
@@ -65,7 +65,8 @@ def oracle_rows(x: inputs.Inputs, scale, causal, rows=None):
                 h = hk * G + g
                 qh = oracle.decode(x.q[b:b + 1, h:h + 1], x.dtype)
                 r = None if rows is None else rows[h]
-                oh, lh = oracle.attention(qh, kh, vh, sc, causal, rows=r)
+                oh, lh = oracle.attention(qh, kh, vh, sc, causal, rows=r,
+                                          causal_offset=causal_offset)
                 o[b, h] = oh[0, 0]
                 lse[b, h] = lh[0, 0]
     return o, lse
@@ -73,6 +74,7 @@ def oracle_rows(x: inputs.Inputs, scale, causal, rows=None):
 
 def run_gpu(x: inputs.Inputs, scale, causal, device, num_splits=0,
             return_lse=True):
+    """``causal``: False, True / "top_left" or "bottom_right"."""
     import torch
     q = to_device(x.q, x.dtype, device)
     k = to_device(x.k, x.dtype, device)
@@ -106,8 +108,10 @@ def compare(o_gpu, l_gpu, o_ref, l_ref, dtype, rounding_allowance=False,
         mbound = mean_err + float(hu.mean())
     r = Result(float(err.max()), float(err.mean()), 0.0, err.size)
     if l_gpu is not None:
-        assert np.all(np.isfinite(l_gpu)), f"{what}: non-finite lse"
-        r.lse_err = float(np.abs(l_gpu - l_ref).max())
+        empty = np.isneginf(l_ref)      # rows that see no key (bottom-right causal)
+        assert np.all(np.isneginf(l_gpu[empty])), f"{what}: lse of key-less rows not -inf"
+        assert np.all(np.isfinite(l_gpu[~empty])), f"{what}: non-finite lse"
+        r.lse_err = float(np.abs(l_gpu[~empty] - l_ref[~empty]).max()) if (~empty).any() else 0.0
     log(f"  {what}: max|err| {r.max_err:.3e} mean|err| {r.mean_err:.3e} "
         f"lse {r.lse_err:.3e} over {r.n} values")
     worst = np.unravel_index(np.argmax(err - bound), err.shape)

@@ -72,7 +72,7 @@ def check_grad(name, got, ref, dtype, what, zero_from=None, extra=0.0):
     assert err.mean() <= mbound, f"{what} {name}: mean err {err.mean():.3e} > {mbound:.3e}"
 
 
-def delta_terms(x, do, ref, causal):
+def delta_terms(x, do, ref, causal, causal_offset=0):
     """Per-row Delta terms of the bound for (dq, dk, dv) (see the header)."""
     dtype = x.dtype
     q, k, v, g = (_decode(a, dtype) for a in (x.q, x.k, x.v, do))
@@ -81,17 +81,19 @@ def delta_terms(x, do, ref, causal):
     G = Hq // Hkv
     sc = oracle.scale_value(None, D)
     u = U[dtype]
-    o, _ = oracle.attention(q, k, v, sc, causal)
-    pk, _ = oracle.attention(q, k, k, sc, causal)                      # sum_j P_ij K_j
+    o, _ = oracle.attention(q, k, v, sc, causal, causal_offset=causal_offset)
+    pk, _ = oracle.attention(q, k, k, sc, causal, causal_offset=causal_offset)  # sum_j P_ij K_j
     b = np.sqrt(np.sum((g * o) ** 2, axis=-1, keepdims=True))        # [B,Hq,Nq,1]
     t_dq = 12.0 * sc * u * b * np.abs(pk)
     bg = b[..., 0].reshape(B, Hkv, G, Nq).max(axis=2)                 # [B,Hkv,Nq]
     Nkv = k.shape[2]
-    if causal:   # rows i >= j see key j
+    if causal:   # rows i >= j - offset see key j
         suffix = np.maximum.accumulate(bg[:, :, ::-1], axis=-1)[:, :, ::-1]
         bmax = np.zeros((B, Hkv, Nkv))
-        n = min(Nq, Nkv)
-        bmax[:, :, :n] = suffix[:, :, :n]
+        for j in range(Nkv):
+            i0 = max(0, j - causal_offset)
+            if i0 < Nq:
+                bmax[:, :, j] = suffix[:, :, i0]
         bmax = bmax[..., None]
     else:
         bmax = bg.max(axis=-1)[:, :, None, None]
@@ -102,6 +104,7 @@ def delta_terms(x, do, ref, causal):
 
 
 def run_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed):
+    """``causal``: False, True (top-left) or "bottom_right"."""
     import torch
     what = (f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} "
             f"causal={causal} seed={seed}")
@@ -113,10 +116,15 @@ def run_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed):
     dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, g, causal=causal)
     torch.cuda.synchronize(device)
     sc = oracle.scale_value(None, D)
+    off = Nkv - Nq if causal == "bottom_right" else 0
     ref = oracle.attention_backward(_decode(x.q, dtype), _decode(x.k, dtype),
-                                    _decode(x.v, dtype), _decode(do, dtype), sc, causal)
-    unseen = Nq if causal and Nkv > Nq else None
-    terms = delta_terms(x, do, ref, causal)
+                                    _decode(x.v, dtype), _decode(do, dtype), sc, bool(causal),
+                                    causal_offset=off)
+    # keys no query may see: past the last row's reach
+    unseen = Nq + off if causal and Nkv > Nq + off else None
+    terms = delta_terms(x, do, ref, bool(causal), off)
+    if off < 0:   # rows that see no key
+        assert torch.all(dq[:, :, :-off] == 0), "dq of rows without keys must be 0"
     for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, terms):
         check_grad(name, _host(got), r, dtype, what, None if name == "dq" else unseen, t)
 
@@ -140,6 +148,13 @@ def test_more_keys_than_queries_causal(gpu_device):
 
 def test_more_queries_than_keys(gpu_device):
     run_case(gpu_device, 1, 4, 4, 700, 90, 128, inputs.F16, True, seed=44)
+
+
+@pytest.mark.parametrize("nq,nkv", [(100, 700), (500, 130)])
+def test_bottom_right(gpu_device, nq, nkv):
+    # queries after a cache of keys; more queries than keys (the first rows
+    # see no key and get zero gradients)
+    run_case(gpu_device, 1, 4, 2, nq, nkv, 128, inputs.BF16, "bottom_right", seed=nq)
 
 
 @pytest.mark.parametrize("n", [1, 7, 64, 129])

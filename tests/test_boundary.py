@@ -65,12 +65,13 @@ def test_valid_arguments_pass():
     assert check(D=256) == OK             # head dims 64, 96, 128 and 256
     assert check(D=96) == OK
     assert check(D=80) == OK
+    assert check(causal=2) == OK          # bottom-right causal alignment
 
 
 @pytest.mark.parametrize("kw", [
     dict(B=0), dict(Hq=0), dict(Hkv=0), dict(Nq=0), dict(Nkv=-5),
     dict(Hq=6, Hkv=4),                     # Hq not a multiple of Hkv
-    dict(D=72), dict(D=32), dict(D=512), dict(dtype=2), dict(causal=2),
+    dict(D=72), dict(D=32), dict(D=512), dict(dtype=2), dict(causal=3), dict(causal=-1),
     dict(scale=float("inf")), dict(scale=float("nan")),
     dict(q=None), dict(k=None), dict(v=None), dict(out=None),
     dict(q=Q + 8), dict(out=O + 2), dict(lse=L + 2),       # misaligned

@@ -66,6 +66,30 @@ def test_unsupported_inputs():
     assert "scale" in reason(q, q, q, scale=float("inf"))
 
 
+def test_causal_biases_are_served():
+    from torch.nn.attention.bias import causal_lower_right, causal_upper_left
+    q, k = t(1, 2, 10, 64), t(1, 2, 30, 64)
+    assert reason(q, k, k, attn_mask=causal_lower_right(10, 30)) == \
+        "inputs must be on one HIP device"
+    assert reason(q, k, k, attn_mask=causal_upper_left(10, 30)) == \
+        "inputs must be on one HIP device"
+    assert "lengths" in reason(q, k, k, attn_mask=causal_lower_right(10, 31))
+    assert "is_causal" in reason(q, k, k, attn_mask=causal_lower_right(10, 30),
+                                 is_causal=True)
+    assert frontend.causal_mode(causal_lower_right(10, 30), False) == "bottom_right"
+    assert frontend.causal_mode(causal_upper_left(10, 30), False) == "top_left"
+    assert frontend.causal_mode(None, True) == "top_left"
+    assert frontend.causal_mode(None, False) is False
+
+
+def test_causal_codes():
+    assert binding.causal_code(False) == 0 and binding.causal_code(True) == 1
+    assert binding.causal_code("top_left") == 1
+    assert binding.causal_code("bottom_right") == 2
+    with pytest.raises(ValueError):
+        binding.causal_code("diagonal")
+
+
 def test_sdpa_raises_for_unsupported_calls():
     q = t(1, 2, 10, 64)
     with pytest.raises(NotImplementedError):

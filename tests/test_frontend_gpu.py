@@ -136,3 +136,30 @@ def test_patched_torch_sdpa(gpu_device):
         assert mta.sdpa_stats()["fallback"] == s1["fallback"] + 1
     finally:
         mta.unpatch()
+
+
+def test_sdpa_causal_lower_right_bias(gpu_device):
+    """PyTorch's lower-right causal bias as attn_mask: bottom-right alignment
+    in the forward and under autograd."""
+    import torch
+    from torch.nn.attention.bias import causal_lower_right
+    import oracle
+    import memory_efficient_tiled_amd as mta
+    from tests.test_backward_gpu import check_grad, delta_terms
+    x = inputs.make_inputs(1, 4, 2, 96, 400, 64, inputs.BF16, seed=29)
+    do = inputs.make_dout(x)
+    leaves = [to_device(a, inputs.BF16, gpu_device).requires_grad_(True)
+              for a in (x.q, x.k, x.v)]
+    o = mta.sdpa(*leaves, attn_mask=causal_lower_right(96, 400), enable_gqa=True)
+    o.backward(to_device(do, inputs.BF16, gpu_device))
+    torch.cuda.synchronize(gpu_device)
+    o_ref, _ = oracle_rows(x, None, True, causal_offset=304)
+    compare(o.detach().float().cpu().numpy().astype(np.float64), None, o_ref, None,
+            inputs.BF16, rounding_allowance=True, what="sdpa lower-right")
+    dec = [oracle.decode(a, inputs.BF16) for a in (x.q, x.k, x.v, do)]
+    ref = oracle.attention_backward(*dec, oracle.scale_value(None, 64), True,
+                                    causal_offset=304)
+    terms = delta_terms(x, do, ref, True, 304)
+    for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
+        check_grad(name, leaf.grad.float().cpu().numpy().astype(np.float64), r,
+                   inputs.BF16, "sdpa lower-right autograd", None, t)

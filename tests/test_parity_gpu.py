@@ -238,6 +238,39 @@ def test_d80_strided(gpu_device):
             rounding_allowance=True, what="D=80 strided")
 
 
+# -- bottom-right causal alignment (keys j <= i + Nkv - Nq) ------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("nq,nkv", [(100, 1000), (1, 777), (513, 600), (700, 90), (64, 64)])
+def test_bottom_right(gpu_device, nq, nkv, D):
+    """Queries after a cache of keys (Nq < Nkv) and more queries than keys
+    (the first Nq - Nkv rows see no key: 0 and LSE -inf)."""
+    x = inputs.make_inputs(1, 6, 2, nq, nkv, D, inputs.BF16, seed=nq + 3 * nkv)
+    o, l = run_gpu(x, None, "bottom_right", gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, True, causal_offset=nkv - nq)
+    compare(o, l, o_ref, l_ref, inputs.BF16, rounding_allowance=True,
+            what=f"bottom-right {nq}x{nkv} D={D}")
+    if nq > nkv:
+        assert np.all(o[:, :, :nq - nkv] == 0.0)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_bottom_right_forced_splits(gpu_device, splits):
+    x = inputs.make_inputs(1, 4, 4, 300, 2000, 64, inputs.F16, seed=90 + splits)
+    o, l = run_gpu(x, None, "bottom_right", gpu_device, num_splits=splits)
+    o_ref, l_ref = oracle_rows(x, None, True, causal_offset=1700)
+    compare(o, l, o_ref, l_ref, inputs.F16, rounding_allowance=True,
+            what=f"bottom-right splits={splits}")
+
+
+def test_bottom_right_d256_long_rows(gpu_device):
+    x = inputs.make_inputs(1, 8, 4, 1000, 3000, 256, inputs.BF16, seed=93, sampled_rows=24)
+    o, l = run_gpu(x, None, "bottom_right", gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, True, rows=x.rows, causal_offset=2000)
+    compare(gather_rows(o, x.rows), gather_rows(l, x.rows), o_ref, l_ref, inputs.BF16,
+            rounding_allowance=True, what="bottom-right D=256")
+
+
 # -- split of the last partial round ---------------------------------------
 # Grids that fill the device but end in a partial round of workgroups cut
 # only that round's tiles over their key range (first split tile inside a
