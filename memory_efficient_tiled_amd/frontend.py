@@ -16,10 +16,15 @@ it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
   Calls it cannot serve are handed to the original PyTorch function only
   with ``fallback=True`` (the default raises); ``unpatch()`` restores the
   original; ``stats()`` counts the calls each way.
-* With autograd on and an input that requires grad, ``sdpa`` keeps the
-  forward's log-sum-exp and its backward is the library's gradient kernels
-  (``binding.attn_bwd``), which need contiguous tensors: strided inputs are
-  copied once, in the backward only.
+* ``sdpa`` runs through two torch custom ops (``torch_ops()``):
+  ``memory_efficient_tiled_amd::attention`` (O and the log-sum-exp) and
+  ``memory_efficient_tiled_amd::attention_backward``, registered with fake
+  (shape-only) implementations and autograd, so torch.compile traces the
+  call without a graph break and autograd uses the library's gradient
+  kernels (``binding.attn_bwd``), which need contiguous tensors: strided
+  inputs are copied once, in the backward only.
+* ``available()`` is the backend probe: the library is built and the device
+  is a gfx950; calls on other devices are reported as unsupported.
 
 Only argument checks and marshalling happen here; the computation is the
 HIP library's (``binding.attn_fwd`` / ``binding.attn_bwd``), which raises if
@@ -57,8 +62,13 @@ def causal_mode(attn_mask, is_causal):
 
 
 def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
-                       is_causal=False, scale=None, enable_gqa=False):
-    """Why this library cannot serve an SDPA call, or None if it can."""
+                       is_causal=False, scale=None, enable_gqa=False, tracing=False):
+    """Why this library cannot serve an SDPA call, or None if it can.
+
+    With ``tracing`` (under torch.compile) the checks that need the data
+    pointers or the device's properties are left to the library, which
+    repeats them when the op runs and raises.
+    """
     import torch
     ts = (query, key, value)
     if not all(isinstance(t, torch.Tensor) for t in ts):
@@ -91,8 +101,8 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
         return "query heads must equal key heads, or be a multiple with enable_gqa"
     if any(t.stride(-1) != 1 for t in ts):
         return "the last dimension must be contiguous"
-    if any(s % 8 for t in ts for s in t.stride()[:-1]) or any(
-            t.data_ptr() % 16 for t in ts):
+    if any(s % 8 for t in ts for s in t.stride()[:-1]) or (
+            not tracing and any(t.data_ptr() % 16 for t in ts)):
         return "strides must be multiples of 8 elements and data 16-byte aligned"
     if any(t.stride(-2) < E or t.stride(-2) > (1 << 24) for t in ts):
         return "sequence strides must lie in [E, 2^24]"
@@ -104,7 +114,35 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
     if any(t.device.type != "cuda" for t in ts) or not (
             query.device == key.device == value.device):
         return "inputs must be on one HIP device"
+    if not tracing and not _device_ok(query.device):
+        return "the device is not a gfx950 (MI355X)"
     return None
+
+
+_arch = {}
+
+
+def _device_ok(device) -> bool:
+    import torch
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _arch:
+        name = getattr(torch.cuda.get_device_properties(idx), "gcnArchName", "")
+        _arch[idx] = name.split(":")[0] == "gfx950"
+    return _arch[idx]
+
+
+def available(device=None) -> bool:
+    """True when the HIP library is built and loads and ``device`` (default:
+    the current one) is a gfx950 GPU."""
+    import torch
+    try:
+        binding.load_library()
+    except Exception:
+        return False
+    if not torch.cuda.is_available():
+        return False
+    return _device_ok(torch.device("cuda", device) if isinstance(device, int)
+                      else torch.device(device or "cuda"))
 
 
 def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,
@@ -115,51 +153,79 @@ def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,
     returns a new contiguous tensor of the query's shape.  Raises
     NotImplementedError for calls the library cannot serve.
     """
-    reason = unsupported_reason(query, key, value, attn_mask, dropout_p,
-                                is_causal, scale, enable_gqa)
+    import torch
+    reason = unsupported_reason(query, key, value, attn_mask, dropout_p, is_causal, scale,
+                                enable_gqa, tracing=torch.compiler.is_compiling())
     if reason is not None:
         raise NotImplementedError(f"memory_efficient_tiled_amd.sdpa: {reason}")
-    import torch
     squeeze = query.dim() == 3
     q, k, v = ((t.unsqueeze(0) for t in (query, key, value)) if squeeze
                else (query, key, value))
-    mode = causal_mode(attn_mask, is_causal)
-    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
-        out = _attention_fn().apply(q, k, v, mode, scale)
-    else:
-        out = binding.attn_fwd(q, k, v, causal=mode, scale=scale, return_lse=False)
+    code = binding.causal_code(causal_mode(attn_mask, is_causal))
+    sc = float(scale) if scale is not None else 1.0 / math.sqrt(q.shape[-1])
+    out, _ = torch_ops()[0](q, k, v, code, sc)
     return out.squeeze(0) if squeeze else out
 
 
-_fn = None
+_ops = None
 
 
-def _attention_fn():
-    """torch.autograd.Function over the library's forward and gradients
-    (defined on first use so that importing this module needs no torch)."""
-    global _fn
-    if _fn is not None:
-        return _fn
+def torch_ops():
+    """Register (once) and return the torch custom ops behind ``sdpa``:
+
+    * ``memory_efficient_tiled_amd::attention(q, k, v, causal, scale) -> (out, lse)``
+      (``causal`` the C ABI's code: 0 none, 1 top-left, 2 bottom-right);
+    * ``memory_efficient_tiled_amd::attention_backward(dout, q, k, v, out, lse,
+      causal, scale) -> (dq, dk, dv)``, the first op's autograd formula (the
+      log-sum-exp output is not differentiable).
+
+    Both have fake implementations (output shapes only) for tracing.
+    """
+    global _ops
+    if _ops is not None:
+        return _ops
     import torch
 
-    class _Attention(torch.autograd.Function):
-        @staticmethod
-        def forward(ctx, q, k, v, causal, scale):
-            out, lse = binding.attn_fwd(q, k, v, causal=causal, scale=scale)
-            ctx.save_for_backward(q, k, v, out, lse)
-            ctx.causal, ctx.scale = causal, scale
-            return out
+    @torch.library.custom_op(
+        "memory_efficient_tiled_amd::attention", mutates_args=(),
+        schema="(Tensor q, Tensor k, Tensor v, int causal, float scale) -> (Tensor, Tensor)")
+    def attention(q, k, v, causal, scale):
+        return binding.attn_fwd(q, k, v, causal=causal, scale=scale)
 
-        @staticmethod
-        def backward(ctx, dout):
-            q, k, v, out, lse = ctx.saved_tensors
-            q, k, v, dout = (t.contiguous() for t in (q, k, v, dout))
-            dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, dout, causal=ctx.causal,
-                                          scale=ctx.scale)
-            return dq, dk, dv, None, None
+    @attention.register_fake
+    def _(q, k, v, causal, scale):
+        B, Hq, Nq, D = q.shape
+        return q.new_empty((B, Hq, Nq, D)), q.new_empty((B, Hq, Nq), dtype=torch.float32)
 
-    _fn = _Attention
-    return _fn
+    @torch.library.custom_op(
+        "memory_efficient_tiled_amd::attention_backward", mutates_args=(),
+        schema="(Tensor dout, Tensor q, Tensor k, Tensor v, Tensor out, Tensor lse, "
+               "int causal, float scale) -> (Tensor, Tensor, Tensor)")
+    def attention_backward(dout, q, k, v, out, lse, causal, scale):
+        q, k, v, dout = (t.contiguous() for t in (q, k, v, dout))
+        return binding.attn_bwd(q, k, v, out.contiguous(), lse, dout, causal=causal,
+                                scale=scale)
+
+    @attention_backward.register_fake
+    def _(dout, q, k, v, out, lse, causal, scale):
+        return tuple(torch.empty_like(t, memory_format=torch.contiguous_format)
+                     for t in (q, k, v))
+
+    def setup_context(ctx, inputs, output):
+        q, k, v, causal, scale = inputs
+        out, lse = output
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.mark_non_differentiable(lse)
+        ctx.causal, ctx.scale = causal, scale
+
+    def backward(ctx, dout, _dlse):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv = attention_backward(dout, q, k, v, out, lse, ctx.causal, ctx.scale)
+        return dq, dk, dv, None, None
+
+    attention.register_autograd(backward, setup_context=setup_context)
+    _ops = (attention, attention_backward)
+    return _ops
 
 
 def _patched(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,

@@ -149,3 +149,21 @@ def test_strided_check_accepts_common_layouts():
 ])
 def test_strided_check_rejects(kw):
     assert check(**kw) == EINVAL
+
+
+def test_custom_op_fake_shapes():
+    """The custom ops' fake implementations give the output shapes on meta
+    tensors (what tracing sees); no kernel runs."""
+    mta.torch_ops()
+    q = torch.empty(2, 4, 10, 64, device="meta", dtype=torch.bfloat16)
+    k = torch.empty(2, 2, 30, 64, device="meta", dtype=torch.bfloat16)
+    o, lse = torch.ops.memory_efficient_tiled_amd.attention(q, k, k, 1, 0.125)
+    assert o.shape == q.shape and o.dtype == q.dtype and o.is_contiguous()
+    assert lse.shape == (2, 4, 10) and lse.dtype == torch.float32
+    dq, dk, dv = torch.ops.memory_efficient_tiled_amd.attention_backward(
+        o, q, k, k, o, lse, 2, 0.125)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == k.shape
+
+
+def test_backend_probe_without_gpu():
+    assert mta.available() is False

@@ -163,3 +163,49 @@ def test_sdpa_causal_lower_right_bias(gpu_device):
     for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
         check_grad(name, leaf.grad.float().cpu().numpy().astype(np.float64), r,
                    inputs.BF16, "sdpa lower-right autograd", None, t)
+
+
+def test_custom_ops_opcheck(gpu_device):
+    """torch.library.opcheck: schema, fake implementation and autograd
+    registration of the custom ops against real runs."""
+    import torch
+    import memory_efficient_tiled_amd as mta
+    att, bwd = mta.torch_ops()
+    assert mta.available()
+    x = inputs.make_inputs(1, 4, 2, 130, 200, 64, inputs.BF16, seed=31)
+    q, k, v = (to_device(a, inputs.BF16, gpu_device).requires_grad_(True)
+               for a in (x.q, x.k, x.v))
+    for causal in (0, 1, 2):
+        torch.library.opcheck(att, (q, k, v, causal, 0.125),
+                              test_utils=("test_schema", "test_faketensor",
+                                          "test_autograd_registration"))
+
+
+def test_sdpa_compiles_without_graph_break(gpu_device):
+    """torch.compile(fullgraph=True) traces sdpa through the custom op (the
+    aot_eager backend: no code generation), forward and backward."""
+    import torch
+    import memory_efficient_tiled_amd as mta
+    x = inputs.make_inputs(1, 4, 4, 120, 120, 64, inputs.F16, seed=32)
+    q, k, v = (to_device(a, inputs.F16, gpu_device).requires_grad_(True)
+               for a in (x.q, x.k, x.v))
+    w = torch.linspace(-1.0, 1.0, 64, device=gpu_device)
+
+    def loss_fn(a, b, c):
+        return (mta.sdpa(a, b, c, is_causal=True).float() * w).sum()
+
+    f = torch.compile(loss_fn, fullgraph=True, backend="aot_eager")
+    loss = f(q, k, v)
+    loss.backward()
+    grads = [t.grad.clone() for t in (q, k, v)]
+    for t in (q, k, v):
+        t.grad = None
+    ref = loss_fn(q, k, v)           # eager: the same kernels, so the same bits
+    ref.backward()
+    torch.cuda.synchronize(gpu_device)
+    assert torch.equal(loss, ref)
+    for g, t in zip(grads, (q, k, v)):
+        assert torch.equal(g, t.grad)
+    o_ref, _ = oracle_rows(x, None, True)
+    want = float((o_ref * np.linspace(-1.0, 1.0, 64)).sum())
+    assert abs(float(loss.detach()) - want) <= 2e-3 * o_ref.size ** 0.5
