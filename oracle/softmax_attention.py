@@ -30,6 +30,11 @@ Readings where the pages are silent (listed again in the design notes):
     alignment of PyTorch's causal_lower_right bias, where the last query
     row sees every key).  A row whose J_i is empty (bottom-right with
     Nq > Nkv) has o_i = 0 and lse_i = -inf: the sum over an empty set;
+  * an attention mask follows PyTorch's scaled_dot_product_attention (the
+    API the post patches): a float mask is added to the scaled scores, a
+    boolean mask keeps the keys where it is True; the oracle takes both as
+    an additive ``bias`` (0 / -inf for a boolean mask).  A row whose every
+    allowed key has bias -inf is empty as above;
   * query head hq reads KV head hq // (Hq // Hkv): the post's "flattened GQA"
     groups consecutive query heads on one KV head (section "The DIY
     approach");
@@ -90,12 +95,15 @@ def scale_value(scale: float | None, D: int) -> float:
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
               causal: bool, rows: np.ndarray | None = None,
               row_group: int = 256,
-              causal_offset: int = 0) -> tuple[np.ndarray, np.ndarray]:
+              causal_offset: int = 0,
+              bias: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
     """Exact softmax attention in float64.
 
     q: [B, Hq, Nq, D], k and v: [B, Hkv, Nkv, D], all float64.
     rows: None (all Nq rows) or int array [Hq, R] or [R] of query rows.
     causal_offset: with ``causal``, row i sees keys j <= i + causal_offset.
+    bias: None or float64 broadcastable to [B, Hq, Nq, Nkv], added to the
+    scaled scores (-inf removes a key).
     Returns (o [B, Hq, R, D], lse [B, Hq, R]) in float64, natural log.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -117,6 +125,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     o = np.empty((B, Hq, R, D), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
     key_idx = np.arange(Nkv, dtype=np.int64)
+    if bias is not None:
+        bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, Hq, Nq, Nkv))
     for b in range(B):
         for hq in range(Hq):
             hk = hq // G                      # consecutive query heads share a KV head
@@ -125,6 +135,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
             for r0 in range(0, R, row_group):
                 ri = rows_h[hq, r0:r0 + row_group]
                 s = scale * (q[b, hq, ri] @ kk.T)            # [r, Nkv]
+                if bias is not None:
+                    s = s + bias[b, hq, ri]
                 if causal:
                     s = np.where(key_idx[None, :] <= ri[:, None] + causal_offset, s, -np.inf)
                 m = s.max(axis=1, keepdims=True)

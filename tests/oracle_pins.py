@@ -375,8 +375,62 @@ def pin_causal_offset_shift(attn):
         _close(l1, l2[:, :, 12:], what="offset shift lse")
 
 
+# ---------------------------------------------------------------------------
+# 7. Attention masks (PyTorch SDPA semantics), as an additive bias.
+# ---------------------------------------------------------------------------
+
+def pin_mask_torch(attn):
+    """PyTorch CPU SDPA in float64 with boolean and float masks of several
+    broadcast shapes; rows whose keys are all masked are o = 0, lse = -inf."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(32)
+    B, Hq, Hkv, Nq, Nkv, D = 2, 4, 2, 13, 21, 8
+    q = rng.standard_normal((B, Hq, Nq, D))
+    k = rng.standard_normal((B, Hkv, Nkv, D))
+    v = rng.standard_normal((B, Hkv, Nkv, D))
+    kt, vt = (torch.from_numpy(np.repeat(a, Hq // Hkv, axis=1)) for a in (k, v))
+    keep = rng.random((B, 1, Nq, Nkv)) < 0.6
+    keep[0, 0, 3] = False                               # a row with no key
+    fmask = rng.standard_normal((1, Hq, Nq, Nkv))
+    pad = np.ones((B, 1, 1, Nkv), dtype=bool)
+    pad[1, 0, 0, 15:] = False                           # key padding of batch 1
+    for m in (keep, fmask, pad):
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), kt, vt,
+                                             attn_mask=torch.from_numpy(m), scale=0.4).numpy()
+        bias = np.where(m, 0.0, -np.inf) if m.dtype == bool else m
+        o, lse = attn(q, k, v, 0.4, False, bias=bias)
+        empty = np.isneginf(np.broadcast_to(bias, (B, Hq, Nq, Nkv))).all(axis=-1)
+        _close(o[~empty], ref[~empty], tol=1e-11, what=f"mask {m.dtype} {m.shape} vs torch")
+        assert np.all(o[empty] == 0.0) and np.all(np.isneginf(lse[empty]))
+
+
+def pin_mask_bias_shift(attn):
+    """A bias constant along the keys of a row leaves o unchanged and adds
+    to lse; a bias of log(w_j) weights key j like w_j repeated copies."""
+    rng = _rng(33)
+    q = rng.standard_normal((1, 2, 6, 4))
+    k = rng.standard_normal((1, 2, 9, 4))
+    v = rng.standard_normal((1, 2, 9, 4))
+    c = rng.standard_normal((1, 2, 6, 1))
+    o0, l0 = attn(q, k, v, 0.5, False)
+    o1, l1 = attn(q, k, v, 0.5, False, bias=np.broadcast_to(c, (1, 2, 6, 9)))
+    _close(o1, o0, what="row-constant bias o")
+    _close(l1, l0 + c[..., 0], what="row-constant bias lse")
+    # key 2 given weight 3 equals key 2 appearing three times
+    b = np.zeros((1, 2, 6, 9))
+    b[..., 2] = math.log(3.0)
+    o2, l2 = attn(q, k, v, 0.5, False, bias=b)
+    k3 = np.concatenate([k, k[:, :, 2:3], k[:, :, 2:3]], axis=2)
+    v3 = np.concatenate([v, v[:, :, 2:3], v[:, :, 2:3]], axis=2)
+    o3, l3 = attn(q, k3, v3, 0.5, False)
+    _close(o2, o3, what="log-weight bias o")
+    _close(l2, l3, what="log-weight bias lse")
+
+
 ALL_PINS = [pin_bruteforce, pin_torch_sdpa, pin_golden, pin_q_zero, pin_v_const,
             pin_causal_row0, pin_single_key, pin_dominant_key, pin_key_shift,
             pin_kv_permutation, pin_query_permutation, pin_gqa_repeat,
             pin_linear_in_v, pin_convex_hull, pin_rows_subset,
-            pin_causal_offset_torch, pin_causal_offset_shift]
+            pin_causal_offset_torch, pin_causal_offset_shift, pin_mask_torch,
+            pin_mask_bias_shift]

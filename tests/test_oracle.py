@@ -47,6 +47,9 @@ MUTANTS = [
      "key_idx[None, :] <= ri[:, None] - causal_offset"),
     ("empty rows get lse 0", "np.where(empty, -np.inf, (m + np.log(denom)))",
      "np.where(empty, 0.0, (m + np.log(denom)))"),
+    ("bias ignored", "s = s + bias[b, hq, ri]", "s = s + 0.0"),
+    ("bias before the scale", "s = s + bias[b, hq, ri]", "s = s + scale * bias[b, hq, ri]"),
+    ("bias of the wrong head", "s = s + bias[b, hq, ri]", "s = s + bias[b, hq // G, ri]"),
 ]
 
 
