@@ -46,6 +46,13 @@ extern "C" {
 
 typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
 
+/* Kinds of attention mask (attn_fwd_masked). */
+enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_BOOL = 1, /* bytes: nonzero keeps the key, zero removes it */
+  ATTN_MASK_ADD = 2   /* values of the input dtype added to the scaled scores */
+};
+
 /* Values of the `causal` argument. */
 enum {
   ATTN_CAUSAL_NONE = 0,         /* every key */
@@ -153,6 +160,43 @@ int attn_fwd_strided_check(const void* q, const void* k, const void* v,
                            const long long* v_stride,
                            const long long* o_stride, float scale,
                            int causal, int dtype);
+
+/*
+ * attn_fwd_masked -- attn_fwd_strided with an attention mask, the semantics
+ * of PyTorch's scaled_dot_product_attention attn_mask (the API the post
+ * patches; section "Other areas where this could be useful"): for
+ * ATTN_MASK_BOOL a zero byte removes key j from row i, for ATTN_MASK_ADD the
+ * value (fp16/bf16 per `dtype`) is added to scale * <q_i, k_j> before the
+ * softmax (-inf removes the key).  Rows left with no key give O = 0 and
+ * LSE = -inf.  A causal mode still applies on top of the mask.
+ *
+ * mask        : device pointer, element (b, h, i, j) of the [B,Hq,Nq,Nkv] mask
+ *               at mask + b*s[0] + h*s[1] + i*s[2] + j elements (keys
+ *               contiguous; strides may be 0 to broadcast), 8-byte aligned.
+ * mask_type   : ATTN_MASK_BOOL or ATTN_MASK_ADD (ATTN_MASK_NONE ignores the
+ *               mask and behaves as attn_fwd_strided).
+ * mask_stride : 3 element strides (batch, query head, query row), each a
+ *               non-negative multiple of 4.
+ * The mask must not overlap `out` or `lse`.  Masked calls use the 32-row
+ * query tiles.  Returns as attn_fwd.
+ */
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* out,
+                    float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                    const long long* q_stride, const long long* k_stride,
+                    const long long* v_stride, const long long* o_stride,
+                    const void* mask, int mask_type, const long long* mask_stride,
+                    float scale, int causal, int dtype, int num_splits,
+                    void* stream);
+
+/* attn_fwd_masked_check -- host only: attn_fwd_masked's validation. */
+int attn_fwd_masked_check(const void* q, const void* k, const void* v,
+                          const void* out, const float* lse, int B, int Hq,
+                          int Hkv, int Nq, int Nkv, int D,
+                          const long long* q_stride, const long long* k_stride,
+                          const long long* v_stride, const long long* o_stride,
+                          const void* mask, int mask_type,
+                          const long long* mask_stride, float scale,
+                          int causal, int dtype);
 
 /*
  * attn_plan -- how attn_fwd_split covers a shape (see attn_fwd_plan).

@@ -19,6 +19,10 @@ _LIB_NAME = "libattn.so"
 ATTN_F16 = 0
 ATTN_BF16 = 1
 
+ATTN_MASK_NONE = 0
+ATTN_MASK_BOOL = 1
+ATTN_MASK_ADD = 2
+
 ATTN_CAUSAL_NONE = 0
 ATTN_CAUSAL_TOP_LEFT = 1
 ATTN_CAUSAL_BOTTOM_RIGHT = 2
@@ -83,6 +87,12 @@ def load_library():
     lib.attn_fwd_strided_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
         [_LLP] * 4 + [ctypes.c_float, _INT, _INT]
     lib.attn_fwd_strided_check.restype = _INT
+    lib.attn_fwd_masked.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [_LLP] * 4 + [_VP, _INT, _LLP, ctypes.c_float, _INT, _INT, _INT, _VP]
+    lib.attn_fwd_masked.restype = _INT
+    lib.attn_fwd_masked_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [_LLP] * 4 + [_VP, _INT, _LLP, ctypes.c_float, _INT, _INT]
+    lib.attn_fwd_masked_check.restype = _INT
     lib.attn_fwd_plan.argtypes = shape_args + [_INT, _INT, _INT, _INT,
                                                ctypes.POINTER(AttnPlan)]
     lib.attn_fwd_plan.restype = _INT
@@ -173,12 +183,53 @@ def strides3(t):
     return (ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2))
 
 
+def mask_view(mask, B, Hq, Nq, Nkv, dtype):
+    """(tensor, mask_type, strides) for attn_fwd_masked: ``mask`` (bool, or
+    the inputs' dtype for an additive mask) broadcast to [B, Hq, Nq, Nkv]
+    with zero strides where it broadcasts.  Keys must be contiguous with row
+    strides a multiple of 4 elements; a mask that is not is copied once
+    (its own shape, keys padded to a multiple of 4)."""
+    import torch
+    if mask.dtype == torch.bool:
+        mtype, m = ATTN_MASK_BOOL, mask
+    elif mask.dtype == dtype:
+        mtype, m = ATTN_MASK_ADD, mask
+    else:
+        raise TypeError(f"mask dtype {mask.dtype}: expected bool or {dtype}")
+    if m.dim() > 4:
+        raise ValueError("mask must have at most 4 dimensions")
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    if m.shape[-1] == 1:
+        m = m.expand(*m.shape[:-1], Nkv)
+    for have, want in zip(m.shape, (B, Hq, Nq, Nkv)):
+        if have not in (1, want):
+            raise ValueError(f"mask of shape {tuple(mask.shape)} does not broadcast to "
+                             f"{(B, Hq, Nq, Nkv)}")
+    ok = (m.stride(3) == 1 and all(st % 4 == 0 for st in m.stride()[:3])
+          and m.data_ptr() % 8 == 0)
+    if not ok:
+        pad = (Nkv + 3) // 4 * 4
+        buf = torch.zeros(*m.shape[:3], pad, dtype=m.dtype, device=m.device)
+        buf[..., :Nkv] = m
+        m = buf[..., :Nkv]
+    m = m.expand(B, Hq, Nq, Nkv)
+    if mtype == ATTN_MASK_BOOL:
+        m = m.view(torch.uint8)
+    strides = (ctypes.c_longlong * 3)(m.stride(0), m.stride(1), m.stride(2))
+    return m, mtype, strides
+
+
 def attn_fwd(q, k, v, causal=False, scale: float | None = None,
-             out=None, lse=None, return_lse: bool = True, num_splits: int = 0):
-    """O = softmax(scale * Q K^T [causal mask]) V on the GPU.
+             out=None, lse=None, return_lse: bool = True, num_splits: int = 0,
+             mask=None):
+    """O = softmax(scale * Q K^T [+ mask] [causal mask]) V on the GPU.
 
     ``causal``: False, True (= "top_left", keys j <= i) or "bottom_right"
     (keys j <= i + Nkv - Nq; rows that see no key give 0 and LSE -inf).
+    ``mask``: None, or PyTorch SDPA's attn_mask (bool: True keeps a key;
+    the inputs' dtype: added to the scaled scores), broadcastable to
+    [B, Hq, Nq, Nkv].
 
     q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; same dtype (float16 or
     bfloat16), on one HIP device, any strides with the last dimension
@@ -224,10 +275,19 @@ def attn_fwd(q, k, v, causal=False, scale: float | None = None,
     qs, ks, vs, os_ = strides3(q), strides3(k), strides3(v), strides3(out)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = lib.attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                  out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
-                                  qs, ks, vs, os_, float(scale), causal_code(causal), dt,
-                                  int(num_splits), stream)
+        if mask is None:
+            rc = lib.attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
+                                      qs, ks, vs, os_, float(scale), causal_code(causal), dt,
+                                      int(num_splits), stream)
+        else:
+            if mask.device != q.device:
+                raise ValueError("mask must be on q's device")
+            m, mtype, ms = mask_view(mask, B, Hq, Nq, Nkv, q.dtype)
+            rc = lib.attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
+                                     qs, ks, vs, os_, m.data_ptr(), mtype, ms, float(scale),
+                                     causal_code(causal), dt, int(num_splits), stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (out, lse) if return_lse else out

@@ -62,25 +62,6 @@ struct BwdParams {
   float scale;
 };
 
-template <class Tag>
-__device__ __forceinline__ float lo_f32(uint32_t w);
-template <class Tag>
-__device__ __forceinline__ float hi_f32(uint32_t w);
-template <>
-__device__ __forceinline__ float lo_f32<TagBF16>(uint32_t w) { return __uint_as_float(w << 16); }
-template <>
-__device__ __forceinline__ float hi_f32<TagBF16>(uint32_t w) {
-  return __uint_as_float(w & 0xFFFF0000u);
-}
-template <>
-__device__ __forceinline__ float lo_f32<TagF16>(uint32_t w) {
-  return (float)__builtin_bit_cast(f16x2, w)[0];
-}
-template <>
-__device__ __forceinline__ float hi_f32<TagF16>(uint32_t w) {
-  return (float)__builtin_bit_cast(f16x2, w)[1];
-}
-
 // Delta_r = sum_d dO[r, d] O[r, d] in fp32: D / 8 lanes per row, one 16-byte
 // load of each tensor per lane, a butterfly over the row's lanes.
 template <int D, class Tag>

@@ -58,6 +58,26 @@ struct Num<TagF16> {
   }
 };
 
+// The low / high 16-bit value of a 32-bit word as fp32.
+template <class Tag>
+__device__ __forceinline__ float lo_f32(uint32_t w);
+template <class Tag>
+__device__ __forceinline__ float hi_f32(uint32_t w);
+template <>
+__device__ __forceinline__ float lo_f32<TagBF16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <>
+__device__ __forceinline__ float hi_f32<TagBF16>(uint32_t w) {
+  return __uint_as_float(w & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ float lo_f32<TagF16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+template <>
+__device__ __forceinline__ float hi_f32<TagF16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+
 // Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
 // so that each XCD receives a contiguous range of logical tiles: the query
 // tiles of one head then share that XCD's L2 for their K/V stream.

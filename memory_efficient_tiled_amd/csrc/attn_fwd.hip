@@ -77,6 +77,15 @@ struct Params {
   // dimension is contiguous); row strides fit in 32 bits.
   int64_t qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
   int qsn, ksn, vsn, osn;
+  // Attention mask (MASKED kernels): element strides of batch, query head
+  // and query row (keys contiguous); mask_mode ATTN_MASK_BOOL (bytes,
+  // nonzero keeps the key) or ATTN_MASK_ADD (16-bit values added to the
+  // scaled scores).  Scores are then formed in base-2 units in the mask
+  // step (score * cm + bias * log2 e) and c is 1.
+  const uint8_t* mask;
+  int64_t msb, msh, msq;
+  int mask_mode;
+  float cm;
 };
 
 // One workgroup: NW waves x QB x 32 query rows, all on KV head hq / G,
@@ -114,7 +123,7 @@ struct Params {
 // with the last two 16-byte chunks of every Q, K and V row read as zeros and
 // the matching output columns not stored.
 template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB, bool SPLIT,
-          bool STRIDED>
+          bool STRIDED, bool MASKED>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
   constexpr int DP = compute_dim(D);    // columns of the products and LDS rows
   constexpr int WR = QB * 32;           // query rows per wave
@@ -274,22 +283,67 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     }
   };
 
+  // Four consecutive mask values of one row as base-2 biases (keys from
+  // key0; those past the key range are not read).
+  auto mask_bias4 = [&](const uint8_t* mrow, int key0, float* bias) {
+    if (p.mask_mode == ATTN_MASK_BOOL) {
+      uint32_t w = 0;
+      if (key0 + 3 < p.Nkv) {
+        w = *(const uint32_t*)(mrow + key0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + i < p.Nkv) w |= (uint32_t)mrow[key0 + i] << (8 * i);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias[i] = ((w >> (8 * i)) & 0xffu) ? 0.f : -INFINITY;
+    } else {
+      const uint16_t* m16 = (const uint16_t*)mrow;
+      u32x2 w = {0u, 0u};
+      if (key0 + 3 < p.Nkv) {
+        w = *(const u32x2*)(m16 + key0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + i < p.Nkv) w[i >> 1] |= (uint32_t)m16[key0 + i] << (16 * (i & 1));
+      }
+      bias[0] = lo_f32<Tag>(w[0]) * kLog2e;
+      bias[1] = hi_f32<Tag>(w[0]) * kLog2e;
+      bias[2] = lo_f32<Tag>(w[1]) * kLog2e;
+      bias[3] = hi_f32<Tag>(w[1]) * kLog2e;
+    }
+  };
+
   // Keys past the valid range, and (causal) keys after the row, get -inf.
-  // Only tiles that straddle the end of the key range or the diagonal.
+  // Only tiles that straddle the end of the key range or the diagonal; with
+  // a mask, every tile (scores are scaled and biased here).
   auto mask = [&](int t, f32x16* s) {
     const int k0 = kbeg + t * BN;
-    const bool need = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0 + p.coff);
+    const bool need = MASKED || (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0 + p.coff);
     if (need) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qrow = wq0 + qb * 32 + l32;
+        const uint8_t* mrow = nullptr;
+        if constexpr (MASKED) {
+          const int64_t off = b * p.msb + hq * p.msh + (int64_t)min(qrow, p.Nq - 1) * p.msq;
+          mrow = p.mask + off * (p.mask_mode == ATTN_MASK_BOOL ? 1 : 2);
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-            const bool ok = key < kend && (!CAUSAL || key <= qrow + p.coff);
-            if (!ok) s[qb * NKB + kb][e] = -INFINITY;
+          for (int g = 0; g < 4; ++g) {
+            const int key0 = k0 + kb * 32 + 8 * g + 4 * hl;
+            float bias[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (MASKED) mask_bias4(mrow, key0, bias);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + i;
+              float v = s[qb * NKB + kb][4 * g + i];
+              if constexpr (MASKED) v = fmaf(v, p.cm, bias[i]);
+              const bool ok = key < kend && (!CAUSAL || key <= qrow + p.coff);
+              s[qb * NKB + kb][4 * g + i] = ok ? v : -INFINITY;
+            }
           }
       }
     }
@@ -723,9 +777,16 @@ bool dense_enough(const Strides& s, int B, int H, int N, int D) {
   return true;
 }
 
+// An attention mask: element (b, h, i, j) at ptr + b*sb + h*sh + i*sq + j.
+struct MaskArgs {
+  const void* ptr = nullptr;
+  int type = ATTN_MASK_NONE;
+  int64_t sb = 0, sh = 0, sq = 0;
+};
+
 int validate(const void* q, const void* k, const void* v, const void* out, const float* lse,
              int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
-             int dtype, const Layout& L) {
+             int dtype, const Layout& L, const MaskArgs& M = MaskArgs()) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
   if (!head_dim_ok(D)) return ATTN_EINVAL;
@@ -751,6 +812,17 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
     if (overlaps128(lse, lb, q, qb) || overlaps128(lse, lb, k, kb) ||
         overlaps128(lse, lb, v, vb) || overlaps128(lse, lb, out, ob))
       return ATTN_EINVAL;
+  }
+  if (M.type != ATTN_MASK_NONE) {
+    if (M.type != ATTN_MASK_BOOL && M.type != ATTN_MASK_ADD) return ATTN_EINVAL;
+    if (!M.ptr || ((uintptr_t)M.ptr & 7)) return ATTN_EINVAL;
+    if (M.sb < 0 || M.sh < 0 || M.sq < 0 || ((M.sb | M.sh | M.sq) & 3)) return ATTN_EINVAL;
+    const int esz = M.type == ATTN_MASK_BOOL ? 1 : 2;
+    const __int128 mb = esz * ((__int128)(B - 1) * M.sb + (__int128)(Hq - 1) * M.sh +
+                               (__int128)(Nq - 1) * M.sq + Nkv);
+    if (mb > ((__int128)1 << 62)) return ATTN_EINVAL;
+    if (overlaps128(out, ob, M.ptr, mb)) return ATTN_EINVAL;
+    if (lse && overlaps128(lse, (__int128)rows * 4, M.ptr, mb)) return ATTN_EINVAL;
   }
   return ATTN_OK;
 }
@@ -817,9 +889,10 @@ int causal_splits(long long tiles, long long slots, int ktiles) {
 // tile).  Otherwise, without a mask, the grid runs in rounds of `slots`
 // equal workgroups and only the tiles of the last, partial round are cut,
 // so that they finish in a fraction of a round.
-Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int num_cus) {
+Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int num_cus,
+               bool masked = false) {
   Plan pl;
-  pl.cfg = select_cfg(B, Hq, Nq, D, causal, num_cus);
+  pl.cfg = select_cfg(B, Hq, Nq, D, causal || masked, num_cus);
   pl.D = D;
   const TileCfg c = kCfgs[pl.cfg];
   pl.n_qtiles = (Nq + c.BM() - 1) / c.BM();
@@ -849,33 +922,39 @@ Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits
   return pl;
 }
 
-template <int D, int CFG, class Tag, bool CAUSAL, bool SPLIT>
+// Masked launches always take the strided kernels (the mask has strides
+// of its own) and only the narrow tiles.
+template <int D, int CFG, class Tag, bool CAUSAL, bool SPLIT, bool MASKED>
 hipError_t launch_main(const Params& p, bool strided, hipStream_t stream) {
   constexpr TileCfg c = kCfgs[CFG];
-  if (strided)
+  if (MASKED)
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true>),
+        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, MASKED>),
+        dim3(p.total), dim3(c.NW * 64), 0, stream, p);
+  else if (strided)
+    hipLaunchKernelGGL(
+        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, false>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   else
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, false>),
+        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, false, false>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int CFG, class Tag>
+template <int D, int CFG, class Tag, bool MASKED>
 hipError_t dispatch(const Params& p, bool causal, bool split, bool strided, hipStream_t st) {
   if (causal)
-    return split ? launch_main<D, CFG, Tag, true, true>(p, strided, st)
-                 : launch_main<D, CFG, Tag, true, false>(p, strided, st);
-  return split ? launch_main<D, CFG, Tag, false, true>(p, strided, st)
-               : launch_main<D, CFG, Tag, false, false>(p, strided, st);
+    return split ? launch_main<D, CFG, Tag, true, true, MASKED>(p, strided, st)
+                 : launch_main<D, CFG, Tag, true, false, MASKED>(p, strided, st);
+  return split ? launch_main<D, CFG, Tag, false, true, MASKED>(p, strided, st)
+               : launch_main<D, CFG, Tag, false, false, MASKED>(p, strided, st);
 }
 
 // The wide tiles are only selected without a causal mask.
 template <int D, class Tag>
 hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool strided,
-                      hipStream_t st) {
+                      bool masked, hipStream_t st) {
   constexpr int kNarrow = D == 256 ? kCfgD256
                           : D == 96 || D == 80 ? kCfgD96
                           : D == 128           ? kCfgD128Narrow
@@ -884,10 +963,11 @@ hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool st
                         : D == 96 || D == 80 ? kCfgD96
                         : D == 128           ? kCfgD128Wide
                                              : kCfgD64Wide;
+  if (masked) return dispatch<D, kNarrow, Tag, true>(p, causal, split, true, st);
   if (cfg == kWide && !causal)
-    return split ? launch_main<D, kWide, Tag, false, true>(p, strided, st)
-                 : launch_main<D, kWide, Tag, false, false>(p, strided, st);
-  return dispatch<D, kNarrow, Tag>(p, causal, split, strided, st);
+    return split ? launch_main<D, kWide, Tag, false, true, false>(p, strided, st)
+                 : launch_main<D, kWide, Tag, false, false, false>(p, strided, st);
+  return dispatch<D, kNarrow, Tag, false>(p, causal, split, strided, st);
 }
 
 template <int D, class Tag>
@@ -907,15 +987,16 @@ hipError_t launch_combine(const Params& p, bool strided, hipStream_t st) {
 
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
         int Nq, int Nkv, int D, const Layout& L, float scale, int causal, int dtype,
-        int num_splits, hipStream_t stream) {
-  int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype, L);
+        int num_splits, hipStream_t stream, const MaskArgs& M = MaskArgs()) {
+  int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype, L, M);
+  const bool masked = M.type != ATTN_MASK_NONE;
   if (rc != ATTN_OK) return rc;
   if (num_splits < 0) return ATTN_EINVAL;
   DeviceInfo di;
   rc = device_info(&di);
   if (rc != ATTN_OK) return rc;
 
-  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, causal, num_splits, di.cus);
+  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, causal, num_splits, di.cus, masked);
   const long long split_wgs = (pl.tiles - pl.first_split) * pl.splits;
   if (pl.first_split > INT32_MAX || split_wgs > INT32_MAX) return ATTN_EINVAL;
 
@@ -947,6 +1028,11 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   p.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
   p.coff = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0;
+  p.mask = (const uint8_t*)M.ptr;
+  p.msb = M.sb, p.msh = M.sh, p.msq = M.sq;
+  p.mask_mode = M.type;
+  p.cm = p.c;
+  if (masked) p.c = 1.f;  // the mask step forms base-2 scores
 
   void* ws = nullptr;
   if (split_wgs > 0) {
@@ -966,19 +1052,19 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   const bool strided = !(same(L.q, C.q) && same(L.k, C.k) && same(L.v, C.v) && same(L.o, C.o));
   auto launch = [&](bool split) {
     if (D == 64)
-      return dtype == ATTN_BF16 ? dispatch_d<64, TagBF16>(p, pl.cfg, cz, split, strided, stream)
-                                : dispatch_d<64, TagF16>(p, pl.cfg, cz, split, strided, stream);
+      return dtype == ATTN_BF16 ? dispatch_d<64, TagBF16>(p, pl.cfg, cz, split, strided, masked, stream)
+                                : dispatch_d<64, TagF16>(p, pl.cfg, cz, split, strided, masked, stream);
     if (D == 256)
-      return dtype == ATTN_BF16 ? dispatch_d<256, TagBF16>(p, pl.cfg, cz, split, strided, stream)
-                                : dispatch_d<256, TagF16>(p, pl.cfg, cz, split, strided, stream);
+      return dtype == ATTN_BF16 ? dispatch_d<256, TagBF16>(p, pl.cfg, cz, split, strided, masked, stream)
+                                : dispatch_d<256, TagF16>(p, pl.cfg, cz, split, strided, masked, stream);
     if (D == 96)
-      return dtype == ATTN_BF16 ? dispatch_d<96, TagBF16>(p, pl.cfg, cz, split, strided, stream)
-                                : dispatch_d<96, TagF16>(p, pl.cfg, cz, split, strided, stream);
+      return dtype == ATTN_BF16 ? dispatch_d<96, TagBF16>(p, pl.cfg, cz, split, strided, masked, stream)
+                                : dispatch_d<96, TagF16>(p, pl.cfg, cz, split, strided, masked, stream);
     if (D == 80)
-      return dtype == ATTN_BF16 ? dispatch_d<80, TagBF16>(p, pl.cfg, cz, split, strided, stream)
-                                : dispatch_d<80, TagF16>(p, pl.cfg, cz, split, strided, stream);
-    return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, strided, stream)
-                              : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, strided, stream);
+      return dtype == ATTN_BF16 ? dispatch_d<80, TagBF16>(p, pl.cfg, cz, split, strided, masked, stream)
+                                : dispatch_d<80, TagF16>(p, pl.cfg, cz, split, strided, masked, stream);
+    return dtype == ATTN_BF16 ? dispatch_d<128, TagBF16>(p, pl.cfg, cz, split, strided, masked, stream)
+                              : dispatch_d<128, TagF16>(p, pl.cfg, cz, split, strided, masked, stream);
   };
   hipError_t e = hipSuccess;
   if (pl.first_split > 0) {  // whole tiles
@@ -1090,6 +1176,44 @@ int attn_fwd_strided_check(const void* q, const void* k, const void* v, const vo
                            int causal, int dtype) {
   return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
                   strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride));
+}
+
+static MaskArgs mask_args(const void* mask, int mask_type, const long long* mask_stride) {
+  MaskArgs m;
+  m.ptr = mask;
+  m.type = mask_type;
+  if (mask_type != ATTN_MASK_NONE) {
+    if (!mask_stride) {
+      m.type = -1;  // rejected by validation
+    } else {
+      m.sb = mask_stride[0];
+      m.sh = mask_stride[1];
+      m.sq = mask_stride[2];
+    }
+  }
+  return m;
+}
+
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                    int Hq, int Hkv, int Nq, int Nkv, int D, const long long* q_stride,
+                    const long long* k_stride, const long long* v_stride,
+                    const long long* o_stride, const void* mask, int mask_type,
+                    const long long* mask_stride, float scale, int causal, int dtype,
+                    int num_splits, void* stream) {
+  const Layout L = strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, L, scale, causal, dtype, num_splits,
+             (hipStream_t)stream, mask_args(mask, mask_type, mask_stride));
+}
+
+int attn_fwd_masked_check(const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                          const long long* q_stride, const long long* k_stride,
+                          const long long* v_stride, const long long* o_stride,
+                          const void* mask, int mask_type, const long long* mask_stride,
+                          float scale, int causal, int dtype) {
+  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
+                  strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride),
+                  mask_args(mask, mask_type, mask_stride));
 }
 
 int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,

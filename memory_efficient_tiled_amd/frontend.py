@@ -8,9 +8,10 @@ it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
   what this library computes (head dim 64, 80, 96, 128 or 256; no dropout;
   top-left causal through ``is_causal``; PyTorch's causal biases
   ``causal_upper_left`` / ``causal_lower_right`` as ``attn_mask`` (the
-  latter is bottom-right alignment, rows that see no key give 0); GQA via
-  ``enable_gqa``, default scale 1/sqrt(E)) and raises ``NotImplementedError``
-  for anything else (other masks included); inputs may be strided views such as [B, N, H, E]
+  latter is bottom-right alignment, rows that see no key give 0); boolean
+  or additive ``attn_mask`` tensors broadcastable to [B, H, L, S] (forward
+  only: not under autograd); GQA via ``enable_gqa``, default scale
+  1/sqrt(E)) and raises ``NotImplementedError`` for anything else; inputs may be strided views such as [B, N, H, E]
   storage transposed to [B, H, N, E] (no copy is made).
 * ``patch()`` installs it as ``torch.nn.functional.scaled_dot_product_attention``.
   Calls it cannot serve are handed to the original PyTorch function only
@@ -74,12 +75,26 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
     if not all(isinstance(t, torch.Tensor) for t in ts):
         return "query, key and value must be tensors"
     if attn_mask is not None:
-        if _causal_bias_mode(attn_mask) is None:
-            return "attn_mask is not supported (only PyTorch's causal biases)"
         if is_causal:
-            return "is_causal together with a causal bias"
-        if (attn_mask.seq_len_q, attn_mask.seq_len_kv) != (query.shape[-2], key.shape[-2]):
-            return "the causal bias's lengths differ from the inputs'"
+            return "is_causal together with an attn_mask"
+        if _causal_bias_mode(attn_mask) is not None:
+            if (attn_mask.seq_len_q, attn_mask.seq_len_kv) != (query.shape[-2], key.shape[-2]):
+                return "the causal bias's lengths differ from the inputs'"
+        elif isinstance(attn_mask, torch.Tensor):
+            if attn_mask.dtype != torch.bool and attn_mask.dtype != query.dtype:
+                return "attn_mask must be bool or have the inputs' dtype"
+            if attn_mask.dim() > 4:
+                return "attn_mask must have at most 4 dimensions"
+            full = tuple(query.shape[:-1]) + (key.shape[-2],)
+            for have, want in zip(reversed(attn_mask.shape), reversed(full)):
+                if have not in (1, want):
+                    return "attn_mask does not broadcast to the scores' shape"
+            if attn_mask.device != query.device:
+                return "attn_mask must be on the inputs' device"
+            if torch.is_grad_enabled() and any(t.requires_grad for t in ts):
+                return "gradients with an attention mask are not built"
+        else:
+            return "attn_mask must be a tensor or one of PyTorch's causal biases"
     if dropout_p != 0.0:
         return "dropout is not supported"
     if not (query.dim() == key.dim() == value.dim()) or query.dim() not in (3, 4):
@@ -163,7 +178,10 @@ def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,
                else (query, key, value))
     code = binding.causal_code(causal_mode(attn_mask, is_causal))
     sc = float(scale) if scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    out, _ = torch_ops()[0](q, k, v, code, sc)
+    # PyTorch's causal biases are tensor subclasses: they select a causal mode
+    mask = (attn_mask if isinstance(attn_mask, torch.Tensor)
+            and _causal_bias_mode(attn_mask) is None else None)
+    out, _ = torch_ops()[0](q, k, v, mask, code, sc)
     return out.squeeze(0) if squeeze else out
 
 
@@ -173,8 +191,9 @@ _ops = None
 def torch_ops():
     """Register (once) and return the torch custom ops behind ``sdpa``:
 
-    * ``memory_efficient_tiled_amd::attention(q, k, v, causal, scale) -> (out, lse)``
-      (``causal`` the C ABI's code: 0 none, 1 top-left, 2 bottom-right);
+    * ``memory_efficient_tiled_amd::attention(q, k, v, mask, causal, scale) -> (out, lse)``
+      (``mask`` None or an SDPA attn_mask tensor; ``causal`` the C ABI's
+      code: 0 none, 1 top-left, 2 bottom-right);
     * ``memory_efficient_tiled_amd::attention_backward(dout, q, k, v, out, lse,
       causal, scale) -> (dq, dk, dv)``, the first op's autograd formula (the
       log-sum-exp output is not differentiable).
@@ -188,12 +207,13 @@ def torch_ops():
 
     @torch.library.custom_op(
         "memory_efficient_tiled_amd::attention", mutates_args=(),
-        schema="(Tensor q, Tensor k, Tensor v, int causal, float scale) -> (Tensor, Tensor)")
-    def attention(q, k, v, causal, scale):
-        return binding.attn_fwd(q, k, v, causal=causal, scale=scale)
+        schema="(Tensor q, Tensor k, Tensor v, Tensor? mask, int causal, float scale) "
+               "-> (Tensor, Tensor)")
+    def attention(q, k, v, mask, causal, scale):
+        return binding.attn_fwd(q, k, v, causal=causal, scale=scale, mask=mask)
 
     @attention.register_fake
-    def _(q, k, v, causal, scale):
+    def _(q, k, v, mask, causal, scale):
         B, Hq, Nq, D = q.shape
         return q.new_empty((B, Hq, Nq, D)), q.new_empty((B, Hq, Nq), dtype=torch.float32)
 
@@ -212,16 +232,18 @@ def torch_ops():
                      for t in (q, k, v))
 
     def setup_context(ctx, inputs, output):
-        q, k, v, causal, scale = inputs
+        q, k, v, mask, causal, scale = inputs
         out, lse = output
         ctx.save_for_backward(q, k, v, out, lse)
         ctx.mark_non_differentiable(lse)
-        ctx.causal, ctx.scale = causal, scale
+        ctx.causal, ctx.scale, ctx.masked = causal, scale, mask is not None
 
     def backward(ctx, dout, _dlse):
+        if ctx.masked:
+            raise NotImplementedError("gradients with an attention mask are not built")
         q, k, v, out, lse = ctx.saved_tensors
         dq, dk, dv = attention_backward(dout, q, k, v, out, lse, ctx.causal, ctx.scale)
-        return dq, dk, dv, None, None
+        return dq, dk, dv, None, None, None
 
     attention.register_autograd(backward, setup_context=setup_context)
     _ops = (attention, attention_backward)

@@ -176,3 +176,29 @@ def test_oracle_not_on_product_path():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+
+
+def mcheck(mask=0x60000000, mask_type=1, ms=(0, 0, 64), **kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=2, Hq=8, Hkv=2, Nq=64, Nkv=64, D=128,
+             scale=0.088, causal=0, dtype=BF16)
+    a.update(kw)
+    lib = binding.load_library()
+    null = ctypes.POINTER(ctypes.c_longlong)()
+    st = (ctypes.c_longlong * 3)(*ms) if ms is not None else null
+    return lib.attn_fwd_masked_check(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                     a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["D"],
+                                     null, null, null, null, mask, mask_type, st,
+                                     a["scale"], a["causal"], a["dtype"])
+
+
+def test_masked_validation():
+    assert mcheck() == OK
+    assert mcheck(mask_type=2, ms=(8 * 64 * 64, 64 * 64, 64)) == OK
+    assert mcheck(mask_type=0, mask=None) == OK          # no mask: the strided call
+    assert mcheck(mask=None) == EINVAL
+    assert mcheck(mask=0x60000004) == EINVAL              # not 8-byte aligned
+    assert mcheck(mask_type=3) == EINVAL
+    assert mcheck(ms=(0, 0, 66)) == EINVAL                # row stride not a multiple of 4
+    assert mcheck(ms=(-4, 0, 64)) == EINVAL
+    assert mcheck(ms=None) == EINVAL
+    assert mcheck(mask=O) == EINVAL                       # overlaps the output

@@ -35,7 +35,9 @@ def test_cpu_tensors_only_fail_the_device_check():
 
 
 @pytest.mark.parametrize("kw,frag", [
-    ({"attn_mask": t(100, 100)}, "attn_mask"),
+    ({"attn_mask": t(100, 100, dtype=torch.float32)}, "attn_mask must be bool"),
+    ({"attn_mask": t(3, 100, 100, dtype=torch.bool)}, "broadcast"),
+    ({"attn_mask": t(100, 100, dtype=torch.bool), "is_causal": True}, "is_causal"),
     ({"dropout_p": 0.1}, "dropout"),
 ])
 def test_unsupported_arguments(kw, frag):
@@ -64,6 +66,34 @@ def test_unsupported_inputs():
     g = t(1, 2, 10, 64).requires_grad_()      # differentiable: served (on a device)
     assert reason(g, g, g) == "inputs must be on one HIP device"
     assert "scale" in reason(q, q, q, scale=float("inf"))
+
+
+def test_tensor_masks_are_served():
+    q = t(2, 4, 100, 64)
+    for m in (t(100, 100, dtype=torch.bool), t(2, 1, 100, 100), t(2, 4, 1, 100),
+              t(100, 1, dtype=torch.bool)):
+        assert reason(q, q, q, attn_mask=m) == "inputs must be on one HIP device"
+    g = t(2, 4, 100, 64).requires_grad_()
+    assert "gradients" in reason(g, g, g, attn_mask=t(100, 100, dtype=torch.bool))
+
+
+def test_mask_view_broadcasts_without_copies():
+    """Broadcast dimensions get stride 0; keys stay contiguous; rows that are
+    not a multiple of 4 elements are padded in one copy of the mask's own
+    shape."""
+    m = torch.ones(1, 1, 10, 64, dtype=torch.bool)
+    v, mtype, st = binding.mask_view(m, 2, 3, 10, 64, torch.float16)
+    assert mtype == binding.ATTN_MASK_BOOL and tuple(v.shape) == (2, 3, 10, 64)
+    assert (st[0], st[1], st[2]) == (0, 0, 64) and v.data_ptr() == m.data_ptr()
+    a = torch.randn(3, 10, 30).half()                  # 30 keys: padded to 32
+    v, mtype, st = binding.mask_view(a, 2, 3, 10, 30, torch.float16)
+    assert mtype == binding.ATTN_MASK_ADD and (st[0], st[1], st[2]) == (0, 320, 32)
+    assert torch.equal(v[1], a)
+    kp = torch.tensor([True] * 20 + [False] * 10).reshape(1, 1, 1, 30)  # key padding
+    v, _, st = binding.mask_view(kp, 2, 3, 10, 30, torch.float16)
+    assert (st[0], st[1], st[2]) == (0, 0, 0) and bool(v[1, 2, 7, 19]) and not bool(v[1, 2, 7, 20])
+    with pytest.raises(TypeError):
+        binding.mask_view(a.float(), 2, 3, 10, 30, torch.float16)
 
 
 def test_causal_biases_are_served():
@@ -157,7 +187,7 @@ def test_custom_op_fake_shapes():
     mta.torch_ops()
     q = torch.empty(2, 4, 10, 64, device="meta", dtype=torch.bfloat16)
     k = torch.empty(2, 2, 30, 64, device="meta", dtype=torch.bfloat16)
-    o, lse = torch.ops.memory_efficient_tiled_amd.attention(q, k, k, 1, 0.125)
+    o, lse = torch.ops.memory_efficient_tiled_amd.attention(q, k, k, None, 1, 0.125)
     assert o.shape == q.shape and o.dtype == q.dtype and o.is_contiguous()
     assert lse.shape == (2, 4, 10) and lse.dtype == torch.float32
     dq, dk, dv = torch.ops.memory_efficient_tiled_amd.attention_backward(

@@ -176,9 +176,13 @@ def test_custom_ops_opcheck(gpu_device):
     q, k, v = (to_device(a, inputs.BF16, gpu_device).requires_grad_(True)
                for a in (x.q, x.k, x.v))
     for causal in (0, 1, 2):
-        torch.library.opcheck(att, (q, k, v, causal, 0.125),
+        torch.library.opcheck(att, (q, k, v, None, causal, 0.125),
                               test_utils=("test_schema", "test_faketensor",
                                           "test_autograd_registration"))
+    keep = torch.rand(1, 1, 130, 200, device=gpu_device) < 0.7
+    qd, kd, vd = (t.detach() for t in (q, k, v))
+    torch.library.opcheck(att, (qd, kd, vd, keep, 0, 0.125),
+                          test_utils=("test_schema", "test_faketensor"))
 
 
 def test_sdpa_compiles_without_graph_break(gpu_device):
@@ -209,3 +213,32 @@ def test_sdpa_compiles_without_graph_break(gpu_device):
     o_ref, _ = oracle_rows(x, None, True)
     want = float((o_ref * np.linspace(-1.0, 1.0, 64)).sum())
     assert abs(float(loss.detach()) - want) <= 2e-3 * o_ref.size ** 0.5
+
+
+def test_sdpa_tensor_masks(gpu_device):
+    """Boolean and additive attn_mask tensors through sdpa and the patched
+    PyTorch call (no autograd)."""
+    import torch
+    import torch.nn.functional as F
+    import oracle
+    import memory_efficient_tiled_amd as mta
+    x = inputs.make_inputs(2, 4, 4, 100, 130, 64, inputs.F16, seed=33)
+    q, k, v = (to_device(a, inputs.F16, gpu_device) for a in (x.q, x.k, x.v))
+    rng = np.random.Generator(np.random.PCG64(34))
+    keep = rng.random((2, 1, 100, 130)) < 0.6
+    add = inputs.to_storage(rng.standard_normal((100, 130)).astype(np.float32), inputs.F16)
+    sc = oracle.scale_value(None, 64)
+    dec = [oracle.decode(a, inputs.F16) for a in (x.q, x.k, x.v)]
+    for m, bias in ((torch.from_numpy(keep).to(gpu_device), np.where(keep, 0.0, -np.inf)),
+                    (to_device(add, inputs.F16, gpu_device), oracle.decode(add, inputs.F16))):
+        o = mta.sdpa(q, k, v, attn_mask=m)
+        try:
+            mta.patch()
+            o2 = F.scaled_dot_product_attention(q, k, v, attn_mask=m)
+        finally:
+            mta.unpatch()
+        torch.cuda.synchronize(gpu_device)
+        assert torch.equal(o, o2)
+        o_ref, _ = oracle.attention(*dec, sc, False, bias=np.broadcast_to(bias, (2, 4, 100, 130)))
+        compare(o.float().cpu().numpy().astype(np.float64), None, o_ref, None, inputs.F16,
+                rounding_allowance=True, what=f"sdpa mask {m.dtype}")

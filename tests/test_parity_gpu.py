@@ -271,6 +271,87 @@ def test_bottom_right_d256_long_rows(gpu_device):
             rounding_allowance=True, what="bottom-right D=256")
 
 
+# -- attention masks (PyTorch SDPA attn_mask semantics) -----------------------
+
+def _mask_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, kind, seed, causal=False, splits=0,
+               mshape=None):
+    """kind "bool": random keep mask (one row left with no key); "add": an
+    additive mask in the inputs' dtype with -inf entries; "pad": key padding
+    per batch (batch 1 keeps no key at all).  The mask is broadcast from
+    ``mshape`` (default [B, 1, Nq, Nkv])."""
+    import torch
+    import oracle
+    from memory_efficient_tiled_amd import attn_fwd
+    log(f"mask case {kind} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} "
+        f"causal={causal} splits={splits}")
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed)
+    rng = np.random.Generator(np.random.PCG64([seed, 7]))
+    mshape = mshape or (B, 1, Nq, Nkv)
+    if kind == "bool":
+        keep = rng.random(mshape) < 0.7
+        keep[(0,) * (len(mshape) - 2) + (min(3, mshape[-2] - 1),)] = False
+        mt, bias = torch.from_numpy(keep).to(device), np.where(keep, 0.0, -np.inf)
+    elif kind == "add":
+        a = (2.0 * rng.standard_normal(mshape)).astype(np.float32)
+        a[rng.random(mshape) < 0.2] = -np.inf
+        st = inputs.to_storage(a, dtype)
+        mt = to_device(st, dtype, device)
+        bias = oracle.decode(st, dtype)
+    else:  # key padding: batch b keeps its first n_b keys
+        keep = np.zeros((B, 1, 1, Nkv), dtype=bool)
+        for b in range(B):
+            keep[b, ..., : (Nkv * 2) // 3 if b != 1 else 0] = True
+        mt, bias = torch.from_numpy(keep).to(device), np.where(keep, 0.0, -np.inf)
+    q, k, v = (to_device(a, dtype, device) for a in (x.q, x.k, x.v))
+    o, l = attn_fwd(q, k, v, causal=causal, mask=mt, num_splits=splits)
+    torch.cuda.synchronize(device)
+    o = o.float().cpu().numpy().astype(np.float64)
+    l = l.cpu().numpy().astype(np.float64)
+    sc = oracle.scale_value(None, D)
+    off = Nkv - Nq if causal == "bottom_right" else 0
+    o_ref, l_ref = oracle.attention(oracle.decode(x.q, dtype), oracle.decode(x.k, dtype),
+                                    oracle.decode(x.v, dtype), sc, bool(causal),
+                                    causal_offset=off,
+                                    bias=np.broadcast_to(bias, (B, Hq, Nq, Nkv)))
+    # A strong additive bias concentrates a row's weight on few keys, where
+    # rounding P to the 16-bit MFMA operand (relative 2^-9 bf16, 2^-12 fp16)
+    # moves o by up to that fraction of sum_j P_ij |v_j|: the oracle's
+    # attention with |V| as the values gives that sum exactly.
+    u = 2.0 ** -8 if dtype == inputs.BF16 else 2.0 ** -11
+    pv, _ = oracle.attention(oracle.decode(x.q, dtype), oracle.decode(x.k, dtype),
+                             np.abs(oracle.decode(x.v, dtype)), sc, bool(causal),
+                             causal_offset=off, bias=np.broadcast_to(bias, (B, Hq, Nq, Nkv)))
+    compare(o, l, o_ref, l_ref, dtype, rounding_allowance=True,
+            what=f"mask {kind} {Nq}x{Nkv} D={D}", extra=u * pv)
+    empty = np.isneginf(l_ref)
+    assert np.all(o[empty] == 0.0)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+@pytest.mark.parametrize("kind", ["bool", "add", "pad"])
+def test_masks(gpu_device, kind, dtype, D):
+    # 301 keys: rows of the mask are padded to a multiple of 4 by the binding
+    _mask_case(gpu_device, 2, 4, 2, 200, 301, D, dtype, kind, seed=D + len(kind))
+
+
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_masks_per_head_causal_split(gpu_device, kind):
+    _mask_case(gpu_device, 1, 6, 3, 130, 700, 64, inputs.BF16, kind, seed=95,
+               causal="bottom_right", splits=3, mshape=(1, 6, 130, 700))
+
+
+@pytest.mark.parametrize("D", [80, 96, 256])
+def test_masks_other_head_dims(gpu_device, D):
+    _mask_case(gpu_device, 1, 4, 4, 150, 260, D, inputs.F16, "add", seed=D)
+
+
+def test_mask_long_rows_sampled(gpu_device):
+    """A 2-D boolean mask over 4096 keys, broadcast over batch and heads."""
+    _mask_case(gpu_device, 1, 8, 8, 256, 4096, 128, inputs.BF16, "bool", seed=96,
+               mshape=(256, 4096))
+
+
 # -- split of the last partial round ---------------------------------------
 # Grids that fill the device but end in a partial round of workgroups cut
 # only that round's tiles over their key range (first split tile inside a
