@@ -33,7 +33,9 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc")
 # the kernel sources each pass runs (a measurement taken on other sources is stale)
-SOURCES = {"fwd": ("attn_common.h", "attn_fwd.hip"),
+SOURCES = {"fwd": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_d64.hip",
+                   "attn_fwd_d80.hip", "attn_fwd_d96.hip", "attn_fwd_d128.hip",
+                   "attn_fwd_d256.hip"),
            "bwd": ("attn_common.h", "attn_bwd.hip")}
 PROFILES = os.path.join(ROOT, "profiles")
 BWD_FLOP_FACTOR = 2.5
