@@ -164,7 +164,8 @@ def attention_from_storage(q, k, v, dtype: str, scale: float | None,
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                        do: np.ndarray, scale: float, causal: bool,
-                       row_group: int = 256, causal_offset: int = 0):
+                       row_group: int = 256, causal_offset: int = 0,
+                       bias: np.ndarray | None = None):
     """Gradients of softmax attention in float64: (dq, dk, dv).
 
     For a loss whose gradient with respect to the output is ``do``
@@ -180,7 +181,8 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     K/V gradients of a KV head sum over the query heads that read it (the
     GQA grouping of the forward).  Masked keys have P = 0 and get nothing
     from that row; a row with no allowed key (see ``attention``) has o = 0
-    whatever the inputs, so all its gradients are 0.  The post's first tier keeps autograd through its tiled
+    whatever the inputs, so all its gradients are 0.  ``bias`` is the
+    forward's additive mask (not differentiated).  The post's first tier keeps autograd through its tiled
     forward (section "The DIY approach"); these are the gradients it yields.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -198,6 +200,8 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     key_idx = np.arange(Nkv, dtype=np.int64)
+    if bias is not None:
+        bias = np.broadcast_to(np.asarray(bias, dtype=np.float64), (B, Hq, Nq, Nkv))
     for b in range(B):
         for hq in range(Hq):
             hk = hq // G
@@ -206,6 +210,8 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
             for r0 in range(0, Nq, row_group):
                 ri = np.arange(r0, min(Nq, r0 + row_group), dtype=np.int64)
                 s = scale * (q[b, hq, ri] @ kk.T)
+                if bias is not None:
+                    s = s + bias[b, hq, ri]
                 if causal:
                     s = np.where(key_idx[None, :] <= ri[:, None] + causal_offset, s, -np.inf)
                 m = s.max(axis=1, keepdims=True)

@@ -126,5 +126,32 @@ def pin_finite_differences_offset(bwd):
             assert np.all(np.isfinite(dk)) and np.any(dk[:, :, -1] != 0.0)
 
 
+def pin_finite_differences_bias(bwd):
+    """The derivative check with an additive mask (finite and -inf entries,
+    one row left with no key), against the forward oracle with the same
+    bias."""
+    q, k, v, do = _inputs(13, Hq=2, Hkv=1, Nq=6, Nkv=8)
+    r = _rng(213)
+    bias = r.standard_normal((1, 2, 6, 8))
+    bias[r.random((1, 2, 6, 8)) < 0.3] = -np.inf
+    bias[0, 1, 2] = -np.inf
+    scale = 0.5
+    dq, dk, dv = bwd(q, k, v, do, scale, False, bias=bias)
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        d = r.standard_normal(x.shape)
+        def loss(xx):
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xx
+            o, _ = oracle.attention(args["q"], args["k"], args["v"], scale, False, bias=bias)
+            return float(np.sum(o * do))
+        fd = (loss(x + h * d) - loss(x - h * d)) / (2 * h)
+        an = float(np.sum(g * d))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), \
+            f"d{name} (bias): finite difference {fd:.10f} vs {an:.10f}"
+    assert np.all(dq[0, 1, 2] == 0.0), "a row with no key has no dq"
+
+
 ALL_PINS = [pin_finite_differences, pin_causal_row0_dq, pin_zero_do, pin_column_sums,
-            pin_linear_in_do, pin_gqa_repeat, pin_finite_differences_offset]
+            pin_linear_in_do, pin_gqa_repeat, pin_finite_differences_offset,
+            pin_finite_differences_bias]

@@ -97,6 +97,7 @@ BWD_MUTANTS = [
      "key_idx[None, :] < ri[:, None] + 2 + causal_offset"),
     ("causal offset ignored", "key_idx[None, :] <= ri[:, None] + causal_offset",
      "key_idx[None, :] <= ri[:, None]"),
+    ("bias ignored in the gradients", "s = s + bias[b, hq, ri]", "s = s + 0.0"),
 ]
 
 
