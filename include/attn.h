@@ -274,6 +274,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out,
              int causal, int dtype, void* stream);
 
 /*
+ * attn_bwd_masked -- attn_bwd for a forward computed with an attention mask
+ * (attn_fwd_masked with the same mask, mask_type and mask_stride, whose
+ * conditions apply): the mask enters the recomputed probabilities and is
+ * not differentiated.  Rows the mask (or a causal mode) leaves with no key
+ * get zero gradients.  D in {64, 128}.
+ */
+int attn_bwd_masked(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                    const void* mask, int mask_type, const long long* mask_stride,
+                    float scale, int causal, int dtype, void* stream);
+
+/* attn_bwd_masked_check -- host only: attn_bwd_masked's validation. */
+int attn_bwd_masked_check(const void* q, const void* k, const void* v,
+                          const void* out, const void* dout, const float* lse,
+                          const void* dq, const void* dk, const void* dv, int B,
+                          int Hq, int Hkv, int Nq, int Nkv, int D,
+                          const void* mask, int mask_type,
+                          const long long* mask_stride, float scale,
+                          int causal, int dtype);
+
+/*
  * attn_bwd_check -- host only: attn_bwd's argument validation; makes no HIP
  * call and dereferences no pointer.  Returns ATTN_OK or ATTN_EINVAL.
  */

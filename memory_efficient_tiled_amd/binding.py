@@ -104,6 +104,12 @@ def load_library():
     lib.attn_bwd.restype = _INT
     lib.attn_bwd_check.argtypes = [_VP] * 9 + shape_args + [ctypes.c_float, _INT, _INT]
     lib.attn_bwd_check.restype = _INT
+    lib.attn_bwd_masked.argtypes = [_VP] * 9 + shape_args + [_VP, _INT, _LLP, ctypes.c_float,
+                                                             _INT, _INT, _VP]
+    lib.attn_bwd_masked.restype = _INT
+    lib.attn_bwd_masked_check.argtypes = [_VP] * 9 + shape_args + [_VP, _INT, _LLP,
+                                                                   ctypes.c_float, _INT, _INT]
+    lib.attn_bwd_masked_check.restype = _INT
     lib.attn_strerror.argtypes = [_INT]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -302,11 +308,11 @@ def attn_bwd_check(q_ptr, k_ptr, v_ptr, out_ptr, dout_ptr, lse_ptr, dq_ptr, dk_p
 
 
 def attn_bwd(q, k, v, out, lse, dout, causal=False, scale: float | None = None,
-             dq=None, dk=None, dv=None):
+             dq=None, dk=None, dv=None, mask=None):
     """(dq, dk, dv): gradients of attn_fwd's output with respect to q, k, v.
 
     q, k, v, out, lse are the forward's inputs and outputs (same scale and
-    causal flag), dout the gradient at out.  Every tensor must be contiguous
+    causal flag, and ``mask`` if it had one), dout the gradient at out.  Every tensor must be contiguous
     ([B, H, N, D], lse float32 [B, Hq, Nq]) and on one HIP device; dq, dk, dv
     are allocated unless given.  Runs on torch's current stream.
     """
@@ -349,10 +355,20 @@ def attn_bwd(q, k, v, out, lse, dout, causal=False, scale: float | None = None,
     dq, dk, dv = grads
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                          dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, float(scale),
-                          causal_code(causal), dt, stream)
+        if mask is None:
+            rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, float(scale),
+                              causal_code(causal), dt, stream)
+        else:
+            if mask.device != q.device:
+                raise ValueError("mask must be on q's device")
+            m, mtype, ms = mask_view(mask, B, Hq, Nq, Nkv, q.dtype)
+            rc = lib.attn_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                     dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D,
+                                     m.data_ptr(), mtype, ms, float(scale), causal_code(causal),
+                                     dt, stream)
     if rc != ATTN_OK:
         _raise(rc)
     return dq, dk, dv

@@ -60,6 +60,11 @@ struct BwdParams {
   int total;            // workgroups of the launch
   float cs;             // scale * log2(e) (signed)
   float scale;
+  // Attention mask of the forward (MASKED kernels): element (b, h, i, j) at
+  // mask + b*msb + h*msh + i*msq + j, ATTN_MASK_BOOL or ATTN_MASK_ADD.
+  const uint8_t* mask;
+  int64_t msb, msh, msq;
+  int mask_mode;
 };
 
 // Delta_r = sum_d dO[r, d] O[r, d] in fp32: D / 8 lanes per row, one 16-byte
@@ -190,7 +195,7 @@ __device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst,
 // so two waves fit on a SIMD and one wave's softmax work overlaps the
 // other's matrix products.  Q and dO tiles are in LDS twice each, two
 // buffers deep, with lse2 and Delta.
-template <int D, class Tag, bool CAUSAL>
+template <int D, class Tag, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   constexpr int NW = 8, BK = 128, BQ = 64, NQB = 2;
   constexpr int DC = D / 16, NDB = D / 32, NKC = BQ / 16, CPR = D / 8;
@@ -280,10 +285,15 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   const int v_sw = v_swz<D>(v_key);
 
   // P in place of S (P waves); accumulator register e of block qb is query
-  // row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.
-  auto probs = [&](auto mskc, auto bufc, f32x16* s, int q0) {
+  // row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.  With a mask, its base-2
+  // bias joins the exponent; rows past Nq and rows that saw no key in the
+  // forward (lse -inf) get P = 0.
+  auto probs = [&](auto mskc, auto bufc, f32x16* s, int q0, int hq) {
     constexpr bool MSK = decltype(mskc)::value;
     constexpr int buf = decltype(bufc)::value;
+    const uint8_t* mbase = nullptr;
+    if constexpr (MASKED) mbase = p.mask;
+    const int64_t mrow0 = MASKED ? b * p.msb + hq * p.msh : 0;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -292,7 +302,19 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
         const f32x4 ls = *(const f32x4*)(&lse_s[buf][r]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
+          float pv;
+          if constexpr (MASKED) {
+            const int row = q0 + r + e;
+            const float bias =
+                row < p.Nq && key < p.Nkv
+                    ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + row * p.msq + key)
+                    : 0.f;
+            pv = (row < p.Nq && ls[e] != -INFINITY)
+                     ? fast_exp2(fmaf(p.cs, s[qb][4 * j + e], bias) - ls[e])
+                     : 0.f;
+          } else {
+            pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
+          }
           if (MSK && key > q0 + r + e + p.coff) pv = 0.f;
           s[qb][4 * j + e] = pv;
         }
@@ -320,9 +342,9 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     u32x4 bop[NKC];
     if (pw) {
       if (CAUSAL && kw0 + 31 > q0 + p.coff)
-        probs(std::true_type{}, bufc, s, q0);
+        probs(std::true_type{}, bufc, s, q0, hq);
       else
-        probs(std::false_type{}, bufc, s, q0);
+        probs(std::false_type{}, bufc, s, q0, hq);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) pack_tile<Tag>(s[qb], &bop[qb * 2]);
 #pragma unroll
@@ -400,7 +422,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4) 
 //   dQ^T += K^T dS^T                (rows: D, columns: 32 queries)
 // Q and dO stay in registers; K is copied into LDS twice (row-read and
 // transposed layouts) and V once, two buffers deep, the loop unrolled by two.
-template <int D, class Tag, bool CAUSAL>
+template <int D, class Tag, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   constexpr int NW = 4, BM = NW * 32, BN = 32;
   constexpr int DC = D / 16, NDB = D / 32, CPR = D / 8;
@@ -466,14 +488,32 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
   const int v_sw = v_swz<D>(v_key);
 
-  // register e of the score tile is key t*BN + 8 (e / 4) + 4 hl + e % 4
+  // register e of the score tile is key t*BN + 8 (e / 4) + 4 hl + e % 4.
+  // With a mask, its base-2 bias joins the exponent; rows past Nq and rows
+  // that saw no key in the forward (lse -inf) get P = 0.
+  const uint8_t* mrow = nullptr;
+  if constexpr (MASKED) {
+    const int64_t off = b * p.msb + hq * p.msh + (int64_t)min(qrow, p.Nq - 1) * p.msq;
+    mrow = p.mask + off * (p.mask_mode == ATTN_MASK_BOOL ? 1 : 2);
+  }
+  const bool row_live = qrow < p.Nq && nl2 != INFINITY;
   auto probs = [&](auto mskc, f32x16& s, f32x16& dp, int t) {
     constexpr bool MSK = decltype(mskc)::value;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float pv = fast_exp2(fmaf(p.cs, s[e], nl2));
-      if (MSK && t * BN + 8 * (e >> 2) + 4 * hl + (e & 3) > qrow + p.coff) pv = 0.f;
-      dp[e] = pv * (dp[e] - dl);
+    for (int g = 0; g < 4; ++g) {
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (MASKED) mask_bias4<Tag>(mrow, p.mask_mode, t * BN + 8 * g + 4 * hl, p.Nkv, bias);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * g + i;
+        float pv;
+        if constexpr (MASKED)
+          pv = row_live ? fast_exp2(fmaf(p.cs, s[e], bias[i]) + nl2) : 0.f;
+        else
+          pv = fast_exp2(fmaf(p.cs, s[e], nl2));
+        if (MSK && t * BN + 8 * g + 4 * hl + i > qrow + p.coff) pv = 0.f;
+        dp[e] = pv * (dp[e] - dl);
+      }
     }
   };
 
@@ -559,7 +599,31 @@ int bwd_head_split(int B, int Hkv, int Nkv, int G, int cus) {
   return G;
 }
 
-template <int D, class Tag>
+// The forward's attention mask, as attn_fwd_masked takes it.
+struct BwdMask {
+  const void* ptr = nullptr;
+  int type = ATTN_MASK_NONE;
+  int64_t sb = 0, sh = 0, sq = 0;
+};
+
+int validate_bwd_mask(const BwdMask& m, const void* dq, const void* dk, const void* dv, int B,
+                      int Hq, int Hkv, int Nq, int Nkv, int D) {
+  if (m.type == ATTN_MASK_NONE) return ATTN_OK;
+  if (m.type != ATTN_MASK_BOOL && m.type != ATTN_MASK_ADD) return ATTN_EINVAL;
+  if (!m.ptr || ((uintptr_t)m.ptr & 7)) return ATTN_EINVAL;
+  if (m.sb < 0 || m.sh < 0 || m.sq < 0 || ((m.sb | m.sh | m.sq) & 3)) return ATTN_EINVAL;
+  const int esz = m.type == ATTN_MASK_BOOL ? 1 : 2;
+  const __int128 mb = esz * ((__int128)(B - 1) * m.sb + (__int128)(Hq - 1) * m.sh +
+                             (__int128)(Nq - 1) * m.sq + Nkv);
+  if (mb > ((__int128)1 << 62)) return ATTN_EINVAL;
+  const size_t qb = (size_t)B * Hq * Nq * D * 2, kb = (size_t)B * Hkv * Nkv * D * 2;
+  if (overlaps_bytes(dq, qb, m.ptr, (size_t)mb) || overlaps_bytes(dk, kb, m.ptr, (size_t)mb) ||
+      overlaps_bytes(dv, kb, m.ptr, (size_t)mb))
+    return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+template <int D, class Tag, bool MASKED>
 hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   const int rows = p.B * p.Hq * p.Nq;
   const size_t threads = (size_t)rows * (D / 8);
@@ -571,11 +635,11 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   pk.n_tiles = (p.Nkv + 127) / 128;
   pk.total = p.B * p.Hkv * p.hsplit * pk.n_tiles;
   if (causal)
-    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, true>), dim3(pk.total), dim3(512), 0, st,
-                       pk);
+    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, true, MASKED>), dim3(pk.total), dim3(512),
+                       0, st, pk);
   else
-    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, false>), dim3(pk.total), dim3(512), 0, st,
-                       pk);
+    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, false, MASKED>), dim3(pk.total), dim3(512),
+                       0, st, pk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.hsplit > 1) {
@@ -589,29 +653,21 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   pq.n_tiles = (p.Nq + 127) / 128;
   pq.total = p.B * p.Hq * pq.n_tiles;
   if (causal)
-    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, true>), dim3(pq.total), dim3(256), 0, st, pq);
+    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, true, MASKED>), dim3(pq.total), dim3(256), 0, st,
+                       pq);
   else
-    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, false>), dim3(pq.total), dim3(256), 0, st, pq);
+    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, false, MASKED>), dim3(pq.total), dim3(256), 0, st,
+                       pq);
   return hipGetLastError();
 }
 
-}  // namespace
-
-extern "C" {
-
-int attn_bwd_check(const void* q, const void* k, const void* v, const void* out,
-                   const void* dout, const float* lse, const void* dq, const void* dk,
-                   const void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale,
-                   int causal, int dtype) {
-  return validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
-                      dtype);
-}
-
-int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
-             int Nkv, int D, float scale, int causal, int dtype, void* stream) {
+int run_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+            const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+            int Nkv, int D, float scale, int causal, int dtype, void* stream,
+            const BwdMask& m) {
   int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
                         causal, dtype);
+  if (rc == ATTN_OK) rc = validate_bwd_mask(m, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D);
   if (rc != ATTN_OK) return rc;
   int cus = 0;
   rc = attn_host::check_device(&cus);
@@ -660,12 +716,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   p.coff = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0;
   p.cs = scale * kLog2e;
   p.scale = scale;
-  const bool cz = causal != 0;
-  if (D == 64)
-    e = dtype == ATTN_BF16 ? launch_bwd<64, TagBF16>(p, cz, st) : launch_bwd<64, TagF16>(p, cz, st);
-  else
-    e = dtype == ATTN_BF16 ? launch_bwd<128, TagBF16>(p, cz, st)
-                           : launch_bwd<128, TagF16>(p, cz, st);
+  p.mask = (const uint8_t*)m.ptr;
+  p.msb = m.sb, p.msh = m.sh, p.msq = m.sq;
+  p.mask_mode = m.type;
+  const bool cz = causal != 0, bf = dtype == ATTN_BF16;
+  if (m.type != ATTN_MASK_NONE) {
+    if (D == 64)
+      e = bf ? launch_bwd<64, TagBF16, true>(p, cz, st) : launch_bwd<64, TagF16, true>(p, cz, st);
+    else
+      e = bf ? launch_bwd<128, TagBF16, true>(p, cz, st)
+             : launch_bwd<128, TagF16, true>(p, cz, st);
+  } else {
+    if (D == 64)
+      e = bf ? launch_bwd<64, TagBF16, false>(p, cz, st)
+             : launch_bwd<64, TagF16, false>(p, cz, st);
+    else
+      e = bf ? launch_bwd<128, TagBF16, false>(p, cz, st)
+             : launch_bwd<128, TagF16, false>(p, cz, st);
+  }
   const hipError_t ef = hipFreeAsync(ws, st);
   if (e == hipSuccess) e = ef;
   if (e != hipSuccess) {
@@ -673,6 +741,62 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
     return ATTN_EHIP;
   }
   return ATTN_OK;
+}
+
+BwdMask bwd_mask(const void* mask, int mask_type, const long long* mask_stride) {
+  BwdMask m;
+  m.ptr = mask;
+  m.type = mask_type;
+  if (mask_type != ATTN_MASK_NONE) {
+    if (!mask_stride) {
+      m.type = -1;  // rejected by validation
+    } else {
+      m.sb = mask_stride[0];
+      m.sh = mask_stride[1];
+      m.sq = mask_stride[2];
+    }
+  }
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_check(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, const void* dq, const void* dk,
+                   const void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale,
+                   int causal, int dtype) {
+  return validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                      dtype);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+             int Nkv, int D, float scale, int causal, int dtype, void* stream) {
+  return run_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                 dtype, stream, BwdMask());
+}
+
+int attn_bwd_masked(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                    int Hq, int Hkv, int Nq, int Nkv, int D, const void* mask, int mask_type,
+                    const long long* mask_stride, float scale, int causal, int dtype,
+                    void* stream) {
+  return run_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                 dtype, stream, bwd_mask(mask, mask_type, mask_stride));
+}
+
+int attn_bwd_masked_check(const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, const void* dq, const void* dk,
+                          const void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                          const void* mask, int mask_type, const long long* mask_stride,
+                          float scale, int causal, int dtype) {
+  const int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
+                              causal, dtype);
+  if (rc != ATTN_OK) return rc;
+  return validate_bwd_mask(bwd_mask(mask, mask_type, mask_stride), dq, dk, dv, B, Hq, Hkv, Nq,
+                           Nkv, D);
 }
 
 }  // extern "C"

@@ -78,6 +78,51 @@ __device__ __forceinline__ float hi_f32<TagF16>(uint32_t w) {
   return (float)__builtin_bit_cast(f16x2, w)[1];
 }
 
+// Attention-mask values as base-2 biases.  ATTN_MASK_BOOL: bytes, zero
+// removes the key (-inf), nonzero keeps it (0).  ATTN_MASK_ADD: values of
+// the input type, added to the scaled scores (times log2 e here).
+// mask_bias4: keys key0 .. key0 + 3 of one mask row (16-bit mask rows at
+// `mrow` as bytes); keys at or past nkv are not read (bias 0).
+template <class Tag>
+__device__ __forceinline__ void mask_bias4(const uint8_t* mrow, int mode, int key0, int nkv,
+                                           float* bias) {
+  if (mode == ATTN_MASK_BOOL) {
+    uint32_t w = 0;
+    if (key0 + 3 < nkv) {
+      w = *(const uint32_t*)(mrow + key0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key0 + i < nkv) w |= (uint32_t)mrow[key0 + i] << (8 * i);
+      w |= ~0u << (8 * max(0, min(4, nkv - key0)));  // keys past the end: kept (not read)
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias[i] = ((w >> (8 * i)) & 0xffu) ? 0.f : -INFINITY;
+  } else {
+    const uint16_t* m16 = (const uint16_t*)mrow;
+    u32x2 w = {0u, 0u};
+    if (key0 + 3 < nkv) {
+      w = *(const u32x2*)(m16 + key0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key0 + i < nkv) w[i >> 1] |= (uint32_t)m16[key0 + i] << (16 * (i & 1));
+    }
+    bias[0] = lo_f32<Tag>(w[0]) * kLog2e;
+    bias[1] = hi_f32<Tag>(w[0]) * kLog2e;
+    bias[2] = lo_f32<Tag>(w[1]) * kLog2e;
+    bias[3] = hi_f32<Tag>(w[1]) * kLog2e;
+  }
+}
+
+// One mask value (element `idx` of the mask) as a base-2 bias.
+template <class Tag>
+__device__ __forceinline__ float mask_bias1(const uint8_t* mask, int mode, int64_t idx) {
+  if (mode == ATTN_MASK_BOOL) return mask[idx] ? 0.f : -INFINITY;
+  const uint32_t h = ((const uint16_t*)mask)[idx];
+  return lo_f32<Tag>(h) * kLog2e;
+}
+
 // Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
 // so that each XCD receives a contiguous range of logical tiles: the query
 // tiles of one head then share that XCD's L2 for their K/V stream.

@@ -348,37 +348,6 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     }
   };
 
-  // Four consecutive mask values of one row as base-2 biases (keys from
-  // key0; those past the key range are not read).
-  auto mask_bias4 = [&](const uint8_t* mrow, int key0, float* bias) {
-    if (p.mask_mode == ATTN_MASK_BOOL) {
-      uint32_t w = 0;
-      if (key0 + 3 < p.Nkv) {
-        w = *(const uint32_t*)(mrow + key0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key0 + i < p.Nkv) w |= (uint32_t)mrow[key0 + i] << (8 * i);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bias[i] = ((w >> (8 * i)) & 0xffu) ? 0.f : -INFINITY;
-    } else {
-      const uint16_t* m16 = (const uint16_t*)mrow;
-      u32x2 w = {0u, 0u};
-      if (key0 + 3 < p.Nkv) {
-        w = *(const u32x2*)(m16 + key0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key0 + i < p.Nkv) w[i >> 1] |= (uint32_t)m16[key0 + i] << (16 * (i & 1));
-      }
-      bias[0] = lo_f32<Tag>(w[0]) * kLog2e;
-      bias[1] = hi_f32<Tag>(w[0]) * kLog2e;
-      bias[2] = lo_f32<Tag>(w[1]) * kLog2e;
-      bias[3] = hi_f32<Tag>(w[1]) * kLog2e;
-    }
-  };
-
   // Keys past the valid range, and (causal) keys after the row, get -inf.
   // Only tiles that straddle the end of the key range or the diagonal; with
   // a mask, every tile (scores are scaled and biased here).
@@ -400,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
           for (int g = 0; g < 4; ++g) {
             const int key0 = k0 + kb * 32 + 8 * g + 4 * hl;
             float bias[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (MASKED) mask_bias4(mrow, key0, bias);
+            if constexpr (MASKED) mask_bias4<Tag>(mrow, p.mask_mode, key0, p.Nkv, bias);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int key = key0 + i;

@@ -9,8 +9,8 @@ it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
   top-left causal through ``is_causal``; PyTorch's causal biases
   ``causal_upper_left`` / ``causal_lower_right`` as ``attn_mask`` (the
   latter is bottom-right alignment, rows that see no key give 0); boolean
-  or additive ``attn_mask`` tensors broadcastable to [B, H, L, S] (forward
-  only: not under autograd); GQA via ``enable_gqa``, default scale
+  or additive ``attn_mask`` tensors broadcastable to [B, H, L, S] (the mask
+  itself gets no gradient); GQA via ``enable_gqa``, default scale
   1/sqrt(E)) and raises ``NotImplementedError`` for anything else; inputs may be strided views such as [B, N, H, E]
   storage transposed to [B, H, N, E] (no copy is made).
 * ``patch()`` installs it as ``torch.nn.functional.scaled_dot_product_attention``.
@@ -91,8 +91,9 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
                     return "attn_mask does not broadcast to the scores' shape"
             if attn_mask.device != query.device:
                 return "attn_mask must be on the inputs' device"
-            if torch.is_grad_enabled() and any(t.requires_grad for t in ts):
-                return "gradients with an attention mask are not built"
+            if (torch.is_grad_enabled() and any(t.requires_grad for t in ts)
+                    and query.shape[-1] not in (64, 128)):
+                return "gradients are built for head dimensions 64 and 128 only"
         else:
             return "attn_mask must be a tensor or one of PyTorch's causal biases"
     if dropout_p != 0.0:
@@ -195,8 +196,8 @@ def torch_ops():
       (``mask`` None or an SDPA attn_mask tensor; ``causal`` the C ABI's
       code: 0 none, 1 top-left, 2 bottom-right);
     * ``memory_efficient_tiled_amd::attention_backward(dout, q, k, v, out, lse,
-      causal, scale) -> (dq, dk, dv)``, the first op's autograd formula (the
-      log-sum-exp output is not differentiable).
+      mask, causal, scale) -> (dq, dk, dv)``, the first op's autograd formula
+      (the log-sum-exp output and the mask are not differentiated).
 
     Both have fake implementations (output shapes only) for tracing.
     """
@@ -220,29 +221,27 @@ def torch_ops():
     @torch.library.custom_op(
         "memory_efficient_tiled_amd::attention_backward", mutates_args=(),
         schema="(Tensor dout, Tensor q, Tensor k, Tensor v, Tensor out, Tensor lse, "
-               "int causal, float scale) -> (Tensor, Tensor, Tensor)")
-    def attention_backward(dout, q, k, v, out, lse, causal, scale):
+               "Tensor? mask, int causal, float scale) -> (Tensor, Tensor, Tensor)")
+    def attention_backward(dout, q, k, v, out, lse, mask, causal, scale):
         q, k, v, dout = (t.contiguous() for t in (q, k, v, dout))
         return binding.attn_bwd(q, k, v, out.contiguous(), lse, dout, causal=causal,
-                                scale=scale)
+                                scale=scale, mask=mask)
 
     @attention_backward.register_fake
-    def _(dout, q, k, v, out, lse, causal, scale):
+    def _(dout, q, k, v, out, lse, mask, causal, scale):
         return tuple(torch.empty_like(t, memory_format=torch.contiguous_format)
                      for t in (q, k, v))
 
     def setup_context(ctx, inputs, output):
         q, k, v, mask, causal, scale = inputs
         out, lse = output
-        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.save_for_backward(q, k, v, out, lse, mask)
         ctx.mark_non_differentiable(lse)
-        ctx.causal, ctx.scale, ctx.masked = causal, scale, mask is not None
+        ctx.causal, ctx.scale = causal, scale
 
     def backward(ctx, dout, _dlse):
-        if ctx.masked:
-            raise NotImplementedError("gradients with an attention mask are not built")
-        q, k, v, out, lse = ctx.saved_tensors
-        dq, dk, dv = attention_backward(dout, q, k, v, out, lse, ctx.causal, ctx.scale)
+        q, k, v, out, lse, mask = ctx.saved_tensors
+        dq, dk, dv = attention_backward(dout, q, k, v, out, lse, mask, ctx.causal, ctx.scale)
         return dq, dk, dv, None, None, None
 
     attention.register_autograd(backward, setup_context=setup_context)

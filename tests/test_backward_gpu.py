@@ -202,3 +202,68 @@ def test_sdpa_autograd(gpu_device):
     for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
         got = _host(leaf.grad.transpose(1, 2))
         check_grad(name, got, r, dtype, "sdpa autograd", None, t)
+
+
+@pytest.mark.parametrize("kind", ["bool", "add"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_masked_gradients(gpu_device, kind, D):
+    """Gradients of a masked forward: a per-head boolean mask (one row left
+    with no key) or an additive mask with -inf entries, GQA, ragged sizes."""
+    import torch
+    dtype = inputs.BF16
+    B, Hq, Hkv, Nq, Nkv = 1, 4, 2, 150, 230
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=D + len(kind))
+    do = inputs.make_dout(x)
+    rng = np.random.Generator(np.random.PCG64([D, 9]))
+    if kind == "bool":
+        keep = rng.random((1, Hq, Nq, Nkv)) < 0.7
+        keep[0, 1, 5] = False
+        mt, bias = torch.from_numpy(keep).to(gpu_device), np.where(keep, 0.0, -np.inf)
+    else:
+        a = rng.standard_normal((Nq, Nkv)).astype(np.float32)
+        a[rng.random((Nq, Nkv)) < 0.2] = -np.inf
+        st = inputs.to_storage(a, dtype)
+        mt, bias = to_device(st, dtype, gpu_device), _decode(st, dtype)
+    q, k, v, g = (to_device(a, dtype, gpu_device) for a in (x.q, x.k, x.v, do))
+    out, lse = binding.attn_fwd(q, k, v, mask=mt)
+    dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, g, mask=mt)
+    torch.cuda.synchronize(gpu_device)
+    sc = oracle.scale_value(None, D)
+    bias4 = np.broadcast_to(bias, (B, Hq, Nq, Nkv))
+    dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
+    ref = oracle.attention_backward(*dec, sc, False, bias=bias4)
+    # the Delta terms of the bound, with the mask in the oracle's attention
+    u = U[dtype]
+    o, _ = oracle.attention(*dec[:3], sc, False, bias=bias4)
+    pk, _ = oracle.attention(dec[0], dec[1], dec[1], sc, False, bias=bias4)
+    bq = np.sqrt(np.sum((dec[3] * o) ** 2, axis=-1, keepdims=True))
+    t_dq = 12.0 * sc * u * bq * np.abs(pk)
+    bmax = bq[..., 0].reshape(B, Hkv, -1).max(axis=-1)[:, :, None, None]
+    qmax = np.abs(dec[0]).reshape(B, Hkv, -1).max(axis=-1)[:, :, None, None]
+    t_dk = 6.0 * sc * u * bmax * qmax * np.sqrt(np.mean(ref[2] ** 2, axis=-1, keepdims=True))
+    what = f"masked {kind} D={D}"
+    for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, (t_dq, t_dk, 0.0)):
+        check_grad(name, _host(got), r, dtype, what, None, t)
+    if kind == "bool":
+        assert torch.all(dq[0, 1, 5] == 0), "a row with no key has no gradient"
+
+
+def test_sdpa_masked_autograd(gpu_device):
+    import torch
+    import memory_efficient_tiled_amd as mta
+    dtype = inputs.F16
+    x = inputs.make_inputs(2, 4, 4, 90, 120, 64, dtype, seed=61)
+    do = inputs.make_dout(x)
+    keep = np.ones((2, 1, 1, 120), dtype=bool)
+    keep[1, ..., 100:] = False                        # key padding of batch 1
+    leaves = [to_device(a, dtype, gpu_device).requires_grad_(True) for a in (x.q, x.k, x.v)]
+    o = mta.sdpa(*leaves, attn_mask=torch.from_numpy(keep).to(gpu_device))
+    o.backward(to_device(do, dtype, gpu_device))
+    torch.cuda.synchronize(gpu_device)
+    bias = np.broadcast_to(np.where(keep, 0.0, -np.inf), (2, 4, 90, 120))
+    dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
+    ref = oracle.attention_backward(*dec, oracle.scale_value(None, 64), False, bias=bias)
+    for name, leaf, r in zip(("dq", "dk", "dv"), leaves, ref):
+        check_grad(name, _host(leaf.grad), r, dtype, "sdpa masked autograd", None,
+                   2e-3 * float(np.sqrt(np.mean(r ** 2))))
+    assert torch.all(leaves[1].grad[1, :, 100:] == 0) and torch.all(leaves[2].grad[1, :, 100:] == 0)

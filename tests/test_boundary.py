@@ -202,3 +202,15 @@ def test_masked_validation():
     assert mcheck(ms=(-4, 0, 64)) == EINVAL
     assert mcheck(ms=None) == EINVAL
     assert mcheck(mask=O) == EINVAL                       # overlaps the output
+
+
+def test_masked_backward_validation():
+    lib = binding.load_library()
+    null = ctypes.POINTER(ctypes.c_longlong)()
+    ms = (ctypes.c_longlong * 3)(0, 0, 64)
+    args = (Q, K, V, O, 0x70000000, L, 0x80000000, 0x90000000, 0xA0000000, 2, 8, 2, 64, 64, 128)
+    assert lib.attn_bwd_masked_check(*args, 0x60000000, 1, ms, 0.088, 0, BF16) == OK
+    assert lib.attn_bwd_masked_check(*args, 0x60000000, 1, null, 0.088, 0, BF16) == EINVAL
+    assert lib.attn_bwd_masked_check(*args, 0x60000002, 2, ms, 0.088, 0, BF16) == EINVAL
+    assert lib.attn_bwd_masked_check(*args, 0x80000000, 1, ms, 0.088, 0, BF16) == EINVAL  # = dq
+    assert lib.attn_bwd_masked_check(*args, None, 0, null, 0.088, 0, BF16) == OK

@@ -73,8 +73,11 @@ def test_tensor_masks_are_served():
     for m in (t(100, 100, dtype=torch.bool), t(2, 1, 100, 100), t(2, 4, 1, 100),
               t(100, 1, dtype=torch.bool)):
         assert reason(q, q, q, attn_mask=m) == "inputs must be on one HIP device"
-    g = t(2, 4, 100, 64).requires_grad_()
-    assert "gradients" in reason(g, g, g, attn_mask=t(100, 100, dtype=torch.bool))
+    g = t(2, 4, 100, 64).requires_grad_()   # masked gradients: served
+    assert reason(g, g, g, attn_mask=t(100, 100, dtype=torch.bool)) == \
+        "inputs must be on one HIP device"
+    g96 = t(2, 4, 100, 96).requires_grad_()
+    assert "gradients" in reason(g96, g96, g96, attn_mask=t(100, 100, dtype=torch.bool))
 
 
 def test_mask_view_broadcasts_without_copies():
@@ -191,7 +194,7 @@ def test_custom_op_fake_shapes():
     assert o.shape == q.shape and o.dtype == q.dtype and o.is_contiguous()
     assert lse.shape == (2, 4, 10) and lse.dtype == torch.float32
     dq, dk, dv = torch.ops.memory_efficient_tiled_amd.attention_backward(
-        o, q, k, k, o, lse, 2, 0.125)
+        o, q, k, k, o, lse, None, 2, 0.125)
     assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == k.shape
 
 
