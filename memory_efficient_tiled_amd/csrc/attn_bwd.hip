@@ -67,15 +67,17 @@ struct BwdParams {
   int mask_mode;
 };
 
-// Delta_r = sum_d dO[r, d] O[r, d] in fp32: D / 8 lanes per row, one 16-byte
-// load of each tensor per lane, a butterfly over the row's lanes.
+// Delta_r = sum_d dO[r, d] O[r, d] in fp32: L lanes per row (D / 8 rounded
+// up to a power of two; lanes past the row add nothing), one 16-byte load of
+// each tensor per lane, a butterfly over the row's lanes.
 template <int D, class Tag>
 __global__ __launch_bounds__(256) void attn_delta_kernel(BwdParams p, int rows) {
-  constexpr int L = D / 8;  // lanes per row
+  constexpr int L = D / 8 <= 8 ? 8 : 16;  // lanes per row
+  static_assert(D / 8 <= L, "row fits its lanes");
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int row = gid / L, part = gid % L;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && part * 8 < D) {
     const u32x4 a = *(const u32x4*)(p.o + (size_t)row * D + part * 8);
     const u32x4 g = *(const u32x4*)(p.dout + (size_t)row * D + part * 8);
 #pragma unroll
@@ -90,29 +92,44 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(BwdParams p, int rows) 
   }
 }
 
-// Per-lane byte offsets for copying a [rows x D] tile into LDS with either
-// swizzle, IPW wave copies of 1 KB per wave.
-template <int D, int IPW, bool ROWREAD>
+// Copies of a ROWS-row tile into LDS: NI = ROWS * DP / 512 wave
+// instructions of 1 KB (DP: the compute dimension), instruction n by wave
+// n % NW (a wave-uniform count per wave).  Per-lane byte offsets in memory
+// (rows of D elements) for either swizzle; chunks past the row in memory
+// (D = 80) get an offset past the buffer and read zeros.
+template <int D, int ROWS, int NW>
+struct TileCopy {
+  static constexpr int DP = compute_dim(D);
+  static constexpr int CPR = DP / 8;
+  static constexpr int NI = ROWS * CPR / 64;
+  static constexpr int PER_WAVE = (NI + NW - 1) / NW;
+  static_assert(NI * 64 == ROWS * CPR, "tile copy shape");
+};
+
+template <int D, int ROWS, int NW, bool ROWREAD>
 __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t* off) {
-  constexpr int CPR = D / 8;
+  using C = TileCopy<D, ROWS, NW>;
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int slot = (wave * IPW + j) * 64 + lane;
-    const int row = slot / CPR, pc = slot % CPR;
-    off[j] = row * D * 2 + ((pc ^ (ROWREAD ? k_swz<D>(row) : v_swz<D>(row))) << 4);
+  for (int j = 0; j < C::PER_WAVE; ++j) {
+    const int slot = (wave + NW * j) * 64 + lane;
+    const int row = slot / C::CPR, pc = slot % C::CPR;
+    const int ch = pc ^ (ROWREAD ? k_swz<C::DP>(row) : v_swz<C::DP>(row));
+    off[j] = ch < D / 8 ? row * D * 2 + (ch << 4) : kPadOffset;
   }
 }
 
 // Copies the ROWS-row tile starting at row r0 of a [rows_total x D] matrix
 // at `base` into LDS (rows past rows_total read as zero; r0 < rows_total).
-template <int D, int IPW, int ROWS>
+template <int D, int ROWS, int NW>
 __device__ __forceinline__ void copy_tile(const uint16_t* base, int r0, int rows_total,
                                           uint16_t* dst, int wave, const uint32_t* off) {
+  using C = TileCopy<D, ROWS, NW>;
   const int n = min(ROWS, rows_total - r0);
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(base + (size_t)r0 * D), 0, (uint32_t)(n * D * 2), kRawBufferFlags);
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) buf2lds16(r, dst + (wave * IPW + j) * 512, off[j]);
+  for (int j = 0; j < C::PER_WAVE; ++j)
+    if (wave + NW * j < C::NI) buf2lds16(r, dst + (wave + NW * j) * 512, off[j]);
 }
 
 // A operand read along rows (16 bytes: chunk 2 kc + hl of row `row`).
@@ -148,18 +165,19 @@ __device__ __forceinline__ void pack_tile(const f32x16& s, u32x4* out) {
 }
 
 // Store accumulator tiles acc[db] (rows = d, column = this lane's row r) as
-// row r of a 16-bit [*, D] matrix, times `mul`.
+// row r of a 16-bit [*, D] matrix, times `mul` (columns past D not stored).
 template <int D, class Tag>
 __device__ __forceinline__ void store_row(uint16_t* dst, const f32x16* acc, float mul, int hl) {
   using N = Num<Tag>;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < compute_dim(D) / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int col = db * 32 + 8 * i + 4 * hl;
       const f32x16& o = acc[db];
       u32x2 y = {N::pack2(o[4 * i] * mul, o[4 * i + 1] * mul),
                  N::pack2(o[4 * i + 2] * mul, o[4 * i + 3] * mul)};
-      *(u32x2*)(dst + db * 32 + 8 * i + 4 * hl) = y;
+      if (col < D) *(u32x2*)(dst + col) = y;
     }
 }
 
@@ -169,7 +187,7 @@ template <int D, class Tag>
 __device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst, float* part,
                                               const f32x16* acc, float mul, size_t krow, int hs,
                                               int hl) {
-  constexpr int NDB = D / 32;
+  constexpr int NDB = compute_dim(D) / 32;
   if (p.hsplit == 1) {
     store_row<D, Tag>(dst + krow * D, acc, mul, hl);
     return;
@@ -178,9 +196,12 @@ __device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst,
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(f32x4*)(r + db * 32 + 8 * i + 4 * hl) =
-          f32x4{acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]};
+    for (int i = 0; i < 4; ++i) {
+      const int col = db * 32 + 8 * i + 4 * hl;
+      if (col < D)
+        *(f32x4*)(r + col) =
+            f32x4{acc[db][4 * i], acc[db][4 * i + 1], acc[db][4 * i + 2], acc[db][4 * i + 3]};
+    }
 }
 
 // dK, dV with paired waves: 8 waves over 128 keys; waves w and w + 4 (which
@@ -198,10 +219,10 @@ __device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst,
 template <int D, class Tag, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   constexpr int NW = 8, BK = 128, BQ = 64, NQB = 2;
-  constexpr int DC = D / 16, NDB = D / 32, NKC = BQ / 16, CPR = D / 8;
-  constexpr int TILE = BQ * D;
-  constexpr int IPW = BQ * CPR / 64 / NW;
-  static_assert(IPW >= 1 && IPW * 64 * NW == BQ * CPR, "tile copy shape");
+  constexpr int DP = compute_dim(D);
+  constexpr int DC = DP / 16, NDB = DP / 32, NKC = BQ / 16;
+  constexpr int TILE = BQ * DP;
+  constexpr int IPW = TileCopy<D, BQ, NW>::PER_WAVE;
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t qr[2][TILE];
@@ -237,7 +258,8 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 #pragma unroll
   for (int kc = 0; kc < DC; ++kc) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < p.Nkv) x = *(const u32x4*)(kv + (krow0 + key) * D + kc * 16 + hl * 8);
+    if (key < p.Nkv && kc * 16 + hl * 8 < D)
+      x = *(const u32x4*)(kv + (krow0 + key) * D + kc * 16 + hl * 8);
     bf[kc] = x;
   }
   f32x16 acc[NDB];
@@ -245,8 +267,8 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
   uint32_t roff[IPW], toff[IPW];
-  copy_offsets<D, IPW, true>(wave, lane, roff);
-  copy_offsets<D, IPW, false>(wave, lane, toff);
+  copy_offsets<D, BQ, NW, true>(wave, lane, roff);
+  copy_offsets<D, BQ, NW, false>(wave, lane, toff);
 
   const int nqt = (p.Nq + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? min(nqt, max(0, k0 - p.coff) / BQ) : 0;
@@ -264,10 +286,10 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
     const uint16_t* qb = p.q + qrow0 * D;
     const uint16_t* gb = p.dout + qrow0 * D;
-    copy_tile<D, IPW, BQ>(qb, q0, p.Nq, qr[buf], wave, roff);
-    copy_tile<D, IPW, BQ>(qb, q0, p.Nq, qt[buf], wave, toff);
-    copy_tile<D, IPW, BQ>(gb, q0, p.Nq, gr[buf], wave, roff);
-    copy_tile<D, IPW, BQ>(gb, q0, p.Nq, gt[buf], wave, toff);
+    copy_tile<D, BQ, NW>(qb, q0, p.Nq, qr[buf], wave, roff);
+    copy_tile<D, BQ, NW>(qb, q0, p.Nq, qt[buf], wave, toff);
+    copy_tile<D, BQ, NW>(gb, q0, p.Nq, gr[buf], wave, roff);
+    copy_tile<D, BQ, NW>(gb, q0, p.Nq, gt[buf], wave, toff);
     if (wave < 2) {  // lse2 (wave 0) and Delta (wave 1): one dword per lane
       const float* src = (wave == 0 ? p.lse2 : p.delta) + qrow0 + q0;
       const int n = min(BQ, p.Nq - q0);
@@ -282,7 +304,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
-  const int v_sw = v_swz<D>(v_key);
+  const int v_sw = v_swz<DP>(v_key);
 
   // P in place of S (P waves); accumulator register e of block qb is query
   // row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.  With a mask, its base-2
@@ -337,7 +359,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
       s[qb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < DC; ++kc)
-        s[qb] = N::mfma(read_rows<D>(ra, qb * 32 + l32, kc, hl), bf[kc], s[qb]);
+        s[qb] = N::mfma(read_rows<DP>(ra, qb * 32 + l32, kc, hl), bf[kc], s[qb]);
     }
     u32x4 bop[NKC];
     if (pw) {
@@ -379,7 +401,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
       const int row = kc * 16 + v_key;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = N::mfma(read_cols<D>(rb, row, db, v_d, v_sw), bop[kc], acc[db]);
+        acc[db] = N::mfma(read_cols<DP>(rb, row, db, v_d, v_sw), bop[kc], acc[db]);
     }
   };
 
@@ -425,10 +447,10 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4) 
 template <int D, class Tag, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   constexpr int NW = 4, BM = NW * 32, BN = 32;
-  constexpr int DC = D / 16, NDB = D / 32, CPR = D / 8;
-  constexpr int TILE = BN * D;
-  constexpr int IPW = BN * CPR / 64 / NW;
-  static_assert(IPW >= 1 && IPW * 64 * NW == BN * CPR, "tile copy shape");
+  constexpr int DP = compute_dim(D);
+  constexpr int DC = DP / 16, NDB = DP / 32;
+  constexpr int TILE = BN * DP;
+  constexpr int IPW = TileCopy<D, BN, NW>::PER_WAVE;
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kr[2][TILE];
@@ -458,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int kc = 0; kc < DC; ++kc) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (qrow < p.Nq) {
+    if (qrow < p.Nq && kc * 16 + hl * 8 < D) {
       x = *(const u32x4*)(p.q + (qrow0 + qrow) * D + kc * 16 + hl * 8);
       y = *(const u32x4*)(p.dout + (qrow0 + qrow) * D + kc * 16 + hl * 8);
     }
@@ -472,21 +494,21 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
   uint32_t roff[IPW], toff[IPW];
-  copy_offsets<D, IPW, true>(wave, lane, roff);
-  copy_offsets<D, IPW, false>(wave, lane, toff);
+  copy_offsets<D, BN, NW, true>(wave, lane, roff);
+  copy_offsets<D, BN, NW, false>(wave, lane, toff);
   const uint16_t* Kg = p.k + krow0 * D;
   const uint16_t* Vg = p.v + krow0 * D;
   auto issue = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    copy_tile<D, IPW, BN>(Kg, t * BN, p.Nkv, kr[buf], wave, roff);
-    copy_tile<D, IPW, BN>(Kg, t * BN, p.Nkv, ktr[buf], wave, toff);
-    copy_tile<D, IPW, BN>(Vg, t * BN, p.Nkv, vr[buf], wave, roff);
+    copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, kr[buf], wave, roff);
+    copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, ktr[buf], wave, toff);
+    copy_tile<D, BN, NW>(Vg, t * BN, p.Nkv, vr[buf], wave, roff);
   };
 
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
-  const int v_sw = v_swz<D>(v_key);
+  const int v_sw = v_swz<DP>(v_key);
 
   // register e of the score tile is key t*BN + 8 (e / 4) + 4 hl + e % 4.
   // With a mask, its base-2 bias joins the exponent; rows past Nq and rows
@@ -525,8 +547,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < DC; ++kc) {
-      s = N::mfma(read_rows<D>(kr[buf], l32, kc, hl), qf[kc], s);
-      dp = N::mfma(read_rows<D>(vr[buf], l32, kc, hl), gf[kc], dp);
+      s = N::mfma(read_rows<DP>(kr[buf], l32, kc, hl), qf[kc], s);
+      dp = N::mfma(read_rows<DP>(vr[buf], l32, kc, hl), gf[kc], dp);
     }
     if (CAUSAL && t * BN + 31 > qw0 + p.coff)
       probs(std::true_type{}, s, dp, t);
@@ -539,7 +561,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
       const int row = kc * 16 + v_key;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dq[db] = N::mfma(read_cols<D>(ktr[buf], row, db, v_d, v_sw), ps[kc], dq[db]);
+        dq[db] = N::mfma(read_cols<DP>(ktr[buf], row, db, v_d, v_sw), ps[kc], dq[db]);
     }
   };
 
@@ -565,7 +587,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
-  if (D != 64 && D != 128) return ATTN_EINVAL;
+  if (D != 64 && D != 80 && D != 96 && D != 128) return ATTN_EINVAL;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
   if (!isfinite(scale)) return ATTN_EINVAL;
@@ -626,7 +648,7 @@ int validate_bwd_mask(const BwdMask& m, const void* dq, const void* dk, const vo
 template <int D, class Tag, bool MASKED>
 hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   const int rows = p.B * p.Hq * p.Nq;
-  const size_t threads = (size_t)rows * (D / 8);
+  const size_t threads = (size_t)rows * (D / 8 <= 8 ? 8 : 16);  // the delta kernel's lanes per row
   hipLaunchKernelGGL((attn_delta_kernel<D, Tag>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, st, p, rows);
   hipError_t e = hipGetLastError();
@@ -659,6 +681,23 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
     hipLaunchKernelGGL((attn_dq_kernel<D, Tag, false, MASKED>), dim3(pq.total), dim3(256), 0, st,
                        pq);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_masks(bool bf, bool masked, const BwdParams& p, bool cz, hipStream_t st) {
+  if (masked)
+    return bf ? launch_bwd<D, TagBF16, true>(p, cz, st) : launch_bwd<D, TagF16, true>(p, cz, st);
+  return bf ? launch_bwd<D, TagBF16, false>(p, cz, st) : launch_bwd<D, TagF16, false>(p, cz, st);
+}
+
+hipError_t launch_bwd_d(int D, bool bf, bool masked, const BwdParams& p, bool cz,
+                        hipStream_t st) {
+  switch (D) {
+    case 64: return launch_bwd_masks<64>(bf, masked, p, cz, st);
+    case 80: return launch_bwd_masks<80>(bf, masked, p, cz, st);
+    case 96: return launch_bwd_masks<96>(bf, masked, p, cz, st);
+    default: return launch_bwd_masks<128>(bf, masked, p, cz, st);
+  }
 }
 
 int run_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -720,20 +759,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* out, const 
   p.msb = m.sb, p.msh = m.sh, p.msq = m.sq;
   p.mask_mode = m.type;
   const bool cz = causal != 0, bf = dtype == ATTN_BF16;
-  if (m.type != ATTN_MASK_NONE) {
-    if (D == 64)
-      e = bf ? launch_bwd<64, TagBF16, true>(p, cz, st) : launch_bwd<64, TagF16, true>(p, cz, st);
-    else
-      e = bf ? launch_bwd<128, TagBF16, true>(p, cz, st)
-             : launch_bwd<128, TagF16, true>(p, cz, st);
-  } else {
-    if (D == 64)
-      e = bf ? launch_bwd<64, TagBF16, false>(p, cz, st)
-             : launch_bwd<64, TagF16, false>(p, cz, st);
-    else
-      e = bf ? launch_bwd<128, TagBF16, false>(p, cz, st)
-             : launch_bwd<128, TagF16, false>(p, cz, st);
-  }
+  e = launch_bwd_d(D, bf, m.type != ATTN_MASK_NONE, p, cz, st);
   const hipError_t ef = hipFreeAsync(ws, st);
   if (e == hipSuccess) e = ef;
   if (e != hipSuccess) {

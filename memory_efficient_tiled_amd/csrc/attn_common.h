@@ -123,6 +123,14 @@ __device__ __forceinline__ float mask_bias1(const uint8_t* mask, int mode, int64
   return lo_f32<Tag>(h) * kLog2e;
 }
 
+// Columns the matrix products run over for head dimension D: D itself,
+// except that D = 80 (not a whole number of 32-column output blocks) is
+// computed as 96 with the last two 16-byte chunks of every row zero.
+constexpr int compute_dim(int D) { return D == 80 ? 96 : D; }
+
+// A buffer offset past every tile's buffer size: such a copy reads zeros.
+constexpr uint32_t kPadOffset = 0x80000000u;
+
 // Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
 // so that each XCD receives a contiguous range of logical tiles: the query
 // tiles of one head then share that XCD's L2 for their K/V stream.

@@ -56,11 +56,6 @@ namespace attn_fwd_detail {
 // fails it (and on the first tile, where m is still -inf).
 constexpr float kMaxPartialSum = 256.0f;
 
-// Columns the products run over for head dimension D (see attn_fwd_kernel).
-constexpr int compute_dim(int D) { return D == 80 ? 96 : D; }
-
-// A buffer offset past every tile's buffer size: such a copy reads zeros.
-constexpr uint32_t kPadOffset = 0x80000000u;
 
 struct Params {
   const uint16_t* q;

@@ -267,3 +267,30 @@ def test_sdpa_masked_autograd(gpu_device):
         check_grad(name, _host(leaf.grad), r, dtype, "sdpa masked autograd", None,
                    2e-3 * float(np.sqrt(np.mean(r ** 2))))
     assert torch.all(leaves[1].grad[1, :, 100:] == 0) and torch.all(leaves[2].grad[1, :, 100:] == 0)
+
+
+@pytest.mark.parametrize("D", [80, 96])
+@pytest.mark.parametrize("causal", [False, True, "bottom_right"])
+def test_head_dims_80_96(gpu_device, D, causal):
+    # D = 80 runs the D = 96 kernels with two zero chunks per row
+    run_case(gpu_device, 1, 6, 2, 211, 300, D, inputs.BF16 if D == 96 else inputs.F16,
+             causal, seed=D + 3)
+
+
+def test_masked_gradients_d96(gpu_device):
+    import torch
+    dtype = inputs.F16
+    x = inputs.make_inputs(1, 2, 2, 130, 140, 96, dtype, seed=97)
+    do = inputs.make_dout(x)
+    keep = np.random.Generator(np.random.PCG64(98)).random((130, 140)) < 0.75
+    mt = torch.from_numpy(keep).to(gpu_device)
+    q, k, v, g = (to_device(a, dtype, gpu_device) for a in (x.q, x.k, x.v, do))
+    out, lse = binding.attn_fwd(q, k, v, mask=mt)
+    dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, g, mask=mt)
+    torch.cuda.synchronize(gpu_device)
+    bias = np.broadcast_to(np.where(keep, 0.0, -np.inf), (1, 2, 130, 140))
+    dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
+    ref = oracle.attention_backward(*dec, oracle.scale_value(None, 96), False, bias=bias)
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_grad(name, _host(got), r, dtype, "masked D=96", None,
+                   2e-3 * float(np.sqrt(np.mean(r ** 2))))

@@ -76,8 +76,8 @@ def test_tensor_masks_are_served():
     g = t(2, 4, 100, 64).requires_grad_()   # masked gradients: served
     assert reason(g, g, g, attn_mask=t(100, 100, dtype=torch.bool)) == \
         "inputs must be on one HIP device"
-    g96 = t(2, 4, 100, 96).requires_grad_()
-    assert "gradients" in reason(g96, g96, g96, attn_mask=t(100, 100, dtype=torch.bool))
+    g256 = t(2, 4, 100, 256).requires_grad_()
+    assert "gradients" in reason(g256, g256, g256, attn_mask=t(100, 100, dtype=torch.bool))
 
 
 def test_mask_view_broadcasts_without_copies():
