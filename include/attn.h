@@ -261,8 +261,8 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
  * dq       : [B,Hq,Nq,D]; dk, dv: [B,Hkv,Nkv,D]; same dtype, written
  *            completely (no accumulation into their previous contents);
  *            must not overlap each other or any input.
- * All pointers 16-byte aligned; D in {64, 80, 96, 128} (the forward also
- * takes 256, whose gradients are not built); Hq a multiple of Hkv.
+ * All pointers 16-byte aligned; D in {64, 80, 96, 128, 256}; Hq a multiple
+ * of Hkv.
  * Allocates a float32 [B,Hq,Nq] workspace (Delta) on `stream` with
  * hipMallocAsync and frees it there.  Returns ATTN_OK, ATTN_EINVAL,
  * ATTN_EUNSUPPORTED, ATTN_ENOMEM or ATTN_EHIP.  Results are deterministic
@@ -278,7 +278,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out,
  * (attn_fwd_masked with the same mask, mask_type and mask_stride, whose
  * conditions apply): the mask enters the recomputed probabilities and is
  * not differentiated.  Rows the mask (or a causal mode) leaves with no key
- * get zero gradients.  D in {64, 80, 96, 128}.
+ * get zero gradients.
  */
 int attn_bwd_masked(const void* q, const void* k, const void* v, const void* out,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,

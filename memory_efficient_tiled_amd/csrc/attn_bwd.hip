@@ -67,12 +67,15 @@ struct BwdParams {
   int mask_mode;
 };
 
+// Lanes per row of the delta kernel: D / 8 rounded up to a power of two.
+constexpr int bwd_delta_lanes(int D) { return D / 8 <= 8 ? 8 : D / 8 <= 16 ? 16 : 32; }
+
 // Delta_r = sum_d dO[r, d] O[r, d] in fp32: L lanes per row (D / 8 rounded
 // up to a power of two; lanes past the row add nothing), one 16-byte load of
 // each tensor per lane, a butterfly over the row's lanes.
 template <int D, class Tag>
 __global__ __launch_bounds__(256) void attn_delta_kernel(BwdParams p, int rows) {
-  constexpr int L = D / 8 <= 8 ? 8 : 16;  // lanes per row
+  constexpr int L = bwd_delta_lanes(D);  // lanes per row
   static_assert(D / 8 <= L, "row fits its lanes");
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int row = gid / L, part = gid % L;
@@ -218,7 +221,10 @@ __device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst,
 // buffers deep, with lse2 and Delta.
 template <int D, class Tag, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
-  constexpr int NW = 8, BK = 128, BQ = 64, NQB = 2;
+  // 64-row query tiles; 32 at D = 256, whose K (or V) operands and dK (or
+  // dV) accumulators alone take 192 registers
+  constexpr int NQB = D == 256 ? 1 : 2;
+  constexpr int NW = 8, BK = 128, BQ = NQB * 32;
   constexpr int DP = compute_dim(D);
   constexpr int DC = DP / 16, NDB = DP / 32, NKC = BQ / 16;
   constexpr int TILE = BQ * DP;
@@ -230,8 +236,10 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t gr[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gt[2][TILE];
   __shared__ __attribute__((aligned(1024))) u32x4 xp[4][NKC][64];
-  __shared__ __attribute__((aligned(256))) float lse_s[2][BQ];
-  __shared__ __attribute__((aligned(256))) float del_s[2][BQ];
+  // lse2 and Delta of a tile: one dword per lane of a 64-lane copy (lanes
+  // past the tile's rows write zeros), so 64 entries even when BQ = 32
+  __shared__ __attribute__((aligned(256))) float lse_s[2][64];
+  __shared__ __attribute__((aligned(256))) float del_s[2][64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -444,8 +452,10 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4) 
 //   dQ^T += K^T dS^T                (rows: D, columns: 32 queries)
 // Q and dO stay in registers; K is copied into LDS twice (row-read and
 // transposed layouts) and V once, two buffers deep, the loop unrolled by two.
+// One wave per SIMD at D = 256: Q, dO and the dQ accumulators take 256
+// registers.
 template <int D, class Tag, bool CAUSAL, bool MASKED>
-__global__ __launch_bounds__(256, 2) void attn_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParams p) {
   constexpr int NW = 4, BM = NW * 32, BN = 32;
   constexpr int DP = compute_dim(D);
   constexpr int DC = DP / 16, NDB = DP / 32;
@@ -587,7 +597,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
-  if (D != 64 && D != 80 && D != 96 && D != 128) return ATTN_EINVAL;
+  if (D != 64 && D != 80 && D != 96 && D != 128 && D != 256) return ATTN_EINVAL;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
   if (!isfinite(scale)) return ATTN_EINVAL;
@@ -648,7 +658,7 @@ int validate_bwd_mask(const BwdMask& m, const void* dq, const void* dk, const vo
 template <int D, class Tag, bool MASKED>
 hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   const int rows = p.B * p.Hq * p.Nq;
-  const size_t threads = (size_t)rows * (D / 8 <= 8 ? 8 : 16);  // the delta kernel's lanes per row
+  const size_t threads = (size_t)rows * bwd_delta_lanes(D);
   hipLaunchKernelGGL((attn_delta_kernel<D, Tag>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, st, p, rows);
   hipError_t e = hipGetLastError();
@@ -696,6 +706,7 @@ hipError_t launch_bwd_d(int D, bool bf, bool masked, const BwdParams& p, bool cz
     case 64: return launch_bwd_masks<64>(bf, masked, p, cz, st);
     case 80: return launch_bwd_masks<80>(bf, masked, p, cz, st);
     case 96: return launch_bwd_masks<96>(bf, masked, p, cz, st);
+    case 256: return launch_bwd_masks<256>(bf, masked, p, cz, st);
     default: return launch_bwd_masks<128>(bf, masked, p, cz, st);
   }
 }

@@ -91,9 +91,6 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
                     return "attn_mask does not broadcast to the scores' shape"
             if attn_mask.device != query.device:
                 return "attn_mask must be on the inputs' device"
-            if (torch.is_grad_enabled() and any(t.requires_grad for t in ts)
-                    and query.shape[-1] == 256):
-                return "gradients are built for head dimensions 64, 80, 96 and 128"
         else:
             return "attn_mask must be a tensor or one of PyTorch's causal biases"
     if dropout_p != 0.0:
@@ -106,8 +103,6 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
     E = query.shape[-1]
     if E not in (64, 80, 96, 128, 256) or key.shape[-1] != E or value.shape[-1] != E:
         return "head dimension must be 64, 80, 96, 128 or 256 for query, key and value"
-    if E == 256 and torch.is_grad_enabled() and any(t.requires_grad for t in ts):
-        return "gradients are built for head dimensions 64, 80, 96 and 128"
     if key.shape != value.shape:
         return "key and value must have one shape"
     if query.shape[:-3] != key.shape[:-3]:

@@ -294,3 +294,9 @@ def test_masked_gradients_d96(gpu_device):
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         check_grad(name, _host(got), r, dtype, "masked D=96", None,
                    2e-3 * float(np.sqrt(np.mean(r ** 2))))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256(gpu_device, causal):
+    # 32-row query tiles in the dK/dV kernel, one wave per SIMD in the dQ kernel
+    run_case(gpu_device, 1, 4, 2, 200, 260, 256, inputs.BF16, causal, seed=256)
