@@ -40,6 +40,12 @@ Readings where the pages are silent (listed again in the design notes):
     approach");
   * scale defaults to 1/sqrt(D) (the ai-manual.ru snippet divides by
     sqrt(dim)); it is used as the float32 value the GPU receives;
+  * V rows may be wider or narrower than Q and K rows (Dv != D): nothing in
+    the definition ties them together, each output column is the weighted
+    sum of one V column, and PyTorch's SDPA (the API the post patches) takes
+    such V.  The pages' own snippet allocates the output like the query
+    (ai-manual.ru, section 3), which assumes Dv = D; D alone sets the
+    default scale;
   * no epsilon in the denominator (the ai-manual.ru snippet adds 1e-8; after
     max subtraction the row sum is >= 1, so it is left out) and no flush-to-
     zero threshold (the post's fp16 workaround): the oracle is exact.
@@ -99,19 +105,20 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
               bias: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
     """Exact softmax attention in float64.
 
-    q: [B, Hq, Nq, D], k and v: [B, Hkv, Nkv, D], all float64.
+    q: [B, Hq, Nq, D], k: [B, Hkv, Nkv, D], v: [B, Hkv, Nkv, Dv], float64.
     rows: None (all Nq rows) or int array [Hq, R] or [R] of query rows.
     causal_offset: with ``causal``, row i sees keys j <= i + causal_offset.
     bias: None or float64 broadcastable to [B, Hq, Nq, Nkv], added to the
     scaled scores (-inf removes a key).
-    Returns (o [B, Hq, R, D], lse [B, Hq, R]) in float64, natural log.
+    Returns (o [B, Hq, R, Dv], lse [B, Hq, R]) in float64, natural log.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Nq, D = q.shape
     Bk, Hkv, Nkv, Dk = k.shape
-    if v.shape != k.shape or Bk != B or Dk != D:
+    Dv = v.shape[3]
+    if v.shape[:3] != k.shape[:3] or Bk != B or Dk != D:
         raise ValueError("shape mismatch between q, k and v")
     if Hkv <= 0 or Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
@@ -122,7 +129,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         rows = np.asarray(rows, dtype=np.int64)
         rows_h = np.tile(rows, (Hq, 1)) if rows.ndim == 1 else rows
     R = rows_h.shape[1]
-    o = np.empty((B, Hq, R, D), dtype=np.float64)
+    o = np.empty((B, Hq, R, Dv), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
     key_idx = np.arange(Nkv, dtype=np.int64)
     if bias is not None:

@@ -428,9 +428,49 @@ def pin_mask_bias_shift(attn):
     _close(l2, l3, what="log-weight bias lse")
 
 
+def pin_value_width_torch(attn):
+    """V rows of another width than Q and K (Dv != D): PyTorch CPU SDPA in
+    float64 (its math path takes such V), non-causal, top-left causal and
+    grouped KV heads."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(40)
+    for B, Hq, Hkv, Nq, Nkv, D, Dv, causal in [(1, 2, 2, 9, 13, 12, 8, False),
+                                               (2, 4, 2, 11, 11, 8, 20, True),
+                                               (1, 3, 1, 7, 19, 24, 16, True)]:
+        q = rng.standard_normal((B, Hq, Nq, D))
+        k = rng.standard_normal((B, Hkv, Nkv, D))
+        v = rng.standard_normal((B, Hkv, Nkv, Dv))
+        scale = 1.0 / math.sqrt(D)
+        kt, vt = (torch.from_numpy(np.repeat(a, Hq // Hkv, axis=1)) for a in (k, v))
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), kt, vt, is_causal=causal,
+                                             scale=scale).numpy()
+        o, lse = attn(q, k, v, scale, causal)
+        assert o.shape == (B, Hq, Nq, Dv), f"output shape {o.shape}"
+        _close(o, ref, tol=1e-11, what=f"Dv={Dv} vs D={D} against torch")
+        _, lse_d = attn(q, k, np.ones((B, Hkv, Nkv, D)), scale, causal)
+        _close(lse, lse_d, tol=1e-13, what="lse must not depend on V")
+
+
+def pin_value_width_columns(attn):
+    """Each output column depends on its own V column only: attention with
+    V = [V1 V2] is [attention with V1, attention with V2]."""
+    rng = _rng(41)
+    q = rng.standard_normal((1, 2, 10, 8))
+    k = rng.standard_normal((1, 2, 15, 8))
+    v = rng.standard_normal((1, 2, 15, 24))
+    for causal in (False, True):
+        o, lse = attn(q, k, v, 0.4, causal)
+        o1, l1 = attn(q, k, v[..., :16], 0.4, causal)
+        o2, l2 = attn(q, k, v[..., 16:], 0.4, causal)
+        _close(o, np.concatenate([o1, o2], axis=-1), tol=1e-13, what="V column split")
+        _close(lse, l1, tol=1e-13, what="lse with part of V")
+        _close(lse, l2, tol=1e-13, what="lse with the other part of V")
+
+
 ALL_PINS = [pin_bruteforce, pin_torch_sdpa, pin_golden, pin_q_zero, pin_v_const,
             pin_causal_row0, pin_single_key, pin_dominant_key, pin_key_shift,
             pin_kv_permutation, pin_query_permutation, pin_gqa_repeat,
             pin_linear_in_v, pin_convex_hull, pin_rows_subset,
             pin_causal_offset_torch, pin_causal_offset_shift, pin_mask_torch,
-            pin_mask_bias_shift]
+            pin_mask_bias_shift, pin_value_width_torch, pin_value_width_columns]

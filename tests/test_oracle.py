@@ -50,6 +50,9 @@ MUTANTS = [
     ("bias ignored", "s = s + bias[b, hq, ri]", "s = s + 0.0"),
     ("bias before the scale", "s = s + bias[b, hq, ri]", "s = s + scale * bias[b, hq, ri]"),
     ("bias of the wrong head", "s = s + bias[b, hq, ri]", "s = s + bias[b, hq // G, ri]"),
+    ("output sized by the query's width", "o = np.empty((B, Hq, R, Dv)",
+     "o = np.empty((B, Hq, R, D)"),
+    ("V columns of another head", "vv = v[b, hk]", "vv = v[b, (hk + 1) % Hkv]"),
 ]
 
 
