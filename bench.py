@@ -145,7 +145,7 @@ def main():
         return t.view(torch.bfloat16) if w.dtype == "bf16" else t
 
     q, k, v = up(x.q), up(x.k), up(x.v)
-    out = torch.empty_like(q)
+    out = torch.empty((w.B, w.Hq, w.Nq, w.Dv), dtype=q.dtype, device=dev)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     dcode = ATTN_BF16 if w.dtype == "bf16" else ATTN_F16
     splits = args.splits or attn_fwd_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
@@ -218,7 +218,7 @@ def main():
         "config": {"workload": f"{name}: {w.note}, {w.describe()}",
                    "pass": args.pass_,
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv,
-                   "D": w.D, "causal": w.causal, "scale": w.scale, "seed": args.seed,
+                   "D": w.D, "Dv": w.Dv, "causal": w.causal, "scale": w.scale, "seed": args.seed,
                    "k_offset_std": w.k_offset_std,
                    "split_kv": None if bwd else splits,
                    "kernel_source": source_hash(args.pass_)},
@@ -244,7 +244,7 @@ def cpu_leg_fwd(result, x, w, name, out, lse, np, oracle):
     sc = oracle.scale_value(w.scale, w.D)
     G = w.Hq // w.Hkv
     c0 = time.perf_counter()
-    o_ref = np.empty((w.B, w.Hq, x.rows.shape[1], w.D))
+    o_ref = np.empty((w.B, w.Hq, x.rows.shape[1], w.Dv))
     l_ref = np.empty((w.B, w.Hq, x.rows.shape[1]))
     for b in range(w.B):
         for hk in range(w.Hkv):
@@ -258,10 +258,10 @@ def cpu_leg_fwd(result, x, w, name, out, lse, np, oracle):
     cpu_s = time.perf_counter() - c0
     rows = x.rows
     if w.causal:
-        sample_flops = float(sum(4.0 * w.D * np.minimum(r + 1, w.Nkv).sum()
+        sample_flops = float(sum(2.0 * (w.D + w.Dv) * np.minimum(r + 1, w.Nkv).sum()
                                  for r in rows)) * w.B
     else:
-        sample_flops = 4.0 * w.D * w.Nkv * rows.size * w.B
+        sample_flops = 2.0 * (w.D + w.Dv) * w.Nkv * rows.size * w.B
     o_s, l_s = gather_rows(o_gpu, rows), gather_rows(l_gpu, rows)
     err = np.abs(o_s - o_ref)
     result["parity"] = {"rows_per_head": int(rows.shape[1]),

@@ -199,6 +199,41 @@ int attn_fwd_masked_check(const void* q, const void* k, const void* v,
                           int causal, int dtype);
 
 /*
+ * attn_fwd_dv -- attn_fwd_masked with value and output rows of Dv elements
+ * while Q and K rows keep D.  Nothing in the definition above ties the width
+ * of V to that of Q and K: the scores use D, and each output column is the
+ * softmax-weighted sum of one V column (PyTorch's
+ * scaled_dot_product_attention, the API the post patches, takes such V;
+ * section "Other areas where this could be useful").  Supported: Dv == D
+ * for every D above (the call is then attn_fwd_masked's), and the pair
+ * D = 192, Dv = 128 (multi-head latent attention at prefill).
+ *
+ * V is [B,Hkv,Nkv,Dv] and `out` [B,Hq,Nq,Dv]; v_stride and o_stride are
+ * their element strides (sequence strides in [Dv, 2^24]; NULL =
+ * contiguous).  mask, mask_type and mask_stride are as for
+ * attn_fwd_masked (ATTN_MASK_NONE, with NULL mask and mask_stride, for no
+ * mask).  Split calls allocate fp32 partials of Dv columns.  Returns as
+ * attn_fwd; an unsupported (D, Dv) pair is ATTN_EINVAL.
+ */
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* out,
+                float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                int Dv, const long long* q_stride, const long long* k_stride,
+                const long long* v_stride, const long long* o_stride,
+                const void* mask, int mask_type, const long long* mask_stride,
+                float scale, int causal, int dtype, int num_splits,
+                void* stream);
+
+/* attn_fwd_dv_check -- host only: attn_fwd_dv's validation. */
+int attn_fwd_dv_check(const void* q, const void* k, const void* v,
+                      const void* out, const float* lse, int B, int Hq, int Hkv,
+                      int Nq, int Nkv, int D, int Dv,
+                      const long long* q_stride, const long long* k_stride,
+                      const long long* v_stride, const long long* o_stride,
+                      const void* mask, int mask_type,
+                      const long long* mask_stride, float scale, int causal,
+                      int dtype);
+
+/*
  * attn_plan -- how attn_fwd_split covers a shape (see attn_fwd_plan).
  * Output rows are numbered (b * Hq + h) * Nq + i, 0 <= r < B*Hq*Nq.
  */
@@ -215,16 +250,19 @@ typedef struct attn_plan {
 /*
  * attn_fwd_plan -- host only: fills *plan with what attn_fwd_split (same
  * num_splits; 0 = as attn_fwd) does for this shape on a device with
- * `num_cus` compute units (256 on MI355X; <= 0 means 256).  Returns ATTN_OK,
- * or ATTN_EINVAL for invalid shapes, a negative num_splits or a NULL plan.
+ * `num_cus` compute units (256 on MI355X; <= 0 means 256).  D = 192 stands
+ * for attn_fwd_dv's (192, 128) pair (partials of 128 columns).  Returns
+ * ATTN_OK, or ATTN_EINVAL for invalid shapes, a negative num_splits or a
+ * NULL plan.
  */
 int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal,
                   int dtype, int num_splits, int num_cus, attn_plan* plan);
 
 /*
  * attn_fwd_num_splits -- host only: attn_fwd_plan(..., 0, num_cus)'s
- * num_splits, the split-KV count attn_fwd uses for the tiles it splits.
- * Returns >= 1, or ATTN_EINVAL for invalid shapes.
+ * num_splits, the split-KV count attn_fwd uses for the tiles it splits
+ * (D = 192: attn_fwd_dv's (192, 128) pair).  Returns >= 1, or ATTN_EINVAL
+ * for invalid shapes.
  */
 int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                         int causal, int dtype, int num_cus);
@@ -233,7 +271,8 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D,
  * attn_fwd_workspace_bytes -- host only: device bytes for splitting every
  * row into `num_splits` pieces (0 when num_splits <= 1): fp32 partial
  * outputs [num_splits,B,Hq,Nq,D] and partial LSE [num_splits,B,Hq,Nq].  An
- * upper bound of attn_plan.workspace_bytes for the same num_splits.
+ * upper bound of attn_plan.workspace_bytes for the same num_splits.  For
+ * attn_fwd_dv pass the value head dimension Dv as D.
  */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
                                 int num_splits);

@@ -93,6 +93,13 @@ def load_library():
     lib.attn_fwd_masked_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
         [_LLP] * 4 + [_VP, _INT, _LLP, ctypes.c_float, _INT, _INT]
     lib.attn_fwd_masked_check.restype = _INT
+    shape_dv = shape_args + [_INT]             # ..., D, Dv
+    lib.attn_fwd_dv.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_dv + \
+        [_LLP] * 4 + [_VP, _INT, _LLP, ctypes.c_float, _INT, _INT, _INT, _VP]
+    lib.attn_fwd_dv.restype = _INT
+    lib.attn_fwd_dv_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_dv + \
+        [_LLP] * 4 + [_VP, _INT, _LLP, ctypes.c_float, _INT, _INT]
+    lib.attn_fwd_dv_check.restype = _INT
     lib.attn_fwd_plan.argtypes = shape_args + [_INT, _INT, _INT, _INT,
                                                ctypes.POINTER(AttnPlan)]
     lib.attn_fwd_plan.restype = _INT
@@ -237,10 +244,11 @@ def attn_fwd(q, k, v, causal=False, scale: float | None = None,
     the inputs' dtype: added to the scaled scores), broadcastable to
     [B, Hq, Nq, Nkv].
 
-    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; same dtype (float16 or
-    bfloat16), on one HIP device, any strides with the last dimension
-    contiguous (e.g. [B, N, H, D] storage viewed as [B, H, N, D]).  Returns
-    (out, lse) with out [B, Hq, Nq, D] (new tensors are contiguous; a given
+    q: [B, Hq, Nq, D]; k: [B, Hkv, Nkv, D]; v: [B, Hkv, Nkv, Dv] with Dv = D,
+    or (D, Dv) = (192, 128); same dtype (float16 or bfloat16), on one HIP
+    device, any strides with the last dimension contiguous (e.g. [B, N, H, D]
+    storage viewed as [B, H, N, D]).  Returns
+    (out, lse) with out [B, Hq, Nq, Dv] (new tensors are contiguous; a given
     ``out`` may be strided) and lse float32 [B, Hq, Nq] (natural log), or
     just out when ``return_lse`` is False.  ``num_splits`` = 0 lets the
     library choose the split-KV count; a positive value forces it.  Runs on
@@ -261,16 +269,17 @@ def attn_fwd(q, k, v, causal=False, scale: float | None = None,
         raise ValueError("q, k and v must be on one device")
     B, Hq, Nq, D = q.shape
     Bk, Hkv, Nkv, Dk = k.shape
-    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+    Dv = v.shape[3]
+    if tuple(v.shape[:3]) != tuple(k.shape[:3]) or Bk != B or Dk != D:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
                          f"v{tuple(v.shape)}")
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
-    elif tuple(out.shape) != (B, Hq, Nq, D) or out.dtype != q.dtype or out.device != q.device:
-        raise ValueError("out must be [B, Hq, Nq, D] with the dtype and device of q")
+        out = torch.empty((B, Hq, Nq, Dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, Hq, Nq, Dv) or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must be [B, Hq, Nq, Dv] with the dtype and device of q")
     if return_lse:
         if lse is None:
             lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
@@ -281,7 +290,18 @@ def attn_fwd(q, k, v, causal=False, scale: float | None = None,
     qs, ks, vs, os_ = strides3(q), strides3(k), strides3(v), strides3(out)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if mask is None:
+        if Dv != D:
+            m, mtype, ms = None, ATTN_MASK_NONE, None
+            if mask is not None:
+                if mask.device != q.device:
+                    raise ValueError("mask must be on q's device")
+                m, mtype, ms = mask_view(mask, B, Hq, Nq, Nkv, q.dtype)
+            rc = lib.attn_fwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D, Dv,
+                                 qs, ks, vs, os_, None if m is None else m.data_ptr(),
+                                 mtype, ms, float(scale), causal_code(causal), dt,
+                                 int(num_splits), stream)
+        elif mask is None:
             rc = lib.attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                       out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
                                       qs, ks, vs, os_, float(scale), causal_code(causal), dt,

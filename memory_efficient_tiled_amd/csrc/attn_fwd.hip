@@ -14,6 +14,7 @@ using namespace attn_fwd_detail;
 // The wide tiles of each head dimension are used without a causal mask when
 // they still fill every slot of the device at least once.
 int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
+  if (D == 192) return kCfgD192;
   if (D == 256) return kCfgD256;
   if (D == 96 || D == 80) return kCfgD96;
   const int narrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
@@ -27,6 +28,10 @@ int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
 thread_local int g_last_hip_error = 0;
 
 bool head_dim_ok(int D) { return D == 64 || D == 80 || D == 96 || D == 128 || D == 256; }
+
+// Head dimensions of Q/K (D) and V/O (Dv): equal and supported, or the
+// (192, 128) pair.
+bool head_dims_ok(int D, int Dv) { return Dv == D ? head_dim_ok(D) : (D == 192 && Dv == 128); }
 
 struct DeviceInfo {
   bool init = false;
@@ -70,10 +75,12 @@ struct Layout {
   Strides q, k, v, o;
 };
 
-Layout contiguous_layout(int Hq, int Hkv, int Nq, int Nkv, int D) {
+Layout contiguous_layout(int Hq, int Hkv, int Nq, int Nkv, int D, int Dv) {
   const Strides qs{(int64_t)Hq * Nq * D, (int64_t)Nq * D, D};
   const Strides ks{(int64_t)Hkv * Nkv * D, (int64_t)Nkv * D, D};
-  return Layout{qs, ks, ks, qs};
+  const Strides vs{(int64_t)Hkv * Nkv * Dv, (int64_t)Nkv * Dv, Dv};
+  const Strides os{(int64_t)Hq * Nq * Dv, (int64_t)Nq * Dv, Dv};
+  return Layout{qs, ks, vs, os};
 }
 
 // Bytes from a tensor's base to the end of its last element.
@@ -123,11 +130,11 @@ struct MaskArgs {
 };
 
 int validate(const void* q, const void* k, const void* v, const void* out, const float* lse,
-             int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+             int B, int Hq, int Hkv, int Nq, int Nkv, int D, int Dv, float scale, int causal,
              int dtype, const Layout& L, const MaskArgs& M = MaskArgs()) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
-  if (!head_dim_ok(D)) return ATTN_EINVAL;
+  if (!head_dims_ok(D, Dv)) return ATTN_EINVAL;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
   if (!isfinite(scale)) return ATTN_EINVAL;
@@ -138,11 +145,12 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
   const size_t rows = (size_t)B * Hq * Nq;
   const size_t krows = (size_t)B * Hkv * Nkv;
   if (rows > (size_t)INT32_MAX || krows > (size_t)INT32_MAX) return ATTN_EINVAL;
-  if (!strides_ok(L.q, D) || !strides_ok(L.k, D) || !strides_ok(L.v, D) || !strides_ok(L.o, D))
+  if (!strides_ok(L.q, D) || !strides_ok(L.k, D) || !strides_ok(L.v, Dv) ||
+      !strides_ok(L.o, Dv))
     return ATTN_EINVAL;
-  if (!dense_enough(L.o, B, Hq, Nq, D)) return ATTN_EINVAL;
-  const __int128 qb = extent_bytes(L.q, B, Hq, Nq, D), ob = extent_bytes(L.o, B, Hq, Nq, D);
-  const __int128 kb = extent_bytes(L.k, B, Hkv, Nkv, D), vb = extent_bytes(L.v, B, Hkv, Nkv, D);
+  if (!dense_enough(L.o, B, Hq, Nq, Dv)) return ATTN_EINVAL;
+  const __int128 qb = extent_bytes(L.q, B, Hq, Nq, D), ob = extent_bytes(L.o, B, Hq, Nq, Dv);
+  const __int128 kb = extent_bytes(L.k, B, Hkv, Nkv, D), vb = extent_bytes(L.v, B, Hkv, Nkv, Dv);
   if (overlaps128(out, ob, q, qb) || overlaps128(out, ob, k, kb) || overlaps128(out, ob, v, vb))
     return ATTN_EINVAL;
   if (lse) {
@@ -173,7 +181,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
 // so their rows are one contiguous range [row0, rows).
 struct Plan {
   int cfg;
-  int D;
+  int Dv;  // width of the fp32 partial rows
   int n_qtiles;
   int splits;
   int split_len;
@@ -181,7 +189,7 @@ struct Plan {
   long long first_split;
   long long row0, rows;
   size_t workspace_bytes() const {
-    return splits > 1 ? (size_t)splits * (size_t)(rows - row0) * (D + 1) * sizeof(float) : 0;
+    return splits > 1 ? (size_t)splits * (size_t)(rows - row0) * (Dv + 1) * sizeof(float) : 0;
   }
 };
 
@@ -189,7 +197,7 @@ struct Plan {
 // pieces on `slots` workgroup slots, in key steps of one workgroup: the
 // pieces run in ceil(s * rem / slots) rounds, each piece spends about
 // kPieceFillSteps steps filling its pipeline and writing fp32 partials, and
-// the merge streams ~8 (D + 1) bytes per row and piece through HBM, about
+// the merge streams ~8 (Dv + 1) bytes per row and piece through HBM, about
 // kMergeStepsPerPiece steps of the whole chip per tile and piece (a 64-key
 // step of a 256-row tile is ~8 MFLOP, ~2 us on one CU).
 constexpr double kPieceFillSteps = 2.0;
@@ -227,11 +235,11 @@ int causal_splits(long long tiles, long long slots, int ktiles) {
 // tile).  Otherwise, without a mask, the grid runs in rounds of `slots`
 // equal workgroups and only the tiles of the last, partial round are cut,
 // so that they finish in a fraction of a round.
-Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int num_cus,
-               bool masked = false) {
+Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int Dv, int causal, int num_splits,
+               int num_cus, bool masked = false) {
   Plan pl;
   pl.cfg = select_cfg(B, Hq, Nq, D, causal || masked, num_cus);
-  pl.D = D;
+  pl.Dv = Dv;
   const TileCfg c = kCfgs[pl.cfg];
   pl.n_qtiles = (Nq + c.BM() - 1) / c.BM();
   pl.tiles = (long long)B * Hq * pl.n_qtiles;
@@ -260,19 +268,22 @@ Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits
   return pl;
 }
 
-hipError_t launch_fwd(int D, const Params& p, int cfg, bool causal, bool split, bool strided,
-                      bool masked, bool bf16, hipStream_t st) {
+hipError_t launch_fwd(int D, int Dv, const Params& p, int cfg, bool causal, bool split,
+                      bool strided, bool masked, bool bf16, hipStream_t st) {
+  if (Dv != D)  // the (192, 128) pair
+    return launch_fwd_d<192, 128>(p, cfg, causal, split, strided, masked, bf16, st);
   switch (D) {
-    case 64: return launch_fwd_d<64>(p, cfg, causal, split, strided, masked, bf16, st);
-    case 80: return launch_fwd_d<80>(p, cfg, causal, split, strided, masked, bf16, st);
-    case 96: return launch_fwd_d<96>(p, cfg, causal, split, strided, masked, bf16, st);
-    case 256: return launch_fwd_d<256>(p, cfg, causal, split, strided, masked, bf16, st);
-    default: return launch_fwd_d<128>(p, cfg, causal, split, strided, masked, bf16, st);
+    case 64: return launch_fwd_d<64, 64>(p, cfg, causal, split, strided, masked, bf16, st);
+    case 80: return launch_fwd_d<80, 80>(p, cfg, causal, split, strided, masked, bf16, st);
+    case 96: return launch_fwd_d<96, 96>(p, cfg, causal, split, strided, masked, bf16, st);
+    case 256: return launch_fwd_d<256, 256>(p, cfg, causal, split, strided, masked, bf16, st);
+    default: return launch_fwd_d<128, 128>(p, cfg, causal, split, strided, masked, bf16, st);
   }
 }
 
-hipError_t launch_combine(int D, const Params& p, bool strided, bool bf16, hipStream_t st) {
-  switch (D) {
+// The merge of split partials, for output rows of Dv elements.
+hipError_t launch_combine(int Dv, const Params& p, bool strided, bool bf16, hipStream_t st) {
+  switch (Dv) {
     case 64: return launch_combine_d<64>(p, strided, bf16, st);
     case 80: return launch_combine_d<80>(p, strided, bf16, st);
     case 96: return launch_combine_d<96>(p, strided, bf16, st);
@@ -282,9 +293,9 @@ hipError_t launch_combine(int D, const Params& p, bool strided, bool bf16, hipSt
 }
 
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
-        int Nq, int Nkv, int D, const Layout& L, float scale, int causal, int dtype,
+        int Nq, int Nkv, int D, int Dv, const Layout& L, float scale, int causal, int dtype,
         int num_splits, hipStream_t stream, const MaskArgs& M = MaskArgs()) {
-  int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype, L, M);
+  int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, Dv, scale, causal, dtype, L, M);
   const bool masked = M.type != ATTN_MASK_NONE;
   if (rc != ATTN_OK) return rc;
   if (num_splits < 0) return ATTN_EINVAL;
@@ -292,7 +303,7 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   rc = device_info(&di);
   if (rc != ATTN_OK) return rc;
 
-  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, causal, num_splits, di.cus, masked);
+  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, Dv, causal, num_splits, di.cus, masked);
   const long long split_wgs = (pl.tiles - pl.first_split) * pl.splits;
   if (pl.first_split > INT32_MAX || split_wgs > INT32_MAX) return ATTN_EINVAL;
 
@@ -339,16 +350,16 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
       return ATTN_ENOMEM;
     }
     p.opart = (float*)ws;
-    p.lsepart = p.opart + (size_t)pl.splits * p.prows * D;
+    p.lsepart = p.opart + (size_t)pl.splits * p.prows * Dv;
   }
 
   const bool cz = causal != 0;
-  const Layout C = contiguous_layout(Hq, Hkv, Nq, Nkv, D);
+  const Layout C = contiguous_layout(Hq, Hkv, Nq, Nkv, D, Dv);
   auto same = [](const Strides& a, const Strides& b) { return a.b == b.b && a.h == b.h && a.n == b.n; };
   const bool strided = !(same(L.q, C.q) && same(L.k, C.k) && same(L.v, C.v) && same(L.o, C.o));
   const bool bf16 = dtype == ATTN_BF16;
   auto launch = [&](bool split) {
-    return launch_fwd(D, p, pl.cfg, cz, split, strided, masked, bf16, stream);
+    return launch_fwd(D, Dv, p, pl.cfg, cz, split, strided, masked, bf16, stream);
   };
 
   hipError_t e = hipSuccess;
@@ -362,7 +373,7 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     p.tile0 = (int)pl.first_split;
     e = launch(true);
     if (e == hipSuccess) {
-      e = launch_combine(D, p, strided, bf16, stream);
+      e = launch_combine(Dv, p, strided, bf16, stream);
     }
   }
   if (ws) {
@@ -392,24 +403,26 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
              int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype, void* stream) {
-  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, contiguous_layout(Hq, Hkv, Nq, Nkv, D),
-             scale, causal, dtype, 0, (hipStream_t)stream);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D,
+             contiguous_layout(Hq, Hkv, Nq, Nkv, D, D), scale, causal, dtype, 0,
+             (hipStream_t)stream);
 }
 
 int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype,
                    int num_splits, void* stream) {
-  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, contiguous_layout(Hq, Hkv, Nq, Nkv, D),
-             scale, causal, dtype, num_splits, (hipStream_t)stream);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D,
+             contiguous_layout(Hq, Hkv, Nq, Nkv, D, D), scale, causal, dtype, num_splits,
+             (hipStream_t)stream);
 }
 
 }  // extern "C"
 
 namespace {
 // Strides from the C arrays (batch, head, sequence); NULL = contiguous.
-Layout strided_layout(int Hq, int Hkv, int Nq, int Nkv, int D, const long long* qs,
+Layout strided_layout(int Hq, int Hkv, int Nq, int Nkv, int D, int Dv, const long long* qs,
                       const long long* ks, const long long* vs, const long long* os) {
-  Layout L = contiguous_layout(Hq, Hkv, Nq, Nkv, D);
+  Layout L = contiguous_layout(Hq, Hkv, Nq, Nkv, D, Dv);
   auto take = [](Strides& s, const long long* a) {
     if (a) s = Strides{a[0], a[1], a[2]};
   };
@@ -428,16 +441,16 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* out, flo
                      const long long* k_stride, const long long* v_stride,
                      const long long* o_stride, float scale, int causal, int dtype,
                      int num_splits, void* stream) {
-  const Layout L = strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride);
-  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, L, scale, causal, dtype, num_splits,
+  const Layout L = strided_layout(Hq, Hkv, Nq, Nkv, D, D, q_stride, k_stride, v_stride, o_stride);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D, L, scale, causal, dtype, num_splits,
              (hipStream_t)stream);
 }
 
 int attn_fwd_check(const void* q, const void* k, const void* v, const void* out, const float* lse,
                    int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
                    int dtype) {
-  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
-                  contiguous_layout(Hq, Hkv, Nq, Nkv, D));
+  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D, scale, causal, dtype,
+                  contiguous_layout(Hq, Hkv, Nq, Nkv, D, D));
 }
 
 int attn_fwd_strided_check(const void* q, const void* k, const void* v, const void* out,
@@ -445,8 +458,8 @@ int attn_fwd_strided_check(const void* q, const void* k, const void* v, const vo
                            const long long* q_stride, const long long* k_stride,
                            const long long* v_stride, const long long* o_stride, float scale,
                            int causal, int dtype) {
-  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
-                  strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride));
+  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D, scale, causal, dtype,
+                  strided_layout(Hq, Hkv, Nq, Nkv, D, D, q_stride, k_stride, v_stride, o_stride));
 }
 
 static MaskArgs mask_args(const void* mask, int mask_type, const long long* mask_stride) {
@@ -471,8 +484,8 @@ int attn_fwd_masked(const void* q, const void* k, const void* v, void* out, floa
                     const long long* o_stride, const void* mask, int mask_type,
                     const long long* mask_stride, float scale, int causal, int dtype,
                     int num_splits, void* stream) {
-  const Layout L = strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride);
-  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, L, scale, causal, dtype, num_splits,
+  const Layout L = strided_layout(Hq, Hkv, Nq, Nkv, D, D, q_stride, k_stride, v_stride, o_stride);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D, L, scale, causal, dtype, num_splits,
              (hipStream_t)stream, mask_args(mask, mask_type, mask_stride));
 }
 
@@ -482,28 +495,55 @@ int attn_fwd_masked_check(const void* q, const void* k, const void* v, const voi
                           const long long* v_stride, const long long* o_stride,
                           const void* mask, int mask_type, const long long* mask_stride,
                           float scale, int causal, int dtype) {
-  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
-                  strided_layout(Hq, Hkv, Nq, Nkv, D, q_stride, k_stride, v_stride, o_stride),
+  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D, scale, causal, dtype,
+                  strided_layout(Hq, Hkv, Nq, Nkv, D, D, q_stride, k_stride, v_stride, o_stride),
                   mask_args(mask, mask_type, mask_stride));
 }
+
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                int Hkv, int Nq, int Nkv, int D, int Dv, const long long* q_stride,
+                const long long* k_stride, const long long* v_stride, const long long* o_stride,
+                const void* mask, int mask_type, const long long* mask_stride, float scale,
+                int causal, int dtype, int num_splits, void* stream) {
+  const Layout L = strided_layout(Hq, Hkv, Nq, Nkv, D, Dv, q_stride, k_stride, v_stride, o_stride);
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, Dv, L, scale, causal, dtype, num_splits,
+             (hipStream_t)stream, mask_args(mask, mask_type, mask_stride));
+}
+
+int attn_fwd_dv_check(const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D, int Dv,
+                      const long long* q_stride, const long long* k_stride,
+                      const long long* v_stride, const long long* o_stride, const void* mask,
+                      int mask_type, const long long* mask_stride, float scale, int causal,
+                      int dtype) {
+  return validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, Dv, scale, causal, dtype,
+                  strided_layout(Hq, Hkv, Nq, Nkv, D, Dv, q_stride, k_stride, v_stride, o_stride),
+                  mask_args(mask, mask_type, mask_stride));
+}
+
+// The planning queries take one head dimension: D = 192 stands for the
+// (192, 128) pair, whose partial rows have 128 columns.
+static int plan_dv(int D) { return D == 192 ? 128 : D; }
 
 int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,
                         int num_cus) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
-  if (!head_dim_ok(D) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
+  if (!head_dims_ok(D, plan_dv(D)) || (dtype != ATTN_F16 && dtype != ATTN_BF16))
+    return ATTN_EINVAL;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
-  return make_plan(B, Hq, Nq, Nkv, D, causal, 0, num_cus).splits;
+  return make_plan(B, Hq, Nq, Nkv, D, plan_dv(D), causal, 0, num_cus).splits;
 }
 
 int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,
                   int num_splits, int num_cus, attn_plan* plan) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
-  if (!head_dim_ok(D) || (dtype != ATTN_F16 && dtype != ATTN_BF16)) return ATTN_EINVAL;
+  if (!head_dims_ok(D, plan_dv(D)) || (dtype != ATTN_F16 && dtype != ATTN_BF16))
+    return ATTN_EINVAL;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT || num_splits < 0 || !plan)
     return ATTN_EINVAL;
   if ((long long)B * Hq * Nq > INT32_MAX || (long long)B * Hkv * Nkv > INT32_MAX)
     return ATTN_EINVAL;
-  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, causal, num_splits, num_cus);
+  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, plan_dv(D), causal, num_splits, num_cus);
   plan->tile_rows = kCfgs[pl.cfg].BM();
   plan->num_splits = pl.splits;
   plan->split_rows = pl.rows - pl.row0;

@@ -6,10 +6,10 @@
 namespace attn_fwd_detail {
 
 template <>
-hipError_t launch_fwd_d<80>(const Params& p, int cfg, bool causal, bool split, bool strided,
+hipError_t launch_fwd_d<80, 80>(const Params& p, int cfg, bool causal, bool split, bool strided,
                            bool masked, bool bf16, hipStream_t st) {
-  return bf16 ? dispatch_d<80, TagBF16>(p, cfg, causal, split, strided, masked, st)
-              : dispatch_d<80, TagF16>(p, cfg, causal, split, strided, masked, st);
+  return bf16 ? dispatch_d<80, 80, TagBF16>(p, cfg, causal, split, strided, masked, st)
+              : dispatch_d<80, 80, TagF16>(p, cfg, causal, split, strided, masked, st);
 }
 
 template <>

@@ -3,7 +3,8 @@
 // unit of its own (attn_fwd_d<D>.hip); attn_fwd.hip holds the host side.
 //
 // What is computed: exact softmax attention, O = softmax(scale*Q K^T [causal
-// mask]) V, plus the row log-sum-exp.  The English noflash-attention post
+// mask]) V, plus the row log-sum-exp.  Q and K rows have D elements, V and O
+// rows DV (equal to D except for the (192, 128) pair).  The English noflash-attention post
 // (ai-navigate-news.com) tiles it over query chunks and, in its second tier,
 // over key tiles with a running max and a running sum ("online softmax",
 // section "The DIY approach"), so the Nq x Nkv score matrix never exists.
@@ -63,7 +64,7 @@ struct Params {
   const uint16_t* v;
   uint16_t* o;        // final output (non-split) or unused
   float* lse;         // final LSE (non-split), may be null
-  float* opart;       // split: [S][prows][D] fp32, rows from row0 on
+  float* opart;       // split: [S][prows][DV] fp32, rows from row0 on
   float* lsepart;     // split: [S][prows]
   int Hq, Nq, Nkv, G, Hkv;
   int n_qtiles, n_splits, split_len;
@@ -101,7 +102,10 @@ struct Params {
 // single-buffered pipeline and half of Q^T (8 of 16 chunks) in LDS.  At
 // D = 96 (12 chunks per row) the copies split evenly over 4 waves with
 // 64-key tiles: the D = 64 narrow tile.  D = 80 runs the D = 96 tile with
-// two zero chunks per row.
+// two zero chunks per row.  D = 192 with DV = 128 (24-chunk K rows, 16-chunk
+// V rows): 64-key tiles (the copies of a 32-key K tile would not split over
+// 8 waves), 32-row waves, the single-buffered pipeline and 4 of the 12 Q^T
+// chunks in LDS (double-buffered scores and all of Q^T in registers spill).
 struct TileCfg {
   int NW, QB, BN, QL;
   bool SB;
@@ -114,27 +118,31 @@ enum {
   kCfgD128Narrow = 2,
   kCfgD128Wide = 3,
   kCfgD256 = 4,
-  kCfgD96 = 5
+  kCfgD96 = 5,
+  kCfgD192 = 6
 };
-constexpr TileCfg kCfgs[6] = {{4, 1, 64, 0, false},
+constexpr TileCfg kCfgs[7] = {{4, 1, 64, 0, false},
                               {4, 2, 32, 0, false},
                               {8, 1, 64, 0, false},
                               {8, 2, 32, 3, true},
                               {8, 1, 32, 8, true},
-                              {4, 1, 64, 0, false}};
+                              {4, 1, 64, 0, false},
+                              {8, 1, 64, 4, true}};
 
-// Launch the forward kernels of one head dimension (defined, one head
-// dimension per translation unit, in attn_fwd_d<D>.hip).
-template <int D>
+// Launch the forward kernels of one pair of head dimensions (Q/K, V/O),
+// defined one pair per translation unit in attn_fwd_d<D>[v<DV>].hip.  The
+// merge of split partials depends on DV only.
+template <int D, int DV>
 hipError_t launch_fwd_d(const Params& p, int cfg, bool causal, bool split, bool strided,
                         bool masked, bool bf16, hipStream_t st);
 template <int D>
 hipError_t launch_combine_d(const Params& p, bool strided, bool bf16, hipStream_t st);
-template <> hipError_t launch_fwd_d<64>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
-template <> hipError_t launch_fwd_d<80>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
-template <> hipError_t launch_fwd_d<96>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
-template <> hipError_t launch_fwd_d<128>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
-template <> hipError_t launch_fwd_d<256>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
+template <> hipError_t launch_fwd_d<64, 64>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
+template <> hipError_t launch_fwd_d<80, 80>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
+template <> hipError_t launch_fwd_d<96, 96>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
+template <> hipError_t launch_fwd_d<128, 128>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
+template <> hipError_t launch_fwd_d<256, 256>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
+template <> hipError_t launch_fwd_d<192, 128>(const Params&, int, bool, bool, bool, bool, bool, hipStream_t);
 template <> hipError_t launch_combine_d<64>(const Params&, bool, bool, hipStream_t);
 template <> hipError_t launch_combine_d<80>(const Params&, bool, bool, hipStream_t);
 template <> hipError_t launch_combine_d<96>(const Params&, bool, bool, hipStream_t);
@@ -181,33 +189,41 @@ using namespace attn_fwd_detail;
 // The products run over DP = compute_dim(D) columns: D itself, except that
 // D = 80 (not a multiple of the 32-column output blocks) is computed as 96
 // with the last two 16-byte chunks of every Q, K and V row read as zeros and
-// the matching output columns not stored.
-template <int D, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB, bool SPLIT,
-          bool STRIDED, bool MASKED>
+// the matching output columns not stored.  The V and O widths (DV) are
+// handled the same way, independently of D.
+template <int D, int DV, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB,
+          bool SPLIT, bool STRIDED, bool MASKED>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
-  constexpr int DP = compute_dim(D);    // columns of the products and LDS rows
-  constexpr int WR = QB * 32;           // query rows per wave
+  constexpr int DP = compute_dim(D);     // columns of Q K^T and of K's LDS rows
+  constexpr int DVP = compute_dim(DV);   // columns of P V and of V's LDS rows
+  constexpr int WR = QB * 32;            // query rows per wave
   constexpr int BM = NW * WR;
-  constexpr int CPR = DP / 8;           // 16-byte chunks per LDS row
-  constexpr int CPG = D / 8;            // 16-byte chunks per row in memory
-  constexpr int TILE = BN * DP;         // elements of one K (or V) tile
-  constexpr int INSTR = BN * CPR / 64;  // 1 KB wave copies per tile
-  static_assert(INSTR % NW == 0, "tile copies must split evenly over waves");
+  constexpr int CPR = DP / 8;            // 16-byte chunks per LDS row of K
+  constexpr int CPG = D / 8;             // 16-byte chunks per row of K in memory
+  constexpr int CPRV = DVP / 8;          // the same for V
+  constexpr int CPGV = DV / 8;
+  constexpr int TILE = BN * DP;          // elements of one K tile
+  constexpr int TILEV = BN * DVP;        // elements of one V tile
+  constexpr int INSTR = BN * CPR / 64;   // 1 KB wave copies per K tile
+  constexpr int INSTRV = BN * CPRV / 64;  // and per V tile
+  static_assert(INSTR % NW == 0 && INSTRV % NW == 0, "tile copies must split evenly over waves");
   constexpr int IPW = INSTR / NW;
-  constexpr int DC = DP / 16;           // reduction chunks of Q K^T
-  constexpr int NKB = BN / 32;          // 32-key blocks per tile
-  constexpr int NDB = DP / 32;          // 32-wide output column blocks
-  constexpr int NKC = BN / 16;          // reduction chunks of P V
-  constexpr int ROWB = D * 2;           // bytes per K/V row in memory
+  constexpr int IPWV = INSTRV / NW;
+  constexpr int DC = DP / 16;            // reduction chunks of Q K^T
+  constexpr int NKB = BN / 32;           // 32-key blocks per tile
+  constexpr int NDB = DVP / 32;          // 32-wide output column blocks
+  constexpr int NKC = BN / 16;           // reduction chunks of P V
+  constexpr int ROWB = D * 2;            // bytes per K row in memory
+  constexpr int ROWBV = DV * 2;          // bytes per V row in memory
   constexpr int DCR = DC - QL;          // Q^T chunks held in registers
   static_assert(QL >= 0 && QL < DC, "at least one Q^T chunk stays in registers");
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf0[TILEV];
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t vbuf1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t vbuf2[SB ? TILE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf1[TILEV];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf2[SB ? TILEV : 8];
   __shared__ __attribute__((aligned(1024))) u32x4 qlds[QL > 0 ? NW * QB * QL * 64 : 1];
 
   const int tid = threadIdx.x;
@@ -239,36 +255,52 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
   const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;  // LSE / partial row of query 0
-  const int64_t kvh = (int64_t)p.Nkv * D, qh = (int64_t)p.Nq * D;
+  const int64_t kh = (int64_t)p.Nkv * D, vh = (int64_t)p.Nkv * DV;
+  const int64_t qh = (int64_t)p.Nq * D, oh = (int64_t)p.Nq * DV;
   const int qsn = STRIDED ? p.qsn : D, ksn = STRIDED ? p.ksn : D;
-  const int vsn = STRIDED ? p.vsn : D, osn = STRIDED ? p.osn : D;
+  const int vsn = STRIDED ? p.vsn : DV, osn = STRIDED ? p.osn : DV;
   const uint16_t* Qg = p.q + (STRIDED ? b * p.qsb + hq * p.qsh : ((int64_t)b * p.Hq + hq) * qh);
-  const uint16_t* Kg = p.k + (STRIDED ? b * p.ksb + hk * p.ksh : ((int64_t)b * p.Hkv + hk) * kvh);
-  const uint16_t* Vg = p.v + (STRIDED ? b * p.vsb + hk * p.vsh : ((int64_t)b * p.Hkv + hk) * kvh);
+  const uint16_t* Kg = p.k + (STRIDED ? b * p.ksb + hk * p.ksh : ((int64_t)b * p.Hkv + hk) * kh);
+  const uint16_t* Vg = p.v + (STRIDED ? b * p.vsb + hk * p.vsh : ((int64_t)b * p.Hkv + hk) * vh);
 
   // Per-lane byte offsets of this wave's copy slots within a tile (the same
   // for every tile) and the LDS slot each copy fills.  Padding chunks (past
   // the row in memory) get an offset beyond any buffer, so they read zero.
-  uint32_t koff[IPW], voff[IPW];
+  uint32_t koff[IPW], voff[IPWV];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int slot = (wave * IPW + j) * 64 + lane;
     const int row = slot / CPR, pc = slot % CPR;
-    const int kch = pc ^ k_swz<DP>(row), vch = pc ^ v_swz<DP>(row);
+    const int kch = pc ^ k_swz<DP>(row);
     koff[j] = kch < CPG ? row * ksn * 2 + (kch << 4) : kPadOffset;
-    voff[j] = vch < CPG ? row * vsn * 2 + (vch << 4) : kPadOffset;
   }
-  // Copy tile `t` of K (or V, rows `sn` elements apart) into LDS.  The
-  // buffer ends with the last key's row, so rows past it (which start at or
-  // beyond that end, as sn >= D) read as zero: their scores are masked to
-  // -inf and their V rows are multiplied by exactly 0.
-  auto issue = [&](const uint16_t* base, int sn, int t, uint16_t* dst, const uint32_t* off) {
+#pragma unroll
+  for (int j = 0; j < IPWV; ++j) {
+    const int slot = (wave * IPWV + j) * 64 + lane;
+    const int row = slot / CPRV, pc = slot % CPRV;
+    const int vch = pc ^ v_swz<DVP>(row);
+    voff[j] = vch < CPGV ? row * vsn * 2 + (vch << 4) : kPadOffset;
+  }
+  // Copy tile `t` of K or V (rows `sn` elements and `rowb` bytes long,
+  // IP copies per wave) into LDS.  The buffer ends with the last key's row,
+  // so rows past it (which start at or beyond that end, as a row stride is
+  // at least a row) read as zero: their scores are masked to -inf and their
+  // V rows are multiplied by exactly 0.
+  auto copy_tile = [&](auto ip, int rowb, const uint16_t* base, int sn, int t, uint16_t* dst,
+                       const uint32_t* off) {
+    constexpr int IP = decltype(ip)::value;
     const int k0 = kbeg + t * BN;
     const int nrows = min(BN, p.Nkv - k0);
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + (size_t)k0 * sn), 0, (nrows - 1) * sn * 2 + ROWB, kRawBufferFlags);
+        (void*)(base + (size_t)k0 * sn), 0, (nrows - 1) * sn * 2 + rowb, kRawBufferFlags);
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) buf2lds16(r, dst + (wave * IPW + j) * 512, off[j]);
+    for (int j = 0; j < IP; ++j) buf2lds16(r, dst + (wave * IP + j) * 512, off[j]);
+  };
+  auto issue_k = [&](int t, uint16_t* dst) {
+    copy_tile(std::integral_constant<int, IPW>{}, ROWB, Kg, ksn, t, dst, koff);
+  };
+  auto issue_v = [&](int t, uint16_t* dst) {
+    copy_tile(std::integral_constant<int, IPWV>{}, ROWBV, Vg, vsn, t, dst, voff);
   };
 
   // Q^T operands for the whole key loop: chunks below DCR in registers, the
@@ -318,7 +350,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);          // key within a 16-key chunk (first half)
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);  // column within a 32-wide block
-  const int v_sw = v_swz<DP>(v_key);              // same for key v_key + 16 kc (+ 8)
+  const int v_sw = v_swz<DVP>(v_key);             // same for key v_key + 16 kc (+ 8)
 
   // Scores of a tile: s[qb * NKB + kb] (32 keys x 32 rows); probabilities
   // pf[qb * NKC + kc] (16 keys x 32 rows, the P^T operands).
@@ -481,8 +513,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
       for (int db = 0; db < NDB; ++db) {
         const int d = db * 32 + v_d;
         const int off = (((d >> 3) ^ v_sw) << 3) + (d & 7);
-        const u32x2 lo = lds_read_tr16(vs + key * DP + off);
-        const u32x2 hi = lds_read_tr16(vs + (key + 8) * DP + off);
+        const u32x2 lo = lds_read_tr16(vs + key * DVP + off);
+        const u32x2 hi = lds_read_tr16(vs + (key + 8) * DVP + off);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -500,8 +532,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (!LAST) {
-      if (t + 2 < ntiles) issue(Kg, ksn, t + 2, kc, koff);
-      issue(Vg, vsn, t + 1, vn, voff);
+      if (t + 2 < ntiles) issue_k(t + 2, kc);
+      issue_v(t + 1, vn);
       qk(kn, sn);
     }
     float rs[QB];
@@ -531,8 +563,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (t + 1 < ntiles) {
-        issue(Kg, ksn, t + 1, kn, koff);
-        issue(Vg, vsn, t + 1, vn, voff);
+        issue_k(t + 1, kn);
+        issue_v(t + 1, vn);
       }
       if (late && t > 0) pv(vp, pf);
       qk(kc, sa);
@@ -545,8 +577,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     auto kbufs = [&](int i) { return i ? kbuf1 : kbuf0; };
     auto vbufs = [&](int i) { return i == 0 ? vbuf0 : i == 1 ? vbuf1 : vbuf2; };
     if (ntiles > 0) {
-      issue(Kg, ksn, 0, kbuf0, koff);
-      issue(Vg, vsn, 0, vbuf0, voff);
+      issue_k(0, kbuf0);
+      issue_v(0, vbuf0);
     }
     int t = 0;
     for (; t + 6 <= ntiles; t += 6) {  // K_t in kbuf[t % 2], V_t in vbuf[t % 3]
@@ -564,11 +596,11 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     }
     if (late && ntiles > 0) pv(vbufs((ntiles - 1) % 3), pf);
   } else if (ntiles > 0) {
-    issue(Kg, ksn, 0, kbuf0, koff);
-    issue(Vg, vsn, 0, vbuf0, voff);
+    issue_k(0, kbuf0);
+    issue_v(0, vbuf0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (ntiles > 1) issue(Kg, ksn, 1, kbuf1, koff);
+    if (ntiles > 1) issue_k(1, kbuf1);
     qk(kbuf0, sa);
     int t = 0;
     for (; t + 2 < ntiles; t += 2) {
@@ -593,7 +625,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     if (qrow < p.Nq) {
       if (SPLIT) {
         const size_t prow = (size_t)sp * p.prows + (qrow0 + qrow - p.row0);
-        float* dst = p.opart + prow * D;
+        float* dst = p.opart + prow * DV;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -601,11 +633,11 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
             const int col = db * 32 + 8 * i + 4 * hl;
             const f32x16& o = oacc[qb * NDB + db];
             f32x4 y = {o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv, o[4 * i + 3] * inv};
-            if (DP == D || col < D) *(f32x4*)(dst + col) = y;
+            if (DVP == DV || col < DV) *(f32x4*)(dst + col) = y;
           }
         if (hl == 0) p.lsepart[prow] = lse_v;
       } else {
-        uint16_t* dst = p.o + (STRIDED ? b * p.osb + hq * p.osh : ((int64_t)b * p.Hq + hq) * qh) +
+        uint16_t* dst = p.o + (STRIDED ? b * p.osb + hq * p.osh : ((int64_t)b * p.Hq + hq) * oh) +
                         (size_t)qrow * osn;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -615,7 +647,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
             const f32x16& o = oacc[qb * NDB + db];
             u32x2 y = {N::pack2(o[4 * i] * inv, o[4 * i + 1] * inv),
                        N::pack2(o[4 * i + 2] * inv, o[4 * i + 3] * inv)};
-            if (DP == D || col < D) *(u32x2*)(dst + col) = y;
+            if (DVP == DV || col < DV) *(u32x2*)(dst + col) = y;
           }
         if (hl == 0 && p.lse) p.lse[qrow0 + qrow] = lse_v;
       }
@@ -665,50 +697,52 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 
 // Masked launches always take the strided kernels (the mask has strides
 // of its own) and only the narrow tiles.
-template <int D, int CFG, class Tag, bool CAUSAL, bool SPLIT, bool MASKED>
+template <int D, int DV, int CFG, class Tag, bool CAUSAL, bool SPLIT, bool MASKED>
 hipError_t launch_main(const Params& p, bool strided, hipStream_t stream) {
   constexpr TileCfg c = kCfgs[CFG];
   if (MASKED)
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, MASKED>),
+        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, MASKED>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   else if (strided)
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, false>),
+        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, false>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   else
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, false, false>),
+        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, false, false>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int CFG, class Tag, bool MASKED>
+template <int D, int DV, int CFG, class Tag, bool MASKED>
 hipError_t dispatch(const Params& p, bool causal, bool split, bool strided, hipStream_t st) {
   if (causal)
-    return split ? launch_main<D, CFG, Tag, true, true, MASKED>(p, strided, st)
-                 : launch_main<D, CFG, Tag, true, false, MASKED>(p, strided, st);
-  return split ? launch_main<D, CFG, Tag, false, true, MASKED>(p, strided, st)
-               : launch_main<D, CFG, Tag, false, false, MASKED>(p, strided, st);
+    return split ? launch_main<D, DV, CFG, Tag, true, true, MASKED>(p, strided, st)
+                 : launch_main<D, DV, CFG, Tag, true, false, MASKED>(p, strided, st);
+  return split ? launch_main<D, DV, CFG, Tag, false, true, MASKED>(p, strided, st)
+               : launch_main<D, DV, CFG, Tag, false, false, MASKED>(p, strided, st);
 }
 
 // The wide tiles are only selected without a causal mask.
-template <int D, class Tag>
+template <int D, int DV, class Tag>
 hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool strided,
                       bool masked, hipStream_t st) {
-  constexpr int kNarrow = D == 256 ? kCfgD256
+  constexpr int kNarrow = D == 192             ? kCfgD192
+                          : D == 256           ? kCfgD256
                           : D == 96 || D == 80 ? kCfgD96
                           : D == 128           ? kCfgD128Narrow
                                                : kCfgD64Narrow;
-  constexpr int kWide = D == 256 ? kCfgD256
+  constexpr int kWide = D == 192             ? kCfgD192
+                        : D == 256           ? kCfgD256
                         : D == 96 || D == 80 ? kCfgD96
                         : D == 128           ? kCfgD128Wide
                                              : kCfgD64Wide;
-  if (masked) return dispatch<D, kNarrow, Tag, true>(p, causal, split, true, st);
-  if (cfg == kWide && !causal)
-    return split ? launch_main<D, kWide, Tag, false, true, false>(p, strided, st)
-                 : launch_main<D, kWide, Tag, false, false, false>(p, strided, st);
-  return dispatch<D, kNarrow, Tag, false>(p, causal, split, strided, st);
+  if (masked) return dispatch<D, DV, kNarrow, Tag, true>(p, causal, split, true, st);
+  if (kWide != kNarrow && cfg == kWide && !causal)
+    return split ? launch_main<D, DV, kWide, Tag, false, true, false>(p, strided, st)
+                 : launch_main<D, DV, kWide, Tag, false, false, false>(p, strided, st);
+  return dispatch<D, DV, kNarrow, Tag, false>(p, causal, split, strided, st);
 }
 
 template <int D, class Tag>

@@ -5,7 +5,8 @@ release") ships its method as a replacement for PyTorch's SDPA call: calls
 it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
 
 * ``sdpa(query, key, value, ...)`` has SDPA's signature and semantics for
-  what this library computes (head dim 64, 80, 96, 128 or 256; no dropout;
+  what this library computes (head dim 64, 80, 96, 128 or 256, or query and
+  key head dim 192 with value head dim 128 when no gradient is needed; no dropout;
   top-left causal through ``is_causal``; PyTorch's causal biases
   ``causal_upper_left`` / ``causal_lower_right`` as ``attn_mask`` (the
   latter is bottom-right alignment, rows that see no key give 0); boolean
@@ -100,11 +101,15 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
     if not (query.dtype == key.dtype == value.dtype) or query.dtype not in (
             torch.float16, torch.bfloat16):
         return "dtype must be float16 or bfloat16 for all inputs"
-    E = query.shape[-1]
-    if E not in (64, 80, 96, 128, 256) or key.shape[-1] != E or value.shape[-1] != E:
-        return "head dimension must be 64, 80, 96, 128 or 256 for query, key and value"
-    if key.shape != value.shape:
-        return "key and value must have one shape"
+    E, Ev = query.shape[-1], value.shape[-1]
+    if key.shape[-1] != E or not (
+            (Ev == E and E in (64, 80, 96, 128, 256)) or (E, Ev) == (192, 128)):
+        return ("head dimension must be 64, 80, 96, 128 or 256 for query, key and value, "
+                "or 192 for query and key with 128 for value")
+    if Ev != E and torch.is_grad_enabled() and any(t.requires_grad for t in ts):
+        return "no gradients for a value head dimension other than the query's"
+    if key.shape[:-1] != value.shape[:-1]:
+        return "key and value must have one shape apart from the head dimension"
     if query.shape[:-3] != key.shape[:-3]:
         return "batch dimensions differ"
     Hq, Hkv = query.shape[-3], key.shape[-3]
@@ -115,8 +120,8 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
     if any(s % 8 for t in ts for s in t.stride()[:-1]) or (
             not tracing and any(t.data_ptr() % 16 for t in ts)):
         return "strides must be multiples of 8 elements and data 16-byte aligned"
-    if any(t.stride(-2) < E or t.stride(-2) > (1 << 24) for t in ts):
-        return "sequence strides must lie in [E, 2^24]"
+    if any(t.stride(-2) < t.shape[-1] or t.stride(-2) > (1 << 24) for t in ts):
+        return "sequence strides must lie in [head dimension, 2^24]"
     if query.shape[-2] == 0 or key.shape[-2] == 0 or Hq == 0 or (
             query.dim() == 4 and query.shape[0] == 0):
         return "empty inputs"
@@ -161,7 +166,8 @@ def sdpa(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False,
     """SDPA on the HIP library: softmax(scale * Q K^T [causal]) V.
 
     Same arguments as torch.nn.functional.scaled_dot_product_attention;
-    returns a new contiguous tensor of the query's shape.  Raises
+    returns a new contiguous tensor of the query's shape with the value's
+    head dimension.  Raises
     NotImplementedError for calls the library cannot serve.
     """
     import torch
@@ -210,8 +216,9 @@ def torch_ops():
 
     @attention.register_fake
     def _(q, k, v, mask, causal, scale):
-        B, Hq, Nq, D = q.shape
-        return q.new_empty((B, Hq, Nq, D)), q.new_empty((B, Hq, Nq), dtype=torch.float32)
+        B, Hq, Nq, _ = q.shape
+        return (q.new_empty((B, Hq, Nq, v.shape[-1])),
+                q.new_empty((B, Hq, Nq), dtype=torch.float32))
 
     @torch.library.custom_op(
         "memory_efficient_tiled_amd::attention_backward", mutates_args=(),

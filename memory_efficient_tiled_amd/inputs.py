@@ -41,6 +41,11 @@ class Workload:
     k_offset_std: float | None = None   # per-channel offset added to K
     sampled_rows: int | None = None      # oracle rows per head at full size
     note: str = ""
+    Dv_: int | None = None               # V/O head dimension when it differs from D
+
+    @property
+    def Dv(self) -> int:
+        return self.D if self.Dv_ is None else self.Dv_
 
     @property
     def scale(self) -> float:
@@ -48,13 +53,15 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """Algorithmic flops: 4*B*Hq*Nq*Nkv*D, halved when causal."""
-        f = 4.0 * self.B * self.Hq * self.Nq * self.Nkv * self.D
+        """Algorithmic flops: 2*B*Hq*Nq*Nkv*(D + Dv) (4*...*D when Dv = D),
+        halved when causal."""
+        f = 2.0 * self.B * self.Hq * self.Nq * self.Nkv * (self.D + self.Dv)
         return f / 2.0 if self.causal else f
 
     def describe(self) -> str:
+        dv = f" Dv={self.Dv}" if self.Dv != self.D else ""
         return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} Nq={self.Nq} "
-                f"Nkv={self.Nkv} D={self.D} {self.dtype} "
+                f"Nkv={self.Nkv} D={self.D}{dv} {self.dtype} "
                 f"{'causal' if self.causal else 'non-causal'}")
 
 
@@ -105,6 +112,16 @@ WORKLOADS["hd80-8192"] = _w(name="hd80-8192", B=1, Hq=32, Hkv=32, Nq=8192, Nkv=8
                             D=80, dtype=F16, causal=False,
                             note="head dim 80, non-causal MHA")
 
+# Query/key head dimension 192 with value head dimension 128 (same list:
+# Dv != D), the per-head shape of multi-head latent attention at prefill;
+# 16 heads, 8192 tokens, causal and not.
+WORKLOADS["hd192v128-causal-8192"] = _w(name="hd192v128-causal-8192", B=1, Hq=16, Hkv=16,
+                                        Nq=8192, Nkv=8192, D=192, Dv_=128, dtype=BF16,
+                                        causal=True, note="head dims 192/128, causal prefill")
+WORKLOADS["hd192v128-8192"] = _w(name="hd192v128-8192", B=1, Hq=16, Hkv=16, Nq=8192,
+                                 Nkv=8192, D=192, Dv_=128, dtype=BF16, causal=False,
+                                 note="head dims 192/128, non-causal")
+
 HEADLINE = "dit-17160"
 
 
@@ -131,7 +148,7 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 class Inputs:
     q: np.ndarray          # [B, Hq, Nq, D]   float16 or uint16 (bf16 bits)
     k: np.ndarray          # [B, Hkv, Nkv, D]
-    v: np.ndarray          # [B, Hkv, Nkv, D]
+    v: np.ndarray          # [B, Hkv, Nkv, Dv]
     dtype: str
     seed: int
     k_offset: np.ndarray | None = None   # float32 [D], already folded into k
@@ -140,8 +157,9 @@ class Inputs:
 
 def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
                 dtype: str, seed: int = 0, k_offset_std: float | None = None,
-                sampled_rows: int | None = None) -> Inputs:
-    """Draw q, k, v iid N(0,1) (float32), in that order, from PCG64(seed).
+                sampled_rows: int | None = None, Dv: int | None = None) -> Inputs:
+    """Draw q, k, v iid N(0,1) (float32), in that order, from PCG64(seed);
+    v has Dv columns (default D).
 
     With ``k_offset_std`` a per-channel offset c = std*z, z ~ N(0,1) of shape
     [D], is drawn next and added to every key row in float32 before rounding.
@@ -153,7 +171,7 @@ def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
     qs = to_storage(q, dtype)
     del q
     k = rng.standard_normal((B, Hkv, Nkv, D), dtype=np.float32)
-    v = rng.standard_normal((B, Hkv, Nkv, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Nkv, D if Dv is None else Dv), dtype=np.float32)
     off = None
     if k_offset_std is not None:
         off = (np.float32(k_offset_std)
@@ -194,4 +212,4 @@ def make_workload_inputs(w: Workload, seed: int = 0,
                          sampled_rows: int | None = None) -> Inputs:
     R = sampled_rows if sampled_rows is not None else w.sampled_rows
     return make_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, seed=seed,
-                       k_offset_std=w.k_offset_std, sampled_rows=R)
+                       k_offset_std=w.k_offset_std, sampled_rows=R, Dv=w.Dv)

@@ -51,10 +51,10 @@ class Result:
 def oracle_rows(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
     """Oracle output for all rows, or for rows [Hq, R], one head at a time."""
     B, Hq, Nq, D = x.q.shape
-    Hkv = x.k.shape[1]
+    Hkv, Dv = x.k.shape[1], x.v.shape[3]
     G = Hq // Hkv
     R = Nq if rows is None else rows.shape[1]
-    o = np.empty((B, Hq, R, D))
+    o = np.empty((B, Hq, R, Dv))
     lse = np.empty((B, Hq, R))
     sc = oracle.scale_value(scale, D)
     for b in range(B):

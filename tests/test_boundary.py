@@ -214,3 +214,50 @@ def test_masked_backward_validation():
     assert lib.attn_bwd_masked_check(*args, 0x60000002, 2, ms, 0.088, 0, BF16) == EINVAL
     assert lib.attn_bwd_masked_check(*args, 0x80000000, 1, ms, 0.088, 0, BF16) == EINVAL  # = dq
     assert lib.attn_bwd_masked_check(*args, None, 0, null, 0.088, 0, BF16) == OK
+
+
+def dvcheck(D=192, Dv=128, vs=None, os_=None, mask=None, mask_type=0, ms=None, **kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, B=2, Hq=8, Hkv=2, Nq=64, Nkv=80,
+             scale=0.072, causal=0, dtype=BF16)
+    a.update(kw)
+    lib = binding.load_library()
+    null = ctypes.POINTER(ctypes.c_longlong)()
+    arr = lambda t: (ctypes.c_longlong * 3)(*t) if t is not None else null  # noqa: E731
+    return lib.attn_fwd_dv_check(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                 a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], D, Dv,
+                                 null, null, arr(vs), arr(os_), mask, mask_type, arr(ms),
+                                 a["scale"], a["causal"], a["dtype"])
+
+
+def test_value_width_validation():
+    """attn_fwd_dv: Dv == D for the supported D, or the (192, 128) pair; V and
+    out take strides of Dv-element rows."""
+    assert dvcheck() == OK
+    assert dvcheck(D=128, Dv=128) == OK
+    assert dvcheck(D=80, Dv=80, dtype=F16) == OK
+    for D, Dv in [(192, 192), (128, 64), (192, 64), (64, 128), (128, 192), (192, 256)]:
+        assert dvcheck(D=D, Dv=Dv) == EINVAL, (D, Dv)
+    # V [2, 2, 80, 128]: a sequence stride of 128 is a whole row, 120 is not
+    assert dvcheck(vs=(2 * 80 * 128, 80 * 128, 128)) == OK
+    assert dvcheck(vs=(2 * 80 * 128, 80 * 128, 120)) == EINVAL
+    # out [2, 8, 64, 128] viewed from [B, N, H, Dv] storage
+    assert dvcheck(os_=(64 * 8 * 128, 128, 8 * 128)) == OK
+    assert dvcheck(os_=(64 * 8 * 128, 64, 8 * 128)) == EINVAL     # rows of out overlap
+    # the output ends 2*8*64*128*2 bytes after O: a V placed inside it overlaps
+    assert dvcheck(v=O + 4096) == EINVAL
+    assert dvcheck(mask=0x60000000, mask_type=1, ms=(0, 0, 80)) == OK
+    assert dvcheck(mask=0x60000000, mask_type=1, ms=None) == EINVAL
+    assert dvcheck(causal=2) == OK
+
+
+def test_value_width_plan(lib):
+    """The planning queries read D = 192 as the (192, 128) pair: partials of
+    128 columns."""
+    plan = binding.AttnPlan()
+    assert lib.attn_fwd_plan(1, 16, 16, 8192, 8192, 192, 0, BF16, 4, 256,
+                             ctypes.byref(plan)) == OK
+    rows = plan.split_rows
+    assert plan.num_splits == 4 and rows > 0
+    assert plan.workspace_bytes == 4 * rows * (128 + 1) * 4
+    assert lib.attn_fwd_num_splits(1, 16, 16, 8192, 8192, 192, 1, BF16, 256) >= 1
+    assert lib.attn_fwd_num_splits(1, 16, 16, 8192, 8192, 160, 1, BF16, 256) == EINVAL

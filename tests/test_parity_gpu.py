@@ -16,11 +16,11 @@ pytestmark = pytest.mark.gpu
 
 
 def _case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed=0, scale=None,
-          rows=None, num_splits=0, allowance=True, k_offset_std=None):
-    log(f"case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} "
+          rows=None, num_splits=0, allowance=True, k_offset_std=None, Dv=None):
+    log(f"case B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} Dv={Dv} {dtype} "
         f"causal={causal} seed={seed} splits={num_splits} scale={scale}")
     x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed,
-                           k_offset_std=k_offset_std, sampled_rows=rows)
+                           k_offset_std=k_offset_std, sampled_rows=rows, Dv=Dv)
     o, l = run_gpu(x, scale, causal, device, num_splits=num_splits)
     r = None if rows is None else x.rows
     o_ref, l_ref = oracle_rows(x, scale, causal, rows=r)
@@ -35,7 +35,7 @@ def _case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed=0, scale=None,
 def _workload(device, name, rows=None, allowance=False):
     w = inputs.WORKLOADS[name]
     return _case(device, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, w.causal,
-                 rows=rows, allowance=allowance, k_offset_std=w.k_offset_std)
+                 rows=rows, allowance=allowance, k_offset_std=w.k_offset_std, Dv=w.Dv)
 
 
 def test_tiny_256(gpu_device):
@@ -274,7 +274,7 @@ def test_bottom_right_d256_long_rows(gpu_device):
 # -- attention masks (PyTorch SDPA attn_mask semantics) -----------------------
 
 def _mask_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, kind, seed, causal=False, splits=0,
-               mshape=None):
+               mshape=None, Dv=None):
     """kind "bool": random keep mask (one row left with no key); "add": an
     additive mask in the inputs' dtype with -inf entries; "pad": key padding
     per batch (batch 1 keeps no key at all).  The mask is broadcast from
@@ -284,7 +284,7 @@ def _mask_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, kind, seed, causal=False, 
     from memory_efficient_tiled_amd import attn_fwd
     log(f"mask case {kind} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} "
         f"causal={causal} splits={splits}")
-    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed)
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed, Dv=Dv)
     rng = np.random.Generator(np.random.PCG64([seed, 7]))
     mshape = mshape or (B, 1, Nq, Nkv)
     if kind == "bool":
@@ -444,3 +444,71 @@ def test_no_device_allocation_without_split(gpu_device):
     assert torch.cuda.max_memory_allocated() == before
     free0, _ = torch.cuda.mem_get_info()
     assert free0 > 0
+
+
+# -- value rows of another width: (D, Dv) = (192, 128) -----------------------
+# 24-chunk K rows and 16-chunk V rows in one kernel (64-key tiles, part of
+# Q^T in LDS): ragged query and key tails, GQA, Nq != Nkv, bottom-right
+# alignment, forced splits (fp32 partials of Dv columns), strided views,
+# masks, and sampled rows of the 8192-token workloads.
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 63, 65, 1000])
+def test_value_width_ragged(gpu_device, n, causal, dtype):
+    _case(gpu_device, 2, 4, 2, n, n, 192, dtype, causal, seed=192 + n, Dv=128)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nkv", [(100, 300), (300, 100), (1, 777)])
+def test_value_width_nq_ne_nkv(gpu_device, nq, nkv, causal):
+    _case(gpu_device, 1, 6, 2, nq, nkv, 192, inputs.BF16, causal, seed=nq + nkv, Dv=128)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_value_width_forced_splits(gpu_device, splits, causal):
+    _case(gpu_device, 1, 3, 1, 200, 1500, 192, inputs.BF16, causal, seed=splits,
+          num_splits=splits, Dv=128)
+
+
+@pytest.mark.parametrize("nq,nkv", [(100, 1000), (700, 90)])
+def test_value_width_bottom_right(gpu_device, nq, nkv):
+    x = inputs.make_inputs(1, 4, 2, nq, nkv, 192, inputs.BF16, seed=nq + 5 * nkv, Dv=128)
+    o, l = run_gpu(x, None, "bottom_right", gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, True, causal_offset=nkv - nq)
+    compare(o, l, o_ref, l_ref, inputs.BF16, rounding_allowance=True,
+            what=f"bottom-right {nq}x{nkv} D=192 Dv=128")
+
+
+def test_value_width_strided(gpu_device):
+    """[B, N, H, E] storage for Q, K (E = 192) and V, out (E = 128), viewed
+    as [B, H, N, E]: each tensor's sequence stride is H times its own row."""
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd
+    x = inputs.make_inputs(2, 4, 2, 300, 333, 192, inputs.F16, seed=193, Dv=128)
+    q, k, v = (to_device(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), inputs.F16,
+                         gpu_device).transpose(1, 2) for a in (x.q, x.k, x.v))
+    out = torch.empty(2, 300, 4, 128, dtype=torch.float16, device=gpu_device).transpose(1, 2)
+    _, lse = attn_fwd(q, k, v, causal=True, out=out)
+    torch.cuda.synchronize(gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, True)
+    compare(out.float().cpu().numpy().astype(np.float64),
+            lse.cpu().numpy().astype(np.float64), o_ref, l_ref, inputs.F16,
+            rounding_allowance=True, what="D=192 Dv=128 strided")
+
+
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_value_width_masks(gpu_device, kind):
+    _mask_case(gpu_device, 2, 4, 2, 150, 301, 192, inputs.BF16, kind, seed=194 + len(kind),
+               Dv=128)
+
+
+def test_value_width_mask_causal_split(gpu_device):
+    _mask_case(gpu_device, 1, 4, 2, 130, 700, 192, inputs.F16, "add", seed=195,
+               causal="bottom_right", splits=3, mshape=(1, 4, 130, 700), Dv=128)
+
+
+@pytest.mark.parametrize("name", ["hd192v128-8192", "hd192v128-causal-8192"])
+def test_value_width_workloads(gpu_device, name):
+    _workload(gpu_device, name, rows=48)
