@@ -176,7 +176,7 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     """Gradients of softmax attention in float64: (dq, dk, dv).
 
     For a loss whose gradient with respect to the output is ``do``
-    ([B, Hq, Nq, D]), the chain rule through the definition above, row by
+    ([B, Hq, Nq, Dv], V's width), the chain rule through the definition above, row by
     row: with P_ij = exp(s_ij - lse_i) over the allowed keys,
 
         dv_j  += sum_i P_ij do_i                  (dO flows through the sum)
@@ -198,7 +198,9 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     do = np.asarray(do, dtype=np.float64)
     B, Hq, Nq, D = q.shape
     Bk, Hkv, Nkv, Dk = k.shape
-    if v.shape != k.shape or Bk != B or Dk != D or do.shape != q.shape:
+    Dv = v.shape[3]
+    if (v.shape[:3] != k.shape[:3] or Bk != B or Dk != D
+            or do.shape != (B, Hq, Nq, Dv)):
         raise ValueError("shape mismatch between q, k, v and do")
     if Hkv <= 0 or Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")

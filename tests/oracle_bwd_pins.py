@@ -1,7 +1,8 @@
 """Pins for the oracle's attention gradients: facts fixed by mathematics.
 
 Every pin takes ``bwd(q, k, v, do, scale, causal, causal_offset=0) -> (dq, dk, dv)`` (float64
-arrays, q/do [B,Hq,Nq,D], k/v [B,Hkv,Nkv,D]) and raises AssertionError when
+arrays, q [B,Hq,Nq,D], k [B,Hkv,Nkv,D], v [B,Hkv,Nkv,Dv], do [B,Hq,Nq,Dv])
+and raises AssertionError when
 it disagrees.  The strongest is the derivative itself: central finite
 differences of the (separately pinned) forward oracle along random
 directions.  ``test_oracle.py`` runs them on the oracle and on copies of it
@@ -18,10 +19,11 @@ def _rng(seed):
     return np.random.Generator(np.random.PCG64(seed))
 
 
-def _inputs(seed, B=1, Hq=2, Hkv=1, Nq=6, Nkv=7, D=4):
+def _inputs(seed, B=1, Hq=2, Hkv=1, Nq=6, Nkv=7, D=4, Dv=None):
     r = _rng(seed)
+    Dv = D if Dv is None else Dv
     return (r.standard_normal((B, Hq, Nq, D)), r.standard_normal((B, Hkv, Nkv, D)),
-            r.standard_normal((B, Hkv, Nkv, D)), r.standard_normal((B, Hq, Nq, D)))
+            r.standard_normal((B, Hkv, Nkv, Dv)), r.standard_normal((B, Hq, Nq, Dv)))
 
 
 def _close(a, b, tol, what):
@@ -152,6 +154,33 @@ def pin_finite_differences_bias(bwd):
     assert np.all(dq[0, 1, 2] == 0.0), "a row with no key has no dq"
 
 
+def pin_finite_differences_value_width(bwd):
+    """V (and so O and dO) wider or narrower than Q and K: central
+    differences of the forward oracle, GQA, causal and not, and the column
+    sums of dv (sum over keys = sum of dO over the group's query rows)."""
+    for seed, causal, D, Dv in ((11, False, 4, 7), (12, True, 6, 3)):
+        q, k, v, do = _inputs(seed, Hq=4, Hkv=2, Nq=6, Nkv=8, D=D, Dv=Dv)
+        scale = 0.6
+        dq, dk, dv = bwd(q, k, v, do, scale, causal)
+        assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+        r = _rng(200 + seed)
+        h = 1e-5
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            d = r.standard_normal(x.shape)
+            def loss(xx):
+                args = {"q": q, "k": k, "v": v}
+                args[name] = xx
+                o, _ = oracle.attention(args["q"], args["k"], args["v"], scale, causal)
+                return float(np.sum(o * do))
+            fd = (loss(x + h * d) - loss(x - h * d)) / (2 * h)
+            an = float(np.sum(g * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), \
+                f"d{name} (D={D}, Dv={Dv}): finite difference {fd:.10f} vs {an:.10f}"
+        for hk in range(2):
+            _close(dv[0, hk].sum(axis=0), do[0, 2 * hk:2 * hk + 2].sum(axis=(0, 1)), 1e-12,
+                   f"sum of dv (D={D}, Dv={Dv})")
+
+
 ALL_PINS = [pin_finite_differences, pin_causal_row0_dq, pin_zero_do, pin_column_sums,
             pin_linear_in_do, pin_gqa_repeat, pin_finite_differences_offset,
-            pin_finite_differences_bias]
+            pin_finite_differences_bias, pin_finite_differences_value_width]

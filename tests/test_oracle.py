@@ -101,6 +101,8 @@ BWD_MUTANTS = [
     ("causal offset ignored", "key_idx[None, :] <= ri[:, None] + causal_offset",
      "key_idx[None, :] <= ri[:, None]"),
     ("bias ignored in the gradients", "s = s + bias[b, hq, ri]", "s = s + 0.0"),
+    ("dq from v instead of k", "dq[b, hq, ri] = scale * (ds @ kk)",
+     "dq[b, hq, ri] = scale * (ds @ vv)"),
 ]
 
 
