@@ -35,10 +35,9 @@ CSRC = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc")
 # the kernel sources each pass runs (a measurement taken on other sources is stale)
 SOURCES = {"fwd": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_d64.hip",
                    "attn_fwd_d80.hip", "attn_fwd_d96.hip", "attn_fwd_d128.hip",
-                   "attn_fwd_d256.hip"),
+                   "attn_fwd_d256.hip", "attn_fwd_d192v128.hip"),
            "bwd": ("attn_common.h", "attn_bwd.hip")}
 PROFILES = os.path.join(ROOT, "profiles")
-BWD_FLOP_FACTOR = 2.5
 
 
 def progress(msg):
@@ -187,7 +186,7 @@ def main():
     wall = time.perf_counter() - wall0
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    flops = w.flops * (BWD_FLOP_FACTOR if bwd else 1.0)
+    flops = w.bwd_flops if bwd else w.flops
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.dtype]
     progress(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); "
@@ -306,10 +305,10 @@ def cpu_leg_bwd(result, x, w, name, dout, dq, np, oracle):
                 dq_ref[b, h] = dqh[0, 0]
     cpu_s = time.perf_counter() - c0
     if w.causal:
-        sample_flops = float(sum(10.0 * w.D * np.minimum(r + 1, w.Nkv).sum()
+        sample_flops = float(sum(2.0 * (3 * w.D + 2 * w.Dv) * np.minimum(r + 1, w.Nkv).sum()
                                  for r in rows)) * w.B
     else:
-        sample_flops = 10.0 * w.D * w.Nkv * rows.size * w.B
+        sample_flops = 2.0 * (3 * w.D + 2 * w.Dv) * w.Nkv * rows.size * w.B
     err = np.abs(dq_gpu - dq_ref)
     rms = float(np.sqrt(np.mean(dq_ref ** 2)))
     u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11

@@ -335,6 +335,30 @@ int attn_bwd_masked_check(const void* q, const void* k, const void* v,
                           int causal, int dtype);
 
 /*
+ * attn_bwd_dv -- gradients of attn_fwd_dv: attn_bwd_masked with V, out, dout
+ * and dv of Dv-element rows ([B,Hkv,Nkv,Dv] and [B,Hq,Nq,Dv], contiguous)
+ * while Q, K, dq, dk keep D.  The derivative is the same as attn_bwd's:
+ * dV = P^T dO and dP = dO V^T run over Dv columns, dQ and dK over D.
+ * Supported: Dv == D for every D above, and D = 192 with Dv = 128.  mask,
+ * mask_type and mask_stride as for attn_bwd_masked (ATTN_MASK_NONE, NULL,
+ * NULL for none).  Returns as attn_bwd; an unsupported pair is ATTN_EINVAL.
+ */
+int attn_bwd_dv(const void* q, const void* k, const void* v, const void* out,
+                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                int B, int Hq, int Hkv, int Nq, int Nkv, int D, int Dv,
+                const void* mask, int mask_type, const long long* mask_stride,
+                float scale, int causal, int dtype, void* stream);
+
+/* attn_bwd_dv_check -- host only: attn_bwd_dv's validation. */
+int attn_bwd_dv_check(const void* q, const void* k, const void* v,
+                      const void* out, const void* dout, const float* lse,
+                      const void* dq, const void* dk, const void* dv, int B,
+                      int Hq, int Hkv, int Nq, int Nkv, int D, int Dv,
+                      const void* mask, int mask_type,
+                      const long long* mask_stride, float scale, int causal,
+                      int dtype);
+
+/*
  * attn_bwd_check -- host only: attn_bwd's argument validation; makes no HIP
  * call and dereferences no pointer.  Returns ATTN_OK or ATTN_EINVAL.
  */

@@ -100,6 +100,12 @@ def load_library():
     lib.attn_fwd_dv_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_dv + \
         [_LLP] * 4 + [_VP, _INT, _LLP, ctypes.c_float, _INT, _INT]
     lib.attn_fwd_dv_check.restype = _INT
+    lib.attn_bwd_dv.argtypes = [_VP] * 9 + shape_dv + [_VP, _INT, _LLP, ctypes.c_float,
+                                                       _INT, _INT, _VP]
+    lib.attn_bwd_dv.restype = _INT
+    lib.attn_bwd_dv_check.argtypes = [_VP] * 9 + shape_dv + [_VP, _INT, _LLP,
+                                                             ctypes.c_float, _INT, _INT]
+    lib.attn_bwd_dv_check.restype = _INT
     lib.attn_fwd_plan.argtypes = shape_args + [_INT, _INT, _INT, _INT,
                                                ctypes.POINTER(AttnPlan)]
     lib.attn_fwd_plan.restype = _INT
@@ -333,8 +339,9 @@ def attn_bwd(q, k, v, out, lse, dout, causal=False, scale: float | None = None,
 
     q, k, v, out, lse are the forward's inputs and outputs (same scale and
     causal flag, and ``mask`` if it had one), dout the gradient at out.  Every tensor must be contiguous
-    ([B, H, N, D], lse float32 [B, Hq, Nq]) and on one HIP device; dq, dk, dv
-    are allocated unless given.  Runs on torch's current stream.
+    ([B, H, N, D]; v, out, dout and dv with V's head dimension Dv, which is
+    D or, for D = 192, 128; lse float32 [B, Hq, Nq]) and on one HIP device;
+    dq, dk, dv are allocated unless given.  Runs on torch's current stream.
     """
     import torch
     lib = load_library()
@@ -350,12 +357,13 @@ def attn_bwd(q, k, v, out, lse, dout, causal=False, scale: float | None = None,
         raise ValueError("q must be 4-D [B, H, N, D]")
     B, Hq, Nq, D = q.shape
     Hkv, Nkv = k.shape[1], k.shape[2]
-    if tuple(k.shape) != (B, Hkv, Nkv, D) or tuple(v.shape) != tuple(k.shape):
+    Dv = v.shape[3] if v.dim() == 4 else -1
+    if tuple(k.shape) != (B, Hkv, Nkv, D) or tuple(v.shape) != (B, Hkv, Nkv, Dv):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
                          f"v{tuple(v.shape)}")
     for name, t in (("out", out), ("dout", dout)):
-        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q's shape and dtype")
+        if tuple(t.shape) != (B, Hq, Nq, Dv) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, Hq, Nq, Dv] with q's dtype")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
@@ -375,7 +383,18 @@ def attn_bwd(q, k, v, out, lse, dout, causal=False, scale: float | None = None,
     dq, dk, dv = grads
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if mask is None:
+        if Dv != D:
+            m, mtype, ms = None, ATTN_MASK_NONE, None
+            if mask is not None:
+                if mask.device != q.device:
+                    raise ValueError("mask must be on q's device")
+                m, mtype, ms = mask_view(mask, B, Hq, Nq, Nkv, q.dtype)
+            rc = lib.attn_bwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, Dv,
+                                 None if m is None else m.data_ptr(), mtype, ms, float(scale),
+                                 causal_code(causal), dt, stream)
+        elif mask is None:
             rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                               dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, float(scale),

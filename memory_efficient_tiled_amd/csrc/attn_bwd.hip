@@ -219,22 +219,32 @@ __device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst,
 // so two waves fit on a SIMD and one wave's softmax work overlaps the
 // other's matrix products.  Q and dO tiles are in LDS twice each, two
 // buffers deep, with lse2 and Delta.
-template <int D, class Tag, bool CAUSAL, bool MASKED>
+//
+// With V rows of DV != D elements (the (192, 128) pair) the two waves of a
+// pair differ: the P wave holds K (D) and accumulates dV^T (DV rows), the
+// dS wave holds V (DV) and accumulates dK^T (D rows); Q tiles are D wide
+// and dO tiles DV wide.
+template <int D, int DV, class Tag, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   // 64-row query tiles; 32 at D = 256, whose K (or V) operands and dK (or
-  // dV) accumulators alone take 192 registers
-  constexpr int NQB = D == 256 ? 1 : 2;
+  // dV) accumulators alone take 192 registers, and for the (192, 128) pair
+  // (the same registers; 64-row Q and dO tiles would not fit LDS)
+  constexpr bool SQ = D == DV;
+  constexpr int NQB = D == 256 || !SQ ? 1 : 2;
   constexpr int NW = 8, BK = 128, BQ = NQB * 32;
-  constexpr int DP = compute_dim(D);
+  constexpr int DP = compute_dim(D), DVP = compute_dim(DV);
   constexpr int DC = DP / 16, NDB = DP / 32, NKC = BQ / 16;
-  constexpr int TILE = BQ * DP;
+  constexpr int DCV = DVP / 16, NDBV = DVP / 32;
+  constexpr int DCM = DC > DCV ? DC : DCV, NDBM = NDB > NDBV ? NDB : NDBV;
+  constexpr int TILE = BQ * DP, TILEV = BQ * DVP;
   constexpr int IPW = TileCopy<D, BQ, NW>::PER_WAVE;
+  constexpr int IPWV = TileCopy<DV, BQ, NW>::PER_WAVE;
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t qr[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t qt[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t gr[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t gt[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t gr[2][TILEV];
+  __shared__ __attribute__((aligned(1024))) uint16_t gt[2][TILEV];
   __shared__ __attribute__((aligned(1024))) u32x4 xp[4][NKC][64];
   // lse2 and Delta of a tile: one dword per lane of a 64-lane copy (lanes
   // past the tile's rows write zeros), so 64 entries even when BQ = 32
@@ -262,21 +272,27 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 
   const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
   const uint16_t* kv = pw ? p.k : p.v;
-  u32x4 bf[DC];
+  const int kvw = pw ? D : DV;  // row length of K (P waves) or V (dS waves)
+  u32x4 bf[DCM];
 #pragma unroll
-  for (int kc = 0; kc < DC; ++kc) {
+  for (int kc = 0; kc < DCM; ++kc) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < p.Nkv && kc * 16 + hl * 8 < D)
-      x = *(const u32x4*)(kv + (krow0 + key) * D + kc * 16 + hl * 8);
+    if (key < p.Nkv && kc * 16 + hl * 8 < kvw)
+      x = *(const u32x4*)(kv + (krow0 + key) * kvw + kc * 16 + hl * 8);
     bf[kc] = x;
   }
-  f32x16 acc[NDB];
+  f32x16 acc[NDBM];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NDBM; ++i) acc[i] = f32x16{};
 
-  uint32_t roff[IPW], toff[IPW];
+  // copy offsets of the Q tiles and (DV != D) of the dO tiles
+  uint32_t roff[IPW], toff[IPW], groff[SQ ? 1 : IPWV], gtoff[SQ ? 1 : IPWV];
   copy_offsets<D, BQ, NW, true>(wave, lane, roff);
   copy_offsets<D, BQ, NW, false>(wave, lane, toff);
+  if constexpr (!SQ) {
+    copy_offsets<DV, BQ, NW, true>(wave, lane, groff);
+    copy_offsets<DV, BQ, NW, false>(wave, lane, gtoff);
+  }
 
   const int nqt = (p.Nq + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? min(nqt, max(0, k0 - p.coff) / BQ) : 0;
@@ -293,11 +309,16 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     tile_start(u, &hq, &q0);
     const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
     const uint16_t* qb = p.q + qrow0 * D;
-    const uint16_t* gb = p.dout + qrow0 * D;
+    const uint16_t* gb = p.dout + qrow0 * DV;
     copy_tile<D, BQ, NW>(qb, q0, p.Nq, qr[buf], wave, roff);
     copy_tile<D, BQ, NW>(qb, q0, p.Nq, qt[buf], wave, toff);
-    copy_tile<D, BQ, NW>(gb, q0, p.Nq, gr[buf], wave, roff);
-    copy_tile<D, BQ, NW>(gb, q0, p.Nq, gt[buf], wave, toff);
+    if constexpr (SQ) {
+      copy_tile<D, BQ, NW>(gb, q0, p.Nq, gr[buf], wave, roff);
+      copy_tile<D, BQ, NW>(gb, q0, p.Nq, gt[buf], wave, toff);
+    } else {
+      copy_tile<DV, BQ, NW>(gb, q0, p.Nq, gr[buf], wave, groff);
+      copy_tile<DV, BQ, NW>(gb, q0, p.Nq, gt[buf], wave, gtoff);
+    }
     if (wave < 2) {  // lse2 (wave 0) and Delta (wave 1): one dword per lane
       const float* src = (wave == 0 ? p.lse2 : p.delta) + qrow0 + q0;
       const int n = min(BQ, p.Nq - q0);
@@ -313,6 +334,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   const int v_key = 4 * hl + (v_r >> 2);
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
   const int v_sw = v_swz<DP>(v_key);
+  const int v_swv = v_swz<DVP>(v_key);
 
   // P in place of S (P waves); accumulator register e of block qb is query
   // row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.  With a mask, its base-2
@@ -360,15 +382,24 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     tile_start(u, &hq, &q0);
 
     // 1. S (P waves) or dP (dS waves)
-    const uint16_t* ra = pw ? qr[buf] : gr[buf];
     f32x16 s[NQB];
+    auto prod1 = [&](auto dcc, auto rwc, const uint16_t* ra) {
+      constexpr int DCX = decltype(dcc)::value, RW = decltype(rwc)::value;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      s[qb] = f32x16{};
+      for (int qb = 0; qb < NQB; ++qb) {
+        s[qb] = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < DC; ++kc)
-        s[qb] = N::mfma(read_rows<DP>(ra, qb * 32 + l32, kc, hl), bf[kc], s[qb]);
-    }
+        for (int kc = 0; kc < DCX; ++kc)
+          s[qb] = N::mfma(read_rows<RW>(ra, qb * 32 + l32, kc, hl), bf[kc], s[qb]);
+      }
+    };
+    if constexpr (SQ)
+      prod1(std::integral_constant<int, DC>{}, std::integral_constant<int, DP>{},
+            pw ? qr[buf] : gr[buf]);
+    else if (pw)
+      prod1(std::integral_constant<int, DC>{}, std::integral_constant<int, DP>{}, qr[buf]);
+    else
+      prod1(std::integral_constant<int, DCV>{}, std::integral_constant<int, DVP>{}, gr[buf]);
     u32x4 bop[NKC];
     if (pw) {
       if (CAUSAL && kw0 + 31 > q0 + p.coff)
@@ -403,14 +434,25 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
       }
     }
     // 2. dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves)
-    const uint16_t* rb = pw ? gt[buf] : qt[buf];
+    auto prod2 = [&](auto ndc, auto rwc, const uint16_t* rb, int sw) {
+      constexpr int NDX = decltype(ndc)::value, RW = decltype(rwc)::value;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      const int row = kc * 16 + v_key;
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int row = kc * 16 + v_key;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = N::mfma(read_cols<DP>(rb, row, db, v_d, v_sw), bop[kc], acc[db]);
-    }
+        for (int db = 0; db < NDX; ++db)
+          acc[db] = N::mfma(read_cols<RW>(rb, row, db, v_d, sw), bop[kc], acc[db]);
+      }
+    };
+    if constexpr (SQ)
+      prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{},
+            pw ? gt[buf] : qt[buf], v_sw);
+    else if (pw)
+      prod2(std::integral_constant<int, NDBV>{}, std::integral_constant<int, DVP>{}, gt[buf],
+            v_swv);
+    else
+      prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{}, qt[buf],
+            v_sw);
   };
 
   if (steps > 0) issue(0, std::integral_constant<int, 0>{});
@@ -421,28 +463,29 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 
   if (key < p.Nkv) {
     if (pw)
-      store_kv_grad<D, Tag>(p, p.dv, p.dvp, acc, 1.f, krow0 + key, hs, hl);
+      store_kv_grad<DV, Tag>(p, p.dv, p.dvp, acc, 1.f, krow0 + key, hs, hl);
     else
       store_kv_grad<D, Tag>(p, p.dk, p.dkp, acc, p.scale, krow0 + key, hs, hl);
   }
 }
 
 // dK, dV = sums of the hsplit partials (dK times scale), rounded to 16 bits;
-// four elements per thread.
+// four elements per thread.  n4k (n4v): float4s per partial of dK (dV).
 template <class Tag>
-__global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4) {
+__global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4k, size_t n4v) {
   using N = Num<Tag>;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const size_t stride = n4;  // float4s per partial
-  f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
-  for (int h = 0; h < p.hsplit; ++h) {
-    a += ((const f32x4*)p.dkp)[h * stride + i];
-    c += ((const f32x4*)p.dvp)[h * stride + i];
+  if (i < n4k) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < p.hsplit; ++h) a += ((const f32x4*)p.dkp)[h * n4k + i];
+    a *= p.scale;
+    ((u32x2*)p.dk)[i] = u32x2{N::pack2(a[0], a[1]), N::pack2(a[2], a[3])};
   }
-  a *= p.scale;
-  ((u32x2*)p.dk)[i] = u32x2{N::pack2(a[0], a[1]), N::pack2(a[2], a[3])};
-  ((u32x2*)p.dv)[i] = u32x2{N::pack2(c[0], c[1]), N::pack2(c[2], c[3])};
+  if (i < n4v) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < p.hsplit; ++h) c += ((const f32x4*)p.dvp)[h * n4v + i];
+    ((u32x2*)p.dv)[i] = u32x2{N::pack2(c[0], c[1]), N::pack2(c[2], c[3])};
+  }
 }
 
 // dQ for 128 query rows (4 waves x 32) of query head hq: loop over key
@@ -453,19 +496,22 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4) 
 // Q and dO stay in registers; K is copied into LDS twice (row-read and
 // transposed layouts) and V once, two buffers deep, the loop unrolled by two.
 // One wave per SIMD at D = 256: Q, dO and the dQ accumulators take 256
-// registers.
-template <int D, class Tag, bool CAUSAL, bool MASKED>
-__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParams p) {
+// registers; likewise for the (192, 128) pair (208).  With V rows of
+// DV != D elements, dO and V tiles are DV wide and dP reduces over DV.
+template <int D, int DV, class Tag, bool CAUSAL, bool MASKED>
+__global__ __launch_bounds__(256, D == 256 || D != DV ? 1 : 2) void attn_dq_kernel(BwdParams p) {
+  constexpr bool SQ = D == DV;
   constexpr int NW = 4, BM = NW * 32, BN = 32;
-  constexpr int DP = compute_dim(D);
-  constexpr int DC = DP / 16, NDB = DP / 32;
-  constexpr int TILE = BN * DP;
+  constexpr int DP = compute_dim(D), DVP = compute_dim(DV);
+  constexpr int DC = DP / 16, NDB = DP / 32, DCV = DVP / 16;
+  constexpr int TILE = BN * DP, TILEV = BN * DVP;
   constexpr int IPW = TileCopy<D, BN, NW>::PER_WAVE;
+  constexpr int IPWV = TileCopy<DV, BN, NW>::PER_WAVE;
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kr[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t ktr[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t vr[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vr[2][TILEV];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -486,16 +532,33 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
 
   const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
   const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
-  u32x4 qf[DC], gf[DC];
+  u32x4 qf[DC], gf[DCV];
+  if constexpr (SQ) {
 #pragma unroll
-  for (int kc = 0; kc < DC; ++kc) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (qrow < p.Nq && kc * 16 + hl * 8 < D) {
-      x = *(const u32x4*)(p.q + (qrow0 + qrow) * D + kc * 16 + hl * 8);
-      y = *(const u32x4*)(p.dout + (qrow0 + qrow) * D + kc * 16 + hl * 8);
+    for (int kc = 0; kc < DC; ++kc) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (qrow < p.Nq && kc * 16 + hl * 8 < D) {
+        x = *(const u32x4*)(p.q + (qrow0 + qrow) * D + kc * 16 + hl * 8);
+        y = *(const u32x4*)(p.dout + (qrow0 + qrow) * D + kc * 16 + hl * 8);
+      }
+      qf[kc] = x;
+      gf[kc < DCV ? kc : 0] = y;
     }
-    qf[kc] = x;
-    gf[kc] = y;
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < DC; ++kc) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qrow < p.Nq && kc * 16 + hl * 8 < D)
+        x = *(const u32x4*)(p.q + (qrow0 + qrow) * D + kc * 16 + hl * 8);
+      qf[kc] = x;
+    }
+#pragma unroll
+    for (int kc = 0; kc < DCV; ++kc) {
+      u32x4 y = {0u, 0u, 0u, 0u};
+      if (qrow < p.Nq && kc * 16 + hl * 8 < DV)
+        y = *(const u32x4*)(p.dout + (qrow0 + qrow) * DV + kc * 16 + hl * 8);
+      gf[kc] = y;
+    }
   }
   const float nl2 = qrow < p.Nq ? -p.lse2[qrow0 + qrow] : 0.f;
   const float dl = qrow < p.Nq ? p.delta[qrow0 + qrow] : 0.f;
@@ -503,16 +566,20 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
-  uint32_t roff[IPW], toff[IPW];
+  uint32_t roff[IPW], toff[IPW], vroff[SQ ? 1 : IPWV];
   copy_offsets<D, BN, NW, true>(wave, lane, roff);
   copy_offsets<D, BN, NW, false>(wave, lane, toff);
+  if constexpr (!SQ) copy_offsets<DV, BN, NW, true>(wave, lane, vroff);
   const uint16_t* Kg = p.k + krow0 * D;
-  const uint16_t* Vg = p.v + krow0 * D;
+  const uint16_t* Vg = p.v + krow0 * DV;
   auto issue = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, kr[buf], wave, roff);
     copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, ktr[buf], wave, toff);
-    copy_tile<D, BN, NW>(Vg, t * BN, p.Nkv, vr[buf], wave, roff);
+    if constexpr (SQ)
+      copy_tile<D, BN, NW>(Vg, t * BN, p.Nkv, vr[buf], wave, roff);
+    else
+      copy_tile<DV, BN, NW>(Vg, t * BN, p.Nkv, vr[buf], wave, vroff);
   };
 
   const int v_g = lane >> 4, v_r = lane & 15;
@@ -555,10 +622,18 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
     __syncthreads();
     if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, buf ^ 1>{});
     f32x16 s = f32x16{}, dp = f32x16{};
+    if constexpr (SQ) {
 #pragma unroll
-    for (int kc = 0; kc < DC; ++kc) {
-      s = N::mfma(read_rows<DP>(kr[buf], l32, kc, hl), qf[kc], s);
-      dp = N::mfma(read_rows<DP>(vr[buf], l32, kc, hl), gf[kc], dp);
+      for (int kc = 0; kc < DC; ++kc) {
+        s = N::mfma(read_rows<DP>(kr[buf], l32, kc, hl), qf[kc], s);
+        dp = N::mfma(read_rows<DP>(vr[buf], l32, kc, hl), gf[kc < DCV ? kc : 0], dp);
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < DC; ++kc) s = N::mfma(read_rows<DP>(kr[buf], l32, kc, hl), qf[kc], s);
+#pragma unroll
+      for (int kc = 0; kc < DCV; ++kc)
+        dp = N::mfma(read_rows<DVP>(vr[buf], l32, kc, hl), gf[kc], dp);
     }
     if (CAUSAL && t * BN + 31 > qw0 + p.coff)
       probs(std::true_type{}, s, dp, t);
@@ -592,12 +667,15 @@ bool overlaps_bytes(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Q, K, dQ, dK rows have D elements; V, O, dO, dV rows Dv (= D, or the
+// (192, 128) pair).
 int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, const void* dq, const void* dk, const void* dv, int B, int Hq,
-                 int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype) {
+                 int Hkv, int Nq, int Nkv, int D, int Dv, float scale, int causal, int dtype) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
-  if (D != 64 && D != 80 && D != 96 && D != 128 && D != 256) return ATTN_EINVAL;
+  const bool sq_ok = D == 64 || D == 80 || D == 96 || D == 128 || D == 256;
+  if (!(Dv == D ? sq_ok : (D == 192 && Dv == 128))) return ATTN_EINVAL;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
   if (!isfinite(scale)) return ATTN_EINVAL;
@@ -610,8 +688,9 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   const size_t rows = (size_t)B * Hq * Nq, krows = (size_t)B * Hkv * Nkv;
   if (rows > (size_t)INT32_MAX || krows > (size_t)INT32_MAX) return ATTN_EINVAL;
   const size_t qb = rows * D * 2, kb = krows * D * 2;
-  const size_t in_bytes[6] = {qb, kb, kb, qb, qb, rows * 4};
-  const size_t out_bytes[3] = {qb, kb, kb};
+  const size_t ob = rows * Dv * 2, vb = krows * Dv * 2;
+  const size_t in_bytes[6] = {qb, kb, vb, ob, ob, rows * 4};
+  const size_t out_bytes[3] = {qb, kb, vb};
   for (int i = 0; i < 3; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps_bytes(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_EINVAL;
@@ -639,7 +718,7 @@ struct BwdMask {
 };
 
 int validate_bwd_mask(const BwdMask& m, const void* dq, const void* dk, const void* dv, int B,
-                      int Hq, int Hkv, int Nq, int Nkv, int D) {
+                      int Hq, int Hkv, int Nq, int Nkv, int D, int Dv) {
   if (m.type == ATTN_MASK_NONE) return ATTN_OK;
   if (m.type != ATTN_MASK_BOOL && m.type != ATTN_MASK_ADD) return ATTN_EINVAL;
   if (!m.ptr || ((uintptr_t)m.ptr & 7)) return ATTN_EINVAL;
@@ -649,17 +728,18 @@ int validate_bwd_mask(const BwdMask& m, const void* dq, const void* dk, const vo
                              (__int128)(Nq - 1) * m.sq + Nkv);
   if (mb > ((__int128)1 << 62)) return ATTN_EINVAL;
   const size_t qb = (size_t)B * Hq * Nq * D * 2, kb = (size_t)B * Hkv * Nkv * D * 2;
+  const size_t vb = (size_t)B * Hkv * Nkv * Dv * 2;
   if (overlaps_bytes(dq, qb, m.ptr, (size_t)mb) || overlaps_bytes(dk, kb, m.ptr, (size_t)mb) ||
-      overlaps_bytes(dv, kb, m.ptr, (size_t)mb))
+      overlaps_bytes(dv, vb, m.ptr, (size_t)mb))
     return ATTN_EINVAL;
   return ATTN_OK;
 }
 
-template <int D, class Tag, bool MASKED>
+template <int D, int DV, class Tag, bool MASKED>
 hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   const int rows = p.B * p.Hq * p.Nq;
-  const size_t threads = (size_t)rows * bwd_delta_lanes(D);
-  hipLaunchKernelGGL((attn_delta_kernel<D, Tag>), dim3((unsigned)((threads + 255) / 256)),
+  const size_t threads = (size_t)rows * bwd_delta_lanes(DV);  // Delta: rows of O and dO
+  hipLaunchKernelGGL((attn_delta_kernel<DV, Tag>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, st, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -667,17 +747,19 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   pk.n_tiles = (p.Nkv + 127) / 128;
   pk.total = p.B * p.Hkv * p.hsplit * pk.n_tiles;
   if (causal)
-    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, true, MASKED>), dim3(pk.total), dim3(512),
-                       0, st, pk);
+    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, DV, Tag, true, MASKED>), dim3(pk.total),
+                       dim3(512), 0, st, pk);
   else
-    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, Tag, false, MASKED>), dim3(pk.total), dim3(512),
-                       0, st, pk);
+    hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, DV, Tag, false, MASKED>), dim3(pk.total),
+                       dim3(512), 0, st, pk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.hsplit > 1) {
-    const size_t n4 = (size_t)p.B * p.Hkv * p.Nkv * D / 4;
+    const size_t n4k = (size_t)p.B * p.Hkv * p.Nkv * D / 4;
+    const size_t n4v = (size_t)p.B * p.Hkv * p.Nkv * DV / 4;
+    const size_t n4 = n4k > n4v ? n4k : n4v;
     hipLaunchKernelGGL((attn_dkdv_reduce<Tag>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                       st, p, n4);
+                       st, p, n4k, n4v);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -685,39 +767,42 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
   pq.n_tiles = (p.Nq + 127) / 128;
   pq.total = p.B * p.Hq * pq.n_tiles;
   if (causal)
-    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, true, MASKED>), dim3(pq.total), dim3(256), 0, st,
-                       pq);
+    hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, true, MASKED>), dim3(pq.total), dim3(256), 0,
+                       st, pq);
   else
-    hipLaunchKernelGGL((attn_dq_kernel<D, Tag, false, MASKED>), dim3(pq.total), dim3(256), 0, st,
-                       pq);
+    hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, false, MASKED>), dim3(pq.total), dim3(256), 0,
+                       st, pq);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DV>
 hipError_t launch_bwd_masks(bool bf, bool masked, const BwdParams& p, bool cz, hipStream_t st) {
   if (masked)
-    return bf ? launch_bwd<D, TagBF16, true>(p, cz, st) : launch_bwd<D, TagF16, true>(p, cz, st);
-  return bf ? launch_bwd<D, TagBF16, false>(p, cz, st) : launch_bwd<D, TagF16, false>(p, cz, st);
+    return bf ? launch_bwd<D, DV, TagBF16, true>(p, cz, st)
+              : launch_bwd<D, DV, TagF16, true>(p, cz, st);
+  return bf ? launch_bwd<D, DV, TagBF16, false>(p, cz, st)
+            : launch_bwd<D, DV, TagF16, false>(p, cz, st);
 }
 
-hipError_t launch_bwd_d(int D, bool bf, bool masked, const BwdParams& p, bool cz,
+hipError_t launch_bwd_d(int D, int Dv, bool bf, bool masked, const BwdParams& p, bool cz,
                         hipStream_t st) {
+  if (Dv != D) return launch_bwd_masks<192, 128>(bf, masked, p, cz, st);
   switch (D) {
-    case 64: return launch_bwd_masks<64>(bf, masked, p, cz, st);
-    case 80: return launch_bwd_masks<80>(bf, masked, p, cz, st);
-    case 96: return launch_bwd_masks<96>(bf, masked, p, cz, st);
-    case 256: return launch_bwd_masks<256>(bf, masked, p, cz, st);
-    default: return launch_bwd_masks<128>(bf, masked, p, cz, st);
+    case 64: return launch_bwd_masks<64, 64>(bf, masked, p, cz, st);
+    case 80: return launch_bwd_masks<80, 80>(bf, masked, p, cz, st);
+    case 96: return launch_bwd_masks<96, 96>(bf, masked, p, cz, st);
+    case 256: return launch_bwd_masks<256, 256>(bf, masked, p, cz, st);
+    default: return launch_bwd_masks<128, 128>(bf, masked, p, cz, st);
   }
 }
 
 int run_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
-            int Nkv, int D, float scale, int causal, int dtype, void* stream,
+            int Nkv, int D, int Dv, float scale, int causal, int dtype, void* stream,
             const BwdMask& m) {
-  int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
+  int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, Dv, scale,
                         causal, dtype);
-  if (rc == ATTN_OK) rc = validate_bwd_mask(m, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D);
+  if (rc == ATTN_OK) rc = validate_bwd_mask(m, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, Dv);
   if (rc != ATTN_OK) return rc;
   int cus = 0;
   rc = attn_host::check_device(&cus);
@@ -734,7 +819,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* out, const 
   const size_t rows = (size_t)B * Hq * Nq;
   const size_t rows_bytes = (rows * sizeof(float) + 255) / 256 * 256;
   const size_t part = hsplit > 1 ? (size_t)hsplit * B * Hkv * Nkv * D * sizeof(float) : 0;
-  hipError_t e = hipMallocAsync(&ws, 2 * rows_bytes + 2 * part, st);
+  const size_t partv = hsplit > 1 ? (size_t)hsplit * B * Hkv * Nkv * Dv * sizeof(float) : 0;
+  hipError_t e = hipMallocAsync(&ws, 2 * rows_bytes + part + partv, st);
   if (e != hipSuccess || !ws) {
     attn_host::set_last_hip_error((int)e);
     (void)hipGetLastError();
@@ -770,7 +856,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* out, const 
   p.msb = m.sb, p.msh = m.sh, p.msq = m.sq;
   p.mask_mode = m.type;
   const bool cz = causal != 0, bf = dtype == ATTN_BF16;
-  e = launch_bwd_d(D, bf, m.type != ATTN_MASK_NONE, p, cz, st);
+  e = launch_bwd_d(D, Dv, bf, m.type != ATTN_MASK_NONE, p, cz, st);
   const hipError_t ef = hipFreeAsync(ws, st);
   if (e == hipSuccess) e = ef;
   if (e != hipSuccess) {
@@ -804,14 +890,14 @@ int attn_bwd_check(const void* q, const void* k, const void* v, const void* out,
                    const void* dout, const float* lse, const void* dq, const void* dk,
                    const void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale,
                    int causal, int dtype) {
-  return validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
-                      dtype);
+  return validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, D, scale,
+                      causal, dtype);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
              int Nkv, int D, float scale, int causal, int dtype, void* stream) {
-  return run_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+  return run_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, D, scale, causal,
                  dtype, stream, BwdMask());
 }
 
@@ -820,7 +906,7 @@ int attn_bwd_masked(const void* q, const void* k, const void* v, const void* out
                     int Hq, int Hkv, int Nq, int Nkv, int D, const void* mask, int mask_type,
                     const long long* mask_stride, float scale, int causal, int dtype,
                     void* stream) {
-  return run_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+  return run_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, D, scale, causal,
                  dtype, stream, bwd_mask(mask, mask_type, mask_stride));
 }
 
@@ -829,11 +915,31 @@ int attn_bwd_masked_check(const void* q, const void* k, const void* v, const voi
                           const void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                           const void* mask, int mask_type, const long long* mask_stride,
                           float scale, int causal, int dtype) {
-  const int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
-                              causal, dtype);
+  const int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, D,
+                              scale, causal, dtype);
   if (rc != ATTN_OK) return rc;
   return validate_bwd_mask(bwd_mask(mask, mask_type, mask_stride), dq, dk, dv, B, Hq, Hkv, Nq,
-                           Nkv, D);
+                           Nkv, D, D);
+}
+
+int attn_bwd_dv(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+                int Nkv, int D, int Dv, const void* mask, int mask_type,
+                const long long* mask_stride, float scale, int causal, int dtype, void* stream) {
+  return run_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, Dv, scale, causal,
+                 dtype, stream, bwd_mask(mask, mask_type, mask_stride));
+}
+
+int attn_bwd_dv_check(const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, const void* dq, const void* dk,
+                      const void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D, int Dv,
+                      const void* mask, int mask_type, const long long* mask_stride, float scale,
+                      int causal, int dtype) {
+  const int rc = validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, Dv,
+                              scale, causal, dtype);
+  if (rc != ATTN_OK) return rc;
+  return validate_bwd_mask(bwd_mask(mask, mask_type, mask_stride), dq, dk, dv, B, Hq, Hkv, Nq,
+                           Nkv, D, Dv);
 }
 
 }  // extern "C"

@@ -179,10 +179,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 //  (r >> 2) & 3 (which keeps it below 12) spreads 16 consecutive rows over
 //  all 16 groups, and 4 consecutive keys already cover four disjoint
 //  quarters for the transposing reads.
-//  K rows of 384 bytes (D = 192, 24 chunks) start on bank group 0 or 8 for
-//  even and odd r; XOR-ing the chunk with (r >> 1) & 7 (which keeps it in its
-//  aligned group of 8, so below 24) gives 16 consecutive rows 16 distinct
-//  groups, as for 128-byte rows.  (V rows of 192 elements are not used.)
+//  Rows of 384 bytes (D = 192, 24 chunks) start on bank group 0 or 8 for
+//  even and odd r, as 128-byte rows do, and take their swizzles: XOR-ing
+//  the chunk with (r >> 1) & 7 (row reads) or 4 * ((r >> 1) & 1)
+//  (transposing reads) keeps it in its aligned group of 8, so below 24.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256,
@@ -194,9 +194,12 @@ __device__ __forceinline__ int k_swz(int r) {
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
-  static_assert(D == 64 || D == 96 || D == 128 || D == 256,
-                "V swizzles cover D = 64, 96, 128, 256");
-  return D >= 128 ? 4 * (r & 3) : D == 96 ? 0 : 4 * ((r >> 1) & 1);
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256,
+                "transposed-read swizzles cover D = 64, 96, 128, 192, 256");
+  return D == 192 ? 4 * ((r >> 1) & 1)
+         : D >= 128 ? 4 * (r & 3)
+         : D == 96  ? 0
+                    : 4 * ((r >> 1) & 1);
 }
 
 // Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9.

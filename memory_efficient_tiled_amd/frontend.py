@@ -6,7 +6,7 @@ it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
 
 * ``sdpa(query, key, value, ...)`` has SDPA's signature and semantics for
   what this library computes (head dim 64, 80, 96, 128 or 256, or query and
-  key head dim 192 with value head dim 128 when no gradient is needed; no dropout;
+  key head dim 192 with value head dim 128; no dropout;
   top-left causal through ``is_causal``; PyTorch's causal biases
   ``causal_upper_left`` / ``causal_lower_right`` as ``attn_mask`` (the
   latter is bottom-right alignment, rows that see no key give 0); boolean
@@ -106,8 +106,6 @@ def unsupported_reason(query, key, value, attn_mask=None, dropout_p=0.0,
             (Ev == E and E in (64, 80, 96, 128, 256)) or (E, Ev) == (192, 128)):
         return ("head dimension must be 64, 80, 96, 128 or 256 for query, key and value, "
                 "or 192 for query and key with 128 for value")
-    if Ev != E and torch.is_grad_enabled() and any(t.requires_grad for t in ts):
-        return "no gradients for a value head dimension other than the query's"
     if key.shape[:-1] != value.shape[:-1]:
         return "key and value must have one shape apart from the head dimension"
     if query.shape[:-3] != key.shape[:-3]:

@@ -58,6 +58,14 @@ class Workload:
         f = 2.0 * self.B * self.Hq * self.Nq * self.Nkv * (self.D + self.Dv)
         return f / 2.0 if self.causal else f
 
+    @property
+    def bwd_flops(self) -> float:
+        """Algorithmic flops of the gradients: S, dP, dV, dK, dQ, i.e.
+        2*B*Hq*Nq*Nkv*(3*D + 2*Dv) (10*...*D when Dv = D, 2.5x the forward),
+        halved when causal."""
+        f = 2.0 * self.B * self.Hq * self.Nq * self.Nkv * (3 * self.D + 2 * self.Dv)
+        return f / 2.0 if self.causal else f
+
     def describe(self) -> str:
         dv = f" Dv={self.Dv}" if self.Dv != self.D else ""
         return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} Nq={self.Nq} "
@@ -190,11 +198,13 @@ def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
 
 def make_dout(x: Inputs, seed: int | None = None) -> np.ndarray:
     """The gradient arriving at the output for backward tests: iid N(0,1) of
-    q's shape, rounded to the input type, from its own PCG64 stream (keyed on
-    [seed, 1], so q, k and v are unaffected)."""
+    the output's shape (q's, with v's head dimension), rounded to the input
+    type, from its own PCG64 stream (keyed on [seed, 1], so q, k and v are
+    unaffected)."""
     s = x.seed if seed is None else seed
     rng = np.random.Generator(np.random.PCG64([s, 1]))
-    return to_storage(rng.standard_normal(x.q.shape, dtype=np.float32), x.dtype)
+    shape = tuple(x.q.shape[:3]) + (x.v.shape[3],)
+    return to_storage(rng.standard_normal(shape, dtype=np.float32), x.dtype)
 
 
 def sample_rows(rng: np.random.Generator, Hq: int, Nq: int, R: int) -> np.ndarray:

@@ -103,13 +103,14 @@ def delta_terms(x, do, ref, causal, causal_offset=0):
     return t_dq, t_dk, 0.0
 
 
-def run_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed):
-    """``causal``: False, True (top-left) or "bottom_right"."""
+def run_case(device, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed, Dv=None):
+    """``causal``: False, True (top-left) or "bottom_right"; ``Dv``: V's
+    head dimension (default D)."""
     import torch
-    what = (f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} "
+    what = (f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} Dv={Dv} {dtype} "
             f"causal={causal} seed={seed}")
     log(what)
-    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed)
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=seed, Dv=Dv)
     do = inputs.make_dout(x)
     q, k, v, g = (to_device(a, dtype, device) for a in (x.q, x.k, x.v, do))
     out, lse = binding.attn_fwd(q, k, v, causal=causal)
@@ -300,3 +301,57 @@ def test_masked_gradients_d96(gpu_device):
 def test_head_dim_256(gpu_device, causal):
     # 32-row query tiles in the dK/dV kernel, one wave per SIMD in the dQ kernel
     run_case(gpu_device, 1, 4, 2, 200, 260, 256, inputs.BF16, causal, seed=256)
+
+
+# -- V rows of another width: (D, Dv) = (192, 128) ----------------------------
+# 32-row query tiles in the dK/dV kernel (the P wave holds K and accumulates
+# dV over 128 columns, the dS wave holds V and accumulates dK over 192), one
+# wave per SIMD in the dQ kernel.  GQA 3 (dK/dV over head-split partials)
+# and MHA (written directly).
+
+@pytest.mark.parametrize("causal", [False, True, "bottom_right"])
+def test_value_width_gqa(gpu_device, causal):
+    run_case(gpu_device, 1, 6, 2, 211, 300, 192, inputs.BF16, causal, seed=192, Dv=128)
+
+
+@pytest.mark.parametrize("dtype", [inputs.F16, inputs.BF16])
+def test_value_width_mha(gpu_device, dtype):
+    run_case(gpu_device, 2, 2, 2, 300, 170, 192, dtype, True, seed=193, Dv=128)
+
+
+def test_value_width_masked(gpu_device):
+    import torch
+    dtype = inputs.BF16
+    x = inputs.make_inputs(1, 4, 2, 130, 150, 192, dtype, seed=194, Dv=128)
+    do = inputs.make_dout(x)
+    keep = np.random.Generator(np.random.PCG64(195)).random((130, 150)) < 0.75
+    mt = torch.from_numpy(keep).to(gpu_device)
+    q, k, v, g = (to_device(a, dtype, gpu_device) for a in (x.q, x.k, x.v, do))
+    out, lse = binding.attn_fwd(q, k, v, mask=mt)
+    dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, g, mask=mt)
+    torch.cuda.synchronize(gpu_device)
+    bias = np.broadcast_to(np.where(keep, 0.0, -np.inf), (1, 4, 130, 150))
+    dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
+    ref = oracle.attention_backward(*dec, oracle.scale_value(None, 192), False, bias=bias)
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_grad(name, _host(got), r, dtype, "masked D=192 Dv=128", None,
+                   2e-3 * float(np.sqrt(np.mean(r ** 2))))
+
+
+def test_value_width_sdpa_autograd(gpu_device):
+    """sdpa() under autograd with query/key head dim 192 and value 128."""
+    import torch
+    import memory_efficient_tiled_amd as mta
+    dtype = inputs.BF16
+    x = inputs.make_inputs(1, 4, 4, 180, 180, 192, dtype, seed=196, Dv=128)
+    do = inputs.make_dout(x)
+    leaves = [to_device(a, dtype, gpu_device).requires_grad_(True) for a in (x.q, x.k, x.v)]
+    o = mta.sdpa(*leaves, is_causal=True)
+    assert o.shape == (1, 4, 180, 128)
+    o.backward(to_device(do, dtype, gpu_device))
+    torch.cuda.synchronize(gpu_device)
+    ref = oracle.attention_backward(*(_decode(a, dtype) for a in (x.q, x.k, x.v, do)),
+                                    oracle.scale_value(None, 192), True)
+    terms = delta_terms(x, do, ref, True)
+    for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
+        check_grad(name, _host(leaf.grad), r, dtype, "sdpa autograd D=192 Dv=128", None, t)

@@ -261,3 +261,25 @@ def test_value_width_plan(lib):
     assert plan.workspace_bytes == 4 * rows * (128 + 1) * 4
     assert lib.attn_fwd_num_splits(1, 16, 16, 8192, 8192, 192, 1, BF16, 256) >= 1
     assert lib.attn_fwd_num_splits(1, 16, 16, 8192, 8192, 160, 1, BF16, 256) == EINVAL
+
+
+def test_value_width_backward_validation():
+    """attn_bwd_dv: the (192, 128) pair; V, O, dO and dV sized by Dv."""
+    lib = binding.load_library()
+    null = ctypes.POINTER(ctypes.c_longlong)()
+    # B=1 Hq=4 Hkv=2 Nq=64 Nkv=80: q/dq 64 KiB... placed 1 MiB apart
+    base = [0x10000000 + i * 0x100000 for i in range(9)]
+    q, k, v, o, do, lse, dq, dk, dv = base
+
+    def chk(D=192, Dv=128, **kw):
+        a = dict(q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv)
+        a.update(kw)
+        return lib.attn_bwd_dv_check(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                                     a["dq"], a["dk"], a["dv"], 1, 4, 2, 64, 80, D, Dv,
+                                     None, 0, null, 0.072, 1, BF16)
+    assert chk() == OK
+    assert chk(D=128, Dv=128) == OK
+    assert chk(D=192, Dv=192) == EINVAL and chk(D=128, Dv=64) == EINVAL
+    # dv (2*80*128*2 = 40 KiB) placed so that it ends inside V's buffer
+    assert chk(dv=v - 20 * 1024) == EINVAL
+    assert chk(dv=v - 40 * 1024) == OK
