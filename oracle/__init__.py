@@ -2,9 +2,9 @@
 
 Only tests, the smoke check and the bench's CPU-baseline leg may use it.
 """
-from .softmax_attention import (attention, attention_backward,
+from .softmax_attention import (attention, attention_backward, attention_fp8,
                                 attention_from_storage, decode, decode_bf16,
-                                decode_f16, scale_value)
+                                decode_f16, decode_fp8_e4m3, scale_value)
 
-__all__ = ["attention", "attention_backward", "attention_from_storage",
-           "decode", "decode_bf16", "decode_f16", "scale_value"]
+__all__ = ["attention", "attention_backward", "attention_fp8", "attention_from_storage",
+           "decode", "decode_bf16", "decode_f16", "decode_fp8_e4m3", "scale_value"]

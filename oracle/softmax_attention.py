@@ -79,11 +79,30 @@ def decode_bf16(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def decode_fp8_e4m3(bits: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 bit patterns (uint8) -> float64 (exact).
+
+    Sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is
+    subnormal (m / 8 * 2^-6); there is no infinity, and the two patterns
+    with every exponent and mantissa bit set (0x7f, 0xff) are NaN.  The
+    largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return decode_f16(a)
     if dtype == "bf16":
         return decode_bf16(a)
+    if dtype == "fp8":
+        return decode_fp8_e4m3(a)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -162,6 +181,20 @@ def attention_from_storage(q, k, v, dtype: str, scale: float | None,
     D = q.shape[-1]
     return attention(decode(q, dtype), decode(k, dtype), decode(v, dtype),
                      scale_value(scale, D), causal, rows=rows)
+
+
+def attention_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                  scale: float, causal: bool, rows=None, causal_offset: int = 0):
+    """Attention of FP8 (E4M3) inputs with per-tensor scale factors.
+
+    Reading (the pages are silent on 8-bit inputs): each tensor holds
+    x / x_descale rounded to E4M3, so its values are decode(x8) * x_descale;
+    the result is :func:`attention` of those values (float64), with the
+    softmax scale applied as usual.
+    """
+    return attention(decode_fp8_e4m3(q8) * q_descale, decode_fp8_e4m3(k8) * k_descale,
+                     decode_fp8_e4m3(v8) * v_descale, scale, causal, rows=rows,
+                     causal_offset=causal_offset)
 
 
 # ---------------------------------------------------------------------------

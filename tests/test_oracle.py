@@ -144,6 +144,41 @@ def test_decode_f16_known_patterns():
     assert list(oracle.decode_f16(a)) == [1.0, -2.0, 2.0 ** -24, 65504.0]
 
 
+def test_decode_fp8_known_patterns():
+    """OCP E4M3: closed-form values of chosen patterns."""
+    a = np.array([0x38, 0xB8, 0x01, 0x08, 0x7E, 0x00, 0x80, 0x3C, 0x07], dtype=np.uint8)
+    assert list(oracle.decode_fp8_e4m3(a)) == [1.0, -1.0, 2.0 ** -9, 2.0 ** -6, 448.0, 0.0,
+                                               -0.0, 1.5, 7 * 2.0 ** -9]
+    assert np.isnan(oracle.decode_fp8_e4m3(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+
+
+def test_decode_fp8_matches_torch():
+    """All 256 patterns against PyTorch's float8_e4m3fn conversion."""
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.decode_fp8_e4m3(bits)
+    finite = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~finite)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.signbit(got[finite]), np.signbit(ref[finite]))
+
+
+def test_fp8_descales_fold_into_scale_and_output():
+    """attention(a q, b k, c v, s) = c attention(q, k, v, a b s): the descale
+    factors of the FP8 oracle act as a softmax scale and an output factor."""
+    rng = np.random.default_rng(5)
+    q8, k8, v8 = (rng.integers(0, 256, (1, 2, n, 16)).astype(np.uint8) for n in (9, 13, 13))
+    for a in (q8, k8, v8):
+        a[(a & 0x7F) == 0x7F] = 0x38            # no NaN patterns
+    for causal in (False, True):
+        o, l = oracle.attention_fp8(q8, k8, v8, 0.5, 0.25, 3.0, 0.3, causal)
+        o1, l1 = oracle.attention(oracle.decode_fp8_e4m3(q8), oracle.decode_fp8_e4m3(k8),
+                                  oracle.decode_fp8_e4m3(v8), 0.3 * 0.5 * 0.25, causal)
+        assert np.allclose(o, 3.0 * o1, rtol=1e-12, atol=1e-12)
+        assert np.allclose(l, l1, rtol=1e-12, atol=1e-12)
+
+
 def test_scale_value_is_float32():
     assert oracle.scale_value(None, 64) == 0.125
     assert oracle.scale_value(None, 128) == float(np.float32(1 / math.sqrt(128)))
