@@ -234,6 +234,32 @@ int attn_fwd_dv_check(const void* q, const void* k, const void* v,
                       int dtype);
 
 /*
+ * attn_fwd_fp8 -- the forward on 8-bit inputs: q, k, v hold OCP FP8 E4M3
+ * bytes (torch.float8_e4m3fn) whose values are byte * q_descale (resp.
+ * k_descale, v_descale), one positive finite factor per tensor.  The
+ * pages fix no 8-bit format; this computes O and LSE of the definition
+ * above on those values, with `out` [B,Hq,Nq,D] in out_dtype (ATTN_BF16 or
+ * ATTN_F16) and lse as for attn_fwd.  Both products run on the gfx950
+ * 8-bit matrix instruction; the probabilities are rounded to E4M3 for
+ * P V (relative error up to 2^-4 per probability, 2^-10 absolute below
+ * 2^-6).  Supported: D = 128, contiguous [B,H,N,D] tensors, no mask;
+ * causal modes and num_splits as for attn_fwd_split.  Each call allocates
+ * (stream-ordered) a transposed copy of V, B*Hkv*128*ceil(Nkv/64)*64 bytes,
+ * plus the split partials.  Returns as attn_fwd.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out,
+                 float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                 float q_descale, float k_descale, float v_descale, float scale,
+                 int causal, int out_dtype, int num_splits, void* stream);
+
+/* attn_fwd_fp8_check -- host only: attn_fwd_fp8's validation. */
+int attn_fwd_fp8_check(const void* q, const void* k, const void* v,
+                       const void* out, const float* lse, int B, int Hq,
+                       int Hkv, int Nq, int Nkv, int D, float q_descale,
+                       float k_descale, float v_descale, float scale,
+                       int causal, int out_dtype);
+
+/*
  * attn_plan -- how attn_fwd_split covers a shape (see attn_fwd_plan).
  * Output rows are numbered (b * Hq + h) * Nq + i, 0 <= r < B*Hq*Nq.
  */

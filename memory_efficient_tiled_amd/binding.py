@@ -100,6 +100,11 @@ def load_library():
     lib.attn_fwd_dv_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_dv + \
         [_LLP] * 4 + [_VP, _INT, _LLP, ctypes.c_float, _INT, _INT]
     lib.attn_fwd_dv_check.restype = _INT
+    _F = ctypes.c_float
+    lib.attn_fwd_fp8.argtypes = [_VP] * 5 + shape_args + [_F, _F, _F, _F, _INT, _INT, _INT, _VP]
+    lib.attn_fwd_fp8.restype = _INT
+    lib.attn_fwd_fp8_check.argtypes = [_VP] * 5 + shape_args + [_F, _F, _F, _F, _INT, _INT]
+    lib.attn_fwd_fp8_check.restype = _INT
     lib.attn_bwd_dv.argtypes = [_VP] * 9 + shape_dv + [_VP, _INT, _LLP, ctypes.c_float,
                                                        _INT, _INT, _VP]
     lib.attn_bwd_dv.restype = _INT
@@ -320,6 +325,63 @@ def attn_fwd(q, k, v, causal=False, scale: float | None = None,
                                      out.data_ptr(), lse_ptr, B, Hq, Hkv, Nq, Nkv, D,
                                      qs, ks, vs, os_, m.data_ptr(), mtype, ms, float(scale),
                                      causal_code(causal), dt, int(num_splits), stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return (out, lse) if return_lse else out
+
+
+def attn_fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False,
+                 scale: float | None = None, out_dtype=None, out=None, lse=None,
+                 return_lse: bool = True, num_splits: int = 0):
+    """O = softmax(scale * Q K^T [causal]) V on 8-bit inputs.
+
+    q, k, v: contiguous torch.float8_e4m3fn (or uint8 holding E4M3 bytes)
+    tensors [B, Hq, Nq, 128] and [B, Hkv, Nkv, 128] on one HIP device, whose
+    values are the stored numbers times q_descale, k_descale, v_descale.
+    Returns (out, lse): out [B, Hq, Nq, 128] in ``out_dtype`` (torch.bfloat16
+    by default, or torch.float16), lse float32 [B, Hq, Nq].  ``causal`` and
+    ``num_splits`` as for attn_fwd.  Runs on torch's current stream.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"{name} must be float8_e4m3fn (or uint8 E4M3 bytes)")
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError(f"{name} must be on q's HIP device")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D [B, H, N, D] tensor")
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nkv, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)}")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    codes = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
+    if out_dtype not in codes:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=q.device)
+    elif (tuple(out.shape) != (B, Hq, Nq, D) or out.dtype != out_dtype
+          or not out.is_contiguous() or out.device != q.device):
+        raise ValueError("out must be a contiguous [B, Hq, Nq, D] tensor of out_dtype")
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        elif (tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32
+              or not lse.is_contiguous() or lse.device != q.device):
+            raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if return_lse else None, B, Hq, Hkv, Nq, Nkv, D,
+                              float(q_descale), float(k_descale), float(v_descale),
+                              float(scale), causal_code(causal), codes[out_dtype],
+                              int(num_splits), stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (out, lse) if return_lse else out

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in (
     "attn_fwd.hip", "attn_fwd_d64.hip", "attn_fwd_d80.hip", "attn_fwd_d96.hip",
-    "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_fwd_d192v128.hip", "attn_bwd.hip")]
+    "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_fwd_d192v128.hip", "attn_fwd_fp8.hip",
+    "attn_bwd.hip")]
 OUT = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -225,6 +225,15 @@ namespace attn_host {
 int check_device(int* cus);
 // Records the hipError_t behind an ATTN_EHIP / ATTN_ENOMEM return.
 void set_last_hip_error(int e);
+// How a call on the D = 128 narrow tiles (256 query rows, 64-key tiles)
+// covers its query tiles: tiles [0, first_split) whole, the rest cut into
+// `splits` key ranges of split_len keys whose rows [row0, rows) are merged.
+struct NarrowPlan {
+  int n_qtiles, splits, split_len;
+  long long tiles, first_split, row0, rows;
+};
+void narrow_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int cus,
+                 NarrowPlan* out);
 }  // namespace attn_host
 
 #endif  // ATTN_COMMON_H_

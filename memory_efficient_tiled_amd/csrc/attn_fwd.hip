@@ -397,6 +397,18 @@ int check_device(int* cus) {
   return rc;
 }
 void set_last_hip_error(int e) { g_last_hip_error = e; }
+void narrow_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int cus,
+                 NarrowPlan* out) {
+  // the masked plan always takes the narrow tile of its head dimension
+  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, D, causal, num_splits, cus, true);
+  out->n_qtiles = pl.n_qtiles;
+  out->splits = pl.splits;
+  out->split_len = pl.split_len;
+  out->tiles = pl.tiles;
+  out->first_split = pl.first_split;
+  out->row0 = pl.row0;
+  out->rows = pl.rows;
+}
 }  // namespace attn_host
 
 extern "C" {

@@ -25,6 +25,7 @@ import numpy as np
 
 F16 = "f16"
 BF16 = "bf16"
+FP8 = "fp8"      # OCP E4M3 bytes with one descale factor per tensor
 
 
 @dataclasses.dataclass(frozen=True)
@@ -130,6 +131,15 @@ WORKLOADS["hd192v128-8192"] = _w(name="hd192v128-8192", B=1, Hq=16, Hkv=16, Nq=8
                                  Nkv=8192, D=192, Dv_=128, dtype=BF16, causal=False,
                                  note="head dims 192/128, non-causal")
 
+# 8-bit inputs (no page names a format): the headline shape, and a causal
+# GQA prefill at D = 128, both quantised per tensor to E4M3.
+WORKLOADS["dit-17160-fp8"] = _w(name="dit-17160-fp8", B=1, Hq=24, Hkv=24, Nq=17160,
+                                Nkv=17160, D=128, dtype=FP8, causal=False, k_offset_std=0.5,
+                                note="video-DiT self-attention on E4M3 inputs")
+WORKLOADS["gqa-causal-fp8-8192"] = _w(name="gqa-causal-fp8-8192", B=1, Hq=32, Hkv=8, Nq=8192,
+                                      Nkv=8192, D=128, dtype=FP8, causal=True,
+                                      note="causal GQA prefill on E4M3 inputs")
+
 HEADLINE = "dit-17160"
 
 
@@ -141,6 +151,17 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def quantize_fp8(x: np.ndarray) -> tuple[np.ndarray, float]:
+    """float32 -> (E4M3 bytes, descale): descale = max|x| / 448 (a float32),
+    bytes = x / descale rounded to nearest even by PyTorch's float8_e4m3fn
+    conversion, so that bytes * descale approximates x."""
+    import torch
+    amax = float(np.max(np.abs(x))) if x.size else 1.0
+    ds = float(np.float32(amax / 448.0 if amax > 0 else 1.0))
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32) / np.float32(ds))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), ds
 
 
 def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -161,13 +182,17 @@ class Inputs:
     seed: int
     k_offset: np.ndarray | None = None   # float32 [D], already folded into k
     rows: np.ndarray | None = None       # int64 [Hq, R] sampled query rows
+    q_descale: float = 1.0               # FP8: values are bytes * descale
+    k_descale: float = 1.0
+    v_descale: float = 1.0
 
 
 def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
                 dtype: str, seed: int = 0, k_offset_std: float | None = None,
                 sampled_rows: int | None = None, Dv: int | None = None) -> Inputs:
     """Draw q, k, v iid N(0,1) (float32), in that order, from PCG64(seed);
-    v has Dv columns (default D).
+    v has Dv columns (default D).  For FP8 each tensor is quantised with
+    its own descale factor (quantize_fp8).
 
     With ``k_offset_std`` a per-channel offset c = std*z, z ~ N(0,1) of shape
     [D], is drawn next and added to every key row in float32 before rounding.
@@ -175,8 +200,15 @@ def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
     rows (rows 0 and Nq-1 are always included), sorted.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
+    ds = {}
+
+    def store(name, x):
+        if dtype == FP8:
+            b, ds[name] = quantize_fp8(x)
+            return b
+        return to_storage(x, dtype)
     q = rng.standard_normal((B, Hq, Nq, D), dtype=np.float32)
-    qs = to_storage(q, dtype)
+    qs = store("q", q)
     del q
     k = rng.standard_normal((B, Hkv, Nkv, D), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, Nkv, D if Dv is None else Dv), dtype=np.float32)
@@ -185,15 +217,16 @@ def make_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int,
         off = (np.float32(k_offset_std)
                * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
         k += off
-    ks = to_storage(k, dtype)
+    ks = store("k", k)
     del k
-    vs = to_storage(v, dtype)
+    vs = store("v", v)
     del v
     rows = None
     if sampled_rows is not None:
         rows = sample_rows(rng, Hq, Nq, sampled_rows)
     return Inputs(q=qs, k=ks, v=vs, dtype=dtype, seed=seed, k_offset=off,
-                  rows=rows)
+                  rows=rows, q_descale=ds.get("q", 1.0), k_descale=ds.get("k", 1.0),
+                  v_descale=ds.get("v", 1.0))
 
 
 def make_dout(x: Inputs, seed: int | None = None) -> np.ndarray:

@@ -133,3 +133,65 @@ def gather_rows(a, rows):
     B, Hq = a.shape[:2]
     return np.stack([np.stack([a[b, h, rows[h]] for h in range(Hq)])
                      for b in range(B)])
+
+
+def fp8_bounds(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
+    """Per-element error bound of the FP8 forward against the oracle, and a
+    per-row LSE bound, on rows [Hq, R] (all rows when None).
+
+    Derivation: the kernel rounds each probability P_ij (relative to its
+    running reference max, so P_ij >= exp(s_ij - max_j s_ij)) to E4M3: an
+    error of at most 2^-4 P_ij (normal numbers, 3 mantissa bits) or 2^-10
+    (subnormals, below 2^-6).  Divided by the row sum l_i, the error on
+    the normalised weight p_ij is at most 2^-4 p_ij + 2^-10 / L_i, with
+    L_i = sum_j exp(s_ij - max s) >= 1.  The roundings are independent and
+    uniform, so o_id is off by a sum with standard deviation
+    sigma_id = sqrt(sum_j (2^-4 p_ij + 2^-10 / L_i)^2 v_jd^2 / 3); the bound
+    is 6 sigma plus half an ulp of the output type plus the score error of
+    the 8-bit matrix instruction, whose accumulation is coarser than fp32
+    (measured: about 2^-14.6 of the largest partial sum); it is bounded
+    by dS_ij = 2^-12 sum_d |q_id k_jd| scale q_descale k_descale, moving
+    o_id by at most max_j dS_ij sum_j p_ij (|v_jd| + |o_id|) and the
+    log-sum-exp by max_j dS_ij.  Returns (bound [B,Hq,R,D], mean bound
+    [B,Hq,R,D], lse bound [B,Hq,R]) for the output dtype ``out_dtype``.
+    """
+    q8, k8, v8 = x.q, x.k, x.v
+    B, Hq, Nq, D = q8.shape
+    Hkv, Nkv = k8.shape[1], k8.shape[2]
+    G = Hq // Hkv
+    sc = oracle.scale_value(scale, D)
+    cn = sc * x.q_descale * x.k_descale
+    dec = oracle.decode_fp8_e4m3
+    R = Nq if rows is None else rows.shape[1]
+    bound = np.empty((B, Hq, R, D))
+    mbound = np.empty((B, Hq, R, D))
+    lbound = np.empty((B, Hq, R))
+    keys = np.arange(Nkv)
+    for b in range(B):
+        for hk in range(Hkv):
+            kk = dec(k8[b, hk])
+            vv = dec(v8[b, hk]) * x.v_descale
+            for g in range(G):
+                h = hk * G + g
+                ri = np.arange(Nq) if rows is None else rows[h]
+                qq = dec(q8[b, h, ri])
+                s = cn * (qq @ kk.T)
+                ds = 2.0 ** -12 * cn * (np.abs(qq) @ np.abs(kk).T)
+                if causal:
+                    allowed = keys[None, :] <= ri[:, None] + causal_offset
+                    s = np.where(allowed, s, -np.inf)
+                    ds = np.where(allowed, ds, 0.0)
+                mx = s.max(axis=1, keepdims=True)
+                empty = ~np.isfinite(mx)
+                e = np.exp(s - np.where(empty, 0.0, mx))
+                L = np.where(empty, 1.0, e.sum(axis=1, keepdims=True))
+                p = e / L
+                w = 2.0 ** -4 * p + 2.0 ** -10 / L * (p > 0)
+                sigma = np.sqrt((w ** 2) @ (vv ** 2) / 3.0)
+                o = p @ vv
+                dsm = ds.max(axis=1, keepdims=True)
+                sterm = dsm * (p @ np.abs(vv) + np.abs(o))
+                bound[b, h] = 6.0 * sigma + sterm
+                mbound[b, h] = 2.0 * sigma + sterm
+                lbound[b, h] = dsm[:, 0]
+    return bound, mbound, lbound

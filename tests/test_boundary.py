@@ -283,3 +283,18 @@ def test_value_width_backward_validation():
     # dv (2*80*128*2 = 40 KiB) placed so that it ends inside V's buffer
     assert chk(dv=v - 20 * 1024) == EINVAL
     assert chk(dv=v - 40 * 1024) == OK
+
+
+def test_fp8_validation(lib):
+    """attn_fwd_fp8: D = 128, positive finite descales, 16-bit output."""
+    def chk(D=128, qd=0.01, kd=0.02, vd=0.03, out_dtype=BF16, causal=0, **kw):
+        a = dict(q=Q, k=K, v=V, out=O, lse=L)
+        a.update(kw)
+        return lib.attn_fwd_fp8_check(a["q"], a["k"], a["v"], a["out"], a["lse"], 1, 4, 2, 100,
+                                      300, D, qd, kd, vd, 0.088, causal, out_dtype)
+    assert chk() == OK and chk(out_dtype=F16) == OK and chk(causal=2) == OK
+    assert chk(D=64) == EINVAL and chk(D=256) == EINVAL
+    assert chk(qd=0.0) == EINVAL and chk(kd=-1.0) == EINVAL and chk(vd=float("inf")) == EINVAL
+    assert chk(out_dtype=7) == EINVAL
+    assert chk(out=Q + 4096) == EINVAL          # output overlaps q
+    assert chk(q=Q + 8) == EINVAL               # not 16-byte aligned
