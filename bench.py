@@ -35,8 +35,11 @@ CSRC = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc")
 # the kernel sources each pass runs (a measurement taken on other sources is stale)
 SOURCES = {"fwd": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_d64.hip",
                    "attn_fwd_d80.hip", "attn_fwd_d96.hip", "attn_fwd_d128.hip",
-                   "attn_fwd_d256.hip", "attn_fwd_d192v128.hip", "attn_fwd_fp8.hip"),
-           "bwd": ("attn_common.h", "attn_bwd.hip")}
+                   "attn_fwd_d256.hip", "attn_fwd_d192v128.hip"),
+           "bwd": ("attn_common.h", "attn_bwd.hip"),
+           # the FP8 kernel, and the plan and merge it shares with the 16-bit path
+           "fp8": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_d128.hip",
+                   "attn_fwd_fp8.hip")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -52,16 +55,18 @@ def source_hash(pass_: str = "fwd") -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, pass_: str = "fwd"):
+def measured_traffic(workload: str, pass_: str = "fwd", kernels: str | None = None):
     """HBM bytes per step from a committed counter summary, if it was taken
-    on the current kernel sources; otherwise None."""
+    on the current kernel sources (``kernels``: the SOURCES key, default
+    ``pass_``); otherwise None."""
+    kernels = kernels or pass_
     path = os.path.join(PROFILES, f"attn_{pass_}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
     t = re.search(r"hbm bytes per step:\s*`?([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != source_hash(pass_):
+    if not h or not t or h.group(1) != source_hash(kernels):
         return None
     return float(t.group(1))
 
@@ -205,7 +210,8 @@ def main():
     progress(f"{ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of peak); "
              f"wall {wall:.3f} s")
 
-    traffic = measured_traffic(name, args.pass_)
+    kernels = "fp8" if fp8 else args.pass_
+    traffic = measured_traffic(name, args.pass_, kernels)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                 "traffic": traffic}
@@ -233,7 +239,7 @@ def main():
                    "D": w.D, "Dv": w.Dv, "causal": w.causal, "scale": w.scale, "seed": args.seed,
                    "k_offset_std": w.k_offset_std,
                    "split_kv": None if bwd else splits,
-                   "kernel_source": source_hash(args.pass_)},
+                   "kernel_source": source_hash(kernels)},
         "roofline": roofline,
     }
 
