@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows per head for the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mask", choices=("none", "pad"), default="none",
+                    help="pad: a boolean key-padding mask [B, 1, 1, Nkv] that keeps the "
+                         "first 7/8 of the keys (timing only: no CPU leg)")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the gradients")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -139,7 +142,7 @@ def main():
     w = inputs.WORKLOADS[name]
     dev = torch.device("cuda:0")
     progress(f"workload {name}: {w.describe()}; pass {args.pass_}; generating inputs")
-    want_cpu = not args.no_cpu_baseline
+    want_cpu = not args.no_cpu_baseline and args.mask == "none"
     x = inputs.make_workload_inputs(w, seed=args.seed,
                                     sampled_rows=args.cpu_rows if want_cpu else None)
 
@@ -156,6 +159,12 @@ def main():
         return t.view(torch.bfloat16) if w.dtype == "bf16" else t
 
     q, k, v = up(x.q), up(x.k), up(x.v)
+    mask = None
+    if args.mask == "pad":
+        if w.dtype == "fp8":
+            raise SystemExit("bench.py: the FP8 path takes no mask")
+        mask = torch.zeros((w.B, 1, 1, w.Nkv), dtype=torch.bool, device=dev)
+        mask[..., : w.Nkv - w.Nkv // 8] = True
     out = torch.empty((w.B, w.Hq, w.Nq, w.Dv), dtype=torch.bfloat16 if fp8 else q.dtype,
                       device=dev)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
@@ -172,7 +181,7 @@ def main():
                          scale=w.scale, out=out, lse=lse, num_splits=args.splits)
         else:
             attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse,
-                     num_splits=args.splits)
+                     num_splits=args.splits, mask=mask)
 
     if bwd:
         dout = inputs.make_dout(x, seed=args.seed)
@@ -182,7 +191,7 @@ def main():
 
         def step():
             attn_bwd(q, k, v, out, lse, g, causal=w.causal, scale=w.scale,
-                     dq=dq, dk=dk, dv=dv)
+                     dq=dq, dk=dk, dv=dv, mask=mask)
     else:
         step = fwd_step
 
@@ -237,7 +246,7 @@ def main():
                    "pass": args.pass_,
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv,
                    "D": w.D, "Dv": w.Dv, "causal": w.causal, "scale": w.scale, "seed": args.seed,
-                   "k_offset_std": w.k_offset_std,
+                   "k_offset_std": w.k_offset_std, "mask": args.mask,
                    "split_kv": None if bwd else splits,
                    "kernel_source": source_hash(kernels)},
         "roofline": roofline,
