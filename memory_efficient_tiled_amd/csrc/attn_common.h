@@ -81,21 +81,25 @@ __device__ __forceinline__ float hi_f32<TagF16>(uint32_t w) {
 // Attention-mask values as base-2 biases.  ATTN_MASK_BOOL: bytes, zero
 // removes the key (-inf), nonzero keeps it (0).  ATTN_MASK_ADD: values of
 // the input type, added to the scaled scores (times log2 e here).
+// mask_keep4: the bytes of keys key0 .. key0 + 3 of one boolean mask row
+// (byte i nonzero keeps key key0 + i); keys at or past nkv are not read
+// and come back kept.
+__device__ __forceinline__ uint32_t mask_keep4(const uint8_t* mrow, int key0, int nkv) {
+  if (key0 + 3 < nkv) return *(const uint32_t*)(mrow + key0);
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (key0 + i < nkv) w |= (uint32_t)mrow[key0 + i] << (8 * i);
+  return w | (~0u << (8 * max(0, min(4, nkv - key0))));
+}
+
 // mask_bias4: keys key0 .. key0 + 3 of one mask row (16-bit mask rows at
 // `mrow` as bytes); keys at or past nkv are not read (bias 0).
 template <class Tag>
 __device__ __forceinline__ void mask_bias4(const uint8_t* mrow, int mode, int key0, int nkv,
                                            float* bias) {
   if (mode == ATTN_MASK_BOOL) {
-    uint32_t w = 0;
-    if (key0 + 3 < nkv) {
-      w = *(const uint32_t*)(mrow + key0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (key0 + i < nkv) w |= (uint32_t)mrow[key0 + i] << (8 * i);
-      w |= ~0u << (8 * max(0, min(4, nkv - key0)));  // keys past the end: kept (not read)
-    }
+    const uint32_t w = mask_keep4(mrow, key0, nkv);
 #pragma unroll
     for (int i = 0; i < 4; ++i) bias[i] = ((w >> (8 * i)) & 0xffu) ? 0.f : -INFINITY;
   } else {

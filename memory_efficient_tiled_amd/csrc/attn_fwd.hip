@@ -339,7 +339,7 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   p.msb = M.sb, p.msh = M.sh, p.msq = M.sq;
   p.mask_mode = M.type;
   p.cm = p.c;
-  if (masked) p.c = 1.f;  // the mask step forms base-2 scores
+  if (M.type == ATTN_MASK_ADD) p.c = 1.f;  // the mask step forms base-2 scores
 
   void* ws = nullptr;
   if (split_wgs > 0) {

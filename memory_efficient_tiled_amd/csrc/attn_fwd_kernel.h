@@ -106,6 +106,8 @@ struct Params {
 // V rows): 64-key tiles (the copies of a 32-key K tile would not split over
 // 8 waves), 32-row waves, the single-buffered pipeline and 4 of the 12 Q^T
 // chunks in LDS (double-buffered scores and all of Q^T in registers spill).
+// Masked calls at D = 128 take that pipeline too (same 256 rows and 64-key
+// tiles as the narrow tile): the mask step's registers then fit.
 struct TileCfg {
   int NW, QB, BN, QL;
   bool SB;
@@ -119,14 +121,16 @@ enum {
   kCfgD128Wide = 3,
   kCfgD256 = 4,
   kCfgD96 = 5,
-  kCfgD192 = 6
+  kCfgD192 = 6,
+  kCfgD128Masked = 7
 };
-constexpr TileCfg kCfgs[7] = {{4, 1, 64, 0, false},
+constexpr TileCfg kCfgs[8] = {{4, 1, 64, 0, false},
                               {4, 2, 32, 0, false},
                               {8, 1, 64, 0, false},
                               {8, 2, 32, 3, true},
                               {8, 1, 32, 8, true},
                               {4, 1, 64, 0, false},
+                              {8, 1, 64, 4, true},
                               {8, 1, 64, 4, true}};
 
 // Launch the forward kernels of one pair of head dimensions (Q/K, V/O),
@@ -375,37 +379,84 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     }
   };
 
-  // Keys past the valid range, and (causal) keys after the row, get -inf.
-  // Only tiles that straddle the end of the key range or the diagonal; with
-  // a mask, every tile (scores are scaled and biased here).
-  auto mask = [&](int t, f32x16* s) {
+  // Keys past the valid range, and (causal) keys after the row, get -inf:
+  // only on tiles that straddle the end of the key range or the diagonal.
+  // With a mask, every tile first goes through the mask: a boolean mask
+  // sets the scores of the keys it removes to -inf (the others stay raw; c
+  // scales them in the exponent), an additive one forms base-2 scores
+  // s * cm + bias * log2(e) (then c is 1).
+  // (Always inlined: the score arrays it takes by pointer must stay in
+  // registers.)
+  auto mask = [&](int t, f32x16* s) __attribute__((always_inline)) {
     const int k0 = kbeg + t * BN;
-    const bool need = MASKED || (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0 + p.coff);
-    if (need) {
+    const bool edge = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0 + p.coff);
+    if constexpr (!MASKED) {
+      if (edge) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qrow = wq0 + qb * 32 + l32;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int key0 = k0 + kb * 32 + 8 * g + 4 * hl;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int key = key0 + i;
+                const float v = s[qb * NKB + kb][4 * g + i];
+                const bool ok = key < kend && (!CAUSAL || key <= qrow + p.coff);
+                s[qb * NKB + kb][4 * g + i] = ok ? v : -INFINITY;
+              }
+            }
+        }
+      }
+      return;
+    } else {
+      const bool keep_mode = p.mask_mode == ATTN_MASK_BOOL;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qrow = wq0 + qb * 32 + l32;
-        const uint8_t* mrow = nullptr;
-        if constexpr (MASKED) {
-          const int64_t off = b * p.msb + hq * p.msh + (int64_t)min(qrow, p.Nq - 1) * p.msq;
-          mrow = p.mask + off * (p.mask_mode == ATTN_MASK_BOOL ? 1 : 2);
+        const int64_t off = b * p.msb + hq * p.msh + (int64_t)min(qrow, p.Nq - 1) * p.msq;
+        const uint8_t* mrow = p.mask + off * (keep_mode ? 1 : 2);
+        if (keep_mode) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const uint32_t w = mask_keep4(mrow, k0 + kb * 32 + 8 * g + 4 * hl, p.Nkv);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (((w >> (8 * i)) & 0xffu) == 0u) s[qb * NKB + kb][4 * g + i] = -INFINITY;
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float bias[4];
+              mask_bias4<Tag>(mrow, ATTN_MASK_ADD, k0 + kb * 32 + 8 * g + 4 * hl, p.Nkv, bias);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                s[qb * NKB + kb][4 * g + i] = fmaf(s[qb * NKB + kb][4 * g + i], p.cm, bias[i]);
+            }
         }
+      }
+    }
+    if (edge) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = wq0 + qb * 32 + l32;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int key0 = k0 + kb * 32 + 8 * g + 4 * hl;
-            float bias[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (MASKED) mask_bias4<Tag>(mrow, p.mask_mode, key0, p.Nkv, bias);
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key = key0 + i;
-              float v = s[qb * NKB + kb][4 * g + i];
-              if constexpr (MASKED) v = fmaf(v, p.cm, bias[i]);
+              const int key = k0 + kb * 32 + 8 * g + 4 * hl + i;
               const bool ok = key < kend && (!CAUSAL || key <= qrow + p.coff);
+              const float v = s[qb * NKB + kb][4 * g + i];
               s[qb * NKB + kb][4 * g + i] = ok ? v : -INFINITY;
             }
-          }
       }
     }
   };
@@ -738,7 +789,8 @@ hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool st
                         : D == 96 || D == 80 ? kCfgD96
                         : D == 128           ? kCfgD128Wide
                                              : kCfgD64Wide;
-  if (masked) return dispatch<D, DV, kNarrow, Tag, true>(p, causal, split, true, st);
+  constexpr int kMasked = D == 128 ? kCfgD128Masked : kNarrow;
+  if (masked) return dispatch<D, DV, kMasked, Tag, true>(p, causal, split, true, st);
   if (kWide != kNarrow && cfg == kWide && !causal)
     return split ? launch_main<D, DV, kWide, Tag, false, true, false>(p, strided, st)
                  : launch_main<D, DV, kWide, Tag, false, false, false>(p, strided, st);
