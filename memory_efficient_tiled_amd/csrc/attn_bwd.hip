@@ -340,12 +340,19 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   // row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.  With a mask, its base-2
   // bias joins the exponent; rows past Nq and rows that saw no key in the
   // forward (lse -inf) get P = 0.
-  auto probs = [&](auto mskc, auto bufc, f32x16* s, int q0, int hq) {
+  // A mask with row stride 0 (a key-padding mask, or any mask broadcast
+  // over the query rows) has one value per key of a head: read once.
+  auto probs_impl = [&](auto mskc, auto bufc, auto rowc, f32x16* s, int q0, int hq)
+      __attribute__((always_inline)) {
     constexpr bool MSK = decltype(mskc)::value;
     constexpr int buf = decltype(bufc)::value;
+    constexpr bool ROWMASK = decltype(rowc)::value;  // the mask varies along rows
     const uint8_t* mbase = nullptr;
     if constexpr (MASKED) mbase = p.mask;
     const int64_t mrow0 = MASKED ? b * p.msb + hq * p.msh : 0;
+    float kbias = 0.f;
+    if constexpr (MASKED && !ROWMASK)
+      kbias = key < p.Nkv ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + key) : 0.f;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -357,10 +364,11 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
           float pv;
           if constexpr (MASKED) {
             const int row = q0 + r + e;
-            const float bias =
-                row < p.Nq && key < p.Nkv
-                    ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + row * p.msq + key)
-                    : 0.f;
+            float bias = kbias;
+            if constexpr (ROWMASK)
+              bias = row < p.Nq && key < p.Nkv
+                         ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + row * p.msq + key)
+                         : 0.f;
             pv = (row < p.Nq && ls[e] != -INFINITY)
                      ? fast_exp2(fmaf(p.cs, s[qb][4 * j + e], bias) - ls[e])
                      : 0.f;
@@ -371,6 +379,13 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
           s[qb][4 * j + e] = pv;
         }
       }
+  };
+  auto probs = [&](auto mskc, auto bufc, f32x16* s, int q0, int hq)
+      __attribute__((always_inline)) {
+    if (MASKED && p.msq == 0)
+      probs_impl(mskc, bufc, std::false_type{}, s, q0, hq);
+    else
+      probs_impl(mskc, bufc, std::true_type{}, s, q0, hq);
   };
 
   auto tile = [&](int u, auto bufc) {
