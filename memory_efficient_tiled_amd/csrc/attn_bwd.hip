@@ -511,10 +511,10 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4k,
 // Q and dO stay in registers; K is copied into LDS twice (row-read and
 // transposed layouts) and V once, two buffers deep, the loop unrolled by two.
 // One wave per SIMD at D = 256: Q, dO and the dQ accumulators take 256
-// registers; likewise for the (192, 128) pair (208).  With V rows of
-// DV != D elements, dO and V tiles are DV wide and dP reduces over DV.
+// registers (the (192, 128) pair's 208 still fit two waves).  With V rows
+// of DV != D elements, dO and V tiles are DV wide and dP reduces over DV.
 template <int D, int DV, class Tag, bool CAUSAL, bool MASKED>
-__global__ __launch_bounds__(256, D == 256 || D != DV ? 1 : 2) void attn_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParams p) {
   constexpr bool SQ = D == DV;
   constexpr int NW = 4, BM = NW * 32, BN = 32;
   constexpr int DP = compute_dim(D), DVP = compute_dim(DV);
