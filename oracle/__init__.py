@@ -6,5 +6,7 @@ from .softmax_attention import (attention, attention_backward, attention_fp8,
                                 attention_from_storage, decode, decode_bf16,
                                 decode_f16, decode_fp8_e4m3, scale_value)
 
-__all__ = ["attention", "attention_backward", "attention_fp8", "attention_from_storage",
+from .ffn import ffn, ffn_chunked, gelu_tanh
+
+__all__ = ["ffn", "ffn_chunked", "gelu_tanh", "attention", "attention_backward", "attention_fp8", "attention_from_storage",
            "decode", "decode_bf16", "decode_f16", "decode_fp8_e4m3", "scale_value"]
