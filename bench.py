@@ -39,7 +39,8 @@ SOURCES = {"fwd": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_f
            "bwd": ("attn_common.h", "attn_bwd.hip"),
            # the FP8 kernel, and the plan and merge it shares with the 16-bit path
            "fp8": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_d128.hip",
-                   "attn_fwd_fp8.hip")}
+                   "attn_fwd_fp8.hip"),
+           "ffn": ("attn_common.h", "ffn_chunked.hip")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -106,7 +107,7 @@ def main():
     ap.add_argument("--mask", choices=("none", "pad"), default="none",
                     help="pad: a boolean key-padding mask [B, 1, 1, Nkv] that keeps the "
                          "first 7/8 of the keys (timing only: no CPU leg)")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "ffn"), default="fwd",
                     help="time the forward (default) or the gradients")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this size "
@@ -137,6 +138,8 @@ def main():
                                             attn_fwd_num_splits, inputs)
     from memory_efficient_tiled_amd.binding import ATTN_BF16, ATTN_F16
 
+    if args.pass_ == "ffn":
+        return bench_ffn(args, torch, np)
     bwd = args.pass_ == "bwd"
     name = args.workload or inputs.HEADLINE
     w = inputs.WORKLOADS[name]
@@ -365,6 +368,82 @@ def cpu_leg_bwd(result, x, w, name, dout, dq, np, oracle):
                   f"({sample_flops / 1e9:.1f} GFLOP algorithmic, {cpu_s:.1f} s, "
                   f"float64 numpy, {cpu_model()})"}
     progress(f"oracle {cpu_s:.1f} s; parity {result['parity']}")
+
+
+
+def bench_ffn(args, torch, np):
+    """The chunked feed-forward block (FFN chunking): one ffn_chunked call per
+    step over a 16-bit synthetic batch; roofline against the MFMA peak with
+    the algorithmic flops of the two products (4 N Dm F); the CPU leg runs
+    the float64 oracle on sampled rows."""
+    from memory_efficient_tiled_amd import ffn_chunked, inputs
+    name = args.workload or "dit-ffn-17160"
+    w = inputs.FFN_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    progress(f"workload {name}: {w.describe()}; generating inputs")
+    xi = inputs.make_ffn_inputs(w.N, w.Dm, w.F, w.dtype, seed=args.seed)
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if w.dtype == "bf16"
+                             else np.ascontiguousarray(a)).to(dev)
+        return t.view(torch.bfloat16) if w.dtype == "bf16" else t
+
+    x, w1, b1, w2, b2 = (up(a) for a in (xi.x, xi.w1, xi.b1, xi.w2, xi.b2))
+    y = torch.empty_like(x)
+    ffn_chunked(x, w1, b1, w2, b2, chunk_rows=w.chunk_rows, out=y, verify=True)
+
+    def step():
+        ffn_chunked(x, w1, b1, w2, b2, chunk_rows=w.chunk_rows, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    progress(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[w.dtype]
+    result = {
+        "metric": "chunked feed-forward block TFLOP/s and % of MI355X bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s",
+        "pct_of_mfma_peak": round(100 * tflops / peak, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{name}: {w.note}, {w.describe()}", "pass": "ffn",
+                   "N": w.N, "Dm": w.Dm, "F": w.F, "chunk_rows": w.chunk_rows,
+                   "seed": args.seed, "kernel_source": source_hash("ffn")},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic(name, "ffn")},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = np.unique(np.random.default_rng(args.seed).choice(w.N, 64, replace=False))
+        dec = [oracle.decode(a, w.dtype) for a in (xi.x, xi.w1, xi.b1, xi.w2, xi.b2)]
+        progress(f"oracle on {rows.size} rows")
+        c0 = time.perf_counter()
+        ref = oracle.ffn(dec[0][rows], *dec[1:])
+        cpu_s = time.perf_counter() - c0
+        got = y.float().cpu().numpy().astype(np.float64)[rows]
+        err = np.abs(got - ref)
+        sample_flops = 4.0 * rows.size * w.Dm * w.F
+        result["parity"] = {"rows": int(rows.size), "max_abs_err": float(err.max()),
+                            "mean_abs_err": float(err.mean()),
+                            "rms_ref": float(np.sqrt(np.mean(ref ** 2)))}
+        result["cpu_baseline"] = {
+            "value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{rows.size} rows of {name} ({sample_flops / 1e9:.1f} GFLOP, "
+                      f"{cpu_s:.1f} s, float64 numpy, {cpu_model()})"}
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

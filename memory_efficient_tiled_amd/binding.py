@@ -128,6 +128,15 @@ def load_library():
     lib.attn_bwd_masked_check.argtypes = [_VP] * 9 + shape_args + [_VP, _INT, _LLP,
                                                                    ctypes.c_float, _INT, _INT]
     lib.attn_bwd_masked_check.restype = _INT
+    lib.ffn_chunked.argtypes = [_VP] * 6 + [_INT] * 6 + [_VP]
+    lib.ffn_chunked.restype = _INT
+    lib.ffn_chunked_check.argtypes = [_VP] * 6 + [_INT] * 6
+    lib.ffn_chunked_check.restype = _INT
+    lib.ffn_workspace_bytes.argtypes = [_INT] * 4
+    lib.ffn_workspace_bytes.restype = ctypes.c_size_t
+    _FP = ctypes.POINTER(ctypes.c_float)
+    lib.ffn_verify.argtypes = [_VP] * 5 + [_INT] * 6 + [_FP, _FP, _VP]
+    lib.ffn_verify.restype = _INT
     lib.attn_strerror.argtypes = [_INT]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -473,3 +482,63 @@ def attn_bwd(q, k, v, out, lse, dout, causal=False, scale: float | None = None,
     if rc != ATTN_OK:
         _raise(rc)
     return dq, dk, dv
+
+
+FFN_GELU_TANH = 0
+
+
+def ffn_chunked(x, w1, b1, w2, b2, chunk_rows: int = 0, out=None, verify: bool = False):
+    """y = W2 gelu(W1 x + b1) + b2 (GELU, tanh approximation) over chunks of
+    ``chunk_rows`` token rows (0 = the library's choice), on the GPU.
+
+    x [..., Dm], w1 [F, Dm], b1 [F] or None, w2 [Dm, F], b2 [Dm] or None:
+    contiguous float16 or bfloat16 tensors of one dtype on one HIP device,
+    Dm and F multiples of 8.  Returns y of x's shape (or fills ``out``).
+    With ``verify`` the library first runs its chunking check (ffn_verify)
+    and this raises if the chunked rows differ from the single-chunk rows by
+    more than 2^-6 of the largest output (rounding of the products moves
+    them far less).  Runs on torch's current stream.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("x", x), ("w1", w1), ("w2", w2), ("b1", b1), ("b2", b2)):
+        if t is None and name in ("b1", "b2"):
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda" or t.device != x.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on x's HIP device")
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} must have x's dtype")
+    Dm = x.shape[-1]
+    N = x.numel() // Dm if Dm else 0
+    F = w1.shape[0]
+    if tuple(w1.shape) != (F, Dm) or tuple(w2.shape) != (Dm, F):
+        raise ValueError(f"weights must be w1 [F, Dm], w2 [Dm, F]; got {tuple(w1.shape)}, "
+                         f"{tuple(w2.shape)}")
+    if (b1 is not None and tuple(b1.shape) != (F,)) or (b2 is not None and
+                                                        tuple(b2.shape) != (Dm,)):
+        raise ValueError("biases must be b1 [F], b2 [Dm]")
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    elif tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        if verify:
+            d, r = ctypes.c_float(), ctypes.c_float()
+            rc = lib.ffn_verify(x.data_ptr(), w1.data_ptr(), ptr(b1), w2.data_ptr(), ptr(b2),
+                                N, Dm, F, FFN_GELU_TANH, int(chunk_rows), dt,
+                                ctypes.byref(d), ctypes.byref(r), stream)
+            if rc != ATTN_OK:
+                _raise(rc)
+            if not d.value <= 2.0 ** -6 * max(r.value, 1e-30):
+                raise RuntimeError(f"ffn chunking check failed: chunked rows differ by "
+                                   f"{d.value} (largest output {r.value})")
+        rc = lib.ffn_chunked(x.data_ptr(), w1.data_ptr(), ptr(b1), w2.data_ptr(), ptr(b2),
+                             out.data_ptr(), N, Dm, F, FFN_GELU_TANH, int(chunk_rows), dt, stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return out

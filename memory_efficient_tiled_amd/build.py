@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in (
     "attn_fwd.hip", "attn_fwd_d64.hip", "attn_fwd_d80.hip", "attn_fwd_d96.hip",
     "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_fwd_d192v128.hip", "attn_fwd_fp8.hip",
-    "attn_bwd.hip")]
+    "attn_bwd.hip", "ffn_chunked.hip")]
 OUT = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -59,7 +59,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             if err.strip() and verbose:
                 print(err, file=sys.stderr)
         tmp_out = OUT + ".tmp"
-        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_out]
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_out,
+                "-L/opt/rocm/lib", "-lhipblaslt"]
         if verbose:
             print(" ".join(link), flush=True)
         rc, err = _run(link)

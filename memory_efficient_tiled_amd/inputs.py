@@ -256,3 +256,59 @@ def make_workload_inputs(w: Workload, seed: int = 0,
     R = sampled_rows if sampled_rows is not None else w.sampled_rows
     return make_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, seed=seed,
                        k_offset_std=w.k_offset_std, sampled_rows=R, Dv=w.Dv)
+
+
+# ---------------------------------------------------------------------------
+# The chunked feed-forward block (FFN chunking, the post's second memory
+# saver): token rows x [N, Dm], w1 [F, Dm], b1 [F], w2 [Dm, F], b2 [Dm].
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    name: str
+    N: int
+    Dm: int
+    F: int
+    dtype: str
+    chunk_rows: int = 0
+    note: str = ""
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic flops of the two products: 4 N Dm F."""
+        return 4.0 * self.N * self.Dm * self.F
+
+    def describe(self) -> str:
+        return (f"N={self.N} Dm={self.Dm} F={self.F} {self.dtype} "
+                f"chunk={self.chunk_rows or 'library'}")
+
+
+# The 17K-token 480p video of the post's "The problem" through the FFN of a
+# 14B-parameter video DiT (model width 5120, hidden width 13824).
+FFN_WORKLOADS: dict[str, FfnWorkload] = {
+    "dit-ffn-17160": FfnWorkload(name="dit-ffn-17160", N=17160, Dm=5120, F=13824, dtype=BF16,
+                                 note="video-DiT feed-forward block, 17K tokens"),
+}
+
+
+@dataclasses.dataclass
+class FfnInputs:
+    x: np.ndarray     # [N, Dm] 16-bit storage
+    w1: np.ndarray    # [F, Dm]
+    b1: np.ndarray    # [F]
+    w2: np.ndarray    # [Dm, F]
+    b2: np.ndarray    # [Dm]
+    dtype: str
+
+
+def make_ffn_inputs(N: int, Dm: int, F: int, dtype: str, seed: int = 0) -> FfnInputs:
+    """x iid N(0,1); w1 N(0, 1/Dm), w2 N(0, 1/F) (unit-variance outputs);
+    biases N(0, 0.1^2); drawn in that order from PCG64(seed), float32, then
+    rounded to the 16-bit type."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((N, Dm), dtype=np.float32)
+    w1 = rng.standard_normal((F, Dm), dtype=np.float32) * np.float32(1.0 / math.sqrt(Dm))
+    b1 = rng.standard_normal(F, dtype=np.float32) * np.float32(0.1)
+    w2 = rng.standard_normal((Dm, F), dtype=np.float32) * np.float32(1.0 / math.sqrt(F))
+    b2 = rng.standard_normal(Dm, dtype=np.float32) * np.float32(0.1)
+    return FfnInputs(*(to_storage(a, dtype) for a in (x, w1, b1, w2, b2)), dtype=dtype)

@@ -70,3 +70,15 @@ def test_ffn_validation():
     assert chk(dtype=5) == binding.ATTN_EINVAL
     assert chk(y=X + 64) == binding.ATTN_EINVAL        # output overlaps x
     assert lib.ffn_workspace_bytes(64, 512, 128, binding.ATTN_BF16) >= 64 * 512 * 2
+
+
+def test_library_exports_ffn_header():
+    import os
+    import re
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "include", "ffn.h")
+    names = set(re.findall(r"^\s*(?:size_t|int)\s+(ffn_\w+)\s*\(", open(hdr).read(), re.M))
+    assert names == {"ffn_chunked", "ffn_chunked_check", "ffn_workspace_bytes", "ffn_verify"}
+    so = ctypes.CDLL(binding.lib_path())
+    for n in names:
+        assert hasattr(so, n), n
