@@ -91,7 +91,9 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(BwdParams p, int rows) 
   for (int w = 1; w < L; w <<= 1) acc += __shfl_xor(acc, w, L);
   if (row < rows && part == 0) {
     p.delta[row] = acc;
-    p.lse2[row] = p.lse[row] * kLog2e;
+    // a row that saw no key (LSE -inf) gets +inf, so exp2(s - lse2) = 0
+    const float l = p.lse[row];
+    p.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -362,16 +364,19 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pv;
-          if constexpr (MASKED) {
+          if constexpr (MASKED && ROWMASK) {
             const int row = q0 + r + e;
-            float bias = kbias;
-            if constexpr (ROWMASK)
-              bias = row < p.Nq && key < p.Nkv
-                         ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + row * p.msq + key)
-                         : 0.f;
-            pv = (row < p.Nq && ls[e] != -INFINITY)
+            const float bias =
+                row < p.Nq && key < p.Nkv
+                    ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + row * p.msq + key)
+                    : 0.f;
+            pv = (row < p.Nq && ls[e] != INFINITY)
                      ? fast_exp2(fmaf(p.cs, s[qb][4 * j + e], bias) - ls[e])
                      : 0.f;
+          } else if constexpr (MASKED) {
+            // one bias per key; rows past Nq have Q = 0 and dO = 0 (finite
+            // P, no contribution), rows that saw no key have lse2 = +inf
+            pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], kbias - ls[e]));
           } else {
             pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
           }
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
     const int64_t off = b * p.msb + hq * p.msh + (int64_t)min(qrow, p.Nq - 1) * p.msq;
     mrow = p.mask + off * (p.mask_mode == ATTN_MASK_BOOL ? 1 : 2);
   }
-  const bool row_live = qrow < p.Nq && nl2 != INFINITY;
+  const bool row_live = qrow < p.Nq;  // a row that saw no key has nl2 = -inf: P = 0
   auto probs = [&](auto mskc, f32x16& s, f32x16& dp, int t) {
     constexpr bool MSK = decltype(mskc)::value;
 #pragma unroll
