@@ -294,14 +294,18 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                         int causal, int dtype, int num_cus);
 
 /*
- * attn_fwd_workspace_bytes -- host only: device bytes for splitting every
- * row into `num_splits` pieces (0 when num_splits <= 1): fp32 partial
- * outputs [num_splits,B,Hq,Nq,D] and partial LSE [num_splits,B,Hq,Nq].  An
- * upper bound of attn_plan.workspace_bytes for the same num_splits.  For
- * attn_fwd_dv pass the value head dimension Dv as D.
+ * attn_fwd_workspace_bytes -- host only (no HIP call): the device bytes
+ * attn_fwd allocates for this shape on an MI355X (256 compute units): the
+ * fp32 partial outputs and partial LSE of the rows its plan splits over key
+ * ranges, attn_plan.workspace_bytes of attn_fwd_plan(..., 0, 256, ...).
+ * 0 when nothing is split, and for invalid arguments (a non-positive size,
+ * an unsupported D, or causal outside 0..2).  The number of KV heads and
+ * the dtype do not change the plan.  D = 192 stands for attn_fwd_dv's
+ * (192, 128) pair.  On a device with another compute-unit count use
+ * attn_fwd_plan.
  */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
-                                int num_splits);
+                                int causal);
 
 /*
  * attn_bwd -- gradients of attn_fwd's O with respect to Q, K and V.

@@ -58,7 +58,10 @@ size_t ffn_workspace_bytes(int chunk_rows, int F, int Dm, int dtype);
  * result| to the host floats *max_abs_diff and *max_abs_ref.  Synchronises
  * `stream`.  The row-wise block gives the same rows either way up to the
  * rounding of the products; a wrong chunk offset or size shows up as a
- * difference of the order of the result itself. */
+ * difference of the order of the result itself.  A NaN or infinity in either
+ * evaluation makes *max_abs_diff (and, if in the single-chunk rows,
+ * *max_abs_ref) +inf, so a check that also requires both to be finite
+ * fails on it. */
 int ffn_verify(const void* x, const void* w1, const void* b1, const void* w2,
                const void* b2, int N, int Dm, int F, int act, int chunk_rows,
                int dtype, float* max_abs_diff, float* max_abs_ref, void* stream);

@@ -204,8 +204,10 @@ def attn_fwd_plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype_code, num_splits=0,
     return plan
 
 
-def attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, num_splits) -> int:
-    return load_library().attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, num_splits)
+def attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, causal=False) -> int:
+    """Device bytes attn_fwd allocates for this shape on an MI355X (0 when
+    nothing is split)."""
+    return load_library().attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, causal_code(causal))
 
 
 def strides3(t):
@@ -497,7 +499,7 @@ def ffn_chunked(x, w1, b1, w2, b2, chunk_rows: int = 0, out=None, verify: bool =
     With ``verify`` the library first runs its chunking check (ffn_verify)
     and this raises if the chunked rows differ from the single-chunk rows by
     more than 2^-6 of the largest output (rounding of the products moves
-    them far less).  Runs on torch's current stream.
+    them far less), or if either evaluation holds a NaN or infinity.  Runs on torch's current stream.
     """
     import torch
     lib = load_library()
@@ -534,7 +536,9 @@ def ffn_chunked(x, w1, b1, w2, b2, chunk_rows: int = 0, out=None, verify: bool =
                                 ctypes.byref(d), ctypes.byref(r), stream)
             if rc != ATTN_OK:
                 _raise(rc)
-            if not d.value <= 2.0 ** -6 * max(r.value, 1e-30):
+            # non-finite outputs come back as +inf and fail here
+            if not (math.isfinite(d.value) and math.isfinite(r.value)
+                    and d.value <= 2.0 ** -6 * max(r.value, 1e-30)):
                 raise RuntimeError(f"ffn chunking check failed: chunked rows differ by "
                                    f"{d.value} (largest output {r.value})")
         rc = lib.ffn_chunked(x.data_ptr(), w1.data_ptr(), ptr(b1), w2.data_ptr(), ptr(b2),

@@ -343,7 +343,12 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   // bias joins the exponent; rows past Nq and rows that saw no key in the
   // forward (lse -inf) get P = 0.
   // A mask with row stride 0 (a key-padding mask, or any mask broadcast
-  // over the query rows) has one value per key of a head: read once.
+  // over the query rows) has one value per key of a head: read once, on
+  // every tile whose rows all lie below Nq.  The last tile of a head, which
+  // may hold rows past Nq, takes the per-row path: such rows have Q = 0 and
+  // a zero lse2 slot, so without the row check P would be exp2(bias), which
+  // overflows the 16-bit P operand for large additive biases and turns
+  // 0 * inf into NaN in dV and dK.
   auto probs_impl = [&](auto mskc, auto bufc, auto rowc, f32x16* s, int q0, int hq)
       __attribute__((always_inline)) {
     constexpr bool MSK = decltype(mskc)::value;
@@ -374,8 +379,8 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
                      ? fast_exp2(fmaf(p.cs, s[qb][4 * j + e], bias) - ls[e])
                      : 0.f;
           } else if constexpr (MASKED) {
-            // one bias per key; rows past Nq have Q = 0 and dO = 0 (finite
-            // P, no contribution), rows that saw no key have lse2 = +inf
+            // one bias per key; every row is below Nq here, and rows that
+            // saw no key have lse2 = +inf
             pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], kbias - ls[e]));
           } else {
             pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   };
   auto probs = [&](auto mskc, auto bufc, f32x16* s, int q0, int hq)
       __attribute__((always_inline)) {
-    if (MASKED && p.msq == 0)
+    if (MASKED && p.msq == 0 && q0 + BQ <= p.Nq)
       probs_impl(mskc, bufc, std::false_type{}, s, q0, hq);
     else
       probs_impl(mskc, bufc, std::true_type{}, s, q0, hq);

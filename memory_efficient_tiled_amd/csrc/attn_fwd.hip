@@ -537,6 +537,9 @@ int attn_fwd_dv_check(const void* q, const void* k, const void* v, const void* o
 // (192, 128) pair, whose partial rows have 128 columns.
 static int plan_dv(int D) { return D == 192 ? 128 : D; }
 
+// Compute units of an MI355X, for the host-only workspace query.
+constexpr int kMi355xCus = 256;
+
 int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,
                         int num_cus) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || Hq % Hkv != 0) return ATTN_EINVAL;
@@ -563,11 +566,11 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, in
   return ATTN_OK;
 }
 
-size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D, int num_splits) {
-  (void)Nkv;
-  if (num_splits <= 1 || B <= 0 || Hq <= 0 || Nq <= 0 || D <= 0) return 0;
-  const size_t rows = (size_t)B * Hq * Nq;
-  return (size_t)num_splits * rows * ((size_t)D + 1) * sizeof(float);
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D, int causal) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || Nkv <= 0 || !head_dims_ok(D, plan_dv(D))) return 0;
+  if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return 0;
+  if ((long long)B * Hq * Nq > INT32_MAX) return 0;
+  return make_plan(B, Hq, Nq, Nkv, D, plan_dv(D), causal, 0, kMi355xCus).workspace_bytes();
 }
 
 const char* attn_strerror(int code) {

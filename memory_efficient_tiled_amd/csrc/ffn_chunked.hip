@@ -60,7 +60,13 @@ __global__ __launch_bounds__(256) void ffn_bias_add(uint16_t* y, const uint16_t*
 }
 
 // Per workgroup: max |a - b| and max |b| over its slice of n values, into
-// part[2 * blockIdx.x + {0, 1}] (no atomics); ffn_max_final folds them.
+// part[2 * blockIdx.x + {0, 1}] (no atomics); ffn_max_final folds them.  A
+// NaN difference or output counts as +inf (fmaxf alone would drop it), so
+// any non-finite value in either evaluation makes a result infinite.
+__device__ __forceinline__ float max_keep_nan(float acc, float x) {
+  return x == x ? fmaxf(acc, x) : INFINITY;
+}
+
 template <class Tag>
 __global__ __launch_bounds__(256) void ffn_max_diff(const uint16_t* a, const uint16_t* b, size_t n,
                                                     float* part) {
@@ -69,8 +75,8 @@ __global__ __launch_bounds__(256) void ffn_max_diff(const uint16_t* a, const uin
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     const uint32_t x = a[i], y = b[i];
     const float fx = lo_f32<Tag>(x), fy = lo_f32<Tag>(y);
-    d = fmaxf(d, fabsf(fx - fy));
-    r = fmaxf(r, fabsf(fy));
+    d = max_keep_nan(d, fabsf(fx - fy));
+    r = max_keep_nan(r, fabsf(fy));
   }
   sd[threadIdx.x] = d;
   sr[threadIdx.x] = r;

@@ -72,22 +72,40 @@ def check_grad(name, got, ref, dtype, what, zero_from=None, extra=0.0):
     assert err.mean() <= mbound, f"{what} {name}: mean err {err.mean():.3e} > {mbound:.3e}"
 
 
-def delta_terms(x, do, ref, causal, causal_offset=0):
-    """Per-row Delta terms of the bound for (dq, dk, dv) (see the header)."""
-    dtype = x.dtype
-    q, k, v, g = (_decode(a, dtype) for a in (x.q, x.k, x.v, do))
+def delta_terms(x, do, ref, causal, causal_offset=0, bias=None):
+    """Per-row Delta terms of the bound for (dq, dk, dv) (see the header),
+    for the inputs ``x`` and output gradient ``do``."""
+    dec = [_decode(a, x.dtype) for a in (x.q, x.k, x.v, do)]
+    return delta_terms_dec(dec, ref, x.dtype, causal, causal_offset, bias)
+
+
+def delta_terms_dec(dec, ref, dtype, causal, causal_offset=0, bias=None):
+    """Delta terms from decoded (q, k, v, dO).  ``bias`` (broadcastable to
+    [B, Hq, Nq, Nkv], -inf removes a key) enters the oracle's attention
+    exactly as in the forward; the dK term then takes, for each key, the
+    maximum of b_i over the rows of its group that see it."""
+    q, k, v, g = dec
     B, Hq, Nq, D = q.shape
-    Hkv = k.shape[1]
+    Hkv, Nkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
     sc = oracle.scale_value(None, D)
     u = U[dtype]
-    o, _ = oracle.attention(q, k, v, sc, causal, causal_offset=causal_offset)
-    pk, _ = oracle.attention(q, k, k, sc, causal, causal_offset=causal_offset)  # sum_j P_ij K_j
-    b = np.sqrt(np.sum((g * o) ** 2, axis=-1, keepdims=True))        # [B,Hq,Nq,1]
+    o, _ = oracle.attention(q, k, v, sc, causal, causal_offset=causal_offset, bias=bias)
+    pk, _ = oracle.attention(q, k, k, sc, causal, causal_offset=causal_offset,
+                             bias=bias)                                  # sum_j P_ij K_j
+    b = np.sqrt(np.sum((g * o) ** 2, axis=-1, keepdims=True))         # [B,Hq,Nq,1]
     t_dq = 12.0 * sc * u * b * np.abs(pk)
-    bg = b[..., 0].reshape(B, Hkv, G, Nq).max(axis=2)                 # [B,Hkv,Nq]
-    Nkv = k.shape[2]
-    if causal:   # rows i >= j - offset see key j
+    if bias is not None:
+        # rows i of the group that see key j: bias finite (and causal order)
+        vis = np.isfinite(np.broadcast_to(bias, (B, Hq, Nq, Nkv)))
+        if causal:
+            i = np.arange(Nq)[:, None]
+            j = np.arange(Nkv)[None, :]
+            vis = vis & (j <= i + causal_offset)
+        bmax = np.max(np.where(vis, b, 0.0).reshape(B, Hkv, G * Nq, Nkv), axis=2)
+        bmax = bmax[..., None]                                           # [B,Hkv,Nkv,1]
+    elif causal:   # rows i >= j - offset see key j
+        bg = b[..., 0].reshape(B, Hkv, G, Nq).max(axis=2)             # [B,Hkv,Nq]
         suffix = np.maximum.accumulate(bg[:, :, ::-1], axis=-1)[:, :, ::-1]
         bmax = np.zeros((B, Hkv, Nkv))
         for j in range(Nkv):
@@ -96,6 +114,7 @@ def delta_terms(x, do, ref, causal, causal_offset=0):
                 bmax[:, :, j] = suffix[:, :, i0]
         bmax = bmax[..., None]
     else:
+        bg = b[..., 0].reshape(B, Hkv, G, Nq).max(axis=2)
         bmax = bg.max(axis=-1)[:, :, None, None]
     qmax = np.abs(q).reshape(B, Hkv, -1).max(axis=-1)[:, :, None, None]
     rms_dv = np.sqrt(np.mean(ref[2] ** 2, axis=-1, keepdims=True))
@@ -233,17 +252,9 @@ def test_masked_gradients(gpu_device, kind, D):
     bias4 = np.broadcast_to(bias, (B, Hq, Nq, Nkv))
     dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
     ref = oracle.attention_backward(*dec, sc, False, bias=bias4)
-    # the Delta terms of the bound, with the mask in the oracle's attention
-    u = U[dtype]
-    o, _ = oracle.attention(*dec[:3], sc, False, bias=bias4)
-    pk, _ = oracle.attention(dec[0], dec[1], dec[1], sc, False, bias=bias4)
-    bq = np.sqrt(np.sum((dec[3] * o) ** 2, axis=-1, keepdims=True))
-    t_dq = 12.0 * sc * u * bq * np.abs(pk)
-    bmax = bq[..., 0].reshape(B, Hkv, -1).max(axis=-1)[:, :, None, None]
-    qmax = np.abs(dec[0]).reshape(B, Hkv, -1).max(axis=-1)[:, :, None, None]
-    t_dk = 6.0 * sc * u * bmax * qmax * np.sqrt(np.mean(ref[2] ** 2, axis=-1, keepdims=True))
+    terms = delta_terms_dec(dec, ref, dtype, False, bias=bias4)
     what = f"masked {kind} D={D}"
-    for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, (t_dq, t_dk, 0.0)):
+    for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, terms):
         check_grad(name, _host(got), r, dtype, what, None, t)
     if kind == "bool":
         assert torch.all(dq[0, 1, 5] == 0), "a row with no key has no gradient"
@@ -264,9 +275,9 @@ def test_sdpa_masked_autograd(gpu_device):
     bias = np.broadcast_to(np.where(keep, 0.0, -np.inf), (2, 4, 90, 120))
     dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
     ref = oracle.attention_backward(*dec, oracle.scale_value(None, 64), False, bias=bias)
-    for name, leaf, r in zip(("dq", "dk", "dv"), leaves, ref):
-        check_grad(name, _host(leaf.grad), r, dtype, "sdpa masked autograd", None,
-                   2e-3 * float(np.sqrt(np.mean(r ** 2))))
+    terms = delta_terms_dec(dec, ref, dtype, False, bias=bias)
+    for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
+        check_grad(name, _host(leaf.grad), r, dtype, "sdpa masked autograd", None, t)
     assert torch.all(leaves[1].grad[1, :, 100:] == 0) and torch.all(leaves[2].grad[1, :, 100:] == 0)
 
 
@@ -292,9 +303,9 @@ def test_masked_gradients_d96(gpu_device):
     bias = np.broadcast_to(np.where(keep, 0.0, -np.inf), (1, 2, 130, 140))
     dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
     ref = oracle.attention_backward(*dec, oracle.scale_value(None, 96), False, bias=bias)
-    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-        check_grad(name, _host(got), r, dtype, "masked D=96", None,
-                   2e-3 * float(np.sqrt(np.mean(r ** 2))))
+    terms = delta_terms_dec(dec, ref, dtype, False, bias=bias)
+    for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, terms):
+        check_grad(name, _host(got), r, dtype, "masked D=96", None, t)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -333,9 +344,9 @@ def test_value_width_masked(gpu_device):
     bias = np.broadcast_to(np.where(keep, 0.0, -np.inf), (1, 4, 130, 150))
     dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
     ref = oracle.attention_backward(*dec, oracle.scale_value(None, 192), False, bias=bias)
-    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-        check_grad(name, _host(got), r, dtype, "masked D=192 Dv=128", None,
-                   2e-3 * float(np.sqrt(np.mean(r ** 2))))
+    terms = delta_terms_dec(dec, ref, dtype, False, bias=bias)
+    for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, terms):
+        check_grad(name, _host(got), r, dtype, "masked D=192 Dv=128", None, t)
 
 
 def test_value_width_sdpa_autograd(gpu_device):
@@ -355,3 +366,44 @@ def test_value_width_sdpa_autograd(gpu_device):
     terms = delta_terms(x, do, ref, True)
     for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
         check_grad(name, _host(leaf.grad), r, dtype, "sdpa autograd D=192 Dv=128", None, t)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_broadcast_additive_mask_large_bias(gpu_device, D):
+    """A [B, 1, 1, Nkv] additive fp16 mask (row stride 0) with values of
+    12..20, with Nq not a multiple of the 64-row query tile.  Rows past Nq
+    in the last tile must get P = 0: exp2 of such a bias alone exceeds the
+    fp16 range, and inf * 0 would turn into NaN in dV and dK."""
+    import torch
+    dtype = inputs.F16
+    B, Hq, Hkv, Nq, Nkv = 2, 4, 2, 100, 136
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=300 + D)
+    do = inputs.make_dout(x)
+    rng = np.random.Generator(np.random.PCG64([D, 301]))
+    a = (12.0 + 8.0 * rng.random((B, 1, 1, Nkv))).astype(np.float32)
+    a[rng.random((B, 1, 1, Nkv)) < 0.2] = -np.inf
+    st = inputs.to_storage(a, dtype)
+    mt = to_device(st, dtype, gpu_device)
+    q, k, v, g = (to_device(t, dtype, gpu_device) for t in (x.q, x.k, x.v, do))
+    out, lse = binding.attn_fwd(q, k, v, mask=mt)
+    dq, dk, dv = binding.attn_bwd(q, k, v, out, lse, g, mask=mt)
+    torch.cuda.synchronize(gpu_device)
+    bias = np.broadcast_to(_decode(st, dtype), (B, Hq, Nq, Nkv))
+    dec = [_decode(t, dtype) for t in (x.q, x.k, x.v, do)]
+    ref = oracle.attention_backward(*dec, oracle.scale_value(None, D), False, bias=bias)
+    terms = delta_terms_dec(dec, ref, dtype, False, bias=bias)
+    what = f"broadcast additive mask 12..20 D={D}"
+    for name, got, r, t in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, terms):
+        check_grad(name, _host(got), r, dtype, what, None, t)
+
+
+# -- gradients at several thousand tokens: every element of dQ, dK and dV ----
+
+def test_long_d128_4133(gpu_device):
+    # bf16 MHA, 33 query tiles of the dK/dV kernel's 128 keys with a ragged tail
+    run_case(gpu_device, 1, 3, 3, 4133, 4133, 128, inputs.BF16, False, seed=4133)
+
+
+def test_long_gqa_causal_4096(gpu_device):
+    # the causal GQA 14/2 shape at 4096 tokens (dK/dV over head-split partials)
+    run_case(gpu_device, 1, 14, 2, 4096, 4096, 64, inputs.F16, True, seed=4096)

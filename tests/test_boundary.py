@@ -150,9 +150,33 @@ def test_tail_split_shapes(shape):
 
 
 def test_workspace_bytes():
-    assert binding.attn_fwd_workspace_bytes(1, 16, 1, 65536, 128, 1) == 0
-    assert binding.attn_fwd_workspace_bytes(2, 16, 10, 65536, 128, 4) == \
-        4 * 2 * 16 * 10 * (128 + 1) * 4
+    """attn_fwd_workspace_bytes(B, Hq, Nq, Nkv, D, causal): the bytes
+    attn_fwd allocates on a 256-CU device, i.e. its plan's workspace."""
+    ws = binding.attn_fwd_workspace_bytes
+    for shape in [(1, 24, 17160, 17160, 128, 0), (1, 16, 1, 65536, 128, 0),
+                  (1, 14, 4096, 4096, 64, 1), (2, 16, 10, 65536, 64, 2),
+                  (1, 16, 8192, 8192, 192, 0), (1, 32, 2048, 2048, 128, 0)]:
+        B, Hq, Nq, Nkv, D, causal = shape
+        want = plan(B, Hq, Hq, Nq, Nkv, D, causal).workspace_bytes
+        assert ws(B, Hq, Nq, Nkv, D, causal) == want, shape
+    # one decode row over 64K keys is split; a grid of whole rounds is not
+    assert ws(1, 16, 1, 65536, 128, 0) > 0
+    assert ws(1, 32, 2048, 2048, 128, 0) == 0
+    # invalid arguments give 0
+    lib = binding.load_library()
+    assert lib.attn_fwd_workspace_bytes(0, 16, 10, 100, 128, 0) == 0
+    assert lib.attn_fwd_workspace_bytes(1, 16, 10, 100, 72, 0) == 0
+    assert lib.attn_fwd_workspace_bytes(1, 16, 10, 100, 128, 3) == 0
+
+
+def test_workspace_bytes_signature():
+    """The header declares the query with the scope table's parameters."""
+    import re
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    m = re.search(r"size_t\s+attn_fwd_workspace_bytes\(([^)]*)\)", text)
+    assert m, "attn_fwd_workspace_bytes not declared"
+    params = [p.split()[-1] for p in m.group(1).split(",")]
+    assert params == ["B", "Hq", "Nq", "Nkv", "D", "causal"]
 
 
 def test_strerror(lib):

@@ -84,3 +84,31 @@ def test_ffn_video_width_sampled(gpu_device):
     rows = np.unique(np.concatenate([[0, 999, 1000, 1999, 2000, 3999, 4000, 4099],
                                      np.random.default_rng(9).choice(4100, 56, replace=False)]))
     _run(gpu_device, 4100, 1536, 8960, inputs.BF16, 1000, seed=9, rows=rows, verify=True)
+
+
+def test_ffn_verify_14b_width_default_chunk(gpu_device):
+    """Model width 5120, hidden 13824 (the 14B video DiT's block), 10000 rows
+    with the default chunk (4864 rows at this hidden width): the check
+    evaluates the first 2 * 4864 + 1 = 9729 rows as one chunk, the product
+    shape whose GEMM workspace selection is fixed (a candidate is taken
+    only if its stated workspace fits the buffer).  Output finite, 48
+    sampled rows (chunk edges included) against the oracle."""
+    N, Dm, F = 10000, 5120, 13824
+    rows = np.unique(np.concatenate([[0, 4863, 4864, 9727, 9728, 9729, 9999],
+                                     np.random.default_rng(10).choice(N, 41, replace=False)]))
+    _run(gpu_device, N, Dm, F, inputs.BF16, 0, seed=10, rows=rows, verify=True)
+
+
+def test_ffn_verify_rejects_nan(gpu_device):
+    """A NaN in the input gives NaN rows in both evaluations; the check must
+    fail on it rather than drop it."""
+    import torch
+    from memory_efficient_tiled_amd import ffn_chunked
+    dtype = inputs.BF16
+    xi = inputs.make_ffn_inputs(300, 64, 256, dtype, seed=11)
+    x, w1, b1, w2, b2 = (to_device(a, dtype, gpu_device)
+                         for a in (xi.x, xi.w1, xi.b1, xi.w2, xi.b2))
+    x[5, 3] = float("nan")
+    with pytest.raises(RuntimeError, match="chunking check failed"):
+        ffn_chunked(x, w1, b1, w2, b2, chunk_rows=100, verify=True)
+    torch.cuda.synchronize(gpu_device)
