@@ -65,8 +65,12 @@ enum {
   ATTN_EINVAL = -1,       /* bad argument (shape, pointer, alignment, dtype, scale) */
   ATTN_EUNSUPPORTED = -2, /* the current device is not gfx950 */
   ATTN_ENOMEM = -3,       /* a device workspace could not be allocated */
-  ATTN_EHIP = -4          /* a HIP call or kernel launch failed */
+  ATTN_EHIP = -4,         /* a HIP call or kernel launch failed */
+  ATTN_ESCRATCH = -5      /* attn_fwd_noalloc: the plan needs more than its scratch */
 };
+
+/* Bytes of the per-device scratch array of attn_fwd_noalloc (64 MiB). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * attn_fwd -- O and LSE of exact softmax attention (definition above).
@@ -115,6 +119,33 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* out,
                    float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                    float scale, int causal, int dtype, int num_splits,
                    void* stream);
+
+/*
+ * attn_fwd_noalloc -- attn_fwd_split that allocates nothing, for callers
+ * that cannot call hipMalloc: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, plan, kernels
+ * and results (bit for bit) as attn_fwd_split with the same num_splits.
+ *
+ * The split-KV partials go to a file-scope device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on
+ * holds until the process ends; its address is looked up once per device
+ * on the first call there.  A shape whose plan needs more (the workspace
+ * attn_fwd_plan reports for the same num_splits) returns ATTN_ESCRATCH
+ * before anything is launched; e.g. the 17160-token, 24-head video shape
+ * needs 59 MiB and fits, the 75600-token one does not.  Shapes that split
+ * nothing do not touch the array.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero: each call writes
+ * every partial it reads).  Calls that may overlap on one GPU -- on
+ * different streams, or from different threads without ordering -- race
+ * on it and must be serialised by the caller.  Returns as attn_fwd, plus
+ * ATTN_ESCRATCH.
+ */
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                     float* lse, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     float scale, int causal, int dtype, int num_splits,
+                     void* stream);
 
 /*
  * attn_fwd_check -- the argument validation of attn_fwd, host only: makes no

@@ -32,6 +32,10 @@ ATTN_EINVAL = -1
 ATTN_EUNSUPPORTED = -2
 ATTN_ENOMEM = -3
 ATTN_EHIP = -4
+ATTN_ESCRATCH = -5
+
+# bytes of the per-device scratch array of attn_fwd_noalloc
+ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -77,6 +81,9 @@ def load_library():
     lib.attn_fwd_split.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
         [ctypes.c_float, _INT, _INT, _INT, _VP]
     lib.attn_fwd_split.restype = _INT
+    lib.attn_fwd_noalloc.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
+        [ctypes.c_float, _INT, _INT, _INT, _VP]
+    lib.attn_fwd_noalloc.restype = _INT
     lib.attn_fwd_check.argtypes = [_VP, _VP, _VP, _VP, _VP] + shape_args + \
         [ctypes.c_float, _INT, _INT]
     lib.attn_fwd_check.restype = _INT
@@ -339,6 +346,44 @@ def attn_fwd(q, k, v, causal=False, scale: float | None = None,
     if rc != ATTN_OK:
         _raise(rc)
     return (out, lse) if return_lse else out
+
+
+def attn_fwd_noalloc(q, k, v, out, lse=None, causal=False, scale: float | None = None,
+                     num_splits: int = 0):
+    """attn_fwd on contiguous [B, H, N, D] tensors into the caller's ``out``
+    (and ``lse`` float32 [B, Hq, Nq], or None) without any device
+    allocation: the library's split-KV partials live in its per-device
+    scratch array (ATTN_NOALLOC_SCRATCH_BYTES); a plan that needs more
+    raises AttnError with code ATTN_ESCRATCH before anything runs.  Calls
+    that may overlap on one GPU race on that array.  Runs on torch's
+    current stream.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor on a HIP device")
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous, with q's dtype and device")
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nkv, _ = k.shape
+    if tuple(k.shape) != (B, Hkv, Nkv, D) or tuple(v.shape) != tuple(k.shape) or \
+            tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shapes must be q, out [B, Hq, Nq, D] and k, v [B, Hkv, Nkv, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  None if lse is None else lse.data_ptr(), B, Hq, Hkv, Nq,
+                                  Nkv, D, float(scale), causal_code(causal), _dtype_code(q),
+                                  int(num_splits), stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return out
 
 
 def attn_fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, causal=False,

@@ -37,9 +37,17 @@ struct DeviceInfo {
   bool init = false;
   bool gfx950 = false;
   int cus = 0;
+  void* scratch = nullptr;  // this device's address of `scratch` (attn_fwd_noalloc)
 };
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
+
+// Split-KV partials of attn_fwd_noalloc, for callers that cannot allocate
+// device memory.  Every device the library runs on holds its own copy, from
+// the library's load until the process ends.  In host code this name is not
+// a device address: host code uses only the address hipGetSymbolAddress
+// returns on each device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 int device_info(DeviceInfo* out) {
   int dev = 0;
@@ -64,6 +72,32 @@ int device_info(DeviceInfo* out) {
   }
   *out = d;
   return d.gfx950 ? ATTN_OK : ATTN_EUNSUPPORTED;
+}
+
+// The current device's address of `scratch`, looked up once per device
+// (with that device current) and kept.  ATTN_EHIP if the lookup fails.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_EHIP;
+  }
+  if (dev < 0 || dev >= 64) return ATTN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.scratch) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_last_hip_error = (int)e;
+      (void)hipGetLastError();
+      return ATTN_EHIP;
+    }
+    d.scratch = ptr;
+  }
+  *out = d.scratch;
+  return ATTN_OK;
 }
 
 // Element strides of one tensor's batch, head and sequence dimensions; the
@@ -292,9 +326,13 @@ hipError_t launch_combine(int Dv, const Params& p, bool strided, bool bf16, hipS
   }
 }
 
+// `noalloc`: take the split workspace from this device's `scratch` array
+// (ATTN_ESCRATCH, before any launch, when the plan needs more) instead of
+// hipMallocAsync.
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
         int Nq, int Nkv, int D, int Dv, const Layout& L, float scale, int causal, int dtype,
-        int num_splits, hipStream_t stream, const MaskArgs& M = MaskArgs()) {
+        int num_splits, hipStream_t stream, const MaskArgs& M = MaskArgs(),
+        bool noalloc = false) {
   int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, Dv, scale, causal, dtype, L, M);
   const bool masked = M.type != ATTN_MASK_NONE;
   if (rc != ATTN_OK) return rc;
@@ -342,7 +380,16 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   if (M.type == ATTN_MASK_ADD) p.c = 1.f;  // the mask step forms base-2 scores
 
   void* ws = nullptr;
-  if (split_wgs > 0) {
+  if (noalloc) {
+    void* sp = nullptr;
+    rc = scratch_address(&sp);
+    if (rc != ATTN_OK) return rc;
+    if (split_wgs > 0) {
+      if (pl.workspace_bytes() > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ESCRATCH;
+      p.opart = (float*)sp;
+      p.lsepart = p.opart + (size_t)pl.splits * p.prows * Dv;
+    }
+  } else if (split_wgs > 0) {
     hipError_t e = hipMallocAsync(&ws, pl.workspace_bytes(), stream);
     if (e != hipSuccess || !ws) {
       g_last_hip_error = (int)e;
@@ -426,6 +473,14 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* out, float
   return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D,
              contiguous_layout(Hq, Hkv, Nq, Nkv, D, D), scale, causal, dtype, num_splits,
              (hipStream_t)stream);
+}
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                     int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype,
+                     int num_splits, void* stream) {
+  return run(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, D, D,
+             contiguous_layout(Hq, Hkv, Nq, Nkv, D, D), scale, causal, dtype, num_splits,
+             (hipStream_t)stream, MaskArgs(), true);
 }
 
 }  // extern "C"
@@ -580,6 +635,8 @@ const char* attn_strerror(int code) {
     case ATTN_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case ATTN_ENOMEM: return "device workspace allocation failed";
     case ATTN_EHIP: return "HIP launch or runtime error";
+    case ATTN_ESCRATCH:
+      return "the split workspace exceeds the no-allocation scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

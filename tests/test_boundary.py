@@ -90,6 +90,14 @@ def test_attn_fwd_rejects_before_any_hip_call(lib):
     rc = lib.attn_fwd_split(Q, K, V, O, L, 1, 1, 1, 8, 8, 64, 0.125, 0, F16,
                             -1, None)
     assert rc == EINVAL
+    # the allocation-free variant validates the same way, before any HIP call
+    rc = lib.attn_fwd_noalloc(None, None, None, None, None, 1, 1, 1, 8, 8, 64,
+                              0.125, 0, F16, 0, None)
+    assert rc == EINVAL
+    rc = lib.attn_fwd_noalloc(Q, K, V, O, L, 1, 1, 1, 8, 8, 72, 0.125, 0, F16, 0, None)
+    assert rc == EINVAL
+    rc = lib.attn_fwd_noalloc(Q, K, V, O, L, 1, 1, 1, 8, 8, 64, 0.125, 0, F16, -1, None)
+    assert rc == EINVAL
 
 
 def plan(B, Hq, Hkv, Nq, Nkv, D, causal, dtype=BF16, num_splits=0):
@@ -181,8 +189,9 @@ def test_workspace_bytes_signature():
 
 def test_strerror(lib):
     for code in (OK, EINVAL, binding.ATTN_EUNSUPPORTED, binding.ATTN_ENOMEM,
-                 binding.ATTN_EHIP, 12345):
+                 binding.ATTN_EHIP, binding.ATTN_ESCRATCH, 12345):
         assert lib.attn_strerror(code)
+    assert b"scratch" in lib.attn_strerror(binding.ATTN_ESCRATCH)
 
 
 def test_python_wrapper_rejects_host_tensors():
