@@ -72,6 +72,46 @@ def measured_traffic(workload: str, pass_: str = "fwd", kernels: str | None = No
     return float(t.group(1))
 
 
+class StreamOrderedPeak:
+    """High-water mark of the device's default memory pool, which serves the
+    library's stream-ordered workspace (hipMallocAsync): reset before the
+    timed region, read after it.  Uses the HIP runtime this process has
+    already loaded (the one torch and the library share)."""
+
+    USED_MEM_HIGH = 0x8   # hipMemPoolAttrUsedMemHigh
+
+    def __init__(self, device_index: int = 0):
+        import ctypes
+        self.ok = False
+        path = None
+        with open("/proc/self/maps") as f:
+            for ln in f:
+                if "libamdhip64.so" in ln:
+                    path = ln.split()[-1]
+                    break
+        if path is None:
+            return
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.pool = ctypes.c_void_p()
+        self.ok = self.hip.hipDeviceGetDefaultMemPool(ctypes.byref(self.pool),
+                                                      device_index) == 0
+
+    def reset(self):
+        if self.ok:
+            zero = self.ct.c_uint64(0)
+            self.hip.hipMemPoolSetAttribute(self.pool, self.USED_MEM_HIGH, self.ct.byref(zero))
+
+    def read(self):
+        if not self.ok:
+            return None
+        v = self.ct.c_uint64(0)
+        if self.hip.hipMemPoolGetAttribute(self.pool, self.USED_MEM_HIGH,
+                                           self.ct.byref(v)) != 0:
+            return None
+        return int(v.value)
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -109,6 +149,10 @@ def main():
                          "first 7/8 of the keys (timing only: no CPU leg)")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "ffn"), default="fwd",
                     help="time the forward (default) or the gradients")
+    ap.add_argument("--graph", action="store_true",
+                    help="forward only: capture one step (attn_fwd_noalloc, which allocates "
+                         "nothing) in a HIP graph and time its replays, as a serving loop "
+                         "does for launch-bound shapes such as decode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this size "
                          "(scales the HBM byte counters)")
@@ -134,8 +178,8 @@ def main():
                           "launches": max(1, args.steps)}), flush=True)
         return
 
-    from memory_efficient_tiled_amd import (attn_bwd, attn_fwd, attn_fwd_fp8,
-                                            attn_fwd_num_splits, inputs)
+    from memory_efficient_tiled_amd import (attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_noalloc,
+                                            attn_fwd_num_splits, attn_fwd_plan, inputs)
     from memory_efficient_tiled_amd.binding import ATTN_BF16, ATTN_F16
 
     if args.pass_ == "ffn":
@@ -186,6 +230,20 @@ def main():
             attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=out, lse=lse,
                      num_splits=args.splits, mask=mask)
 
+    graph = None
+    if args.graph:
+        if bwd or fp8 or mask is not None or args.pass_ != "fwd":
+            raise SystemExit("bench.py: --graph covers the 16-bit forward without a mask")
+        # warm the library (device query, scratch address) outside the capture
+        attn_fwd_noalloc(q, k, v, out, lse, causal=w.causal, scale=w.scale,
+                         num_splits=args.splits)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            attn_fwd_noalloc(q, k, v, out, lse, causal=w.causal, scale=w.scale,
+                             num_splits=args.splits)
+        torch.cuda.synchronize()
+
     if bwd:
         dout = inputs.make_dout(x, seed=args.seed)
         g = up(dout)
@@ -195,6 +253,8 @@ def main():
         def step():
             attn_bwd(q, k, v, out, lse, g, causal=w.causal, scale=w.scale,
                      dq=dq, dk=dk, dv=dv, mask=mask)
+    elif graph is not None:
+        step = graph.replay
     else:
         step = fwd_step
 
@@ -202,6 +262,13 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    # peak memory of the timed steps: torch's allocator (the outputs are
+    # allocated before timing, so nothing is expected there) and the pool
+    # that serves the library's stream-ordered workspace
+    pool = StreamOrderedPeak(dev.index or 0)
+    torch.cuda.reset_peak_memory_stats(dev)
+    torch_before = torch.cuda.memory_allocated(dev)
+    pool.reset()
     # one event between consecutive steps: the whole region gives the mean,
     # the gaps give per-step median and minimum
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -214,6 +281,8 @@ def main():
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    torch_delta = torch.cuda.max_memory_allocated(dev) - torch_before
+    pool_peak = pool.read()
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     flops = w.bwd_flops if bwd else w.flops
@@ -224,9 +293,39 @@ def main():
 
     kernels = "fp8" if fp8 else args.pass_
     traffic = measured_traffic(name, args.pass_, kernels)
-    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                "traffic": traffic}
+    if w.bound == "hbm" and not bwd:
+        # below the ridge (decode): algorithmic bytes against HBM bandwidth
+        gbs = w.hbm_bytes / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes": w.hbm_bytes}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                    "traffic": traffic}
+
+    # memory: what the step needs beyond its inputs and preallocated outputs
+    # is the plan's workspace (split partials; the gradients' Delta rows),
+    # never anything of size Nq x Nkv
+    esz = 1 if fp8 else 2
+    out_bytes = (w.B * w.Hq * w.Nq * w.Dv * 2 + w.B * w.Hq * w.Nq * 4)
+    in_bytes = esz * (w.B * w.Hq * w.Nq * w.D + w.B * w.Hkv * w.Nkv * (w.D + w.Dv))
+    if bwd:
+        ws_plan = None   # Delta rows, plus fp32 dK/dV partials when heads are split
+    else:
+        ws_plan = attn_fwd_plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv,
+                                192 if w.Dv != w.D else w.D, w.causal, dcode,
+                                args.splits).workspace_bytes
+    score_bytes = 4.0 * w.B * w.Hq * w.Nq * w.Nkv
+    memory = {"inputs_bytes": in_bytes, "outputs_bytes": out_bytes,
+              "plan_workspace_bytes": None if ws_plan is None else int(ws_plan),
+              "peak_torch_delta_bytes": int(torch_delta),
+              "peak_stream_ordered_bytes": pool_peak,
+              "score_matrix_fp32_bytes": score_bytes}
+    if pool_peak is not None and not fp8 and not bwd:
+        # the library allocates nothing but its workspace (2 MiB pool granularity)
+        memory["within_workspace"] = bool(torch_delta == 0 and
+                                          pool_peak <= ws_plan + (2 << 20))
 
     if bwd:
         metric = ("attention bwd (dQ, dK, dV) TFLOP/s and % of MI355X bf16 MFMA peak "
@@ -250,15 +349,18 @@ def main():
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv,
                    "D": w.D, "Dv": w.Dv, "causal": w.causal, "scale": w.scale, "seed": args.seed,
                    "k_offset_std": w.k_offset_std, "mask": args.mask,
+                   "launch": "hip graph replay (attn_fwd_noalloc)" if graph is not None
+                             else "eager",
                    "split_kv": None if bwd else splits,
                    "kernel_source": source_hash(kernels)},
         "roofline": roofline,
+        "memory": memory,
     }
 
     if want_cpu:
         import oracle
         if bwd:
-            cpu_leg_bwd(result, x, w, name, dout, dq, np, oracle)
+            cpu_leg_bwd(result, x, w, name, dout, dq, dk, dv, np, oracle)
         else:
             cpu_leg_fwd(result, x, w, name, out, lse, np, oracle)
 
@@ -323,12 +425,14 @@ def cpu_leg_fwd(result, x, w, name, out, lse, np, oracle):
     progress(f"oracle {cpu_s:.1f} s; parity {result['parity']}")
 
 
-def cpu_leg_bwd(result, x, w, name, dout, dq, np, oracle):
+def cpu_leg_bwd(result, x, w, name, dout, dq, dk, dv, np, oracle):
     """dQ of sampled query rows against the oracle, and the oracle's gradient
     throughput on them.  dQ of row i depends on row i's inputs and every key
     only, so the oracle runs on the sampled rows alone: every fourth row of
     the forward's sample (causal: the first rows, which keep their
-    positions).  The sample's flops count the five products over those rows."""
+    positions).  The sample's flops count the five products over those rows.
+    Then dK and dV of every key of KV head 0 (batch 0), for which the oracle
+    runs over all query rows of the G query heads that read it."""
     from tests.parity import gather_rows
     R = max(2, x.rows.shape[1] // 4)
     rows = (np.tile(np.arange(min(R, w.Nq)), (w.Hq, 1)) if w.causal else x.rows[:, ::4])
@@ -357,10 +461,28 @@ def cpu_leg_bwd(result, x, w, name, dout, dq, np, oracle):
     err = np.abs(dq_gpu - dq_ref)
     rms = float(np.sqrt(np.mean(dq_ref ** 2)))
     u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11
-    result["parity"] = {"rows_per_head": int(rows.shape[1]), "tensor": "dq",
-                        "max_abs_err": float(err.max()),
-                        "mean_abs_err": float(err.mean()), "rms_ref": rms,
-                        "pass": bool(err.mean() <= 1.5 * u * rms)}
+    parity = {"rows_per_head": int(rows.shape[1]), "tensor": "dq",
+              "max_abs_err": float(err.max()),
+              "mean_abs_err": float(err.mean()), "rms_ref": rms,
+              "pass": bool(err.mean() <= 1.5 * u * rms)}
+    # dK, dV of KV head 0: every key, the oracle over all rows of its group
+    progress(f"oracle dK, dV of KV head 0 ({G} query heads x {w.Nq} rows)")
+    c1 = time.perf_counter()
+    _, dk_ref, dv_ref = oracle.attention_backward(
+        oracle.decode(x.q[:1, :G], w.dtype), oracle.decode(x.k[:1, :1], w.dtype),
+        oracle.decode(x.v[:1, :1], w.dtype), oracle.decode(dout[:1, :G], w.dtype),
+        sc, w.causal)
+    kv_s = time.perf_counter() - c1
+    for tname, got_t, ref in (("dk", dk, dk_ref), ("dv", dv, dv_ref)):
+        got = got_t[:1, :1].float().cpu().numpy().astype(np.float64)
+        e = np.abs(got - ref)
+        r = float(np.sqrt(np.mean(ref ** 2)))
+        parity[tname] = {"keys": int(w.Nkv), "max_abs_err": float(e.max()),
+                         "mean_abs_err": float(e.mean()), "rms_ref": r,
+                         "pass": bool(np.all(np.isfinite(got)) and e.mean() <= 1.5 * u * r)}
+    parity["pass"] = bool(parity["pass"] and parity["dk"]["pass"] and parity["dv"]["pass"])
+    parity["kv_head_oracle_s"] = round(kv_s, 2)
+    result["parity"] = parity
     result["cpu_baseline"] = {
         "value": round(sample_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
         "cores": blas_threads(), "kind": "oracle",

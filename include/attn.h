@@ -96,6 +96,12 @@ enum {
  * dtype   : ATTN_F16 or ATTN_BF16.
  * stream  : hipStream_t to launch on.
  *
+ * GQA head packing: with G = Hq / Hkv > 1 and a query range shorter than
+ * the head dimension's tile (decode, short chunks), the G query heads of a
+ * KV head are computed as one range of G * Nq rows (the post's "flattened
+ * GQA GEMMs", section "The DIY approach"), so each KV head's keys and values
+ * are read once for the group.  Results are the same function either way.
+ *
  * Query rows are processed in tiles of attn_plan.tile_rows rows.  Where
  * the tiles cannot keep every compute unit busy -- a grid smaller than the
  * device, or, without a mask, the last partial round of a grid that fills it
@@ -330,10 +336,12 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D,
  * fp32 partial outputs and partial LSE of the rows its plan splits over key
  * ranges, attn_plan.workspace_bytes of attn_fwd_plan(..., 0, 256, ...).
  * 0 when nothing is split, and for invalid arguments (a non-positive size,
- * an unsupported D, or causal outside 0..2).  The number of KV heads and
- * the dtype do not change the plan.  D = 192 stands for attn_fwd_dv's
- * (192, 128) pair.  On a device with another compute-unit count use
- * attn_fwd_plan.
+ * an unsupported D, or causal outside 0..2).  The dtype does not change the
+ * plan; the number of KV heads does only through GQA head packing (see
+ * attn_fwd), so this returns the largest workspace over every Hkv that
+ * divides Hq, a bound a caller can size a buffer by.  D = 192 stands for
+ * attn_fwd_dv's (192, 128) pair.  For one Hkv, or a device with another
+ * compute-unit count, use attn_fwd_plan.
  */
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
                                 int causal);

@@ -5,24 +5,34 @@
 
 #include "attn_fwd_kernel.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace {
 
 using namespace attn_fwd_detail;
 
-// The wide tiles of each head dimension are used without a causal mask when
-// they still fill every slot of the device at least once.
-int select_cfg(int B, int Hq, int Nq, int D, int causal, int num_cus) {
+// The tile every call of head dimension D may take (masked calls always do).
+int narrow_cfg(int D) {
   if (D == 192) return kCfgD192;
   if (D == 256) return kCfgD256;
   if (D == 96 || D == 80) return kCfgD96;
-  const int narrow = D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
+  return D == 128 ? kCfgD128Narrow : kCfgD64Narrow;
+}
+
+// The wide tiles of each head dimension are used without a causal mask or an
+// attention mask when they still fill every slot of the device at least
+// once; at D = 128 a query range of at most 128 rows per head (decode, or a
+// packed GQA group) takes the 128-row decode tile, unless masked.
+int select_cfg(int B, int Hq, int Nq, int D, int causal, bool masked, int num_cus) {
+  const int narrow = narrow_cfg(D);
+  if (D != 128 && D != 64) return narrow;
+  if (D == 128 && !masked && Nq <= kCfgs[kCfgD128Decode].BM()) return kCfgD128Decode;
   const int wide = D == 128 ? kCfgD128Wide : kCfgD64Wide;
   const TileCfg& w = kCfgs[wide];
   const long long wide_wgs = (long long)B * Hq * ((Nq + w.BM() - 1) / w.BM());
   const long long slots = (long long)w.resident_per_cu() * (num_cus > 0 ? num_cus : 256);
-  return (!causal && wide_wgs >= slots) ? wide : narrow;
+  return (!causal && !masked && wide_wgs >= slots) ? wide : narrow;
 }
 
 thread_local int g_last_hip_error = 0;
@@ -234,19 +244,22 @@ struct Plan {
 // the merge streams ~8 (Dv + 1) bytes per row and piece through HBM, about
 // kMergeStepsPerPiece steps of the whole chip per tile and piece (a 64-key
 // step of a 256-row tile is ~8 MFLOP, ~2 us on one CU).
+// The merge term scales with the tile's live rows (row_frac of its BM;
+// below 1 for short query ranges, e.g. decode).
 constexpr double kPieceFillSteps = 2.0;
 constexpr double kMergeStepsPerPiece = 0.03;
-constexpr int kMaxSplits = 64;
-constexpr int kMinStepsPerPiece = 8;
+constexpr int kMaxSplits = 256;
+constexpr int kMinStepsPerPiece = 4;
 
-int balanced_splits(long long rem, long long slots, int ktiles) {
+int balanced_splits(long long rem, long long slots, int ktiles, double row_frac) {
   int best = 1;
   double best_cost = (double)((rem + slots - 1) / slots) * ktiles;
   const int smax = std::min(kMaxSplits, ktiles / kMinStepsPerPiece);
   for (int s = 2; s <= smax; ++s) {
     const int steps = (ktiles + s - 1) / s;
     const double rounds = (double)((s * rem + slots - 1) / slots);
-    const double cost = rounds * (steps + kPieceFillSteps) + kMergeStepsPerPiece * s * rem;
+    const double cost =
+        rounds * (steps + kPieceFillSteps) + kMergeStepsPerPiece * s * rem * row_frac;
     if (cost < best_cost) {
       best = s;
       best_cost = cost;
@@ -272,7 +285,7 @@ int causal_splits(long long tiles, long long slots, int ktiles) {
 Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int Dv, int causal, int num_splits,
                int num_cus, bool masked = false) {
   Plan pl;
-  pl.cfg = select_cfg(B, Hq, Nq, D, causal || masked, num_cus);
+  pl.cfg = select_cfg(B, Hq, Nq, D, causal, masked, num_cus);
   pl.Dv = Dv;
   const TileCfg c = kCfgs[pl.cfg];
   pl.n_qtiles = (Nq + c.BM() - 1) / c.BM();
@@ -289,7 +302,7 @@ Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int Dv, int causal, int nu
   } else {
     const long long rem = pl.tiles % slots;
     first = pl.tiles - rem;
-    S = rem ? balanced_splits(rem, slots, ktiles) : 1;
+    S = rem ? balanced_splits(rem, slots, ktiles, std::min(1.0, (double)Nq / c.BM())) : 1;
   }
   if (S > ktiles) S = ktiles;
   const int tps = (ktiles + S - 1) / S;
@@ -300,6 +313,68 @@ Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int Dv, int causal, int nu
   const long long bh = pl.first_split / pl.n_qtiles, qt = pl.first_split % pl.n_qtiles;
   pl.row0 = S > 1 ? bh * Nq + qt * c.BM() : pl.rows;
   return pl;
+}
+
+// GQA head packing (the English noflash-attention post's "flattened GQA
+// GEMMs", section "The DIY approach").  The G = Hq / Hkv query heads of a KV
+// head read the same keys, so when each head's query range is shorter than
+// a tile, the G ranges are computed as one range of G * Nq rows of the KV
+// head: K and V stream once per group instead of once per head, and the
+// tiles fill.  Row r of that range is query head hk * G + r / Nq at
+// position r % Nq (the kernel takes the position for the causal mask).
+// That is a plain re-indexing when each head's rows follow the previous
+// head's (head stride = Nq * row stride, or Nq = 1) in Q, the output and
+// the mask; other layouts are not packed.
+struct Packing {
+  bool on = false;
+  int Hq = 0, Nq = 0;  // the launch's heads and rows (packed or not)
+  Layout L;
+  MaskArgs M;
+};
+
+Packing packing(int Hq, int Hkv, int Nq, int D, int Dv, const Layout& L, const MaskArgs& M) {
+  Packing pk;
+  pk.Hq = Hq;
+  pk.Nq = Nq;
+  pk.L = L;
+  pk.M = M;
+  const int G = Hq / Hkv;
+  if (G <= 1 || Nq >= kCfgs[narrow_cfg(D)].BM()) return pk;
+  auto flat = [&](Strides s, Strides* out) {
+    if (Nq == 1)
+      s.n = s.h;
+    else if (s.h != (int64_t)Nq * s.n)
+      return false;
+    s.h *= G;
+    *out = s;
+    return true;
+  };
+  Layout P = L;
+  if (!flat(L.q, &P.q) || !flat(L.o, &P.o) || !strides_ok(P.q, D) || !strides_ok(P.o, Dv))
+    return pk;
+  MaskArgs PM = M;
+  if (M.type != ATTN_MASK_NONE) {
+    if (Nq == 1)
+      PM.sq = M.sh;
+    else if (M.sh != (int64_t)Nq * M.sq)
+      return pk;
+    PM.sh = M.sh * G;
+  }
+  pk.on = true;
+  pk.Hq = Hkv;
+  pk.Nq = G * Nq;
+  pk.L = P;
+  pk.M = PM;
+  return pk;
+}
+
+// The plan of a call on contiguous tensors, packing included (the planning
+// queries describe attn_fwd, whose tensors are contiguous).
+Plan contiguous_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int Dv, int causal,
+                     int num_splits, int num_cus) {
+  const Packing pk = packing(Hq, Hkv, Nq, D, Dv, contiguous_layout(Hq, Hkv, Nq, Nkv, D, Dv),
+                             MaskArgs());
+  return make_plan(B, pk.Hq, pk.Nq, Nkv, D, Dv, causal, num_splits, num_cus);
 }
 
 hipError_t launch_fwd(int D, int Dv, const Params& p, int cfg, bool causal, bool split,
@@ -341,6 +416,12 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   rc = device_info(&di);
   if (rc != ATTN_OK) return rc;
 
+  // From here on the launch's heads, rows and strides are the packed ones
+  // when the G query heads of a KV head are packed.
+  const Packing pk = packing(Hq, Hkv, Nq, D, Dv, L, M);
+  const int Nq0 = Nq;
+  Hq = pk.Hq;
+  Nq = pk.Nq;
   const Plan pl = make_plan(B, Hq, Nq, Nkv, D, Dv, causal, num_splits, di.cus, masked);
   const long long split_wgs = (pl.tiles - pl.first_split) * pl.splits;
   if (pl.first_split > INT32_MAX || split_wgs > INT32_MAX) return ATTN_EINVAL;
@@ -350,17 +431,18 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
   p.o = (uint16_t*)out;
-  p.qsb = L.q.b, p.qsh = L.q.h, p.qsn = (int)L.q.n;
-  p.ksb = L.k.b, p.ksh = L.k.h, p.ksn = (int)L.k.n;
-  p.vsb = L.v.b, p.vsh = L.v.h, p.vsn = (int)L.v.n;
-  p.osb = L.o.b, p.osh = L.o.h, p.osn = (int)L.o.n;
+  const Layout& PL = pk.L;
+  p.qsb = PL.q.b, p.qsh = PL.q.h, p.qsn = (int)PL.q.n;
+  p.ksb = PL.k.b, p.ksh = PL.k.h, p.ksn = (int)PL.k.n;
+  p.vsb = PL.v.b, p.vsh = PL.v.h, p.vsn = (int)PL.v.n;
+  p.osb = PL.o.b, p.osh = PL.o.h, p.osn = (int)PL.o.n;
   p.lse = lse;
   p.opart = nullptr;
   p.lsepart = nullptr;
   p.Hq = Hq;
   p.Nq = Nq;
   p.Nkv = Nkv;
-  p.G = Hq / Hkv;
+  p.G = Hq / Hkv;  // 1 when packed
   p.Hkv = Hkv;
   p.n_qtiles = pl.n_qtiles;
   p.n_splits = pl.splits;
@@ -372,10 +454,11 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   // times FLT_MIN rounds to a base-2 exponent of 0, as it should.
   p.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
-  p.coff = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0;
-  p.mask = (const uint8_t*)M.ptr;
-  p.msb = M.sb, p.msh = M.sh, p.msq = M.sq;
-  p.mask_mode = M.type;
+  p.coff = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq0 : 0;
+  p.pos_nq = pk.on ? Nq0 : 0;
+  p.mask = (const uint8_t*)pk.M.ptr;
+  p.msb = pk.M.sb, p.msh = pk.M.sh, p.msq = pk.M.sq;
+  p.mask_mode = pk.M.type;
   p.cm = p.c;
   if (M.type == ATTN_MASK_ADD) p.c = 1.f;  // the mask step forms base-2 scores
 
@@ -403,7 +486,8 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   const bool cz = causal != 0;
   const Layout C = contiguous_layout(Hq, Hkv, Nq, Nkv, D, Dv);
   auto same = [](const Strides& a, const Strides& b) { return a.b == b.b && a.h == b.h && a.n == b.n; };
-  const bool strided = !(same(L.q, C.q) && same(L.k, C.k) && same(L.v, C.v) && same(L.o, C.o));
+  const bool strided =
+      !(same(PL.q, C.q) && same(PL.k, C.k) && same(PL.v, C.v) && same(PL.o, C.o));
   const bool bf16 = dtype == ATTN_BF16;
   auto launch = [&](bool split) {
     return launch_fwd(D, Dv, p, pl.cfg, cz, split, strided, masked, bf16, stream);
@@ -601,7 +685,7 @@ int attn_fwd_num_splits(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int caus
   if (!head_dims_ok(D, plan_dv(D)) || (dtype != ATTN_F16 && dtype != ATTN_BF16))
     return ATTN_EINVAL;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_EINVAL;
-  return make_plan(B, Hq, Nq, Nkv, D, plan_dv(D), causal, 0, num_cus).splits;
+  return contiguous_plan(B, Hq, Hkv, Nq, Nkv, D, plan_dv(D), causal, 0, num_cus).splits;
 }
 
 int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int dtype,
@@ -613,7 +697,7 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, in
     return ATTN_EINVAL;
   if ((long long)B * Hq * Nq > INT32_MAX || (long long)B * Hkv * Nkv > INT32_MAX)
     return ATTN_EINVAL;
-  const Plan pl = make_plan(B, Hq, Nq, Nkv, D, plan_dv(D), causal, num_splits, num_cus);
+  const Plan pl = contiguous_plan(B, Hq, Hkv, Nq, Nkv, D, plan_dv(D), causal, num_splits, num_cus);
   plan->tile_rows = kCfgs[pl.cfg].BM();
   plan->num_splits = pl.splits;
   plan->split_rows = pl.rows - pl.row0;
@@ -621,11 +705,19 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, in
   return ATTN_OK;
 }
 
+// The plan depends on the number of KV heads only through GQA head
+// packing; without it the query returns the largest workspace over every
+// Hkv that divides Hq.
 size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D, int causal) {
   if (B <= 0 || Hq <= 0 || Nq <= 0 || Nkv <= 0 || !head_dims_ok(D, plan_dv(D))) return 0;
   if (causal < 0 || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return 0;
   if ((long long)B * Hq * Nq > INT32_MAX) return 0;
-  return make_plan(B, Hq, Nq, Nkv, D, plan_dv(D), causal, 0, kMi355xCus).workspace_bytes();
+  size_t most = 0;
+  for (int Hkv = 1; Hkv <= Hq; ++Hkv)
+    if (Hq % Hkv == 0)
+      most = std::max(most, contiguous_plan(B, Hq, Hkv, Nq, Nkv, D, plan_dv(D), causal, 0,
+                                            kMi355xCus).workspace_bytes());
+  return most;
 }
 
 const char* attn_strerror(int code) {

@@ -74,6 +74,9 @@ struct Params {
   float c;            // |scale| * log2(e)
   uint32_t qsign;     // 0x80008000 flips the sign of Q (negative scale)
   int coff;           // causal: row i sees keys j <= i + coff (0 top-left, Nkv - Nq bottom-right)
+  int pos_nq;         // > 0 when the G query heads of a KV head are packed into one
+                      // [G * Nq] row range: row r is then position r % pos_nq
+                      // (pos_nq = the real Nq) for the causal mask; 0 = not packed
   // Element strides of the batch, head and sequence dimensions (the head
   // dimension is contiguous); row strides fit in 32 bits.
   int64_t qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
@@ -114,6 +117,10 @@ struct TileCfg {
   constexpr int BM() const { return NW * QB * 32; }
   constexpr int resident_per_cu() const { return 4 * kWavesPerSimd / NW; }
 };
+// Short query ranges at D = 128 (decode, or the packed query heads of a
+// GQA group: at most 128 rows) take a 4-wave, 128-row tile: two workgroups
+// per CU then stream two key ranges at once, and waves without rows skip
+// the arithmetic.
 enum {
   kCfgD64Narrow = 0,
   kCfgD64Wide = 1,
@@ -122,16 +129,18 @@ enum {
   kCfgD256 = 4,
   kCfgD96 = 5,
   kCfgD192 = 6,
-  kCfgD128Masked = 7
+  kCfgD128Masked = 7,
+  kCfgD128Decode = 8
 };
-constexpr TileCfg kCfgs[8] = {{4, 1, 64, 0, false},
+constexpr TileCfg kCfgs[9] = {{4, 1, 64, 0, false},
                               {4, 2, 32, 0, false},
                               {8, 1, 64, 0, false},
                               {8, 2, 32, 3, true},
                               {8, 1, 32, 8, true},
                               {4, 1, 64, 0, false},
                               {8, 1, 64, 4, true},
-                              {8, 1, 64, 4, true}};
+                              {8, 1, 64, 4, true},
+                              {4, 1, 64, 0, false}};
 
 // Launch the forward kernels of one pair of head dimensions (Q/K, V/O),
 // defined one pair per translation unit in attn_fwd_d<D>[v<DV>].hip.  The
@@ -251,11 +260,20 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const int hk = hq / p.G;
   const int q0 = qt * BM;
   const int wq0 = q0 + wave * WR;       // first query row of this wave
+  // A wave whose rows all lie past Nq (the ragged last tile, or the short
+  // row ranges of decode) computes nothing: it only copies its share of
+  // every K/V tile and meets every barrier.
+  const bool idle = wq0 >= p.Nq;
+  // Causal position of this wave's first row (packed rows: the smallest
+  // position any of them can have, 0).
+  const int wpos0 = p.pos_nq ? 0 : wq0;
 
   // A split launch covers one key range per piece; otherwise every key.
   const int kbeg = SPLIT ? sp * p.split_len : 0;
   int kend = SPLIT ? min(p.Nkv, kbeg + p.split_len) : p.Nkv;
-  if (CAUSAL) kend = max(0, min(kend, q0 + BM + p.coff));  // keys past the last row's are masked
+  // Causal: keys past the reach of the tile's last position are masked.
+  // Packed rows hold positions 0 .. pos_nq - 1 of several heads.
+  if (CAUSAL) kend = max(0, min(kend, (p.pos_nq ? min(q0 + BM, p.pos_nq) : q0 + BM) + p.coff));
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
   const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;  // LSE / partial row of query 0
@@ -379,6 +397,9 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     }
   };
 
+  // Causal position of query row r of this launch (packed rows: r % pos_nq).
+  auto qpos_of = [&](int r) { return p.pos_nq ? r % p.pos_nq : r; };
+
   // Keys past the valid range, and (causal) keys after the row, get -inf:
   // only on tiles that straddle the end of the key range or the diagonal.
   // With a mask, every tile first goes through the mask: a boolean mask
@@ -389,12 +410,12 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   // registers.)
   auto mask = [&](int t, f32x16* s) __attribute__((always_inline)) {
     const int k0 = kbeg + t * BN;
-    const bool edge = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wq0 + p.coff);
+    const bool edge = (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > wpos0 + p.coff);
     if constexpr (!MASKED) {
       if (edge) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int qrow = wq0 + qb * 32 + l32;
+          const int qpos = qpos_of(wq0 + qb * 32 + l32);
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -404,7 +425,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
               for (int i = 0; i < 4; ++i) {
                 const int key = key0 + i;
                 const float v = s[qb * NKB + kb][4 * g + i];
-                const bool ok = key < kend && (!CAUSAL || key <= qrow + p.coff);
+                const bool ok = key < kend && (!CAUSAL || key <= qpos + p.coff);
                 s[qb * NKB + kb][4 * g + i] = ok ? v : -INFINITY;
               }
             }
@@ -445,7 +466,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     if (edge) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wq0 + qb * 32 + l32;
+        const int qpos = qpos_of(wq0 + qb * 32 + l32);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -453,7 +474,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int key = k0 + kb * 32 + 8 * g + 4 * hl + i;
-              const bool ok = key < kend && (!CAUSAL || key <= qrow + p.coff);
+              const bool ok = key < kend && (!CAUSAL || key <= qpos + p.coff);
               const float v = s[qb * NKB + kb][4 * g + i];
               s[qb * NKB + kb][4 * g + i] = ok ? v : -INFINITY;
             }
@@ -602,8 +623,45 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   // work overlaps the other's matrix work.  K_t sits in kbuf[t % 2] and V_t
   // in vbuf[t % 3]: the copies of step t (K_{t+1}, V_{t+1}) overwrite K_{t-1}
   // and V_{t-2}, which every wave has finished with once past the barrier.
+  // Idle waves (no rows below Nq): the copies and barriers of the loops
+  // below, in the same order and into the same buffers, and nothing else.
+  // Single-buffered: one barrier per tile, after which K_{t+1}, V_{t+1}
+  // go to kbuf[(t+1) % 2], vbuf[(t+1) % 3].  Double-buffered: one barrier
+  // after the first tile's copies, then one per tile, after which K_{t+2}
+  // goes to kbuf[t % 2] and V_{t+1} to vbuf[(t+1) % 2].
+  auto idle_loop = [&]() {
+    if (ntiles <= 0) return;
+    issue_k(0, kbuf0);
+    issue_v(0, vbuf0);
+    if constexpr (SB) {
+      for (int t = 0; t < ntiles; ++t) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 1 < ntiles) {
+          const int v3 = (t + 1) % 3;
+          issue_k(t + 1, ((t + 1) & 1) ? kbuf1 : kbuf0);
+          issue_v(t + 1, v3 == 0 ? vbuf0 : v3 == 1 ? vbuf1 : vbuf2);
+        }
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (ntiles > 1) issue_k(1, kbuf1);
+      for (int t = 0; t < ntiles; ++t) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 1 < ntiles) {
+          if (t + 2 < ntiles) issue_k(t + 2, (t & 1) ? kbuf1 : kbuf0);
+          issue_v(t + 1, ((t + 1) & 1) ? vbuf1 : vbuf0);
+        }
+      }
+    }
+  };
+
   f32x16 sa[QB * NKB], sb[SB ? 1 : QB * NKB];
-  if constexpr (SB) {
+  if (idle) {
+    idle_loop();
+  } else if constexpr (SB) {
     const bool late = NW >= 2 && wave >= NW / 2;
     u32x4 pf[QB * NKC];
     // One step: K_t in kc, V_t in vc, V_{t-1} in vp; K_{t+1}, V_{t+1} go to
@@ -746,6 +804,90 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   if (c4 == 0 && lse) lse[row0 + row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
+// The same merge for rows cut into many pieces (decode: a few rows, up to
+// 256 pieces each): one workgroup of 1024 threads per output row, so that
+// every piece's loads are in flight at once (with few rows the merge is
+// bound by load latency).  The threads first find the largest piece LSE
+// together; then groups of GS threads take every NG-th piece, each thread
+// 4 columns, and the groups' sums meet in LDS.
+constexpr int kRowMergeThreads = 1024;
+
+template <int D, class Tag, bool STRIDED>
+__global__ __launch_bounds__(kRowMergeThreads) void attn_combine_rows_kernel(
+    const float* __restrict__ opart, const float* __restrict__ lsepart, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int rows, int row0, int n_splits, int Hq, int Nq, int64_t osb,
+    int64_t osh, int osn) {
+  using N = Num<Tag>;
+  constexpr int T = kRowMergeThreads;
+  constexpr int C4 = D / 4;
+  constexpr int GS = C4 <= 32 ? 32 : 64;
+  constexpr int NG = T / GS;
+  __shared__ float red[T];
+  __shared__ f32x4 part[NG][GS];
+  __shared__ float wpart[NG];
+  const int row = blockIdx.x;  // grid = rows
+  const int t = threadIdx.x;
+  float mx = -INFINITY;
+  for (int s = t; s < n_splits; s += T) mx = fmaxf(mx, lsepart[(size_t)s * rows + row]);
+  red[t] = mx;
+  __syncthreads();
+  for (int w = T / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
+  }
+  mx = red[0];
+  const int g = t / GS, c4 = t % GS;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    // eight pieces per round, their loads issued together (few rows: the
+    // merge is bound by load latency, not bandwidth)
+    constexpr int U = 8;
+    for (int s0 = g; s0 < n_splits; s0 += U * NG) {
+      float ls[U];
+      f32x4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u * NG;
+        ls[u] = s < n_splits ? lsepart[(size_t)s * rows + row] : -INFINITY;
+        x[u] = (s < n_splits && c4 < C4)
+                   ? *(const f32x4*)(opart + ((size_t)s * rows + row) * D + c4 * 4)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = (ls[u] == -INFINITY) ? 0.f : expf(ls[u] - mx);
+        wsum += w;
+        acc += w * x[u];
+      }
+    }
+  }
+  part[g][c4] = acc;
+  if (c4 == 0) wpart[g] = wsum;
+  __syncthreads();
+  if (t >= C4) return;
+  f32x4 a = part[0][t];
+  float ws = wpart[0];
+#pragma unroll
+  for (int gg = 1; gg < NG; ++gg) {
+    a += part[gg][t];
+    ws += wpart[gg];
+  }
+  const float inv = ws > 0.f ? 1.f / ws : 0.f;
+  u32x2 y = {N::pack2(a[0] * inv, a[1] * inv), N::pack2(a[2] * inv, a[3] * inv)};
+  const int r = row0 + row;
+  size_t at = (size_t)r * D;  // contiguous: output row r
+  if (STRIDED) {
+    const int i = r % Nq, bh = r / Nq;
+    at = (bh / Hq) * osb + (bh % Hq) * osh + (size_t)i * osn;
+  }
+  *(u32x2*)(o + at + t * 4) = y;
+  if (t == 0 && lse) lse[row0 + row] = ws > 0.f ? mx + logf(ws) : -INFINITY;
+}
+
+// Pieces per row above which the merge takes a workgroup per row.
+constexpr int kRowMergeSplits = 16;
+
 // Masked launches always take the strided kernels (the mask has strides
 // of its own) and only the narrow tiles.
 template <int D, int DV, int CFG, class Tag, bool CAUSAL, bool SPLIT, bool MASKED>
@@ -791,6 +933,8 @@ hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool st
                                              : kCfgD64Wide;
   constexpr int kMasked = D == 128 ? kCfgD128Masked : kNarrow;
   if (masked) return dispatch<D, DV, kMasked, Tag, true>(p, causal, split, true, st);
+  if constexpr (D == 128 && DV == 128)
+    if (cfg == kCfgD128Decode) return dispatch<D, DV, kCfgD128Decode, Tag, false>(p, causal, split, strided, st);
   if (kWide != kNarrow && cfg == kWide && !causal)
     return split ? launch_main<D, DV, kWide, Tag, false, true, false>(p, strided, st)
                  : launch_main<D, DV, kWide, Tag, false, false, false>(p, strided, st);
@@ -799,6 +943,17 @@ hipError_t dispatch_d(const Params& p, int cfg, bool causal, bool split, bool st
 
 template <int D, class Tag>
 hipError_t launch_combine(const Params& p, bool strided, hipStream_t st) {
+  if (p.n_splits > kRowMergeSplits) {
+    if (strided)
+      hipLaunchKernelGGL((attn_combine_rows_kernel<D, Tag, true>), dim3(p.prows),
+                         dim3(kRowMergeThreads), 0, st, p.opart, p.lsepart, p.o, p.lse, p.prows,
+                         p.row0, p.n_splits, p.Hq, p.Nq, p.osb, p.osh, p.osn);
+    else
+      hipLaunchKernelGGL((attn_combine_rows_kernel<D, Tag, false>), dim3(p.prows),
+                         dim3(kRowMergeThreads), 0, st, p.opart, p.lsepart, p.o, p.lse, p.prows,
+                         p.row0, p.n_splits, p.Hq, p.Nq, p.osb, p.osh, p.osn);
+    return hipGetLastError();
+  }
   const size_t threads = (size_t)p.prows * (D / 4);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (strided)

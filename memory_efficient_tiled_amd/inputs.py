@@ -67,6 +67,22 @@ class Workload:
         f = 2.0 * self.B * self.Hq * self.Nq * self.Nkv * (3 * self.D + 2 * self.Dv)
         return f / 2.0 if self.causal else f
 
+    @property
+    def hbm_bytes(self) -> float:
+        """Algorithmic HBM bytes of one forward: Q, K, V read once, O written
+        once (2 bytes an element; 1 for FP8 inputs), LSE written once (fp32)."""
+        e = 1 if self.dtype == FP8 else 2
+        q = self.B * self.Hq * self.Nq * self.D
+        kv = self.B * self.Hkv * self.Nkv * (self.D + self.Dv)
+        o = self.B * self.Hq * self.Nq * self.Dv
+        return float(e * (q + kv) + 2 * o + 4 * self.B * self.Hq * self.Nq)
+
+    @property
+    def bound(self) -> str:
+        """The roofline bound: "hbm" below the MI355X ridge of 2.5e15 / 8e12
+        = 312.5 flop per byte, else "mfma"."""
+        return "hbm" if self.flops / self.hbm_bytes < 2.5e15 / 8e12 else "mfma"
+
     def describe(self) -> str:
         dv = f" Dv={self.Dv}" if self.Dv != self.D else ""
         return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} Nq={self.Nq} "
@@ -98,6 +114,15 @@ WORKLOADS["dit-75600"] = _w(name="dit-75600", B=1, Hq=24, Hkv=24, Nq=75600,
                             Nkv=75600, D=128, dtype=BF16, causal=False,
                             sampled_rows=256,
                             note="long video-DiT self-attention")
+
+# Decode: one new query row per head over a 64K-token cache, 16 query heads
+# on 2 KV heads (the GQA grouping the post flattens, section "The DIY
+# approach"; its long-context LLM table, section "Where it landed").  HBM-
+# bound: K and V are read once per KV head when the 8 query heads of a group
+# are packed into one tile.
+WORKLOADS["decode-64k"] = _w(name="decode-64k", B=1, Hq=16, Hkv=2, Nq=1, Nkv=65536,
+                             D=128, dtype=BF16, causal=False,
+                             note="GQA decode over a 64K-token cache")
 
 # Head dimension 256, beyond the pages' 64/128 (the scope's list of further
 # head dimensions): an MHA sweep point and a causal GQA prefill shape.

@@ -195,3 +195,30 @@ def fp8_bounds(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
                 mbound[b, h] = 2.0 * sigma + sterm
                 lbound[b, h] = dsm[:, 0]
     return bound, mbound, lbound
+
+
+class PoolPeak:
+    """High-water mark of the device's default memory pool, which serves the
+    library's stream-ordered workspace (hipMallocAsync), through the HIP
+    runtime this process has already loaded."""
+
+    USED_MEM_HIGH = 0x8   # hipMemPoolAttrUsedMemHigh
+
+    def __init__(self, device_index: int = 0):
+        import ctypes
+        path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64.so" in ln)
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.pool = ctypes.c_void_p()
+        assert self.hip.hipDeviceGetDefaultMemPool(ctypes.byref(self.pool), device_index) == 0
+
+    def reset(self):
+        zero = self.ct.c_uint64(0)
+        assert self.hip.hipMemPoolSetAttribute(self.pool, self.USED_MEM_HIGH,
+                                               self.ct.byref(zero)) == 0
+
+    def read(self) -> int:
+        v = self.ct.c_uint64(0)
+        assert self.hip.hipMemPoolGetAttribute(self.pool, self.USED_MEM_HIGH,
+                                               self.ct.byref(v)) == 0
+        return int(v.value)

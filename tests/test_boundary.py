@@ -143,6 +143,27 @@ def test_split_heuristic():
         plan(1, 3, 2, 10, 10, 64, 0)
 
 
+def test_gqa_packing_plans():
+    """Short query ranges of a GQA group are packed into one row range of
+    the KV head.  Decode over 64K keys with 16 query heads on 2 KV heads:
+    2 tiles of 8 rows (the 128-row decode tile), cut into enough key ranges
+    for two workgroups per CU; the 16 output rows are the ones merged."""
+    p = plan(1, 16, 2, 1, 65536, 128, 0)
+    assert p.tile_rows == 128 and p.split_rows == 16
+    assert 2 * p.num_splits >= 2 * 256
+    assert p.workspace_bytes == p.num_splits * 16 * 129 * 4
+    # MHA decode is not packed: 16 one-row tiles
+    m = plan(1, 16, 16, 1, 65536, 128, 0)
+    assert m.tile_rows == 128 and 16 * m.num_splits >= 2 * 256
+    # packed causal GQA with 100-row chunks (D = 64, 128-row tiles)
+    g = plan(1, 14, 2, 100, 4096, 64, 1)
+    assert g.tile_rows == 128 and g.split_rows == 1400
+    # a long query range is not packed and takes the 256-row tile
+    assert plan(1, 14, 2, 4096, 4096, 128, 1).tile_rows == 256
+    # the (192, 128) pair has one tile of 256 rows
+    assert plan(1, 16, 2, 1, 65536, 192, 0).tile_rows == 256
+
+
 @pytest.mark.parametrize("shape", [
     (1, 26, 26, 2600, 2000, 128), (1, 26, 13, 2600, 2000, 128),
     (1, 40, 8, 1700, 1000, 64), (2, 32, 8, 2100, 2000, 64),
@@ -165,7 +186,9 @@ def test_workspace_bytes():
                   (1, 14, 4096, 4096, 64, 1), (2, 16, 10, 65536, 64, 2),
                   (1, 16, 8192, 8192, 192, 0), (1, 32, 2048, 2048, 128, 0)]:
         B, Hq, Nq, Nkv, D, causal = shape
-        want = plan(B, Hq, Hq, Nq, Nkv, D, causal).workspace_bytes
+        # the largest plan over every KV head count (GQA packing changes it)
+        want = max(plan(B, Hq, Hkv, Nq, Nkv, D, causal).workspace_bytes
+                   for Hkv in range(1, Hq + 1) if Hq % Hkv == 0)
         assert ws(B, Hq, Nq, Nkv, D, causal) == want, shape
     # one decode row over 64K keys is split; a grid of whole rounds is not
     assert ws(1, 16, 1, 65536, 128, 0) > 0

@@ -94,6 +94,83 @@ def test_decode_long_keys(gpu_device, G):
     _case(gpu_device, 1, 2 * G, 2, 1, 65536, 128, inputs.BF16, False, seed=40 + G)
 
 
+# -- GQA head packing --------------------------------------------------------
+# With G = Hq / Hkv > 1 query heads per KV head and a query range shorter
+# than a tile, the G ranges are computed as one range of G * Nq rows (row r
+# is head r / Nq, position r % Nq): causal masks take the position, tiles
+# hold rows of several heads, and waves without rows skip the arithmetic.
+# G = 1 (not packed) runs the same shapes through the decode tile alone.
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True, "bottom_right"])
+@pytest.mark.parametrize("G", [1, 7, 8])
+@pytest.mark.parametrize("nq", [1, 4, 16])
+def test_gqa_packed_short_queries(gpu_device, nq, G, causal, D):
+    dtype = inputs.BF16 if D == 128 else inputs.F16
+    x = inputs.make_inputs(2, 2 * G, 2, nq, 1000, D, dtype, seed=nq * 31 + G)
+    o, l = run_gpu(x, None, causal, gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, bool(causal),
+                               causal_offset=1000 - nq if causal == "bottom_right" else 0)
+    compare(o, l, o_ref, l_ref, dtype, rounding_allowance=True,
+            what=f"packed G={G} Nq={nq} D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("nq,G,D", [(50, 7, 64), (100, 8, 128), (33, 3, 96), (60, 4, 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_packed_tiles_cross_heads(gpu_device, nq, G, D, causal):
+    """Packed tiles whose rows span a head boundary (Nq not dividing the
+    tile), ragged keys, forced and planned splits."""
+    dtype = inputs.BF16 if D in (128, 256) else inputs.F16
+    x = inputs.make_inputs(1, 2 * G, 2, nq, 777, D, dtype, seed=nq + G + D)
+    for splits in (0, 3):
+        o, l = run_gpu(x, None, causal, gpu_device, num_splits=splits)
+        o_ref, l_ref = oracle_rows(x, None, causal)
+        compare(o, l, o_ref, l_ref, dtype, rounding_allowance=True,
+                what=f"packed G={G} Nq={nq} D={D} causal={causal} splits={splits}")
+
+
+@pytest.mark.parametrize("nq", [1, 3])
+def test_gqa_packed_strided(gpu_device, nq):
+    """[B, N, H, D] storage viewed as [B, H, N, D]: one row per head packs
+    (the head stride becomes the row stride); three rows per head cannot be
+    re-indexed and run unpacked.  Both must give the same function."""
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd
+    x = inputs.make_inputs(2, 16, 2, nq, 900, 128, inputs.BF16, seed=70 + nq)
+    q, k, v = (to_device(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), inputs.BF16,
+                         gpu_device).transpose(1, 2) for a in (x.q, x.k, x.v))
+    for causal in (False, "bottom_right"):
+        out, lse = attn_fwd(q, k, v, causal=causal)
+        torch.cuda.synchronize(gpu_device)
+        o_ref, l_ref = oracle_rows(x, None, bool(causal),
+                                   causal_offset=900 - nq if causal else 0)
+        compare(out.float().cpu().numpy().astype(np.float64),
+                lse.cpu().numpy().astype(np.float64), o_ref, l_ref, inputs.BF16,
+                rounding_allowance=True, what=f"packed strided Nq={nq} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 80, 96, 128, 256])
+@pytest.mark.parametrize("strided", [False, True])
+def test_many_pieces_merge(gpu_device, D, strided):
+    """Rows cut into more than 16 pieces are merged by a workgroup per row
+    (40 forced pieces over 5000 keys; a few packed GQA rows); strided output
+    rows ([B, N, H, D] storage) take the strided merge."""
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd
+    dtype = inputs.F16 if D == 80 else inputs.BF16
+    x = inputs.make_inputs(2, 6, 2, 3, 5000, D, dtype, seed=500 + D)
+    q, k, v = (to_device(a, dtype, gpu_device) for a in (x.q, x.k, x.v))
+    out = None
+    if strided:
+        out = torch.empty((2, 3, 6, D), dtype=q.dtype, device=gpu_device).transpose(1, 2)
+    o, l = attn_fwd(q, k, v, num_splits=40, out=out)
+    torch.cuda.synchronize(gpu_device)
+    o_ref, l_ref = oracle_rows(x, None, False)
+    compare(o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64),
+            o_ref, l_ref, dtype, rounding_allowance=True,
+            what=f"40 pieces D={D} strided={strided}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forced_splits(gpu_device, splits, causal):
@@ -346,6 +423,17 @@ def test_masks_other_head_dims(gpu_device, D):
     _mask_case(gpu_device, 1, 4, 4, 150, 260, D, inputs.F16, "add", seed=D)
 
 
+@pytest.mark.parametrize("kind,nq,mshape", [
+    ("bool", 4, (2, 8, 4, 300)),     # per-head mask: packs (head stride = Nq rows)
+    ("pad", 1, None),                # key padding [B, 1, 1, Nkv]: packs
+    ("add", 1, (2, 1, 1, 300)),      # one row per head, broadcast over heads: packs
+    ("add", 3, (2, 1, 3, 300)),      # broadcast over heads with 3 rows: not packed
+])
+def test_masks_gqa_short_queries(gpu_device, kind, nq, mshape):
+    _mask_case(gpu_device, 2, 8, 1, nq, 300, 64, inputs.BF16, kind, seed=97 + nq,
+               mshape=mshape)
+
+
 def test_mask_long_rows_sampled(gpu_device):
     """A 2-D boolean mask over 4096 keys, broadcast over batch and heads."""
     _mask_case(gpu_device, 1, 8, 8, 256, 4096, 128, inputs.BF16, "bool", seed=96,
@@ -444,6 +532,46 @@ def test_no_device_allocation_without_split(gpu_device):
     assert torch.cuda.max_memory_allocated() == before
     free0, _ = torch.cuda.mem_get_info()
     assert free0 > 0
+
+
+@pytest.mark.parametrize("name,splits", [("decode-64k", 0), ("dit-17160", 0),
+                                         ("gqa-causal-4096", 0), ("sweep-4096", 4)])
+def test_split_path_memory_is_workspace_only(gpu_device, name, splits):
+    """Peak device memory of a forward beyond its inputs and preallocated
+    outputs: torch's allocator sees nothing, and the stream-ordered pool
+    peaks at the plan's workspace (the split partials, O(rows x D)), far
+    below one fp32 Nq x Nkv score matrix."""
+    import torch
+    from memory_efficient_tiled_amd import attn_fwd, attn_fwd_plan
+    from tests.parity import PoolPeak
+    w = inputs.WORKLOADS[name]
+    dt = 1 if w.dtype == inputs.BF16 else 0
+    plan = attn_fwd_plan(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.causal, dt, splits)
+    ws = plan.workspace_bytes
+    # the workspace is the split rows' fp32 partial outputs and LSE: linear in rows
+    assert ws == plan.num_splits * plan.split_rows * (w.Dv + 1) * 4
+    x = inputs.make_workload_inputs(w, seed=5, sampled_rows=None)
+    q, k, v = (to_device(a, w.dtype, gpu_device) for a in (x.q, x.k, x.v))
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=gpu_device)
+    attn_fwd(q, k, v, causal=w.causal, out=out, lse=lse, num_splits=splits)   # warm the pool
+    torch.cuda.synchronize(gpu_device)
+    pool = PoolPeak(gpu_device.index or 0)
+    torch.cuda.reset_peak_memory_stats(gpu_device)
+    before = torch.cuda.memory_allocated(gpu_device)
+    pool.reset()
+    attn_fwd(q, k, v, causal=w.causal, out=out, lse=lse, num_splits=splits)
+    torch.cuda.synchronize(gpu_device)
+    torch_delta = torch.cuda.max_memory_allocated(gpu_device) - before
+    peak = pool.read()
+    score = 4 * w.B * w.Hq * w.Nq * w.Nkv
+    log(f"  {name}: workspace {ws} B, pool peak {peak} B, torch delta {torch_delta} B, "
+        f"score matrix {score} B")
+    assert torch_delta == 0
+    assert ws > 0 and peak >= ws
+    assert peak <= ws + (2 << 20)          # pool granularity
+    if w.Nq >= 1024:
+        assert peak * 15 < score
 
 
 # -- value rows of another width: (D, Dv) = (192, 128) -----------------------

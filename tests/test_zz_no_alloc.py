@@ -110,3 +110,39 @@ def test_noalloc_rejects_oversized_plan(gpu_device):
     with pytest.raises(binding.AttnError) as ei:
         binding.attn_fwd_noalloc(q, q, q, out, lse, num_splits=16)
     assert ei.value.code == binding.ATTN_ESCRATCH
+
+
+def test_noalloc_graph_replays(gpu_device):
+    """attn_fwd_noalloc captured in a HIP graph (the case it exists for: a
+    capture may not allocate): three replays, with eager work, new query
+    values copied into the captured buffer and a synchronisation between
+    them; every replay equals attn_fwd_split on the same inputs bit for bit.
+    Decode over 20000 keys with 14/2 GQA, so the plan splits and merges."""
+    import torch
+    shape = (1, 14, 2, 1, 20000, 128)
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    x = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, inputs.BF16, seed=11)
+    q, k, v = (to_device(a, inputs.BF16, gpu_device) for a in (x.q, x.k, x.v))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=gpu_device)
+    binding.attn_fwd_noalloc(q, k, v, out, lse)          # first call on the device
+    torch.cuda.synchronize(gpu_device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.attn_fwd_noalloc(q, k, v, out, lse)
+    torch.cuda.synchronize(gpu_device)
+    lib = binding.load_library()
+    for rep in range(3):
+        qn = inputs.make_inputs(B, Hq, Hkv, Nq, Nkv, D, inputs.BF16, seed=100 + rep).q
+        q.copy_(to_device(qn, inputs.BF16, gpu_device))  # eager work between replays
+        torch.cuda.synchronize(gpu_device)
+        g.replay()
+        torch.cuda.synchronize(gpu_device)
+        ref_o, ref_l = torch.full_like(out, 5.0), torch.full_like(lse, 5.0)
+        rc = _launch(lib.attn_fwd_split, q, k, v, ref_o, ref_l, shape, 1.0 / np.sqrt(D), 0,
+                     binding.ATTN_BF16, 0)
+        torch.cuda.synchronize(gpu_device)
+        assert rc == binding.ATTN_OK
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep}"
+        log(f"  graph replay {rep}: equal to the eager split entry point")
