@@ -114,6 +114,7 @@ struct Params {
 struct TileCfg {
   int NW, QB, BN, QL;
   bool SB;
+  bool PD;  // double-buffered pipeline with P V deferred by one step (see the kernel)
   constexpr int BM() const { return NW * QB * 32; }
   constexpr int resident_per_cu() const { return 4 * kWavesPerSimd / NW; }
 };
@@ -132,15 +133,15 @@ enum {
   kCfgD128Masked = 7,
   kCfgD128Decode = 8
 };
-constexpr TileCfg kCfgs[9] = {{4, 1, 64, 0, false},
-                              {4, 2, 32, 0, false},
-                              {8, 1, 64, 0, false},
-                              {8, 2, 32, 3, true},
-                              {8, 1, 32, 8, true},
-                              {4, 1, 64, 0, false},
-                              {8, 1, 64, 4, true},
-                              {8, 1, 64, 4, true},
-                              {4, 1, 64, 0, false}};
+constexpr TileCfg kCfgs[9] = {{4, 1, 64, 0, false, true},
+                              {4, 2, 32, 0, false, false},
+                              {8, 1, 64, 0, false, false},
+                              {8, 2, 32, 3, true, false},
+                              {8, 1, 32, 8, true, false},
+                              {4, 1, 64, 0, false, false},
+                              {8, 1, 64, 4, true, false},
+                              {8, 1, 64, 4, true, false},
+                              {4, 1, 64, 0, false, false}};
 
 // Launch the forward kernels of one pair of head dimensions (Q/K, V/O),
 // defined one pair per translation unit in attn_fwd_d<D>[v<DV>].hip.  The
@@ -205,7 +206,7 @@ using namespace attn_fwd_detail;
 // the matching output columns not stored.  The V and O widths (DV) are
 // handled the same way, independently of D.
 template <int D, int DV, class Tag, bool CAUSAL, int NW, int QB, int BN, int QL, bool SB,
-          bool SPLIT, bool STRIDED, bool MASKED>
+          bool PD, bool SPLIT, bool STRIDED, bool MASKED>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params p) {
   constexpr int DP = compute_dim(D);     // columns of Q K^T and of K's LDS rows
   constexpr int DVP = compute_dim(DV);   // columns of P V and of V's LDS rows
@@ -230,13 +231,14 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   constexpr int ROWBV = DV * 2;          // bytes per V row in memory
   constexpr int DCR = DC - QL;          // Q^T chunks held in registers
   static_assert(QL >= 0 && QL < DC, "at least one Q^T chunk stays in registers");
+  static_assert(!(SB && PD), "the deferred P V step belongs to the double-buffered pipeline");
   using N = Num<Tag>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vbuf0[TILEV];
   __shared__ __attribute__((aligned(1024))) uint16_t kbuf1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vbuf1[TILEV];
-  __shared__ __attribute__((aligned(1024))) uint16_t vbuf2[SB ? TILEV : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf2[SB || PD ? TILEV : 8];
   __shared__ __attribute__((aligned(1024))) u32x4 qlds[QL > 0 ? NW * QB * QL * 64 : 1];
 
   const int tid = threadIdx.x;
@@ -628,7 +630,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   // Single-buffered: one barrier per tile, after which K_{t+1}, V_{t+1}
   // go to kbuf[(t+1) % 2], vbuf[(t+1) % 3].  Double-buffered: one barrier
   // after the first tile's copies, then one per tile, after which K_{t+2}
-  // goes to kbuf[t % 2] and V_{t+1} to vbuf[(t+1) % 2].
+  // goes to kbuf[t % 2] and V_{t+1} to vbuf[(t+1) % 2] (with PD, to
+  // vbuf[(t+1) % 3]).
   auto idle_loop = [&]() {
     if (ntiles <= 0) return;
     issue_k(0, kbuf0);
@@ -652,7 +655,12 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
         __syncthreads();
         if (t + 1 < ntiles) {
           if (t + 2 < ntiles) issue_k(t + 2, (t & 1) ? kbuf1 : kbuf0);
-          issue_v(t + 1, ((t + 1) & 1) ? vbuf1 : vbuf0);
+          if constexpr (PD) {
+            const int v3 = (t + 1) % 3;
+            issue_v(t + 1, v3 == 0 ? vbuf0 : v3 == 1 ? vbuf1 : vbuf2);
+          } else {
+            issue_v(t + 1, ((t + 1) & 1) ? vbuf1 : vbuf0);
+          }
         }
       }
     }
@@ -704,6 +712,72 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
               vbufs(v3 == 2 ? 0 : v3 + 1));
     }
     if (late && ntiles > 0) pv(vbufs((ntiles - 1) % 3), pf);
+  } else if constexpr (PD) {
+    // Double-buffered with P V deferred by one step: after the barrier of
+    // step t the wave issues O += P_{t-1} V_{t-1} and S_{t+1} = K_{t+1} Q^T
+    // on the matrix cores and the softmax of S_t on the vector ALUs, all
+    // independent of one another, so the in-order instruction stream can
+    // interleave them; only the packing of P_t follows the softmax.  V_{t-1}
+    // is still read in step t, so V rotates through three LDS buffers:
+    // K_t in kbuf[t % 2], V_t in vbuf[t % 3], S_t in sa (t even) or sb.
+    if (ntiles > 0) {
+      u32x4 pf[QB * NKC];
+      // kc: K_t (refilled with K_{t+2}); kn: K_{t+1}; vp: V_{t-1}; vn: gets V_{t+1}.
+      // FIRST: t = 0, no P V of a previous tile (a compile-time flag, so that
+      // every later step is one basic block from the barrier to the softmax).
+      auto pd_step = [&](auto last, auto first, int t, f32x16* s, f32x16* sn, uint16_t* kc,
+                         uint16_t* kn, uint16_t* vp, uint16_t* vn) {
+        constexpr bool LAST = decltype(last)::value;
+        constexpr bool FIRST = decltype(first)::value;
+        mask(t, s);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (!LAST) {
+          if (t + 2 < ntiles) issue_k(t + 2, kc);
+          issue_v(t + 1, vn);
+        }
+        if (!FIRST) pv(vp, pf);
+        if (!LAST) qk(kn, sn);
+        float rs[QB];
+        const bool bad = softmax_fast(s, rs);
+        softmax_finish(t, s, rs, bad, pf, nullptr);
+      };
+      auto vbufs = [&](int i) { return i == 0 ? vbuf0 : i == 1 ? vbuf1 : vbuf2; };
+      issue_k(0, kbuf0);
+      issue_v(0, vbuf0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (ntiles > 1) issue_k(1, kbuf1);
+      qk(kbuf0, sa);
+      using First = std::integral_constant<bool, true>;
+      using Next = std::integral_constant<bool, false>;
+      if (ntiles == 1) {
+        pd_step(Last{}, First{}, 0, sa, sb, kbuf0, kbuf1, vbuf2, vbuf1);
+      } else {
+        pd_step(More{}, First{}, 0, sa, sb, kbuf0, kbuf1, vbuf2, vbuf1);
+        int t = 1;
+        for (; t + 6 < ntiles; t += 6) {  // six steps, each with a successor
+          pd_step(More{}, Next{}, t, sb, sa, kbuf1, kbuf0, vbuf0, vbuf2);
+          pd_step(More{}, Next{}, t + 1, sa, sb, kbuf0, kbuf1, vbuf1, vbuf0);
+          pd_step(More{}, Next{}, t + 2, sb, sa, kbuf1, kbuf0, vbuf2, vbuf1);
+          pd_step(More{}, Next{}, t + 3, sa, sb, kbuf0, kbuf1, vbuf0, vbuf2);
+          pd_step(More{}, Next{}, t + 4, sb, sa, kbuf1, kbuf0, vbuf1, vbuf0);
+          pd_step(More{}, Next{}, t + 5, sa, sb, kbuf0, kbuf1, vbuf2, vbuf1);
+        }
+        // t is odd here: K_t in kbuf1, S_t in sb
+        for (; t + 2 < ntiles; t += 2) {
+          pd_step(More{}, Next{}, t, sb, sa, kbuf1, kbuf0, vbufs((t + 2) % 3), vbufs((t + 1) % 3));
+          pd_step(More{}, Next{}, t + 1, sa, sb, kbuf0, kbuf1, vbufs(t % 3), vbufs((t + 2) % 3));
+        }
+        if (t + 1 < ntiles) {
+          pd_step(More{}, Next{}, t, sb, sa, kbuf1, kbuf0, vbufs((t + 2) % 3), vbufs((t + 1) % 3));
+          pd_step(Last{}, Next{}, t + 1, sa, sb, kbuf0, kbuf1, vbufs(t % 3), vbufs((t + 2) % 3));
+        } else {
+          pd_step(Last{}, Next{}, t, sb, sa, kbuf1, kbuf0, vbufs((t + 2) % 3), vbufs((t + 1) % 3));
+        }
+      }
+      pv(vbufs((ntiles - 1) % 3), pf);  // O += P_{last} V_{last}
+    }
   } else if (ntiles > 0) {
     issue_k(0, kbuf0);
     issue_v(0, vbuf0);
@@ -895,15 +969,15 @@ hipError_t launch_main(const Params& p, bool strided, hipStream_t stream) {
   constexpr TileCfg c = kCfgs[CFG];
   if (MASKED)
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, MASKED>),
+        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, c.PD && !MASKED, SPLIT, true, MASKED>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   else if (strided)
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, true, false>),
+        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, c.PD, SPLIT, true, false>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   else
     hipLaunchKernelGGL(
-        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, SPLIT, false, false>),
+        (attn_fwd_kernel<D, DV, Tag, CAUSAL, c.NW, c.QB, c.BN, c.QL, c.SB, c.PD, SPLIT, false, false>),
         dim3(p.total), dim3(c.NW * 64), 0, stream, p);
   return hipGetLastError();
 }
