@@ -149,6 +149,8 @@ def main():
                          "first 7/8 of the keys (timing only: no CPU leg)")
     ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "ffn"), default="fwd",
                     help="time the forward (default) or the gradients")
+    ap.add_argument("--ffn-chunk", type=int, default=None,
+                    help="--pass ffn: token rows per chunk (default: the workload's; 0 = library)")
     ap.add_argument("--graph", action="store_true",
                     help="forward only: capture one step (attn_fwd_noalloc, which allocates "
                          "nothing) in a HIP graph and time its replays, as a serving loop "
@@ -512,10 +514,11 @@ def bench_ffn(args, torch, np):
 
     x, w1, b1, w2, b2 = (up(a) for a in (xi.x, xi.w1, xi.b1, xi.w2, xi.b2))
     y = torch.empty_like(x)
-    ffn_chunked(x, w1, b1, w2, b2, chunk_rows=w.chunk_rows, out=y, verify=True)
+    chunk = w.chunk_rows if args.ffn_chunk is None else args.ffn_chunk
+    ffn_chunked(x, w1, b1, w2, b2, chunk_rows=chunk, out=y, verify=True)
 
     def step():
-        ffn_chunked(x, w1, b1, w2, b2, chunk_rows=w.chunk_rows, out=y)
+        ffn_chunked(x, w1, b1, w2, b2, chunk_rows=chunk, out=y)
 
     for _ in range(args.warmup):
         step()
@@ -540,7 +543,7 @@ def bench_ffn(args, torch, np):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{name}: {w.note}, {w.describe()}", "pass": "ffn",
-                   "N": w.N, "Dm": w.Dm, "F": w.F, "chunk_rows": w.chunk_rows,
+                   "N": w.N, "Dm": w.Dm, "F": w.F, "chunk_rows": chunk,
                    "seed": args.seed, "kernel_source": source_hash("ffn")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),

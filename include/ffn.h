@@ -12,10 +12,13 @@
  * over chunks of `chunk_rows` rows, so that the N x F hidden activation
  * never exists at once: peak extra memory is chunk_rows x F elements plus
  * the matrix-product workspace (128 MiB; each product runs the first of
- * hipBLASLt's candidate algorithms whose stated workspace fits it).  The two products are hipBLASLt GEMMs
- * (fp32 accumulation); bias, GELU and the output bias are this library's
- * kernels.  The hidden activation is rounded to the input type between
- * the products.
+ * hipBLASLt's candidate algorithms whose stated workspace fits it).  The
+ * two products are hipBLASLt GEMMs (fp32 accumulation) with the bias and
+ * GELU (first product) and the output bias (second) applied to the fp32
+ * accumulator in hipBLASLt's epilogue; where hipBLASLt offers no algorithm
+ * with that epilogue for a shape, the plain product is followed by this
+ * library's elementwise kernel.  The hidden activation is rounded to the
+ * input type between the products.
  *
  * Layout: row-major, 16-bit (dtype ATTN_F16 or ATTN_BF16 of attn.h):
  * x [N, Dm], w1 [F, Dm], b1 [F], w2 [Dm, F], b2 [Dm], y [N, Dm]; Dm and F
@@ -38,8 +41,9 @@ extern "C" {
 typedef enum { FFN_GELU_TANH = 0 } ffn_act_t;
 
 /* y = W2 gelu(W1 x + b1) + b2 over chunks of chunk_rows rows (0 = the
- * library's choice: rows whose hidden activation fits 128 MiB, at least
- * 256).  act must be FFN_GELU_TANH.  y must not overlap any input. */
+ * library's choice: rows whose hidden activation fits 96 MiB, rounded down
+ * to a multiple of 1024, at least 1024).  act must be FFN_GELU_TANH.  y
+ * must not overlap any input. */
 int ffn_chunked(const void* x, const void* w1, const void* b1, const void* w2,
                 const void* b2, void* y, int N, int Dm, int F, int act,
                 int chunk_rows, int dtype, void* stream);

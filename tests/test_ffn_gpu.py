@@ -86,17 +86,18 @@ def test_ffn_video_width_sampled(gpu_device):
     _run(gpu_device, 4100, 1536, 8960, inputs.BF16, 1000, seed=9, rows=rows, verify=True)
 
 
-def test_ffn_verify_14b_width_default_chunk(gpu_device):
-    """Model width 5120, hidden 13824 (the 14B video DiT's block), 10000 rows
-    with the default chunk (4864 rows at this hidden width): the check
-    evaluates the first 2 * 4864 + 1 = 9729 rows as one chunk, the product
-    shape whose GEMM workspace selection is fixed (a candidate is taken
-    only if its stated workspace fits the buffer).  Output finite, 48
-    sampled rows (chunk edges included) against the oracle."""
+@pytest.mark.parametrize("chunk", [4864, 0])
+def test_ffn_verify_14b_width(gpu_device, chunk):
+    """Model width 5120, hidden 13824 (the 14B video DiT's block), 10000 rows.
+    With 4864-row chunks the check evaluates the first 2 * 4864 + 1 = 9729
+    rows as one chunk, the product shape whose GEMM workspace selection is
+    fixed (a candidate is taken only if its stated workspace fits the
+    buffer); 0 takes the library's chunk (3072 rows at this width).  Output
+    finite, 48 sampled rows (chunk edges included) against the oracle."""
     N, Dm, F = 10000, 5120, 13824
-    rows = np.unique(np.concatenate([[0, 4863, 4864, 9727, 9728, 9729, 9999],
-                                     np.random.default_rng(10).choice(N, 41, replace=False)]))
-    _run(gpu_device, N, Dm, F, inputs.BF16, 0, seed=10, rows=rows, verify=True)
+    rows = np.unique(np.concatenate([[0, 3071, 3072, 4863, 4864, 9727, 9728, 9729, 9999],
+                                     np.random.default_rng(10).choice(N, 39, replace=False)]))
+    _run(gpu_device, N, Dm, F, inputs.BF16, chunk, seed=10, rows=rows, verify=True)
 
 
 def test_ffn_verify_rejects_nan(gpu_device):
