@@ -845,7 +845,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* out, const 
   const size_t rows_bytes = (rows * sizeof(float) + 255) / 256 * 256;
   const size_t part = hsplit > 1 ? (size_t)hsplit * B * Hkv * Nkv * D * sizeof(float) : 0;
   const size_t partv = hsplit > 1 ? (size_t)hsplit * B * Hkv * Nkv * Dv * sizeof(float) : 0;
-  hipError_t e = hipMallocAsync(&ws, 2 * rows_bytes + part + partv, st);
+  hipError_t e = attn_host::workspace_alloc(&ws, 2 * rows_bytes + part + partv, st);
   if (e != hipSuccess || !ws) {
     attn_host::set_last_hip_error((int)e);
     (void)hipGetLastError();

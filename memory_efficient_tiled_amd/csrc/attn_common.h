@@ -229,6 +229,12 @@ namespace attn_host {
 int check_device(int* cus);
 // Records the hipError_t behind an ATTN_EHIP / ATTN_ENOMEM return.
 void set_last_hip_error(int e);
+// Stream-ordered workspace (hipMallocAsync on `st`).  With the environment
+// variable ATTN_FAIL_WORKSPACE set to 1 the request fails with
+// hipErrorOutOfMemory without allocating: failure injection for tests of
+// the ATTN_ENOMEM paths (read at every call; nothing has been launched
+// when a workspace request fails).
+hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t st);
 // How a call on the D = 128 narrow tiles (256 query rows, 64-key tiles)
 // covers its query tiles: tiles [0, first_split) whole, the rest cut into
 // `splits` key ranges of split_len keys whose rows [row0, rows) are merged.

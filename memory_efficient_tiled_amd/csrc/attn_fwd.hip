@@ -5,6 +5,8 @@
 
 #include "attn_fwd_kernel.h"
 
+#include <stdlib.h>
+
 #include <algorithm>
 #include <mutex>
 
@@ -473,7 +475,7 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
       p.lsepart = p.opart + (size_t)pl.splits * p.prows * Dv;
     }
   } else if (split_wgs > 0) {
-    hipError_t e = hipMallocAsync(&ws, pl.workspace_bytes(), stream);
+    hipError_t e = attn_host::workspace_alloc(&ws, pl.workspace_bytes(), stream);
     if (e != hipSuccess || !ws) {
       g_last_hip_error = (int)e;
       (void)hipGetLastError();
@@ -528,6 +530,14 @@ int check_device(int* cus) {
   return rc;
 }
 void set_last_hip_error(int e) { g_last_hip_error = e; }
+hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t st) {
+  const char* f = getenv("ATTN_FAIL_WORKSPACE");
+  if (f && f[0] == '1' && f[1] == '\0') {
+    *p = nullptr;
+    return hipErrorOutOfMemory;
+  }
+  return hipMallocAsync(p, bytes, st);
+}
 void narrow_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int cus,
                  NarrowPlan* out) {
   // the masked plan always takes the narrow tile of its head dimension

@@ -431,7 +431,7 @@ int run_fp8(const void* q, const void* k, const void* v, void* out, float* lse, 
   const size_t part_bytes =
       split_wgs > 0 ? (size_t)pl.splits * (size_t)(pl.rows - pl.row0) * (D + 1) * sizeof(float) : 0;
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, vt_bytes + part_bytes, st);
+  hipError_t e = attn_host::workspace_alloc(&ws, vt_bytes + part_bytes, st);
   if (e != hipSuccess || !ws) {
     attn_host::set_last_hip_error((int)e);
     (void)hipGetLastError();

@@ -326,7 +326,7 @@ int ffn_chunked(const void* x, const void* w1, const void* b1, const void* w2, c
   hipStream_t st = (hipStream_t)stream;
   const int chunk = chunk_rows > 0 ? (chunk_rows < N ? chunk_rows : N) : default_chunk(N, F);
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, hidden_bytes(chunk, F) + kGemmWorkspace, st);
+  hipError_t e = attn_host::workspace_alloc(&ws, hidden_bytes(chunk, F) + kGemmWorkspace, st);
   if (e != hipSuccess || !ws) {
     attn_host::set_last_hip_error((int)e);
     (void)hipGetLastError();
@@ -360,7 +360,7 @@ int ffn_verify(const void* x, const void* w1, const void* b1, const void* w2, co
   constexpr int kParts = 256;
   const size_t wsb = hidden_bytes(R, F) + kGemmWorkspace;  // enough for either chunking
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, wsb + 2 * yb + (2 * kParts + 2) * sizeof(float), st);
+  hipError_t e = attn_host::workspace_alloc(&ws, wsb + 2 * yb + (2 * kParts + 2) * sizeof(float), st);
   if (e != hipSuccess || !ws) {
     attn_host::set_last_hip_error((int)e);
     (void)hipGetLastError();

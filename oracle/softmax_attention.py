@@ -175,6 +175,74 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return o, lse
 
 
+def attention_two_pass(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                       causal: bool, rows: np.ndarray | None = None,
+                       row_block: int = 256, key_block: int = 4096,
+                       causal_offset: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """The same definition as :func:`attention`, streamed over key blocks in
+    two passes so that no row's full score vector is held: for each block
+    of query rows, pass 1 walks the key blocks for the exact row maximum
+    m_i; pass 2 walks them again accumulating l_i = sum_j exp(s_ij - m_i)
+    and sum_j exp(s_ij - m_i) v_j with m_i fixed; then o_i is the second
+    sum over l_i and lse_i = m_i + ln l_i.  This is the plain
+    max-subtraction of the definition done block by block (the ai-manual.ru
+    article's chunked snippet, section 3, subtracts the maximum the same
+    way), deliberately not the running-max rescaling the kernels use.
+    Memory is O(row_block * key_block + row_block * Dv); the scores are
+    computed twice.  Arguments and results as for :func:`attention`
+    (no bias).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    if v.shape[:3] != k.shape[:3] or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch between q, k and v")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if rows is None:
+        rows_h = np.tile(np.arange(Nq, dtype=np.int64), (Hq, 1))
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        rows_h = np.tile(rows, (Hq, 1)) if rows.ndim == 1 else rows
+    R = rows_h.shape[1]
+    o = np.empty((B, Hq, R, Dv))
+    lse = np.empty((B, Hq, R))
+
+    def scores(qr, kk, ri, j0):
+        s = scale * (qr @ kk[j0:j0 + key_block].T)
+        if causal:
+            j = np.arange(j0, j0 + s.shape[1], dtype=np.int64)
+            s = np.where(j[None, :] <= ri[:, None] + causal_offset, s, -np.inf)
+        return s
+
+    for b in range(B):
+        for hq in range(Hq):
+            kk = k[b, hq // G]
+            vv = v[b, hq // G]
+            for r0 in range(0, R, row_block):
+                ri = rows_h[hq, r0:r0 + row_block]
+                qr = q[b, hq, ri]
+                m = np.full(len(ri), -np.inf)
+                for j0 in range(0, Nkv, key_block):          # pass 1: the row maxima
+                    m = np.maximum(m, scores(qr, kk, ri, j0).max(axis=1))
+                empty = ~np.isfinite(m)                        # rows with no allowed key
+                mz = np.where(empty, 0.0, m)
+                l_sum = np.zeros(len(ri))
+                acc = np.zeros((len(ri), Dv))
+                for j0 in range(0, Nkv, key_block):          # pass 2: sums against m
+                    e = np.exp(scores(qr, kk, ri, j0) - mz[:, None])
+                    l_sum += e.sum(axis=1)
+                    acc += e @ vv[j0:j0 + key_block]
+                den = np.where(empty, 1.0, l_sum)
+                o[b, hq, r0:r0 + len(ri)] = acc / den[:, None]
+                lse[b, hq, r0:r0 + len(ri)] = np.where(empty, -np.inf, mz + np.log(den))
+    return o, lse
+
+
 def attention_from_storage(q, k, v, dtype: str, scale: float | None,
                            causal: bool, rows=None):
     """Decode 16-bit storage arrays, then evaluate :func:`attention`."""

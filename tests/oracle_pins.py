@@ -220,6 +220,30 @@ def pin_dominant_key(attn):
     _close(lse[0, 0, 0], 144.0, what="dominant key lse")
 
 
+def pin_extreme_scores(attn):
+    """Scores spread over thousands of natural-log units (exp of most of them
+    over- or underflows float64): softmax is still defined and picks the
+    largest, so o_i = v_j* and lse_i = s_ij* to rounding, whichever key
+    position holds the maximum (first, middle or last of 40 keys), causal
+    or not; only a true row maximum keeps every exponent finite."""
+    rng = _rng(18)
+    Nkv, D = 40, 4
+    v = rng.standard_normal((1, 1, Nkv, D))
+    for js in (0, 17, Nkv - 1):
+        s = np.linspace(-3000.0, 2000.0, Nkv)          # distinct scores, gaps > 100
+        s[[js, Nkv - 1]] = s[[Nkv - 1, js]]             # the maximum at key js
+        k = np.zeros((1, 1, Nkv, D))
+        k[0, 0, :, 0] = s
+        q = np.zeros((1, 1, 1, D))
+        q[0, 0, 0, 0] = 1.0
+        for causal in (False, True):
+            qq = q if not causal else np.repeat(q, Nkv, axis=2)
+            o, lse = attn(qq, k, v, 1.0, causal)
+            i = Nkv - 1 if causal else 0                 # the last row sees every key
+            _close(o[0, 0, i], v[0, 0, js], tol=1e-12, what=f"extreme scores o (j*={js})")
+            _close(lse[0, 0, i], 2000.0, tol=1e-12, what=f"extreme scores lse (j*={js})")
+
+
 # ---------------------------------------------------------------------------
 # 5. Invariants.
 # ---------------------------------------------------------------------------
@@ -469,7 +493,8 @@ def pin_value_width_columns(attn):
 
 
 ALL_PINS = [pin_bruteforce, pin_torch_sdpa, pin_golden, pin_q_zero, pin_v_const,
-            pin_causal_row0, pin_single_key, pin_dominant_key, pin_key_shift,
+            pin_causal_row0, pin_single_key, pin_dominant_key, pin_extreme_scores,
+            pin_key_shift,
             pin_kv_permutation, pin_query_permutation, pin_gqa_repeat,
             pin_linear_in_v, pin_convex_hull, pin_rows_subset,
             pin_causal_offset_torch, pin_causal_offset_shift, pin_mask_torch,

@@ -230,3 +230,69 @@ def test_workload_table():
     # the 26 GB quoted for 17K tokens and >500 GB for 75K tokens
     assert abs(24 * 17160 ** 2 * 4 / 2 ** 30 - 26.3) < 0.1
     assert 24 * 75600 ** 2 * 4 > 500e9
+
+
+# -- the streaming two-pass mode (the CPU baseline's oracle) -------------------
+# It computes the same definition block by block; every pin that takes no
+# attention mask applies to it directly (with tiny blocks, so that rows and
+# keys span several of them), it must equal the materialised mode to
+# 1e-12 on the cross-check shapes, and planted mistakes must be caught.
+
+_TWO_PASS_PINS = [p for p in oracle_pins.ALL_PINS
+                  if p not in (oracle_pins.pin_mask_torch, oracle_pins.pin_mask_bias_shift)]
+
+
+def _two_pass_small_blocks(fn):
+    def attn(q, k, v, scale, causal, **kw):
+        return fn(q, k, v, scale, causal, row_block=2, key_block=3, **kw)
+    return attn
+
+
+@pytest.mark.parametrize("pin", _TWO_PASS_PINS, ids=lambda p: p.__name__)
+def test_two_pass_pin(pin):
+    pin(_two_pass_small_blocks(oracle.attention_two_pass))
+
+
+@pytest.mark.parametrize("G", [1, 7])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 256, 1000, 2048])
+def test_two_pass_equals_materialised(n, causal, G):
+    rng = np.random.default_rng(n + 7 * G + causal)
+    q = rng.standard_normal((1, G, n, 16))
+    k = rng.standard_normal((1, 1, n, 16))
+    v = rng.standard_normal((1, 1, n, 16))
+    o1, l1 = oracle.attention(q, k, v, 0.25, causal)
+    o2, l2 = oracle.attention_two_pass(q, k, v, 0.25, causal, row_block=100, key_block=300)
+    assert np.max(np.abs(o1 - o2) / (np.abs(o1) + 1e-3)) <= 1e-12
+    assert np.max(np.abs(l1 - l2) / (np.abs(l1) + 1.0)) <= 1e-12
+
+
+TWO_PASS_MUTANTS = [
+    ("second pass without the row maximum", "e = np.exp(scores(qr, kk, ri, j0) - mz[:, None])",
+     "e = np.exp(scores(qr, kk, ri, j0))"),
+    ("maximum of the first key block only", "m = np.maximum(m, scores(qr, kk, ri, j0).max(axis=1))",
+     "m = np.maximum(m, scores(qr, kk, ri, 0).max(axis=1))"),
+    ("key block offset dropped in the causal test", "j = np.arange(j0, j0 + s.shape[1], dtype=np.int64)",
+     "j = np.arange(0, s.shape[1], dtype=np.int64)"),
+    ("values of the first key block", "acc += e @ vv[j0:j0 + key_block]",
+     "acc += e @ vv[0:key_block]"),
+    ("lse without the maximum", "mz + np.log(den)", "np.log(den)"),
+]
+
+
+@pytest.mark.parametrize("name,original,replacement", TWO_PASS_MUTANTS,
+                         ids=[m[0] for m in TWO_PASS_MUTANTS])
+def test_two_pass_pins_catch_planted_mistake(name, original, replacement):
+    src = inspect.getsource(oracle_mod)
+    assert original in src, f"mutation anchor not found: {original!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(original, replacement), "<oracle mutant>", "exec"), mod.__dict__)
+    attn = _two_pass_small_blocks(mod.attention_two_pass)
+    caught = []
+    for pin in _TWO_PASS_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(attn)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake: {name}"
