@@ -135,25 +135,46 @@ def gather_rows(a, rows):
                      for b in range(B)])
 
 
+def _e4m3_units(b: np.ndarray) -> np.ndarray:
+    """2^e(x) of E4M3 bytes, e the exponent field minus 7 (field 0 counts as
+    1); 0 for the two zero patterns."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    e = (b >> 3) & 15
+    unit = np.exp2(np.where(e == 0, 1, e) - 7.0)
+    return np.where((b & 0x7F) == 0, 0.0, unit)
+
+
 def fp8_bounds(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
     """Per-element error bound of the FP8 forward against the oracle, and a
     per-row LSE bound, on rows [Hq, R] (all rows when None).
 
-    Derivation: the kernel rounds each probability P_ij (relative to its
-    running reference max, so P_ij >= exp(s_ij - max_j s_ij)) to E4M3: an
-    error of at most 2^-4 P_ij (normal numbers, 3 mantissa bits) or 2^-10
-    (subnormals, below 2^-6).  Divided by the row sum l_i, the error on
-    the normalised weight p_ij is at most 2^-4 p_ij + 2^-10 / L_i, with
-    L_i = sum_j exp(s_ij - max s) >= 1.  The roundings are independent and
-    uniform, so o_id is off by a sum with standard deviation
-    sigma_id = sqrt(sum_j (2^-4 p_ij + 2^-10 / L_i)^2 v_jd^2 / 3); the bound
-    is 6 sigma plus half an ulp of the output type plus the score error of
-    the 8-bit matrix instruction, whose accumulation is coarser than fp32
-    (measured: about 2^-14.6 of the largest partial sum); it is bounded
-    by dS_ij = 2^-12 sum_d |q_id k_jd| scale q_descale k_descale, moving
-    o_id by at most max_j dS_ij sum_j p_ij (|v_jd| + |o_id|) and the
-    log-sum-exp by max_j dS_ij.  Returns (bound [B,Hq,R,D], mean bound
-    [B,Hq,R,D], lse bound [B,Hq,R]) for the output dtype ``out_dtype``.
+    Both products run on the 8-bit matrix instruction, whose accumulation
+    tests/test_mma_fp8_gpu.py pins: per instruction, |D - (C + sum_k a_k b_k)|
+    <= 7 * 2^-13 sum_g 2^E_g + 2^-19 max(|C|, 2^(max_g E_g + 1)), with eight
+    groups of eight products and E_g the largest e(a_k) + e(b_k) of a group
+    (e: exponent field minus 7).  Since 2^E_g <= sum over the group of
+    2^(e(a_k) + e(b_k)), and |C| <= 4 sum_k 2^(e(a_k) + e(b_k)) for the second
+    of the two chained score instructions (D = 128), the raw score error is
+    at most 2^-10 U_ij with U_ij = sum_d 2^(e(q_id) + e(k_jd)):
+    dS_ij = 2^-10 U_ij scale q_descale k_descale.  It moves o_id by at most
+    max_j dS_ij sum_j p_ij (|v_jd| + |o_id|) and the log-sum-exp by
+    max_j dS_ij.
+
+    P V: the kernel rounds each probability P_ij (relative to its running
+    reference max, so P_ij >= exp(s_ij - max_j s_ij) and the row sum
+    l_i >= L_i = sum_j exp(s_ij - max s) >= 1) to E4M3: an error of at most
+    2^-4 P_ij (normal numbers, 3 mantissa bits) or 2^-10 (subnormals, below
+    2^-6), i.e. 2^-4 p_ij + 2^-10 / L_i on the normalised weight p_ij.  The
+    roundings are independent and uniform, so o_id is off by a sum with
+    standard deviation sigma_id = sqrt(sum_j (2^-4 p_ij + 2^-10 / L_i)^2
+    v_jd^2 / 3), bounded by 6 sigma.  The instruction's own error on
+    V^T P^T adds, in normalised units, 2^-10 sum_j max(1.0625 p_ij, 2^-6 / L_i)
+    2^e(v_jd) v_descale (2^e of a rounded probability is at most
+    1.0625 P_ij, or 2^-6 for a subnormal) plus 2^-19 per key tile on the
+    running accumulator, at most 2^-18 n_tiles sum_j p_ij |v_jd|.  The bound
+    is the sum of these terms; half an ulp of the output type is added by
+    the caller.  Returns (bound [B,Hq,R,D], mean bound [B,Hq,R,D], lse bound
+    [B,Hq,R]).
     """
     q8, k8, v8 = x.q, x.k, x.v
     B, Hq, Nq, D = q8.shape
@@ -162,6 +183,7 @@ def fp8_bounds(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
     sc = oracle.scale_value(scale, D)
     cn = sc * x.q_descale * x.k_descale
     dec = oracle.decode_fp8_e4m3
+    n_tiles = (Nkv + 63) // 64 + 1
     R = Nq if rows is None else rows.shape[1]
     bound = np.empty((B, Hq, R, D))
     mbound = np.empty((B, Hq, R, D))
@@ -170,13 +192,15 @@ def fp8_bounds(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
     for b in range(B):
         for hk in range(Hkv):
             kk = dec(k8[b, hk])
+            uk = _e4m3_units(k8[b, hk])
             vv = dec(v8[b, hk]) * x.v_descale
+            uv = _e4m3_units(v8[b, hk]) * x.v_descale
             for g in range(G):
                 h = hk * G + g
                 ri = np.arange(Nq) if rows is None else rows[h]
                 qq = dec(q8[b, h, ri])
                 s = cn * (qq @ kk.T)
-                ds = 2.0 ** -12 * cn * (np.abs(qq) @ np.abs(kk).T)
+                ds = 2.0 ** -10 * cn * (_e4m3_units(q8[b, h, ri]) @ uk.T)
                 if causal:
                     allowed = keys[None, :] <= ri[:, None] + causal_offset
                     s = np.where(allowed, s, -np.inf)
@@ -189,10 +213,13 @@ def fp8_bounds(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
                 w = 2.0 ** -4 * p + 2.0 ** -10 / L * (p > 0)
                 sigma = np.sqrt((w ** 2) @ (vv ** 2) / 3.0)
                 o = p @ vv
+                pabs_v = p @ np.abs(vv)
                 dsm = ds.max(axis=1, keepdims=True)
-                sterm = dsm * (p @ np.abs(vv) + np.abs(o))
-                bound[b, h] = 6.0 * sigma + sterm
-                mbound[b, h] = 2.0 * sigma + sterm
+                sterm = dsm * (pabs_v + np.abs(o))
+                pu = np.where(p > 0, np.maximum(1.0625 * p, 2.0 ** -6 / L), 0.0)
+                pvterm = 2.0 ** -10 * (pu @ uv) + 2.0 ** -18 * n_tiles * pabs_v
+                bound[b, h] = 6.0 * sigma + sterm + pvterm
+                mbound[b, h] = 2.0 * sigma + sterm + pvterm
                 lbound[b, h] = dsm[:, 0]
     return bound, mbound, lbound
 

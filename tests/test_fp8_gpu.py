@@ -4,9 +4,10 @@ Inputs are Gaussian tensors quantised per tensor to E4M3 (inputs.py); the
 oracle evaluates exact attention on the decoded values times their descale
 factors (oracle.attention_fp8).  The outputs are compared element by
 element against the bound derived in tests/parity.py (fp8_bounds: the
-rounding of the probabilities to E4M3 for P V, and the coarser score
-accumulation of the 8-bit matrix instruction) plus half an ulp of the
-output type; the log-sum-exp within 1e-3 plus the score-error term.
+rounding of the probabilities to E4M3 for P V, and the accumulation of the
+8-bit matrix instruction in both products, pinned on the instruction alone
+in tests/test_mma_fp8_gpu.py) plus half an ulp of the output type; the
+log-sum-exp within 1e-3 plus the score-error term.
 """
 import numpy as np
 import pytest
