@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include "attn.h"
+#include "attn_tiles.h"
 
 namespace {
 
@@ -209,9 +210,7 @@ __device__ __forceinline__ int v_swz(int r) {
 // Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9.
 constexpr int kRawBufferFlags = 0x00020000;
 
-// Waves per SIMD that every kernel is compiled for: each wave may use up to
-// 256 of the SIMD's 512 vector registers (arch + accumulation).
-constexpr int kWavesPerSimd = 2;
+using attn_tiles::kWavesPerSimd;
 
 // Copy 16 bytes per lane from a buffer into LDS: lane i writes lds + 16 i
 // (lds wave-uniform).  Offsets at or beyond the buffer's size read zero.

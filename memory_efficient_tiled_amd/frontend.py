@@ -25,8 +25,13 @@ it can serve go to the memory-efficient path, the rest to PyTorch.  Here:
   call without a graph break and autograd uses the library's gradient
   kernels (``binding.attn_bwd``), which need contiguous tensors: strided
   inputs are copied once, in the backward only.
-* ``available()`` is the backend probe: the library is built and the device
-  is a gfx950; calls on other devices are reported as unsupported.
+* ``available()``: the library is built and the device is a gfx950; calls on
+  other devices are reported as unsupported.
+* ``auto_patch()`` is the start-up rule of the same post's section "From
+  gfx906 to a broader release": probe whether PyTorch itself has a fused
+  SDPA kernel (flash or memory-efficient) for the device
+  (``efficient_backend_available``); if it has, stay out of the way,
+  otherwise patch.
 
 Only argument checks and marshalling happen here; the computation is the
 HIP library's (``binding.attn_fwd`` / ``binding.attn_bwd``), which raises if
@@ -279,6 +284,54 @@ def patch(fallback: bool = False):
         _original = F.scaled_dot_product_attention
     _fallback = bool(fallback)
     F.scaled_dot_product_attention = _patched
+
+
+def efficient_backend_available(device=None) -> bool:
+    """Whether PyTorch has a fused SDPA kernel (flash or memory-efficient)
+    for ``device`` (default: the current GPU): one small fp16 call to
+    PyTorch's own function, restricted to those two backends, which raises
+    when neither can run it.  PyTorch's global switches
+    (``torch.backends.cuda.enable_flash_sdp`` / ``enable_mem_efficient_sdp``)
+    are honoured, so a backend switched off counts as absent."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    if not torch.cuda.is_available():
+        return False
+    dev = torch.device("cuda", device) if isinstance(device, int) else \
+        torch.device(device or "cuda")
+    # sdpa_kernel() enables what it lists, so list only what is switched on
+    backends = ([SDPBackend.FLASH_ATTENTION] if torch.backends.cuda.flash_sdp_enabled()
+                else []) + ([SDPBackend.EFFICIENT_ATTENTION]
+                            if torch.backends.cuda.mem_efficient_sdp_enabled() else [])
+    if not backends:
+        return False
+    fn = _original if _original is not None else F.scaled_dot_product_attention
+    q = torch.zeros((1, 2, 16, 64), dtype=torch.float16, device=dev)
+    try:
+        with sdpa_kernel(backends):
+            fn(q, q, q)
+    except RuntimeError:
+        return False
+    return True
+
+
+def auto_patch(fallback: bool = True, device=None) -> bool:
+    """Patch only where PyTorch lacks a fused SDPA kernel.
+
+    At start-up: when PyTorch has a flash or memory-efficient kernel for the
+    device, SDPA is left alone; when it has not (only the math path, which
+    builds the full score matrix) and this library can run there (a
+    gfx950), ``patch(fallback)`` is applied.  Returns whether SDPA is now
+    patched.  A missing build raises, as in ``patch``.
+    """
+    binding.load_library()
+    if not available(device):
+        return False
+    if efficient_backend_available(device):
+        return False
+    patch(fallback=fallback)
+    return True
 
 
 def unpatch():

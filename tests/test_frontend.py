@@ -201,6 +201,27 @@ def test_custom_op_fake_shapes():
 
 def test_backend_probe_without_gpu():
     assert mta.available() is False
+    assert mta.efficient_backend_available() is False
+
+
+@pytest.mark.parametrize("usable,fused,patched", [(False, False, False), (False, True, False),
+                                                 (True, True, False), (True, False, True)])
+def test_auto_patch_rule(monkeypatch, usable, fused, patched):
+    """Patched exactly when the library can run on the device and PyTorch has
+    no fused SDPA kernel there; calls it cannot serve then fall back."""
+    from memory_efficient_tiled_amd import frontend
+    orig = F.scaled_dot_product_attention
+    monkeypatch.setattr(frontend, "available", lambda device=None: usable)
+    monkeypatch.setattr(frontend, "efficient_backend_available", lambda device=None: fused)
+    try:
+        assert frontend.auto_patch() is patched
+        assert (F.scaled_dot_product_attention is not orig) is patched
+        if patched:
+            q = torch.randn(1, 2, 10, 64)       # CPU tensors: handed to PyTorch
+            assert torch.equal(F.scaled_dot_product_attention(q, q, q), orig(q, q, q))
+    finally:
+        mta.unpatch()
+    assert F.scaled_dot_product_attention is orig
 
 
 def test_value_head_dimension():

@@ -138,6 +138,43 @@ def test_patched_torch_sdpa(gpu_device):
         mta.unpatch()
 
 
+def test_auto_patch_follows_the_backend_probe(gpu_device):
+    """With PyTorch's flash and memory-efficient kernels switched off, the
+    probe finds no fused backend and auto_patch routes SDPA here; with them
+    on, it patches exactly when the probe still finds none."""
+    import torch
+    import torch.nn.functional as F
+    import memory_efficient_tiled_amd as mta
+    orig = F.scaled_dot_product_attention
+    flash, eff = (torch.backends.cuda.flash_sdp_enabled(),
+                  torch.backends.cuda.mem_efficient_sdp_enabled())
+    x = inputs.make_inputs(1, 2, 2, 70, 70, 64, inputs.F16, seed=29)
+    q, k, v = (to_device(a, inputs.F16, gpu_device) for a in (x.q, x.k, x.v))
+    try:
+        torch.backends.cuda.enable_flash_sdp(False)
+        torch.backends.cuda.enable_mem_efficient_sdp(False)
+        assert mta.efficient_backend_available(gpu_device) is False
+        assert mta.auto_patch(device=gpu_device) is True
+        s0 = mta.sdpa_stats()["native"]
+        o = F.scaled_dot_product_attention(q, k, v)
+        torch.cuda.synchronize(gpu_device)
+        assert mta.sdpa_stats()["native"] == s0 + 1
+        compare(o.float().cpu().numpy().astype(np.float64), None, _oracle_out(x, False),
+                None, inputs.F16, rounding_allowance=True, what="auto-patched sdpa")
+        mta.unpatch()
+        torch.backends.cuda.enable_flash_sdp(True)
+        torch.backends.cuda.enable_mem_efficient_sdp(True)
+        fused = mta.efficient_backend_available(gpu_device)
+        log(f"  PyTorch fused SDPA kernel on this device: {fused}")
+        assert mta.auto_patch(device=gpu_device) is (not fused)
+        assert (F.scaled_dot_product_attention is not orig) is (not fused)
+    finally:
+        mta.unpatch()
+        torch.backends.cuda.enable_flash_sdp(flash)
+        torch.backends.cuda.enable_mem_efficient_sdp(eff)
+    assert F.scaled_dot_product_attention is orig
+
+
 def test_sdpa_causal_lower_right_bias(gpu_device):
     """PyTorch's lower-right causal bias as attn_mask: bottom-right alignment
     in the forward and under autograd."""
