@@ -206,13 +206,16 @@ __global__ __launch_bounds__(kNW8 * 64, kWavesPerSimd) void attn_fwd_fp8_kernel(
   };
 
   auto probs = [&](f32x16* s, float mb) {
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[4];   // started from their first terms (an add of 0 is not folded)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         s[kb][e] = fast_exp2(fmaf(s[kb][e], p.c, -mb));
-        rs[e & 3] += s[kb][e];
+        if (kb == 0 && e < 4)
+          rs[e] = s[kb][e];
+        else
+          rs[e & 3] += s[kb][e];
       }
     return (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };

@@ -438,14 +438,19 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
 
   // Scores of query block qb of one tile -> probabilities against reference
   // max mb, in place; returns the lane-partial row sum.
+  // (The four partial sums start from their first terms: an add of 0 is
+  // not folded away, since 0 + -0 is +0.)
   auto probs = [&](f32x16* s, int qb, float mb) {
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[4];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         s[qb * NKB + kb][e] = fast_exp2(fmaf(s[qb * NKB + kb][e], p.c, -mb));
-        rs[e & 3] += s[qb * NKB + kb][e];
+        if (kb == 0 && e < 4)
+          rs[e] = s[qb * NKB + kb][e];
+        else
+          rs[e & 3] += s[qb * NKB + kb][e];
       }
     return (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
