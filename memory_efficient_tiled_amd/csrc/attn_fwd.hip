@@ -201,19 +201,22 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     return launch_fwd(D, Dv, p, pl.cfg, cz, split, strided, masked, bf16, stream);
   };
 
+  // Whole tiles and the pieces of the remaining tiles run in one launch,
+  // whole tiles first: the pieces take the slots of the tiles that finish
+  // first instead of waiting for the last one.  Then the merge.
   hipError_t e = hipSuccess;
-  if (pl.first_split > 0) {  // whole tiles
+  p.n_whole = 0;
+  if (split_wgs > 0) {
+    if (pl.first_split + split_wgs > INT32_MAX) return ATTN_EINVAL;
+    p.n_whole = (int)pl.first_split;
+    p.total = (int)(pl.first_split + split_wgs);
+    p.tile0 = (int)pl.first_split;
+    e = launch(true);
+    if (e == hipSuccess) e = launch_combine(Dv, p, strided, bf16, stream);
+  } else if (pl.first_split > 0) {
     p.total = (int)pl.first_split;
     p.tile0 = 0;
     e = launch(false);
-  }
-  if (e == hipSuccess && split_wgs > 0) {  // pieces of the remaining tiles, then the merge
-    p.total = (int)split_wgs;
-    p.tile0 = (int)pl.first_split;
-    e = launch(true);
-    if (e == hipSuccess) {
-      e = launch_combine(Dv, p, strided, bf16, stream);
-    }
   }
   if (ws) {
     hipError_t ef = hipFreeAsync(ws, stream);

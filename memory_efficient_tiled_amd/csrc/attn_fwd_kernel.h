@@ -72,7 +72,10 @@ struct Params {
   int Hq, Nq, Nkv, G, Hkv;
   int n_qtiles, n_splits, split_len;
   int total;          // workgroups of this launch
-  int tile0;          // first query tile of this launch
+  int tile0;          // first query tile of this launch's pieces (split) or tiles
+  int n_whole;        // split launches: the first n_whole workgroups are whole
+                      // tiles 0 .. n_whole - 1 (then come the pieces of tiles
+                      // tile0 ..); 0 for a launch of pieces only
   int row0, prows;    // split: output rows [row0, row0 + prows) have partials
   float c;            // |scale| * log2(e)
   uint32_t qsign;     // 0x80008000 flips the sign of Q (negative scale)
@@ -199,13 +202,20 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  int bid = xcd_remap(blockIdx.x, p.total);
-  int sp = 0;
-  if (SPLIT) {
+  // A split launch may start with whole tiles, so that its pieces take the
+  // slots those tiles free (each part renumbered over its own range).
+  int bid, sp = 0;
+  bool piece = SPLIT;
+  if (SPLIT && (int)blockIdx.x < p.n_whole) {
+    piece = false;
+    bid = xcd_remap(blockIdx.x, p.n_whole);
+  } else if (SPLIT) {
+    bid = xcd_remap(blockIdx.x - p.n_whole, p.total - p.n_whole);
     sp = bid % p.n_splits;
-    bid /= p.n_splits;
+    bid = bid / p.n_splits + p.tile0;
+  } else {
+    bid = xcd_remap(blockIdx.x, p.total) + p.tile0;
   }
-  bid += p.tile0;
   int qt = bid % p.n_qtiles;
   bid /= p.n_qtiles;
   const int hq = bid % p.Hq;
@@ -223,8 +233,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
   const int wpos0 = p.pos_nq ? 0 : wq0;
 
   // A split launch covers one key range per piece; otherwise every key.
-  const int kbeg = SPLIT ? sp * p.split_len : 0;
-  int kend = SPLIT ? min(p.Nkv, kbeg + p.split_len) : p.Nkv;
+  const int kbeg = piece ? sp * p.split_len : 0;
+  int kend = piece ? min(p.Nkv, kbeg + p.split_len) : p.Nkv;
   // Causal: keys past the reach of the tile's last position are masked.
   // Packed rows hold positions 0 .. pos_nq - 1 of several heads.
   if (CAUSAL) kend = max(0, min(kend, (p.pos_nq ? min(q0 + BM, p.pos_nq) : q0 + BM) + p.coff));
@@ -763,7 +773,7 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse_v = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
     if (qrow < p.Nq) {
-      if (SPLIT) {
+      if (piece) {
         const size_t prow = (size_t)sp * p.prows + (qrow0 + qrow - p.row0);
         float* dst = p.opart + prow * DV;
 #pragma unroll
