@@ -35,6 +35,7 @@
 
 #include "attn_common.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace {
@@ -760,14 +761,76 @@ int validate_bwd_mask(const BwdMask& m, const void* dq, const void* dk, const vo
   return ATTN_OK;
 }
 
+// dQ and dK/dV need only the Delta rows, not each other: dQ runs on a
+// second stream of the library's, forked from the caller's stream after the
+// Delta kernel and joined back before the caller's stream goes on, so that
+// each kernel's last, partial round of workgroups shares the device with
+// the other's instead of leaving CUs idle.  Measured against one stream:
+// +3.5% to +21% at D = 64 (sweep and causal GQA, 4096 and 16384 tokens),
+// +5.8% at D = 256, neutral at 96 and (192, 128); at D = 128 the two
+// kernels' streams through L2 collide (video-DiT 17160 -3.5%, 75600
+// neutral), so D = 128 keeps one stream.  One side stream and a pair of
+// events per device; the events are recorded and waited on under a host
+// lock, so concurrent calls cannot mix up their fork and join points.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool init = false;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// With g_side_mu held: the current device's side stream and events.
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.init) {
+    e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    ss.init = true;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 template <int D, int DV, class Tag, bool MASKED>
-hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
+hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st, SideStream* side) {
+  constexpr bool kFork = D != 128;
   const int rows = p.B * p.Hq * p.Nq;
   const size_t threads = (size_t)rows * bwd_delta_lanes(DV);  // Delta: rows of O and dO
   hipLaunchKernelGGL((attn_delta_kernel<DV, Tag>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, st, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // dQ on the side stream, after Delta (one stream at D = 128: dQ after dK/dV)
+  const hipStream_t sq = kFork ? side->s : st;
+  if (kFork) {
+    e = hipEventRecord(side->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return e;
+  }
+  BwdParams pq = p;
+  pq.n_tiles = (p.Nq + 127) / 128;
+  pq.total = p.B * p.Hq * pq.n_tiles;
+  auto launch_dq = [&]() {
+    if (causal)
+      hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, true, MASKED>), dim3(pq.total), dim3(256),
+                         0, sq, pq);
+    else
+      hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, false, MASKED>), dim3(pq.total), dim3(256),
+                         0, sq, pq);
+    return hipGetLastError();
+  };
+  if (kFork) {
+    e = launch_dq();
+    if (e != hipSuccess) return e;
+  }
   BwdParams pk = p;
   pk.n_tiles = (p.Nkv + 127) / 128;
   pk.total = p.B * p.Hkv * p.hsplit * pk.n_tiles;
@@ -788,36 +851,36 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  BwdParams pq = p;
-  pq.n_tiles = (p.Nq + 127) / 128;
-  pq.total = p.B * p.Hq * pq.n_tiles;
-  if (causal)
-    hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, true, MASKED>), dim3(pq.total), dim3(256), 0,
-                       st, pq);
-  else
-    hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, false, MASKED>), dim3(pq.total), dim3(256), 0,
-                       st, pq);
-  return hipGetLastError();
+  if (!kFork) return launch_dq();
+  // join: the caller's stream goes on after dQ too
+  e = hipEventRecord(side->join, side->s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
+  return e;
 }
 
 template <int D, int DV>
-hipError_t launch_bwd_masks(bool bf, bool masked, const BwdParams& p, bool cz, hipStream_t st) {
+hipError_t launch_bwd_masks(bool bf, bool masked, const BwdParams& p, bool cz, hipStream_t st,
+                            SideStream* side) {
   if (masked)
-    return bf ? launch_bwd<D, DV, TagBF16, true>(p, cz, st)
-              : launch_bwd<D, DV, TagF16, true>(p, cz, st);
-  return bf ? launch_bwd<D, DV, TagBF16, false>(p, cz, st)
-            : launch_bwd<D, DV, TagF16, false>(p, cz, st);
+    return bf ? launch_bwd<D, DV, TagBF16, true>(p, cz, st, side)
+              : launch_bwd<D, DV, TagF16, true>(p, cz, st, side);
+  return bf ? launch_bwd<D, DV, TagBF16, false>(p, cz, st, side)
+            : launch_bwd<D, DV, TagF16, false>(p, cz, st, side);
 }
 
 hipError_t launch_bwd_d(int D, int Dv, bool bf, bool masked, const BwdParams& p, bool cz,
                         hipStream_t st) {
-  if (Dv != D) return launch_bwd_masks<192, 128>(bf, masked, p, cz, st);
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  const hipError_t e = side_stream(&side);
+  if (e != hipSuccess) return e;
+  if (Dv != D) return launch_bwd_masks<192, 128>(bf, masked, p, cz, st, side);
   switch (D) {
-    case 64: return launch_bwd_masks<64, 64>(bf, masked, p, cz, st);
-    case 80: return launch_bwd_masks<80, 80>(bf, masked, p, cz, st);
-    case 96: return launch_bwd_masks<96, 96>(bf, masked, p, cz, st);
-    case 256: return launch_bwd_masks<256, 256>(bf, masked, p, cz, st);
-    default: return launch_bwd_masks<128, 128>(bf, masked, p, cz, st);
+    case 64: return launch_bwd_masks<64, 64>(bf, masked, p, cz, st, side);
+    case 80: return launch_bwd_masks<80, 80>(bf, masked, p, cz, st, side);
+    case 96: return launch_bwd_masks<96, 96>(bf, masked, p, cz, st, side);
+    case 256: return launch_bwd_masks<256, 256>(bf, masked, p, cz, st, side);
+    default: return launch_bwd_masks<128, 128>(bf, masked, p, cz, st, side);
   }
 }
 
