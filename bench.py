@@ -73,10 +73,10 @@ def measured_traffic(workload: str, pass_: str = "fwd", kernels: str | None = No
 
 
 class StreamOrderedPeak:
-    """High-water mark of the device's default memory pool, which serves the
-    library's stream-ordered workspace (hipMallocAsync): reset before the
-    timed region, read after it.  Uses the HIP runtime this process has
-    already loaded (the one torch and the library share)."""
+    """High-water mark of the library's workspace pool on the device
+    (attn_workspace_pool; it serves every stream-ordered workspace): reset
+    before the timed region, read after it, through the HIP runtime this
+    process has already loaded (the one torch and the library share)."""
 
     USED_MEM_HIGH = 0x8   # hipMemPoolAttrUsedMemHigh
 
@@ -93,9 +93,11 @@ class StreamOrderedPeak:
             return
         self.ct = ctypes
         self.hip = ctypes.CDLL(path)
-        self.pool = ctypes.c_void_p()
-        self.ok = self.hip.hipDeviceGetDefaultMemPool(ctypes.byref(self.pool),
-                                                      device_index) == 0
+        from memory_efficient_tiled_amd import binding
+        import torch
+        with torch.cuda.device(device_index):
+            self.pool = ctypes.c_void_p(binding.workspace_pool())
+        self.ok = True
 
     def reset(self):
         if self.ok:

@@ -443,6 +443,28 @@ const char* attn_strerror(int code);
  * ATTN_EHIP / ATTN_ENOMEM / ATTN_EUNSUPPORTED, 0 if none. */
 int attn_last_hip_error(void);
 
+/*
+ * attn_workspace_pool -- the memory pool that serves the library's
+ * stream-ordered workspace on the current device (split-KV partials of
+ * attn_fwd and its variants, the gradients' Delta rows and head-split
+ * partials, the FP8 path's transposed V, the FFN's hidden chunks).
+ *
+ * The library creates one pool per device on first use and allocates from
+ * it with hipMallocFromPoolAsync on the caller's stream.  The pool's release
+ * threshold is the maximum: memory it has handed out stays mapped between
+ * calls, so a call after a stream or device synchronisation does not map its
+ * workspace again (with a threshold of 0 that cost ~0.4 ms on a 62 MB
+ * workspace).  The memory is therefore held until the process ends.
+ *
+ * pool : out, the hipMemPool_t (as void*).  The library owns it: callers may
+ *        read its attributes (e.g. hipMemPoolAttrUsedMemHigh for the peak
+ *        workspace) or release idle memory with hipMemPoolTrimTo, and must
+ *        not destroy it.
+ * Returns ATTN_OK; ATTN_EINVAL if pool is NULL; ATTN_EHIP if the device
+ * query or the pool's creation fails (attn_last_hip_error).
+ */
+int attn_workspace_pool(void** pool);
+
 #ifdef __cplusplus
 }
 #endif

@@ -148,8 +148,22 @@ def load_library():
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
     lib.attn_last_hip_error.restype = _INT
+    lib.attn_workspace_pool.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.attn_workspace_pool.restype = _INT
     _lib = lib
     return lib
+
+
+def workspace_pool() -> int:
+    """attn_workspace_pool: the current device's hipMemPool_t (as an int)
+    that serves the library's stream-ordered workspace.  Owned by the
+    library; read its attributes or trim it, never destroy it."""
+    lib = load_library()
+    pool = ctypes.c_void_p()
+    rc = lib.attn_workspace_pool(ctypes.byref(pool))
+    if rc != ATTN_OK:
+        _raise(rc)
+    return int(pool.value)
 
 
 def _raise(code: int):

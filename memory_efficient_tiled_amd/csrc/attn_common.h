@@ -228,7 +228,9 @@ namespace attn_host {
 int check_device(int* cus);
 // Records the hipError_t behind an ATTN_EHIP / ATTN_ENOMEM return.
 void set_last_hip_error(int e);
-// Stream-ordered workspace (hipMallocAsync on `st`).  With the environment
+// Stream-ordered workspace on `st`, from the library's memory pool of the
+// current device (hipMallocFromPoolAsync; the pool keeps its memory between
+// calls, see attn_workspace_pool).  With the environment
 // variable ATTN_FAIL_WORKSPACE set to 1 the request fails with
 // hipErrorOutOfMemory without allocating: failure injection for tests of
 // the ATTN_ENOMEM paths (read at every call; nothing has been launched

@@ -23,6 +23,7 @@ struct DeviceInfo {
   bool gfx950 = false;
   int cus = 0;
   void* scratch = nullptr;  // this device's address of `scratch` (attn_fwd_noalloc)
+  hipMemPool_t pool = nullptr;  // stream-ordered workspace pool (workspace_pool)
 };
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
@@ -229,6 +230,40 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   return ATTN_OK;
 }
 
+// The library's stream-ordered workspace pool on the current device, created
+// on first use.  Its release threshold is the maximum, so memory it has
+// handed out stays mapped between calls: with the default pool (threshold
+// 0) every stream or device synchronisation returned the workspace to the
+// driver, and the next call after it mapped it again (the first video-DiT
+// step after a synchronisation took 3.3-3.4 ms instead of 2.9).
+hipError_t workspace_pool(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.pool) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
+    d.pool = pool;
+  }
+  *out = d.pool;
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace attn_host {
@@ -245,7 +280,10 @@ hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t st) {
     *p = nullptr;
     return hipErrorOutOfMemory;
   }
-  return hipMallocAsync(p, bytes, st);
+  hipMemPool_t pool = nullptr;
+  const hipError_t e = workspace_pool(&pool);
+  if (e != hipSuccess) return e;
+  return hipMallocFromPoolAsync(p, bytes, pool, st);
 }
 void narrow_plan(int B, int Hq, int Nq, int Nkv, int D, int causal, int num_splits, int cus,
                  NarrowPlan* out) {
@@ -453,5 +491,18 @@ const char* attn_strerror(int code) {
 }
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_workspace_pool(void** pool) {
+  if (!pool) return ATTN_EINVAL;
+  hipMemPool_t mp = nullptr;
+  const hipError_t e = workspace_pool(&mp);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    (void)hipGetLastError();
+    return ATTN_EHIP;
+  }
+  *pool = (void*)mp;
+  return ATTN_OK;
+}
 
 }  // extern "C"

@@ -225,9 +225,9 @@ def fp8_bounds(x: inputs.Inputs, scale, causal, rows=None, causal_offset=0):
 
 
 class PoolPeak:
-    """High-water mark of the device's default memory pool, which serves the
-    library's stream-ordered workspace (hipMallocAsync), through the HIP
-    runtime this process has already loaded."""
+    """High-water mark of the library's workspace pool on the device
+    (attn_workspace_pool), through the HIP runtime this process has already
+    loaded."""
 
     USED_MEM_HIGH = 0x8   # hipMemPoolAttrUsedMemHigh
 
@@ -236,8 +236,10 @@ class PoolPeak:
         path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64.so" in ln)
         self.ct = ctypes
         self.hip = ctypes.CDLL(path)
-        self.pool = ctypes.c_void_p()
-        assert self.hip.hipDeviceGetDefaultMemPool(ctypes.byref(self.pool), device_index) == 0
+        from memory_efficient_tiled_amd import binding
+        import torch
+        with torch.cuda.device(device_index):
+            self.pool = ctypes.c_void_p(binding.workspace_pool())
 
     def reset(self):
         zero = self.ct.c_uint64(0)

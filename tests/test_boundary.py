@@ -354,3 +354,8 @@ def test_fp8_validation(lib):
     assert chk(out_dtype=7) == EINVAL
     assert chk(out=Q + 4096) == EINVAL          # output overlaps q
     assert chk(q=Q + 8) == EINVAL               # not 16-byte aligned
+
+
+def test_workspace_pool_rejects_null(lib):
+    # the argument check comes before any HIP call
+    assert lib.attn_workspace_pool(None) == EINVAL

@@ -104,3 +104,33 @@ def test_fp8_enomem(gpu_device):
     o, _ = binding.attn_fwd_fp8(q, k, v, x.q_descale, x.k_descale, x.v_descale)
     torch.cuda.synchronize(gpu_device)
     assert bool(torch.isfinite(o.float()).all())
+
+
+def test_workspace_pool_keeps_memory(gpu_device):
+    """The library's workspace pool keeps what it handed out across a device
+    synchronisation (release threshold at the maximum), can be trimmed by
+    the caller, and serves the next call afterwards."""
+    import ctypes
+    import torch
+    path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64.so" in ln)
+    hip = ctypes.CDLL(path)
+    pool = ctypes.c_void_p(binding.workspace_pool())
+    assert pool.value == binding.workspace_pool(), "one pool per device"
+
+    def reserved():
+        v = ctypes.c_uint64(0)
+        assert hip.hipMemPoolGetAttribute(pool, 0x5, ctypes.byref(v)) == 0  # ReservedMemCurrent
+        return int(v.value)
+
+    x = inputs.make_inputs(1, 14, 2, 3, 20000, 128, inputs.BF16, seed=604)
+    q, k, v = (to_device(a, inputs.BF16, gpu_device) for a in (x.q, x.k, x.v))
+    ws = binding.attn_fwd_plan(1, 14, 2, 3, 20000, 128, False, binding.ATTN_BF16).workspace_bytes
+    assert ws > 0
+    o1, l1 = binding.attn_fwd(q, k, v)
+    torch.cuda.synchronize(gpu_device)
+    assert reserved() >= ws, "the workspace was returned at the synchronisation"
+    assert hip.hipMemPoolTrimTo(pool, ctypes.c_size_t(0)) == 0
+    o2, l2 = binding.attn_fwd(q, k, v)
+    torch.cuda.synchronize(gpu_device)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    log(f"  workspace pool: {reserved()} bytes reserved after the call (plan {ws})")
