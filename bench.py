@@ -33,14 +33,14 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}   # MI355X den
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc")
 # the kernel sources each pass runs (a measurement taken on other sources is stale)
-SOURCES = {"fwd": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_d64.hip",
-                   "attn_fwd_d80.hip", "attn_fwd_d96.hip", "attn_fwd_d128.hip",
-                   "attn_fwd_d256.hip", "attn_fwd_d192v128.hip"),
-           "bwd": ("attn_common.h", "attn_bwd.hip"),
+SOURCES = {"fwd": ("attn_common.h", "attn_tiles.h", "attn_plan.h", "attn_fwd_kernel.h",
+                   "attn_fwd.hip", "attn_fwd_d64.hip", "attn_fwd_d80.hip", "attn_fwd_d96.hip",
+                   "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_fwd_d192v128.hip"),
+           "bwd": ("attn_common.h", "attn_tiles.h", "attn_bwd.hip"),
            # the FP8 kernel, and the plan and merge it shares with the 16-bit path
-           "fp8": ("attn_common.h", "attn_fwd_kernel.h", "attn_fwd.hip", "attn_fwd_d128.hip",
-                   "attn_fwd_fp8.hip"),
-           "ffn": ("attn_common.h", "ffn_chunked.hip")}
+           "fp8": ("attn_common.h", "attn_tiles.h", "attn_plan.h", "attn_fwd_kernel.h",
+                   "attn_fwd.hip", "attn_fwd_d128.hip", "attn_fwd_fp8.hip"),
+           "ffn": ("attn_common.h", "attn_tiles.h", "ffn_chunked.hip")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
