@@ -262,21 +262,23 @@ def main():
     else:
         step = fwd_step
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     # peak memory of the timed steps: torch's allocator (the outputs are
     # allocated before timing, so nothing is expected there) and the pool
     # that serves the library's stream-ordered workspace
     pool = StreamOrderedPeak(dev.index or 0)
+    # one event between consecutive steps: the whole region gives the mean,
+    # the gaps give per-step median and minimum.  Everything the host does
+    # before timing happens before the warm-up, so the device idles as
+    # little as possible between the warm-up and the first timed step.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    progress(f"warm-up {args.warmup} steps, then timing {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     torch_before = torch.cuda.memory_allocated(dev)
     pool.reset()
-    # one event between consecutive steps: the whole region gives the mean,
-    # the gaps give per-step median and minimum
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    progress(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev[0].record(stream)
