@@ -133,7 +133,8 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   Nq = pk.Nq;
   const Plan pl = make_plan(B, Hq, Nq, Nkv, D, Dv, causal, num_splits, di.cus, masked);
   const long long split_wgs = (pl.tiles - pl.first_split) * pl.splits;
-  if (pl.first_split > INT32_MAX || split_wgs > INT32_MAX) return ATTN_EINVAL;
+  // grid sizes are ints: whole tiles and pieces share one launch
+  if (pl.first_split + split_wgs > INT32_MAX) return ATTN_EINVAL;
 
   Params p;
   p.q = (const uint16_t*)q;
@@ -208,7 +209,6 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
   hipError_t e = hipSuccess;
   p.n_whole = 0;
   if (split_wgs > 0) {
-    if (pl.first_split + split_wgs > INT32_MAX) return ATTN_EINVAL;
     p.n_whole = (int)pl.first_split;
     p.total = (int)(pl.first_split + split_wgs);
     p.tile0 = (int)pl.first_split;

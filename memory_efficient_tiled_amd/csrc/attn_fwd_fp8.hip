@@ -110,13 +110,20 @@ __global__ __launch_bounds__(kNW8 * 64, kWavesPerSimd) void attn_fwd_fp8_kernel(
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  int bid = xcd_remap(blockIdx.x, p.total);
-  int sp = 0;
-  if (SPLIT) {
+  // A split launch may start with whole tiles (as in the 16-bit path): its
+  // pieces then take the slots of the whole tiles that finish first.
+  int bid, sp = 0;
+  bool piece = SPLIT;
+  if (SPLIT && (int)blockIdx.x < p.n_whole) {
+    piece = false;
+    bid = xcd_remap(blockIdx.x, p.n_whole);
+  } else if (SPLIT) {
+    bid = xcd_remap(blockIdx.x - p.n_whole, p.total - p.n_whole);
     sp = bid % p.n_splits;
-    bid /= p.n_splits;
+    bid = bid / p.n_splits + p.tile0;
+  } else {
+    bid = xcd_remap(blockIdx.x, p.total) + p.tile0;
   }
-  bid += p.tile0;
   int qt = bid % p.n_qtiles;
   bid /= p.n_qtiles;
   const int hq = bid % p.Hq;
@@ -127,8 +134,8 @@ __global__ __launch_bounds__(kNW8 * 64, kWavesPerSimd) void attn_fwd_fp8_kernel(
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + l32;
 
-  const int kbeg = SPLIT ? sp * p.split_len : 0;
-  int kend = SPLIT ? min(p.Nkv, kbeg + p.split_len) : p.Nkv;
+  const int kbeg = piece ? sp * p.split_len : 0;
+  int kend = piece ? min(p.Nkv, kbeg + p.split_len) : p.Nkv;
   if (CAUSAL) kend = max(0, min(kend, q0 + BM + p.coff));
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(kNW8 * 64, kWavesPerSimd) void attn_fwd_fp8_kernel(
   const float inv = lt > 0.f ? v_descale / lt : 0.f;
   const float lse_v = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   if (qrow < p.Nq) {
-    if (SPLIT) {
+    if (piece) {
       const size_t prow = (size_t)sp * p.prows + (qrow0 + qrow - p.row0);
       float* dst = p.opart + prow * D;
 #pragma unroll
@@ -427,7 +434,8 @@ int run_fp8(const void* q, const void* k, const void* v, void* out, float* lse, 
   attn_host::NarrowPlan pl;
   attn_host::narrow_plan(B, Hq, Nq, Nkv, D, causal, num_splits, cus, &pl);
   const long long split_wgs = (pl.tiles - pl.first_split) * pl.splits;
-  if (pl.first_split > INT32_MAX || split_wgs > INT32_MAX) return ATTN_EINVAL;
+  // grid sizes are ints: whole tiles and pieces share one launch
+  if (pl.first_split + split_wgs > INT32_MAX) return ATTN_EINVAL;
 
   const int nkv_pad = (Nkv + kBN8 - 1) / kBN8 * kBN8;
   const size_t vt_bytes = ((size_t)B * Hkv * D * nkv_pad + 255) / 256 * 256;
@@ -473,16 +481,18 @@ int run_fp8(const void* q, const void* k, const void* v, void* out, float* lse, 
                      0, st, (const uint8_t*)v, vt, Nkv, nkv_pad, tph);
   e = hipGetLastError();
   const bool bf16 = out_dtype == ATTN_BF16, cz = causal != 0;
-  if (e == hipSuccess && pl.first_split > 0) {
-    p.total = (int)pl.first_split;
-    p.tile0 = 0;
-    e = launch_fp8(p, bf16, cz, false, vt, nkv_pad, vds, st);
-  }
+  // whole tiles and the pieces of the rest in one launch, whole tiles first
+  p.n_whole = 0;
   if (e == hipSuccess && split_wgs > 0) {
-    p.total = (int)split_wgs;
+    p.n_whole = (int)pl.first_split;
+    p.total = (int)(pl.first_split + split_wgs);
     p.tile0 = (int)pl.first_split;
     e = launch_fp8(p, bf16, cz, true, vt, nkv_pad, vds, st);
     if (e == hipSuccess) e = launch_combine_d<kD8>(p, false, bf16, st);
+  } else if (e == hipSuccess && pl.first_split > 0) {
+    p.total = (int)pl.first_split;
+    p.tile0 = 0;
+    e = launch_fp8(p, bf16, cz, false, vt, nkv_pad, vds, st);
   }
   const hipError_t ef = hipFreeAsync(ws, st);
   if (e == hipSuccess) e = ef;
