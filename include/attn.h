@@ -106,9 +106,10 @@ enum {
  * the tiles cannot keep every compute unit busy -- a grid smaller than the
  * device, or, without a mask, the last partial round of a grid that fills it
  * -- those tiles are split over key ranges (split-KV) and the pieces merged
- * by their log-sum-exp.  Pieces take a workspace of
- * attn_plan.workspace_bytes bytes from hipMallocAsync/hipFreeAsync on
- * `stream`; when nothing is split nothing is allocated.
+ * by their log-sum-exp; whole tiles and pieces share one launch, whole
+ * tiles first.  Pieces take a workspace of attn_plan.workspace_bytes bytes,
+ * stream-ordered on `stream` from the library's pool (attn_workspace_pool);
+ * when nothing is split nothing is allocated.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nkv, int D,
@@ -371,8 +372,11 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
  *            must not overlap each other or any input.
  * All pointers 16-byte aligned; D in {64, 80, 96, 128, 256}; Hq a multiple
  * of Hkv.
- * Allocates a float32 [B,Hq,Nq] workspace (Delta) on `stream` with
- * hipMallocAsync and frees it there.  Returns ATTN_OK, ATTN_EINVAL,
+ * Allocates a float32 [B,Hq,Nq] workspace (Delta) stream-ordered on `stream`
+ * from the library's pool (attn_workspace_pool) and frees it there.  dQ runs
+ * on a second stream of the library's, forked from `stream` after Delta and
+ * joined back before the call returns (except at D = 128); the caller sees
+ * ordinary stream order on `stream`.  Returns ATTN_OK, ATTN_EINVAL,
  * ATTN_EUNSUPPORTED, ATTN_ENOMEM or ATTN_EHIP.  Results are deterministic
  * (no atomics).
  */

@@ -112,7 +112,7 @@ hipError_t launch_combine(int Dv, const Params& p, bool strided, bool bf16, hipS
 
 // `noalloc`: take the split workspace from this device's `scratch` array
 // (ATTN_ESCRATCH, before any launch, when the plan needs more) instead of
-// hipMallocAsync.
+// the workspace pool.
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
         int Nq, int Nkv, int D, int Dv, const Layout& L, float scale, int causal, int dtype,
         int num_splits, hipStream_t stream, const MaskArgs& M = MaskArgs(),

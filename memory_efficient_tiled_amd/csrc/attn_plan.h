@@ -156,10 +156,10 @@ inline int validate(const void* q, const void* k, const void* v, const void* out
 }
 
 // How one call covers its query tiles (tile index (b * Hq + h) * n_qtiles +
-// qt): tiles [0, first_split) run whole in a launch that writes the output
-// directly; the key range of each tile in [first_split, tiles) is cut into
-// `splits` pieces of `split_len` keys, computed by a second launch into fp32
-// partials and merged by their log-sum-exp.  Those tiles are the last ones,
+// qt): tiles [0, first_split) run whole and write the output directly; the
+// key range of each tile in [first_split, tiles) is cut into `splits`
+// pieces of `split_len` keys, computed into fp32 partials (in the same
+// launch, after the whole tiles) and merged by their log-sum-exp.  Those tiles are the last ones,
 // so their rows are one contiguous range [row0, rows).
 struct Plan {
   int cfg;

@@ -1,7 +1,8 @@
 """HIP graph capture of the allocating entry points.
 
-attn_fwd takes its split-KV partials from the stream-ordered pool
-(hipMallocAsync / hipFreeAsync on the caller's stream) and attn_bwd forks
+attn_fwd takes its split-KV partials stream-ordered from the library's
+memory pool (hipMallocFromPoolAsync / hipFreeAsync on the caller's stream)
+and attn_bwd forks
 its dQ kernel onto a second stream of the library's (event record and wait)
 except at D = 128.  Both must be capturable by a caller (torch.cuda.graph,
 as torch.compile's CUDA-graph mode does): each captured call is replayed
