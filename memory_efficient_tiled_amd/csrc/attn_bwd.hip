@@ -260,7 +260,8 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   const int kw = wave & 3;
   const bool pw = wave < 4;  // computes P (else dS)
 
-  int bid = xcd_remap(blockIdx.x, p.total);
+  // (causal: key tile 0 sees the most query tiles)
+  int bid = CAUSAL ? longest_first(blockIdx.x, p.n_tiles, p.total) : xcd_remap(blockIdx.x, p.total);
   const int kt = bid % p.n_tiles;
   bid /= p.n_tiles;
   const int hs = bid % p.hsplit;
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
 
-  int bid = xcd_remap(blockIdx.x, p.total);
+  int bid = CAUSAL ? longest_first(blockIdx.x, p.n_tiles, p.total) : xcd_remap(blockIdx.x, p.total);
   int qt = bid % p.n_tiles;
   bid /= p.n_tiles;
   const int hq = bid % p.Hq;

@@ -145,6 +145,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + s;
 }
 
+// Causal grids, whose tiles differ in length: workgroup j of a launch of
+// `total` = count x ntiles tiles (tile index fastest in the logical order)
+// takes logical tile (j % count) * ntiles + j / count, so the launch runs
+// tile index 0 of every head first, then index 1, and so on.  The caller
+// orders tile indices longest first.  Dealt round-robin over the 8 XCDs,
+// every XCD then gets an equal share of each length and runs its share
+// longest first; xcd_remap would give each XCD a contiguous range of heads
+// instead, whose long tiles some XCDs would reach only late.
+__device__ __forceinline__ int longest_first(int j, int ntiles, int total) {
+  const int count = total / ntiles;
+  return (j % count) * ntiles + j / count;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transposing LDS read: in each 16-lane group, lane i receives element i%4 of

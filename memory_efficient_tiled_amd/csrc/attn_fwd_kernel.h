@@ -213,6 +213,8 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
     bid = xcd_remap(blockIdx.x - p.n_whole, p.total - p.n_whole);
     sp = bid % p.n_splits;
     bid = bid / p.n_splits + p.tile0;
+  } else if (CAUSAL) {
+    bid = longest_first(blockIdx.x, p.n_qtiles, p.total);  // (the launch holds every tile)
   } else {
     bid = xcd_remap(blockIdx.x, p.total) + p.tile0;
   }
