@@ -206,14 +206,49 @@ inline int balanced_splits(long long rem, long long slots, int ktiles, double ro
   return best;
 }
 
-// Causal tiles differ in length and are launched longest first, so the
-// hardware's dynamic dispatch balances them; only a grid smaller than the
-// chip is split, into enough pieces to fill every slot.
-inline int causal_splits(long long tiles, long long slots, int ktiles) {
+// Causal tiles differ in length and are launched longest first, which the
+// hardware's dynamic dispatch balances, so only a grid smaller than the chip
+// is split, into enough pieces to fill every slot -- and only when that
+// pays: a launch lasts about as long as its longest piece or its mean load
+// per slot, whichever is more, and a split call adds the merge and a fixed
+// cost for the second launch and the workspace.  In microseconds,
+// calibrated on MI355X with forced piece counts (eager calls; e.g. causal
+// GQA 14/2 at 4096 tokens, D = 64: 54-58 us whole, 80-102 us in 2-8
+// pieces; 16 heads x 1024: 18 us whole, 38-44 us in 2-16; 4 heads x 2048
+// at D = 128: 57 us whole, 38-45 us in 2-8): a key step of a workgroup
+// takes its flops at 1 PFLOP/s over the slots, a split call costs
+// kSplitFixedUs more, and the merge moves the partials (written once, read
+// once) at kMergeBytesPerUs.  Query tile qt of a head (rows up to
+// min((qt + 1) BM, Nq)) reaches keys below that row + coff.
+constexpr double kChipFlopsPerUs = 1.0e9;
+constexpr double kSplitFixedUs = 30.0;
+constexpr double kMergeBytesPerUs = 3.0e6;
+
+inline int causal_splits(long long bh, int n_qtiles, int BM, int BN, int D, int Dv, int Nq,
+                         int Nkv, int coff, long long slots, int ktiles) {
+  const long long tiles = bh * n_qtiles;
   if (tiles >= slots) return 1;
-  long long s = (slots + tiles - 1) / tiles;
-  s = std::min<long long>(s, std::min(kMaxSplits, ktiles / kMinStepsPerPiece));
-  return s < 1 ? 1 : (int)s;
+  const int s = (int)std::min<long long>((slots + tiles - 1) / tiles,
+                                         std::min(kMaxSplits, ktiles / kMinStepsPerPiece));
+  if (s < 2) return 1;
+  long long sum = 0;
+  int lmax = 0;
+  for (int qt = 0; qt < n_qtiles; ++qt) {
+    const long long end =
+        std::min<long long>(std::min<long long>((long long)(qt + 1) * BM, Nq) + coff, Nkv);
+    const int len = end > 0 ? (int)((end + BN - 1) / BN) : 0;
+    sum += len;
+    lmax = std::max(lmax, len);
+  }
+  const double work = (double)sum * bh;
+  const double step_us = 2.0 * BM * BN * (double)(D + Dv) * slots / kChipFlopsPerUs;
+  const double whole =
+      std::max(lmax + kPieceFillSteps, (work + kPieceFillSteps * tiles) / slots) * step_us;
+  const int steps = (ktiles + s - 1) / s;
+  const double cut = std::max(std::min(lmax, steps) + kPieceFillSteps,
+                              (work + kPieceFillSteps * tiles * s) / slots) * step_us +
+                     kSplitFixedUs + s * (double)bh * Nq * (Dv + 1) * 8.0 / kMergeBytesPerUs;
+  return cut < whole ? s : 1;
 }
 
 // num_splits > 0 cuts every tile into that many pieces (at most one per key
@@ -236,7 +271,8 @@ inline Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int Dv, int causal,
   if (num_splits > 0) {
     S = num_splits;
   } else if (causal) {
-    S = causal_splits(pl.tiles, slots, ktiles);
+    S = causal_splits((long long)B * Hq, pl.n_qtiles, c.BM(), c.BN, D, Dv, Nq, Nkv,
+                      causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0, slots, ktiles);
   } else {
     const long long rem = pl.tiles % slots;
     first = pl.tiles - rem;

@@ -155,9 +155,13 @@ def test_gqa_packing_plans():
     # MHA decode is not packed: 16 one-row tiles
     m = plan(1, 16, 16, 1, 65536, 128, 0)
     assert m.tile_rows == 128 and 16 * m.num_splits >= 2 * 256
-    # packed causal GQA with 100-row chunks (D = 64, 128-row tiles)
-    g = plan(1, 14, 2, 100, 4096, 64, 1)
-    assert g.tile_rows == 128 and g.split_rows == 1400
+    # packed causal GQA with 100-row chunks (D = 64, 128-row tiles): aligned
+    # bottom-right, each row sees about 4000 keys and the 700 packed rows of
+    # each KV head are split; aligned top-left, no row sees more than 100
+    # keys, and the pieces would cost more than they save
+    g = plan(1, 14, 2, 100, 4096, 64, 2)
+    assert g.tile_rows == 128 and g.num_splits >= 2 and g.split_rows == 1400
+    assert plan(1, 14, 2, 100, 4096, 64, 1).num_splits == 1
     # a long query range is not packed and takes the 256-row tile
     assert plan(1, 14, 2, 4096, 4096, 128, 1).tile_rows == 256
     # the (192, 128) pair has one tile of 256 rows
