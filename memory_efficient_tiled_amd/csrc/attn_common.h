@@ -179,6 +179,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Max over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = pair_max(x);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
 
 // LDS swizzles.  gfx950 serves a 16-byte LDS read 16 lanes (256 bytes, all
 // 64 banks) at a time and an 8-byte read 32 lanes at a time, so a pattern is

@@ -865,44 +865,50 @@ __global__ __launch_bounds__(kRowMergeThreads) void attn_combine_rows_kernel(
   constexpr int C4 = D / 4;
   constexpr int GS = C4 <= 32 ? 32 : 64;
   constexpr int NG = T / GS;
-  __shared__ float red[T];
+  __shared__ float red[T / 64];
   __shared__ f32x4 part[NG][GS];
   __shared__ float wpart[NG];
   const int row = blockIdx.x;  // grid = rows
   const int t = threadIdx.x;
+  const int g = t / GS, c4 = t % GS;
+  // The first round of eight pieces per group is loaded before the largest
+  // LSE is known (the loads do not depend on it), so the two round trips to
+  // memory overlap (few rows: the merge is bound by load latency).
+  constexpr int U = 8;
+  float ls[U];
+  f32x4 x[U];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * NG;
+      ls[u] = s < n_splits ? lsepart[(size_t)s * rows + row] : -INFINITY;
+      x[u] = (s < n_splits && c4 < C4)
+                 ? *(const f32x4*)(opart + ((size_t)s * rows + row) * D + c4 * 4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_round(g);
   float mx = -INFINITY;
   for (int s = t; s < n_splits; s += T) mx = fmaxf(mx, lsepart[(size_t)s * rows + row]);
-  red[t] = mx;
+  mx = wave_max(mx);  // then the 16 waves' maxima through LDS
+  if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
-  for (int w = T / 2; w > 0; w >>= 1) {
-    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
-    __syncthreads();
-  }
   mx = red[0];
-  const int g = t / GS, c4 = t % GS;
+#pragma unroll
+  for (int w = 1; w < T / 64; ++w) mx = fmaxf(mx, red[w]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    // eight pieces per round, their loads issued together (few rows: the
-    // merge is bound by load latency, not bandwidth)
-    constexpr int U = 8;
-    for (int s0 = g; s0 < n_splits; s0 += U * NG) {
-      float ls[U];
-      f32x4 x[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u * NG;
-        ls[u] = s < n_splits ? lsepart[(size_t)s * rows + row] : -INFINITY;
-        x[u] = (s < n_splits && c4 < C4)
-                   ? *(const f32x4*)(opart + ((size_t)s * rows + row) * D + c4 * 4)
-                   : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int s0 = g;;) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float w = (ls[u] == -INFINITY) ? 0.f : expf(ls[u] - mx);
         wsum += w;
         acc += w * x[u];
       }
+      s0 += U * NG;
+      if (s0 >= n_splits) break;
+      load_round(s0);
     }
   }
   part[g][c4] = acc;
