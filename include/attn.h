@@ -106,8 +106,10 @@ enum {
  * the tiles cannot keep every compute unit busy -- a grid smaller than the
  * device, or, without a mask, the last partial round of a grid that fills it
  * -- those tiles are split over key ranges (split-KV) and the pieces merged
- * by their log-sum-exp; whole tiles and pieces share one launch, whole
- * tiles first.  Pieces take a workspace of attn_plan.workspace_bytes bytes,
+ * by their log-sum-exp, when a cost model finds that the pieces save more
+ * than the split costs (for a small causal grid, whose tiles differ in
+ * length, often they do not); whole tiles and pieces share one launch,
+ * whole tiles first.  Pieces take a workspace of attn_plan.workspace_bytes bytes,
  * stream-ordered on `stream` from the library's pool (attn_workspace_pool);
  * when nothing is split nothing is allocated.
  */
