@@ -77,6 +77,21 @@ def test_ragged_lengths(gpu_device, n, causal, D, dtype):
     _case(gpu_device, 2, 4, 2, n, n, D, dtype, causal, seed=n)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [True, "bottom_right"])
+def test_causal_whole_grid_batches(gpu_device, D, causal):
+    """One launch of whole causal tiles over 2 batches x 6 heads (a head
+    count that is not a multiple of the 8 XCDs), tile index 0 of every
+    (batch, head) first: every tile lands on its own rows."""
+    nq, nkv = 1500, 1700 if causal == "bottom_right" else 1500
+    log(f"causal whole grid D={D} {causal}")
+    x = inputs.make_inputs(2, 6, 3, nq, nkv, D, inputs.F16, seed=D + len(str(causal)))
+    o, l = run_gpu(x, None, causal, gpu_device, num_splits=1)
+    o_ref, l_ref = oracle_rows(x, None, True, causal_offset=nkv - nq if causal == "bottom_right" else 0)
+    compare(o, l, o_ref, l_ref, inputs.F16, rounding_allowance=True,
+            what=f"causal whole grid D={D} {causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nkv", [(100, 300), (300, 100), (1, 777), (513, 64)])
 def test_nq_ne_nkv(gpu_device, nq, nkv, causal):
