@@ -36,7 +36,7 @@ CSRC = os.path.join(ROOT, "memory_efficient_tiled_amd", "csrc")
 SOURCES = {"fwd": ("attn_common.h", "attn_tiles.h", "attn_plan.h", "attn_fwd_kernel.h",
                    "attn_fwd.hip", "attn_fwd_d64.hip", "attn_fwd_d80.hip", "attn_fwd_d96.hip",
                    "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_fwd_d192v128.hip"),
-           "bwd": ("attn_common.h", "attn_tiles.h", "attn_bwd.hip"),
+           "bwd": ("attn_common.h", "attn_tiles.h", "attn_plan.h", "attn_bwd.hip"),
            # the FP8 kernel, and the plan and merge it shares with the 16-bit path
            "fp8": ("attn_common.h", "attn_tiles.h", "attn_plan.h", "attn_fwd_kernel.h",
                    "attn_fwd.hip", "attn_fwd_d128.hip", "attn_fwd_fp8.hip"),

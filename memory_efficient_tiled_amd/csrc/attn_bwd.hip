@@ -34,6 +34,7 @@
 // mask is applied, and only on the tiles that straddle the diagonal.
 
 #include "attn_common.h"
+#include "attn_plan.h"
 
 #include <mutex>
 #include <type_traits>
@@ -66,6 +67,14 @@ struct BwdParams {
   const uint8_t* mask;
   int64_t msb, msh, msq;
   int mask_mode;
+  // dQ launch without a causal mask, when its grid ends in a partial round:
+  // workgroups [0, dq_whole) take whole query tiles 0 .. dq_whole - 1, and
+  // each later tile is cut into dq_splits key ranges of dq_split_len keys,
+  // whose workgroups write unscaled fp32 partial dQ rows (dqp:
+  // [dq_splits][dq_rows][D], row (tile - dq_whole) * 128 + row in tile),
+  // added by attn_dq_reduce.  dq_splits = 1: every tile whole.
+  int dq_whole, dq_splits, dq_split_len, dq_rows;
+  float* dqp;
 };
 
 // Lanes per row of the delta kernel: D / 8 rounded up to a power of two.
@@ -544,7 +553,21 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
 
-  int bid = CAUSAL ? longest_first(blockIdx.x, p.n_tiles, p.total) : xcd_remap(blockIdx.x, p.total);
+  // (a split launch renumbers its whole tiles and its pieces separately, as
+  // the forward does)
+  int bid, sp = 0;
+  bool piece = false;
+  if (!CAUSAL && p.dq_splits > 1 && (int)blockIdx.x >= p.dq_whole) {
+    const int j = xcd_remap(blockIdx.x - p.dq_whole, p.total - p.dq_whole);
+    piece = true;
+    sp = j % p.dq_splits;
+    bid = p.dq_whole + j / p.dq_splits;
+  } else if (!CAUSAL && p.dq_splits > 1) {
+    bid = xcd_remap(blockIdx.x, p.dq_whole);
+  } else {
+    bid = CAUSAL ? longest_first(blockIdx.x, p.n_tiles, p.total) : xcd_remap(blockIdx.x, p.total);
+  }
+  const int tile_id = bid;
   int qt = bid % p.n_tiles;
   bid /= p.n_tiles;
   const int hq = bid % p.Hq;
@@ -555,7 +578,10 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   const int qw0 = q0 + wave * 32;         // the wave's first query row
   const int qrow = qw0 + l32;             // this lane's query (accumulator column)
   const int kend = CAUSAL ? max(0, min(p.Nkv, q0 + BM + p.coff)) : p.Nkv;
-  const int ntiles = (kend + BN - 1) / BN;
+  // key tiles [t0, t1): every tile, or this piece's key range
+  const int t0 = piece ? sp * (p.dq_split_len / BN) : 0;
+  const int t1 = piece ? min((kend + BN - 1) / BN, (sp + 1) * (p.dq_split_len / BN))
+                       : (kend + BN - 1) / BN;
 
   const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
   const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
@@ -647,7 +673,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
     constexpr int buf = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, std::integral_constant<int, buf ^ 1>{});
+    if (t + 1 < t1) issue(t + 1, std::integral_constant<int, buf ^ 1>{});
     f32x16 s = f32x16{}, dp = f32x16{};
     if constexpr (SQ) {
 #pragma unroll
@@ -677,12 +703,45 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
     }
   };
 
-  if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
-  for (int t = 0; t < ntiles; t += 2) {
+  if (t0 < t1) issue(t0, std::integral_constant<int, 0>{});
+  for (int t = t0; t < t1; t += 2) {
     tile(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < t1) tile(t + 1, std::integral_constant<int, 1>{});
   }
-  if (qrow < p.Nq) store_row<D, Tag>(p.dq + (qrow0 + qrow) * D, dq, p.scale, hl);
+  if (qrow >= p.Nq) return;
+  if (!piece) {
+    store_row<D, Tag>(p.dq + (qrow0 + qrow) * D, dq, p.scale, hl);
+    return;
+  }
+  float* const dst =
+      p.dqp + ((size_t)sp * p.dq_rows + (size_t)(tile_id - p.dq_whole) * BM + (qrow - q0)) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = db * 32 + 8 * i + 4 * hl;
+      const f32x16& o = dq[db];
+      if (col < D) *(f32x4*)(dst + col) = f32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+    }
+}
+
+// dQ rows of the split tiles: the sum of the pieces' fp32 partials times
+// the scale, rounded to 16 bits; four elements per thread.
+template <int D, class Tag>
+__global__ __launch_bounds__(256) void attn_dq_reduce(BwdParams p, size_t n4) {
+  using N = Num<Tag>;
+  constexpr int C4 = D / 4;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const size_t r = i / C4;
+  const int c = (int)(i % C4) * 4;
+  const long long tile = p.dq_whole + (long long)(r / 128);
+  const int q = (int)(tile % p.n_tiles) * 128 + (int)(r % 128);
+  if (q >= p.Nq) return;
+  f32x4 a = *(const f32x4*)(p.dqp + r * D + c);
+  for (int s = 1; s < p.dq_splits; ++s) a += *(const f32x4*)(p.dqp + ((size_t)s * p.dq_rows + r) * D + c);
+  const u32x2 y = {N::pack2(a[0] * p.scale, a[1] * p.scale), N::pack2(a[2] * p.scale, a[3] * p.scale)};
+  *(u32x2*)(p.dq + ((size_t)(tile / p.n_tiles) * p.Nq + q) * D + c) = y;
 }
 
 // ---------------------------------------------------------------------------
@@ -818,7 +877,8 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st, SideStream* side
   }
   BwdParams pq = p;
   pq.n_tiles = (p.Nq + 127) / 128;
-  pq.total = p.B * p.Hq * pq.n_tiles;
+  pq.total = p.dq_splits > 1 ? p.dq_whole + (p.B * p.Hq * pq.n_tiles - p.dq_whole) * p.dq_splits
+                             : p.B * p.Hq * pq.n_tiles;
   auto launch_dq = [&]() {
     if (causal)
       hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, true, MASKED>), dim3(pq.total), dim3(256),
@@ -826,7 +886,14 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st, SideStream* side
     else
       hipLaunchKernelGGL((attn_dq_kernel<D, DV, Tag, false, MASKED>), dim3(pq.total), dim3(256),
                          0, sq, pq);
-    return hipGetLastError();
+    hipError_t e2 = hipGetLastError();
+    if (e2 == hipSuccess && p.dq_splits > 1) {
+      const size_t n4 = (size_t)p.dq_rows * (D / 4);
+      hipLaunchKernelGGL((attn_dq_reduce<D, Tag>), dim3((unsigned)((n4 + 255) / 256)), dim3(256),
+                         0, sq, pq, n4);
+      e2 = hipGetLastError();
+    }
+    return e2;
   };
   if (kFork) {
     e = launch_dq();
@@ -901,6 +968,27 @@ int run_bwd(const void* q, const void* k, const void* v, const void* out, const 
   const long long kgrid = (long long)B * Hkv * hsplit * ((Nkv + 127) / 128);
   const long long qgrid = (long long)B * Hq * ((Nq + 127) / 128);
   if (kgrid > INT32_MAX || qgrid > INT32_MAX) return ATTN_EINVAL;
+  // dQ without a causal mask: the tiles of a last, partial round of
+  // workgroups are cut into key ranges (the forward's cost model), so they
+  // finish in a fraction of a round.  Two dQ workgroups per CU (one at
+  // D = 256).
+  int dq_whole = 0, dq_splits = 1, dq_len = 0, dq_rows = 0;
+  if (!causal) {
+    const long long slots = (long long)(D == 256 ? 1 : 2) * cus;
+    const long long rem = qgrid % slots;
+    const int ktiles = (Nkv + 31) / 32;
+    if (rem > 0 && qgrid > rem) {
+      int S = attn_planner::balanced_splits(rem, slots, ktiles, 1.0);
+      const int tps = (ktiles + S - 1) / S;
+      S = (ktiles + tps - 1) / tps;
+      if (S > 1 && qgrid + rem * (S - 1) <= INT32_MAX) {
+        dq_splits = S;
+        dq_len = tps * 32;
+        dq_whole = (int)(qgrid - rem);
+        dq_rows = (int)rem * 128;
+      }
+    }
+  }
 
   // workspace: Delta and lse2 per query row, then (split) the fp32 partials
   hipStream_t st = (hipStream_t)stream;
@@ -909,7 +997,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* out, const 
   const size_t rows_bytes = (rows * sizeof(float) + 255) / 256 * 256;
   const size_t part = hsplit > 1 ? (size_t)hsplit * B * Hkv * Nkv * D * sizeof(float) : 0;
   const size_t partv = hsplit > 1 ? (size_t)hsplit * B * Hkv * Nkv * Dv * sizeof(float) : 0;
-  hipError_t e = attn_host::workspace_alloc(&ws, 2 * rows_bytes + part + partv, st);
+  const size_t partq = (size_t)dq_splits * dq_rows * D * sizeof(float);  // 0 unless split
+  hipError_t e = attn_host::workspace_alloc(&ws, 2 * rows_bytes + part + partv + partq, st);
   if (e != hipSuccess || !ws) {
     attn_host::set_last_hip_error((int)e);
     (void)hipGetLastError();
@@ -927,6 +1016,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* out, const 
   p.dkp = hsplit > 1 ? (float*)((char*)ws + 2 * rows_bytes) : nullptr;
   p.dvp = hsplit > 1 ? (float*)((char*)ws + 2 * rows_bytes + part) : nullptr;
   p.hsplit = hsplit;
+  p.dq_whole = dq_whole;
+  p.dq_splits = dq_splits;
+  p.dq_split_len = dq_len;
+  p.dq_rows = dq_rows;
+  p.dqp = dq_splits > 1 ? (float*)((char*)ws + 2 * rows_bytes + part + partv) : nullptr;
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;

@@ -182,6 +182,33 @@ def test_short_sequences(gpu_device, n):
     run_case(gpu_device, 1, 2, 2, n, n, 64, inputs.BF16, False, seed=45 + n)
 
 
+@pytest.mark.parametrize("D,dtype", [(128, inputs.BF16), (64, inputs.F16)])
+def test_dq_last_round_split(gpu_device, D, dtype):
+    """33 heads x 16 query tiles of 128 rows = 528 dQ workgroups on 512
+    slots (256 CUs x 2): the 16 tiles of the last, partial round are cut
+    into 8 key ranges of 128 keys, whose fp32 partials the reduce kernel
+    adds.  Element-wise parity of dQ, dK and dV; the workspace pool's peak
+    holds the partials (8 x 16 x 128 rows x D fp32) besides Delta and the
+    base-2 LSE."""
+    import torch
+    from tests.parity import PoolPeak
+    B, H, Nq, Nkv = 1, 33, 2000, 1024
+    run_case(gpu_device, B, H, H, Nq, Nkv, D, dtype, False, seed=60 + D)
+    x = inputs.make_inputs(B, H, H, Nq, Nkv, D, dtype, seed=61)
+    do = inputs.make_dout(x)
+    q, k, v, g = (to_device(a, dtype, gpu_device) for a in (x.q, x.k, x.v, do))
+    out, lse = binding.attn_fwd(q, k, v)
+    binding.attn_bwd(q, k, v, out, lse, g)
+    torch.cuda.synchronize(gpu_device)
+    pool = PoolPeak(gpu_device.index or 0)
+    pool.reset()
+    binding.attn_bwd(q, k, v, out, lse, g)
+    torch.cuda.synchronize(gpu_device)
+    rows_bytes = (B * H * Nq * 4 + 255) // 256 * 256
+    partials = 8 * 16 * 128 * D * 4
+    assert pool.read() >= 2 * rows_bytes + partials
+
+
 def test_long_d128_several_tiles(gpu_device):
     run_case(gpu_device, 1, 4, 4, 1500, 1500, 128, inputs.BF16, False, seed=46)
 
