@@ -374,8 +374,12 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Nq, int Nkv, int D,
  *            must not overlap each other or any input.
  * All pointers 16-byte aligned; D in {64, 80, 96, 128, 256}; Hq a multiple
  * of Hkv.
- * Allocates a float32 [B,Hq,Nq] workspace (Delta) stream-ordered on `stream`
- * from the library's pool (attn_workspace_pool) and frees it there.  dQ runs
+ * Allocates its workspace stream-ordered on `stream` from the library's
+ * pool (attn_workspace_pool) and frees it there: Delta and the base-2 LSE
+ * (float32 [B,Hq,Nq] each), fp32 dK/dV partials when the query heads of a
+ * GQA group are split over workgroups, and fp32 dQ partials when the dQ
+ * grid (without a causal mask) ends in a partial round of workgroups whose
+ * key ranges are split -- all O(N * D).  dQ runs
  * on a second stream of the library's, forked from `stream` after Delta and
  * joined back before the call returns (except at D = 128); the caller sees
  * ordinary stream order on `stream`.  Returns ATTN_OK, ATTN_EINVAL,
