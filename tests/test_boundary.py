@@ -143,6 +143,21 @@ def test_split_heuristic():
         plan(1, 3, 2, 10, 10, 64, 0)
 
 
+def test_causal_split_choice():
+    """A causal grid smaller than the device is cut over key ranges only when
+    the pieces save more than the split path costs (values measured on
+    MI355X: causal GQA 14/2 at 4096 tokens runs 54-58 us whole, 78-108 us
+    in 2-8 pieces; one head of 16384 tokens at D = 128 358 us whole,
+    126-135 us in 4 pieces; 4 heads x 2048 at D = 128 57 us whole, 38-45 us
+    in 2-8; 16 heads x 1024 at D = 64 18 us whole, 38-44 us in 2-16)."""
+    assert plan(1, 14, 2, 4096, 4096, 64, 1, F16).num_splits == 1
+    assert plan(1, 16, 16, 1024, 1024, 64, 1, F16).num_splits == 1
+    assert plan(1, 1, 1, 16384, 16384, 128, 1).num_splits == 4
+    assert plan(1, 4, 4, 2048, 2048, 128, 1).num_splits == 8
+    # grids of at least two tiles per slot never split
+    assert plan(1, 14, 2, 8192, 8192, 64, 1, F16).num_splits == 1
+
+
 def test_gqa_packing_plans():
     """Short query ranges of a GQA group are packed into one row range of
     the KV head.  Decode over 64K keys with 16 query heads on 2 KV heads:
