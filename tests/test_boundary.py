@@ -154,7 +154,7 @@ def test_causal_split_choice():
     assert plan(1, 16, 16, 1024, 1024, 64, 1, F16).num_splits == 1
     assert plan(1, 1, 1, 16384, 16384, 128, 1).num_splits == 4
     assert plan(1, 4, 4, 2048, 2048, 128, 1).num_splits == 8
-    # grids of at least two tiles per slot never split
+    # grids that fill every slot are balanced by their longest-first order
     assert plan(1, 14, 2, 8192, 8192, 64, 1, F16).num_splits == 1
 
 
