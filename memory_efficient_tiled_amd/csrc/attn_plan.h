@@ -223,6 +223,15 @@ inline int balanced_splits(long long rem, long long slots, int ktiles, double ro
 constexpr double kChipFlopsPerUs = 1.0e9;
 constexpr double kSplitFixedUs = 30.0;
 constexpr double kMergeBytesPerUs = 3.0e6;
+// A non-causal grid smaller than the device: an eager call that splits
+// costs at least kSplitFloorUs (38-45 us measured over such shapes, pieces
+// of 4-16 key steps included), so a grid that runs whole in less never
+// splits.  Its workgroups, fewer than the CUs, run their key steps at
+// about kLoneStepFactor of the shared-CU time (e.g. one
+// head of 1000 tokens at D = 64: 18 us whole, 42-47 us in 2-8 pieces; four
+// heads of 1000 x 3000: 32 us whole, 43-45 us in 2-16).
+constexpr double kSplitFloorUs = 40.0;
+constexpr double kLoneStepFactor = 0.6;
 
 inline int causal_splits(long long bh, int n_qtiles, int BM, int BN, int D, int Dv, int Nq,
                          int Nkv, int coff, long long slots, int ktiles) {
@@ -277,6 +286,10 @@ inline Plan make_plan(int B, int Hq, int Nq, int Nkv, int D, int Dv, int causal,
     const long long rem = pl.tiles % slots;
     first = pl.tiles - rem;
     S = rem ? balanced_splits(rem, slots, ktiles, std::min(1.0, (double)Nq / c.BM())) : 1;
+    if (S > 1 && first == 0) {
+      const double step_us = 2.0 * c.BM() * c.BN * (double)(D + Dv) * slots / kChipFlopsPerUs;
+      if ((ktiles + kPieceFillSteps) * step_us * kLoneStepFactor < kSplitFloorUs) S = 1;
+    }
   }
   if (S > ktiles) S = ktiles;
   const int tps = (ktiles + S - 1) / S;

@@ -158,6 +158,18 @@ def test_causal_split_choice():
     assert plan(1, 14, 2, 8192, 8192, 64, 1, F16).num_splits == 1
 
 
+def test_small_grid_split_floor():
+    """A non-causal grid smaller than the device that runs whole in less than
+    an eager split call costs is not split (measured on MI355X: one head of
+    1000 tokens at D = 64 18 us whole, 42-52 us in 2-8 pieces; four heads of
+    1000 x 3000 32 us whole, 42-48 us in 2-16), while longer key ranges still
+    are (two heads of 2048 at D = 128: 55 us whole, 41-46 us in 2-16)."""
+    assert plan(1, 1, 1, 1000, 1000, 64, 0, F16).num_splits == 1
+    assert plan(1, 4, 4, 1000, 3000, 64, 0, F16).num_splits == 1
+    assert plan(1, 2, 2, 2048, 2048, 128, 0).num_splits >= 2
+    assert plan(1, 8, 8, 512, 8192, 128, 0).num_splits >= 8
+
+
 def test_gqa_packing_plans():
     """Short query ranges of a GQA group are packed into one row range of
     the KV head.  Decode over 64K keys with 16 query heads on 2 KV heads:
