@@ -147,6 +147,35 @@ __device__ __forceinline__ void copy_tile(const uint16_t* base, int r0, int rows
     if (wave + NW * j < C::NI) buf2lds16(r, dst + (wave + NW * j) * 512, off[j]);
 }
 
+// s_waitcnt immediate that waits for lgkmcnt 0 only (vmcnt 63 and expcnt 7
+// are the no-wait values: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Buffer B (0 or 1) of a double-buffered LDS tile of N elements.  With SEP
+// each buffer is an LDS variable of its own (b0, b1): the compiler then
+// sees that a copy still in flight into one buffer cannot alias reads of
+// the other, and does not wait for the next tile's copies before the
+// current tile's reads.  Without SEP both buffers are halves of b0 and it
+// must wait; head dimensions 256 and the (192, 128) pair keep that form,
+// whose kernels spill more registers when the compiler may move LDS reads
+// above the copies.
+template <int B, bool SEP, int N, class T>
+__device__ __forceinline__ T* buf_at(T* b0, T* b1) {
+  if constexpr (!SEP) return b0 + B * N;
+  else if constexpr (B == 0) return b0;
+  else return b1;
+}
+constexpr bool bwd_sep_buffers(int D, int DV) { return D != 256 && D == DV; }
+
+// The Q (g = 0) or dO (g = 1) tile of buffer B when both are staged per
+// buffer: with SEP buffer B's variable holds [Q | dO], else one variable
+// holds [Q0 | Q1 | dO0 | dO1] (TQ, TG: elements of a Q and a dO tile).
+template <int B, bool SEP, int TQ, int TG, class T>
+__device__ __forceinline__ T* qg_tile(T* b0, T* b1, int g) {
+  if constexpr (SEP) return (B == 0 ? b0 : b1) + g * TQ;
+  else return b0 + (g ? 2 * TQ + B * TG : B * TQ);
+}
+
 // A operand read along rows (16 bytes: chunk 2 kc + hl of row `row`).
 template <int D>
 __device__ __forceinline__ u32x4 read_rows(const uint16_t* t, int row, int kc, int hl) {
@@ -253,15 +282,17 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   constexpr int IPWV = TileCopy<DV, BQ, NW>::PER_WAVE;
   using N = Num<Tag>;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t qr[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t qt[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t gr[2][TILEV];
-  __shared__ __attribute__((aligned(1024))) uint16_t gt[2][TILEV];
+  // per buffer: Q then dO tiles read along rows (rows) and transposed
+  // (cols); a wave picks its tile by an offset within the buffer
+  constexpr bool SEP = bwd_sep_buffers(D, DV);
+  constexpr int TQG = TILE + TILEV;
+  __shared__ __attribute__((aligned(1024))) uint16_t rows0[SEP ? TQG : 2 * TQG], rows1[SEP ? TQG : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t cols0[SEP ? TQG : 2 * TQG], cols1[SEP ? TQG : 1];
   __shared__ __attribute__((aligned(1024))) u32x4 xp[4][NKC][64];
   // lse2 and Delta of a tile: one dword per lane of a 64-lane copy (lanes
   // past the tile's rows write zeros), so 64 entries even when BQ = 32
-  __shared__ __attribute__((aligned(256))) float lse_s[2][64];
-  __shared__ __attribute__((aligned(256))) float del_s[2][64];
+  // (lse2 at 0, Delta at 64 of each buffer)
+  __shared__ __attribute__((aligned(256))) float ld0[SEP ? 128 : 256], ld1[SEP ? 128 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -323,14 +354,20 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
     const uint16_t* qb = p.q + qrow0 * D;
     const uint16_t* gb = p.dout + qrow0 * DV;
-    copy_tile<D, BQ, NW>(qb, q0, p.Nq, qr[buf], wave, roff);
-    copy_tile<D, BQ, NW>(qb, q0, p.Nq, qt[buf], wave, toff);
+    copy_tile<D, BQ, NW>(qb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 0), wave,
+                         roff);
+    copy_tile<D, BQ, NW>(qb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 0), wave,
+                         toff);
     if constexpr (SQ) {
-      copy_tile<D, BQ, NW>(gb, q0, p.Nq, gr[buf], wave, roff);
-      copy_tile<D, BQ, NW>(gb, q0, p.Nq, gt[buf], wave, toff);
+      copy_tile<D, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 1), wave,
+                           roff);
+      copy_tile<D, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 1), wave,
+                           toff);
     } else {
-      copy_tile<DV, BQ, NW>(gb, q0, p.Nq, gr[buf], wave, groff);
-      copy_tile<DV, BQ, NW>(gb, q0, p.Nq, gt[buf], wave, gtoff);
+      copy_tile<DV, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 1), wave,
+                            groff);
+      copy_tile<DV, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 1), wave,
+                            gtoff);
     }
     if (wave < 2) {  // lse2 (wave 0) and Delta (wave 1): one dword per lane
       const float* src = (wave == 0 ? p.lse2 : p.delta) + qrow0 + q0;
@@ -338,8 +375,8 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 4, kRawBufferFlags);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(wave == 0 ? lse_s[buf] : del_s[buf]), 4,
-          lane * 4, 0, 0, 0);
+          r, (__attribute__((address_space(3))) void*)(buf_at<buf, SEP, 128>(ld0, ld1) + wave * 64),
+          4, lane * 4, 0, 0, 0);
     }
   };
 
@@ -376,7 +413,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = qb * 32 + 8 * j + 4 * hl;
-        const f32x4 ls = *(const f32x4*)(&lse_s[buf][r]);
+        const f32x4 ls = *(const f32x4*)(buf_at<buf, SEP, 128>(ld0, ld1) + r);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float pv;
@@ -431,11 +468,13 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     };
     if constexpr (SQ)
       prod1(std::integral_constant<int, DC>{}, std::integral_constant<int, DP>{},
-            pw ? qr[buf] : gr[buf]);
+            qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, pw ? 0 : 1));
     else if (pw)
-      prod1(std::integral_constant<int, DC>{}, std::integral_constant<int, DP>{}, qr[buf]);
+      prod1(std::integral_constant<int, DC>{}, std::integral_constant<int, DP>{},
+            qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 0));
     else
-      prod1(std::integral_constant<int, DCV>{}, std::integral_constant<int, DVP>{}, gr[buf]);
+      prod1(std::integral_constant<int, DCV>{}, std::integral_constant<int, DVP>{},
+            qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 1));
     u32x4 bop[NKC];
     if (pw) {
       if (CAUSAL && kw0 + 31 > q0 + p.coff)
@@ -447,7 +486,19 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) xp[kw][kc][lane] = bop[kc];
     }
-    __syncthreads();
+    // P is in LDS for the partner wave: this wave's LDS stores are done
+    // (lgkmcnt 0), then the barrier.  Not __syncthreads, whose fence would
+    // also wait for the next tile's copies still in flight into the other
+    // buffers; the empty asm statements keep the compiler from moving LDS
+    // accesses across the barrier.
+    if constexpr (SEP) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      __syncthreads();
+    }
     if (!pw) {
       // dS = P (dP - Delta) from the partner's P
 #pragma unroll
@@ -458,7 +509,8 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * hf + jj;
-            const f32x4 dl = *(const f32x4*)(&del_s[buf][qb * 32 + 8 * j + 4 * hl]);
+            const f32x4 dl =
+                *(const f32x4*)(buf_at<buf, SEP, 128>(ld0, ld1) + 64 + qb * 32 + 8 * j + 4 * hl);
             const float pv[4] = {lo_f32<Tag>(w[2 * jj]), hi_f32<Tag>(w[2 * jj]),
                                  lo_f32<Tag>(w[2 * jj + 1]), hi_f32<Tag>(w[2 * jj + 1])};
 #pragma unroll
@@ -482,13 +534,13 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     };
     if constexpr (SQ)
       prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{},
-            pw ? gt[buf] : qt[buf], v_sw);
+            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, pw ? 1 : 0), v_sw);
     else if (pw)
-      prod2(std::integral_constant<int, NDBV>{}, std::integral_constant<int, DVP>{}, gt[buf],
-            v_swv);
+      prod2(std::integral_constant<int, NDBV>{}, std::integral_constant<int, DVP>{},
+            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 1), v_swv);
     else
-      prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{}, qt[buf],
-            v_sw);
+      prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{},
+            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 0), v_sw);
   };
 
   if (steps > 0) issue(0, std::integral_constant<int, 0>{});
@@ -545,9 +597,10 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   constexpr int IPWV = TileCopy<DV, BN, NW>::PER_WAVE;
   using N = Num<Tag>;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t kr[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ktr[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t vr[2][TILEV];
+  constexpr bool SEP = bwd_sep_buffers(D, DV);
+  __shared__ __attribute__((aligned(1024))) uint16_t kr0[SEP ? TILE : 2 * TILE], kr1[SEP ? TILE : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t ktr0[SEP ? TILE : 2 * TILE], ktr1[SEP ? TILE : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t vr0[SEP ? TILEV : 2 * TILEV], vr1[SEP ? TILEV : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -627,12 +680,12 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   const uint16_t* Vg = p.v + krow0 * DV;
   auto issue = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, kr[buf], wave, roff);
-    copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, ktr[buf], wave, toff);
+    copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, buf_at<buf, SEP, TILE>(kr0, kr1), wave, roff);
+    copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, buf_at<buf, SEP, TILE>(ktr0, ktr1), wave, toff);
     if constexpr (SQ)
-      copy_tile<D, BN, NW>(Vg, t * BN, p.Nkv, vr[buf], wave, roff);
+      copy_tile<D, BN, NW>(Vg, t * BN, p.Nkv, buf_at<buf, SEP, TILEV>(vr0, vr1), wave, roff);
     else
-      copy_tile<DV, BN, NW>(Vg, t * BN, p.Nkv, vr[buf], wave, vroff);
+      copy_tile<DV, BN, NW>(Vg, t * BN, p.Nkv, buf_at<buf, SEP, TILEV>(vr0, vr1), wave, vroff);
   };
 
   const int v_g = lane >> 4, v_r = lane & 15;
@@ -675,18 +728,20 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
     __syncthreads();
     if (t + 1 < t1) issue(t + 1, std::integral_constant<int, buf ^ 1>{});
     f32x16 s = f32x16{}, dp = f32x16{};
+    const uint16_t* kb = buf_at<buf, SEP, TILE>(kr0, kr1);
+    const uint16_t* vb = buf_at<buf, SEP, TILEV>(vr0, vr1);
     if constexpr (SQ) {
 #pragma unroll
       for (int kc = 0; kc < DC; ++kc) {
-        s = N::mfma(read_rows<DP>(kr[buf], l32, kc, hl), qf[kc], s);
-        dp = N::mfma(read_rows<DP>(vr[buf], l32, kc, hl), gf[kc < DCV ? kc : 0], dp);
+        s = N::mfma(read_rows<DP>(kb, l32, kc, hl), qf[kc], s);
+        dp = N::mfma(read_rows<DP>(vb, l32, kc, hl), gf[kc < DCV ? kc : 0], dp);
       }
     } else {
 #pragma unroll
-      for (int kc = 0; kc < DC; ++kc) s = N::mfma(read_rows<DP>(kr[buf], l32, kc, hl), qf[kc], s);
+      for (int kc = 0; kc < DC; ++kc) s = N::mfma(read_rows<DP>(kb, l32, kc, hl), qf[kc], s);
 #pragma unroll
       for (int kc = 0; kc < DCV; ++kc)
-        dp = N::mfma(read_rows<DVP>(vr[buf], l32, kc, hl), gf[kc], dp);
+        dp = N::mfma(read_rows<DVP>(vb, l32, kc, hl), gf[kc], dp);
     }
     if (CAUSAL && t * BN + 31 > qw0 + p.coff)
       probs(std::true_type{}, s, dp, t);
@@ -699,7 +754,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
       const int row = kc * 16 + v_key;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dq[db] = N::mfma(read_cols<DP>(ktr[buf], row, db, v_d, v_sw), ps[kc], dq[db]);
+        dq[db] = N::mfma(read_cols<DP>(buf_at<buf, SEP, TILE>(ktr0, ktr1), row, db, v_d, v_sw), ps[kc],
+                         dq[db]);
     }
   };
 
