@@ -121,14 +121,42 @@ struct TileCopy {
   static_assert(NI * 64 == ROWS * CPR, "tile copy shape");
 };
 
-template <int D, int ROWS, int NW, bool ROWREAD>
+// How a staged tile is read: along rows (16-byte reads, k_swz), transposed
+// (ds_read_b64_tr_b16, v_swz), or both from one copy (u_swz).
+enum { kReadRows = 0, kReadCols = 1, kReadBoth = 2 };
+
+// One LDS layout that serves both reads without bank conflicts, for rows
+// of 128 bytes (D = 64) and 256 bytes (D = 128): the 16-byte chunk index is
+// XORed with a permutation of row bits.  Row reads (16 lanes, 16
+// consecutive rows, one chunk) need distinct bank groups over any 16
+// consecutive rows; transposing reads (32 lanes, 4 consecutive rows x 64
+// bytes) need those 4 rows in disjoint 64-byte quarters of the banks.  At
+// D = 128 rows r & 3 pick the quarter (XOR bits 3:2) and (r >> 2) & 3 the
+// chunk within it (bits 1:0); at D = 64, where rows r and r + 1 share the
+// banks, (r >> 1) & 1 picks the quarter within the half-row and
+// (r >> 2) & 3 the chunk.
+template <int D>
+constexpr bool has_both_swz() { return D == 64 || D == 128; }
+template <int D>
+__device__ __forceinline__ int u_swz(int r) {
+  static_assert(has_both_swz<D>(), "one-copy layout only at D = 64 and 128");
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+template <int D, int RD>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (RD == kReadRows) return k_swz<D>(r);
+  else if constexpr (RD == kReadCols) return v_swz<D>(r);
+  else return u_swz<D>(r);
+}
+
+template <int D, int ROWS, int NW, int RD>
 __device__ __forceinline__ void copy_offsets(int wave, int lane, uint32_t* off) {
   using C = TileCopy<D, ROWS, NW>;
 #pragma unroll
   for (int j = 0; j < C::PER_WAVE; ++j) {
     const int slot = (wave + NW * j) * 64 + lane;
     const int row = slot / C::CPR, pc = slot % C::CPR;
-    const int ch = pc ^ (ROWREAD ? k_swz<C::DP>(row) : v_swz<C::DP>(row));
+    const int ch = pc ^ tile_swz<C::DP, RD>(row);
     off[j] = ch < D / 8 ? row * D * 2 + (ch << 4) : kPadOffset;
   }
 }
@@ -176,21 +204,22 @@ __device__ __forceinline__ T* qg_tile(T* b0, T* b1, int g) {
   else return b0 + (g ? 2 * TQ + B * TG : B * TQ);
 }
 
-// A operand read along rows (16 bytes: chunk 2 kc + hl of row `row`).
-template <int D>
+// A operand read along rows (16 bytes: chunk 2 kc + hl of row `row`) of a
+// tile staged for reads RD (kReadRows or kReadBoth).
+template <int D, int RD = kReadRows>
 __device__ __forceinline__ u32x4 read_rows(const uint16_t* t, int row, int kc, int hl) {
-  return *(const u32x4*)(t + row * D + (((2 * kc + hl) ^ k_swz<D>(row)) << 3));
+  return *(const u32x4*)(t + row * D + (((2 * kc + hl) ^ tile_swz<D, RD>(row)) << 3));
 }
 
 // A operand read transposed: 8 consecutive rows (in the accumulator's
-// interleaving) of columns db*32 + v_d .. + 3, rows from `row` and row + 8.
+// interleaving) of columns db*32 + v_d .. + 3, rows from `row` (swizzle
+// sw_lo) and row + 8 (sw_hi; the two differ only for kReadBoth tiles).
 template <int D>
 __device__ __forceinline__ u32x4 read_cols(const uint16_t* t, int row, int db, int v_d,
-                                           int v_sw) {
+                                           int sw_lo, int sw_hi) {
   const int d = db * 32 + v_d;
-  const int off = (((d >> 3) ^ v_sw) << 3) + (d & 7);
-  const u32x2 lo = lds_read_tr16(t + row * D + off);
-  const u32x2 hi = lds_read_tr16(t + (row + 8) * D + off);
+  const u32x2 lo = lds_read_tr16(t + row * D + (((d >> 3) ^ sw_lo) << 3) + (d & 7));
+  const u32x2 hi = lds_read_tr16(t + (row + 8) * D + (((d >> 3) ^ sw_hi) << 3) + (d & 7));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -283,11 +312,15 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   using N = Num<Tag>;
 
   // per buffer: Q then dO tiles read along rows (rows) and transposed
-  // (cols); a wave picks its tile by an offset within the buffer
+  // (cols); a wave picks its tile by an offset within the buffer.  With
+  // UNI one copy in the layout of both reads (rows) serves both.
   constexpr bool SEP = bwd_sep_buffers(D, DV);
+  constexpr bool UNI = SEP && has_both_swz<D>();
+  constexpr int RDR = UNI ? kReadBoth : kReadRows;
   constexpr int TQG = TILE + TILEV;
   __shared__ __attribute__((aligned(1024))) uint16_t rows0[SEP ? TQG : 2 * TQG], rows1[SEP ? TQG : 1];
-  __shared__ __attribute__((aligned(1024))) uint16_t cols0[SEP ? TQG : 2 * TQG], cols1[SEP ? TQG : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t cols0[UNI ? 1 : SEP ? TQG : 2 * TQG],
+      cols1[SEP && !UNI ? TQG : 1];
   __shared__ __attribute__((aligned(1024))) u32x4 xp[4][NKC][64];
   // lse2 and Delta of a tile: one dword per lane of a 64-lane copy (lanes
   // past the tile's rows write zeros), so 64 entries even when BQ = 32
@@ -330,12 +363,12 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   for (int i = 0; i < NDBM; ++i) acc[i] = f32x16{};
 
   // copy offsets of the Q tiles and (DV != D) of the dO tiles
-  uint32_t roff[IPW], toff[IPW], groff[SQ ? 1 : IPWV], gtoff[SQ ? 1 : IPWV];
-  copy_offsets<D, BQ, NW, true>(wave, lane, roff);
-  copy_offsets<D, BQ, NW, false>(wave, lane, toff);
+  uint32_t roff[IPW], toff[UNI ? 1 : IPW], groff[SQ ? 1 : IPWV], gtoff[SQ ? 1 : IPWV];
+  copy_offsets<D, BQ, NW, RDR>(wave, lane, roff);
+  if constexpr (!UNI) copy_offsets<D, BQ, NW, kReadCols>(wave, lane, toff);
   if constexpr (!SQ) {
-    copy_offsets<DV, BQ, NW, true>(wave, lane, groff);
-    copy_offsets<DV, BQ, NW, false>(wave, lane, gtoff);
+    copy_offsets<DV, BQ, NW, kReadRows>(wave, lane, groff);
+    copy_offsets<DV, BQ, NW, kReadCols>(wave, lane, gtoff);
   }
 
   const int nqt = (p.Nq + BQ - 1) / BQ;
@@ -356,13 +389,15 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
     const uint16_t* gb = p.dout + qrow0 * DV;
     copy_tile<D, BQ, NW>(qb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 0), wave,
                          roff);
-    copy_tile<D, BQ, NW>(qb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 0), wave,
-                         toff);
+    if constexpr (!UNI)
+      copy_tile<D, BQ, NW>(qb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 0), wave,
+                           toff);
     if constexpr (SQ) {
       copy_tile<D, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 1), wave,
                            roff);
-      copy_tile<D, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 1), wave,
-                           toff);
+      if constexpr (!UNI)
+        copy_tile<D, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 1), wave,
+                             toff);
     } else {
       copy_tile<DV, BQ, NW>(gb, q0, p.Nq, qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, 1), wave,
                             groff);
@@ -383,7 +418,9 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
-  const int v_sw = v_swz<DP>(v_key);
+  // swizzles of the transposed reads' rows v_key (+ 16 kc) and v_key + 8
+  const int v_sw = UNI ? u_swz<UNI ? DP : 64>(v_key) : v_swz<DP>(v_key);
+  const int v_sw8 = UNI ? u_swz<UNI ? DP : 64>(v_key + 8) : v_sw;
   const int v_swv = v_swz<DVP>(v_key);
 
   // P in place of S (P waves); accumulator register e of block qb is query
@@ -463,7 +500,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
         s[qb] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < DCX; ++kc)
-          s[qb] = N::mfma(read_rows<RW>(ra, qb * 32 + l32, kc, hl), bf[kc], s[qb]);
+          s[qb] = N::mfma(read_rows<RW, RDR>(ra, qb * 32 + l32, kc, hl), bf[kc], s[qb]);
       }
     };
     if constexpr (SQ)
@@ -522,25 +559,28 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
       }
     }
     // 2. dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves)
-    auto prod2 = [&](auto ndc, auto rwc, const uint16_t* rb, int sw) {
+    auto prod2 = [&](auto ndc, auto rwc, const uint16_t* rb, int sw, int sw8) {
       constexpr int NDX = decltype(ndc)::value, RW = decltype(rwc)::value;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const int row = kc * 16 + v_key;
 #pragma unroll
         for (int db = 0; db < NDX; ++db)
-          acc[db] = N::mfma(read_cols<RW>(rb, row, db, v_d, sw), bop[kc], acc[db]);
+          acc[db] = N::mfma(read_cols<RW>(rb, row, db, v_d, sw, sw8), bop[kc], acc[db]);
       }
     };
-    if constexpr (SQ)
+    if constexpr (UNI)
       prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{},
-            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, pw ? 1 : 0), v_sw);
+            qg_tile<buf, SEP, TILE, TILEV>(rows0, rows1, pw ? 1 : 0), v_sw, v_sw8);
+    else if constexpr (SQ)
+      prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{},
+            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, pw ? 1 : 0), v_sw, v_sw);
     else if (pw)
       prod2(std::integral_constant<int, NDBV>{}, std::integral_constant<int, DVP>{},
-            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 1), v_swv);
+            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 1), v_swv, v_swv);
     else
       prod2(std::integral_constant<int, NDB>{}, std::integral_constant<int, DP>{},
-            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 0), v_sw);
+            qg_tile<buf, SEP, TILE, TILEV>(cols0, cols1, 0), v_sw, v_sw);
   };
 
   if (steps > 0) issue(0, std::integral_constant<int, 0>{});
@@ -597,9 +637,14 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   constexpr int IPWV = TileCopy<DV, BN, NW>::PER_WAVE;
   using N = Num<Tag>;
 
+  // With UNI one copy of K in the layout of both reads (kr) serves the row
+  // reads of S and the transposed reads of dQ, and V shares that layout.
   constexpr bool SEP = bwd_sep_buffers(D, DV);
+  constexpr bool UNI = SEP && has_both_swz<D>();
+  constexpr int RDR = UNI ? kReadBoth : kReadRows;
   __shared__ __attribute__((aligned(1024))) uint16_t kr0[SEP ? TILE : 2 * TILE], kr1[SEP ? TILE : 1];
-  __shared__ __attribute__((aligned(1024))) uint16_t ktr0[SEP ? TILE : 2 * TILE], ktr1[SEP ? TILE : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t ktr0[UNI ? 1 : SEP ? TILE : 2 * TILE],
+      ktr1[SEP && !UNI ? TILE : 1];
   __shared__ __attribute__((aligned(1024))) uint16_t vr0[SEP ? TILEV : 2 * TILEV], vr1[SEP ? TILEV : 1];
 
   const int tid = threadIdx.x;
@@ -672,16 +717,17 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
-  uint32_t roff[IPW], toff[IPW], vroff[SQ ? 1 : IPWV];
-  copy_offsets<D, BN, NW, true>(wave, lane, roff);
-  copy_offsets<D, BN, NW, false>(wave, lane, toff);
-  if constexpr (!SQ) copy_offsets<DV, BN, NW, true>(wave, lane, vroff);
+  uint32_t roff[IPW], toff[UNI ? 1 : IPW], vroff[SQ ? 1 : IPWV];
+  copy_offsets<D, BN, NW, RDR>(wave, lane, roff);
+  if constexpr (!UNI) copy_offsets<D, BN, NW, kReadCols>(wave, lane, toff);
+  if constexpr (!SQ) copy_offsets<DV, BN, NW, kReadRows>(wave, lane, vroff);
   const uint16_t* Kg = p.k + krow0 * D;
   const uint16_t* Vg = p.v + krow0 * DV;
   auto issue = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, buf_at<buf, SEP, TILE>(kr0, kr1), wave, roff);
-    copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, buf_at<buf, SEP, TILE>(ktr0, ktr1), wave, toff);
+    if constexpr (!UNI)
+      copy_tile<D, BN, NW>(Kg, t * BN, p.Nkv, buf_at<buf, SEP, TILE>(ktr0, ktr1), wave, toff);
     if constexpr (SQ)
       copy_tile<D, BN, NW>(Vg, t * BN, p.Nkv, buf_at<buf, SEP, TILEV>(vr0, vr1), wave, roff);
     else
@@ -691,7 +737,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
-  const int v_sw = v_swz<DP>(v_key);
+  const int v_sw = UNI ? u_swz<UNI ? DP : 64>(v_key) : v_swz<DP>(v_key);
+  const int v_sw8 = UNI ? u_swz<UNI ? DP : 64>(v_key + 8) : v_sw;
 
   // register e of the score tile is key t*BN + 8 (e / 4) + 4 hl + e % 4.
   // With a mask, its base-2 bias joins the exponent; rows past Nq and rows
@@ -733,8 +780,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
     if constexpr (SQ) {
 #pragma unroll
       for (int kc = 0; kc < DC; ++kc) {
-        s = N::mfma(read_rows<DP>(kb, l32, kc, hl), qf[kc], s);
-        dp = N::mfma(read_rows<DP>(vb, l32, kc, hl), gf[kc < DCV ? kc : 0], dp);
+        s = N::mfma(read_rows<DP, RDR>(kb, l32, kc, hl), qf[kc], s);
+        dp = N::mfma(read_rows<DP, RDR>(vb, l32, kc, hl), gf[kc < DCV ? kc : 0], dp);
       }
     } else {
 #pragma unroll
@@ -754,8 +801,9 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
       const int row = kc * 16 + v_key;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        dq[db] = N::mfma(read_cols<DP>(buf_at<buf, SEP, TILE>(ktr0, ktr1), row, db, v_d, v_sw), ps[kc],
-                         dq[db]);
+        dq[db] = N::mfma(read_cols<DP>(UNI ? kb : buf_at<buf, SEP, TILE>(ktr0, ktr1), row, db,
+                                       v_d, v_sw, v_sw8),
+                         ps[kc], dq[db]);
     }
   };
 
