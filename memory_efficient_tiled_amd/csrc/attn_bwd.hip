@@ -287,8 +287,9 @@ __device__ __forceinline__ void store_kv_grad(const BwdParams& p, uint16_t* dst,
 //      wave w + 4: reads P, dS = P (dP - Delta), dK^T += Q^T dS.
 // Each wave needs half the registers of one that does all four products,
 // so two waves fit on a SIMD and one wave's softmax work overlaps the
-// other's matrix products.  Q and dO tiles are in LDS twice each, two
-// buffers deep, with lse2 and Delta.
+// other's matrix products.  Q and dO tiles are in LDS two buffers deep,
+// with lse2 and Delta: once each in the layout of both reads at D = 64 and
+// 128, else twice each (row-read and transposed layouts).
 //
 // With V rows of DV != D elements (the (192, 128) pair) the two waves of a
 // pair differ: the P wave holds K (D) and accumulates dV^T (DV rows), the
@@ -621,8 +622,9 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce(BwdParams p, size_t n4k,
 //   S^T = K Q^T, dP^T = V dO^T      (rows: 32 keys, columns: 32 queries)
 //   P, dS as above (lse2 and Delta: one value per lane)
 //   dQ^T += K^T dS^T                (rows: D, columns: 32 queries)
-// Q and dO stay in registers; K is copied into LDS twice (row-read and
-// transposed layouts) and V once, two buffers deep, the loop unrolled by two.
+// Q and dO stay in registers; K is copied into LDS once in the layout of
+// both reads at D = 64 and 128, else twice (row-read and transposed
+// layouts), and V once, two buffers deep, the loop unrolled by two.
 // One wave per SIMD at D = 256: Q, dO and the dQ accumulators take 256
 // registers (the (192, 128) pair's 208 still fit two waves).  With V rows
 // of DV != D elements, dO and V tiles are DV wide and dP reduces over DV.
