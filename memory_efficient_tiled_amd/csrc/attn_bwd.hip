@@ -17,9 +17,11 @@
 //  * attn_dkdv_pair_kernel: one workgroup per block of 128 keys of one KV
 //    head, looping over every query tile of the query heads it covers, with
 //    dK and dV accumulated in registers (dV in one wave of a pair, dK in the
-//    other).  When the KV heads alone give too few
-//    workgroups, the query heads of a group are split over several
-//    workgroups that write fp32 partial sums, and attn_dkdv_reduce adds them;
+//    other); at D = 64 without a mask attn_dkdv_solo_kernel instead, where
+//    each wave does all four products for its keys.  When the KV heads alone
+//    give too few workgroups, the query heads of a group are split over
+//    several workgroups that write fp32 partial sums, and attn_dkdv_reduce
+//    adds them;
 //  * attn_dq_kernel: one workgroup per 128 query rows, looping over key tiles
 //    like the forward, with dQ accumulated in registers.
 // The matrix products use the forward's operand layouts (see attn_fwd.hip):
@@ -598,6 +600,178 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   }
 }
 
+// dK, dV with each wave doing all four products for its own 32 keys
+// (D = 64 without a mask; written for D = 128 too, where it spills): 4
+// waves over 128 keys, K and V of the wave's keys in registers.  Per query
+// tile of BQ rows (64 at D = 64; 32 at D = 128, where K, V and the two
+// accumulators take 192 registers):
+//   S = Q K^T and dP = dO V^T (row reads of the Q and dO tiles),
+//   P = exp2(cs S - lse2) (0 above the causal diagonal), dS = P (dP - Delta),
+//   dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the same tiles,
+//   staged once in the layout of both reads).
+// Nothing passes between waves, so a tile needs only the copies' barrier,
+// and the two workgroups on a CU overlap one another's vector and matrix
+// work.
+template <int D, class Tag, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
+  static_assert(has_both_swz<D>(), "one-copy tile layout");
+  constexpr int NW = 4, BK = 128;
+  constexpr int NQB = D == 64 ? 2 : 1, BQ = NQB * 32;
+  constexpr int DC = D / 16, NDB = D / 32, NKC = BQ / 16;
+  constexpr int TILE = BQ * D;
+  constexpr int IPW = TileCopy<D, BQ, NW>::PER_WAVE;
+  using N = Num<Tag>;
+
+  // per buffer: the Q tile, then the dO tile; lse2 at 0 and Delta at 64
+  // (one dword per lane of a 64-lane copy, zeros past the tile's rows)
+  __shared__ __attribute__((aligned(1024))) uint16_t tq0[2 * TILE], tq1[2 * TILE];
+  __shared__ __attribute__((aligned(256))) float ld0[128], ld1[128];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+
+  int bid = CAUSAL ? longest_first(blockIdx.x, p.n_tiles, p.total) : xcd_remap(blockIdx.x, p.total);
+  const int kt = bid % p.n_tiles;
+  bid /= p.n_tiles;
+  const int hs = bid % p.hsplit;
+  bid /= p.hsplit;
+  const int hk = bid % p.Hkv;
+  const int b = bid / p.Hkv;
+  const int k0 = kt * BK;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+  const int hpw = p.G / p.hsplit;
+  const int h0 = hk * p.G + hs * hpw;
+
+  const size_t krow0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  u32x4 kf[DC], vf[DC];
+#pragma unroll
+  for (int kc = 0; kc < DC; ++kc) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key < p.Nkv) {
+      x = *(const u32x4*)(p.k + (krow0 + key) * D + kc * 16 + hl * 8);
+      y = *(const u32x4*)(p.v + (krow0 + key) * D + kc * 16 + hl * 8);
+    }
+    kf[kc] = x;
+    vf[kc] = y;
+  }
+  f32x16 acck[NDB], accv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acck[i] = accv[i] = f32x16{};
+
+  uint32_t roff[IPW];
+  copy_offsets<D, BQ, NW, kReadBoth>(wave, lane, roff);
+
+  const int nqt = (p.Nq + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? min(nqt, max(0, k0 - p.coff) / BQ) : 0;
+  const int per_head = nqt - qt0;
+  const int steps = hpw * per_head;
+
+  auto tile_start = [&](int u, int* hq, int* q0) {
+    *hq = h0 + u / per_head;
+    *q0 = (qt0 + u % per_head) * BQ;
+  };
+  auto issue = [&](int u, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    int hq, q0;
+    tile_start(u, &hq, &q0);
+    const size_t qrow0 = ((size_t)b * p.Hq + hq) * (size_t)p.Nq;
+    uint16_t* const tb = buf_at<buf, true, 0>(tq0, tq1);
+    copy_tile<D, BQ, NW>(p.q + qrow0 * D, q0, p.Nq, tb, wave, roff);
+    copy_tile<D, BQ, NW>(p.dout + qrow0 * D, q0, p.Nq, tb + TILE, wave, roff);
+    if (wave < 2) {  // lse2 (wave 0) and Delta (wave 1)
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + qrow0 + q0;
+      const int n = min(BQ, p.Nq - q0);
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 4, kRawBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(buf_at<buf, true, 0>(ld0, ld1) + wave * 64),
+          4, lane * 4, 0, 0, 0);
+    }
+  };
+
+  const int v_g = lane >> 4, v_r = lane & 15;
+  const int v_key = 4 * hl + (v_r >> 2);
+  const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
+  const int v_sw = u_swz<D>(v_key), v_sw8 = u_swz<D>(v_key + 8);
+
+  // P and dS in place of S and dP; accumulator register e of block qb is
+  // query row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.
+  auto grads = [&](auto mskc, const float* lsb, f32x16* s, f32x16* dp, int q0)
+      __attribute__((always_inline)) {
+    constexpr bool MSK = decltype(mskc)::value;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = qb * 32 + 8 * j + 4 * hl;
+        const f32x4 ls = *(const f32x4*)(lsb + r);
+        const f32x4 dl = *(const f32x4*)(lsb + 64 + r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
+          if (MSK && key > q0 + r + e + p.coff) pv = 0.f;
+          s[qb][4 * j + e] = pv;
+          dp[qb][4 * j + e] = pv * (dp[qb][4 * j + e] - dl[e]);
+        }
+      }
+  };
+
+  auto tile = [&](int u, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (u + 1 < steps) issue(u + 1, std::integral_constant<int, buf ^ 1>{});
+    int hq, q0;
+    tile_start(u, &hq, &q0);
+    const uint16_t* const tq = buf_at<buf, true, 0>(tq0, tq1);
+    const uint16_t* const tg = tq + TILE;
+    f32x16 s[NQB], dp[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      s[qb] = f32x16{};
+      dp[qb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < DC; ++kc) {
+        s[qb] = N::mfma(read_rows<D, kReadBoth>(tq, qb * 32 + l32, kc, hl), kf[kc], s[qb]);
+        dp[qb] = N::mfma(read_rows<D, kReadBoth>(tg, qb * 32 + l32, kc, hl), vf[kc], dp[qb]);
+      }
+    }
+    const float* const lsb = buf_at<buf, true, 0>(ld0, ld1);
+    if (CAUSAL && kw0 + 31 > q0 + p.coff)
+      grads(std::true_type{}, lsb, s, dp, q0);
+    else
+      grads(std::false_type{}, lsb, s, dp, q0);
+    u32x4 bp[NKC], bs[NKC];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      pack_tile<Tag>(s[qb], &bp[qb * 2]);
+      pack_tile<Tag>(dp[qb], &bs[qb * 2]);
+    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int row = kc * 16 + v_key;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        accv[db] = N::mfma(read_cols<D>(tg, row, db, v_d, v_sw, v_sw8), bp[kc], accv[db]);
+        acck[db] = N::mfma(read_cols<D>(tq, row, db, v_d, v_sw, v_sw8), bs[kc], acck[db]);
+      }
+    }
+  };
+
+  if (steps > 0) issue(0, std::integral_constant<int, 0>{});
+  for (int u = 0; u < steps; u += 2) {
+    tile(u, std::integral_constant<int, 0>{});
+    if (u + 1 < steps) tile(u + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (key < p.Nkv) {
+    store_kv_grad<D, Tag>(p, p.dv, p.dvp, accv, 1.f, krow0 + key, hs, hl);
+    store_kv_grad<D, Tag>(p, p.dk, p.dkp, acck, p.scale, krow0 + key, hs, hl);
+  }
+}
+
 // dK, dV = sums of the hsplit partials (dK times scale), rounded to 16 bits;
 // four elements per thread.  n4k (n4v): float4s per partial of dK (dV).
 template <class Tag>
@@ -965,6 +1139,13 @@ hipError_t side_stream(SideStream** out) {
   return hipSuccess;
 }
 
+// The dK/dV kernel: one wave per 32 keys doing all four products where its
+// registers allow (D = 64 without a mask; at D = 128 it spills 124-216
+// bytes per lane and runs 1.5x slower than the wave pairs), else the pairs.
+constexpr bool bwd_solo_dkdv(int D, int DV, bool masked) {
+  return !masked && D == DV && D == 64;
+}
+
 template <int D, int DV, class Tag, bool MASKED>
 hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st, SideStream* side) {
   constexpr bool kFork = D != 128;
@@ -1008,12 +1189,20 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st, SideStream* side
   BwdParams pk = p;
   pk.n_tiles = (p.Nkv + 127) / 128;
   pk.total = p.B * p.Hkv * p.hsplit * pk.n_tiles;
-  if (causal)
+  if constexpr (bwd_solo_dkdv(D, DV, MASKED)) {
+    if (causal)
+      hipLaunchKernelGGL((attn_dkdv_solo_kernel<D, Tag, true>), dim3(pk.total), dim3(256), 0, st,
+                         pk);
+    else
+      hipLaunchKernelGGL((attn_dkdv_solo_kernel<D, Tag, false>), dim3(pk.total), dim3(256), 0,
+                         st, pk);
+  } else if (causal) {
     hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, DV, Tag, true, MASKED>), dim3(pk.total),
                        dim3(512), 0, st, pk);
-  else
+  } else {
     hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, DV, Tag, false, MASKED>), dim3(pk.total),
                        dim3(512), 0, st, pk);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.hsplit > 1) {
