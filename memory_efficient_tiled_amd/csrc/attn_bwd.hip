@@ -17,8 +17,8 @@
 //  * attn_dkdv_pair_kernel: one workgroup per block of 128 keys of one KV
 //    head, looping over every query tile of the query heads it covers, with
 //    dK and dV accumulated in registers (dV in one wave of a pair, dK in the
-//    other); at D = 64 without a mask attn_dkdv_solo_kernel instead, where
-//    each wave does all four products for its keys.  When the KV heads alone
+//    other); at D = 64, 80 and 96 without a mask attn_dkdv_solo_kernel
+//    instead, where each wave does all four products for its keys.  When the KV heads alone
 //    give too few workgroups, the query heads of a group are split over
 //    several workgroups that write fp32 partial sums, and attn_dkdv_reduce
 //    adds them;
@@ -128,21 +128,25 @@ struct TileCopy {
 enum { kReadRows = 0, kReadCols = 1, kReadBoth = 2 };
 
 // One LDS layout that serves both reads without bank conflicts, for rows
-// of 128 bytes (D = 64) and 256 bytes (D = 128): the 16-byte chunk index is
-// XORed with a permutation of row bits.  Row reads (16 lanes, 16
-// consecutive rows, one chunk) need distinct bank groups over any 16
-// consecutive rows; transposing reads (32 lanes, 4 consecutive rows x 64
-// bytes) need those 4 rows in disjoint 64-byte quarters of the banks.  At
-// D = 128 rows r & 3 pick the quarter (XOR bits 3:2) and (r >> 2) & 3 the
-// chunk within it (bits 1:0); at D = 64, where rows r and r + 1 share the
-// banks, (r >> 1) & 1 picks the quarter within the half-row and
-// (r >> 2) & 3 the chunk.
+// of 128 bytes (D = 64), 192 bytes (compute dimension 96) and 256 bytes
+// (D = 128): the 16-byte chunk index is XORed with a permutation of row
+// bits.  Row reads (16 lanes, 16 consecutive rows, one chunk) need
+// distinct bank groups over any 16 consecutive rows; transposing reads (32
+// lanes, 4 consecutive rows x 64 bytes) need those 4 rows in disjoint
+// 64-byte quarters of the banks.  At D = 128 rows r & 3 pick the quarter
+// (XOR bits 3:2) and (r >> 2) & 3 the chunk within it (bits 1:0); at
+// D = 64, where rows r and r + 1 share the banks, (r >> 1) & 1 picks the
+// quarter within the half-row and (r >> 2) & 3 the chunk.  192-byte rows
+// start in a different quarter for each r % 4, so the row swizzle
+// (r >> 2) & 3, which permutes chunks within a quarter, serves both.
 template <int D>
-constexpr bool has_both_swz() { return D == 64 || D == 128; }
+constexpr bool has_both_swz() { return D == 64 || D == 96 || D == 128; }
 template <int D>
 __device__ __forceinline__ int u_swz(int r) {
-  static_assert(has_both_swz<D>(), "one-copy layout only at D = 64 and 128");
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  static_assert(has_both_swz<D>(), "one-copy layout only at D = 64, 96 and 128");
+  return D == 128  ? (((r & 3) << 2) | ((r >> 2) & 3))
+         : D == 96 ? ((r >> 2) & 3)
+                   : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 template <int D, int RD>
 __device__ __forceinline__ int tile_swz(int r) {
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
   // (cols); a wave picks its tile by an offset within the buffer.  With
   // UNI one copy in the layout of both reads (rows) serves both.
   constexpr bool SEP = bwd_sep_buffers(D, DV);
-  constexpr bool UNI = SEP && has_both_swz<D>();
+  constexpr bool UNI = SEP && (D == 64 || D == 128);  // (at 96: 5% slower here)
   constexpr int RDR = UNI ? kReadBoth : kReadRows;
   constexpr int TQG = TILE + TILEV;
   __shared__ __attribute__((aligned(1024))) uint16_t rows0[SEP ? TQG : 2 * TQG], rows1[SEP ? TQG : 1];
@@ -601,10 +605,10 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 }
 
 // dK, dV with each wave doing all four products for its own 32 keys
-// (D = 64 without a mask; written for D = 128 too, where it spills): 4
-// waves over 128 keys, K and V of the wave's keys in registers.  Per query
-// tile of BQ rows (64 at D = 64; 32 at D = 128, where K, V and the two
-// accumulators take 192 registers):
+// (D = 64, 80 and 96 without a mask; written for D = 128 too, where it
+// spills): 4 waves over 128 keys, K and V of the wave's keys in registers.
+// Per query tile of BQ rows (64 at D = 64; 32 at 80, 96 and 128, where K,
+// V and the two accumulators take 144 or 192 registers):
 //   S = Q K^T and dP = dO V^T (row reads of the Q and dO tiles),
 //   P = exp2(cs S - lse2) (0 above the causal diagonal), dS = P (dP - Delta),
 //   dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the same tiles,
@@ -614,11 +618,12 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 // work.
 template <int D, class Tag, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
-  static_assert(has_both_swz<D>(), "one-copy tile layout");
+  constexpr int DP = compute_dim(D);
+  static_assert(has_both_swz<DP>(), "one-copy tile layout");
   constexpr int NW = 4, BK = 128;
   constexpr int NQB = D == 64 ? 2 : 1, BQ = NQB * 32;
-  constexpr int DC = D / 16, NDB = D / 32, NKC = BQ / 16;
-  constexpr int TILE = BQ * D;
+  constexpr int DC = DP / 16, NDB = DP / 32, NKC = BQ / 16;
+  constexpr int TILE = BQ * DP;
   constexpr int IPW = TileCopy<D, BQ, NW>::PER_WAVE;
   using N = Num<Tag>;
 
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
 #pragma unroll
   for (int kc = 0; kc < DC; ++kc) {
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key < p.Nkv) {
+    if (key < p.Nkv && kc * 16 + hl * 8 < D) {
       x = *(const u32x4*)(p.k + (krow0 + key) * D + kc * 16 + hl * 8);
       y = *(const u32x4*)(p.v + (krow0 + key) * D + kc * 16 + hl * 8);
     }
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
   const int v_g = lane >> 4, v_r = lane & 15;
   const int v_key = 4 * hl + (v_r >> 2);
   const int v_d = 16 * (v_g & 1) + 4 * (v_r & 3);
-  const int v_sw = u_swz<D>(v_key), v_sw8 = u_swz<D>(v_key + 8);
+  const int v_sw = u_swz<DP>(v_key), v_sw8 = u_swz<DP>(v_key + 8);
 
   // P and dS in place of S and dP; accumulator register e of block qb is
   // query row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.
@@ -734,8 +739,8 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
       dp[qb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < DC; ++kc) {
-        s[qb] = N::mfma(read_rows<D, kReadBoth>(tq, qb * 32 + l32, kc, hl), kf[kc], s[qb]);
-        dp[qb] = N::mfma(read_rows<D, kReadBoth>(tg, qb * 32 + l32, kc, hl), vf[kc], dp[qb]);
+        s[qb] = N::mfma(read_rows<DP, kReadBoth>(tq, qb * 32 + l32, kc, hl), kf[kc], s[qb]);
+        dp[qb] = N::mfma(read_rows<DP, kReadBoth>(tg, qb * 32 + l32, kc, hl), vf[kc], dp[qb]);
       }
     }
     const float* const lsb = buf_at<buf, true, 0>(ld0, ld1);
@@ -754,8 +759,8 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
       const int row = kc * 16 + v_key;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        accv[db] = N::mfma(read_cols<D>(tg, row, db, v_d, v_sw, v_sw8), bp[kc], accv[db]);
-        acck[db] = N::mfma(read_cols<D>(tq, row, db, v_d, v_sw, v_sw8), bs[kc], acck[db]);
+        accv[db] = N::mfma(read_cols<DP>(tg, row, db, v_d, v_sw, v_sw8), bp[kc], accv[db]);
+        acck[db] = N::mfma(read_cols<DP>(tq, row, db, v_d, v_sw, v_sw8), bs[kc], acck[db]);
       }
     }
   };
@@ -816,7 +821,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
   // With UNI one copy of K in the layout of both reads (kr) serves the row
   // reads of S and the transposed reads of dQ, and V shares that layout.
   constexpr bool SEP = bwd_sep_buffers(D, DV);
-  constexpr bool UNI = SEP && has_both_swz<D>();
+  constexpr bool UNI = SEP && (D == 64 || D == 128);  // (at 96: 5% slower here)
   constexpr int RDR = UNI ? kReadBoth : kReadRows;
   __shared__ __attribute__((aligned(1024))) uint16_t kr0[SEP ? TILE : 2 * TILE], kr1[SEP ? TILE : 1];
   __shared__ __attribute__((aligned(1024))) uint16_t ktr0[UNI ? 1 : SEP ? TILE : 2 * TILE],
@@ -1140,10 +1145,11 @@ hipError_t side_stream(SideStream** out) {
 }
 
 // The dK/dV kernel: one wave per 32 keys doing all four products where its
-// registers allow (D = 64 without a mask; at D = 128 it spills 124-216
-// bytes per lane and runs 1.5x slower than the wave pairs), else the pairs.
+// registers allow (D = 64, 80 and 96 without a mask; at D = 128 it spills
+// 124-216 bytes per lane and runs 1.5x slower than the wave pairs), else
+// the pairs.
 constexpr bool bwd_solo_dkdv(int D, int DV, bool masked) {
-  return !masked && D == DV && D == 64;
+  return !masked && D == DV && (D == 64 || D == 80 || D == 96);
 }
 
 template <int D, int DV, class Tag, bool MASKED>
