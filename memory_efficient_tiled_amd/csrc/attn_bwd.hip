@@ -17,8 +17,8 @@
 //  * attn_dkdv_pair_kernel: one workgroup per block of 128 keys of one KV
 //    head, looping over every query tile of the query heads it covers, with
 //    dK and dV accumulated in registers (dV in one wave of a pair, dK in the
-//    other); at D = 64, 80 and 96 without a mask attn_dkdv_solo_kernel
-//    instead, where each wave does all four products for its keys.  When the KV heads alone
+//    other); at D = 64, 80 and 96 attn_dkdv_solo_kernel instead, where
+//    each wave does all four products for its keys.  When the KV heads alone
 //    give too few workgroups, the query heads of a group are split over
 //    several workgroups that write fp32 partial sums, and attn_dkdv_reduce
 //    adds them;
@@ -605,8 +605,8 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 }
 
 // dK, dV with each wave doing all four products for its own 32 keys
-// (D = 64, 80 and 96 without a mask; written for D = 128 too, where it
-// spills): 4 waves over 128 keys, K and V of the wave's keys in registers.
+// (D = 64, 80 and 96; written for D = 128 too, where it spills): 4 waves
+// over 128 keys, K and V of the wave's keys in registers.
 // Per query tile of BQ rows (64 at D = 64; 32 at 80, 96 and 128, where K,
 // V and the two accumulators take 144 or 192 registers):
 //   S = Q K^T and dP = dO V^T (row reads of the Q and dO tiles),
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(512, 2) void attn_dkdv_pair_kernel(BwdParams p) {
 // Nothing passes between waves, so a tile needs only the copies' barrier,
 // and the two workgroups on a CU overlap one another's vector and matrix
 // work.
-template <int D, class Tag, bool CAUSAL>
+template <int D, class Tag, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
   constexpr int DP = compute_dim(D);
   static_assert(has_both_swz<DP>(), "one-copy tile layout");
@@ -702,10 +702,21 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
   const int v_sw = u_swz<DP>(v_key), v_sw8 = u_swz<DP>(v_key + 8);
 
   // P and dS in place of S and dP; accumulator register e of block qb is
-  // query row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.
-  auto grads = [&](auto mskc, const float* lsb, f32x16* s, f32x16* dp, int q0)
-      __attribute__((always_inline)) {
+  // query row q0 + qb*32 + 8 (e / 4) + 4 hl + e % 4.  A mask enters as in
+  // the wave pairs: its base-2 bias joins the exponent, read once per key
+  // when it does not vary along rows and the tile holds no row past Nq,
+  // else per element with rows past Nq and rows that saw no key (lse2
+  // +inf) getting P = 0.
+  auto grads_impl = [&](auto mskc, auto rowc, const float* lsb, f32x16* s, f32x16* dp, int q0,
+                        int hq) __attribute__((always_inline)) {
     constexpr bool MSK = decltype(mskc)::value;
+    constexpr bool ROWMASK = decltype(rowc)::value;
+    const uint8_t* mbase = nullptr;
+    if constexpr (MASKED) mbase = p.mask;
+    const int64_t mrow0 = MASKED ? b * p.msb + hq * p.msh : 0;
+    float kbias = 0.f;
+    if constexpr (MASKED && !ROWMASK)
+      kbias = key < p.Nkv ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + key) : 0.f;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -715,12 +726,33 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
         const f32x4 dl = *(const f32x4*)(lsb + 64 + r);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
+          float pv;
+          if constexpr (MASKED && ROWMASK) {
+            const int row = q0 + r + e;
+            const float bias =
+                row < p.Nq && key < p.Nkv
+                    ? mask_bias1<Tag>(mbase, p.mask_mode, mrow0 + row * p.msq + key)
+                    : 0.f;
+            pv = (row < p.Nq && ls[e] != INFINITY)
+                     ? fast_exp2(fmaf(p.cs, s[qb][4 * j + e], bias) - ls[e])
+                     : 0.f;
+          } else if constexpr (MASKED) {
+            pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], kbias - ls[e]));
+          } else {
+            pv = fast_exp2(fmaf(p.cs, s[qb][4 * j + e], -ls[e]));
+          }
           if (MSK && key > q0 + r + e + p.coff) pv = 0.f;
           s[qb][4 * j + e] = pv;
           dp[qb][4 * j + e] = pv * (dp[qb][4 * j + e] - dl[e]);
         }
       }
+  };
+  auto grads = [&](auto mskc, const float* lsb, f32x16* s, f32x16* dp, int q0, int hq)
+      __attribute__((always_inline)) {
+    if (MASKED && p.msq == 0 && q0 + BQ <= p.Nq)
+      grads_impl(mskc, std::false_type{}, lsb, s, dp, q0, hq);
+    else
+      grads_impl(mskc, std::true_type{}, lsb, s, dp, q0, hq);
   };
 
   auto tile = [&](int u, auto bufc) {
@@ -745,9 +777,9 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_solo_kernel(BwdParams p) {
     }
     const float* const lsb = buf_at<buf, true, 0>(ld0, ld1);
     if (CAUSAL && kw0 + 31 > q0 + p.coff)
-      grads(std::true_type{}, lsb, s, dp, q0);
+      grads(std::true_type{}, lsb, s, dp, q0, hq);
     else
-      grads(std::false_type{}, lsb, s, dp, q0);
+      grads(std::false_type{}, lsb, s, dp, q0, hq);
     u32x4 bp[NKC], bs[NKC];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -1145,11 +1177,11 @@ hipError_t side_stream(SideStream** out) {
 }
 
 // The dK/dV kernel: one wave per 32 keys doing all four products where its
-// registers allow (D = 64, 80 and 96 without a mask; at D = 128 it spills
-// 124-216 bytes per lane and runs 1.5x slower than the wave pairs), else
-// the pairs.
-constexpr bool bwd_solo_dkdv(int D, int DV, bool masked) {
-  return !masked && D == DV && (D == 64 || D == 80 || D == 96);
+// registers allow (D = 64, 80 and 96, with or without a mask; at D = 128 it
+// spills 124-216 bytes per lane and runs 1.5x slower than the wave pairs),
+// else the pairs.
+constexpr bool bwd_solo_dkdv(int D, int DV, bool) {
+  return D == DV && (D == 64 || D == 80 || D == 96);
 }
 
 template <int D, int DV, class Tag, bool MASKED>
@@ -1197,11 +1229,11 @@ hipError_t launch_bwd(BwdParams p, bool causal, hipStream_t st, SideStream* side
   pk.total = p.B * p.Hkv * p.hsplit * pk.n_tiles;
   if constexpr (bwd_solo_dkdv(D, DV, MASKED)) {
     if (causal)
-      hipLaunchKernelGGL((attn_dkdv_solo_kernel<D, Tag, true>), dim3(pk.total), dim3(256), 0, st,
-                         pk);
+      hipLaunchKernelGGL((attn_dkdv_solo_kernel<D, Tag, true, MASKED>), dim3(pk.total), dim3(256),
+                         0, st, pk);
     else
-      hipLaunchKernelGGL((attn_dkdv_solo_kernel<D, Tag, false>), dim3(pk.total), dim3(256), 0,
-                         st, pk);
+      hipLaunchKernelGGL((attn_dkdv_solo_kernel<D, Tag, false, MASKED>), dim3(pk.total),
+                         dim3(256), 0, st, pk);
   } else if (causal) {
     hipLaunchKernelGGL((attn_dkdv_pair_kernel<D, DV, Tag, true, MASKED>), dim3(pk.total),
                        dim3(512), 0, st, pk);
