@@ -213,9 +213,12 @@ def test_long_d128_several_tiles(gpu_device):
     run_case(gpu_device, 1, 4, 4, 1500, 1500, 128, inputs.BF16, False, seed=46)
 
 
-def test_deterministic(gpu_device):
+@pytest.mark.parametrize("D", [128, 64, 96])
+def test_deterministic(gpu_device, D):
+    # the wave-pair dK/dV kernel (128) and the one-wave kernel (64, 96), both
+    # with head-split partials summed by the reduce kernel
     import torch
-    x = inputs.make_inputs(1, 4, 2, 500, 500, 128, inputs.BF16, seed=47)
+    x = inputs.make_inputs(1, 4, 2, 500, 500, D, inputs.BF16, seed=47)
     q, k, v, g = (to_device(a, inputs.BF16, gpu_device)
                   for a in (x.q, x.k, x.v, inputs.make_dout(x)))
     out, lse = binding.attn_fwd(q, k, v)
