@@ -398,10 +398,10 @@ def test_value_width_sdpa_autograd(gpu_device):
         check_grad(name, _host(leaf.grad), r, dtype, "sdpa autograd D=192 Dv=128", None, t)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 def test_broadcast_additive_mask_large_bias(gpu_device, D):
     """A [B, 1, 1, Nkv] additive fp16 mask (row stride 0) with values of
-    12..20, with Nq not a multiple of the 64-row query tile.  Rows past Nq
+    12..20, with Nq not a multiple of the 64- or 32-row query tile.  Rows past Nq
     in the last tile must get P = 0: exp2 of such a bias alone exceeds the
     fp16 range, and inf * 0 would turn into NaN in dV and dK."""
     import torch
