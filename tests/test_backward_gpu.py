@@ -182,17 +182,18 @@ def test_short_sequences(gpu_device, n):
     run_case(gpu_device, 1, 2, 2, n, n, 64, inputs.BF16, False, seed=45 + n)
 
 
-@pytest.mark.parametrize("D,dtype", [(128, inputs.BF16), (64, inputs.F16)])
-def test_dq_last_round_split(gpu_device, D, dtype):
-    """33 heads x 16 query tiles of 128 rows = 528 dQ workgroups on 512
-    slots (256 CUs x 2): the 16 tiles of the last, partial round are cut
-    into 8 key ranges of 128 keys, whose fp32 partials the reduce kernel
-    adds.  Element-wise parity of dQ, dK and dV; the workspace pool's peak
-    holds the partials (8 x 16 x 128 rows x D fp32) besides Delta and the
-    base-2 LSE."""
+@pytest.mark.parametrize("D,dtype,Nq,bm", [(128, inputs.BF16, 2000, 128),
+                                            (64, inputs.F16, 4000, 256)])
+def test_dq_last_round_split(gpu_device, D, dtype, Nq, bm):
+    """33 heads x 16 query tiles of bm rows (128; 256 at D = 64) = 528 dQ
+    workgroups on 512 slots (256 CUs x 2): the 16 tiles of the last, partial
+    round are cut into 8 key ranges of 128 keys, whose fp32 partials the
+    reduce kernel adds.  Element-wise parity of dQ, dK and dV; the workspace
+    pool's peak holds the partials (8 x 16 x bm rows x D fp32) besides Delta
+    and the base-2 LSE."""
     import torch
     from tests.parity import PoolPeak
-    B, H, Nq, Nkv = 1, 33, 2000, 1024
+    B, H, Nkv = 1, 33, 1024
     run_case(gpu_device, B, H, H, Nq, Nkv, D, dtype, False, seed=60 + D)
     x = inputs.make_inputs(B, H, H, Nq, Nkv, D, dtype, seed=61)
     do = inputs.make_dout(x)
@@ -205,7 +206,7 @@ def test_dq_last_round_split(gpu_device, D, dtype):
     binding.attn_bwd(q, k, v, out, lse, g)
     torch.cuda.synchronize(gpu_device)
     rows_bytes = (B * H * Nq * 4 + 255) // 256 * 256
-    partials = 8 * 16 * 128 * D * 4
+    partials = 8 * 16 * bm * D * 4
     assert pool.read() >= 2 * rows_bytes + partials
 
 
