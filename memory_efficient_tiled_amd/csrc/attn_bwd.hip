@@ -205,8 +205,7 @@ constexpr bool bwd_sep_buffers(int D, int DV) { return D != 256 && D == DV; }
 // Query rows per wave (32 x) and per workgroup of the dQ kernel: 64 per wave
 // at D = 64 without a causal mask, where Q, dO and dQ of 64 rows fit the
 // registers and each K and V operand read from LDS serves two row blocks
-// (D = 64 sweep 16384 +3.4%, 4096 +5%; causal GQA 16384 lost 3% and keeps
-// 32); 32 elsewhere.
+// (with a causal mask 64-row waves ran slower); 32 elsewhere.
 constexpr int dq_row_blocks(int D, bool causal) { return D == 64 && !causal ? 2 : 1; }
 constexpr int dq_block_rows(int D, bool causal) { return 4 * 32 * dq_row_blocks(D, causal); }
 

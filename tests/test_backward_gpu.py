@@ -69,7 +69,11 @@ def check_grad(name, got, ref, dtype, what, zero_from=None, extra=0.0):
             f"{what} {name}: non-zero gradient for keys no query sees"
     worst = np.unravel_index(np.argmax(err - bound), err.shape)
     assert np.all(err <= bound), f"{what} {name}: err {err[worst]:.3e} at {worst} > bound"
-    assert err.mean() <= mbound, f"{what} {name}: mean err {err.mean():.3e} > {mbound:.3e}"
+    # The mean criterion is relative to rms(ref).  An identically zero exact
+    # gradient (one key: dS = P (dP - Delta) = 0) leaves only rounding noise
+    # of dP - Delta, which the element bound's Delta term covers.
+    if rms > 0.0:
+        assert err.mean() <= mbound, f"{what} {name}: mean err {err.mean():.3e} > {mbound:.3e}"
 
 
 def delta_terms(x, do, ref, causal, causal_offset=0, bias=None):
@@ -166,20 +170,24 @@ def test_more_keys_than_queries_causal(gpu_device):
     run_case(gpu_device, 1, 2, 1, 130, 600, 64, inputs.F16, True, seed=43)
 
 
-def test_more_queries_than_keys(gpu_device):
-    run_case(gpu_device, 1, 4, 4, 700, 90, 128, inputs.F16, True, seed=44)
+@pytest.mark.parametrize("D", [128, 64])
+def test_more_queries_than_keys(gpu_device, D):
+    run_case(gpu_device, 1, 4, 4, 700, 90, D, inputs.F16, True, seed=44)
 
 
+@pytest.mark.parametrize("D", [128, 64, 96])
 @pytest.mark.parametrize("nq,nkv", [(100, 700), (500, 130)])
-def test_bottom_right(gpu_device, nq, nkv):
+def test_bottom_right(gpu_device, nq, nkv, D):
     # queries after a cache of keys; more queries than keys (the first rows
-    # see no key and get zero gradients)
-    run_case(gpu_device, 1, 4, 2, nq, nkv, 128, inputs.BF16, "bottom_right", seed=nq)
+    # see no key and get zero gradients); the wave-pair dK/dV kernel (128)
+    # and the one-wave kernel (64, 96)
+    run_case(gpu_device, 1, 4, 2, nq, nkv, D, inputs.BF16, "bottom_right", seed=nq + D)
 
 
+@pytest.mark.parametrize("D", [64, 96])
 @pytest.mark.parametrize("n", [1, 7, 64, 129])
-def test_short_sequences(gpu_device, n):
-    run_case(gpu_device, 1, 2, 2, n, n, 64, inputs.BF16, False, seed=45 + n)
+def test_short_sequences(gpu_device, n, D):
+    run_case(gpu_device, 1, 2, 2, n, n, D, inputs.BF16, False, seed=45 + n)
 
 
 @pytest.mark.parametrize("D,dtype,Nq,bm", [(128, inputs.BF16, 2000, 128),
