@@ -406,15 +406,29 @@ __global__ __launch_bounds__(NW * 64, kWavesPerSimd) void attn_fwd_kernel(Params
         const int64_t off = b * p.msb + hq * p.msh + (int64_t)min(qrow, p.Nq - 1) * p.msq;
         const uint8_t* mrow = p.mask + off * (keep_mode ? 1 : 2);
         if (keep_mode) {
+          // A tile in which the mask keeps every key of every row of the wave
+          // (most tiles of a key-padding mask) skips the per-score selects:
+          // any zero byte among a lane's mask words shows in the usual
+          // has-a-zero-byte test, and the wave votes.
+          uint32_t w[NKB][4];
+          uint32_t zero = 0u;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const uint32_t w = mask_keep4(mrow, k0 + kb * 32 + 8 * g + 4 * hl, p.Nkv);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (((w >> (8 * i)) & 0xffu) == 0u) s[qb * NKB + kb][4 * g + i] = -INFINITY;
+              w[kb][g] = mask_keep4(mrow, k0 + kb * 32 + 8 * g + 4 * hl, p.Nkv);
+              zero |= (w[kb][g] - 0x01010101u) & ~w[kb][g] & 0x80808080u;
             }
+          if (__builtin_amdgcn_ballot_w64(zero != 0u)) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (((w[kb][g] >> (8 * i)) & 0xffu) == 0u)
+                    s[qb * NKB + kb][4 * g + i] = -INFINITY;
+          }
         } else {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
