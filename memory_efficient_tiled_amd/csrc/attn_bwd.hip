@@ -987,6 +987,34 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_dq_kernel(BwdParam
     constexpr bool MSK = decltype(mskc)::value;
     const int qrow = qw0 + 32 * qb + l32;
     const bool row_live = qrow < p.Nq;
+    if constexpr (MASKED) {
+      // A boolean mask that keeps all of this tile's keys for every row of
+      // the wave (most tiles of a key-padding mask) changes nothing: take
+      // the unmasked form (has-a-zero-byte test on each word, wave vote).
+      // A row that saw no key in the forward has a removed key here, or
+      // lies entirely above the causal diagonal (MSK zeroes it), and rows
+      // past Nq have Q = dO = 0 and give dS = 0 either way.
+      if (p.mask_mode == ATTN_MASK_BOOL) {
+        uint32_t zero = 0u;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t w = mask_keep4(mrow[qb], t * BN + 8 * g + 4 * hl, p.Nkv);
+          zero |= (w - 0x01010101u) & ~w & 0x80808080u;
+        }
+        if (!__builtin_amdgcn_ballot_w64(zero != 0u)) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int e = 4 * g + i;
+              float pv = fast_exp2(fmaf(p.cs, s[e], nl2[qb]));
+              if (MSK && t * BN + 8 * g + 4 * hl + i > qrow + p.coff) pv = 0.f;
+              dp[e] = pv * (dp[e] - dl[qb]);
+            }
+          return;
+        }
+      }
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float bias[4] = {0.f, 0.f, 0.f, 0.f};
