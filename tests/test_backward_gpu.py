@@ -299,11 +299,14 @@ def test_masked_gradients(gpu_device, kind, D):
         assert torch.all(dq[0, 1, 5] == 0), "a row with no key has no gradient"
 
 
-def test_sdpa_masked_autograd(gpu_device):
+@pytest.mark.parametrize("D", [64, 128])
+def test_sdpa_masked_autograd(gpu_device, D):
+    # a boolean key-padding mask: batch 0 keeps every key (the kernels' paths
+    # for tiles that keep all keys), batch 1 drops keys 100..119
     import torch
     import memory_efficient_tiled_amd as mta
     dtype = inputs.F16
-    x = inputs.make_inputs(2, 4, 4, 90, 120, 64, dtype, seed=61)
+    x = inputs.make_inputs(2, 4, 4, 90, 120, D, dtype, seed=61)
     do = inputs.make_dout(x)
     keep = np.ones((2, 1, 1, 120), dtype=bool)
     keep[1, ..., 100:] = False                        # key padding of batch 1
@@ -313,10 +316,10 @@ def test_sdpa_masked_autograd(gpu_device):
     torch.cuda.synchronize(gpu_device)
     bias = np.broadcast_to(np.where(keep, 0.0, -np.inf), (2, 4, 90, 120))
     dec = [_decode(a, dtype) for a in (x.q, x.k, x.v, do)]
-    ref = oracle.attention_backward(*dec, oracle.scale_value(None, 64), False, bias=bias)
+    ref = oracle.attention_backward(*dec, oracle.scale_value(None, D), False, bias=bias)
     terms = delta_terms_dec(dec, ref, dtype, False, bias=bias)
     for name, leaf, r, t in zip(("dq", "dk", "dv"), leaves, ref, terms):
-        check_grad(name, _host(leaf.grad), r, dtype, "sdpa masked autograd", None, t)
+        check_grad(name, _host(leaf.grad), r, dtype, f"sdpa masked autograd D={D}", None, t)
     assert torch.all(leaves[1].grad[1, :, 100:] == 0) and torch.all(leaves[2].grad[1, :, 100:] == 0)
 
 
